@@ -99,9 +99,11 @@ def haar_rotation(d: int, rng: np.random.Generator) -> np.ndarray:
 
 
 def head_inputs(cfg_seed: int, layer: int, kv_head: int, g: int, n_cache: int,
-                n_dec_q: int = 1, layout: int = HALF, qk_std: str = "shared") -> dict:
+                n_dec_q: int = 1, layout: int = HALF, qk_std: str = "shared", seq: int = 0) -> dict:
     """All inputs of one (layer, KV head): calibration (pre-RoPE), cache K (post-RoPE),
-    cache V, decode queries (post-RoPE, position n_cache), as fp32 numpy arrays."""
+    cache V, decode queries (post-RoPE, position n_cache), as fp32 numpy arrays.
+    `seq` selects the batch row: it changes the cache and query streams, not the
+    per-head scales or the calibration set."""
     D = HEAD_DIM
     sig = block_std(rng_for(cfg_seed, layer, kv_head, S_SIGMA))
     sc = coord_std(sig, layout)
@@ -109,11 +111,12 @@ def head_inputs(cfg_seed: int, layer: int, kv_head: int, g: int, n_cache: int,
         sq = sc
     else:
         sq = coord_std(block_std(rng_for(cfg_seed, layer, kv_head, S_SIGMA + 100)), layout)
-    rk = rng_for(cfg_seed, layer, kv_head, S_CACHE_K)
+    so = 16 * seq
+    rk = rng_for(cfg_seed, layer, kv_head, S_CACHE_K + so)
     k_pre = (rk.standard_normal((n_cache, D)) * sc).astype(np.float32)
     k = apply_rope(k_pre, np.arange(n_cache), layout=layout)
-    v = rng_for(cfg_seed, layer, kv_head, S_CACHE_V).standard_normal((n_cache, D)).astype(np.float32)
-    q_pre = (rng_for(cfg_seed, layer, kv_head, S_DEC_Q).standard_normal((n_dec_q, g, D)) * sq).astype(np.float32)
+    v = rng_for(cfg_seed, layer, kv_head, S_CACHE_V + so).standard_normal((n_cache, D)).astype(np.float32)
+    q_pre = (rng_for(cfg_seed, layer, kv_head, S_DEC_Q + so).standard_normal((n_dec_q, g, D)) * sq).astype(np.float32)
     q = apply_rope(q_pre.reshape(n_dec_q * g, D), np.full(n_dec_q * g, n_cache), layout=layout)
     q = q.reshape(n_dec_q, g, D)
     cq = (rng_for(cfg_seed, layer, kv_head, S_CAL_Q).standard_normal((N_CALIB, g, D)) * sq).astype(np.float32)

@@ -1,0 +1,269 @@
+/*
+ * gtq.h -- C ABI of libgtq: Block-GTQ packed mixed-rate TQ-MSE KV cache and
+ * attention over it, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the Block-GTQ page ("Block-GTQ: RoPE-Block Rate
+ * Allocation for KV-Cache Quantization", abstract) and the TurboQuant pipeline
+ * diagram (hsthanb4.github.io kvcache_quant_tutorial_2026, 01_turboquant_pipeline,
+ * "paper" column):
+ *   - keys are split into the 64 two-coordinate RoPE frequency blocks of a
+ *     128-dim head; each block gets its own bit width (abstract, 2nd sentence);
+ *   - the width comes from largest-marginal-gain allocation of a label-free
+ *     query-key energy score weighted by codec rate penalties (3rd, 4th sentence);
+ *   - blocks of equal rate form a group; each group of a key, and the whole value
+ *     vector, is a TurboQuant-MSE vector: norm, random rotation, per-coordinate
+ *     Lloyd-Max scalar quantization, bit packing (5th sentence; diagram boxes
+ *     "random rotation", "per-coordinate MSE scalar quantization");
+ *   - attention reads the packed cache directly and never builds a decoded
+ *     fp16 K/V cache (5th sentence).
+ *
+ * Conventions for every call:
+ *   - head_dim is 128 (64 RoPE blocks); other sizes return GTQ_EUNSUPPORTED.
+ *   - "host" pointers are read during the call only; the library copies what it
+ *     keeps. "device" pointers are caller-owned GPU memory (e.g. torch tensors).
+ *   - Calls that take a hip_stream enqueue asynchronous GPU work on that stream
+ *     (NULL = the default stream) and return before it finishes. They allocate no
+ *     device memory; scratch memory comes from a caller-provided workspace.
+ *   - Every call validates its arguments on the host before enqueuing anything.
+ *     On failure it returns a nonzero gtq_status, enqueues nothing, and
+ *     gtq_last_error() returns a message (per thread) describing the failure.
+ *   - Device-side slot/length overruns that the host cannot see (slot values in
+ *     device arrays) are skipped by the kernels and counted; see
+ *     gtq_plan_overflow_count.
+ */
+#ifndef GTQ_H_
+#define GTQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gtq_status;
+enum {
+  GTQ_OK = 0,
+  GTQ_EINVAL = 1,        /* bad argument (null pointer, out-of-range value)     */
+  GTQ_EUNSUPPORTED = 2,  /* valid but not supported by this build (head_dim)    */
+  GTQ_ENOMEM = 3,        /* host or device allocation failed (plan creation)   */
+  GTQ_EDEVICE = 4,       /* HIP runtime or kernel launch error                  */
+  GTQ_ECAPACITY = 5      /* cache or workspace too small for the request        */
+};
+
+enum { GTQ_ROPE_HALF = 0,        /* block j = coordinates (j, j + 64)          */
+       GTQ_ROPE_INTERLEAVED = 1  /* block j = coordinates (2j, 2j + 1)         */ };
+
+#define GTQ_HEAD_DIM 128
+#define GTQ_BLOCKS 64
+#define GTQ_MAX_GROUPS 4
+#define GTQ_KNORM_STRIDE 4  /* floats per token of K norms (one per group, padded) */
+#define GTQ_VBLOCK 8        /* tokens per V code block                          */
+#define GTQ_SEQ_ALIGN 32    /* cache capacity must be a multiple of this        */
+
+/* Message of the last failing call on this thread ("" if none). Never NULL. */
+const char* gtq_last_error(void);
+
+/* ---------------------------------------------------------------- host math */
+
+/* Rate penalties: d_out[b] for b = 0..b_max (b_max <= 4) is the mean squared error
+ * of the b-bit Lloyd-Max quantizer of a unit Gaussian (d_out[0] = 1). These are the
+ * "codec-dependent rate penalties" of the abstract (3rd sentence) for TQ-MSE.
+ * Errors: EINVAL if d_out is NULL or b_max outside [1, 4]. */
+gtq_status gtq_rate_distortion(int32_t b_max, double* d_out);
+
+/* The stored codebook of rate `bits` (1..4): centroids[2^bits] ascending (the
+ * Lloyd-Max centroids of N(0,1), rounded to binary16 and returned as float) and
+ * thresholds[2^bits - 1] (midpoints; a value >= t_k is above threshold k). A group of
+ * dimension d quantizes sqrt(d) * Pi * x / ||x|| against these. Either output may be
+ * NULL. Errors: EINVAL if bits outside [1, 4]. */
+gtq_status gtq_codebook(int32_t bits, float* centroids, float* thresholds);
+
+/* Largest-marginal-gain rate allocation for one (layer, KV head)
+ * (abstract, 3rd and 4th sentence).
+ *   q_cal [n_q][head_dim] host fp32: pre-RoPE calibration queries of all the query
+ *         heads that share this KV head, flattened;
+ *   k_cal [n_k][head_dim] host fp32: pre-RoPE calibration keys.
+ * Energy score s_j = mean_q ||q_j||^2 * mean_k ||k_j||^2 per RoPE block j (fp64).
+ * Starting from b_j = b_min, one bit at a time goes to the block with the largest
+ * s_j * (D(b_j) - D(b_j + 1)) among blocks with b_j < b_max (ties: smallest j) until
+ * sum_j b_j == budget. Outputs: rates_out[64] (required), scores_out[64] and
+ * proxy_out (= sum_j s_j D(b_j)) optional.
+ * Errors: EINVAL for NULL inputs, n_q/n_k < 1, bad rope_layout, b_min/b_max outside
+ * 1 <= b_min <= b_max <= 4, budget outside [64 b_min, 64 b_max];
+ * EUNSUPPORTED if head_dim != 128. */
+gtq_status gtq_alloc_rates(const float* q_cal, int64_t n_q, const float* k_cal, int64_t n_k,
+                           int32_t head_dim, int32_t rope_layout, int32_t b_min, int32_t b_max,
+                           int32_t budget, uint8_t* rates_out, double* scores_out,
+                           double* proxy_out);
+
+/* Group layout of one head's packed key record, derived from its 64 block rates.
+ * Groups are the distinct rates in ascending order; inside a group, blocks ascend
+ * and each contributes its two coordinates (abstract, 5th sentence). The key record
+ * is one little-endian bit stream: code i of group g occupies bits
+ * [bit_offset[g] + i*rate[g], ... + rate[g]); bit p is bit (p % 32) of u32 word p/32. */
+typedef struct gtq_head_layout {
+  int32_t n_groups;                 /* distinct rates present (1..4)                 */
+  int32_t rate[GTQ_MAX_GROUPS];     /* ascending                                    */
+  int32_t dim[GTQ_MAX_GROUPS];      /* 2 * number of blocks at that rate             */
+  int32_t bit_offset[GTQ_MAX_GROUPS];
+  int32_t rot_offset[GTQ_MAX_GROUPS]; /* float offset of the group's rotation inside
+                                         this head's slice of gtq_plan_desc.k_rot   */
+  int32_t k_words;                  /* u32 words of one token's key record          */
+  int32_t coord[GTQ_HEAD_DIM];      /* head coordinate of each record position      */
+} gtq_head_layout;
+
+/* Computes the layout from rates[64] (each in [1, 4]). Host only.
+ * Errors: EINVAL for NULL pointers, rates outside [1,4], bad rope_layout. */
+gtq_status gtq_head_layout_from_rates(const uint8_t* rates, int32_t rope_layout,
+                                      gtq_head_layout* out);
+
+/* ---------------------------------------------------------------- plans */
+
+enum { GTQ_PLAN_HOST_ONLY = 1 /* build and validate on the host, no device copy */ };
+
+typedef struct gtq_plan_desc {
+  int32_t n_layers, n_kv_heads, n_q_heads; /* n_q_heads a multiple of n_kv_heads      */
+  int32_t head_dim;                        /* 128                                     */
+  int32_t rope_layout;                     /* GTQ_ROPE_HALF | GTQ_ROPE_INTERLEAVED     */
+  int32_t k_budget;                        /* sum_j b_j of every head (128 = K2, 192 = K3) */
+  int32_t v_bits;                          /* 1..4, values are one 128-dim group       */
+  int32_t flags;                           /* GTQ_PLAN_HOST_ONLY or 0                 */
+  const uint8_t* k_rates; /* host [n_layers][n_kv_heads][64], each head summing to k_budget */
+  const float* k_rot;     /* host: for l, h, groups in ascending rate: the group's d x d
+                             rotation, row-major fp32, concatenated (each head's slice is
+                             sum_g d_g^2 floats)                                     */
+  const float* v_rot;     /* host [n_layers][n_kv_heads][128][128] row-major fp32      */
+} gtq_plan_desc;
+
+typedef struct gtq_plan gtq_plan;
+
+/* Builds a plan: group layouts, codebooks, decode tables; copies the rotations and
+ * uploads everything to the current HIP device (unless GTQ_PLAN_HOST_ONLY). The plan
+ * is immutable afterwards and may be used from several streams at once.
+ * Errors: EINVAL (NULL, counts < 1, rates outside [1,4] or not summing to k_budget,
+ * k_budget not a multiple of 16, v_bits outside [1,4], bad flags/layout);
+ * EUNSUPPORTED (head_dim != 128); ENOMEM; EDEVICE (no device / upload failed). */
+gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out);
+/* Frees the plan (host and device copies). Synchronizes the device. NULL is a no-op. */
+gtq_status gtq_plan_destroy(gtq_plan* plan);
+gtq_status gtq_plan_layout(const gtq_plan* plan, int32_t layer, int32_t kv_head,
+                           gtq_head_layout* out);
+/* Number of device-side overruns (slot >= capacity, seq >= batch) skipped by append
+ * kernels since the plan was created. Synchronizes the device. */
+gtq_status gtq_plan_overflow_count(const gtq_plan* plan, int64_t* out);
+
+/* ---------------------------------------------------------------- caches */
+
+/* One layer's packed cache, device memory owned by the caller:
+ *   k_codes [batch][n_kv_heads][capacity][k_words]   u32, token-major key records
+ *   k_norms [batch][n_kv_heads][capacity][4]          fp32, one norm per key group
+ *   v_codes [batch][n_kv_heads][capacity/8][32*v_bits] u32: blocks of 8 tokens; inside
+ *           a block, coordinate c (in the value rotation's basis) owns bits
+ *           [8*v_bits*c, 8*v_bits*(c+1)) and token j of the block the v_bits at
+ *           8*v_bits*c + v_bits*j (little-endian u32 words)
+ *   v_norms [batch][n_kv_heads][capacity]            fp32
+ * capacity is a multiple of 32. */
+typedef struct gtq_cache_view {
+  uint32_t* k_codes;
+  float* k_norms;
+  uint32_t* v_codes;
+  float* v_norms;
+  int32_t batch;
+  int64_t capacity;
+} gtq_cache_view;
+
+typedef struct gtq_cache_sizes {
+  size_t k_codes_bytes, k_norms_bytes, v_codes_bytes, v_norms_bytes;
+  int32_t k_words, v_words_per_block;
+  /* code bits per token and KV head ("logical bits", abstract 7th sentence) and the
+     bytes per token and KV head including norms */
+  int32_t logical_bits_per_token;
+  int32_t bytes_per_token;
+} gtq_cache_sizes;
+
+/* Byte sizes of one layer's cache. Errors: EINVAL (NULL, batch < 1, capacity < 1 or
+ * not a multiple of 32). */
+gtq_status gtq_cache_bytes(const gtq_plan* plan, int32_t batch, int64_t capacity,
+                           gtq_cache_sizes* out);
+
+/* ---------------------------------------------------------------- append */
+
+/* Fused rotate + quantize + pack of n_tok new tokens into layer `layer`'s cache
+ * (TurboQuant diagram, "paper" column: input -> rotation -> scalar MSE quantization).
+ *   k, v     device [n_tok][n_kv_heads][128] fp32, post-RoPE keys, values;
+ *   seq_idx  device [n_tok] int32: sequence (batch row) of each token;
+ *   slot     device [n_tok] int64: position of each token in its sequence.
+ * Per token and KV head: for each key group, nu = ||x_g|| (accumulated in fp64,
+ * stored fp32), z = sqrt(d_g) * Pi_g * x_g / nu, code_i = #{k : z_i >= t_k}; same for
+ * the value vector with Pi_V and v_bits. A zero vector stores norm 0 and codes
+ * 2^(b-1). Tokens with seq_idx outside [0, batch) or slot outside [0, capacity) are
+ * skipped and counted (gtq_plan_overflow_count). Two tokens of one call must not
+ * target the same (sequence, slot).
+ * Errors: EINVAL (NULL, layer out of range, host-only plan, n_tok < 0). */
+gtq_status gtq_quantize_append(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                               const float* k, const float* v, const int32_t* seq_idx,
+                               const int64_t* slot, int64_t n_tok, void* hip_stream);
+
+/* Same for n_tok consecutive tokens of one sequence at slots pos0 .. pos0+n_tok-1
+ * (a prompt chunk); k, v device [n_tok][n_kv_heads][128]. Writes whole value blocks
+ * without atomics where the chunk covers them.
+ * Errors: EINVAL (as above, seq outside [0, batch)); ECAPACITY if
+ * pos0 + n_tok > capacity. */
+gtq_status gtq_quantize_append_chunk(const gtq_plan* plan, int32_t layer,
+                                     const gtq_cache_view* cache, const float* k,
+                                     const float* v, int32_t seq, int64_t pos0,
+                                     int64_t n_tok, void* hip_stream);
+
+/* ---------------------------------------------------------------- attention */
+
+/* Workspace bytes that gtq_decode_attn needs for `batch` sequences of at most
+ * max_len cached tokens with split size `chunk` (0 = automatic; else a multiple of
+ * 32). The workspace holds the split-K partials and one arrival counter per row tile:
+ * it must be zero-filled before its first use, and every completed call leaves the
+ * counters at zero again, so one workspace can serve any later decode or prefill
+ * call whose size fits. Calls that share a workspace must be ordered on one stream. */
+gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64_t max_len,
+                                      int32_t chunk, size_t* out);
+
+/* Decode attention of one new query per sequence over the packed cache, without a
+ * decoded K/V cache (abstract, 5th sentence).
+ *   q        device [batch][n_q_heads][128] fp32, post-RoPE; query head h reads KV
+ *            head h / (n_q_heads / n_kv_heads);
+ *   seq_len  device [batch] int32: cached tokens of each sequence (all visible;
+ *            values are clamped to [0, min(max_len, capacity)]);
+ *   max_len  host: an upper bound of seq_len (sizes the split grid);
+ *   out      device [batch][n_q_heads][128] fp32;
+ *   logits   optional device [batch][n_q_heads][max_len] fp32 (scale * q . k_hat for
+ *            every visible token; entries >= seq_len untouched), for tests.
+ * Logit of token n, query head h: scale * sum_g nu_{n,g} / sqrt(d_g) *
+ * sum_{i in g} (Pi_g q_g)_i C_{b_g}[code_{n,i}]; softmax over n < seq_len; output
+ * Pi_V^T sum_n p_n nu^V_n C_{b_V}[vcode_n] / sqrt(128). Split-K over `chunk`-token
+ * pieces with a log-sum-exp merge, all in one kernel launch (the last workgroup of a
+ * row tile merges). A sequence with seq_len 0 gets a zero output.
+ * Errors: EINVAL (NULL, layer, scale not finite, chunk not a multiple of 32, host-only
+ * plan, max_len < 0); ECAPACITY (workspace too small, max_len > capacity). */
+gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                           const float* q, const int32_t* seq_len, int64_t max_len,
+                           float softmax_scale, int32_t chunk, float* out, float* logits,
+                           void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Workspace bytes for gtq_prefill_attn on a chunk of n_tok queries whose last
+ * position is pos0 + n_tok - 1 (same zero-fill contract as the decode workspace). */
+gtq_status gtq_prefill_workspace_bytes(const gtq_plan* plan, int64_t pos0, int64_t n_tok,
+                                       int32_t chunk, size_t* out);
+
+/* Causal attention of a prompt chunk over the packed cache of sequence `seq`:
+ * q device [n_tok][n_q_heads][128] fp32 (post-RoPE) at positions pos0 .. pos0+n_tok-1;
+ * the chunk's own keys/values must already be appended (gtq_quantize_append_chunk).
+ * Query t sees cached positions 0 .. pos0 + t. out device [n_tok][n_q_heads][128].
+ * Errors: as gtq_decode_attn; ECAPACITY if pos0 + n_tok > capacity. */
+gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                            const float* q, int32_t seq, int64_t pos0, int64_t n_tok,
+                            float softmax_scale, int32_t chunk, float* out, void* workspace,
+                            size_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GTQ_H_ */

@@ -1,0 +1,1419 @@
+// GPU part of libgtq for gfx950: plan upload, the fused rotate+quantize+pack
+// append kernel, query rotation, the split-K packed-cache attention kernel and
+// the log-sum-exp merge with the inverse value rotation.
+//
+// Method: Block-GTQ page (abstract, 5th sentence: attention over packed caches
+// without a decoded fp16 KV cache) and the TurboQuant pipeline diagram ("paper"
+// column: norm, random rotation, per-coordinate Lloyd-Max quantization).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "gtq_internal.h"
+
+using namespace gtq;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#define LOG2E_F 1.4426950408889634f
+#define LN2_F 0.6931471805599453f
+
+namespace {
+
+gtq_status hip_fail(hipError_t e, const char* what) {
+  return fail(GTQ_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ============================================================================
+// Append: per token and KV head, for each key group and for the value vector:
+//   nu = ||x|| (fp64 sum of squares, stored fp32), z = sqrt(d) * Pi * x / nu,
+//   code_i = #{k : z_i >= t_k}; pack (TurboQuant diagram, "paper" column).
+// Chunk path: one wave handles the up to 8 consecutive slots that a prompt chunk
+// covers in one value block; the workgroup keeps the head's rotations (transposed)
+// in LDS.
+// ============================================================================
+
+constexpr int kAppendWaves = 2;
+
+struct AppendArgs {
+  const DevHead* heads;  // this layer's heads [n_kv]
+  const float* rot;
+  const DevCodebook* cb;
+  uint32_t* k_codes;
+  float* k_norms;
+  uint32_t* v_codes;
+  float* v_norms;
+  const float* k;
+  const float* v;
+  const int32_t* seq_idx;
+  const int64_t* slot;
+  unsigned long long* overflow;
+  int64_t capacity;
+  int64_t n_tok;
+  int64_t n_items;
+  int64_t pos0;
+  int32_t seq;
+  int32_t batch;
+  int32_t n_kv;
+  int32_t k_words;
+  int32_t v_bits;
+  int32_t krot_lds;  // floats reserved for K rotations in LDS
+};
+
+struct AppendWaveLds {
+  float xk[kD][8];       // key coordinates in record order, [position][token]
+  float xv[kD][8];       // value coordinates, [coordinate][token]
+  float scale[8][5];     // sqrt(d)/nu per token and vector (4 = value)
+  float nu[8][5];
+  uint32_t krec[8][16];  // packed key records
+  uint32_t vblk[128];    // packed value block words
+  uint32_t vmask[128];   // bits of the value block written by this item
+};
+
+__device__ inline int quantize(float z, const float* thr, int n_thr) {
+  int c = 0;
+  for (int k = 0; k < n_thr; ++k) c += (z >= thr[k]) ? 1 : 0;
+  return c;
+}
+
+__global__ void __launch_bounds__(64 * kAppendWaves) append_chunk_kernel(AppendArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* rotv_t = reinterpret_cast<float*>(smem);             // [j][i], 128 x 128
+  float* rotk_t = rotv_t + kD * kD;                            // per group [j][i]
+  AppendWaveLds* wl = reinterpret_cast<AppendWaveLds*>(rotk_t + a.krot_lds);
+
+  const int h = blockIdx.y;
+  const DevHead& hd = a.heads[h];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  AppendWaveLds& L = wl[wave];
+
+  // Stage the rotations transposed: rot_t[j*d + i] = Pi[i][j].
+  {
+    const float* pv = a.rot + hd.vrot_off;
+    for (int e = tid; e < kD * kD; e += blockDim.x) {
+      const int i = e >> 7, j = e & 127;
+      rotv_t[j * kD + i] = pv[e];
+    }
+    int base = 0;
+    for (int g = 0; g < hd.n_groups; ++g) {
+      const int d = hd.dim[g];
+      const float* pk = a.rot + hd.krot_off[g];
+      for (int e = tid; e < d * d; e += blockDim.x) {
+        const int i = e / d, j = e - i * d;
+        rotk_t[base + j * d + i] = pk[e];
+      }
+      base += d * d;
+    }
+  }
+  __syncthreads();
+
+  const int vb = a.v_bits;
+  const int kw = a.k_words;
+  // lane's pair of key record positions (2*lane, 2*lane+1): group, index in group
+  const int p0 = 2 * lane;
+  int kg = 0;
+  for (int g = 1; g < hd.n_groups; ++g)
+    if (p0 >= hd.pos_off[g]) kg = g;
+  const int kd = hd.dim[kg];
+  const int ki = p0 - hd.pos_off[kg];
+  int krot_base = 0;
+  for (int g = 0; g < kg; ++g) krot_base += hd.dim[g] * hd.dim[g];
+  const int kb = hd.rate[kg];
+  const float* kthr = a.cb->t[kb];
+  const float* vthr = a.cb->t[vb];
+
+  for (int64_t item = (int64_t)blockIdx.x * kAppendWaves + wave; item < a.n_items;
+       item += (int64_t)gridDim.x * kAppendWaves) {
+    // item = the part of value block (pos0/8 + item) that the chunk covers
+    const int64_t blk = a.pos0 / GTQ_VBLOCK + item;
+    const int64_t lo = max(a.pos0, blk * GTQ_VBLOCK);
+    const int64_t hi = min(a.pos0 + a.n_tok, (blk + 1) * GTQ_VBLOCK);
+    const int64_t s_first = lo;
+    const int nt = (int)(hi - lo);
+    const int64_t tok_first = lo - a.pos0;
+    const int seq = a.seq;
+    const int j0 = (int)(s_first & (GTQ_VBLOCK - 1));
+    const size_t sh = (size_t)seq * a.n_kv + h;
+
+    // -- stage inputs (record order for keys), zero the pack buffers
+    for (int t = 0; t < 8; ++t) {
+      float xk0 = 0.f, xk1 = 0.f, xv0 = 0.f, xv1 = 0.f;
+      if (t < nt) {
+        const size_t row = ((size_t)(tok_first + t) * a.n_kv + h) * kD;
+        xk0 = a.k[row + hd.coord[p0]];
+        xk1 = a.k[row + hd.coord[p0 + 1]];
+        const float2 vv = *reinterpret_cast<const float2*>(a.v + row + p0);
+        xv0 = vv.x;
+        xv1 = vv.y;
+      }
+      L.xk[p0][t] = xk0;
+      L.xk[p0 + 1][t] = xk1;
+      L.xv[p0][t] = xv0;
+      L.xv[p0 + 1][t] = xv1;
+    }
+    for (int e = lane; e < 8 * 16; e += 64) (&L.krec[0][0])[e] = 0u;
+    for (int e = lane; e < 128; e += 64) {
+      L.vblk[e] = 0u;
+      L.vmask[e] = 0u;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // -- norms: one lane per (token, vector), fp64 sum of squares
+    if (lane < 40) {
+      const int t = lane / 5, vec = lane - 5 * (lane / 5);
+      if (t < nt && (vec == 4 || vec < hd.n_groups)) {
+        double s = 0.0;
+        int d;
+        if (vec == 4) {
+          d = kD;
+          for (int c = 0; c < kD; ++c) {
+            const double x = L.xv[c][t];
+            s = fma(x, x, s);
+          }
+        } else {
+          d = hd.dim[vec];
+          const int off = hd.pos_off[vec];
+          for (int c = 0; c < d; ++c) {
+            const double x = L.xk[off + c][t];
+            s = fma(x, x, s);
+          }
+        }
+        const double nu = sqrt(s);
+        L.nu[t][vec] = (float)nu;
+        L.scale[t][vec] = nu > 0.0 ? (float)(sqrt((double)d) / nu) : 0.f;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // -- key rotation: this lane's two outputs of its group, for all 8 tokens
+    {
+      float acc0[8], acc1[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc0[t] = acc1[t] = 0.f;
+      const float* rt = rotk_t + krot_base + ki;
+      const int xoff = hd.pos_off[kg];
+      for (int j = 0; j < kd; ++j) {
+        const float2 r = *reinterpret_cast<const float2*>(rt + j * kd);
+        const float4 xa = *reinterpret_cast<const float4*>(&L.xk[xoff + j][0]);
+        const float4 xb = *reinterpret_cast<const float4*>(&L.xk[xoff + j][4]);
+        const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          acc0[t] = fmaf(r.x, x[t], acc0[t]);
+          acc1[t] = fmaf(r.y, x[t], acc1[t]);
+        }
+      }
+      const int nthr = (1 << kb) - 1;
+      const int bitpos = hd.bit_off[kg] + ki * kb;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t < nt) {
+          const float sc = L.scale[t][kg];
+          const uint32_t c0 = quantize(acc0[t] * sc, kthr, nthr);
+          const uint32_t c1 = quantize(acc1[t] * sc, kthr, nthr);
+          const uint64_t f = (uint64_t)(c0 | (c1 << kb)) << (bitpos & 31);
+          atomicOr(&L.krec[t][bitpos >> 5], (uint32_t)f);
+          if ((f >> 32) != 0) atomicOr(&L.krec[t][(bitpos >> 5) + 1], (uint32_t)(f >> 32));
+        }
+      }
+    }
+    // -- value rotation and packing into the 8-token block
+    {
+      float acc0[8], acc1[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc0[t] = acc1[t] = 0.f;
+      const float* rt = rotv_t + p0;
+      for (int j = 0; j < kD; ++j) {
+        const float2 r = *reinterpret_cast<const float2*>(rt + j * kD);
+        const float4 xa = *reinterpret_cast<const float4*>(&L.xv[j][0]);
+        const float4 xb = *reinterpret_cast<const float4*>(&L.xv[j][4]);
+        const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          acc0[t] = fmaf(r.x, x[t], acc0[t]);
+          acc1[t] = fmaf(r.y, x[t], acc1[t]);
+        }
+      }
+      const int nthr = (1 << vb) - 1;
+      const uint32_t ones = (1u << vb) - 1u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t < nt) {
+          const float sc = L.scale[t][4];
+          const uint32_t c[2] = {(uint32_t)quantize(acc0[t] * sc, vthr, nthr),
+                                 (uint32_t)quantize(acc1[t] * sc, vthr, nthr)};
+          const int j = j0 + t;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int bit = 8 * vb * (p0 + u) + vb * j;
+            const uint64_t f = (uint64_t)c[u] << (bit & 31);
+            const uint64_t m = (uint64_t)ones << (bit & 31);
+            atomicOr(&L.vblk[bit >> 5], (uint32_t)f);
+            atomicOr(&L.vmask[bit >> 5], (uint32_t)m);
+            if ((m >> 32) != 0) {
+              atomicOr(&L.vblk[(bit >> 5) + 1], (uint32_t)(f >> 32));
+              atomicOr(&L.vmask[(bit >> 5) + 1], (uint32_t)(m >> 32));
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // -- stores
+    for (int e = lane; e < nt * kw; e += 64) {
+      const int t = e / kw, w = e - t * kw;
+      a.k_codes[(sh * a.capacity + s_first + t) * kw + w] = L.krec[t][w];
+    }
+    if (lane < nt * kNS) {
+      const int t = lane / kNS, g = lane - kNS * (lane / kNS);
+      a.k_norms[(sh * a.capacity + s_first + t) * kNS + g] = g < hd.n_groups ? L.nu[t][g] : 0.f;
+    }
+    if (lane < nt) a.v_norms[sh * a.capacity + s_first + lane] = L.nu[lane][4];
+    {
+      const int vw = 32 * vb;
+      uint32_t* blk = a.v_codes + (sh * (size_t)(a.capacity / GTQ_VBLOCK) +
+                                   (size_t)(s_first / GTQ_VBLOCK)) * vw;
+      if (nt == GTQ_VBLOCK) {
+        for (int w = lane; w < vw; w += 64) blk[w] = L.vblk[w];
+      } else {
+        for (int w = lane; w < vw; w += 64) {
+          const uint32_t m = L.vmask[w];
+          if (m) {
+            atomicAnd(blk + w, ~m);
+            atomicOr(blk + w, L.vblk[w] & m);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ============================================================================
+// Append of scattered single tokens (decode steps): one 1024-thread workgroup per
+// (token, KV head); each of the 256 outputs (128 key record positions, 128 value
+// coordinates) is a dot product split over 4 thread groups so that the rotation rows
+// are read with many loads in flight. Norms: fp64 sums of squares, reduced by a
+// fixed shuffle tree.
+// ============================================================================
+
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
+  __shared__ float xs[2 * kD];          // key (record order) then value coordinates
+  __shared__ float red[4][2 * kD];
+  __shared__ float nu_s[5], sc_s[5];
+  __shared__ uint32_t krec[16];
+  __shared__ uint32_t vblk[128], vmask[128];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int64_t tok = blockIdx.x;
+  const DevHead& hd = a.heads[h];
+  const int seq = a.seq_idx[tok];
+  const int64_t slot = a.slot[tok];
+  if (seq < 0 || seq >= a.batch || slot < 0 || slot >= a.capacity) {
+    if (tid == 0 && h == 0) atomicAdd(a.overflow, 1ull);  // once per token
+    return;
+  }
+  const size_t row = ((size_t)tok * a.n_kv + h) * kD;
+  if (tid < kD) xs[tid] = a.k[row + hd.coord[tid]];
+  else if (tid < 2 * kD) xs[tid] = a.v[row + tid - kD];
+  if (tid < 16) krec[tid] = 0u;
+  if (tid < 128) {
+    vblk[tid] = 0u;
+    vmask[tid] = 0u;
+  }
+  __syncthreads();
+  // norms: wave 0 the key groups, wave 1 the value vector
+  if (tid < 64) {
+    const double x0 = xs[2 * tid], x1 = xs[2 * tid + 1];
+    const double sq = x0 * x0 + x1 * x1;
+    int mg = 0;
+    for (int g = 1; g < hd.n_groups; ++g)
+      if (2 * tid >= hd.pos_off[g]) mg = g;
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) {
+      const double s = wave_sum_f64(mg == g ? sq : 0.0);
+      if (tid == 0 && g < hd.n_groups) {
+        const double nu = sqrt(s);
+        nu_s[g] = (float)nu;
+        sc_s[g] = nu > 0.0 ? (float)(sqrt((double)hd.dim[g]) / nu) : 0.f;
+      }
+    }
+  } else if (tid < 128) {
+    const int l = tid - 64;
+    const double x0 = xs[kD + 2 * l], x1 = xs[kD + 2 * l + 1];
+    const double s = wave_sum_f64(x0 * x0 + x1 * x1);
+    if (l == 0) {
+      const double nu = sqrt(s);
+      nu_s[4] = (float)nu;
+      sc_s[4] = nu > 0.0 ? (float)(sqrt((double)kD) / nu) : 0.f;
+    }
+  }
+  // rotation partial sums
+  {
+    const int o = tid & 255, qq = tid >> 8;
+    float acc = 0.f;
+    if (o < kD) {
+      int g = 0;
+      for (int gg = 1; gg < hd.n_groups; ++gg)
+        if (o >= hd.pos_off[gg]) g = gg;
+      const int d = hd.dim[g], i = o - hd.pos_off[g];
+      const int lo = (d * qq) >> 2, hi = (d * (qq + 1)) >> 2;
+      const float* pr = a.rot + hd.krot_off[g] + (size_t)i * d;
+      const float* x = xs + hd.pos_off[g];
+#pragma unroll 8
+      for (int j = lo; j < hi; ++j) acc = fmaf(pr[j], x[j], acc);
+    } else {
+      const int i = o - kD;
+      const float4* pr = reinterpret_cast<const float4*>(a.rot + hd.vrot_off + (size_t)i * kD + 32 * qq);
+      const float* x = xs + kD + 32 * qq;
+#pragma unroll
+      for (int j4 = 0; j4 < 8; ++j4) {
+        const float4 w = pr[j4];
+        acc = fmaf(w.x, x[4 * j4], acc);
+        acc = fmaf(w.y, x[4 * j4 + 1], acc);
+        acc = fmaf(w.z, x[4 * j4 + 2], acc);
+        acc = fmaf(w.w, x[4 * j4 + 3], acc);
+      }
+    }
+    red[qq][o] = acc;
+  }
+  __syncthreads();
+  const int vb = a.v_bits;
+  const int j0 = (int)(slot & (GTQ_VBLOCK - 1));
+  if (tid < 2 * kD) {
+    const float z0 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    if (tid < kD) {
+      int g = 0;
+      for (int gg = 1; gg < hd.n_groups; ++gg)
+        if (tid >= hd.pos_off[gg]) g = gg;
+      const int b = hd.rate[g];
+      const uint32_t c = quantize(z0 * sc_s[g], a.cb->t[b], (1 << b) - 1);
+      const int bit = hd.bit_off[g] + (tid - hd.pos_off[g]) * b;
+      const uint64_t f = (uint64_t)c << (bit & 31);
+      atomicOr(&krec[bit >> 5], (uint32_t)f);
+      if (f >> 32) atomicOr(&krec[(bit >> 5) + 1], (uint32_t)(f >> 32));
+    } else {
+      const int cidx = tid - kD;
+      const uint32_t c = quantize(z0 * sc_s[4], a.cb->t[vb], (1 << vb) - 1);
+      const int bit = 8 * vb * cidx + vb * j0;
+      const uint64_t f = (uint64_t)c << (bit & 31);
+      const uint64_t m = (uint64_t)((1u << vb) - 1u) << (bit & 31);
+      atomicOr(&vblk[bit >> 5], (uint32_t)f);
+      atomicOr(&vmask[bit >> 5], (uint32_t)m);
+      if (m >> 32) {
+        atomicOr(&vblk[(bit >> 5) + 1], (uint32_t)(f >> 32));
+        atomicOr(&vmask[(bit >> 5) + 1], (uint32_t)(m >> 32));
+      }
+    }
+  }
+  __syncthreads();
+  const size_t sh = (size_t)seq * a.n_kv + h;
+  if (tid < a.k_words) a.k_codes[(sh * a.capacity + slot) * a.k_words + tid] = krec[tid];
+  if (tid >= 64 && tid < 64 + kNS) {
+    const int g = tid - 64;
+    a.k_norms[(sh * a.capacity + slot) * kNS + g] = g < hd.n_groups ? nu_s[g] : 0.f;
+  }
+  if (tid == 128) a.v_norms[sh * a.capacity + slot] = nu_s[4];
+  if (tid >= 256 && tid < 256 + 32 * vb) {
+    const int w = tid - 256;
+    const uint32_t m = vmask[w];
+    if (m) {
+      uint32_t* blk = a.v_codes + (sh * (size_t)(a.capacity / GTQ_VBLOCK) + (size_t)(slot / GTQ_VBLOCK)) * (32 * vb);
+      atomicAnd(blk + w, ~m);
+      atomicOr(blk + w, vblk[w] & m);
+    }
+  }
+}
+
+// ============================================================================
+// Split-K attention over the packed cache, one launch per call.
+//
+// A workgroup (4 waves) takes one row tile (up to 8 query rows of one sequence and
+// KV head) and one chunk of cached tokens.
+// Prologue: r_g = Pi_g q_g for each key group of each row, scaled by
+//   scale / sqrt(d_g) * log2(e), split into a binary16 high part and a binary16
+//   remainder (together ~22 bits), stored as the QK B operand.
+// Per 32-token block and wave:
+//   QK: MFMA 16x16x32 f16, A = decoded key codes (16 tokens x 32 coordinates of one
+//       group; the codebook values are exact binary16), B = rotated queries, columns
+//       0..7 = high parts of rows 0..7, columns 8..15 = low parts of rows 7..0.
+//       One accumulator per key group; the per-token group norms are applied after
+//       the product, then a row-mirror DPP adds the high and low halves.
+//   online softmax (base 2) per row, with lane-local partial sums;
+//   PV: MFMA with A = p * nu_V split in high/low parts (rows as above) and
+//       B = decoded value codes (8 tokens x 16 coordinates), accumulating in the
+//       value rotation's basis.
+// Epilogue: the 4 waves merge in LDS and write one (m, l, acc[128]) partial per row;
+// the last workgroup of a tile to finish (device-scope counter in the workspace,
+// reset by that workgroup) merges the tile's partials by log-sum-exp and applies
+// o = Pi_V^T o_rot / sqrt(128).
+// ============================================================================
+
+constexpr int kWaves = 4;
+
+struct AttnArgs {
+  const DevHead* heads;
+  const float* rot;
+  const DevCodebook* cb;
+  const uint32_t* k_codes;
+  const float* k_norms;
+  const uint32_t* v_codes;
+  const float* v_norms;
+  const float* q;          // [rows][128]
+  float* out;              // [rows][128]
+  float* logits;           // decode only, optional
+  const int32_t* seq_len;  // decode
+  float* partials;         // [rows][n_chunks][130]
+  uint32_t* counters;      // [n_tiles]
+  int64_t capacity;
+  int64_t logits_ld;
+  int64_t pos0;            // prefill
+  int32_t n_kv, n_q, g, k_words;
+  int32_t tiles_per_kv;    // ceil(rows per KV head / 8)
+  int32_t prefill;         // 0 decode, 1 prefill
+  int32_t seq;             // prefill sequence
+  int32_t n_tok;           // prefill: tokens in chunk
+  int32_t chunk;           // tokens per split (multiple of 32)
+  int32_t n_chunks;
+  int32_t max_len;         // decode clamp
+  float qscale;            // softmax scale * log2(e)
+};
+
+struct AttnLds {
+  uint32_t lut1[256][4];  // 1-bit: byte -> 8 binary16 centroids
+  uint32_t lut2[256][2];  // 2-bit: byte -> 4
+  uint32_t lut3[64];      // 3-bit: 6 bits -> 2
+  uint32_t lut4[256];     // 4-bit: byte -> 2
+  uint4 qb[kMaxKB][4][16];            // B operand of QK per K-block / lane
+  uint32_t ktile[kWaves][kBlk * 16 + 16];
+  float kn[kWaves][kBlk * kNS];
+  float om[kWaves][8];
+  float ol[kWaves][8];
+  float oacc[kWaves][8][kD];          // also holds the query rows and the merged rows
+  int32_t row_id[8];
+  int32_t row_len[8];
+  int32_t last;
+};
+
+__device__ inline uint32_t pack2h(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__device__ inline float dpp_row_mirror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+}
+
+union H8 {
+  half8 h;
+  uint32_t u[4];
+  uint4 v;
+};
+
+template <int RATE>
+__device__ inline half8 dequant8(const AttnLds& S, uint32_t F) {
+  H8 r;
+  if (RATE == 1) {
+    r.v = *reinterpret_cast<const uint4*>(S.lut1[F & 0xFF]);
+  } else if (RATE == 2) {
+    const uint2 a = *reinterpret_cast<const uint2*>(S.lut2[F & 0xFF]);
+    const uint2 b = *reinterpret_cast<const uint2*>(S.lut2[(F >> 8) & 0xFF]);
+    r.u[0] = a.x;
+    r.u[1] = a.y;
+    r.u[2] = b.x;
+    r.u[3] = b.y;
+  } else if (RATE == 3) {
+    r.u[0] = S.lut3[F & 63];
+    r.u[1] = S.lut3[(F >> 6) & 63];
+    r.u[2] = S.lut3[(F >> 12) & 63];
+    r.u[3] = S.lut3[(F >> 18) & 63];
+  } else {
+    r.u[0] = S.lut4[F & 0xFF];
+    r.u[1] = S.lut4[(F >> 8) & 0xFF];
+    r.u[2] = S.lut4[(F >> 16) & 0xFF];
+    r.u[3] = S.lut4[(F >> 24) & 0xFF];
+  }
+  return r.h;
+}
+
+template <int RATE>
+__device__ inline void qk_group(const AttnLds& S, const uint32_t* kt, int kw, int kb0, int nkb,
+                                const int32_t* kb_bit, int q, int n, floatx4& d0, floatx4& d1) {
+  // A-row n of the two 16-token halves holds tokens 8(n/4) + n%4 and that + 4
+  const int tau0 = 8 * (n >> 2) + (n & 3);
+  const int tau1 = tau0 + 4;
+  const uint32_t* r0 = kt + tau0 * kw;
+  const uint32_t* r1 = kt + tau1 * kw;
+  for (int i = 0; i < nkb; ++i) {
+    const int kbi = kb0 + i;
+    H8 qbv;
+    qbv.v = S.qb[kbi][q][n];
+    const int bit = kb_bit[kbi] + 8 * q * RATE;
+    const int w = bit >> 5, s = bit & 31;
+    const uint32_t f0 = __builtin_amdgcn_alignbit(r0[w + 1], r0[w], s);
+    const uint32_t f1 = __builtin_amdgcn_alignbit(r1[w + 1], r1[w], s);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<RATE>(S, f0), qbv.h, d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<RATE>(S, f1), qbv.h, d1, 0, 0, 0);
+  }
+}
+
+template <int VB>
+__device__ inline uint32_t vfield(const uint32_t (&vw)[2 * VB], int t) {
+  if (VB == 1) return (vw[t >> 2] >> (8 * (t & 3))) & 0xFFu;
+  if (VB == 2) return (vw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+  if (VB == 4) return vw[t];
+  // VB == 3: 24 bits at bit 24 t
+  const int bit = 24 * t, w = bit >> 5, s = bit & 31;
+  if (s + 24 <= 32) return vw[w] >> s;
+  return __builtin_amdgcn_alignbit(vw[w + 1], vw[w], s);
+}
+
+constexpr int kPS = 132;          // partial record: m, l, 2 pad, acc[128] (16-byte aligned acc)
+constexpr int kMaxChunks = 256;   // splits per row (bounded by the merge's LDS weights)
+
+struct BlockRegs {
+  uint32_t kr[8];   // key codes: words lane + 64 i of the 32-token tile
+  float2 kn;        // key norms: floats 2 lane, 2 lane + 1 of the tile
+  uint32_t vw[8];   // value codes of 8 tokens x coordinates 8n..8n+7 (2 VB words)
+  float4 vn0, vn1;  // value norms of tokens 8q..8q+7
+};
+
+template <int VB>
+__device__ inline void load_block(BlockRegs& B, const uint32_t* kc, const float* knp, const uint32_t* vc,
+                                  const float* vnp, int t0, int kw, int lane, int q, int n) {
+  const uint32_t* ks = kc + (size_t)t0 * kw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (lane + 64 * i < kBlk * kw) B.kr[i] = ks[lane + 64 * i];
+  B.kn = *reinterpret_cast<const float2*>(knp + (size_t)t0 * kNS + 2 * lane);
+  const uint32_t* src = vc + ((size_t)(t0 / GTQ_VBLOCK) + q) * (32 * VB) + n * (2 * VB);
+  if (VB == 2) {
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    B.vw[0] = x.x; B.vw[1] = x.y; B.vw[2] = x.z; B.vw[3] = x.w;
+  } else if (VB == 4) {
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    const uint4 y = *reinterpret_cast<const uint4*>(src + 4);
+    B.vw[0] = x.x; B.vw[1] = x.y; B.vw[2] = x.z; B.vw[3] = x.w;
+    B.vw[4] = y.x; B.vw[5] = y.y; B.vw[6] = y.z; B.vw[7] = y.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2 * VB; ++i) B.vw[i] = src[i];
+  }
+  B.vn0 = *reinterpret_cast<const float4*>(vnp + t0 + 8 * q);
+  B.vn1 = *reinterpret_cast<const float4*>(vnp + t0 + 8 * q + 4);
+}
+
+template <int VB>
+__global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
+  extern __shared__ __align__(16) float rotk_t[];  // this head's key rotations, [g][j][i]
+  __shared__ AttnLds S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, n = lane & 15;
+  const int chunk_idx = blockIdx.x;
+  const int tile = blockIdx.y;
+
+  // ---- tile -> (sequence, KV head, rows)
+  int seq, h, tr;
+  if (a.prefill) {
+    h = tile / a.tiles_per_kv;
+    tr = tile - h * a.tiles_per_kv;
+    seq = a.seq;
+  } else {
+    seq = tile / (a.n_kv * a.tiles_per_kv);
+    const int rem = tile - seq * a.n_kv * a.tiles_per_kv;
+    h = rem / a.tiles_per_kv;
+    tr = rem - h * a.tiles_per_kv;
+  }
+  if (tid < 8) {
+    const int f = tr * 8 + tid;
+    int id = -1, len = 0;
+    if (a.prefill) {
+      if (f < a.n_tok * a.g) {
+        const int t = f / a.g;
+        id = t * a.n_q + h * a.g + (f - t * a.g);
+        len = (int)(a.pos0 + t + 1);
+      }
+    } else if (f < a.g) {
+      id = seq * a.n_q + h * a.g + f;
+      len = min(max(a.seq_len[seq], 0), a.max_len);
+    }
+    S.row_id[tid] = id;
+    S.row_len[tid] = len;
+  }
+  __syncthreads();
+  int tile_len = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) tile_len = max(tile_len, S.row_len[r]);
+  const int c0 = chunk_idx * a.chunk;
+  if (c0 >= tile_len) {
+    // nothing cached for this chunk; an all-empty tile still owes zero outputs
+    if (tile_len == 0 && chunk_idx == 0) {
+      for (int e = tid; e < 8 * kD; e += 256) {
+        const int id = S.row_id[e >> 7];
+        if (id >= 0) a.out[(size_t)id * kD + (e & 127)] = 0.f;
+      }
+    }
+    return;
+  }
+  const DevHead& hd = a.heads[h];
+  const int c1 = min(c0 + a.chunk, tile_len);
+  const size_t sh = (size_t)seq * a.n_kv + h;
+  const int kw = a.k_words;
+  const uint32_t* kc = a.k_codes + sh * a.capacity * kw;
+  const float* knp = a.k_norms + sh * a.capacity * kNS;
+  const uint32_t* vc = a.v_codes + sh * (a.capacity / GTQ_VBLOCK) * (32 * VB);
+  const float* vnp = a.v_norms + sh * a.capacity;
+
+  // ---- first block of this wave: loads issued before the prologue
+  BlockRegs cur;
+  int t0 = c0 + kBlk * wave;
+  if (t0 < c1) load_block<VB>(cur, kc, knp, vc, vnp, t0, kw, lane, q, n);
+
+  float(*qrow)[kD] = S.oacc[0];  // 8 query rows, until the main loop starts
+  // ---- prologue: key rotations (transposed) and query rows into LDS, decode tables
+  {
+    const float4* src = reinterpret_cast<const float4*>(a.rot + hd.krot_off[0]);
+    const int nf4 = hd.krot_floats >> 2;
+    for (int e4 = tid; e4 < nf4; e4 += 256) {
+      const float4 x = src[e4];
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int e = 4 * e4 + u, base = 0, g = 0;
+#pragma unroll
+        for (int gg = 0; gg < kMaxGroups - 1; ++gg) {
+          const int sz = hd.dim[gg] * hd.dim[gg];
+          if (g == gg && gg < hd.n_groups - 1 && e >= base + sz) {  // scan forward from group 0
+            base += sz;
+            g = gg + 1;
+          }
+        }
+        const int d = hd.dim[g], idx = e - base;
+        const int i = idx / d, j = idx - i * d;
+        rotk_t[base + j * d + i] = xs[u];
+      }
+    }
+    for (int e = tid; e < 8 * kD; e += 256) {
+      const int id = S.row_id[e >> 7];
+      qrow[e >> 7][e & 127] = id >= 0 ? a.q[(size_t)id * kD + (e & 127)] : 0.f;
+    }
+    const float* c1b = a.cb->c[1];
+    const float* c2b = a.cb->c[2];
+    const float* c3b = a.cb->c[3];
+    const float* c4b = a.cb->c[4];
+    const int idx = tid;  // 256 threads, 256 entries
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      S.lut1[idx][k] = pack2h(c1b[(idx >> (2 * k)) & 1], c1b[(idx >> (2 * k + 1)) & 1]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      S.lut2[idx][k] = pack2h(c2b[(idx >> (4 * k)) & 3], c2b[(idx >> (4 * k + 2)) & 3]);
+    if (idx < 64) S.lut3[idx] = pack2h(c3b[idx & 7], c3b[(idx >> 3) & 7]);
+    S.lut4[idx] = pack2h(c4b[idx & 15], c4b[(idx >> 4) & 15]);
+    for (int e = tid; e < kMaxKB * 64; e += 256) (&S.qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  // ---- rotated queries into the QK B operand (column r: high part, 15-r: low part)
+  for (int e = tid; e < 8 * kD; e += 256) {
+    const int r = e >> 7, p = e & 127;
+    if (S.row_id[r] < 0) continue;
+    int g = 0, base = 0;
+#pragma unroll
+    for (int gg = 1; gg < kMaxGroups; ++gg)
+      if (gg < hd.n_groups && p >= hd.pos_off[gg]) g = gg;
+    for (int gg = 0; gg < g; ++gg) base += hd.dim[gg] * hd.dim[gg];
+    const int d = hd.dim[g], i = p - hd.pos_off[g];
+    const float* rt = rotk_t + base + i;
+    const uint8_t* co = hd.coord + hd.pos_off[g];
+    float acc = 0.f;
+    for (int j = 0; j < d; ++j) acc = fmaf(rt[j * d], qrow[r][co[j]], acc);
+    const float val = acc * (a.qscale / sqrtf((float)d));
+    const _Float16 hi = (_Float16)val;
+    const _Float16 lo = (_Float16)(val - (float)hi);
+    const int kp = hd.kp_off[g] + i;
+    _Float16* bh = reinterpret_cast<_Float16*>(&S.qb[kp >> 5][(kp >> 3) & 3][r]);
+    _Float16* bl = reinterpret_cast<_Float16*>(&S.qb[kp >> 5][(kp >> 3) & 3][15 - r]);
+    bh[kp & 7] = hi;
+    bl[kp & 7] = lo;
+  }
+  __syncthreads();
+
+  const int my_row = n < 8 ? n : 15 - n;
+  const int my_len = S.row_len[my_row];
+  uint32_t* kt = S.ktile[wave];
+  float* kn = S.kn[wave];
+
+  floatx4 oacc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) oacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (; t0 < c1; t0 += kBlk * kWaves) {
+    BlockRegs nxt;
+    const int tn = t0 + kBlk * kWaves;
+    if (tn < c1) load_block<VB>(nxt, kc, knp, vc, vnp, tn, kw, lane, q, n);
+    // ---- stage this block's key codes and norms in LDS
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (lane + 64 * i < kBlk * kw) kt[lane + 64 * i] = cur.kr[i];
+    kn[2 * lane] = cur.kn.x;
+    kn[2 * lane + 1] = cur.kn.y;
+    const float vn[8] = {cur.vn0.x, cur.vn0.y, cur.vn0.z, cur.vn0.w,
+                         cur.vn1.x, cur.vn1.y, cur.vn1.z, cur.vn1.w};
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- QK per key group
+    floatx4 dg[kMaxGroups][2];
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) dg[g][0] = dg[g][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    int kb0 = 0;
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) {
+      if (g < hd.n_groups) {
+        const int nk = hd.nkb_g[g];
+        switch (hd.rate[g]) {
+          case 1: qk_group<1>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, dg[g][0], dg[g][1]); break;
+          case 2: qk_group<2>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, dg[g][0], dg[g][1]); break;
+          case 3: qk_group<3>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, dg[g][0], dg[g][1]); break;
+          default: qk_group<4>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, dg[g][0], dg[g][1]); break;
+        }
+        kb0 += nk;
+      }
+    }
+    // ---- logits of tokens 8q + j (j = 4*half + e), column n
+    float lg[8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * hf + e;
+        const float4 nu = *reinterpret_cast<const float4*>(kn + (8 * q + j) * kNS);
+        float s = nu.x * dg[0][hf][e];
+        s = fmaf(nu.y, dg[1][hf][e], s);
+        s = fmaf(nu.z, dg[2][hf][e], s);
+        s = fmaf(nu.w, dg[3][hf][e], s);
+        lg[j] = s;
+      }
+    }
+    float mblk = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v = lg[j] + dpp_row_mirror(lg[j]);
+      const int pos = t0 + 8 * q + j;
+      if (pos >= my_len) v = -INFINITY;
+      lg[j] = v;
+      mblk = fmaxf(mblk, v);
+    }
+    if (a.logits && n < 8) {
+      const int id = S.row_id[my_row];
+      if (id >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pos = t0 + 8 * q + j;
+          if (pos < my_len) a.logits[(size_t)id * a.logits_ld + pos] = lg[j] * LN2_F;
+        }
+      }
+    }
+    mblk = fmaxf(mblk, __shfl_xor(mblk, 16));
+    mblk = fmaxf(mblk, __shfl_xor(mblk, 32));
+    const float m_new = fmaxf(m_run, mblk);
+    // rescale the running state when a row's maximum grows
+    const bool grow = m_new > m_run;
+    if (__any(grow)) {
+      const float f = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      l_run *= grow ? f : 1.f;
+      // accumulator rows 4q+e live in lanes with n == row: fetch their factors
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fe = __shfl(grow ? f : 1.f, 4 * q + e);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) oacc[t][e] *= fe;
+      }
+    }
+    m_run = m_new;
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    // ---- probabilities times value norms, split high/low by column
+    uint32_t pp[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float x[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = 2 * jj + u;
+        const float p = (lg[j] == -INFINITY) ? 0.f : exp2f(lg[j] - m_use);
+        l_run += p;
+        const float pv = (p == 0.f) ? 0.f : p * vn[j];
+        const float hi = (float)(_Float16)pv;
+        x[u] = n < 8 ? hi : pv - hi;
+      }
+      pp[jj] = pack2h(x[0], x[1]);
+    }
+    H8 pa;
+    pa.u[0] = pp[0];
+    pa.u[1] = pp[1];
+    pa.u[2] = pp[2];
+    pa.u[3] = pp[3];
+    // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
+    uint32_t vwc[2 * VB];
+#pragma unroll
+    for (int i = 0; i < 2 * VB; ++i) vwc[i] = cur.vw[i];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t F = vfield<VB>(vwc, t);
+      half8 vb;
+      if (VB == 1) vb = dequant8<1>(S, F);
+      else if (VB == 2) vb = dequant8<2>(S, F);
+      else if (VB == 3) vb = dequant8<3>(S, F);
+      else vb = dequant8<4>(S, F);
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, vb, oacc[t], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+    cur = nxt;
+  }
+
+  // ---- per-wave epilogue: rows 0..7 = high row + mirrored low row
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();  // the query rows in S.oacc[0] are no longer needed
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float partner = __shfl_xor(oacc[t][3 - e], 48);
+      if (q < 2) S.oacc[wave][4 * q + e][8 * n + t] = oacc[t][e] + partner;
+    }
+  }
+  if (q == 0 && n < 8) {
+    S.om[wave][n] = m_run;
+    S.ol[wave][n] = l_run;
+  }
+  __syncthreads();
+  // ---- merge the 4 waves, write one partial per row
+  for (int e = tid; e < 8 * kD; e += 256) {
+    const int r = e >> 7, c = e & 127;
+    const int id = S.row_id[r];
+    if (id < 0) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.om[w][r]);
+    float acc = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float s = exp2f(S.om[w][r] - M);
+        acc = fmaf(s, S.oacc[w][r][c], acc);
+        l = fmaf(s, S.ol[w][r], l);
+      }
+    }
+    float* dst = a.partials + ((size_t)id * a.n_chunks + chunk_idx) * kPS;
+    dst[4 + c] = acc;
+    if (c == 0) {
+      dst[0] = M;
+      dst[1] = l;
+    }
+  }
+  // ---- the last workgroup of this tile merges all chunks
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const uint32_t arrivals = (uint32_t)((tile_len + a.chunk - 1) / a.chunk);
+    const uint32_t old = atomicAdd(a.counters + tile, 1u);
+    const int last = (old == arrivals - 1);
+    if (last) a.counters[tile] = 0u;  // every arrival has counted: reset for the next call
+    S.last = last;
+  }
+  __syncthreads();
+  if (!S.last) return;
+  __threadfence();
+  float* wgt = &S.oacc[0][0][0];                               // [8][kMaxChunks] split weights
+  float4* red = reinterpret_cast<float4*>(&S.oacc[2][0][0]);   // [8 slices][32]
+  float(*orot)[kD] = S.oacc[3];                                // merged rows (rotated basis)
+  // phase A: per row, 32 threads: maximum and weights exp2(m_k - M), sum of l
+  {
+    const int r = tid >> 5, j = tid & 31;
+    const int id = S.row_id[r];
+    const int nv = id >= 0 ? (S.row_len[r] + a.chunk - 1) / a.chunk : 0;
+    const float* pp = a.partials + (size_t)(id >= 0 ? id : 0) * a.n_chunks * kPS;
+    float mk[kMaxChunks / 32], lk[kMaxChunks / 32];
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMaxChunks / 32; ++u) {
+      const int k = j + 32 * u;
+      mk[u] = -INFINITY;
+      lk[u] = 0.f;
+      if (k < nv) {
+        mk[u] = pp[(size_t)k * kPS];
+        lk[u] = pp[(size_t)k * kPS + 1];
+      }
+      M = fmaxf(M, mk[u]);
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
+    float L = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMaxChunks / 32; ++u) {
+      const int k = j + 32 * u;
+      const float w = (mk[u] == -INFINITY) ? 0.f : exp2f(mk[u] - M);
+      if (k < kMaxChunks) wgt[r * kMaxChunks + k] = w;
+      L = fmaf(w, lk[u], L);
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o, 32);
+    if (j == 0) S.ol[0][r] = L;
+  }
+  __syncthreads();
+  // phase B: acc[r][c] = sum_k w_k acc_k[c]; thread = (float4 column c4, k slice)
+  {
+    const int c4 = tid & 31, ks = tid >> 5;
+    for (int r = 0; r < 8; ++r) {
+      const int id = S.row_id[r];
+      if (id < 0) continue;  // uniform across the workgroup
+      const int nv = (S.row_len[r] + a.chunk - 1) / a.chunk;
+      const float* pp = a.partials + (size_t)id * a.n_chunks * kPS + 4 + 4 * c4;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+      for (int k = ks; k < nv; k += 8) {
+        const float w = wgt[r * kMaxChunks + k];
+        const float4 x = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS);
+        acc.x = fmaf(w, x.x, acc.x);
+        acc.y = fmaf(w, x.y, acc.y);
+        acc.z = fmaf(w, x.z, acc.z);
+        acc.w = fmaf(w, x.w, acc.w);
+      }
+      red[ks * 32 + c4] = acc;
+      __syncthreads();
+      if (tid < 32) {
+        float4 s = red[tid];
+#pragma unroll
+        for (int k2 = 1; k2 < 8; ++k2) {
+          const float4 y = red[k2 * 32 + tid];
+          s.x += y.x;
+          s.y += y.y;
+          s.z += y.z;
+          s.w += y.w;
+        }
+        // value reconstruction is nu * Pi_V^T C[code] / sqrt(128)
+        const float L = S.ol[0][r];
+        const float f = L > 0.f ? 0.08838834764831845f / L : 0.f;
+        orot[r][4 * tid] = s.x * f;
+        orot[r][4 * tid + 1] = s.y * f;
+        orot[r][4 * tid + 2] = s.z * f;
+        orot[r][4 * tid + 3] = s.w * f;
+      }
+      __syncthreads();
+    }
+  }
+  // o = Pi_V^T o_rot: thread i reads row i of Pi_V^T (column i of Pi_V) contiguously
+  {
+    const int i = tid & 127, r0 = (tid >> 7) * 4;
+    const float4* pt = reinterpret_cast<const float4*>(a.rot + hd.vrot_t_off + (size_t)i * kD);
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int c4 = 0; c4 < kD / 4; ++c4) {
+      const float4 w = pt[c4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float4 x = *reinterpret_cast<const float4*>(&orot[r0 + rr][4 * c4]);
+        o[rr] = fmaf(w.x, x.x, o[rr]);
+        o[rr] = fmaf(w.y, x.y, o[rr]);
+        o[rr] = fmaf(w.z, x.z, o[rr]);
+        o[rr] = fmaf(w.w, x.w, o[rr]);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int id = S.row_id[r0 + rr];
+      if (id >= 0) a.out[(size_t)id * kD + i] = o[rr];
+    }
+  }
+}
+
+// ============================================================================
+// host helpers
+// ============================================================================
+
+bool check_device_plan(const gtq_plan* p, const char* fn, gtq_status* st) {
+  if (!p) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": plan is NULL");
+    return false;
+  }
+  if (!p->d_heads) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": plan was created host-only");
+    return false;
+  }
+  return true;
+}
+
+bool check_cache(const gtq_plan* p, const gtq_cache_view* c, const char* fn, gtq_status* st) {
+  if (!c || !c->k_codes || !c->k_norms || !c->v_codes || !c->v_norms) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": cache view or one of its buffers is NULL");
+    return false;
+  }
+  if (c->batch < 1 || c->capacity < 1 || c->capacity % GTQ_SEQ_ALIGN) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": cache batch >= 1 and capacity a positive multiple of 32");
+    return false;
+  }
+  (void)p;
+  return true;
+}
+
+// rotations (V: 128^2, K: at most 128^2 floats) plus the per-wave staging
+constexpr int kAppendLdsMax = 2 * kD * kD * 4 + kAppendWaves * (int)sizeof(AppendWaveLds);
+
+int append_lds_bytes(const gtq_plan* p, int layer, int* krot_lds) {
+  int mx = 0;
+  for (int h = 0; h < p->n_kv; ++h) mx = std::max(mx, p->heads[(size_t)layer * p->n_kv + h].krot_floats);
+  mx = (mx + 3) & ~3;
+  *krot_lds = mx;
+  return (kD * kD + mx) * 4 + kAppendWaves * (int)sizeof(AppendWaveLds);
+}
+
+gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* k,
+                         const float* v, const int32_t* seq_idx, const int64_t* slot, int32_t seq,
+                         int64_t pos0, int64_t n_tok, bool chunk, hipStream_t stream) {
+  AppendArgs a{};
+  a.heads = p->d_heads + (size_t)layer * p->n_kv;
+  a.rot = p->d_rot;
+  a.cb = p->d_cb;
+  a.k_codes = c->k_codes;
+  a.k_norms = c->k_norms;
+  a.v_codes = c->v_codes;
+  a.v_norms = c->v_norms;
+  a.k = k;
+  a.v = v;
+  a.seq_idx = seq_idx;
+  a.slot = slot;
+  a.overflow = p->d_overflow;
+  a.capacity = c->capacity;
+  a.n_tok = n_tok;
+  a.pos0 = pos0;
+  a.seq = seq;
+  a.batch = c->batch;
+  a.n_kv = p->n_kv;
+  a.k_words = p->k_words;
+  a.v_bits = p->v_bits;
+  if (!chunk) {
+    if (n_tok > 0x7FFFFFFF) return fail(GTQ_EUNSUPPORTED, "gtq_quantize_append: too many tokens");
+    hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)n_tok, p->n_kv), dim3(1024), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "gtq append: launch");
+    return ok();
+  }
+  a.n_items = (pos0 + n_tok - 1) / GTQ_VBLOCK - pos0 / GTQ_VBLOCK + 1;
+  const int lds = append_lds_bytes(p, layer, &a.krot_lds);
+  const int64_t wg_needed = (a.n_items + kAppendWaves - 1) / kAppendWaves;
+  const int gx = (int)std::min<int64_t>(wg_needed, std::max(1, 2048 / p->n_kv));
+  dim3 grid(gx, p->n_kv);
+  // allow the largest dynamic LDS any plan can need (set once)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)append_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kAppendLdsMax);
+  hipError_t e = attr;
+  if (e != hipSuccess) return hip_fail(e, "gtq append: LDS attribute");
+  hipLaunchKernelGGL(append_chunk_kernel, grid, dim3(64 * kAppendWaves), lds, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gtq append: launch");
+  return ok();
+}
+
+int auto_chunk(int64_t max_len, int64_t tiles) {
+  // aim for >= 1024 workgroups (4 waves each), at least 4 blocks per wave
+  const int64_t target =
+      std::min<int64_t>(kMaxChunks, std::max<int64_t>(1, 1024 / std::max<int64_t>(1, tiles)));
+  int64_t ch = (max_len + target - 1) / target;
+  ch = ((ch + 511) / 512) * 512;
+  return (int)std::max<int64_t>(512, ch);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t attn_ws_bytes(int64_t n_tiles, int64_t rows, int64_t n_chunks) {
+  return align256((size_t)n_tiles * 4) + align256((size_t)rows * n_chunks * kPS * 4);
+}
+
+struct AttnLaunch {
+  int64_t rows;
+  int tiles_per_kv;
+  int n_tiles;
+  int chunk;
+  int n_chunks;
+};
+
+gtq_status launch_attn(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* q,
+                       AttnArgs& aa, const AttnLaunch& L, float scale, float* out,
+                       void* ws, hipStream_t stream) {
+  const DevHead* heads = p->d_heads + (size_t)layer * p->n_kv;
+  aa.heads = heads;
+  aa.rot = p->d_rot;
+  aa.cb = p->d_cb;
+  aa.k_codes = c->k_codes;
+  aa.k_norms = c->k_norms;
+  aa.v_codes = c->v_codes;
+  aa.v_norms = c->v_norms;
+  aa.q = q;
+  aa.out = out;
+  aa.counters = reinterpret_cast<uint32_t*>(ws);
+  aa.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)L.n_tiles * 4));
+  aa.capacity = c->capacity;
+  aa.n_kv = p->n_kv;
+  aa.n_q = p->n_q;
+  aa.g = p->n_q / p->n_kv;
+  aa.k_words = p->k_words;
+  aa.tiles_per_kv = L.tiles_per_kv;
+  aa.chunk = L.chunk;
+  aa.n_chunks = L.n_chunks;
+  aa.qscale = scale * LOG2E_F;
+  dim3 grid(L.n_chunks, L.n_tiles);
+  int kr = 0;
+  for (int h = 0; h < p->n_kv; ++h) kr = std::max(kr, p->heads[(size_t)layer * p->n_kv + h].krot_floats);
+  const size_t lds = (size_t)kr * 4;
+  static const hipError_t attr[4] = {
+      hipFuncSetAttribute((const void*)attn_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kD * kD * 4),
+      hipFuncSetAttribute((const void*)attn_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kD * kD * 4),
+      hipFuncSetAttribute((const void*)attn_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, kD * kD * 4),
+      hipFuncSetAttribute((const void*)attn_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, kD * kD * 4)};
+  if (attr[p->v_bits - 1] != hipSuccess) return hip_fail(attr[p->v_bits - 1], "gtq attention: LDS attribute");
+  switch (p->v_bits) {
+    case 1: hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(256), lds, stream, aa); break;
+    case 2: hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(256), lds, stream, aa); break;
+    case 3: hipLaunchKernelGGL(attn_kernel<3>, grid, dim3(256), lds, stream, aa); break;
+    default: hipLaunchKernelGGL(attn_kernel<4>, grid, dim3(256), lds, stream, aa); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gtq attention: launch");
+  return ok();
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out) {
+  if (!out) return fail(GTQ_EINVAL, "gtq_plan_create: out is NULL");
+  *out = nullptr;
+  gtq_plan* p = new (std::nothrow) gtq_plan();
+  if (!p) return fail(GTQ_ENOMEM, "gtq_plan_create: host allocation failed");
+  gtq_status st = plan_build_host(desc, p);
+  if (st != GTQ_OK) {
+    delete p;
+    return st;
+  }
+  if (!(p->flags & GTQ_PLAN_HOST_ONLY)) {
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "gtq_plan_create: no HIP device");
+    }
+    const size_t hb = p->heads.size() * sizeof(DevHead);
+    const size_t rb = p->rot.size() * sizeof(float);
+    if ((e = hipMalloc(&p->d_heads, hb)) != hipSuccess || (e = hipMalloc(&p->d_rot, rb)) != hipSuccess ||
+        (e = hipMalloc(&p->d_cb, sizeof(DevCodebook))) != hipSuccess ||
+        (e = hipMalloc(&p->d_overflow, sizeof(unsigned long long))) != hipSuccess) {
+      gtq_plan_destroy(p);
+      return fail(GTQ_ENOMEM, std::string("gtq_plan_create: device allocation failed: ") + hipGetErrorString(e));
+    }
+    if ((e = hipMemcpy(p->d_heads, p->heads.data(), hb, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(p->d_rot, p->rot.data(), rb, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(p->d_cb, &p->cb, sizeof(DevCodebook), hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemset(p->d_overflow, 0, sizeof(unsigned long long))) != hipSuccess) {
+      gtq_plan_destroy(p);
+      return hip_fail(e, "gtq_plan_create: upload");
+    }
+  }
+  *out = p;
+  return ok();
+}
+
+gtq_status gtq_plan_destroy(gtq_plan* p) {
+  if (!p) return ok();
+  if (p->d_heads || p->d_rot || p->d_cb || p->d_overflow) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(p->d_heads);
+    (void)hipFree(p->d_rot);
+    (void)hipFree(p->d_cb);
+    (void)hipFree(p->d_overflow);
+  }
+  delete p;
+  return ok();
+}
+
+gtq_status gtq_plan_overflow_count(const gtq_plan* p, int64_t* out) {
+  gtq_status st;
+  if (!out) return fail(GTQ_EINVAL, "gtq_plan_overflow_count: out is NULL");
+  if (!check_device_plan(p, "gtq_plan_overflow_count", &st)) return st;
+  unsigned long long v = 0;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(&v, p->d_overflow, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "gtq_plan_overflow_count");
+  *out = (int64_t)v;
+  return ok();
+}
+
+gtq_status gtq_quantize_append(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                               const float* k, const float* v, const int32_t* seq_idx,
+                               const int64_t* slot, int64_t n_tok, void* hip_stream) {
+  gtq_status st;
+  if (!check_device_plan(plan, "gtq_quantize_append", &st)) return st;
+  if (!check_cache(plan, cache, "gtq_quantize_append", &st)) return st;
+  if (layer < 0 || layer >= plan->n_layers) return fail(GTQ_EINVAL, "gtq_quantize_append: layer out of range");
+  if (n_tok < 0) return fail(GTQ_EINVAL, "gtq_quantize_append: n_tok < 0");
+  if (n_tok == 0) return ok();
+  if (!k || !v || !seq_idx || !slot) return fail(GTQ_EINVAL, "gtq_quantize_append: NULL input");
+  return launch_append(plan, layer, cache, k, v, seq_idx, slot, 0, 0, n_tok, false,
+                       (hipStream_t)hip_stream);
+}
+
+gtq_status gtq_quantize_append_chunk(const gtq_plan* plan, int32_t layer,
+                                     const gtq_cache_view* cache, const float* k, const float* v,
+                                     int32_t seq, int64_t pos0, int64_t n_tok, void* hip_stream) {
+  gtq_status st;
+  if (!check_device_plan(plan, "gtq_quantize_append_chunk", &st)) return st;
+  if (!check_cache(plan, cache, "gtq_quantize_append_chunk", &st)) return st;
+  if (layer < 0 || layer >= plan->n_layers) return fail(GTQ_EINVAL, "gtq_quantize_append_chunk: layer out of range");
+  if (seq < 0 || seq >= cache->batch) return fail(GTQ_EINVAL, "gtq_quantize_append_chunk: seq out of range");
+  if (n_tok < 0 || pos0 < 0) return fail(GTQ_EINVAL, "gtq_quantize_append_chunk: negative pos0 or n_tok");
+  if (pos0 + n_tok > cache->capacity) return fail(GTQ_ECAPACITY, "gtq_quantize_append_chunk: pos0 + n_tok > capacity");
+  if (n_tok == 0) return ok();
+  if (!k || !v) return fail(GTQ_EINVAL, "gtq_quantize_append_chunk: NULL input");
+  return launch_append(plan, layer, cache, k, v, nullptr, nullptr, seq, pos0, n_tok, true,
+                       (hipStream_t)hip_stream);
+}
+
+static bool decode_shape(const gtq_plan* p, int32_t batch, int64_t max_len, int32_t chunk,
+                         AttnLaunch* L, gtq_status* st, const char* fn) {
+  if (max_len < 0) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": max_len < 0");
+    return false;
+  }
+  if (chunk < 0 || chunk % kBlk) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk must be 0 or a positive multiple of 32");
+    return false;
+  }
+  const int g = p->n_q / p->n_kv;
+  L->rows = (int64_t)batch * p->n_q;
+  L->tiles_per_kv = (g + 7) / 8;
+  L->n_tiles = batch * p->n_kv * L->tiles_per_kv;
+  L->chunk = chunk ? chunk : auto_chunk(max_len, L->n_tiles);
+  L->n_chunks = (int)std::max<int64_t>(1, (max_len + L->chunk - 1) / L->chunk);
+  if (L->n_chunks > kMaxChunks) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk too small (more than 256 splits per sequence)");
+    return false;
+  }
+  return true;
+}
+
+gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64_t max_len,
+                                      int32_t chunk, size_t* out) {
+  if (!plan || !out) return fail(GTQ_EINVAL, "gtq_decode_workspace_bytes: NULL pointer");
+  if (batch < 1) return fail(GTQ_EINVAL, "gtq_decode_workspace_bytes: batch < 1");
+  AttnLaunch L;
+  gtq_status st;
+  if (!decode_shape(plan, batch, max_len, chunk, &L, &st, "gtq_decode_workspace_bytes")) return st;
+  *out = attn_ws_bytes(L.n_tiles, L.rows, L.n_chunks);
+  return ok();
+}
+
+gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                           const float* q, const int32_t* seq_len, int64_t max_len,
+                           float softmax_scale, int32_t chunk, float* out, float* logits,
+                           void* workspace, size_t ws_bytes, void* hip_stream) {
+  gtq_status st;
+  if (!check_device_plan(plan, "gtq_decode_attn", &st)) return st;
+  if (!check_cache(plan, cache, "gtq_decode_attn", &st)) return st;
+  if (layer < 0 || layer >= plan->n_layers) return fail(GTQ_EINVAL, "gtq_decode_attn: layer out of range");
+  if (!q || !seq_len || !out || !workspace) return fail(GTQ_EINVAL, "gtq_decode_attn: NULL pointer");
+  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_decode_attn: softmax_scale not finite");
+  if (max_len > cache->capacity) return fail(GTQ_ECAPACITY, "gtq_decode_attn: max_len > capacity");
+  if (max_len > INT32_MAX) return fail(GTQ_EUNSUPPORTED, "gtq_decode_attn: max_len too large");
+  AttnLaunch L;
+  if (!decode_shape(plan, cache->batch, max_len, chunk, &L, &st, "gtq_decode_attn")) return st;
+  if (ws_bytes < attn_ws_bytes(L.n_tiles, L.rows, L.n_chunks))
+    return fail(GTQ_ECAPACITY, "gtq_decode_attn: workspace too small");
+  AttnArgs aa{};
+  aa.logits = logits;
+  aa.logits_ld = max_len;
+  aa.seq_len = seq_len;
+  aa.prefill = 0;
+  aa.max_len = (int32_t)max_len;
+  return launch_attn(plan, layer, cache, q, aa, L, softmax_scale, out, workspace,
+                     (hipStream_t)hip_stream);
+}
+
+static bool prefill_shape(const gtq_plan* p, int64_t pos0, int64_t n_tok, int32_t chunk,
+                          AttnLaunch* L, gtq_status* st, const char* fn) {
+  if (pos0 < 0 || n_tok < 1) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": need pos0 >= 0 and n_tok >= 1");
+    return false;
+  }
+  if (chunk < 0 || chunk % kBlk) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk must be 0 or a positive multiple of 32");
+    return false;
+  }
+  const int g = p->n_q / p->n_kv;
+  const int64_t total = pos0 + n_tok;
+  L->rows = n_tok * p->n_q;
+  L->tiles_per_kv = (int)((n_tok * g + 7) / 8);
+  L->n_tiles = p->n_kv * L->tiles_per_kv;
+  L->chunk = chunk ? chunk : auto_chunk(total, L->n_tiles);
+  L->n_chunks = (int)((total + L->chunk - 1) / L->chunk);
+  if (L->n_chunks > kMaxChunks) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk too small (more than 256 splits per sequence)");
+    return false;
+  }
+  return true;
+}
+
+gtq_status gtq_prefill_workspace_bytes(const gtq_plan* plan, int64_t pos0, int64_t n_tok,
+                                       int32_t chunk, size_t* out) {
+  if (!plan || !out) return fail(GTQ_EINVAL, "gtq_prefill_workspace_bytes: NULL pointer");
+  AttnLaunch L;
+  gtq_status st;
+  if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_workspace_bytes")) return st;
+  *out = attn_ws_bytes(L.n_tiles, L.rows, L.n_chunks);
+  return ok();
+}
+
+gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                            const float* q, int32_t seq, int64_t pos0, int64_t n_tok,
+                            float softmax_scale, int32_t chunk, float* out, void* workspace,
+                            size_t ws_bytes, void* hip_stream) {
+  gtq_status st;
+  if (!check_device_plan(plan, "gtq_prefill_attn", &st)) return st;
+  if (!check_cache(plan, cache, "gtq_prefill_attn", &st)) return st;
+  if (layer < 0 || layer >= plan->n_layers) return fail(GTQ_EINVAL, "gtq_prefill_attn: layer out of range");
+  if (seq < 0 || seq >= cache->batch) return fail(GTQ_EINVAL, "gtq_prefill_attn: seq out of range");
+  if (!q || !out || !workspace) return fail(GTQ_EINVAL, "gtq_prefill_attn: NULL pointer");
+  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_prefill_attn: softmax_scale not finite");
+  AttnLaunch L;
+  if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_attn")) return st;
+  if (pos0 + n_tok > cache->capacity) return fail(GTQ_ECAPACITY, "gtq_prefill_attn: pos0 + n_tok > capacity");
+  if (ws_bytes < attn_ws_bytes(L.n_tiles, L.rows, L.n_chunks))
+    return fail(GTQ_ECAPACITY, "gtq_prefill_attn: workspace too small");
+  AttnArgs aa{};
+  aa.logits = nullptr;
+  aa.prefill = 1;
+  aa.seq = seq;
+  aa.pos0 = pos0;
+  aa.n_tok = (int32_t)n_tok;
+  aa.max_len = (int32_t)(pos0 + n_tok);
+  return launch_attn(plan, layer, cache, q, aa, L, softmax_scale, out, workspace,
+                     (hipStream_t)hip_stream);
+}
+
+}  // extern "C"

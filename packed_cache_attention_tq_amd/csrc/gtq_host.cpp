@@ -1,0 +1,371 @@
+// Host-side part of libgtq: error reporting, Lloyd-Max codebooks, energy scores,
+// largest-marginal-gain allocation, group layouts and host validation of plans.
+// Nothing here touches the GPU.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+
+#include "gtq_internal.h"
+
+namespace gtq {
+
+static thread_local std::string g_last_error;
+
+gtq_status fail(gtq_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+gtq_status ok() {
+  g_last_error.clear();
+  return GTQ_OK;
+}
+
+// ---------------------------------------------------------------- Lloyd-Max
+// MSE-optimal scalar quantizer of a unit Gaussian (TurboQuant diagram, "paper"
+// column, per-coordinate MSE scalar quantization), by Lloyd's alternation of the
+// nearest-neighbour cells (edges at centroid midpoints) and the centroid
+// condition (each centroid is the conditional mean of its cell).
+static double pdf(double x) {
+  if (isinf(x)) return 0.0;
+  return exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+}
+static double cell_mass(double a, double b) {  // P(a < X < b)
+  const double r2 = sqrt(2.0);
+  if (a >= 0.0) return 0.5 * (erfc(a / r2) - erfc(b / r2));
+  if (b <= 0.0) return 0.5 * (erfc(-b / r2) - erfc(-a / r2));
+  return 1.0 - 0.5 * erfc(-a / r2) - 0.5 * erfc(b / r2);
+}
+
+void lloyd_max(int bits, double* c, double* mse) {
+  const int n = 1 << bits;
+  double edge[17];
+  for (int k = 0; k < n; ++k) c[k] = 2.0 * (-1.0 + (2.0 * k + 1.0) / n);
+  for (int it = 0; it < 200000; ++it) {
+    edge[0] = -INFINITY;
+    edge[n] = INFINITY;
+    for (int k = 1; k < n; ++k) edge[k] = 0.5 * (c[k - 1] + c[k]);
+    double delta = 0.0;
+    for (int k = 0; k < n; ++k) {
+      double nk = (pdf(edge[k]) - pdf(edge[k + 1])) / cell_mass(edge[k], edge[k + 1]);
+      delta = std::max(delta, fabs(nk - c[k]));
+      c[k] = nk;
+    }
+    if (delta < 1e-15) break;
+  }
+  edge[0] = -INFINITY;
+  edge[n] = INFINITY;
+  for (int k = 1; k < n; ++k) edge[k] = 0.5 * (c[k - 1] + c[k]);
+  double s = 0.0;
+  for (int k = 0; k < n; ++k) s += cell_mass(edge[k], edge[k + 1]) * c[k] * c[k];
+  *mse = 1.0 - s;
+}
+
+struct Tables {
+  double mse[5];
+  float cent[5][16];
+  float thr[5][16];
+};
+
+// binary16 round-to-nearest-even of a double, returned as float (exact).
+static float round_to_half(double x) {
+  _Float16 h = (_Float16)x;  // IEEE conversion, round to nearest even
+  return (float)h;
+}
+
+static const Tables& tables() {
+  static Tables t;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    t.mse[0] = 1.0;
+    memset(t.cent, 0, sizeof(t.cent));
+    memset(t.thr, 0, sizeof(t.thr));
+    for (int b = 1; b <= 4; ++b) {
+      double c[16];
+      lloyd_max(b, c, &t.mse[b]);
+      const int n = 1 << b;
+      for (int k = 0; k < n; ++k) t.cent[b][k] = round_to_half(c[k]);
+      // midpoint of two binary16 values is exact in fp32
+      for (int k = 0; k + 1 < n; ++k)
+        t.thr[b][k] = (float)(0.5 * ((double)t.cent[b][k] + (double)t.cent[b][k + 1]));
+    }
+  });
+  return t;
+}
+
+void fill_codebook(DevCodebook* cb) {
+  const Tables& t = tables();
+  memcpy(cb->c, t.cent, sizeof(cb->c));
+  memcpy(cb->t, t.thr, sizeof(cb->t));
+}
+
+// ---------------------------------------------------------------- layouts
+static inline void block_coords(int j, int layout, int* a, int* b) {
+  if (layout == GTQ_ROPE_HALF) {
+    *a = j;
+    *b = j + kJ;
+  } else {
+    *a = 2 * j;
+    *b = 2 * j + 1;
+  }
+}
+
+// Equal-rate groups in ascending rate (Block-GTQ abstract, 5th sentence) and the
+// decode kernel's K-block table. Rates must already be validated in [1, 4].
+void build_head(const uint8_t* rates, int layout, gtq_head_layout* lay, DevHead* dh) {
+  memset(lay, 0, sizeof(*lay));
+  memset(dh, 0, sizeof(*dh));
+  int pos = 0, bit = 0, kp = 0, kb = 0, rot = 0;
+  for (int r = 1; r <= 4; ++r) {
+    int count = 0;
+    for (int j = 0; j < kJ; ++j) count += (rates[j] == r);
+    if (!count) continue;
+    const int g = lay->n_groups++;
+    const int d = 2 * count;
+    lay->rate[g] = r;
+    lay->dim[g] = d;
+    lay->bit_offset[g] = bit;
+    lay->rot_offset[g] = rot;
+    dh->rate[g] = r;
+    dh->dim[g] = d;
+    dh->bit_off[g] = bit;
+    dh->pos_off[g] = pos;
+    dh->kp_off[g] = kp;
+    dh->krot_off[g] = rot;  // relative; made absolute by the plan
+    const int nk = (d + kKB - 1) / kKB;
+    dh->nkb_g[g] = nk;
+    for (int i = 0; i < nk; ++i) dh->kb_bit[kb + i] = bit + i * kKB * r;
+    for (int j = 0; j < kJ; ++j) {
+      if (rates[j] != r) continue;
+      int a, b;
+      block_coords(j, layout, &a, &b);
+      lay->coord[pos] = a;
+      dh->coord[pos] = (uint8_t)a;
+      ++pos;
+      lay->coord[pos] = b;
+      dh->coord[pos] = (uint8_t)b;
+      ++pos;
+    }
+    bit += d * r;
+    kp += nk * kKB;
+    kb += nk;
+    rot += d * d;
+  }
+  dh->n_groups = lay->n_groups;
+  dh->nkb = kb;
+  dh->krot_floats = rot;
+  lay->k_words = (bit + 31) / 32;
+}
+
+}  // namespace gtq
+
+using namespace gtq;
+
+extern "C" {
+
+const char* gtq_last_error(void) { return g_last_error.c_str(); }
+
+gtq_status gtq_rate_distortion(int32_t b_max, double* d_out) {
+  if (!d_out) return fail(GTQ_EINVAL, "gtq_rate_distortion: d_out is NULL");
+  if (b_max < 1 || b_max > 4) return fail(GTQ_EINVAL, "gtq_rate_distortion: b_max must be in [1, 4]");
+  const Tables& t = tables();
+  for (int b = 0; b <= b_max; ++b) d_out[b] = t.mse[b];
+  return ok();
+}
+
+gtq_status gtq_codebook(int32_t bits, float* centroids, float* thresholds) {
+  if (bits < 1 || bits > 4) return fail(GTQ_EINVAL, "gtq_codebook: bits must be in [1, 4]");
+  const Tables& t = tables();
+  const int n = 1 << bits;
+  if (centroids)
+    for (int k = 0; k < n; ++k) centroids[k] = t.cent[bits][k];
+  if (thresholds)
+    for (int k = 0; k + 1 < n; ++k) thresholds[k] = t.thr[bits][k];
+  return ok();
+}
+
+gtq_status gtq_alloc_rates(const float* q_cal, int64_t n_q, const float* k_cal, int64_t n_k,
+                           int32_t head_dim, int32_t rope_layout, int32_t b_min, int32_t b_max,
+                           int32_t budget, uint8_t* rates_out, double* scores_out,
+                           double* proxy_out) {
+  if (!q_cal || !k_cal || !rates_out) return fail(GTQ_EINVAL, "gtq_alloc_rates: NULL pointer");
+  if (head_dim != kD) return fail(GTQ_EUNSUPPORTED, "gtq_alloc_rates: head_dim must be 128");
+  if (n_q < 1 || n_k < 1) return fail(GTQ_EINVAL, "gtq_alloc_rates: n_q and n_k must be >= 1");
+  if (rope_layout != GTQ_ROPE_HALF && rope_layout != GTQ_ROPE_INTERLEAVED)
+    return fail(GTQ_EINVAL, "gtq_alloc_rates: bad rope_layout");
+  if (!(1 <= b_min && b_min <= b_max && b_max <= 4))
+    return fail(GTQ_EINVAL, "gtq_alloc_rates: need 1 <= b_min <= b_max <= 4");
+  if (budget < kJ * b_min || budget > kJ * b_max)
+    return fail(GTQ_EINVAL, "gtq_alloc_rates: budget outside [64*b_min, 64*b_max]");
+
+  // Energy score per RoPE block (abstract, 3rd sentence): mean query block energy
+  // times mean key block energy, fp64 with compensated (Neumaier) summation.
+  double s[kJ];
+  for (int j = 0; j < kJ; ++j) {
+    int a, b;
+    block_coords(j, rope_layout, &a, &b);
+    double e[2];
+    const float* src[2] = {q_cal, k_cal};
+    const int64_t cnt[2] = {n_q, n_k};
+    for (int w = 0; w < 2; ++w) {
+      double sum = 0.0, comp = 0.0;
+      for (int64_t r = 0; r < cnt[w]; ++r) {
+        const double x = src[w][r * kD + a], y = src[w][r * kD + b];
+        const double v = x * x + y * y;
+        const double t = sum + v;
+        comp += (fabs(sum) >= fabs(v)) ? (sum - t) + v : (v - t) + sum;
+        sum = t;
+      }
+      e[w] = (sum + comp) / (double)cnt[w];
+    }
+    s[j] = e[0] * e[1];
+    if (!isfinite(s[j])) return fail(GTQ_EINVAL, "gtq_alloc_rates: non-finite calibration data");
+  }
+  // Largest marginal gain (abstract, 4th sentence): repeatedly give one bit to the
+  // block whose proxy sum_j s_j D(b_j) drops most; ties go to the smallest block.
+  const Tables& t = tables();
+  int rate[kJ];
+  int total = 0;
+  for (int j = 0; j < kJ; ++j) {
+    rate[j] = b_min;
+    total += b_min;
+  }
+  while (total < budget) {
+    int best = -1;
+    double best_gain = -INFINITY;
+    for (int j = 0; j < kJ; ++j) {
+      if (rate[j] >= b_max) continue;
+      const double gain = s[j] * (t.mse[rate[j]] - t.mse[rate[j] + 1]);
+      if (gain > best_gain) {
+        best_gain = gain;
+        best = j;
+      }
+    }
+    ++rate[best];
+    ++total;
+  }
+  double proxy = 0.0;
+  for (int j = 0; j < kJ; ++j) {
+    rates_out[j] = (uint8_t)rate[j];
+    if (scores_out) scores_out[j] = s[j];
+    proxy += s[j] * t.mse[rate[j]];
+  }
+  if (proxy_out) *proxy_out = proxy;
+  return ok();
+}
+
+gtq_status gtq_head_layout_from_rates(const uint8_t* rates, int32_t rope_layout,
+                                      gtq_head_layout* out) {
+  if (!rates || !out) return fail(GTQ_EINVAL, "gtq_head_layout_from_rates: NULL pointer");
+  if (rope_layout != GTQ_ROPE_HALF && rope_layout != GTQ_ROPE_INTERLEAVED)
+    return fail(GTQ_EINVAL, "gtq_head_layout_from_rates: bad rope_layout");
+  for (int j = 0; j < kJ; ++j)
+    if (rates[j] < 1 || rates[j] > 4)
+      return fail(GTQ_EINVAL, "gtq_head_layout_from_rates: rates must be in [1, 4]");
+  DevHead dh;
+  build_head(rates, rope_layout, out, &dh);
+  return ok();
+}
+
+gtq_status gtq_plan_layout(const gtq_plan* plan, int32_t layer, int32_t kv_head,
+                           gtq_head_layout* out) {
+  if (!plan || !out) return fail(GTQ_EINVAL, "gtq_plan_layout: NULL pointer");
+  if (layer < 0 || layer >= plan->n_layers || kv_head < 0 || kv_head >= plan->n_kv)
+    return fail(GTQ_EINVAL, "gtq_plan_layout: layer or kv_head out of range");
+  *out = plan->layouts[(size_t)layer * plan->n_kv + kv_head];
+  return ok();
+}
+
+gtq_status gtq_cache_bytes(const gtq_plan* plan, int32_t batch, int64_t capacity,
+                           gtq_cache_sizes* out) {
+  if (!plan || !out) return fail(GTQ_EINVAL, "gtq_cache_bytes: NULL pointer");
+  if (batch < 1 || capacity < 1 || capacity % GTQ_SEQ_ALIGN)
+    return fail(GTQ_EINVAL, "gtq_cache_bytes: batch >= 1 and capacity a positive multiple of 32");
+  const size_t bh = (size_t)batch * plan->n_kv;
+  out->k_words = plan->k_words;
+  out->v_words_per_block = 32 * plan->v_bits;
+  out->k_codes_bytes = bh * capacity * plan->k_words * 4;
+  out->k_norms_bytes = bh * capacity * kNS * 4;
+  out->v_codes_bytes = bh * (capacity / GTQ_VBLOCK) * 32 * plan->v_bits * 4;
+  out->v_norms_bytes = bh * capacity * 4;
+  out->logical_bits_per_token = 2 * plan->k_budget + kD * plan->v_bits;
+  out->bytes_per_token = plan->k_words * 4 + kNS * 4 + 16 * plan->v_bits + 4;
+  return ok();
+}
+
+}  // extern "C"
+
+namespace gtq {
+// Host validation and construction of a plan (everything except the device copy).
+gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
+  if (!d) return fail(GTQ_EINVAL, "gtq_plan_create: desc is NULL");
+  if (d->head_dim != kD) return fail(GTQ_EUNSUPPORTED, "gtq_plan_create: head_dim must be 128");
+  if (d->n_layers < 1 || d->n_kv_heads < 1 || d->n_q_heads < 1)
+    return fail(GTQ_EINVAL, "gtq_plan_create: layer and head counts must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(GTQ_EINVAL, "gtq_plan_create: n_q_heads must be a multiple of n_kv_heads");
+  if (d->rope_layout != GTQ_ROPE_HALF && d->rope_layout != GTQ_ROPE_INTERLEAVED)
+    return fail(GTQ_EINVAL, "gtq_plan_create: bad rope_layout");
+  if (d->v_bits < 1 || d->v_bits > 4) return fail(GTQ_EINVAL, "gtq_plan_create: v_bits must be in [1, 4]");
+  if (d->k_budget < kJ || d->k_budget > 4 * kJ || d->k_budget % 16)
+    return fail(GTQ_EINVAL, "gtq_plan_create: k_budget must be a multiple of 16 in [64, 256]");
+  if (d->flags & ~GTQ_PLAN_HOST_ONLY) return fail(GTQ_EINVAL, "gtq_plan_create: unknown flags");
+  if (!d->k_rates || !d->k_rot || !d->v_rot) return fail(GTQ_EINVAL, "gtq_plan_create: NULL table");
+  p->n_layers = d->n_layers;
+  p->n_kv = d->n_kv_heads;
+  p->n_q = d->n_q_heads;
+  p->rope_layout = d->rope_layout;
+  p->k_budget = d->k_budget;
+  p->v_bits = d->v_bits;
+  p->k_words = 2 * d->k_budget / 32;
+  p->flags = d->flags;
+  const size_t nh = (size_t)d->n_layers * d->n_kv_heads;
+  p->heads.resize(nh);
+  p->layouts.resize(nh);
+  size_t krot_total = 0;
+  for (size_t h = 0; h < nh; ++h) {
+    const uint8_t* r = d->k_rates + h * kJ;
+    int sum = 0;
+    for (int j = 0; j < kJ; ++j) {
+      if (r[j] < 1 || r[j] > 4) return fail(GTQ_EINVAL, "gtq_plan_create: rates must be in [1, 4]");
+      sum += r[j];
+    }
+    if (sum != d->k_budget)
+      return fail(GTQ_EINVAL, "gtq_plan_create: a head's rates do not sum to k_budget (head " +
+                                  std::to_string(h) + ")");
+    build_head(r, d->rope_layout, &p->layouts[h], &p->heads[h]);
+    krot_total += p->heads[h].krot_floats;
+  }
+  // rotation pool: all K group rotations (as given), all V rotations, then the V
+  // rotations transposed (read column-wise by the attention kernel's last step)
+  const size_t vsz = (size_t)kD * kD;
+  try {
+    p->rot.resize(krot_total + 2 * nh * vsz);
+  } catch (...) {
+    return fail(GTQ_ENOMEM, "gtq_plan_create: host allocation failed");
+  }
+  memcpy(p->rot.data(), d->k_rot, krot_total * sizeof(float));
+  memcpy(p->rot.data() + krot_total, d->v_rot, nh * vsz * sizeof(float));
+  for (size_t h = 0; h < nh; ++h) {
+    const float* src = d->v_rot + h * vsz;
+    float* dst = p->rot.data() + krot_total + nh * vsz + h * vsz;
+    for (int i = 0; i < kD; ++i)
+      for (int j = 0; j < kD; ++j) dst[(size_t)j * kD + i] = src[(size_t)i * kD + j];
+  }
+  size_t off = 0;
+  for (size_t h = 0; h < nh; ++h) {
+    DevHead& dh = p->heads[h];
+    for (int g = 0; g < dh.n_groups; ++g) dh.krot_off[g] += (int64_t)off;
+    off += dh.krot_floats;
+    dh.vrot_off = (int64_t)(krot_total + h * vsz);
+    dh.vrot_t_off = (int64_t)(krot_total + nh * vsz + h * vsz);
+    for (size_t i = 0; i < (size_t)dh.krot_floats; ++i)
+      if (!isfinite(p->rot[dh.krot_off[0] + i]))
+        return fail(GTQ_EINVAL, "gtq_plan_create: non-finite K rotation");
+  }
+  fill_codebook(&p->cb);
+  return ok();
+}
+}  // namespace gtq

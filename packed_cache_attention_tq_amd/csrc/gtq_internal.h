@@ -1,0 +1,71 @@
+// Internal types shared by the host code and the HIP kernels of libgtq.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "gtq.h"
+
+namespace gtq {
+
+constexpr int kD = GTQ_HEAD_DIM;      // head dimension
+constexpr int kJ = GTQ_BLOCKS;        // RoPE blocks
+constexpr int kMaxGroups = GTQ_MAX_GROUPS;
+constexpr int kKB = 32;               // coordinates per MFMA K-block of the decode kernel
+constexpr int kMaxKB = 8;             // sum_g ceil(d_g / 32) <= 4 + 128/32
+constexpr int kKP = kKB * kMaxKB;     // padded query length (halves)
+constexpr int kBlk = 32;              // tokens per decode block
+constexpr int kNS = GTQ_KNORM_STRIDE;
+
+// Per (layer, KV head) tables, uploaded once per plan (plain data, same layout on
+// host and device).
+struct DevHead {
+  int32_t n_groups;
+  int32_t nkb;                    // MFMA K-blocks (each inside one group)
+  int32_t rate[kMaxGroups];
+  int32_t dim[kMaxGroups];
+  int32_t bit_off[kMaxGroups];    // group start in the key record (bits)
+  int32_t pos_off[kMaxGroups];    // group start in record position order (0..127)
+  int32_t kp_off[kMaxGroups];     // group start in the padded K-block order
+  int32_t nkb_g[kMaxGroups];      // K-blocks of each group
+  int32_t kb_bit[kMaxKB];         // record bit of each K-block's first coordinate
+  int64_t krot_off[kMaxGroups];   // float offset of Pi_g (row-major d x d) in the pool
+  int64_t vrot_off;               // float offset of Pi_V (row-major 128 x 128)
+  int64_t vrot_t_off;             // float offset of Pi_V^T (row-major, i.e. Pi_V column-major)
+  int32_t krot_floats;            // sum_g d_g^2
+  int32_t pad_;
+  uint8_t coord[kD];              // record position -> head coordinate
+};
+
+struct DevCodebook {
+  float c[5][16];   // c[b][k]: centroid k of rate b (binary16 values)
+  float t[5][16];   // t[b][k]: threshold k of rate b (midpoints), k < 2^b - 1
+};
+
+}  // namespace gtq
+
+struct gtq_plan {
+  int32_t n_layers = 0, n_kv = 0, n_q = 0, rope_layout = 0, k_budget = 0, v_bits = 0;
+  int32_t k_words = 0, flags = 0;
+  std::vector<gtq::DevHead> heads;      // [L][H_kv]
+  std::vector<gtq_head_layout> layouts; // [L][H_kv]
+  std::vector<float> rot;               // rotation pool
+  gtq::DevCodebook cb{};
+  // device copies (null for host-only plans)
+  int device = -1;
+  gtq::DevHead* d_heads = nullptr;
+  float* d_rot = nullptr;
+  gtq::DevCodebook* d_cb = nullptr;
+  unsigned long long* d_overflow = nullptr;
+};
+
+namespace gtq {
+gtq_status fail(gtq_status st, const std::string& msg);
+gtq_status ok();
+// host math shared by the host entry points
+void lloyd_max(int bits, double* centroids, double* mse);
+void build_head(const uint8_t* rates, int rope_layout, gtq_head_layout* lay, DevHead* dh);
+void fill_codebook(DevCodebook* cb);
+gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p);
+}  // namespace gtq

@@ -1,0 +1,149 @@
+"""Helpers for the GPU parity tests: building matching plans for the oracle and the
+library from the seeded generator, and converting between the canonical per-token
+code stream and the library's physical cache layout (bit marshalling only)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from gtq_inputs import head_inputs, head_rotations
+from oracle import gtq_oracle as O
+
+TOL_REL, TOL_ABS = 2e-3, 1e-4     # |gpu - ref| <= TOL_ABS + TOL_REL * |ref|
+TIE_WINDOW = 1e-6
+
+
+def assert_close(gpu, ref, what):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(gpu - ref)
+    lim = TOL_ABS + TOL_REL * np.abs(ref)
+    bad = ~(err <= lim)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at {tuple(i)}: "
+                             f"gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r}")
+    return float((err / (TOL_ABS + TOL_REL * np.abs(ref))).max()) if err.size else 0.0
+
+
+class Case:
+    """Plans (oracle + library) and per-sequence inputs for n_layers x h_kv heads."""
+
+    def __init__(self, seed, n_layers, h_kv, g, n_cache, k_budget, v_bits, batch=1, layout=O.HALF,
+                 n_dec_q=1, b_min=1, b_max=4):
+        import packed_cache_attention_tq_amd as G
+        self.seed, self.L, self.H, self.g = seed, n_layers, h_kv, g
+        self.HQ = h_kv * g
+        self.n, self.k_budget, self.v_bits, self.batch, self.layout = n_cache, k_budget, v_bits, batch, layout
+        self.rates = np.zeros((n_layers, h_kv, 64), np.uint8)
+        self.heads = {}
+        k_rot_all, v_rot_all = [], []
+        self.inputs = {}
+        for l in range(n_layers):
+            kl, vl = [], []
+            for h in range(h_kv):
+                inp = [head_inputs(seed, l, h, g, n_cache, n_dec_q=n_dec_q, layout=layout, seq=b)
+                       for b in range(batch)]
+                self.inputs[l, h] = inp
+                # the oracle allocates for itself; the library's allocation must agree
+                s = O.energy_scores(inp[0]["calib_q"], inp[0]["calib_k"], layout)
+                r = O.greedy_allocate(s, O.rate_distortion(), b_min, b_max, k_budget)
+                r_lib, _, _ = G.gtq_alloc_rates(inp[0]["calib_q"], inp[0]["calib_k"], b_min, b_max,
+                                                k_budget, rope_layout=layout)
+                assert np.array_equal(r_lib, r), f"rate allocation differs at layer {l} head {h}"
+                self.rates[l, h] = r_lib
+                dims = [len(c) for _, c in O.groups_from_rates(r, layout)]
+                kr, vr = head_rotations(seed, l, h, dims)
+                self.heads[l, h] = O.HeadPlan(r, kr, vr, v_bits, layout)
+                kl.append(kr)
+                vl.append(vr)
+            k_rot_all.append(kl)
+            v_rot_all.append(vl)
+        self.k_rot, self.v_rot = k_rot_all, np.array(v_rot_all)
+
+    def plan(self, host_only=False):
+        import packed_cache_attention_tq_amd as G
+        return G.Plan(self.L, self.H, self.HQ, self.k_budget, self.v_bits, self.rates, self.k_rot,
+                      self.v_rot, rope_layout=self.layout, host_only=host_only)
+
+    def kv(self, l, b, lo=0, hi=None):
+        """k, v [n_tok, H_kv, 128] of sequence b, tokens lo..hi-1."""
+        hi = self.n if hi is None else hi
+        k = np.stack([self.inputs[l, h][b]["k"][lo:hi] for h in range(self.H)], axis=1)
+        v = np.stack([self.inputs[l, h][b]["v"][lo:hi] for h in range(self.H)], axis=1)
+        return np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+    def q(self, l, b, qi=0):
+        """decode query [H_q, 128] of sequence b (query heads of KV head h are h*g .. h*g+g-1)."""
+        return np.concatenate([self.inputs[l, h][b]["q"][qi] for h in range(self.H)], axis=0)
+
+
+# ---------------------------------------------------------------- layout marshalling
+
+def v_codes_from_physical(words: np.ndarray, n_tok: int, vb: int) -> np.ndarray:
+    """Physical value blocks [n_blocks][32*vb] u32 -> codes [n_tok][128]."""
+    w = np.asarray(words, np.uint32).astype(np.uint64)
+    s = np.arange(n_tok)[:, None]
+    c = np.arange(128)[None, :]
+    blk, j = s // 8, s % 8
+    bit = 8 * vb * c + vb * j
+    wi, sh = bit // 32, (bit % 32).astype(np.uint64)
+    lo = w[blk, wi]
+    hi = np.where(wi + 1 < w.shape[1], w[blk, np.minimum(wi + 1, w.shape[1] - 1)], np.uint64(0))
+    val = lo | (hi << np.uint64(32))
+    return ((val >> sh) & np.uint64((1 << vb) - 1)).astype(np.int64)
+
+
+def v_codes_to_physical(codes: np.ndarray, vb: int, n_blocks: int) -> np.ndarray:
+    """codes [n_tok][128] -> physical blocks [n_blocks][32*vb] u32 (unwritten bits 0)."""
+    words = np.zeros((n_blocks, 32 * vb + 1), np.uint64)
+    n = codes.shape[0]
+    s = np.arange(n)[:, None]
+    c = np.arange(128)[None, :]
+    blk, j = np.broadcast_arrays(s // 8, s % 8)
+    bit = 8 * vb * c + vb * j
+    wi, sh = bit // 32, (bit % 32).astype(np.uint64)
+    v = np.asarray(codes, np.uint64) << sh
+    np.bitwise_or.at(words, (blk, wi), v & np.uint64(0xFFFFFFFF))
+    np.bitwise_or.at(words, (blk, wi + 1), v >> np.uint64(32))
+    return words[:, :32 * vb].astype(np.uint32)
+
+
+def unpack_key_record(words, plan: O.HeadPlan):
+    return O.unpack_codes(np.asarray(words, np.uint32), plan.group_dims, plan.group_rates)
+
+
+def tie_mask(z: np.ndarray, bits: int) -> np.ndarray:
+    """True where z lies within TIE_WINDOW of one of the codebook thresholds."""
+    _, t = O.codebook(bits)
+    return (np.abs(z[..., None] - t[None, :]) < TIE_WINDOW).any(axis=-1)
+
+
+def compare_codes(gpu_codes, ref_codes, ref_z, bits, what):
+    """Codes must be equal except where the oracle's z is within the tie window of a
+    threshold; returns the number of such tie mismatches."""
+    gpu_codes = np.asarray(gpu_codes)
+    mism = gpu_codes != ref_codes
+    ties = tie_mask(ref_z, bits)
+    hard = mism & ~ties
+    if hard.any():
+        i = tuple(np.argwhere(hard)[0])
+        raise AssertionError(f"{what}: {hard.sum()} code mismatches outside the tie window; first at {i}: "
+                             f"gpu={gpu_codes[i]} ref={ref_codes[i]} z={ref_z[i]!r}")
+    return int((mism & ties).sum())
+
+
+def compare_norms(gpu, ref, what):
+    """fp32 norms equal, or 1 ulp apart (fp64 summation order); returns ulp-off count."""
+    gpu = np.asarray(gpu, np.float32)
+    ref = np.asarray(ref, np.float32)
+    d = np.abs(gpu.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    if (d > 1).any():
+        i = tuple(np.argwhere(d > 1)[0])
+        raise AssertionError(f"{what}: norm off by {d[i]} ulp at {i}: gpu={gpu[i]!r} ref={ref[i]!r}")
+    return int((d == 1).sum())
+
+
+def scale_default():
+    return 1.0 / math.sqrt(128)

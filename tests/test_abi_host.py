@@ -1,0 +1,189 @@
+"""Host-side checks of libgtq (no GPU needed): every symbol that include/gtq.h declares
+is exported, the host math (rate penalties, codebooks, energy scores, allocation,
+group layouts) matches the oracle, and every host-checkable error path returns its
+status with a message."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gtq_inputs import HALF, INTERLEAVED, head_inputs, head_rotations
+from oracle import gtq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+G = pytest.importorskip("packed_cache_attention_tq_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(G.LIB_PATH):
+        pytest.fail("libgtq.so is not built (run __graft_entry__.build())")
+    return G.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "gtq.h")).read()
+    declared = set(re.findall(r"^\s*(?:gtq_status|const char\*)\s+(gtq_\w+)\s*\(", hdr, re.M))
+    assert len(declared) == len(G.EXPORTS) == 16
+    raw = C.CDLL(G.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(raw, name), name
+    assert declared == set(G.EXPORTS)
+
+
+def test_rate_distortion_matches_oracle(lib):
+    assert np.allclose(G.gtq_rate_distortion(4), O.rate_distortion(), rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle(lib, bits):
+    c, t = G.gtq_codebook(bits)
+    c2, t2 = O.codebook(bits)
+    assert np.array_equal(c.astype(np.float64), c2)
+    assert np.array_equal(t.astype(np.float64), t2)
+
+
+@pytest.mark.parametrize("layout", [HALF, INTERLEAVED])
+@pytest.mark.parametrize("budget,bmin,bmax", [(128, 1, 4), (192, 1, 4), (160, 1, 3), (64, 1, 4),
+                                               (256, 1, 4), (150, 2, 3)])
+def test_alloc_matches_oracle(lib, layout, budget, bmin, bmax):
+    for seed in range(3):
+        inp = head_inputs(seed, 0, 0, 4, 8, layout=layout)
+        r, s, p = G.gtq_alloc_rates(inp["calib_q"], inp["calib_k"], bmin, bmax, budget, rope_layout=layout)
+        so = O.energy_scores(inp["calib_q"], inp["calib_k"], layout)
+        ro = O.greedy_allocate(so, O.rate_distortion(), bmin, bmax, budget)
+        assert np.allclose(s, so, rtol=1e-12, atol=0)
+        assert np.array_equal(r, ro)
+        assert p == pytest.approx(O.proxy(so, O.rate_distortion(), ro), rel=1e-12)
+        assert int(r.sum()) == budget
+
+
+def test_alloc_uniform_special_case(lib):
+    q = np.ones((10, 128), np.float32)
+    k = np.ones((3, 128), np.float32)
+    r, s, _ = G.gtq_alloc_rates(q, k, 1, 4, 128)
+    assert np.all(r == 2) and np.allclose(s, 4.0)
+
+
+@pytest.mark.parametrize("layout", [HALF, INTERLEAVED])
+def test_layout_matches_oracle_groups(lib, layout):
+    rng = np.random.default_rng(4)
+    for budget in (100, 128, 192):
+        rates = O.greedy_allocate(np.exp(2 * rng.standard_normal(64)), O.rate_distortion(), 1, 4, budget)
+        lay = G.gtq_head_layout_from_rates(rates, layout)
+        groups = O.groups_from_rates(rates, layout)
+        assert lay["n_groups"] == len(groups)
+        assert lay["rate"] == [r for r, _ in groups]
+        assert lay["dim"] == [len(c) for _, c in groups]
+        assert lay["coord"] == [int(x) for _, c in groups for x in c]
+        off, rot = 0, 0
+        for gi, (r, c) in enumerate(groups):
+            assert lay["bit_offset"][gi] == off and lay["rot_offset"][gi] == rot
+            off += len(c) * r
+            rot += len(c) ** 2
+        assert lay["k_words"] == (2 * budget + 31) // 32
+
+
+def _small_plan_inputs(L=2, H=2, budget=128, layout=HALF):
+    rates = np.zeros((L, H, 64), np.uint8)
+    krot, vrot = [], []
+    for l in range(L):
+        kl, vl = [], []
+        for h in range(H):
+            inp = head_inputs(9, l, h, 2, 4, layout=layout)
+            r = O.greedy_allocate(O.energy_scores(inp["calib_q"], inp["calib_k"], layout),
+                                  O.rate_distortion(), 1, 4, budget)
+            rates[l, h] = r
+            kr, vr = head_rotations(9, l, h, [len(c) for _, c in O.groups_from_rates(r, layout)])
+            kl.append(kr)
+            vl.append(vr)
+        krot.append(kl)
+        vrot.append(vl)
+    return rates, krot, np.array(vrot)
+
+
+def test_host_only_plan_layout_and_sizes(lib):
+    rates, krot, vrot = _small_plan_inputs()
+    p = G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True)
+    for l in range(2):
+        for h in range(2):
+            assert p.layout(l, h) == G.gtq_head_layout_from_rates(rates[l, h])
+    s = p.cache_sizes(3, 64)
+    assert s.k_words == 8 and s.v_words_per_block == 64
+    assert s.k_codes_bytes == 3 * 2 * 64 * 8 * 4
+    assert s.v_codes_bytes == 3 * 2 * 8 * 64 * 4
+    assert s.logical_bits_per_token == 2 * 128 + 2 * 128          # K2V2: 2 bits per coordinate
+    assert s.bytes_per_token == 84                                  # 32 + 16 + 32 + 4
+    p.destroy()
+
+
+def _expect(st_exc, status, text):
+    assert st_exc.value.status == status
+    assert text in str(st_exc.value)
+
+
+def test_error_paths(lib):
+    q = np.ones((4, 128), np.float32)
+    with pytest.raises(G.GtqError) as e:
+        G.gtq_alloc_rates(q, q, 1, 4, 20)
+    _expect(e, 1, "budget")
+    with pytest.raises(G.GtqError) as e:
+        G.gtq_alloc_rates(q, q, 3, 2, 150)
+    _expect(e, 1, "b_min")
+    with pytest.raises(G.GtqError) as e:
+        G.gtq_alloc_rates(q, q, 1, 4, 128, head_dim=64)
+    _expect(e, 2, "head_dim")
+    with pytest.raises(G.GtqError) as e:
+        G.gtq_alloc_rates(q, q, 1, 4, 128, rope_layout=7)
+    _expect(e, 1, "rope_layout")
+    with pytest.raises(G.GtqError) as e:
+        G.gtq_codebook(5)
+    _expect(e, 1, "bits")
+    bad = np.full(64, 5, np.uint8)
+    with pytest.raises(G.GtqError) as e:
+        G.gtq_head_layout_from_rates(bad)
+    _expect(e, 1, "rates")
+    assert lib.gtq_alloc_rates(None, 1, None, 1, 128, 0, 1, 4, 128, None, None, None) == 1
+    assert b"NULL" in lib.gtq_last_error()
+
+    rates, krot, vrot = _small_plan_inputs()
+    with pytest.raises(G.GtqError) as e:        # rates not summing to the budget
+        G.Plan(2, 2, 4, 192, 2, rates, krot, vrot, host_only=True)
+    _expect(e, 1, "k_budget")
+    with pytest.raises(G.GtqError) as e:
+        G.Plan(2, 2, 4, 128, 5, rates, krot, vrot, host_only=True)
+    _expect(e, 1, "v_bits")
+    with pytest.raises(G.GtqError) as e:
+        G.Plan(2, 2, 3, 128, 2, rates, krot, vrot, host_only=True)
+    _expect(e, 1, "multiple")
+    with pytest.raises(G.GtqError) as e:
+        G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True, head_dim=64)
+    _expect(e, 2, "head_dim")
+    p = G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True)
+    with pytest.raises(G.GtqError) as e:
+        p.layout(2, 0)
+    _expect(e, 1, "out of range")
+    with pytest.raises(G.GtqError) as e:
+        p.cache_sizes(1, 100)
+    _expect(e, 1, "multiple of 32")
+    # GPU entry points on a host-only plan fail on the host, before any launch
+    cv = G.CacheView(1, 1, 1, 1, 1, 64)
+    st = lib.gtq_decode_attn(p.handle, 0, C.byref(cv), C.c_void_p(1), C.c_void_p(1), 64, 0.1, 0,
+                             C.c_void_p(1), None, C.c_void_p(1), 1 << 20, None)
+    assert st == 1 and b"host-only" in lib.gtq_last_error()
+    st = lib.gtq_quantize_append_chunk(p.handle, 0, C.byref(cv), C.c_void_p(1), C.c_void_p(1), 0, 0, 8, None)
+    assert st == 1 and b"host-only" in lib.gtq_last_error()
+    ws = C.c_size_t(0)
+    assert lib.gtq_decode_workspace_bytes(p.handle, 2, 1000, 33, C.byref(ws)) == 1
+    assert b"multiple of 32" in lib.gtq_last_error()
+    assert lib.gtq_decode_workspace_bytes(p.handle, 2, 1000, 64, C.byref(ws)) == 0
+    # one u32 arrival counter per row tile + rows * chunks * 132 floats, each 256-byte aligned
+    tiles, rows, chunks = 2 * 2, 2 * 4, (1000 + 63) // 64
+    exp = -(-tiles * 4 // 256) * 256 + -(-rows * chunks * 132 * 4 // 256) * 256
+    assert ws.value == exp
+    assert lib.gtq_prefill_workspace_bytes(p.handle, 0, 0, 0, C.byref(ws)) == 1
+    p.destroy()
+    assert lib.gtq_plan_destroy(None) == 0

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Append: codes bit-exact except values whose oracle z lies within 1e-6 of a
+threshold (counted), fp32 norms equal or 1 ulp apart (counted). Attention:
+logits and outputs within 1e-4 + 2e-3 |ref| element-wise. Decode parity feeds the
+GPU the oracle's own packed cache (written into the library's layout), so that
+append tie cases cannot leak into it; the end-to-end tests run append then decode.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gtq_oracle as O
+from gtq_testutil import (Case, assert_close, compare_codes, compare_norms, scale_default,
+                          unpack_key_record, v_codes_from_physical, v_codes_to_physical)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import packed_cache_attention_tq_amd as G
+    G.lib()
+    return G
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def _cache_arrays(cache, case):
+    s = cache.sizes
+    B, H, cap = cache.batch, case.H, cache.capacity
+    kc = cache.k_codes.cpu().numpy().view(np.uint32).reshape(B, H, cap, s.k_words)
+    kn = cache.k_norms.cpu().numpy().reshape(B, H, cap, 4)
+    vc = cache.v_codes.cpu().numpy().view(np.uint32).reshape(B, H, cap // 8, s.v_words_per_block)
+    vn = cache.v_norms.cpu().numpy().reshape(B, H, cap)
+    return kc, kn, vc, vn
+
+
+def _check_append(case, cache, l, b, n, enc_by_head, what):
+    kc, kn, vc, vn = _cache_arrays(cache, case)
+    ties = ulps = 0
+    for h in range(case.H):
+        hp = case.heads[l, h]
+        enc = enc_by_head[h]
+        got = unpack_key_record(kc[b, h, :n], hp)
+        for gi, (r, _) in enumerate(hp.groups):
+            ties += compare_codes(got[gi], enc["k_codes"][gi], enc["k_z"][gi], r, f"{what} K group {gi} h{h}")
+            ulps += compare_norms(kn[b, h, :n, gi], enc["k_norms"][:, gi], f"{what} K norm g{gi} h{h}")
+        assert np.all(kn[b, h, :n, len(hp.groups):] == 0)
+        vg = v_codes_from_physical(vc[b, h], n, case.v_bits)
+        ties += compare_codes(vg, enc["v_codes"], enc["v_z"], case.v_bits, f"{what} V h{h}")
+        ulps += compare_norms(vn[b, h, :n], enc["v_norms"], f"{what} V norm h{h}")
+    return ties, ulps
+
+
+def _upload_oracle_cache(case, cache, l, b, n, enc_by_head):
+    """Write the oracle's packed records into the library's cache layout."""
+    s = cache.sizes
+    B, H, cap = cache.batch, case.H, cache.capacity
+    kc = cache.k_codes.cpu().numpy().view(np.uint32).reshape(B, H, cap, s.k_words).copy()
+    kn = cache.k_norms.cpu().numpy().reshape(B, H, cap, 4).copy()
+    vc = cache.v_codes.cpu().numpy().view(np.uint32).reshape(B, H, cap // 8, s.v_words_per_block).copy()
+    vn = cache.v_norms.cpu().numpy().reshape(B, H, cap).copy()
+    for h in range(H):
+        e = enc_by_head[h]
+        kc[b, h, :n] = e["k_words"]
+        kn[b, h, :n] = 0
+        kn[b, h, :n, :e["k_norms"].shape[1]] = e["k_norms"]
+        vc[b, h] = v_codes_to_physical(e["v_codes"], case.v_bits, cap // 8)
+        vn[b, h, :n] = e["v_norms"]
+    cache.k_codes.copy_(torch.from_numpy(kc.view(np.int32).reshape(-1)))
+    cache.k_norms.copy_(torch.from_numpy(kn.reshape(-1)))
+    cache.v_codes.copy_(torch.from_numpy(vc.view(np.int32).reshape(-1)))
+    cache.v_norms.copy_(torch.from_numpy(vn.reshape(-1)))
+
+
+def _oracle_decode(case, l, b, n, enc_by_head, q, scale):
+    """q [HQ, 128] -> (logits [HQ, n], out [HQ, 128])."""
+    lg = np.zeros((case.HQ, n))
+    out = np.zeros((case.HQ, 128))
+    for h in range(case.H):
+        e = enc_by_head[h]
+        sl = slice(h * case.g, (h + 1) * case.g)
+        lg[sl], out[sl] = O.decode_attention(case.heads[l, h], q[sl], e["k_words"], e["k_norms"],
+                                             e["v_words"], e["v_norms"], scale, length=n)
+    return lg, out
+
+
+def _encode(case, l, b, n):
+    return [O.encode_kv(case.heads[l, h], case.inputs[l, h][b]["k"][:n], case.inputs[l, h][b]["v"][:n])
+            for h in range(case.H)]
+
+
+# ------------------------------------------------------------------------ tests
+
+def test_config0_tiny_single_head(G):
+    """1 head, 1024 tokens, K2V2, 4 queries at position 1024 (queries go to 4 batch rows
+    holding the same cache)."""
+    _say("case: config0 tiny single head, K2V2, N=1024, 4 queries")
+    case = Case(0, 1, 1, 1, 1024, 128, 2, batch=1, n_dec_q=4)
+    plan = case.plan()
+    cache = G.PackedCache(plan, 4, 1024)
+    k, v = case.kv(0, 0)
+    kk = np.concatenate([k] * 4)
+    vv = np.concatenate([v] * 4)
+    seq_idx = np.repeat(np.arange(4, dtype=np.int32), 1024)
+    slot = np.tile(np.arange(1024, dtype=np.int64), 4)
+    G.gtq_quantize_append(plan, 0, cache, _dev(kk), _dev(vv), _dev(seq_idx), _dev(slot))
+    torch.cuda.synchronize()
+    enc = _encode(case, 0, 0, 1024)
+    ties = ulps = 0
+    for b in range(4):
+        t, u = _check_append(case, cache, 0, b, 1024, enc, f"config0 b{b}")
+        ties, ulps = ties + t, ulps + u
+    _say(f"  append ties={ties} norm-ulps={ulps}")
+    q = np.stack([case.inputs[0, 0][0]["q"][i, 0] for i in range(4)])[:, None, :]     # [4, 1, 128]
+    sc = scale_default()
+    logits = torch.full((4, 1, 1024), float("nan"), device="cuda")
+    out = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(np.full(4, 1024, np.int32)), 1024, sc,
+                            logits=logits)
+    torch.cuda.synchronize()
+    for b in range(4):
+        lg_ref, out_ref = O.decode_attention(case.heads[0, 0], q[b], enc[0]["k_words"], enc[0]["k_norms"],
+                                             enc[0]["v_words"], enc[0]["v_norms"], sc)
+        if ties == 0:
+            assert_close(logits[b].cpu().numpy(), lg_ref, f"config0 logits q{b}")
+            assert_close(out[b].cpu().numpy(), out_ref, f"config0 out q{b}")
+
+
+@pytest.mark.parametrize("chunk", [32, 96, 512, 0])
+def test_gqa_ragged_decode_on_oracle_cache(G, chunk):
+    """4 KV heads x g=4, batch 3 with lengths 1, 333, 600; split sizes 32..auto."""
+    _say(f"case: gqa ragged decode, chunk={chunk}")
+    case = Case(1, 1, 4, 4, 600, 128, 2, batch=3)
+    plan = case.plan()
+    cap = 608
+    lens = [1, 333, 600]
+    cache = G.PackedCache(plan, 3, cap)
+    encs = []
+    for b, n in enumerate(lens):
+        e = _encode(case, 0, b, n)
+        encs.append(e)
+        _upload_oracle_cache(case, cache, 0, b, n, e)
+    q = np.stack([case.q(0, b) for b in range(3)])
+    sc = scale_default()
+    logits = torch.zeros((3, case.HQ, 600), device="cuda")
+    out = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(np.array(lens, np.int32)), 600, sc, chunk=chunk,
+                            logits=logits)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        lg_ref, out_ref = _oracle_decode(case, 0, b, n, encs[b], q[b], sc)
+        assert_close(logits[b, :, :n].cpu().numpy(), lg_ref, f"logits b{b}")
+        assert_close(out[b].cpu().numpy(), out_ref, f"out b{b}")
+
+
+@pytest.mark.parametrize("k_budget,v_bits,g,layout", [(128, 1, 8, 0), (192, 3, 8, 0), (160, 4, 2, 0),
+                                                      (64, 2, 8, 0), (256, 2, 4, 0), (192, 3, 2, 1),
+                                                      (96, 1, 1, 1)])
+def test_append_and_decode_rates(G, k_budget, v_bits, g, layout):
+    """Chunked append (partial and whole value blocks) then decode, several rate mixes."""
+    _say(f"case: append+decode budget={k_budget} v_bits={v_bits} g={g} layout={layout}")
+    n = 203
+    case = Case(2, 1, 2, g, n, k_budget, v_bits, batch=1, layout=layout)
+    plan = case.plan()
+    cache = G.PackedCache(plan, 1, 224)
+    k, v = case.kv(0, 0)
+    for lo, hi in [(0, 5), (5, 77), (77, 80), (80, 203)]:
+        G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k[lo:hi]), _dev(v[lo:hi]), 0, lo)
+    torch.cuda.synchronize()
+    enc = _encode(case, 0, 0, n)
+    ties, ulps = _check_append(case, cache, 0, 0, n, enc, "chunked append")
+    _say(f"  append ties={ties} norm-ulps={ulps}")
+    _upload_oracle_cache(case, cache, 0, 0, n, enc)
+    q = case.q(0, 0)[None]
+    sc = 0.11
+    logits = torch.zeros((1, case.HQ, n), device="cuda")
+    out = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(np.array([n], np.int32)), n, sc, chunk=64,
+                            logits=logits)
+    torch.cuda.synchronize()
+    lg_ref, out_ref = _oracle_decode(case, 0, 0, n, enc, q[0], sc)
+    assert_close(logits[0].cpu().numpy(), lg_ref, "logits")
+    assert_close(out[0].cpu().numpy(), out_ref, "out")
+
+
+def test_scatter_append_random_order_and_overflow(G):
+    _say("case: scatter append in random order + overflow counting")
+    n = 150
+    case = Case(3, 2, 2, 2, n, 128, 2, batch=2)
+    plan = case.plan()
+    rng = np.random.default_rng(0)
+    for l in range(2):
+        cache = G.PackedCache(plan, 2, 160)
+        ks, vs, sq, sl = [], [], [], []
+        for b in range(2):
+            k, v = case.kv(l, b)
+            ks.append(k)
+            vs.append(v)
+            sq.append(np.full(n, b, np.int32))
+            sl.append(np.arange(n, dtype=np.int64))
+        k, v, sq, sl = map(np.concatenate, (ks, vs, sq, sl))
+        perm = rng.permutation(len(sq))
+        k, v, sq, sl = k[perm], v[perm], sq[perm], sl[perm]
+        before = plan.overflow_count()
+        # three extra tokens that must be skipped: bad slot, bad sequence, negative slot
+        k = np.concatenate([k, k[:3]])
+        v = np.concatenate([v, v[:3]])
+        sq = np.concatenate([sq, np.array([0, 2, 1], np.int32)])
+        sl = np.concatenate([sl, np.array([160, 3, -1], np.int64)])
+        G.gtq_quantize_append(plan, l, cache, _dev(k), _dev(v), _dev(sq), _dev(sl))
+        torch.cuda.synchronize()
+        assert plan.overflow_count() - before == 3
+        for b in range(2):
+            ties, _ = _check_append(case, cache, l, b, n, _encode(case, l, b, n), f"scatter l{l} b{b}")
+            if ties == 0:
+                q = case.q(l, b)[None]
+                lens = np.array([n, n], np.int32)
+                out = G.gtq_decode_attn(plan, l, cache, _dev(np.concatenate([q, q])), _dev(lens), n,
+                                        scale_default())
+                torch.cuda.synchronize()
+                _, out_ref = _oracle_decode(case, l, b, n, _encode(case, l, b, n), q[0], scale_default())
+                assert_close(out[b].cpu().numpy(), out_ref, f"end-to-end out l{l} b{b}")
+
+
+def test_prefill_chunk(G):
+    """g = 5 (Qwen2.5-32B ratio): append 176 tokens, then a 60-token chunk appended and
+    attended causally over the packed cache."""
+    _say("case: chunked prefill g=5")
+    n0, T = 176, 60
+    case = Case(4, 1, 2, 5, n0 + T, 192, 2, batch=1)
+    plan = case.plan()
+    cache = G.PackedCache(plan, 1, 256)
+    k, v = case.kv(0, 0)
+    enc = _encode(case, 0, 0, n0 + T)
+    _upload_oracle_cache(case, cache, 0, 0, n0 + T, enc)
+    rng = np.random.default_rng(5)
+    q = (rng.standard_normal((T, case.HQ, 128)) * 3).astype(np.float32)
+    sc = scale_default()
+    out = G.gtq_prefill_attn(plan, 0, cache, _dev(q), 0, n0, sc, chunk=64)
+    torch.cuda.synchronize()
+    for h in range(case.H):
+        sl = slice(h * 5, h * 5 + 5)
+        ref = O.prefill_attention(case.heads[0, h], q[:, sl], n0, enc[h]["k_words"], enc[h]["k_norms"],
+                                  enc[h]["v_words"], enc[h]["v_norms"], sc)
+        assert_close(out[:, sl].cpu().numpy(), ref, f"prefill out h{h}")
+    # and the same after the library's own chunk append of the prompt chunk
+    G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k[n0:]), _dev(v[n0:]), 0, n0)
+    torch.cuda.synchronize()
+    ties, _ = _check_append(case, cache, 0, 0, n0 + T, enc, "prefill-chunk append")
+    assert ties == 0 or ties < 3
+
+
+def test_edge_cases(G):
+    """Zero vectors (norm 0, codes 2^(b-1)), sequences of length 0 and 1, determinism."""
+    _say("case: edge cases")
+    n = 40
+    case = Case(5, 1, 1, 4, n, 128, 3, batch=3)
+    plan = case.plan()
+    cache = G.PackedCache(plan, 3, 64)
+    k, v = case.kv(0, 0)
+    k[7] = 0
+    v[9] = 0
+    k[11, :, :] = 0
+    G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k), _dev(v), 0, 0)
+    G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k[:1]), _dev(v[:1]), 2, 0)
+    torch.cuda.synchronize()
+    kc, kn, vc, vn = _cache_arrays(cache, case)
+    assert np.all(kn[0, 0, 7] == 0) and np.all(vn[0, 0, 9] == 0)
+    hp = case.heads[0, 0]
+    codes = unpack_key_record(kc[0, 0, 7:8], hp)
+    for (r, _), cg in zip(hp.groups, codes):
+        assert np.all(cg == (1 << (r - 1)))
+    assert np.all(v_codes_from_physical(vc[0, 0], 10, 3)[9] == 4)
+    q = np.stack([case.q(0, 0)] * 3)
+    lens = np.array([n, 0, 1], np.int32)
+    o1 = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(lens), 64, scale_default(), chunk=32)
+    o2 = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(lens), 64, scale_default(), chunk=32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.all(o1[1] == 0)
+    vhat = O.dequantized_values(hp, O.encode_kv(hp, k[:1, 0], v[:1, 0])["v_words"],
+                                O.encode_kv(hp, k[:1, 0], v[:1, 0])["v_norms"])
+    assert_close(o1[2].cpu().numpy(), np.repeat(vhat, 4, axis=0), "length-1 sequence returns its value")
+    _, ref = _oracle_decode(case, 0, 0, n, [O.encode_kv(hp, k[:, 0], v[:, 0])], q[0], scale_default())
+    assert_close(o1[0].cpu().numpy(), ref, "zero-vector sequence")
