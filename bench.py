@@ -3,14 +3,15 @@
 One step = one decode step of one Llama-3.1-8B-shaped attention layer at batch 1:
 quantize-append the step's new key/value token (8 KV heads) into the packed cache,
 then split-K packed decode attention of the 32 query heads over the 32768 cached
-tokens (rotated queries, partials, log-sum-exp merge and inverse value rotation in
-one kernel). Inputs are seeded synthetic tensors with the pages' distributions,
+tokens (one kernel for the rotated queries and the per-split online-softmax partials,
+one for the log-sum-exp merge and inverse value rotation). Inputs are seeded synthetic tensors with the pages' distributions,
 resident in HBM before timing. The cache is replicated into --copies layer caches
 that the steps cycle through (as a 32-layer stack would), so that each step reads
 its cache from HBM rather than from the 256 MB last-level cache.
 
-Prints one JSON line (metric, value = KV tokens/s, roofline of the attention kernel
-measured with HIP events around each launch in the timed region, cpu_baseline = the
+Prints one JSON line (metric, value = KV tokens/s, roofline of the attention
+(partials) kernel measured with HIP events around each of its launches in the timed
+region, cpu_baseline = the
 fp64 oracle timed on a bounded slice of the same workload on this host).
 """
 from __future__ import annotations
@@ -142,7 +143,7 @@ def main():
     q = torch.from_numpy(w["q"]).to(dev)
     seq_len = torch.full((1,), n, dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
-    ws = torch.zeros(G.gtq_decode_workspace_bytes(plan, 1, n, args.chunk), dtype=torch.uint8, device=dev)
+    ws = torch.empty(G.gtq_decode_workspace_bytes(plan, 1, n, args.chunk), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(128)
     stream = torch.cuda.current_stream()
 
@@ -151,10 +152,10 @@ def main():
         G.gtq_quantize_append(plan, 0, c, k_new, v_new, seq_idx, slot, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        G.gtq_decode_attn(plan, 0, c, q, seq_len, n, scale, chunk=args.chunk, out=out, workspace=ws,
-                          stream=stream)
+        G.gtq_decode_attn_partials(plan, 0, c, q, seq_len, n, scale, ws, chunk=args.chunk, stream=stream)
         if ev is not None:
             ev[1].record(stream)
+        G.gtq_decode_attn_merge(plan, 0, c, seq_len, n, out, ws, chunk=args.chunk, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -177,10 +178,10 @@ def main():
     ms_per_step = total_ms / args.steps
     value = n / (ms_per_step / 1e3)
 
-    # algorithmic bytes of one attention launch: the packed records of every attended
-    # (token, KV head) + per-head rotations and queries/outputs
+    # algorithmic bytes of one launch of the attention (partials) kernel: the packed
+    # records of every attended (token, KV head), the key-group rotations, the queries
     krot_bytes = sum(sum(int(np.prod(m.shape)) for m in hh) for hh in w["krot"][0]) * 4
-    alg_bytes = n * h_kv * sizes.bytes_per_token + krot_bytes + h_kv * 128 * 128 * 4 + 2 * hq * 128 * 4
+    alg_bytes = n * h_kv * sizes.bytes_per_token + krot_bytes + hq * 128 * 4
     kern_avg = float(kern_ms.mean())
     achieved = alg_bytes / (kern_avg / 1e3) / 1e9
     res = {
@@ -202,7 +203,7 @@ def main():
                    "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "attn_kernel<2>", "kernel_avg_us": round(kern_avg * 1e3, 3),
+                     "kernel": "attn_partials_kernel<2>", "kernel_avg_us": round(kern_avg * 1e3, 3),
                      "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
                      "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
                      "alg_bytes_per_launch": int(alg_bytes)},

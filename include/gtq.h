@@ -219,10 +219,9 @@ gtq_status gtq_quantize_append_chunk(const gtq_plan* plan, int32_t layer,
 
 /* Workspace bytes that gtq_decode_attn needs for `batch` sequences of at most
  * max_len cached tokens with split size `chunk` (0 = automatic; else a multiple of
- * 32). The workspace holds the split-K partials and one arrival counter per row tile:
- * it must be zero-filled before its first use, and every completed call leaves the
- * counters at zero again, so one workspace can serve any later decode or prefill
- * call whose size fits. Calls that share a workspace must be ordered on one stream. */
+ * 32, at most 256 splits per sequence). The workspace holds the split-K partials
+ * (m, l, acc[128] per query row and split); its contents need no initialisation.
+ * Calls that share a workspace must be ordered on one stream. */
 gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64_t max_len,
                                       int32_t chunk, size_t* out);
 
@@ -239,17 +238,32 @@ gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64
  * Logit of token n, query head h: scale * sum_g nu_{n,g} / sqrt(d_g) *
  * sum_{i in g} (Pi_g q_g)_i C_{b_g}[code_{n,i}]; softmax over n < seq_len; output
  * Pi_V^T sum_n p_n nu^V_n C_{b_V}[vcode_n] / sqrt(128). Split-K over `chunk`-token
- * pieces with a log-sum-exp merge, all in one kernel launch (the last workgroup of a
- * row tile merges). A sequence with seq_len 0 gets a zero output.
- * Errors: EINVAL (NULL, layer, scale not finite, chunk not a multiple of 32, host-only
- * plan, max_len < 0); ECAPACITY (workspace too small, max_len > capacity). */
+ * pieces (gtq_decode_attn_partials) followed by a log-sum-exp merge and the inverse
+ * value rotation (gtq_decode_attn_merge). A sequence with seq_len 0 gets a zero output.
+ * Errors: EINVAL (NULL, layer, scale not finite, chunk not a multiple of 32 or more than
+ * 256 splits, host-only plan, max_len < 0); ECAPACITY (workspace too small,
+ * max_len > capacity). */
 gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
                            const float* q, const int32_t* seq_len, int64_t max_len,
                            float softmax_scale, int32_t chunk, float* out, float* logits,
                            void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* The two phases of gtq_decode_attn, for callers that interleave other work between
+ * them or time them separately. The partials phase writes, per query row and split, the
+ * running maximum m (base 2), the sum l of 2^(logit*log2(e) - m) and the accumulator of
+ * p * nu_V * C[vcode] in the value rotation's basis into the workspace; the merge phase
+ * reads them with the same (seq_len, max_len, chunk) and writes `out`. Arguments and
+ * errors as for gtq_decode_attn. */
+gtq_status gtq_decode_attn_partials(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                    const float* q, const int32_t* seq_len, int64_t max_len,
+                                    float softmax_scale, int32_t chunk, float* logits,
+                                    void* workspace, size_t ws_bytes, void* hip_stream);
+gtq_status gtq_decode_attn_merge(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                 const int32_t* seq_len, int64_t max_len, int32_t chunk, float* out,
+                                 const void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Workspace bytes for gtq_prefill_attn on a chunk of n_tok queries whose last
- * position is pos0 + n_tok - 1 (same zero-fill contract as the decode workspace). */
+ * position is pos0 + n_tok - 1 (no initialisation needed). */
 gtq_status gtq_prefill_workspace_bytes(const gtq_plan* plan, int64_t pos0, int64_t n_tok,
                                        int32_t chunk, size_t* out);
 

@@ -84,6 +84,11 @@ _SIGS = [
     ("gtq_decode_attn", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_void_p,
                                     C.c_int64, C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("gtq_decode_attn_partials", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p,
+                                             C.c_void_p, C.c_int64, C.c_float, C.c_int32, C.c_void_p,
+                                             C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("gtq_decode_attn_merge", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_int64,
+                                          C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     ("gtq_prefill_workspace_bytes", C.c_int32, [C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
                                                 C.POINTER(C.c_size_t)]),
     ("gtq_prefill_attn", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_int32,
@@ -291,7 +296,7 @@ def gtq_decode_attn(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_
         out = torch.empty_like(q)
     if workspace is None:
         nb = gtq_decode_workspace_bytes(plan, cache.batch, max_len, chunk)
-        workspace = torch.zeros(nb, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
     cv = cache.view()
     st = lib().gtq_decode_attn(plan.handle, layer, C.byref(cv), _dev(q, torch.float32, "q"),
                                _dev(seq_len, torch.int32, "seq_len"), max_len, float(scale), chunk,
@@ -299,6 +304,27 @@ def gtq_decode_attn(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_
                                _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
                                _stream(stream))
     _check(st, "gtq_decode_attn")
+    return out
+
+
+def gtq_decode_attn_partials(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_len: int,
+                             scale: float, workspace, chunk: int = 0, logits=None, stream=None):
+    cv = cache.view()
+    st = lib().gtq_decode_attn_partials(plan.handle, layer, C.byref(cv), _dev(q, torch.float32, "q"),
+                                        _dev(seq_len, torch.int32, "seq_len"), max_len, float(scale), chunk,
+                                        _dev(logits, torch.float32, "logits"), _dev(workspace, None, "workspace"),
+                                        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gtq_decode_attn_partials")
+
+
+def gtq_decode_attn_merge(plan: Plan, layer: int, cache: PackedCache, seq_len, max_len: int, out, workspace,
+                          chunk: int = 0, stream=None):
+    cv = cache.view()
+    st = lib().gtq_decode_attn_merge(plan.handle, layer, C.byref(cv), _dev(seq_len, torch.int32, "seq_len"),
+                                     max_len, chunk, _dev(out, torch.float32, "out"),
+                                     _dev(workspace, None, "workspace"),
+                                     workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gtq_decode_attn_merge")
     return out
 
 
@@ -316,7 +342,7 @@ def gtq_prefill_attn(plan: Plan, layer: int, cache: PackedCache, q, seq: int, po
         out = torch.empty_like(q)
     if workspace is None:
         nb = gtq_prefill_workspace_bytes(plan, pos0, n, chunk)
-        workspace = torch.zeros(nb, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
     cv = cache.view()
     st = lib().gtq_prefill_attn(plan.handle, layer, C.byref(cv), _dev(q, torch.float32, "q"), seq, pos0, n,
                                 float(scale), chunk, _dev(out, torch.float32, "out"),

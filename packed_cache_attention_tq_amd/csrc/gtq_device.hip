@@ -462,7 +462,11 @@ __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
 // o = Pi_V^T o_rot / sqrt(128).
 // ============================================================================
 
-constexpr int kWaves = 4;
+constexpr int kMaxArgHeads = 64;   // KV heads per layer the attention kernels accept
+constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPS = 132;           // partial record: m, l, 2 pad, acc[128] (16-byte aligned acc)
+constexpr int kMaxChunks = 256;    // splits per row
 
 struct AttnArgs {
   const DevHead* heads;
@@ -473,11 +477,9 @@ struct AttnArgs {
   const uint32_t* v_codes;
   const float* v_norms;
   const float* q;          // [rows][128]
-  float* out;              // [rows][128]
   float* logits;           // decode only, optional
   const int32_t* seq_len;  // decode
-  float* partials;         // [rows][n_chunks][130]
-  uint32_t* counters;      // [n_tiles]
+  float* partials;         // [rows][n_chunks][kPS]
   int64_t capacity;
   int64_t logits_ld;
   int64_t pos0;            // prefill
@@ -489,24 +491,42 @@ struct AttnArgs {
   int32_t chunk;           // tokens per split (multiple of 32)
   int32_t n_chunks;
   int32_t max_len;         // decode clamp
+  int32_t region_bytes;    // size of the phase region of shared memory
   float qscale;            // softmax scale * log2(e)
+  float cbv[4][16];        // centroids of rates 1..4 (binary16 values)
+  int64_t krot_off[kMaxArgHeads];   // per KV head of the layer: float offset of its key rotations
+  int32_t krot_n[kMaxArgHeads];     // and their size (floats)
 };
 
-struct AttnLds {
+// Shared memory: fixed tables, then one region that the prologue (key rotations,
+// query rows), the main loop (per-wave key tiles and norms) and the epilogue
+// (partial rows of the waves) use in turn.
+struct AttnFixed {
   uint32_t lut1[256][4];  // 1-bit: byte -> 8 binary16 centroids
   uint32_t lut2[256][2];  // 2-bit: byte -> 4
   uint32_t lut3[64];      // 3-bit: 6 bits -> 2
   uint32_t lut4[256];     // 4-bit: byte -> 2
-  uint4 qb[kMaxKB][4][16];            // B operand of QK per K-block / lane
-  uint32_t ktile[kWaves][kBlk * 16 + 16];
-  float kn[kWaves][kBlk * kNS];
+  uint4 qb[kMaxKB][4][16];  // B operand of QK per K-block / lane
   float om[kWaves][8];
   float ol[kWaves][8];
-  float oacc[kWaves][8][kD];          // also holds the query rows and the merged rows
   int32_t row_id[8];
   int32_t row_len[8];
-  int32_t last;
+  DevHead hd;             // this KV head's tables, copied from global memory
+  float oacc_scratch[8][kD];  // query rows as loaded (prologue)
 };
+struct AttnWave {
+  uint32_t ktile[kBlk * 17 + 16];  // 32 key records at an odd pitch (kw + 1 words)
+  float kn[kBlk * kNS];
+  float vn[kBlk];
+};
+
+size_t attn_region_bytes(int krot_floats) {
+  // rotations at row pitch d + 1 (at most sum_g d_g extra floats) + 8 query rows
+  const size_t pro = ((size_t)krot_floats + kD + 4) * 4 + 8 * kD * 4;
+  const size_t mainb = kWaves * sizeof(AttnWave);
+  const size_t epi = (kWaves / 2) * 8 * kD * 4;
+  return std::max(pro, std::max(mainb, epi));
+}
 
 __device__ inline uint32_t pack2h(float a, float b) {
   const _Float16 ha = (_Float16)a, hb = (_Float16)b;
@@ -524,7 +544,7 @@ union H8 {
 };
 
 template <int RATE>
-__device__ inline half8 dequant8(const AttnLds& S, uint32_t F) {
+__device__ inline half8 dequant8(const AttnFixed& S, uint32_t F) {
   H8 r;
   if (RATE == 1) {
     r.v = *reinterpret_cast<const uint4*>(S.lut1[F & 0xFF]);
@@ -550,23 +570,36 @@ __device__ inline half8 dequant8(const AttnLds& S, uint32_t F) {
 }
 
 template <int RATE>
-__device__ inline void qk_group(const AttnLds& S, const uint32_t* kt, int kw, int kb0, int nkb,
+__device__ inline void qk_group(const AttnFixed& S, const uint32_t* kt, int kw, int kb0, int nkb,
                                 const int32_t* kb_bit, int q, int n, floatx4& d0, floatx4& d1) {
   // A-row n of the two 16-token halves holds tokens 8(n/4) + n%4 and that + 4
   const int tau0 = 8 * (n >> 2) + (n & 3);
   const int tau1 = tau0 + 4;
-  const uint32_t* r0 = kt + tau0 * kw;
-  const uint32_t* r1 = kt + tau1 * kw;
-  for (int i = 0; i < nkb; ++i) {
-    const int kbi = kb0 + i;
-    H8 qbv;
-    qbv.v = S.qb[kbi][q][n];
-    const int bit = kb_bit[kbi] + 8 * q * RATE;
-    const int w = bit >> 5, s = bit & 31;
-    const uint32_t f0 = __builtin_amdgcn_alignbit(r0[w + 1], r0[w], s);
-    const uint32_t f1 = __builtin_amdgcn_alignbit(r1[w + 1], r1[w], s);
-    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<RATE>(S, f0), qbv.h, d0, 0, 0, 0);
-    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<RATE>(S, f1), qbv.h, d1, 0, 0, 0);
+  const uint32_t* r0 = kt + tau0 * (kw + 1);
+  const uint32_t* r1 = kt + tau1 * (kw + 1);
+  // a group has at most 4 K-blocks of 32 coordinates: gather every operand first so
+  // that the LDS reads of all K-blocks are in flight together, then multiply
+  H8 qbv[4];
+  half8 a0[4], a1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < nkb) {
+      const int kbi = kb0 + i;
+      qbv[i].v = S.qb[kbi][q][n];
+      const int bit = kb_bit[kbi] + 8 * q * RATE;
+      const int w = bit >> 5, s = bit & 31;
+      const uint32_t f0 = __builtin_amdgcn_alignbit(r0[w + 1], r0[w], s);
+      const uint32_t f1 = __builtin_amdgcn_alignbit(r1[w + 1], r1[w], s);
+      a0[i] = dequant8<RATE>(S, f0);
+      a1[i] = dequant8<RATE>(S, f1);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < nkb) {
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[i], qbv[i].h, d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[i], qbv[i].h, d1, 0, 0, 0);
+    }
   }
 }
 
@@ -581,23 +614,23 @@ __device__ inline uint32_t vfield(const uint32_t (&vw)[2 * VB], int t) {
   return __builtin_amdgcn_alignbit(vw[w + 1], vw[w], s);
 }
 
-constexpr int kPS = 132;          // partial record: m, l, 2 pad, acc[128] (16-byte aligned acc)
-constexpr int kMaxChunks = 256;   // splits per row (bounded by the merge's LDS weights)
-
+template <int VB>
 struct BlockRegs {
-  uint32_t kr[8];   // key codes: words lane + 64 i of the 32-token tile
-  float2 kn;        // key norms: floats 2 lane, 2 lane + 1 of the tile
-  uint32_t vw[8];   // value codes of 8 tokens x coordinates 8n..8n+7 (2 VB words)
-  float4 vn0, vn1;  // value norms of tokens 8q..8q+7
+  uint32_t kr[8];       // key codes: words lane + 64 i of the 32-token tile
+  float2 kn;            // key norms: floats 2 lane, 2 lane + 1 of the tile
+  uint32_t vw[2 * VB];  // value codes of 8 tokens x coordinates 8n..8n+7
+  float vn;             // value norm of token (lane & 31)
 };
 
+// Every load is unconditional (addresses clamped inside the block) so that the
+// compiler can count the loads in flight and overlap the next block with this one.
 template <int VB>
-__device__ inline void load_block(BlockRegs& B, const uint32_t* kc, const float* knp, const uint32_t* vc,
+__device__ inline void load_block(BlockRegs<VB>& B, const uint32_t* kc, const float* knp, const uint32_t* vc,
                                   const float* vnp, int t0, int kw, int lane, int q, int n) {
   const uint32_t* ks = kc + (size_t)t0 * kw;
+  const int last = kBlk * kw - 1;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (lane + 64 * i < kBlk * kw) B.kr[i] = ks[lane + 64 * i];
+  for (int i = 0; i < 8; ++i) B.kr[i] = ks[min(lane + 64 * i, last)];
   B.kn = *reinterpret_cast<const float2*>(knp + (size_t)t0 * kNS + 2 * lane);
   const uint32_t* src = vc + ((size_t)(t0 / GTQ_VBLOCK) + q) * (32 * VB) + n * (2 * VB);
   if (VB == 2) {
@@ -612,21 +645,22 @@ __device__ inline void load_block(BlockRegs& B, const uint32_t* kc, const float*
 #pragma unroll
     for (int i = 0; i < 2 * VB; ++i) B.vw[i] = src[i];
   }
-  B.vn0 = *reinterpret_cast<const float4*>(vnp + t0 + 8 * q);
-  B.vn1 = *reinterpret_cast<const float4*>(vnp + t0 + 8 * q + 4);
+  B.vn = vnp[t0 + (lane & 31)];
 }
 
+// Phase 1 of the attention: per (row tile, chunk) online-softmax partials.
 template <int VB>
-__global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
-  extern __shared__ __align__(16) float rotk_t[];  // this head's key rotations, [g][j][i]
-  __shared__ AttnLds S;
+__global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  AttnFixed& S = *reinterpret_cast<AttnFixed*>(smem);
+  unsigned char* region = smem + ((sizeof(AttnFixed) + 15) & ~(size_t)15);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, n = lane & 15;
   const int chunk_idx = blockIdx.x;
   const int tile = blockIdx.y;
 
-  // ---- tile -> (sequence, KV head, rows)
+  // ---- tile -> (sequence, KV head, rows); row ids need no global data
   int seq, h, tr;
   if (a.prefill) {
     h = tile / a.tiles_per_kv;
@@ -638,6 +672,45 @@ __global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
     h = rem / a.tiles_per_kv;
     tr = rem - h * a.tiles_per_kv;
   }
+  // ---- one round of independent global loads: head table, rotations, query rows,
+  //      sequence length and this wave's first cache block
+  constexpr int kHeadWords = (int)(sizeof(DevHead) / 4);
+  const uint32_t hword = tid < kHeadWords ? reinterpret_cast<const uint32_t*>(a.heads + h)[tid] : 0u;
+  const int krot_n = a.krot_n[h];
+  const float4* rsrc = reinterpret_cast<const float4*>(a.rot + a.krot_off[h]);
+  constexpr int kRotRegs = 8;  // rotations up to 8192 floats arrive in this round
+  float4 rreg[kRotRegs];
+  const int nf4 = krot_n >> 2;
+#pragma unroll
+  for (int u = 0; u < kRotRegs; ++u) rreg[u] = rsrc[min(tid + kThreads * u, nf4 - 1)];
+  float4 qreg;
+  {
+    const int r = tid >> 5, c4 = tid & 31, f = tr * 8 + r;
+    int id = -1;
+    if (a.prefill) {
+      if (f < a.n_tok * a.g) id = (f / a.g) * a.n_q + h * a.g + (f % a.g);
+    } else if (f < a.g) {
+      id = seq * a.n_q + h * a.g + f;
+    }
+    const int idc = id >= 0 ? id : 0;  // row 0 always exists; unused rows are zeroed below
+    qreg = reinterpret_cast<const float4*>(a.q + (size_t)idc * kD)[c4];
+    if (id < 0) qreg = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int len_ld = a.prefill ? 0 : a.seq_len[seq];
+  const size_t sh = (size_t)seq * a.n_kv + h;
+  const int kw = a.k_words;
+  const uint32_t* kc = a.k_codes + sh * a.capacity * kw;
+  const float* knp = a.k_norms + sh * a.capacity * kNS;
+  const uint32_t* vc = a.v_codes + sh * (a.capacity / GTQ_VBLOCK) * (32 * VB);
+  const float* vnp = a.v_norms + sh * a.capacity;
+  const int c0 = chunk_idx * a.chunk;
+  BlockRegs<VB> cur;
+  int t0 = c0 + kBlk * wave;
+  // loads of the first block (clamped to the last block of the cache; unused if outside
+  // the tile's tokens)
+  load_block<VB>(cur, kc, knp, vc, vnp, (int)min<int64_t>(t0, a.capacity - kBlk), kw, lane, q, n);
+
+  if (tid < kHeadWords) reinterpret_cast<uint32_t*>(&S.hd)[tid] = hword;
   if (tid < 8) {
     const int f = tr * 8 + tid;
     int id = -1, len = 0;
@@ -649,98 +722,103 @@ __global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
       }
     } else if (f < a.g) {
       id = seq * a.n_q + h * a.g + f;
-      len = min(max(a.seq_len[seq], 0), a.max_len);
+      len = min(max(len_ld, 0), a.max_len);
     }
     S.row_id[tid] = id;
     S.row_len[tid] = len;
+  }
+  // decode tables from the kernel arguments
+  {
+    const int idx = tid;  // 256 threads, 256 entries
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      S.lut1[idx][k] = pack2h(a.cbv[0][(idx >> (2 * k)) & 1], a.cbv[0][(idx >> (2 * k + 1)) & 1]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      S.lut2[idx][k] = pack2h(a.cbv[1][(idx >> (4 * k)) & 3], a.cbv[1][(idx >> (4 * k + 2)) & 3]);
+    if (idx < 64) S.lut3[idx] = pack2h(a.cbv[2][idx & 7], a.cbv[2][(idx >> 3) & 7]);
+    S.lut4[idx] = pack2h(a.cbv[3][idx & 15], a.cbv[3][(idx >> 4) & 15]);
+    for (int e = tid; e < kMaxKB * 64; e += kThreads) (&S.qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
   int tile_len = 0;
 #pragma unroll
   for (int r = 0; r < 8; ++r) tile_len = max(tile_len, S.row_len[r]);
-  const int c0 = chunk_idx * a.chunk;
-  if (c0 >= tile_len) {
-    // nothing cached for this chunk; an all-empty tile still owes zero outputs
-    if (tile_len == 0 && chunk_idx == 0) {
-      for (int e = tid; e < 8 * kD; e += 256) {
-        const int id = S.row_id[e >> 7];
-        if (id >= 0) a.out[(size_t)id * kD + (e & 127)] = 0.f;
-      }
-    }
-    return;
-  }
-  const DevHead& hd = a.heads[h];
+  if (c0 >= tile_len) return;  // no cached token of this tile in this chunk
+  const DevHead& hd = S.hd;
   const int c1 = min(c0 + a.chunk, tile_len);
-  const size_t sh = (size_t)seq * a.n_kv + h;
-  const int kw = a.k_words;
-  const uint32_t* kc = a.k_codes + sh * a.capacity * kw;
-  const float* knp = a.k_norms + sh * a.capacity * kNS;
-  const uint32_t* vc = a.v_codes + sh * (a.capacity / GTQ_VBLOCK) * (32 * VB);
-  const float* vnp = a.v_norms + sh * a.capacity;
+  const int n_groups = hd.n_groups;
 
-  // ---- first block of this wave: loads issued before the prologue
-  BlockRegs cur;
-  int t0 = c0 + kBlk * wave;
-  if (t0 < c1) load_block<VB>(cur, kc, knp, vc, vnp, t0, kw, lane, q, n);
-
-  float(*qrow)[kD] = S.oacc[0];  // 8 query rows, until the main loop starts
-  // ---- prologue: key rotations (transposed) and query rows into LDS, decode tables
+  float* rotk_t = reinterpret_cast<float*>(region);  // per group: rows of Pi_g at pitch d + 1
+  float(*qrec)[kD] = reinterpret_cast<float(*)[kD]>(region + ((size_t)krot_n + kD + 4) * 4);
+  // ---- key rotations into LDS, row-major at row pitch d + 1; query rows in record order
+  int gbase[kMaxGroups], gpad[kMaxGroups];  // per group: float offset in global slice / in LDS
   {
-    const float4* src = reinterpret_cast<const float4*>(a.rot + hd.krot_off[0]);
-    const int nf4 = hd.krot_floats >> 2;
-    for (int e4 = tid; e4 < nf4; e4 += 256) {
-      const float4 x = src[e4];
-      const float xs[4] = {x.x, x.y, x.z, x.w};
+    int gb = 0, gp = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int e = 4 * e4 + u, base = 0, g = 0;
+    for (int g = 0; g < kMaxGroups; ++g) {
+      gbase[g] = gb;
+      gpad[g] = gp;
+      const int d = g < n_groups ? hd.dim[g] : 0;
+      gb += d * d;
+      gp += d * (d + 1);
+    }
+  }
+  for (int u = 0; u < 16; ++u) {
+    const int e4 = tid + kThreads * u;
+    if (e4 < (krot_n >> 2)) {
+      float4 x4;
+      if (u < kRotRegs) {
 #pragma unroll
-        for (int gg = 0; gg < kMaxGroups - 1; ++gg) {
-          const int sz = hd.dim[gg] * hd.dim[gg];
-          if (g == gg && gg < hd.n_groups - 1 && e >= base + sz) {  // scan forward from group 0
-            base += sz;
-            g = gg + 1;
-          }
-        }
-        const int d = hd.dim[g], idx = e - base;
-        const int i = idx / d, j = idx - i * d;
-        rotk_t[base + j * d + i] = xs[u];
+        for (int v = 0; v < kRotRegs; ++v)
+          if (v == u) x4 = rreg[v];
+      } else {
+        x4 = rsrc[e4];  // larger rotations: a second round
+      }
+      const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int e = 4 * e4 + v4;
+        int g = 0;
+#pragma unroll
+        for (int gg = 1; gg < kMaxGroups; ++gg)
+          if (gg < n_groups && e >= gbase[gg]) g = gg;
+        const int d = hd.dim[g], idx = e - gbase[g];
+        const int i = idx / d;
+        rotk_t[gpad[g] + idx + i] = xs[v4];  // (i, j) at i (d + 1) + j
       }
     }
-    for (int e = tid; e < 8 * kD; e += 256) {
-      const int id = S.row_id[e >> 7];
-      qrow[e >> 7][e & 127] = id >= 0 ? a.q[(size_t)id * kD + (e & 127)] : 0.f;
-    }
-    const float* c1b = a.cb->c[1];
-    const float* c2b = a.cb->c[2];
-    const float* c3b = a.cb->c[3];
-    const float* c4b = a.cb->c[4];
-    const int idx = tid;  // 256 threads, 256 entries
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      S.lut1[idx][k] = pack2h(c1b[(idx >> (2 * k)) & 1], c1b[(idx >> (2 * k + 1)) & 1]);
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      S.lut2[idx][k] = pack2h(c2b[(idx >> (4 * k)) & 3], c2b[(idx >> (4 * k + 2)) & 3]);
-    if (idx < 64) S.lut3[idx] = pack2h(c3b[idx & 7], c3b[(idx >> 3) & 7]);
-    S.lut4[idx] = pack2h(c4b[idx & 15], c4b[(idx >> 4) & 15]);
-    for (int e = tid; e < kMaxKB * 64; e += 256) (&S.qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
+  }
+  {
+    float* qraw = &S.oacc_scratch[0][0];
+    reinterpret_cast<float4*>(qraw)[tid] = qreg;  // [8][128] rows as loaded
   }
   __syncthreads();
+  for (int e = tid; e < 8 * kD; e += kThreads) qrec[e >> 7][e & 127] = S.oacc_scratch[e >> 7][hd.coord[e & 127]];
+  __syncthreads();
   // ---- rotated queries into the QK B operand (column r: high part, 15-r: low part)
-  for (int e = tid; e < 8 * kD; e += 256) {
+  for (int e = tid; e < 8 * kD; e += kThreads) {
     const int r = e >> 7, p = e & 127;
     if (S.row_id[r] < 0) continue;
-    int g = 0, base = 0;
+    int g = 0;
 #pragma unroll
     for (int gg = 1; gg < kMaxGroups; ++gg)
-      if (gg < hd.n_groups && p >= hd.pos_off[gg]) g = gg;
-    for (int gg = 0; gg < g; ++gg) base += hd.dim[gg] * hd.dim[gg];
+      if (gg < n_groups && p >= hd.pos_off[gg]) g = gg;
+    int base = 0;
+#pragma unroll
+    for (int gg = 0; gg < kMaxGroups; ++gg)
+      if (gg == g) base = gpad[gg];
     const int d = hd.dim[g], i = p - hd.pos_off[g];
-    const float* rt = rotk_t + base + i;
-    const uint8_t* co = hd.coord + hd.pos_off[g];
-    float acc = 0.f;
-    for (int j = 0; j < d; ++j) acc = fmaf(rt[j * d], qrow[r][co[j]], acc);
+    const float* rt = rotk_t + base + i * (d + 1);  // row i of Pi_g
+    const float* xq = qrec[r] + hd.pos_off[g];
+    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+    int j = 0;
+    for (; j + 4 <= d; j += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc4[u] = fmaf(rt[j + u], xq[j + u], acc4[u]);
+    }
+    for (; j < d; ++j) acc4[0] = fmaf(rt[j], xq[j], acc4[0]);
+    const float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     const float val = acc * (a.qscale / sqrtf((float)d));
     const _Float16 hi = (_Float16)val;
     const _Float16 lo = (_Float16)(val - (float)hi);
@@ -750,12 +828,15 @@ __global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
     bh[kp & 7] = hi;
     bl[kp & 7] = lo;
   }
-  __syncthreads();
+  __syncthreads();  // the prologue part of the region is free from here on
 
   const int my_row = n < 8 ? n : 15 - n;
   const int my_len = S.row_len[my_row];
-  uint32_t* kt = S.ktile[wave];
-  float* kn = S.kn[wave];
+  const int inv_kw = (65536 + kw - 1) / kw;  // floor(lw * inv_kw / 2^16) == lw / kw for lw < 512
+  AttnWave& W = reinterpret_cast<AttnWave*>(region)[wave];
+  uint32_t* kt = W.ktile;
+  float* kn = W.kn;
+  float* vnl = W.vn;
 
   floatx4 oacc[8];
 #pragma unroll
@@ -763,50 +844,43 @@ __global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   for (; t0 < c1; t0 += kBlk * kWaves) {
-    BlockRegs nxt;
+    BlockRegs<VB> nxt;
     const int tn = t0 + kBlk * kWaves;
-    if (tn < c1) load_block<VB>(nxt, kc, knp, vc, vnp, tn, kw, lane, q, n);
-    // ---- stage this block's key codes and norms in LDS
+    // next block (this block again if none is left: same addresses, cached)
+    load_block<VB>(nxt, kc, knp, vc, vnp, tn < c1 ? tn : t0, kw, lane, q, n);
+    // ---- stage this block's key codes (pitch kw + 1) and norms, value norms in LDS
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (lane + 64 * i < kBlk * kw) kt[lane + 64 * i] = cur.kr[i];
+    for (int i = 0; i < 8; ++i) {
+      const int lw = lane + 64 * i;
+      if (lw < kBlk * kw) kt[lw + ((lw * inv_kw) >> 16)] = cur.kr[i];  // + token index
+    }
     kn[2 * lane] = cur.kn.x;
     kn[2 * lane + 1] = cur.kn.y;
-    const float vn[8] = {cur.vn0.x, cur.vn0.y, cur.vn0.z, cur.vn0.w,
-                         cur.vn1.x, cur.vn1.y, cur.vn1.z, cur.vn1.w};
+    if (lane < 32) vnl[lane] = cur.vn;
     __builtin_amdgcn_wave_barrier();
 
-    // ---- QK per key group
-    floatx4 dg[kMaxGroups][2];
+    // ---- QK per key group, folded into the logits of tokens 8q + j (j = 4*half + e)
+    float lg[8];
 #pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g) dg[g][0] = dg[g][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) lg[j] = 0.f;
     int kb0 = 0;
 #pragma unroll
     for (int g = 0; g < kMaxGroups; ++g) {
-      if (g < hd.n_groups) {
+      if (g < n_groups) {
+        floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
         const int nk = hd.nkb_g[g];
         switch (hd.rate[g]) {
-          case 1: qk_group<1>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, dg[g][0], dg[g][1]); break;
-          case 2: qk_group<2>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, dg[g][0], dg[g][1]); break;
-          case 3: qk_group<3>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, dg[g][0], dg[g][1]); break;
-          default: qk_group<4>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, dg[g][0], dg[g][1]); break;
+          case 1: qk_group<1>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, d0, d1); break;
+          case 2: qk_group<2>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, d0, d1); break;
+          case 3: qk_group<3>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, d0, d1); break;
+          default: qk_group<4>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, d0, d1); break;
         }
         kb0 += nk;
-      }
-    }
-    // ---- logits of tokens 8q + j (j = 4*half + e), column n
-    float lg[8];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 4 * hf + e;
-        const float4 nu = *reinterpret_cast<const float4*>(kn + (8 * q + j) * kNS);
-        float s = nu.x * dg[0][hf][e];
-        s = fmaf(nu.y, dg[1][hf][e], s);
-        s = fmaf(nu.z, dg[2][hf][e], s);
-        s = fmaf(nu.w, dg[3][hf][e], s);
-        lg[j] = s;
+        for (int e = 0; e < 4; ++e) {
+          lg[e] = fmaf(kn[(8 * q + e) * kNS + g], d0[e], lg[e]);
+          lg[4 + e] = fmaf(kn[(8 * q + 4 + e) * kNS + g], d1[e], lg[4 + e]);
+        }
       }
     }
     float mblk = -INFINITY;
@@ -847,6 +921,9 @@ __global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
     m_run = m_new;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     // ---- probabilities times value norms, split high/low by column
+    const float4 vna = *reinterpret_cast<const float4*>(vnl + 8 * q);
+    const float4 vnb = *reinterpret_cast<const float4*>(vnl + 8 * q + 4);
+    const float vn[8] = {vna.x, vna.y, vna.z, vna.w, vnb.x, vnb.y, vnb.z, vnb.w};
     uint32_t pp[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -854,7 +931,8 @@ __global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = 2 * jj + u;
-        const float p = (lg[j] == -INFINITY) ? 0.f : exp2f(lg[j] - m_use);
+        // lg - m_use <= 0: the hardware 2^x (denormal results flush to 0) is exact enough
+        const float p = (lg[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[j] - m_use);
         l_run += p;
         const float pv = (p == 0.f) ? 0.f : p * vn[j];
         const float hi = (float)(_Float16)pv;
@@ -868,178 +946,198 @@ __global__ void __launch_bounds__(64 * kWaves) attn_kernel(AttnArgs a) {
     pa.u[2] = pp[2];
     pa.u[3] = pp[3];
     // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
-    uint32_t vwc[2 * VB];
-#pragma unroll
-    for (int i = 0; i < 2 * VB; ++i) vwc[i] = cur.vw[i];
+    half8 vbs[8];  // all value operands of the block first, then the 8 products
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const uint32_t F = vfield<VB>(vwc, t);
-      half8 vb;
-      if (VB == 1) vb = dequant8<1>(S, F);
-      else if (VB == 2) vb = dequant8<2>(S, F);
-      else if (VB == 3) vb = dequant8<3>(S, F);
-      else vb = dequant8<4>(S, F);
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, vb, oacc[t], 0, 0, 0);
+      const uint32_t F = vfield<VB>(cur.vw, t);
+      if (VB == 1) vbs[t] = dequant8<1>(S, F);
+      else if (VB == 2) vbs[t] = dequant8<2>(S, F);
+      else if (VB == 3) vbs[t] = dequant8<3>(S, F);
+      else vbs[t] = dequant8<4>(S, F);
     }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, vbs[t], oacc[t], 0, 0, 0);
     __builtin_amdgcn_wave_barrier();
     cur = nxt;
   }
 
-  // ---- per-wave epilogue: rows 0..7 = high row + mirrored low row
+  // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  __syncthreads();  // the query rows in S.oacc[0] are no longer needed
+  float vrow[8][4];  // combined rows 4q+e (q < 2) for the 8 tiles
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float partner = __shfl_xor(oacc[t][3 - e], 48);
-      if (q < 2) S.oacc[wave][4 * q + e][8 * n + t] = oacc[t][e] + partner;
-    }
+    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + __shfl_xor(oacc[t][3 - e], 48);
   }
   if (q == 0 && n < 8) {
     S.om[wave][n] = m_run;
     S.ol[wave][n] = l_run;
   }
+  __syncthreads();  // every wave is done with its key tile
+  float(*slots)[8][kD] = reinterpret_cast<float(*)[8][kD]>(region);  // [kWaves/2][8][128]
+  const int slot = wave & (kWaves / 2 - 1);
+  if (wave < kWaves / 2 && q < 2) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) slots[slot][4 * q + e][8 * n + t] = vrow[t][e];
+  }
   __syncthreads();
-  // ---- merge the 4 waves, write one partial per row
-  for (int e = tid; e < 8 * kD; e += 256) {
-    const int r = e >> 7, c = e & 127;
+  if (wave >= kWaves / 2 && q < 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * q + e;
+      const float ma = S.om[slot][r], mb = S.om[wave][r];
+      const float M = fmaxf(ma, mb);
+      const float sa = (ma == -INFINITY) ? 0.f : exp2f(ma - M);
+      const float sb = (mb == -INFINITY) ? 0.f : exp2f(mb - M);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        float* pd = &slots[slot][r][8 * n + t];
+        *pd = sa * *pd + sb * vrow[t][e];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 8 * (kWaves / 2)) {  // merged (m, l) of each slot pair
+    const int sl = tid >> 3, r = tid & 7;
+    const float ma = S.om[sl][r], mb = S.om[sl + kWaves / 2][r];
+    const float M = fmaxf(ma, mb);
+    const float sa = (ma == -INFINITY) ? 0.f : exp2f(ma - M);
+    const float sb = (mb == -INFINITY) ? 0.f : exp2f(mb - M);
+    S.ol[sl][r] = sa * S.ol[sl][r] + sb * S.ol[sl + kWaves / 2][r];
+    S.om[sl][r] = M;
+  }
+  __syncthreads();
+  // ---- publish one partial (m, l, acc) per row for this chunk
+  for (int e = tid; e < 8 * (kD / 4); e += kThreads) {
+    const int r = e >> 5, c4 = e & 31;
     const int id = S.row_id[r];
     if (id < 0) continue;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.om[w][r]);
-    float acc = 0.f, l = 0.f;
+    for (int w = 0; w < kWaves / 2; ++w) M = fmaxf(M, S.om[w][r]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < kWaves / 2; ++w) {
         const float s = exp2f(S.om[w][r] - M);
-        acc = fmaf(s, S.oacc[w][r][c], acc);
+        const float4 x = *reinterpret_cast<const float4*>(&slots[w][r][4 * c4]);
+        acc.x = fmaf(s, x.x, acc.x);
+        acc.y = fmaf(s, x.y, acc.y);
+        acc.z = fmaf(s, x.z, acc.z);
+        acc.w = fmaf(s, x.w, acc.w);
         l = fmaf(s, S.ol[w][r], l);
       }
     }
     float* dst = a.partials + ((size_t)id * a.n_chunks + chunk_idx) * kPS;
-    dst[4 + c] = acc;
-    if (c == 0) {
-      dst[0] = M;
-      dst[1] = l;
-    }
+    *reinterpret_cast<float4*>(dst + 4 + 4 * c4) = acc;
+    if (c4 == 0) *reinterpret_cast<float4*>(dst) = make_float4(M, l, 0.f, 0.f);
   }
-  // ---- the last workgroup of this tile merges all chunks
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const uint32_t arrivals = (uint32_t)((tile_len + a.chunk - 1) / a.chunk);
-    const uint32_t old = atomicAdd(a.counters + tile, 1u);
-    const int last = (old == arrivals - 1);
-    if (last) a.counters[tile] = 0u;  // every arrival has counted: reset for the next call
-    S.last = last;
-  }
-  __syncthreads();
-  if (!S.last) return;
-  __threadfence();
-  float* wgt = &S.oacc[0][0][0];                               // [8][kMaxChunks] split weights
-  float4* red = reinterpret_cast<float4*>(&S.oacc[2][0][0]);   // [8 slices][32]
-  float(*orot)[kD] = S.oacc[3];                                // merged rows (rotated basis)
-  // phase A: per row, 32 threads: maximum and weights exp2(m_k - M), sum of l
+}
+
+// ============================================================================
+// Phase 2: per row, log-sum-exp merge of its chunk partials, then
+// o = Pi_V^T o_rot / sqrt(128) (value reconstruction nu * Pi_V^T C[code] / sqrt(128)).
+// ============================================================================
+
+struct MergeArgs {
+  const DevHead* heads;
+  const float* rot;
+  const float* partials;
+  const int32_t* seq_len;
+  float* out;
+  int64_t pos0;
+  int32_t n_q, g, n_chunks, chunk, prefill, max_len;
+};
+
+__global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
+  __shared__ float wgt[kMaxChunks];
+  __shared__ float4 red[8][32];
+  __shared__ float orot[kD];
+  __shared__ float opart[2][kD];
+  __shared__ float rm[8], rl[8];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int hq = row % a.n_q;
+  const DevHead& hd = a.heads[hq / a.g];
+  int len;
+  if (a.prefill) len = (int)(a.pos0 + row / a.n_q + 1);
+  else len = min(max(a.seq_len[row / a.n_q], 0), a.max_len);
+  const int nv = (len + a.chunk - 1) / a.chunk;
+  // inverse rotation operand: thread (i, half) holds Pi_V^T[i][64 half .. + 63]
+  const int oi = tid & 127, oh = tid >> 7;
+  float4 pvt[16];
   {
-    const int r = tid >> 5, j = tid & 31;
-    const int id = S.row_id[r];
-    const int nv = id >= 0 ? (S.row_len[r] + a.chunk - 1) / a.chunk : 0;
-    const float* pp = a.partials + (size_t)(id >= 0 ? id : 0) * a.n_chunks * kPS;
-    float mk[kMaxChunks / 32], lk[kMaxChunks / 32];
-    float M = -INFINITY;
+    const float4* pt = reinterpret_cast<const float4*>(a.rot + hd.vrot_t_off + (size_t)oi * kD + 64 * oh);
 #pragma unroll
-    for (int u = 0; u < kMaxChunks / 32; ++u) {
-      const int k = j + 32 * u;
-      mk[u] = -INFINITY;
-      lk[u] = 0.f;
-      if (k < nv) {
-        mk[u] = pp[(size_t)k * kPS];
-        lk[u] = pp[(size_t)k * kPS + 1];
-      }
-      M = fmaxf(M, mk[u]);
-    }
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
-    float L = 0.f;
-#pragma unroll
-    for (int u = 0; u < kMaxChunks / 32; ++u) {
-      const int k = j + 32 * u;
-      const float w = (mk[u] == -INFINITY) ? 0.f : exp2f(mk[u] - M);
-      if (k < kMaxChunks) wgt[r * kMaxChunks + k] = w;
-      L = fmaf(w, lk[u], L);
-    }
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o, 32);
-    if (j == 0) S.ol[0][r] = L;
+    for (int u = 0; u < 16; ++u) pvt[u] = pt[u];
   }
+  const float* pp = a.partials + (size_t)row * a.n_chunks * kPS;
+  // maximum over the chunks
+  const float mk = tid < nv ? pp[(size_t)tid * kPS] : -INFINITY;
+  const float lk = tid < nv ? pp[(size_t)tid * kPS + 1] : 0.f;
+  float M = mk;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if ((tid & 63) == 0) rm[tid >> 6] = M;
   __syncthreads();
-  // phase B: acc[r][c] = sum_k w_k acc_k[c]; thread = (float4 column c4, k slice)
+  M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+  const float w = (mk == -INFINITY) ? 0.f : exp2f(mk - M);
+  float L = w * lk;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  if ((tid & 63) == 0) rl[tid >> 6] = L;
+  if (tid < kMaxChunks) wgt[tid] = w;
+  __syncthreads();
+  L = (rl[0] + rl[1]) + (rl[2] + rl[3]);
+  // weighted sum of the accumulators: thread = (float4 column c4, chunk slice of 8)
   {
     const int c4 = tid & 31, ks = tid >> 5;
-    for (int r = 0; r < 8; ++r) {
-      const int id = S.row_id[r];
-      if (id < 0) continue;  // uniform across the workgroup
-      const int nv = (S.row_len[r] + a.chunk - 1) / a.chunk;
-      const float* pp = a.partials + (size_t)id * a.n_chunks * kPS + 4 + 4 * c4;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-      for (int k = ks; k < nv; k += 8) {
-        const float w = wgt[r * kMaxChunks + k];
-        const float4 x = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS);
-        acc.x = fmaf(w, x.x, acc.x);
-        acc.y = fmaf(w, x.y, acc.y);
-        acc.z = fmaf(w, x.z, acc.z);
-        acc.w = fmaf(w, x.w, acc.w);
-      }
-      red[ks * 32 + c4] = acc;
-      __syncthreads();
-      if (tid < 32) {
-        float4 s = red[tid];
-#pragma unroll
-        for (int k2 = 1; k2 < 8; ++k2) {
-          const float4 y = red[k2 * 32 + tid];
-          s.x += y.x;
-          s.y += y.y;
-          s.z += y.z;
-          s.w += y.w;
-        }
-        // value reconstruction is nu * Pi_V^T C[code] / sqrt(128)
-        const float L = S.ol[0][r];
-        const float f = L > 0.f ? 0.08838834764831845f / L : 0.f;
-        orot[r][4 * tid] = s.x * f;
-        orot[r][4 * tid + 1] = s.y * f;
-        orot[r][4 * tid + 2] = s.z * f;
-        orot[r][4 * tid + 3] = s.w * f;
-      }
-      __syncthreads();
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int k = ks; k < nv; k += 8) {
+      const float wk = wgt[k];
+      const float4 x = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS + 4 + 4 * c4);
+      acc.x = fmaf(wk, x.x, acc.x);
+      acc.y = fmaf(wk, x.y, acc.y);
+      acc.z = fmaf(wk, x.z, acc.z);
+      acc.w = fmaf(wk, x.w, acc.w);
     }
+    red[ks][c4] = acc;
   }
-  // o = Pi_V^T o_rot: thread i reads row i of Pi_V^T (column i of Pi_V) contiguously
-  {
-    const int i = tid & 127, r0 = (tid >> 7) * 4;
-    const float4* pt = reinterpret_cast<const float4*>(a.rot + hd.vrot_t_off + (size_t)i * kD);
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int c4 = 0; c4 < kD / 4; ++c4) {
-      const float4 w = pt[c4];
+  __syncthreads();
+  if (tid < 32) {
+    float4 s = red[0][tid];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float4 x = *reinterpret_cast<const float4*>(&orot[r0 + rr][4 * c4]);
-        o[rr] = fmaf(w.x, x.x, o[rr]);
-        o[rr] = fmaf(w.y, x.y, o[rr]);
-        o[rr] = fmaf(w.z, x.z, o[rr]);
-        o[rr] = fmaf(w.w, x.w, o[rr]);
-      }
+    for (int k2 = 1; k2 < 8; ++k2) {
+      const float4 y = red[k2][tid];
+      s.x += y.x;
+      s.y += y.y;
+      s.z += y.z;
+      s.w += y.w;
     }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int id = S.row_id[r0 + rr];
-      if (id >= 0) a.out[(size_t)id * kD + i] = o[rr];
-    }
+    const float f = L > 0.f ? 0.08838834764831845f / L : 0.f;
+    orot[4 * tid] = s.x * f;
+    orot[4 * tid + 1] = s.y * f;
+    orot[4 * tid + 2] = s.z * f;
+    orot[4 * tid + 3] = s.w * f;
   }
+  __syncthreads();
+  float o = 0.f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const float4 x = *reinterpret_cast<const float4*>(&orot[64 * oh + 4 * u]);
+    o = fmaf(pvt[u].x, x.x, o);
+    o = fmaf(pvt[u].y, x.y, o);
+    o = fmaf(pvt[u].z, x.z, o);
+    o = fmaf(pvt[u].w, x.w, o);
+  }
+  opart[oh][oi] = o;
+  __syncthreads();
+  if (tid < kD) a.out[(size_t)row * kD + tid] = opart[0][tid] + opart[1][tid];
 }
 
 // ============================================================================
@@ -1130,19 +1228,16 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
 }
 
 int auto_chunk(int64_t max_len, int64_t tiles) {
-  // aim for >= 1024 workgroups (4 waves each), at least 4 blocks per wave
-  const int64_t target =
-      std::min<int64_t>(kMaxChunks, std::max<int64_t>(1, 1024 / std::max<int64_t>(1, tiles)));
+  // about two 4-wave workgroups per compute unit; at least 4 splits per row tile
+  // so that ragged batches balance; splits of whole 128-token rounds (4 waves x 32)
+  int64_t target = std::max<int64_t>(1, 512 / std::max<int64_t>(1, tiles));
+  target = std::min<int64_t>(kMaxChunks, std::max<int64_t>(4, target));
   int64_t ch = (max_len + target - 1) / target;
-  ch = ((ch + 511) / 512) * 512;
-  return (int)std::max<int64_t>(512, ch);
+  ch = ((ch + 127) / 128) * 128;
+  return (int)std::max<int64_t>(128, ch);
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-size_t attn_ws_bytes(int64_t n_tiles, int64_t rows, int64_t n_chunks) {
-  return align256((size_t)n_tiles * 4) + align256((size_t)rows * n_chunks * kPS * 4);
-}
+size_t attn_ws_bytes(int64_t rows, int64_t n_chunks) { return (size_t)rows * n_chunks * kPS * 4; }
 
 struct AttnLaunch {
   int64_t rows;
@@ -1152,11 +1247,9 @@ struct AttnLaunch {
   int n_chunks;
 };
 
-gtq_status launch_attn(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* q,
-                       AttnArgs& aa, const AttnLaunch& L, float scale, float* out,
-                       void* ws, hipStream_t stream) {
-  const DevHead* heads = p->d_heads + (size_t)layer * p->n_kv;
-  aa.heads = heads;
+gtq_status launch_partials(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* q,
+                           AttnArgs& aa, const AttnLaunch& L, float scale, void* ws, hipStream_t stream) {
+  aa.heads = p->d_heads + (size_t)layer * p->n_kv;
   aa.rot = p->d_rot;
   aa.cb = p->d_cb;
   aa.k_codes = c->k_codes;
@@ -1164,9 +1257,7 @@ gtq_status launch_attn(const gtq_plan* p, int layer, const gtq_cache_view* c, co
   aa.v_codes = c->v_codes;
   aa.v_norms = c->v_norms;
   aa.q = q;
-  aa.out = out;
-  aa.counters = reinterpret_cast<uint32_t*>(ws);
-  aa.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)L.n_tiles * 4));
+  aa.partials = reinterpret_cast<float*>(ws);
   aa.capacity = c->capacity;
   aa.n_kv = p->n_kv;
   aa.n_q = p->n_q;
@@ -1176,24 +1267,46 @@ gtq_status launch_attn(const gtq_plan* p, int layer, const gtq_cache_view* c, co
   aa.chunk = L.chunk;
   aa.n_chunks = L.n_chunks;
   aa.qscale = scale * LOG2E_F;
-  dim3 grid(L.n_chunks, L.n_tiles);
+  if (p->n_kv > kMaxArgHeads)
+    return fail(GTQ_EUNSUPPORTED, "gtq attention: more than 64 KV heads per layer");
+  for (int b = 1; b <= 4; ++b)
+    for (int k = 0; k < 16; ++k) aa.cbv[b - 1][k] = p->cb.c[b][k];
   int kr = 0;
-  for (int h = 0; h < p->n_kv; ++h) kr = std::max(kr, p->heads[(size_t)layer * p->n_kv + h].krot_floats);
-  const size_t lds = (size_t)kr * 4;
+  for (int h = 0; h < p->n_kv; ++h) {
+    const DevHead& dh = p->heads[(size_t)layer * p->n_kv + h];
+    kr = std::max(kr, dh.krot_floats);
+    aa.krot_off[h] = dh.krot_off[0];
+    aa.krot_n[h] = dh.krot_floats;
+  }
+  aa.region_bytes = (int32_t)attn_region_bytes(kr);
+  const size_t lds = ((sizeof(AttnFixed) + 15) & ~(size_t)15) + aa.region_bytes;
+  const int lds_max = (int)(((sizeof(AttnFixed) + 15) & ~(size_t)15) + attn_region_bytes(kD * kD));
   static const hipError_t attr[4] = {
-      hipFuncSetAttribute((const void*)attn_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kD * kD * 4),
-      hipFuncSetAttribute((const void*)attn_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kD * kD * 4),
-      hipFuncSetAttribute((const void*)attn_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, kD * kD * 4),
-      hipFuncSetAttribute((const void*)attn_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, kD * kD * 4)};
+      hipFuncSetAttribute((const void*)attn_partials_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max),
+      hipFuncSetAttribute((const void*)attn_partials_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max),
+      hipFuncSetAttribute((const void*)attn_partials_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max),
+      hipFuncSetAttribute((const void*)attn_partials_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max)};
   if (attr[p->v_bits - 1] != hipSuccess) return hip_fail(attr[p->v_bits - 1], "gtq attention: LDS attribute");
+  dim3 grid(L.n_chunks, L.n_tiles);
   switch (p->v_bits) {
-    case 1: hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(256), lds, stream, aa); break;
-    case 2: hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(256), lds, stream, aa); break;
-    case 3: hipLaunchKernelGGL(attn_kernel<3>, grid, dim3(256), lds, stream, aa); break;
-    default: hipLaunchKernelGGL(attn_kernel<4>, grid, dim3(256), lds, stream, aa); break;
+    case 1: hipLaunchKernelGGL(attn_partials_kernel<1>, grid, dim3(kThreads), lds, stream, aa); break;
+    case 2: hipLaunchKernelGGL(attn_partials_kernel<2>, grid, dim3(kThreads), lds, stream, aa); break;
+    case 3: hipLaunchKernelGGL(attn_partials_kernel<3>, grid, dim3(kThreads), lds, stream, aa); break;
+    default: hipLaunchKernelGGL(attn_partials_kernel<4>, grid, dim3(kThreads), lds, stream, aa); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "gtq attention: launch");
+  if (e != hipSuccess) return hip_fail(e, "gtq attention partials: launch");
+  return ok();
+}
+
+gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const int32_t* seq_len,
+                        int64_t pos0, int prefill, int max_len, float* out, const void* ws,
+                        hipStream_t stream) {
+  MergeArgs ma{p->d_heads + (size_t)layer * p->n_kv, p->d_rot, reinterpret_cast<const float*>(ws), seq_len,
+               out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill, max_len};
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows), dim3(256), 0, stream, ma);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gtq attention merge: launch");
   return ok();
 }
 
@@ -1301,6 +1414,10 @@ static bool decode_shape(const gtq_plan* p, int32_t batch, int64_t max_len, int3
     *st = fail(GTQ_EINVAL, std::string(fn) + ": max_len < 0");
     return false;
   }
+  if (max_len > INT32_MAX) {
+    *st = fail(GTQ_EUNSUPPORTED, std::string(fn) + ": max_len too large");
+    return false;
+  }
   if (chunk < 0 || chunk % kBlk) {
     *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk must be 0 or a positive multiple of 32");
     return false;
@@ -1325,40 +1442,75 @@ gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64
   AttnLaunch L;
   gtq_status st;
   if (!decode_shape(plan, batch, max_len, chunk, &L, &st, "gtq_decode_workspace_bytes")) return st;
-  *out = attn_ws_bytes(L.n_tiles, L.rows, L.n_chunks);
+  *out = attn_ws_bytes(L.rows, L.n_chunks);
   return ok();
 }
 
-gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
-                           const float* q, const int32_t* seq_len, int64_t max_len,
-                           float softmax_scale, int32_t chunk, float* out, float* logits,
-                           void* workspace, size_t ws_bytes, void* hip_stream) {
+static gtq_status decode_check(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                               int64_t max_len, int32_t chunk, size_t ws_bytes, const void* ws,
+                               AttnLaunch* L, const char* fn) {
   gtq_status st;
-  if (!check_device_plan(plan, "gtq_decode_attn", &st)) return st;
-  if (!check_cache(plan, cache, "gtq_decode_attn", &st)) return st;
-  if (layer < 0 || layer >= plan->n_layers) return fail(GTQ_EINVAL, "gtq_decode_attn: layer out of range");
-  if (!q || !seq_len || !out || !workspace) return fail(GTQ_EINVAL, "gtq_decode_attn: NULL pointer");
-  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_decode_attn: softmax_scale not finite");
-  if (max_len > cache->capacity) return fail(GTQ_ECAPACITY, "gtq_decode_attn: max_len > capacity");
-  if (max_len > INT32_MAX) return fail(GTQ_EUNSUPPORTED, "gtq_decode_attn: max_len too large");
+  if (!check_device_plan(plan, fn, &st)) return st;
+  if (!check_cache(plan, cache, fn, &st)) return st;
+  if (layer < 0 || layer >= plan->n_layers) return fail(GTQ_EINVAL, std::string(fn) + ": layer out of range");
+  if (!ws) return fail(GTQ_EINVAL, std::string(fn) + ": workspace is NULL");
+  if (max_len > cache->capacity) return fail(GTQ_ECAPACITY, std::string(fn) + ": max_len > capacity");
+  if (!decode_shape(plan, cache->batch, max_len, chunk, L, &st, fn)) return st;
+  if (ws_bytes < attn_ws_bytes(L->rows, L->n_chunks))
+    return fail(GTQ_ECAPACITY, std::string(fn) + ": workspace too small");
+  return GTQ_OK;
+}
+
+gtq_status gtq_decode_attn_partials(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                    const float* q, const int32_t* seq_len, int64_t max_len,
+                                    float softmax_scale, int32_t chunk, float* logits, void* workspace,
+                                    size_t ws_bytes, void* hip_stream) {
   AttnLaunch L;
-  if (!decode_shape(plan, cache->batch, max_len, chunk, &L, &st, "gtq_decode_attn")) return st;
-  if (ws_bytes < attn_ws_bytes(L.n_tiles, L.rows, L.n_chunks))
-    return fail(GTQ_ECAPACITY, "gtq_decode_attn: workspace too small");
+  gtq_status st = decode_check(plan, layer, cache, max_len, chunk, ws_bytes, workspace, &L,
+                               "gtq_decode_attn_partials");
+  if (st != GTQ_OK) return st;
+  if (!q || !seq_len) return fail(GTQ_EINVAL, "gtq_decode_attn_partials: NULL pointer");
+  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_decode_attn_partials: softmax_scale not finite");
   AttnArgs aa{};
   aa.logits = logits;
   aa.logits_ld = max_len;
   aa.seq_len = seq_len;
   aa.prefill = 0;
   aa.max_len = (int32_t)max_len;
-  return launch_attn(plan, layer, cache, q, aa, L, softmax_scale, out, workspace,
-                     (hipStream_t)hip_stream);
+  return launch_partials(plan, layer, cache, q, aa, L, softmax_scale, workspace, (hipStream_t)hip_stream);
+}
+
+gtq_status gtq_decode_attn_merge(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                 const int32_t* seq_len, int64_t max_len, int32_t chunk, float* out,
+                                 const void* workspace, size_t ws_bytes, void* hip_stream) {
+  AttnLaunch L;
+  gtq_status st = decode_check(plan, layer, cache, max_len, chunk, ws_bytes, workspace, &L,
+                               "gtq_decode_attn_merge");
+  if (st != GTQ_OK) return st;
+  if (!seq_len || !out) return fail(GTQ_EINVAL, "gtq_decode_attn_merge: NULL pointer");
+  return launch_merge(plan, layer, L, seq_len, 0, 0, (int)max_len, out, workspace, (hipStream_t)hip_stream);
+}
+
+gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                           const float* q, const int32_t* seq_len, int64_t max_len,
+                           float softmax_scale, int32_t chunk, float* out, float* logits,
+                           void* workspace, size_t ws_bytes, void* hip_stream) {
+  if (!out) return fail(GTQ_EINVAL, "gtq_decode_attn: out is NULL");
+  gtq_status st = gtq_decode_attn_partials(plan, layer, cache, q, seq_len, max_len, softmax_scale, chunk,
+                                           logits, workspace, ws_bytes, hip_stream);
+  if (st != GTQ_OK) return st;
+  return gtq_decode_attn_merge(plan, layer, cache, seq_len, max_len, chunk, out, workspace, ws_bytes,
+                               hip_stream);
 }
 
 static bool prefill_shape(const gtq_plan* p, int64_t pos0, int64_t n_tok, int32_t chunk,
                           AttnLaunch* L, gtq_status* st, const char* fn) {
   if (pos0 < 0 || n_tok < 1) {
     *st = fail(GTQ_EINVAL, std::string(fn) + ": need pos0 >= 0 and n_tok >= 1");
+    return false;
+  }
+  if (pos0 + n_tok > INT32_MAX || n_tok * (int64_t)p->n_q > INT32_MAX) {
+    *st = fail(GTQ_EUNSUPPORTED, std::string(fn) + ": sizes too large");
     return false;
   }
   if (chunk < 0 || chunk % kBlk) {
@@ -1385,7 +1537,7 @@ gtq_status gtq_prefill_workspace_bytes(const gtq_plan* plan, int64_t pos0, int64
   AttnLaunch L;
   gtq_status st;
   if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_workspace_bytes")) return st;
-  *out = attn_ws_bytes(L.n_tiles, L.rows, L.n_chunks);
+  *out = attn_ws_bytes(L.rows, L.n_chunks);
   return ok();
 }
 
@@ -1403,7 +1555,7 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
   AttnLaunch L;
   if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_attn")) return st;
   if (pos0 + n_tok > cache->capacity) return fail(GTQ_ECAPACITY, "gtq_prefill_attn: pos0 + n_tok > capacity");
-  if (ws_bytes < attn_ws_bytes(L.n_tiles, L.rows, L.n_chunks))
+  if (ws_bytes < attn_ws_bytes(L.rows, L.n_chunks))
     return fail(GTQ_ECAPACITY, "gtq_prefill_attn: workspace too small");
   AttnArgs aa{};
   aa.logits = nullptr;
@@ -1412,8 +1564,10 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
   aa.pos0 = pos0;
   aa.n_tok = (int32_t)n_tok;
   aa.max_len = (int32_t)(pos0 + n_tok);
-  return launch_attn(plan, layer, cache, q, aa, L, softmax_scale, out, workspace,
-                     (hipStream_t)hip_stream);
+  hipStream_t s = (hipStream_t)hip_stream;
+  st = launch_partials(plan, layer, cache, q, aa, L, softmax_scale, workspace, s);
+  if (st != GTQ_OK) return st;
+  return launch_merge(plan, layer, L, nullptr, pos0, 1, (int)(pos0 + n_tok), out, workspace, s);
 }
 
 }  // extern "C"
