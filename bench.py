@@ -44,7 +44,29 @@ def parse():
     p.add_argument("--chunk", type=int, default=0, help="split size (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="after timing, run a plain device copy (torch.neg) of this many MiB three "
+                        "times: a kernel of known traffic that calibrates the HBM byte counters")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_partials_k2v2_32k_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "packed_cache_attention_tq_amd", "csrc", "gtq_device.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention (partials) kernel from the committed counter
+    summary, or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE).read().splitlines()
+                  if ":" in line and not line.startswith("#"))
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if kv["kernel_source_sha256"].strip() != sha:
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def build_workload(seed, n_ctx=32768, h_kv=8, g=4, k_budget=128, v_bits=2):
@@ -72,35 +94,39 @@ def build_workload(seed, n_ctx=32768, h_kv=8, g=4, k_budget=128, v_bits=2):
                 n_ctx=n_ctx, h_kv=h_kv, g=g, k_budget=k_budget, v_bits=v_bits)
 
 
-def cpu_baseline(w, seed):
-    """The fp64 oracle on one KV head of the step (1-token encode + decode of its g
-    query heads over all cached tokens), scaled to the 8 heads of the step."""
+def cpu_baseline(w, seed, min_seconds=10.0):
+    """The fp64 oracle on the whole step (1-token encode + decode of all 32 query heads over
+    every cached token, 8 KV heads), repeated until at least min_seconds of CPU time."""
     from oracle import gtq_oracle as O
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    n, g = w["n_ctx"], w["g"]
-    inp = w["inps"][0]
-    lay_r = w["rates"][0, 0]
-    hp = O.HeadPlan(lay_r, w["krot"][0][0], w["vrot"][0][0], w["v_bits"])
-    enc = O.encode_kv(hp, inp["k"][: n - 1], inp["v"][: n - 1])      # cache fill (untimed setup)
+    n, g, h_kv = w["n_ctx"], w["g"], w["h_kv"]
+    heads, caches = [], []
+    for h in range(h_kv):                                    # cache fill (untimed setup)
+        inp = w["inps"][h]
+        hp = O.HeadPlan(w["rates"][0, h], w["krot"][0][h], w["vrot"][0][h], w["v_bits"])
+        heads.append(hp)
+        caches.append(O.encode_kv(hp, inp["k"][: n - 1], inp["v"][: n - 1]))
     reps, t_total = 0, 0.0
-    while t_total < 10.0 and reps < 3:
+    while t_total < min_seconds and reps < 100:
         t0 = time.perf_counter()
-        new = O.encode_kv(hp, inp["k"][n - 1: n], inp["v"][n - 1: n])
-        kw = np.concatenate([enc["k_words"], new["k_words"]])
-        kn = np.concatenate([enc["k_norms"], new["k_norms"]])
-        vw = np.concatenate([enc["v_words"], new["v_words"]])
-        vn = np.concatenate([enc["v_norms"], new["v_norms"]])
-        O.decode_attention(hp, inp["q"][0], kw, kn, vw, vn, 1 / math.sqrt(128))
+        for h in range(h_kv):
+            inp, enc, hp = w["inps"][h], caches[h], heads[h]
+            new = O.encode_kv(hp, inp["k"][n - 1: n], inp["v"][n - 1: n])
+            kw = np.concatenate([enc["k_words"], new["k_words"]])
+            kn = np.concatenate([enc["k_norms"], new["k_norms"]])
+            vw = np.concatenate([enc["v_words"], new["v_words"]])
+            vn = np.concatenate([enc["v_norms"], new["v_norms"]])
+            O.decode_attention(hp, inp["q"][0], kw, kn, vw, vn, 1 / math.sqrt(128))
         t_total += time.perf_counter() - t0
         reps += 1
-    t_step = t_total / reps * w["h_kv"]
+    t_step = t_total / reps
     return {"value": n / t_step, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 of {w['h_kv']} KV heads of the step (1-token encode + decode of {g} query heads "
-                      f"over {n} tokens), {reps} repetition(s), scaled x{w['h_kv']}",
+            "sample": f"the whole step (1-token encode + decode of {h_kv * g} query heads over {n} tokens, "
+                      f"{h_kv} KV heads), {reps} step(s), {t_total:.1f} s",
             "seconds": round(t_total, 2)}
 
 
@@ -202,12 +228,19 @@ def main():
                    "global_batch": 1, "seq_len": n, "parallelism": "none (1 GPU)",
                    "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "attn_partials_kernel<2>", "kernel_avg_us": round(kern_avg * 1e3, 3),
                      "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
                      "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
                      "alg_bytes_per_launch": int(alg_bytes)},
     }
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded slice ...")
         res["cpu_baseline"] = cpu_baseline(w, args.seed)
