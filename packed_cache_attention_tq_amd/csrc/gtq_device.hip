@@ -439,31 +439,30 @@ __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
 }
 
 // ============================================================================
-// Split-K attention over the packed cache, one launch per call.
+// Split-K attention over the packed cache (Block-GTQ page, abstract, 5th
+// sentence): phase 1 writes one online-softmax partial (m, l, acc[128]) per query
+// row and split; phase 2 (attn_merge_kernel) combines the splits.
 //
-// A workgroup (4 waves) takes one row tile (up to 8 query rows of one sequence and
-// KV head) and one chunk of cached tokens.
-// Prologue: r_g = Pi_g q_g for each key group of each row, scaled by
-//   scale / sqrt(d_g) * log2(e), split into a binary16 high part and a binary16
-//   remainder (together ~22 bits), stored as the QK B operand.
-// Per 32-token block and wave:
-//   QK: MFMA 16x16x32 f16, A = decoded key codes (16 tokens x 32 coordinates of one
-//       group; the codebook values are exact binary16), B = rotated queries, columns
-//       0..7 = high parts of rows 0..7, columns 8..15 = low parts of rows 7..0.
-//       One accumulator per key group; the per-token group norms are applied after
-//       the product, then a row-mirror DPP adds the high and low halves.
-//   online softmax (base 2) per row, with lane-local partial sums;
-//   PV: MFMA with A = p * nu_V split in high/low parts (rows as above) and
+// A workgroup (8 waves) takes one row tile (up to 8 query rows of one sequence and
+// KV head) and one split of `chunk` cached tokens; each wave walks 32-token blocks.
+// Prologue: r_g = Pi_g q_g for every key group and row on the matrix cores
+//   (fp32 MFMA 16x16x4), scaled by scale / sqrt(d_g) * log2(e) and split into a
+//   binary16 high part and a binary16 remainder (together ~22 bits): the QK
+//   B operand. Columns 0..7 hold the high parts of rows 0..7, columns 8..15 the
+//   low parts of rows 7..0.
+// Per block:
+//   QK: MFMA 16x16x32 f16 per 32-coordinate K-block of a key group; A = decoded
+//       key codes (exact binary16 codebook values, two codes per table read),
+//       16 tokens per A tile. The per-token group norm multiplies each group's
+//       product; a row-mirror DPP then adds the high and low halves.
+//   online softmax in base 2 (the scale carries log2(e));
+//   PV: MFMA with A = p * nu_V split into high/low parts (rows as above) and
 //       B = decoded value codes (8 tokens x 16 coordinates), accumulating in the
 //       value rotation's basis.
-// Epilogue: the 4 waves merge in LDS and write one (m, l, acc[128]) partial per row;
-// the last workgroup of a tile to finish (device-scope counter in the workspace,
-// reset by that workgroup) merges the tile's partials by log-sum-exp and applies
-// o = Pi_V^T o_rot / sqrt(128).
+// Epilogue: the waves merge through LDS into one partial per row.
 // ============================================================================
 
-constexpr int kMaxArgHeads = 64;   // KV heads per layer the attention kernels accept
-constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kWaves = 8;          // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPS = 132;           // partial record: m, l, 2 pad, acc[128] (16-byte aligned acc)
 constexpr int kMaxChunks = 256;    // splits per row
@@ -471,7 +470,6 @@ constexpr int kMaxChunks = 256;    // splits per row
 struct AttnArgs {
   const DevHead* heads;
   const float* rot;
-  const DevCodebook* cb;
   const uint32_t* k_codes;
   const float* k_norms;
   const uint32_t* v_codes;
@@ -488,45 +486,37 @@ struct AttnArgs {
   int32_t prefill;         // 0 decode, 1 prefill
   int32_t seq;             // prefill sequence
   int32_t n_tok;           // prefill: tokens in chunk
-  int32_t chunk;           // tokens per split (multiple of 32)
+  int32_t chunk;           // tokens per split (multiple of 32 * kWaves)
   int32_t n_chunks;
   int32_t max_len;         // decode clamp
-  int32_t region_bytes;    // size of the phase region of shared memory
   float qscale;            // softmax scale * log2(e)
   float cbv[4][16];        // centroids of rates 1..4 (binary16 values)
-  int64_t krot_off[kMaxArgHeads];   // per KV head of the layer: float offset of its key rotations
-  int32_t krot_n[kMaxArgHeads];     // and their size (floats)
 };
 
-// Shared memory: fixed tables, then one region that the prologue (key rotations,
-// query rows), the main loop (per-wave key tiles and norms) and the epilogue
-// (partial rows of the waves) use in turn.
-struct AttnFixed {
-  uint32_t lut1[256][4];  // 1-bit: byte -> 8 binary16 centroids
-  uint32_t lut2[256][2];  // 2-bit: byte -> 4
-  uint32_t lut3[64];      // 3-bit: 6 bits -> 2
-  uint32_t lut4[256];     // 4-bit: byte -> 2
-  uint4 qb[kMaxKB][4][16];  // B operand of QK per K-block / lane
-  float om[kWaves][8];
-  float ol[kWaves][8];
-  int32_t row_id[8];
-  int32_t row_len[8];
-  DevHead hd;             // this KV head's tables, copied from global memory
-  float oacc_scratch[8][kD];  // query rows as loaded (prologue)
-};
 struct AttnWave {
-  uint32_t ktile[kBlk * 17 + 16];  // 32 key records at an odd pitch (kw + 1 words)
-  float kn[kBlk * kNS];
+  uint32_t ktile[kBlk * 17];         // 32 key records at an odd pitch (kw + 1 words, kw <= 16)
+  float knt[kMaxGroups][kBlk];       // group norms, group-major
   float vn[kBlk];
 };
 
-size_t attn_region_bytes(int krot_floats) {
-  // rotations at row pitch d + 1 (at most sum_g d_g extra floats) + 8 query rows
-  const size_t pro = ((size_t)krot_floats + kD + 4) * 4 + 8 * kD * 4;
-  const size_t mainb = kWaves * sizeof(AttnWave);
-  const size_t epi = (kWaves / 2) * 8 * kD * 4;
-  return std::max(pro, std::max(mainb, epi));
-}
+struct AttnShared {
+  uint4 lut1[256];                   // 1-bit codes: byte -> 8 binary16 centroids
+  uint2 lut2[256];                   // 2-bit: byte -> 4
+  uint32_t lut3[64];                 // 3-bit: 6 bits -> 2
+  uint32_t lut4[256];                // 4-bit: byte -> 2
+  int32_t rate_nk[4], rate_grp[4], rate_bit[4], rate_kb[4];  // per rate 1..4: K-blocks, group,
+                                                             // record bit, first K-block
+  uint4 qb[kMaxKB][4][16];           // QK B operand per K-block and lane
+  int32_t row_id[8];
+  int32_t row_len[8];
+  float om[kWaves][8];
+  float ol[kWaves][8];
+  union alignas(16) {
+    float qrec[8][kD];               // prologue: query rows in record order
+    AttnWave w[kWaves][2];           // main loop: two block tiles per wave
+    float slot[kWaves][8][kD];       // epilogue: accumulator rows of each wave
+  } u;
+};
 
 __device__ inline uint32_t pack2h(float a, float b) {
   const _Float16 ha = (_Float16)a, hb = (_Float16)b;
@@ -537,68 +527,81 @@ __device__ inline float dpp_row_mirror(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
 }
 
+// Lane swaps of gfx950. v_permlane16_swap(x, y) exchanges the odd 16-lane rows of x
+// with the even rows of y (permlane32_swap: the upper half of x with the lower half of
+// y). The second operand is an opaque copy: handed the same value twice, this compiler
+// folds the two results into one.
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// value of lane l ^ 16 and of lane l ^ 32
+__device__ inline float xor16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto p = __builtin_amdgcn_permlane16_swap(u, opaque(u), false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? p[0] : p[1]);
+}
+__device__ inline float xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto p = __builtin_amdgcn_permlane32_swap(u, opaque(u), false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? p[0] : p[1]);
+}
+// max / sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ inline float max_over_q(float x) {
+  x = fmaxf(x, xor16(x));
+  return fmaxf(x, xor32(x));
+}
+__device__ inline float sum_over_q(float x) {
+  x += xor16(x);
+  return x + xor32(x);
+}
+// value of lane l ^ 48
+__device__ inline float swap_q3(float x) { return xor16(xor32(x)); }
+
 union H8 {
   half8 h;
   uint32_t u[4];
   uint4 v;
 };
 
-template <int RATE>
-__device__ inline half8 dequant8(const AttnFixed& S, uint32_t F) {
-  H8 r;
-  if (RATE == 1) {
-    r.v = *reinterpret_cast<const uint4*>(S.lut1[F & 0xFF]);
-  } else if (RATE == 2) {
-    const uint2 a = *reinterpret_cast<const uint2*>(S.lut2[F & 0xFF]);
-    const uint2 b = *reinterpret_cast<const uint2*>(S.lut2[(F >> 8) & 0xFF]);
-    r.u[0] = a.x;
-    r.u[1] = a.y;
-    r.u[2] = b.x;
-    r.u[3] = b.y;
-  } else if (RATE == 3) {
-    r.u[0] = S.lut3[F & 63];
-    r.u[1] = S.lut3[(F >> 6) & 63];
-    r.u[2] = S.lut3[(F >> 12) & 63];
-    r.u[3] = S.lut3[(F >> 18) & 63];
+// 8 codes of rate R (code k at bits [k R, (k + 1) R) of F) -> 8 binary16 centroids
+template <int R>
+__device__ inline half8 dequant8(const AttnShared& S, uint32_t F) {
+  H8 o;
+  if (R == 1) {
+    o.v = S.lut1[F & 0xFF];
+  } else if (R == 2) {
+    const uint2 x = S.lut2[F & 0xFF], y = S.lut2[(F >> 8) & 0xFF];
+    o.u[0] = x.x;
+    o.u[1] = x.y;
+    o.u[2] = y.x;
+    o.u[3] = y.y;
+  } else if (R == 3) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.u[j] = S.lut3[(F >> (6 * j)) & 63];
   } else {
-    r.u[0] = S.lut4[F & 0xFF];
-    r.u[1] = S.lut4[(F >> 8) & 0xFF];
-    r.u[2] = S.lut4[(F >> 16) & 0xFF];
-    r.u[3] = S.lut4[(F >> 24) & 0xFF];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.u[j] = S.lut4[(F >> (8 * j)) & 0xFF];
   }
-  return r.h;
+  return o.h;
 }
 
-template <int RATE>
-__device__ inline void qk_group(const AttnFixed& S, const uint32_t* kt, int kw, int kb0, int nkb,
-                                const int32_t* kb_bit, int q, int n, floatx4& d0, floatx4& d1) {
-  // A-row n of the two 16-token halves holds tokens 8(n/4) + n%4 and that + 4
-  const int tau0 = 8 * (n >> 2) + (n & 3);
-  const int tau1 = tau0 + 4;
-  const uint32_t* r0 = kt + tau0 * (kw + 1);
-  const uint32_t* r1 = kt + tau1 * (kw + 1);
-  // a group has at most 4 K-blocks of 32 coordinates: gather every operand first so
-  // that the LDS reads of all K-blocks are in flight together, then multiply
-  H8 qbv[4];
-  half8 a0[4], a1[4];
+// QK of the key group of rate R: its K-blocks (at most 4) into two accumulators
+// (tokens of A-rows n of the two 16-token halves)
+template <int R>
+__device__ inline void qk_rate(const AttnShared& S, const uint32_t* r0, const uint32_t* r1, int nk, int bit0,
+                               int kb0, int q, int n, floatx4& d0, floatx4& d1) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (i < nkb) {
-      const int kbi = kb0 + i;
-      qbv[i].v = S.qb[kbi][q][n];
-      const int bit = kb_bit[kbi] + 8 * q * RATE;
-      const int w = bit >> 5, s = bit & 31;
-      const uint32_t f0 = __builtin_amdgcn_alignbit(r0[w + 1], r0[w], s);
-      const uint32_t f1 = __builtin_amdgcn_alignbit(r1[w + 1], r1[w], s);
-      a0[i] = dequant8<RATE>(S, f0);
-      a1[i] = dequant8<RATE>(S, f1);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i < nkb) {
-      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[i], qbv[i].h, d0, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[i], qbv[i].h, d1, 0, 0, 0);
+    if (i < nk) {
+      const int bit = bit0 + R * (32 * i + 8 * q);
+      const int w = bit >> 5, sb = bit & 31;
+      const uint32_t f0 = __builtin_amdgcn_alignbit(r0[w + 1], r0[w], sb);
+      const uint32_t f1 = __builtin_amdgcn_alignbit(r1[w + 1], r1[w], sb);
+      H8 qv;
+      qv.v = S.qb[kb0 + i][q][n];
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<R>(S, f0), qv.h, d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<R>(S, f1), qv.h, d1, 0, 0, 0);
     }
   }
 }
@@ -614,24 +617,30 @@ __device__ inline uint32_t vfield(const uint32_t (&vw)[2 * VB], int t) {
   return __builtin_amdgcn_alignbit(vw[w + 1], vw[w], s);
 }
 
-template <int VB>
-struct BlockRegs {
-  uint32_t kr[8];       // key codes: words lane + 64 i of the 32-token tile
-  float2 kn;            // key norms: floats 2 lane, 2 lane + 1 of the tile
-  uint32_t vw[2 * VB];  // value codes of 8 tokens x coordinates 8n..8n+7
-  float vn;             // value norm of token (lane & 31)
+// Per-lane registers of one 32-token block: key code words lane + 64 i (KWL of them,
+// enough for k_words <= 2 KWL), group norms 2 lane, 2 lane + 1 of the [32][4] block,
+// the value norm of token lane & 31 and the value codes of tokens 8q..8q+7 x
+// coordinates 8n..8n+7.
+template <int VB, int KWL>
+struct BlockData {
+  uint32_t kr[KWL];
+  float2 kn;
+  float vn;
+  uint32_t vw[2 * VB];
 };
 
-// Every load is unconditional (addresses clamped inside the block) so that the
-// compiler can count the loads in flight and overlap the next block with this one.
-template <int VB>
-__device__ inline void load_block(BlockRegs<VB>& B, const uint32_t* kc, const float* knp, const uint32_t* vc,
+// t0 is uniform, so every address is a scalar base plus a lane offset. Word lane + 64 i
+// exists when lane + 64 i < 32 kw.
+template <int VB, int KWL>
+__device__ inline void load_block(BlockData<VB, KWL>& B, const uint32_t* kc, const float* knp, const uint32_t* vc,
                                   const float* vnp, int t0, int kw, int lane, int q, int n) {
   const uint32_t* ks = kc + (size_t)t0 * kw;
-  const int last = kBlk * kw - 1;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) B.kr[i] = ks[min(lane + 64 * i, last)];
+  for (int i = 0; i < KWL; ++i) {
+    if (2 * i + 1 < kw || (2 * i < kw && lane < 32)) B.kr[i] = ks[lane + 64 * i];
+  }
   B.kn = *reinterpret_cast<const float2*>(knp + (size_t)t0 * kNS + 2 * lane);
+  B.vn = vnp[t0 + (lane & 31)];
   const uint32_t* src = vc + ((size_t)(t0 / GTQ_VBLOCK) + q) * (32 * VB) + n * (2 * VB);
   if (VB == 2) {
     const uint4 x = *reinterpret_cast<const uint4*>(src);
@@ -645,22 +654,183 @@ __device__ inline void load_block(BlockRegs<VB>& B, const uint32_t* kc, const fl
 #pragma unroll
     for (int i = 0; i < 2 * VB; ++i) B.vw[i] = src[i];
   }
-  B.vn = vnp[t0 + (lane & 31)];
 }
 
-// Phase 1 of the attention: per (row tile, chunk) online-softmax partials.
-template <int VB>
+constexpr int kDepth = 4;  // blocks of a wave in flight
+
+// One step of a wave's online softmax over two 32-token blocks (the second may be
+// absent): stage both, QK, one max / rescale for both, PV.
+template <int VB, int KWL>
+__device__ inline void attn_blocks(const AttnShared& S, AttnWave (&W)[2], const BlockData<VB, KWL>& B0,
+                                   const BlockData<VB, KWL>& B1, bool has1, const AttnArgs& a, int t0a, int t0b,
+                                   int kw, int inv_kw, int lane, int q, int n, int my_row, int my_len,
+                                   const int (&r_nk)[4], const int (&r_grp)[4], const int (&r_bit)[4],
+                                   const int (&r_kb)[4], floatx4 (&oacc)[8], float& m_run, float& l_run) {
+  const int nb = has1 ? 2 : 1;
+  // ---- stage the blocks' key codes (pitch kw + 1), group norms and value norms
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if (b < nb) {
+      const BlockData<VB, KWL>& B = b ? B1 : B0;
+#pragma unroll
+      for (int i = 0; i < KWL; ++i) {
+        const int lw = lane + 64 * i;
+        if (lw < kBlk * kw) W[b].ktile[lw + ((lw * inv_kw) >> 16)] = B.kr[i];  // + token index
+      }
+      W[b].knt[2 * (lane & 1)][lane >> 1] = B.kn.x;
+      W[b].knt[2 * (lane & 1) + 1][lane >> 1] = B.kn.y;
+      if (lane < 32) W[b].vn[lane] = B.vn;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int tau0 = 8 * (n >> 2) + (n & 3);  // A-row n of the two 16-token halves
+  const int ro = tau0 * (kw + 1);
+
+  // ---- QK per key group (one rate each), folded with the per-token group norm into
+  //      the logits of tokens 8q + j (j = 4 half + e) of each block
+  float lg[2][8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lg[b][j] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (r_nk[r] > 0) {
+      floatx4 d[2][2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) d[b][0] = d[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int nk = r_nk[r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < nk) {
+          const int R = r + 1;
+          const int bit = r_bit[r] + R * (32 * i + 8 * q);
+          const int w = bit >> 5, sb = bit & 31;
+          H8 qv;
+          qv.v = S.qb[r_kb[r] + i][q][n];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            if (b < nb) {
+              const uint32_t* p0 = W[b].ktile + ro + w;
+              const uint32_t* p1 = p0 + 4 * (kw + 1);
+              const uint32_t f0 = __builtin_amdgcn_alignbit(p0[1], p0[0], sb);
+              const uint32_t f1 = __builtin_amdgcn_alignbit(p1[1], p1[0], sb);
+              half8 A0, A1;
+              if (r == 0) { A0 = dequant8<1>(S, f0); A1 = dequant8<1>(S, f1); }
+              if (r == 1) { A0 = dequant8<2>(S, f0); A1 = dequant8<2>(S, f1); }
+              if (r == 2) { A0 = dequant8<3>(S, f0); A1 = dequant8<3>(S, f1); }
+              if (r == 3) { A0 = dequant8<4>(S, f0); A1 = dequant8<4>(S, f1); }
+              d[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qv.h, d[b][0], 0, 0, 0);
+              d[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qv.h, d[b][1], 0, 0, 0);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        if (b < nb) {
+          const float4 na = *reinterpret_cast<const float4*>(&W[b].knt[r_grp[r]][8 * q]);
+          const float4 nbv = *reinterpret_cast<const float4*>(&W[b].knt[r_grp[r]][8 * q + 4]);
+          lg[b][0] = fmaf(na.x, d[b][0][0], lg[b][0]);
+          lg[b][1] = fmaf(na.y, d[b][0][1], lg[b][1]);
+          lg[b][2] = fmaf(na.z, d[b][0][2], lg[b][2]);
+          lg[b][3] = fmaf(na.w, d[b][0][3], lg[b][3]);
+          lg[b][4] = fmaf(nbv.x, d[b][1][0], lg[b][4]);
+          lg[b][5] = fmaf(nbv.y, d[b][1][1], lg[b][5]);
+          lg[b][6] = fmaf(nbv.z, d[b][1][2], lg[b][6]);
+          lg[b][7] = fmaf(nbv.w, d[b][1][3], lg[b][7]);
+        }
+      }
+    }
+  }
+  float mblk = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t0 = b ? t0b : t0a;
+    const bool full = b < nb && t0 + kBlk <= my_len;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v = lg[b][j] + dpp_row_mirror(lg[b][j]);
+      if (!full && (b >= nb || t0 + 8 * q + j >= my_len)) v = -INFINITY;
+      lg[b][j] = v;
+      mblk = fmaxf(mblk, v);
+    }
+    if (a.logits && n < 8 && b < nb) {
+      const int id = S.row_id[my_row];
+      if (id >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pos = t0 + 8 * q + j;
+          if (pos < my_len) a.logits[(size_t)id * a.logits_ld + pos] = lg[b][j] * LN2_F;
+        }
+      }
+    }
+  }
+  mblk = max_over_q(mblk);
+  const bool grow = mblk > m_run;
+  if (__any(grow)) {
+    const float m_new = grow ? mblk : m_run;
+    // the accumulators only need rescaling once they hold something
+    const bool rescale = grow && m_run != -INFINITY;
+    if (__any(rescale)) {
+      const float f = rescale ? exp2f(m_run - m_new) : 1.f;
+      l_run *= f;
+      // accumulator rows 4q + e live in lanes with n == row: fetch their factors
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fe = __shfl(f, 4 * q + e);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) oacc[t][e] *= fe;
+      }
+    }
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  // ---- probabilities times value norms, split high/low by column; PV over the 8 value
+  //      tiles (coordinate 8n + t of the rotated basis)
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    if (b < nb) {
+      const float4 vna = *reinterpret_cast<const float4*>(W[b].vn + 8 * q);
+      const float4 vnb = *reinterpret_cast<const float4*>(W[b].vn + 8 * q + 4);
+      const float vn[8] = {vna.x, vna.y, vna.z, vna.w, vnb.x, vnb.y, vnb.z, vnb.w};
+      H8 pa;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float x[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * jj + u;
+          // lg - m_use <= 0: the hardware 2^x (denormal results flush to 0) is exact enough
+          const float p = (lg[b][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[b][j] - m_use);
+          l_run += p;
+          const float pv = (p == 0.f) ? 0.f : p * vn[j];
+          const float hi = (float)(_Float16)pv;
+          x[u] = n < 8 ? hi : pv - hi;
+        }
+        pa.u[jj] = pack2h(x[0], x[1]);
+      }
+      const BlockData<VB, KWL>& B = b ? B1 : B0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S, vfield<VB>(B.vw, t)), oacc[t], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Phase 1 of the attention: per (row tile, split) online-softmax partials.
+template <int VB, int KWL>
 __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  AttnFixed& S = *reinterpret_cast<AttnFixed*>(smem);
-  unsigned char* region = smem + ((sizeof(AttnFixed) + 15) & ~(size_t)15);
+  __shared__ AttnShared S;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int q = lane >> 4, n = lane & 15;
   const int chunk_idx = blockIdx.x;
   const int tile = blockIdx.y;
 
-  // ---- tile -> (sequence, KV head, rows); row ids need no global data
+  // ---- tile -> (sequence, KV head, rows)
   int seq, h, tr;
   if (a.prefill) {
     h = tile / a.tiles_per_kv;
@@ -672,31 +842,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
     h = rem / a.tiles_per_kv;
     tr = rem - h * a.tiles_per_kv;
   }
-  // ---- one round of independent global loads: head table, rotations, query rows,
-  //      sequence length and this wave's first cache block
-  constexpr int kHeadWords = (int)(sizeof(DevHead) / 4);
-  const uint32_t hword = tid < kHeadWords ? reinterpret_cast<const uint32_t*>(a.heads + h)[tid] : 0u;
-  const int krot_n = a.krot_n[h];
-  const float4* rsrc = reinterpret_cast<const float4*>(a.rot + a.krot_off[h]);
-  constexpr int kRotRegs = 8;  // rotations up to 8192 floats arrive in this round
-  float4 rreg[kRotRegs];
-  const int nf4 = krot_n >> 2;
-#pragma unroll
-  for (int u = 0; u < kRotRegs; ++u) rreg[u] = rsrc[min(tid + kThreads * u, nf4 - 1)];
-  float4 qreg;
-  {
-    const int r = tid >> 5, c4 = tid & 31, f = tr * 8 + r;
-    int id = -1;
-    if (a.prefill) {
-      if (f < a.n_tok * a.g) id = (f / a.g) * a.n_q + h * a.g + (f % a.g);
-    } else if (f < a.g) {
-      id = seq * a.n_q + h * a.g + f;
-    }
-    const int idc = id >= 0 ? id : 0;  // row 0 always exists; unused rows are zeroed below
-    qreg = reinterpret_cast<const float4*>(a.q + (size_t)idc * kD)[c4];
-    if (id < 0) qreg = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const int len_ld = a.prefill ? 0 : a.seq_len[seq];
+  const DevHead* __restrict__ hp = a.heads + h;
   const size_t sh = (size_t)seq * a.n_kv + h;
   const int kw = a.k_words;
   const uint32_t* kc = a.k_codes + sh * a.capacity * kw;
@@ -704,337 +850,269 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
   const uint32_t* vc = a.v_codes + sh * (a.capacity / GTQ_VBLOCK) * (32 * VB);
   const float* vnp = a.v_norms + sh * a.capacity;
   const int c0 = chunk_idx * a.chunk;
-  BlockRegs<VB> cur;
-  int t0 = c0 + kBlk * wave;
-  // loads of the first block (clamped to the last block of the cache; unused if outside
-  // the tile's tokens)
-  load_block<VB>(cur, kc, knp, vc, vnp, (int)min<int64_t>(t0, a.capacity - kBlk), kw, lane, q, n);
+  const int cap_last = (int)(a.capacity - kBlk);
+  // ---- first: the loads of this wave's first kDepth blocks (clamped inside the cache;
+  //      unused when outside the tile's tokens), then everything else of the prologue
+  const int n_groups = hp->n_groups;
+  const int len_ld = a.prefill ? 0 : a.seq_len[seq];
+  // this wave's slices of the query rotation (group, first coordinate): slices are
+  // numbered over the groups in order, 16 coordinates each; wave w takes w and w + 8
+  int rg[2] = {-1, -1}, ri0[2] = {0, 0};
+  {
+    int t = 0;
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) {
+      if (g < n_groups) {
+        const int ns = (hp->dim[g] + 15) >> 4;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int idx = wave + kWaves * j;
+          if (idx >= t && idx < t + ns) {
+            rg[j] = g;
+            ri0[j] = 16 * (idx - t);
+          }
+        }
+        t += ns;
+      }
+    }
+  }
+  // Pi_g rows of the slices: lane (q, n) holds row i0 + n, columns k0 + 4q + 0..3 for
+  // k0 = 0, 16, ... (d is even: a pair of columns is wholly inside or outside)
+  float2 pa_[2][8][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int g = rg[j] < 0 ? 0 : rg[j];
+    const int d = rg[j] < 0 ? 0 : hp->dim[g];
+    const float* R = a.rot + hp->krot_off[g];
+    const int i = ri0[j] + n;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kk = 16 * u + 4 * q;
+      pa_[j][u][0] = (i < d && kk < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk) : make_float2(0.f, 0.f);
+      pa_[j][u][1] = (i < d && kk + 2 < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk + 2) : make_float2(0.f, 0.f);
+    }
+  }
 
-  if (tid < kHeadWords) reinterpret_cast<uint32_t*>(&S.hd)[tid] = hword;
-  if (tid < 8) {
-    const int f = tr * 8 + tid;
-    int id = -1, len = 0;
+  // ---- row ids and lengths; query rows in natural order, and the head's record order
+  auto row_of = [&](int r, int* len) {
+    const int f = tr * 8 + r;
+    int id = -1, L = 0;
     if (a.prefill) {
       if (f < a.n_tok * a.g) {
         const int t = f / a.g;
         id = t * a.n_q + h * a.g + (f - t * a.g);
-        len = (int)(a.pos0 + t + 1);
+        L = (int)(a.pos0 + t + 1);
       }
     } else if (f < a.g) {
       id = seq * a.n_q + h * a.g + f;
-      len = min(max(len_ld, 0), a.max_len);
+      L = min(max(len_ld, 0), a.max_len);
     }
+    *len = L;
+    return id;
+  };
+  float qn[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + kThreads * u, r = e >> 7, c = e & (kD - 1);
+    int L;
+    const int id = row_of(r, &L);
+    qn[u] = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
+  }
+  const int crd = tid < kD ? hp->coord[tid] : 0;
+  // this wave's first block (clamped inside the cache; unused when outside the tile's
+  // tokens); the others follow once the prologue's own loads are out
+  BlockData<VB, KWL> blk[kDepth];
+  load_block<VB, KWL>(blk[0], kc, knp, vc, vnp, min(c0 + kBlk * wave, cap_last), kw, lane, q, n);
+  if (tid < 8) {
+    int L;
+    const int id = row_of(tid, &L);
     S.row_id[tid] = id;
-    S.row_len[tid] = len;
+    S.row_len[tid] = L;
   }
-  // decode tables from the kernel arguments
+  (&S.qb[0][0][0])[tid] = make_uint4(0, 0, 0, 0);  // kMaxKB * 64 == kThreads entries
   {
-    const int idx = tid;  // 256 threads, 256 entries
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      S.lut1[idx][k] = pack2h(a.cbv[0][(idx >> (2 * k)) & 1], a.cbv[0][(idx >> (2 * k + 1)) & 1]);
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      S.lut2[idx][k] = pack2h(a.cbv[1][(idx >> (4 * k)) & 3], a.cbv[1][(idx >> (4 * k + 2)) & 3]);
-    if (idx < 64) S.lut3[idx] = pack2h(a.cbv[2][idx & 7], a.cbv[2][(idx >> 3) & 7]);
-    S.lut4[idx] = pack2h(a.cbv[3][idx & 15], a.cbv[3][(idx >> 4) & 15]);
-    for (int e = tid; e < kMaxKB * 64; e += kThreads) (&S.qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
+    // decode tables: byte (or 6 bits) -> binary16 centroids
+    const float* c1 = a.cbv[0];
+    const float* c2 = a.cbv[1];
+    const float* c3 = a.cbv[2];
+    const float* c4 = a.cbv[3];
+    for (int e = tid; e < 1024; e += kThreads) {
+      const int b = e >> 2, k = e & 3;
+      reinterpret_cast<uint32_t*>(S.lut1)[e] = pack2h(c1[(b >> (2 * k)) & 1], c1[(b >> (2 * k + 1)) & 1]);
+    }
+    {
+      const int b = tid >> 1, k = tid & 1;
+      reinterpret_cast<uint32_t*>(S.lut2)[tid] = pack2h(c2[(b >> (4 * k)) & 3], c2[(b >> (4 * k + 2)) & 3]);
+    }
+    if (tid < 64) S.lut3[tid] = pack2h(c3[tid & 7], c3[(tid >> 3) & 7]);
+    if (tid < 256) S.lut4[tid] = pack2h(c4[tid & 15], c4[(tid >> 4) & 15]);
+    if (tid < 4) {  // per rate: its group (at most one), K-blocks, record bit, first K-block
+      int nk = 0, grp = 0, bit = 0, kb = 0, kbs = 0;
+      for (int g = 0; g < n_groups; ++g) {
+        if (hp->rate[g] == tid + 1) {
+          nk = hp->nkb_g[g];
+          grp = g;
+          bit = hp->bit_off[g];
+          kb = kbs;
+        }
+        kbs += hp->nkb_g[g];
+      }
+      S.rate_nk[tid] = nk;
+      S.rate_grp[tid] = grp;
+      S.rate_bit[tid] = bit;
+      S.rate_kb[tid] = kb;
+    }
   }
+  float* qnat = &S.u.slot[1][0][0];  // query rows in natural order [8][128]; clear of qrec
+  qnat[tid] = qn[0];
+  qnat[tid + kThreads] = qn[1];
   __syncthreads();
   int tile_len = 0;
 #pragma unroll
   for (int r = 0; r < 8; ++r) tile_len = max(tile_len, S.row_len[r]);
-  if (c0 >= tile_len) return;  // no cached token of this tile in this chunk
-  const DevHead& hd = S.hd;
+  if (c0 >= tile_len) return;  // no cached token of this tile in this split
   const int c1 = min(c0 + a.chunk, tile_len);
-  const int n_groups = hd.n_groups;
-
-  float* rotk_t = reinterpret_cast<float*>(region);  // per group: rows of Pi_g at pitch d + 1
-  float(*qrec)[kD] = reinterpret_cast<float(*)[kD]>(region + ((size_t)krot_n + kD + 4) * 4);
-  // ---- key rotations into LDS, row-major at row pitch d + 1; query rows in record order
-  int gbase[kMaxGroups], gpad[kMaxGroups];  // per group: float offset in global slice / in LDS
-  {
-    int gb = 0, gp = 0;
+  if (tid < kD) {  // record order: qrec[r][pos] = q[r][coord[pos]]
 #pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g) {
-      gbase[g] = gb;
-      gpad[g] = gp;
-      const int d = g < n_groups ? hd.dim[g] : 0;
-      gb += d * d;
-      gp += d * (d + 1);
-    }
-  }
-  for (int u = 0; u < 16; ++u) {
-    const int e4 = tid + kThreads * u;
-    if (e4 < (krot_n >> 2)) {
-      float4 x4;
-      if (u < kRotRegs) {
-#pragma unroll
-        for (int v = 0; v < kRotRegs; ++v)
-          if (v == u) x4 = rreg[v];
-      } else {
-        x4 = rsrc[e4];  // larger rotations: a second round
-      }
-      const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int e = 4 * e4 + v4;
-        int g = 0;
-#pragma unroll
-        for (int gg = 1; gg < kMaxGroups; ++gg)
-          if (gg < n_groups && e >= gbase[gg]) g = gg;
-        const int d = hd.dim[g], idx = e - gbase[g];
-        const int i = idx / d;
-        rotk_t[gpad[g] + idx + i] = xs[v4];  // (i, j) at i (d + 1) + j
-      }
-    }
-  }
-  {
-    float* qraw = &S.oacc_scratch[0][0];
-    reinterpret_cast<float4*>(qraw)[tid] = qreg;  // [8][128] rows as loaded
+    for (int r = 0; r < 8; ++r) S.u.qrec[r][tid] = qnat[r * kD + crd];
   }
   __syncthreads();
-  for (int e = tid; e < 8 * kD; e += kThreads) qrec[e >> 7][e & 127] = S.oacc_scratch[e >> 7][hd.coord[e & 127]];
-  __syncthreads();
-  // ---- rotated queries into the QK B operand (column r: high part, 15-r: low part)
-  for (int e = tid; e < 8 * kD; e += kThreads) {
-    const int r = e >> 7, p = e & 127;
-    if (S.row_id[r] < 0) continue;
-    int g = 0;
-#pragma unroll
-    for (int gg = 1; gg < kMaxGroups; ++gg)
-      if (gg < n_groups && p >= hd.pos_off[gg]) g = gg;
-    int base = 0;
-#pragma unroll
-    for (int gg = 0; gg < kMaxGroups; ++gg)
-      if (gg == g) base = gpad[gg];
-    const int d = hd.dim[g], i = p - hd.pos_off[g];
-    const float* rt = rotk_t + base + i * (d + 1);  // row i of Pi_g
-    const float* xq = qrec[r] + hd.pos_off[g];
-    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
-    int j = 0;
-    for (; j + 4 <= d; j += 4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc4[u] = fmaf(rt[j + u], xq[j + u], acc4[u]);
-    }
-    for (; j < d; ++j) acc4[0] = fmaf(rt[j], xq[j], acc4[0]);
-    const float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-    const float val = acc * (a.qscale / sqrtf((float)d));
-    const _Float16 hi = (_Float16)val;
-    const _Float16 lo = (_Float16)(val - (float)hi);
-    const int kp = hd.kp_off[g] + i;
-    _Float16* bh = reinterpret_cast<_Float16*>(&S.qb[kp >> 5][(kp >> 3) & 3][r]);
-    _Float16* bl = reinterpret_cast<_Float16*>(&S.qb[kp >> 5][(kp >> 3) & 3][15 - r]);
-    bh[kp & 7] = hi;
-    bl[kp & 7] = lo;
-  }
-  __syncthreads();  // the prologue part of the region is free from here on
 
+  // ---- query rotation on the matrix cores (fp32 MFMA 16x16x4): D[i][r] =
+  //      sum_k Pi_g[i0 + i][k] qrec[r][pos_off + k]; the 4 k of lane (q, n) per MFMA
+  //      are k0 + 4q + s
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (rg[j] >= 0) {
+      const int g = rg[j], i0 = ri0[j];
+      const int d = hp->dim[g], po = hp->pos_off[g], kp0 = hp->kp_off[g];
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (16 * u < d) {
+          const int kk = 16 * u + 4 * q;
+          float2 b0 = make_float2(0.f, 0.f), b1 = make_float2(0.f, 0.f);
+          if (n < 8 && kk < d) b0 = *reinterpret_cast<const float2*>(&S.u.qrec[n][po + kk]);
+          if (n < 8 && kk + 2 < d) b1 = *reinterpret_cast<const float2*>(&S.u.qrec[n][po + kk + 2]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa_[j][u][0].x, b0.x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa_[j][u][0].y, b0.y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa_[j][u][1].x, b1.x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa_[j][u][1].y, b1.y, acc, 0, 0, 0);
+        }
+      }
+      // lane (q, n) holds D[4q + e][n]: coordinate i0 + 4q + e of row n
+      if (n < 8) {
+        const float sc = a.qscale / sqrtf((float)d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = i0 + 4 * q + e;
+          if (ii < d) {
+            const float val = acc[e] * sc;
+            const _Float16 hi = (_Float16)val;
+            const _Float16 lo = (_Float16)(val - (float)hi);
+            const int kp = kp0 + ii;
+            reinterpret_cast<_Float16*>(&S.qb[kp >> 5][(kp >> 3) & 3][n])[kp & 7] = hi;
+            reinterpret_cast<_Float16*>(&S.qb[kp >> 5][(kp >> 3) & 3][15 - n])[kp & 7] = lo;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();  // B operand ready; the query rows' space becomes the wave tiles
+
+  // ---- per rate 1..4 (uniform): K-blocks, group, record bit, first K-block
+  int r_nk[4], r_grp[4], r_bit[4], r_kb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    r_nk[r] = __builtin_amdgcn_readfirstlane(S.rate_nk[r]);
+    r_grp[r] = __builtin_amdgcn_readfirstlane(S.rate_grp[r]);
+    r_bit[r] = __builtin_amdgcn_readfirstlane(S.rate_bit[r]);
+    r_kb[r] = __builtin_amdgcn_readfirstlane(S.rate_kb[r]);
+  }
   const int my_row = n < 8 ? n : 15 - n;
   const int my_len = S.row_len[my_row];
   const int inv_kw = (65536 + kw - 1) / kw;  // floor(lw * inv_kw / 2^16) == lw / kw for lw < 512
-  AttnWave& W = reinterpret_cast<AttnWave*>(region)[wave];
-  uint32_t* kt = W.ktile;
-  float* kn = W.kn;
-  float* vnl = W.vn;
+  AttnWave(&W)[2] = S.u.w[wave];
+  constexpr int kStep = kBlk * kWaves;
+#pragma unroll
+  for (int j = 1; j < kDepth; ++j) {
+    const int t = c0 + kBlk * wave + kStep * j;
+    if (t < c1) load_block<VB, KWL>(blk[j], kc, knp, vc, vnp, t, kw, lane, q, n);
+  }
 
   floatx4 oacc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) oacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (; t0 < c1; t0 += kBlk * kWaves) {
-    BlockRegs<VB> nxt;
-    const int tn = t0 + kBlk * kWaves;
-    // next block (this block again if none is left: same addresses, cached)
-    load_block<VB>(nxt, kc, knp, vc, vnp, tn < c1 ? tn : t0, kw, lane, q, n);
-    // ---- stage this block's key codes (pitch kw + 1) and norms, value norms in LDS
+  // ---- main loop: kDepth blocks per round, two per step; each register set is
+  //      refilled kDepth blocks ahead
+  for (int tb = c0 + kBlk * wave; tb < c1; tb += kStep * kDepth) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int lw = lane + 64 * i;
-      if (lw < kBlk * kw) kt[lw + ((lw * inv_kw) >> 16)] = cur.kr[i];  // + token index
-    }
-    kn[2 * lane] = cur.kn.x;
-    kn[2 * lane + 1] = cur.kn.y;
-    if (lane < 32) vnl[lane] = cur.vn;
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- QK per key group, folded into the logits of tokens 8q + j (j = 4*half + e)
-    float lg[8];
+    for (int j = 0; j < kDepth; j += 2) {
+      const int ta = tb + kStep * j, tb2 = ta + kStep;
+      if (ta < c1) {
+        attn_blocks<VB, KWL>(S, W, blk[j], blk[j + 1], tb2 < c1, a, ta, tb2, kw, inv_kw, lane, q, n, my_row,
+                             my_len, r_nk, r_grp, r_bit, r_kb, oacc, m_run, l_run);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lg[j] = 0.f;
-    int kb0 = 0;
-#pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g) {
-      if (g < n_groups) {
-        floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-        const int nk = hd.nkb_g[g];
-        switch (hd.rate[g]) {
-          case 1: qk_group<1>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, d0, d1); break;
-          case 2: qk_group<2>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, d0, d1); break;
-          case 3: qk_group<3>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, d0, d1); break;
-          default: qk_group<4>(S, kt, kw, kb0, nk, hd.kb_bit, q, n, d0, d1); break;
-        }
-        kb0 += nk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lg[e] = fmaf(kn[(8 * q + e) * kNS + g], d0[e], lg[e]);
-          lg[4 + e] = fmaf(kn[(8 * q + 4 + e) * kNS + g], d1[e], lg[4 + e]);
+        for (int u = 0; u < 2; ++u) {
+          const int tn = ta + kStep * (u + kDepth);
+          if (tn < c1) load_block<VB, KWL>(blk[j + u], kc, knp, vc, vnp, tn, kw, lane, q, n);
         }
       }
     }
-    float mblk = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v = lg[j] + dpp_row_mirror(lg[j]);
-      const int pos = t0 + 8 * q + j;
-      if (pos >= my_len) v = -INFINITY;
-      lg[j] = v;
-      mblk = fmaxf(mblk, v);
-    }
-    if (a.logits && n < 8) {
-      const int id = S.row_id[my_row];
-      if (id >= 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int pos = t0 + 8 * q + j;
-          if (pos < my_len) a.logits[(size_t)id * a.logits_ld + pos] = lg[j] * LN2_F;
-        }
-      }
-    }
-    mblk = fmaxf(mblk, __shfl_xor(mblk, 16));
-    mblk = fmaxf(mblk, __shfl_xor(mblk, 32));
-    const float m_new = fmaxf(m_run, mblk);
-    // rescale the running state when a row's maximum grows
-    const bool grow = m_new > m_run;
-    if (__any(grow)) {
-      const float f = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      l_run *= grow ? f : 1.f;
-      // accumulator rows 4q+e live in lanes with n == row: fetch their factors
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float fe = __shfl(grow ? f : 1.f, 4 * q + e);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) oacc[t][e] *= fe;
-      }
-    }
-    m_run = m_new;
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    // ---- probabilities times value norms, split high/low by column
-    const float4 vna = *reinterpret_cast<const float4*>(vnl + 8 * q);
-    const float4 vnb = *reinterpret_cast<const float4*>(vnl + 8 * q + 4);
-    const float vn[8] = {vna.x, vna.y, vna.z, vna.w, vnb.x, vnb.y, vnb.z, vnb.w};
-    uint32_t pp[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float x[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int j = 2 * jj + u;
-        // lg - m_use <= 0: the hardware 2^x (denormal results flush to 0) is exact enough
-        const float p = (lg[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[j] - m_use);
-        l_run += p;
-        const float pv = (p == 0.f) ? 0.f : p * vn[j];
-        const float hi = (float)(_Float16)pv;
-        x[u] = n < 8 ? hi : pv - hi;
-      }
-      pp[jj] = pack2h(x[0], x[1]);
-    }
-    H8 pa;
-    pa.u[0] = pp[0];
-    pa.u[1] = pp[1];
-    pa.u[2] = pp[2];
-    pa.u[3] = pp[3];
-    // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
-    half8 vbs[8];  // all value operands of the block first, then the 8 products
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t F = vfield<VB>(cur.vw, t);
-      if (VB == 1) vbs[t] = dequant8<1>(S, F);
-      else if (VB == 2) vbs[t] = dequant8<2>(S, F);
-      else if (VB == 3) vbs[t] = dequant8<3>(S, F);
-      else vbs[t] = dequant8<4>(S, F);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, vbs[t], oacc[t], 0, 0, 0);
-    __builtin_amdgcn_wave_barrier();
-    cur = nxt;
   }
 
   // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  float vrow[8][4];  // combined rows 4q+e (q < 2) for the 8 tiles
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + __shfl_xor(oacc[t][3 - e], 48);
-  }
+  l_run = sum_over_q(l_run);
   if (q == 0 && n < 8) {
     S.om[wave][n] = m_run;
     S.ol[wave][n] = l_run;
   }
-  __syncthreads();  // every wave is done with its key tile
-  float(*slots)[8][kD] = reinterpret_cast<float(*)[8][kD]>(region);  // [kWaves/2][8][128]
-  const int slot = wave & (kWaves / 2 - 1);
-  if (wave < kWaves / 2 && q < 2) {
+  // combined rows 4q + e (q < 2): own high row plus the low row held by lane l ^ 48
+  float vrow[8][4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < 8; ++t) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) slots[slot][4 * q + e][8 * n + t] = vrow[t][e];
+    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
   }
-  __syncthreads();
-  if (wave >= kWaves / 2 && q < 2) {
+  __syncthreads();  // every wave is done with its key tile
+  if (q < 2) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 4 * q + e;
-      const float ma = S.om[slot][r], mb = S.om[wave][r];
-      const float M = fmaxf(ma, mb);
-      const float sa = (ma == -INFINITY) ? 0.f : exp2f(ma - M);
-      const float sb = (mb == -INFINITY) ? 0.f : exp2f(mb - M);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        float* pd = &slots[slot][r][8 * n + t];
-        *pd = sa * *pd + sb * vrow[t][e];
-      }
+      float* dst = &S.u.slot[wave][4 * q + e][8 * n];
+      *reinterpret_cast<float4*>(dst) = make_float4(vrow[0][e], vrow[1][e], vrow[2][e], vrow[3][e]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(vrow[4][e], vrow[5][e], vrow[6][e], vrow[7][e]);
     }
   }
   __syncthreads();
-  if (tid < 8 * (kWaves / 2)) {  // merged (m, l) of each slot pair
-    const int sl = tid >> 3, r = tid & 7;
-    const float ma = S.om[sl][r], mb = S.om[sl + kWaves / 2][r];
-    const float M = fmaxf(ma, mb);
-    const float sa = (ma == -INFINITY) ? 0.f : exp2f(ma - M);
-    const float sb = (mb == -INFINITY) ? 0.f : exp2f(mb - M);
-    S.ol[sl][r] = sa * S.ol[sl][r] + sb * S.ol[sl + kWaves / 2][r];
-    S.om[sl][r] = M;
-  }
-  __syncthreads();
-  // ---- publish one partial (m, l, acc) per row for this chunk
-  for (int e = tid; e < 8 * (kD / 4); e += kThreads) {
-    const int r = e >> 5, c4 = e & 31;
+  // ---- one partial (m, l, acc) per row for this split
+  if (tid < 8 * (kD / 4)) {
+    const int r = tid >> 5, c4 = tid & 31;
     const int id = S.row_id[r];
-    if (id < 0) continue;
-    float M = -INFINITY;
+    if (id >= 0) {
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves / 2; ++w) M = fmaxf(M, S.om[w][r]);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float l = 0.f;
-    if (M != -INFINITY) {
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.om[w][r]);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float l = 0.f;
+      if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves / 2; ++w) {
-        const float s = exp2f(S.om[w][r] - M);
-        const float4 x = *reinterpret_cast<const float4*>(&slots[w][r][4 * c4]);
-        acc.x = fmaf(s, x.x, acc.x);
-        acc.y = fmaf(s, x.y, acc.y);
-        acc.z = fmaf(s, x.z, acc.z);
-        acc.w = fmaf(s, x.w, acc.w);
-        l = fmaf(s, S.ol[w][r], l);
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = S.om[w][r];
+          const float s = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+          const float4 x = *reinterpret_cast<const float4*>(&S.u.slot[w][r][4 * c4]);
+          acc.x = fmaf(s, x.x, acc.x);
+          acc.y = fmaf(s, x.y, acc.y);
+          acc.z = fmaf(s, x.z, acc.z);
+          acc.w = fmaf(s, x.w, acc.w);
+          l = fmaf(s, S.ol[w][r], l);
+        }
       }
+      float* dst = a.partials + ((size_t)id * a.n_chunks + chunk_idx) * kPS;
+      *reinterpret_cast<float4*>(dst + 4 + 4 * c4) = acc;
+      if (c4 == 0) *reinterpret_cast<float4*>(dst) = make_float4(M, l, 0.f, 0.f);
     }
-    float* dst = a.partials + ((size_t)id * a.n_chunks + chunk_idx) * kPS;
-    *reinterpret_cast<float4*>(dst + 4 + 4 * c4) = acc;
-    if (c4 == 0) *reinterpret_cast<float4*>(dst) = make_float4(M, l, 0.f, 0.f);
   }
 }
 
@@ -1228,13 +1306,15 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
 }
 
 int auto_chunk(int64_t max_len, int64_t tiles) {
-  // about two 4-wave workgroups per compute unit; at least 4 splits per row tile
-  // so that ragged batches balance; splits of whole 128-token rounds (4 waves x 32)
-  int64_t target = std::max<int64_t>(1, 512 / std::max<int64_t>(1, tiles));
-  target = std::min<int64_t>(kMaxChunks, std::max<int64_t>(4, target));
+  // one round of workgroups (one per compute unit), at least 4 splits per row tile so
+  // that ragged batches balance; splits of whole rounds of the main loop (8 waves x
+  // 4 blocks x 32 tokens)
+  constexpr int64_t kRound = kBlk * kWaves * kDepth;
+  int64_t target = std::max<int64_t>(4, 256 / std::max<int64_t>(1, tiles));
+  target = std::min<int64_t>(kMaxChunks, target);
   int64_t ch = (max_len + target - 1) / target;
-  ch = ((ch + 127) / 128) * 128;
-  return (int)std::max<int64_t>(128, ch);
+  ch = ((ch + kRound - 1) / kRound) * kRound;
+  return (int)std::max<int64_t>(kRound, ch);
 }
 
 size_t attn_ws_bytes(int64_t rows, int64_t n_chunks) { return (size_t)rows * n_chunks * kPS * 4; }
@@ -1251,7 +1331,6 @@ gtq_status launch_partials(const gtq_plan* p, int layer, const gtq_cache_view* c
                            AttnArgs& aa, const AttnLaunch& L, float scale, void* ws, hipStream_t stream) {
   aa.heads = p->d_heads + (size_t)layer * p->n_kv;
   aa.rot = p->d_rot;
-  aa.cb = p->d_cb;
   aa.k_codes = c->k_codes;
   aa.k_norms = c->k_norms;
   aa.v_codes = c->v_codes;
@@ -1267,33 +1346,21 @@ gtq_status launch_partials(const gtq_plan* p, int layer, const gtq_cache_view* c
   aa.chunk = L.chunk;
   aa.n_chunks = L.n_chunks;
   aa.qscale = scale * LOG2E_F;
-  if (p->n_kv > kMaxArgHeads)
-    return fail(GTQ_EUNSUPPORTED, "gtq attention: more than 64 KV heads per layer");
+  if (p->k_words > 16) return fail(GTQ_EUNSUPPORTED, "gtq attention: more than 16 key code words per token");
   for (int b = 1; b <= 4; ++b)
     for (int k = 0; k < 16; ++k) aa.cbv[b - 1][k] = p->cb.c[b][k];
-  int kr = 0;
-  for (int h = 0; h < p->n_kv; ++h) {
-    const DevHead& dh = p->heads[(size_t)layer * p->n_kv + h];
-    kr = std::max(kr, dh.krot_floats);
-    aa.krot_off[h] = dh.krot_off[0];
-    aa.krot_n[h] = dh.krot_floats;
-  }
-  aa.region_bytes = (int32_t)attn_region_bytes(kr);
-  const size_t lds = ((sizeof(AttnFixed) + 15) & ~(size_t)15) + aa.region_bytes;
-  const int lds_max = (int)(((sizeof(AttnFixed) + 15) & ~(size_t)15) + attn_region_bytes(kD * kD));
-  static const hipError_t attr[4] = {
-      hipFuncSetAttribute((const void*)attn_partials_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max),
-      hipFuncSetAttribute((const void*)attn_partials_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max),
-      hipFuncSetAttribute((const void*)attn_partials_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max),
-      hipFuncSetAttribute((const void*)attn_partials_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max)};
-  if (attr[p->v_bits - 1] != hipSuccess) return hip_fail(attr[p->v_bits - 1], "gtq attention: LDS attribute");
   dim3 grid(L.n_chunks, L.n_tiles);
+  const bool wide = p->k_words > 8;  // key words per lane: 4 (k_words <= 8) or 8
+#define GTQ_LAUNCH(VB)                                                                          \
+  if (wide) hipLaunchKernelGGL((attn_partials_kernel<VB, 8>), grid, dim3(kThreads), 0, stream, aa); \
+  else hipLaunchKernelGGL((attn_partials_kernel<VB, 4>), grid, dim3(kThreads), 0, stream, aa);
   switch (p->v_bits) {
-    case 1: hipLaunchKernelGGL(attn_partials_kernel<1>, grid, dim3(kThreads), lds, stream, aa); break;
-    case 2: hipLaunchKernelGGL(attn_partials_kernel<2>, grid, dim3(kThreads), lds, stream, aa); break;
-    case 3: hipLaunchKernelGGL(attn_partials_kernel<3>, grid, dim3(kThreads), lds, stream, aa); break;
-    default: hipLaunchKernelGGL(attn_partials_kernel<4>, grid, dim3(kThreads), lds, stream, aa); break;
+    case 1: GTQ_LAUNCH(1) break;
+    case 2: GTQ_LAUNCH(2) break;
+    case 3: GTQ_LAUNCH(3) break;
+    default: GTQ_LAUNCH(4) break;
   }
+#undef GTQ_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq attention partials: launch");
   return ok();

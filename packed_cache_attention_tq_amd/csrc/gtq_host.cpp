@@ -95,10 +95,23 @@ static const Tables& tables() {
   return t;
 }
 
+static uint32_t half_bits(float x) {
+  const _Float16 h = (_Float16)x;  // exact: the centroids are binary16 values
+  uint16_t u;
+  memcpy(&u, &h, 2);
+  return u;
+}
+
 void fill_codebook(DevCodebook* cb) {
   const Tables& t = tables();
   memcpy(cb->c, t.cent, sizeof(cb->c));
   memcpy(cb->t, t.thr, sizeof(cb->t));
+  memset(cb->pair, 0, sizeof(cb->pair));
+  for (int b = 1; b <= 4; ++b) {
+    const int base = ((1 << (2 * b)) - 4) / 3, m = (1 << b) - 1;
+    for (int x = 0; x < (1 << (2 * b)); ++x)
+      cb->pair[base + x] = half_bits(t.cent[b][x & m]) | (half_bits(t.cent[b][x >> b]) << 16);
+  }
 }
 
 // ---------------------------------------------------------------- layouts
@@ -136,7 +149,10 @@ void build_head(const uint8_t* rates, int layout, gtq_head_layout* lay, DevHead*
     dh->krot_off[g] = rot;  // relative; made absolute by the plan
     const int nk = (d + kKB - 1) / kKB;
     dh->nkb_g[g] = nk;
-    for (int i = 0; i < nk; ++i) dh->kb_bit[kb + i] = bit + i * kKB * r;
+    for (int i = 0; i < nk; ++i) {
+      dh->kb_bit[kb + i] = bit + i * kKB * r;
+      dh->kb_rg[kb + i] = r | (g << 8);
+    }
     for (int j = 0; j < kJ; ++j) {
       if (rates[j] != r) continue;
       int a, b;
@@ -155,6 +171,10 @@ void build_head(const uint8_t* rates, int layout, gtq_head_layout* lay, DevHead*
   }
   dh->n_groups = lay->n_groups;
   dh->nkb = kb;
+  for (int i = kb; i < kMaxKB; ++i) {  // unused slots: valid reads, multiplied by zero
+    dh->kb_bit[i] = dh->kb_bit[0];
+    dh->kb_rg[i] = dh->kb_rg[0];
+  }
   dh->krot_floats = rot;
   lay->k_words = (bit + 31) / 32;
 }

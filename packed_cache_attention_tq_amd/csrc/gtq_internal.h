@@ -30,6 +30,7 @@ struct DevHead {
   int32_t kp_off[kMaxGroups];     // group start in the padded K-block order
   int32_t nkb_g[kMaxGroups];      // K-blocks of each group
   int32_t kb_bit[kMaxKB];         // record bit of each K-block's first coordinate
+  int32_t kb_rg[kMaxKB];          // rate | group << 8 of each K-block; slots past nkb repeat slot 0
   int64_t krot_off[kMaxGroups];   // float offset of Pi_g (row-major d x d) in the pool
   int64_t vrot_off;               // float offset of Pi_V (row-major 128 x 128)
   int64_t vrot_t_off;             // float offset of Pi_V^T (row-major, i.e. Pi_V column-major)
@@ -38,9 +39,14 @@ struct DevHead {
   uint8_t coord[kD];              // record position -> head coordinate
 };
 
+constexpr int kPairTable = 340;  // (code, code) pairs of rates 1..4: 4 + 16 + 64 + 256 entries
+
 struct DevCodebook {
   float c[5][16];   // c[b][k]: centroid k of rate b (binary16 values)
   float t[5][16];   // t[b][k]: threshold k of rate b (midpoints), k < 2^b - 1
+  // decode table: entry (4^b - 4) / 3 + (k0 | k1 << b) holds the binary16 centroids
+  // k0 (low half) and k1 (high half) of rate b
+  uint32_t pair[kPairTable + 4];
 };
 
 }  // namespace gtq
