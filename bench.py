@@ -3,8 +3,8 @@
 One step = one decode step of one Llama-3.1-8B-shaped attention layer at batch 1:
 quantize-append the step's new key/value token (8 KV heads) into the packed cache,
 then split-K packed decode attention of the 32 query heads over the 32768 cached
-tokens (one kernel for the rotated queries and the per-split online-softmax partials,
-one for the log-sum-exp merge and inverse value rotation). Inputs are seeded synthetic tensors with the pages' distributions,
+tokens (the query rotation, the per-split online-softmax partials, and the
+log-sum-exp merge with the inverse value rotation: three kernels). Inputs are seeded synthetic tensors with the pages' distributions,
 resident in HBM before timing. The cache is replicated into --copies layer caches
 that the steps cycle through (as a 32-layer stack would), so that each step reads
 its cache from HBM rather than from the 256 MB last-level cache.
@@ -176,9 +176,10 @@ def main():
     def step(i, ev=None):
         c = caches[i % len(caches)]
         G.gtq_quantize_append(plan, 0, c, k_new, v_new, seq_idx, slot, stream=stream)
+        G.gtq_decode_rotate_queries(plan, 0, c, q, n, scale, ws, chunk=args.chunk, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        G.gtq_decode_attn_partials(plan, 0, c, q, seq_len, n, scale, ws, chunk=args.chunk, stream=stream)
+        G.gtq_decode_attn_partials(plan, 0, c, seq_len, n, ws, chunk=args.chunk, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         G.gtq_decode_attn_merge(plan, 0, c, seq_len, n, out, ws, chunk=args.chunk, stream=stream)

@@ -219,8 +219,10 @@ gtq_status gtq_quantize_append_chunk(const gtq_plan* plan, int32_t layer,
 
 /* Workspace bytes that gtq_decode_attn needs for `batch` sequences of at most
  * max_len cached tokens with split size `chunk` (0 = automatic; else a multiple of
- * 32, at most 256 splits per sequence). The workspace holds the split-K partials
- * (m, l, acc[128] per query row and split); its contents need no initialisation.
+ * 32, at most 256 splits per sequence). The workspace holds the rotated queries
+ * (8 KB per tile of up to 8 query rows of one sequence and KV head) and the split-K
+ * partials (m, l, acc[128] per query row and split); its contents need no
+ * initialisation.
  * Calls that share a workspace must be ordered on one stream. */
 gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64_t max_len,
                                       int32_t chunk, size_t* out);
@@ -248,15 +250,22 @@ gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_
                            float softmax_scale, int32_t chunk, float* out, float* logits,
                            void* workspace, size_t ws_bytes, void* hip_stream);
 
-/* The two phases of gtq_decode_attn, for callers that interleave other work between
- * them or time them separately. The partials phase writes, per query row and split, the
- * running maximum m (base 2), the sum l of 2^(logit*log2(e) - m) and the accumulator of
- * p * nu_V * C[vcode] in the value rotation's basis into the workspace; the merge phase
- * reads them with the same (seq_len, max_len, chunk) and writes `out`. Arguments and
- * errors as for gtq_decode_attn. */
+/* The three phases of gtq_decode_attn, for callers that interleave other work between
+ * them or time them separately; all three take the same (cache, max_len, chunk) and
+ * workspace, ordered on one stream.
+ * gtq_decode_rotate_queries: r_g = Pi_g q_g for every key group of every query row
+ *   (the query side of the logit above), scaled by softmax_scale * log2(e) / sqrt(d_g),
+ *   stored in the workspace as the operand the partials phase reads. Errors as for
+ *   gtq_decode_attn.
+ * gtq_decode_attn_partials: per query row and split, the running maximum m (base 2),
+ *   the sum l of 2^(logit*log2(e) - m) and the accumulator of p * nu_V * C[vcode] in
+ *   the value rotation's basis, into the workspace (needs the rotated queries).
+ * gtq_decode_attn_merge: combines the splits and writes `out`. */
+gtq_status gtq_decode_rotate_queries(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                     const float* q, int64_t max_len, float softmax_scale, int32_t chunk,
+                                     void* workspace, size_t ws_bytes, void* hip_stream);
 gtq_status gtq_decode_attn_partials(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
-                                    const float* q, const int32_t* seq_len, int64_t max_len,
-                                    float softmax_scale, int32_t chunk, float* logits,
+                                    const int32_t* seq_len, int64_t max_len, int32_t chunk, float* logits,
                                     void* workspace, size_t ws_bytes, void* hip_stream);
 gtq_status gtq_decode_attn_merge(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
                                  const int32_t* seq_len, int64_t max_len, int32_t chunk, float* out,

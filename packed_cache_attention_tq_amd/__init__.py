@@ -84,9 +84,12 @@ _SIGS = [
     ("gtq_decode_attn", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_void_p,
                                     C.c_int64, C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("gtq_decode_rotate_queries", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p,
+                                              C.c_int64, C.c_float, C.c_int32, C.c_void_p, C.c_size_t,
+                                              C.c_void_p]),
     ("gtq_decode_attn_partials", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p,
-                                             C.c_void_p, C.c_int64, C.c_float, C.c_int32, C.c_void_p,
-                                             C.c_void_p, C.c_size_t, C.c_void_p]),
+                                             C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t,
+                                             C.c_void_p]),
     ("gtq_decode_attn_merge", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_int64,
                                           C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     ("gtq_prefill_workspace_bytes", C.c_int32, [C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
@@ -307,12 +310,21 @@ def gtq_decode_attn(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_
     return out
 
 
-def gtq_decode_attn_partials(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_len: int,
-                             scale: float, workspace, chunk: int = 0, logits=None, stream=None):
+def gtq_decode_rotate_queries(plan: Plan, layer: int, cache: PackedCache, q, max_len: int, scale: float,
+                              workspace, chunk: int = 0, stream=None):
     cv = cache.view()
-    st = lib().gtq_decode_attn_partials(plan.handle, layer, C.byref(cv), _dev(q, torch.float32, "q"),
-                                        _dev(seq_len, torch.int32, "seq_len"), max_len, float(scale), chunk,
-                                        _dev(logits, torch.float32, "logits"), _dev(workspace, None, "workspace"),
+    st = lib().gtq_decode_rotate_queries(plan.handle, layer, C.byref(cv), _dev(q, torch.float32, "q"), max_len,
+                                         float(scale), chunk, _dev(workspace, None, "workspace"),
+                                         workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gtq_decode_rotate_queries")
+
+
+def gtq_decode_attn_partials(plan: Plan, layer: int, cache: PackedCache, seq_len, max_len: int, workspace,
+                             chunk: int = 0, logits=None, stream=None):
+    cv = cache.view()
+    st = lib().gtq_decode_attn_partials(plan.handle, layer, C.byref(cv), _dev(seq_len, torch.int32, "seq_len"),
+                                        max_len, chunk, _dev(logits, torch.float32, "logits"),
+                                        _dev(workspace, None, "workspace"),
                                         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gtq_decode_attn_partials")
 

@@ -440,43 +440,47 @@ __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
 
 // ============================================================================
 // Split-K attention over the packed cache (Block-GTQ page, abstract, 5th
-// sentence): phase 1 writes one online-softmax partial (m, l, acc[128]) per query
-// row and split; phase 2 (attn_merge_kernel) combines the splits.
-//
-// A workgroup (8 waves) takes one row tile (up to 8 query rows of one sequence and
-// KV head) and one split of `chunk` cached tokens; each wave walks 32-token blocks.
-// Prologue: r_g = Pi_g q_g for every key group and row on the matrix cores
-//   (fp32 MFMA 16x16x4), scaled by scale / sqrt(d_g) * log2(e) and split into a
-//   binary16 high part and a binary16 remainder (together ~22 bits): the QK
-//   B operand. Columns 0..7 hold the high parts of rows 0..7, columns 8..15 the
-//   low parts of rows 7..0.
-// Per block:
-//   QK: MFMA 16x16x32 f16 per 32-coordinate K-block of a key group; A = decoded
-//       key codes (exact binary16 codebook values, two codes per table read),
-//       16 tokens per A tile. The per-token group norm multiplies each group's
-//       product; a row-mirror DPP then adds the high and low halves.
+// sentence), in three launches:
+//   attn_qrot_kernel      r_g = Pi_g q_g for every key group and query row, scaled by
+//                         scale / sqrt(d_g) * log2(e) and split into a binary16 high part
+//                         and a binary16 remainder (together ~22 bits): the QK B operand
+//                         of each row tile (columns 0..7: high parts of rows 0..7,
+//                         columns 8..15: low parts of rows 7..0), kept in the workspace;
+//   attn_partials_kernel  per (row tile, split of `chunk` tokens) one online-softmax
+//                         partial (m, l, acc[128]) per row;
+//   attn_merge_kernel     log-sum-exp merge of the splits and o = Pi_V^T acc / sqrt(128).
+// Partials: a workgroup (8 waves) takes one row tile (up to 8 query rows of one sequence
+// and KV head) and one split; each wave walks 32-token blocks:
+//   QK: MFMA 16x16x32 f16 per 32-coordinate K-block of a key group; A = decoded key
+//       codes (exact binary16 codebook values, two codes per table read), 16 tokens per
+//       A tile. The per-token group norm multiplies each group's product; a row-mirror
+//       DPP then adds the high and low halves.
 //   online softmax in base 2 (the scale carries log2(e));
 //   PV: MFMA with A = p * nu_V split into high/low parts (rows as above) and
-//       B = decoded value codes (8 tokens x 16 coordinates), accumulating in the
-//       value rotation's basis.
-// Epilogue: the waves merge through LDS into one partial per row.
+//       B = decoded value codes (8 tokens x 16 coordinates), accumulating in the value
+//       rotation's basis.
+// The waves merge through LDS into one partial per row.
 // ============================================================================
 
-constexpr int kWaves = 8;          // waves per workgroup
+constexpr int kWaves = 8;          // waves per partials workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPS = 132;           // partial record: m, l, 2 pad, acc[128] (16-byte aligned acc)
 constexpr int kMaxChunks = 256;    // splits per row
+constexpr int kQB = kMaxKB * 64;   // uint4 entries of a tile's QK B operand (8 KB)
+constexpr int kDepth = 2;          // blocks of a wave in flight
 
 struct AttnArgs {
   const DevHead* heads;
   const float* rot;
+  const DevCodebook* cb;
   const uint32_t* k_codes;
   const float* k_norms;
   const uint32_t* v_codes;
   const float* v_norms;
-  const float* q;          // [rows][128]
+  const float* q;          // [rows][128] (rotation only)
   float* logits;           // decode only, optional
   const int32_t* seq_len;  // decode
+  uint4* qb;               // [tiles][kQB] QK B operands
   float* partials;         // [rows][n_chunks][kPS]
   int64_t capacity;
   int64_t logits_ld;
@@ -486,37 +490,43 @@ struct AttnArgs {
   int32_t prefill;         // 0 decode, 1 prefill
   int32_t seq;             // prefill sequence
   int32_t n_tok;           // prefill: tokens in chunk
-  int32_t chunk;           // tokens per split (multiple of 32 * kWaves)
+  int32_t chunk;           // tokens per split (multiple of 32)
   int32_t n_chunks;
   int32_t max_len;         // decode clamp
   float qscale;            // softmax scale * log2(e)
-  float cbv[4][16];        // centroids of rates 1..4 (binary16 values)
 };
 
-struct AttnWave {
-  uint32_t ktile[kBlk * 17];         // 32 key records at an odd pitch (kw + 1 words, kw <= 16)
-  float knt[kMaxGroups][kBlk];       // group norms, group-major
-  float vn[kBlk];
-};
+// tile -> (sequence, KV head, tile within the head)
+__device__ inline void tile_coords(const AttnArgs& a, int tile, int* seq, int* h, int* tr) {
+  if (a.prefill) {
+    *h = tile / a.tiles_per_kv;
+    *tr = tile - *h * a.tiles_per_kv;
+    *seq = a.seq;
+  } else {
+    *seq = tile / (a.n_kv * a.tiles_per_kv);
+    const int rem = tile - *seq * a.n_kv * a.tiles_per_kv;
+    *h = rem / a.tiles_per_kv;
+    *tr = rem - *h * a.tiles_per_kv;
+  }
+}
 
-struct AttnShared {
-  uint4 lut1[256];                   // 1-bit codes: byte -> 8 binary16 centroids
-  uint2 lut2[256];                   // 2-bit: byte -> 4
-  uint32_t lut3[64];                 // 3-bit: 6 bits -> 2
-  uint32_t lut4[256];                // 4-bit: byte -> 2
-  int32_t rate_nk[4], rate_grp[4], rate_bit[4], rate_kb[4];  // per rate 1..4: K-blocks, group,
-                                                             // record bit, first K-block
-  uint4 qb[kMaxKB][4][16];           // QK B operand per K-block and lane
-  int32_t row_id[8];
-  int32_t row_len[8];
-  float om[kWaves][8];
-  float ol[kWaves][8];
-  union alignas(16) {
-    float qrec[8][kD];               // prologue: query rows in record order
-    AttnWave w[kWaves][2];           // main loop: two block tiles per wave
-    float slot[kWaves][8][kD];       // epilogue: accumulator rows of each wave
-  } u;
-};
+// query row r (0..7) of a tile: its global row id (-1 if absent) and visible length
+__device__ inline int tile_row(const AttnArgs& a, int seq, int h, int tr, int r, int len_ld, int* len) {
+  const int f = tr * 8 + r;
+  int id = -1, L = 0;
+  if (a.prefill) {
+    if (f < a.n_tok * a.g) {
+      const int t = f / a.g;
+      id = t * a.n_q + h * a.g + (f - t * a.g);
+      L = (int)(a.pos0 + t + 1);
+    }
+  } else if (f < a.g) {
+    id = seq * a.n_q + h * a.g + f;
+    L = min(max(len_ld, 0), a.max_len);
+  }
+  *len = L;
+  return id;
+}
 
 __device__ inline uint32_t pack2h(float a, float b) {
   const _Float16 ha = (_Float16)a, hb = (_Float16)b;
@@ -564,25 +574,121 @@ union H8 {
   uint4 v;
 };
 
-// 8 codes of rate R (code k at bits [k R, (k + 1) R) of F) -> 8 binary16 centroids
-template <int R>
-__device__ inline half8 dequant8(const AttnShared& S, uint32_t F) {
-  H8 o;
-  if (R == 1) {
-    o.v = S.lut1[F & 0xFF];
-  } else if (R == 2) {
-    const uint2 x = S.lut2[F & 0xFF], y = S.lut2[(F >> 8) & 0xFF];
-    o.u[0] = x.x;
-    o.u[1] = x.y;
-    o.u[2] = y.x;
-    o.u[3] = y.y;
-  } else if (R == 3) {
+// ---------------------------------------------------------------- query rotation
+
+// One workgroup (4 waves) per row tile: the tile's query rows in record order, then
+// per group and 16-coordinate slice i0.. the fp32 MFMA 16x16x4 product
+// D[i][r] = sum_k Pi_g[i0 + i][k] qrec[r][pos_off + k] (the 4 k of lane (q, n) per MFMA
+// are k0 + 4q + s), written as the tile's B operand.
+constexpr int kQrotWaves = 4;
+__global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) {
+  __shared__ float qnat[8][kD];
+  __shared__ float qrec[8][kD];
+  __shared__ uint4 qb[kMaxKB][4][16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, n = lane & 15;
+  const int tile = blockIdx.x;
+  int seq, h, tr;
+  tile_coords(a, tile, &seq, &h, &tr);
+  const DevHead* __restrict__ hp = a.heads + h;
+  const int n_groups = hp->n_groups;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.u[j] = S.lut3[(F >> (6 * j)) & 63];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o.u[j] = S.lut4[(F >> (8 * j)) & 0xFF];
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + 256 * u, r = e >> 7, c = e & (kD - 1);
+    int L;
+    const int id = tile_row(a, seq, h, tr, r, 0, &L);
+    qnat[r][c] = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
   }
+  const int crd = tid < kD ? hp->coord[tid] : 0;
+  for (int e = tid; e < kQB; e += 256) (&qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  if (tid < kD) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) qrec[r][tid] = qnat[r][crd];
+  }
+  __syncthreads();
+  int t = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    const int d = hp->dim[g], po = hp->pos_off[g], kp0 = hp->kp_off[g];
+    const float* R = a.rot + hp->krot_off[g];
+    const float sc = a.qscale / sqrtf((float)d);
+    for (int i0 = 0; i0 < d; i0 += 16, ++t) {
+      if ((t & (kQrotWaves - 1)) != wave) continue;
+      const int i = i0 + n;
+      float2 pa[8][2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {  // all of the slice's rotation entries first
+        const int kk = 16 * u + 4 * q;  // d is even: a pair of columns is wholly in or out
+        pa[u][0] = (i < d && kk < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk) : make_float2(0.f, 0.f);
+        pa[u][1] = (i < d && kk + 2 < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk + 2)
+                                         : make_float2(0.f, 0.f);
+      }
+      floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (16 * u < d) {
+          const int kk = 16 * u + 4 * q;
+          float2 b0 = make_float2(0.f, 0.f), b1 = make_float2(0.f, 0.f);
+          if (n < 8 && kk < d) b0 = *reinterpret_cast<const float2*>(&qrec[n][po + kk]);
+          if (n < 8 && kk + 2 < d) b1 = *reinterpret_cast<const float2*>(&qrec[n][po + kk + 2]);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][0].x, b0.x, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][0].y, b0.y, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][1].x, b1.x, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][1].y, b1.y, acc[u & 1], 0, 0, 0);
+        }
+      }
+      // lane (q, n) holds D[4q + e][n]: coordinate i0 + 4q + e of row n
+      if (n < 8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = i0 + 4 * q + e;
+          if (ii < d) {
+            const float val = (acc[0][e] + acc[1][e]) * sc;
+            const _Float16 hi = (_Float16)val;
+            const _Float16 lo = (_Float16)(val - (float)hi);
+            const int kp = kp0 + ii;
+            reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][n])[kp & 7] = hi;
+            reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][15 - n])[kp & 7] = lo;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < kQB; e += 256) a.qb[(size_t)tile * kQB + e] = (&qb[0][0][0])[e];
+}
+
+// ---------------------------------------------------------------- partials
+
+struct AttnWave {
+  uint32_t ktile[kBlk * 17];         // 32 key records at an odd pitch (kw + 1 words, kw <= 16)
+  float knt[kMaxGroups][kBlk];       // group norms, group-major
+  float vn[kBlk];
+};
+
+struct AttnShared {
+  uint32_t lut[kPairTable + 4];      // decode table (DevCodebook::pair)
+  uint4 qb[kMaxKB][4][16];           // QK B operand per K-block and lane
+  int32_t row_id[8];
+  int32_t row_len[8];
+  float om[kWaves][8];
+  float ol[kWaves][8];
+  union alignas(16) {
+    AttnWave w[kWaves];              // main loop
+    float slot[kWaves][8][kD];       // epilogue: accumulator rows of each wave
+  } u;
+};
+
+// 8 codes of rate R (code k at bits [k R, (k + 1) R) of F) -> 8 binary16 centroids, two
+// codes per table read
+template <int R>
+__device__ inline half8 dequant8(const uint32_t* lut, uint32_t F) {
+  constexpr int base = ((1 << (2 * R)) - 4) / 3;
+  constexpr uint32_t m = (1u << (2 * R)) - 1;
+  H8 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o.u[j] = lut[base + ((F >> (2 * R * j)) & m)];
   return o.h;
 }
 
@@ -600,8 +706,8 @@ __device__ inline void qk_rate(const AttnShared& S, const uint32_t* r0, const ui
       const uint32_t f1 = __builtin_amdgcn_alignbit(r1[w + 1], r1[w], sb);
       H8 qv;
       qv.v = S.qb[kb0 + i][q][n];
-      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<R>(S, f0), qv.h, d0, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<R>(S, f1), qv.h, d1, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<R>(S.lut, f0), qv.h, d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<R>(S.lut, f1), qv.h, d1, 0, 0, 0);
     }
   }
 }
@@ -637,7 +743,8 @@ __device__ inline void load_block(BlockData<VB, KWL>& B, const uint32_t* kc, con
   const uint32_t* ks = kc + (size_t)t0 * kw;
 #pragma unroll
   for (int i = 0; i < KWL; ++i) {
-    if (2 * i + 1 < kw || (2 * i < kw && lane < 32)) B.kr[i] = ks[lane + 64 * i];
+    if (2 * i + 1 < kw) B.kr[i] = ks[lane + 64 * i];
+    else if (2 * i < kw && lane < 32) B.kr[i] = ks[lane + 64 * i];
   }
   B.kn = *reinterpret_cast<const float2*>(knp + (size_t)t0 * kNS + 2 * lane);
   B.vn = vnp[t0 + (lane & 31)];
@@ -656,113 +763,65 @@ __device__ inline void load_block(BlockData<VB, KWL>& B, const uint32_t* kc, con
   }
 }
 
-constexpr int kDepth = 4;  // blocks of a wave in flight
-
-// One step of a wave's online softmax over two 32-token blocks (the second may be
-// absent): stage both, QK, one max / rescale for both, PV.
+// One step of a wave's online softmax over one staged 32-token block.
 template <int VB, int KWL>
-__device__ inline void attn_blocks(const AttnShared& S, AttnWave (&W)[2], const BlockData<VB, KWL>& B0,
-                                   const BlockData<VB, KWL>& B1, bool has1, const AttnArgs& a, int t0a, int t0b,
-                                   int kw, int inv_kw, int lane, int q, int n, int my_row, int my_len,
-                                   const int (&r_nk)[4], const int (&r_grp)[4], const int (&r_bit)[4],
-                                   const int (&r_kb)[4], floatx4 (&oacc)[8], float& m_run, float& l_run) {
-  const int nb = has1 ? 2 : 1;
-  // ---- stage the blocks' key codes (pitch kw + 1), group norms and value norms
+__device__ inline void attn_block(const AttnShared& S, AttnWave& W, const BlockData<VB, KWL>& B, const AttnArgs& a,
+                                  int t0, int kw, int lane, int q, int n, int my_row, int my_len,
+                                  const int (&st)[KWL], const uint32_t* r0, const uint32_t* r1,
+                                  const int (&r_nk)[4], const int (&r_grp)[4], const int (&r_bit)[4],
+                                  const int (&r_kb)[4], floatx4 (&oacc)[8], float& m_run, float& l_run) {
+  // ---- stage the block's key codes (pitch kw + 1), group norms and value norms
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if (b < nb) {
-      const BlockData<VB, KWL>& B = b ? B1 : B0;
-#pragma unroll
-      for (int i = 0; i < KWL; ++i) {
-        const int lw = lane + 64 * i;
-        if (lw < kBlk * kw) W[b].ktile[lw + ((lw * inv_kw) >> 16)] = B.kr[i];  // + token index
-      }
-      W[b].knt[2 * (lane & 1)][lane >> 1] = B.kn.x;
-      W[b].knt[2 * (lane & 1) + 1][lane >> 1] = B.kn.y;
-      if (lane < 32) W[b].vn[lane] = B.vn;
-    }
+  for (int i = 0; i < KWL; ++i) {
+    if (2 * i + 1 < kw) W.ktile[st[i]] = B.kr[i];
+    else if (2 * i < kw && lane < 32) W.ktile[st[i]] = B.kr[i];
   }
+  W.knt[2 * (lane & 1)][lane >> 1] = B.kn.x;
+  W.knt[2 * (lane & 1) + 1][lane >> 1] = B.kn.y;
+  if (lane < 32) W.vn[lane] = B.vn;
   __builtin_amdgcn_wave_barrier();
-  const int tau0 = 8 * (n >> 2) + (n & 3);  // A-row n of the two 16-token halves
-  const int ro = tau0 * (kw + 1);
 
   // ---- QK per key group (one rate each), folded with the per-token group norm into
-  //      the logits of tokens 8q + j (j = 4 half + e) of each block
-  float lg[2][8];
+  //      the logits of tokens 8q + j (j = 4 half + e)
+  float lg[8];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lg[b][j] = 0.f;
+  for (int j = 0; j < 8; ++j) lg[j] = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     if (r_nk[r] > 0) {
-      floatx4 d[2][2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) d[b][0] = d[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int nk = r_nk[r];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < nk) {
-          const int R = r + 1;
-          const int bit = r_bit[r] + R * (32 * i + 8 * q);
-          const int w = bit >> 5, sb = bit & 31;
-          H8 qv;
-          qv.v = S.qb[r_kb[r] + i][q][n];
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            if (b < nb) {
-              const uint32_t* p0 = W[b].ktile + ro + w;
-              const uint32_t* p1 = p0 + 4 * (kw + 1);
-              const uint32_t f0 = __builtin_amdgcn_alignbit(p0[1], p0[0], sb);
-              const uint32_t f1 = __builtin_amdgcn_alignbit(p1[1], p1[0], sb);
-              half8 A0, A1;
-              if (r == 0) { A0 = dequant8<1>(S, f0); A1 = dequant8<1>(S, f1); }
-              if (r == 1) { A0 = dequant8<2>(S, f0); A1 = dequant8<2>(S, f1); }
-              if (r == 2) { A0 = dequant8<3>(S, f0); A1 = dequant8<3>(S, f1); }
-              if (r == 3) { A0 = dequant8<4>(S, f0); A1 = dequant8<4>(S, f1); }
-              d[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qv.h, d[b][0], 0, 0, 0);
-              d[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qv.h, d[b][1], 0, 0, 0);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        if (b < nb) {
-          const float4 na = *reinterpret_cast<const float4*>(&W[b].knt[r_grp[r]][8 * q]);
-          const float4 nbv = *reinterpret_cast<const float4*>(&W[b].knt[r_grp[r]][8 * q + 4]);
-          lg[b][0] = fmaf(na.x, d[b][0][0], lg[b][0]);
-          lg[b][1] = fmaf(na.y, d[b][0][1], lg[b][1]);
-          lg[b][2] = fmaf(na.z, d[b][0][2], lg[b][2]);
-          lg[b][3] = fmaf(na.w, d[b][0][3], lg[b][3]);
-          lg[b][4] = fmaf(nbv.x, d[b][1][0], lg[b][4]);
-          lg[b][5] = fmaf(nbv.y, d[b][1][1], lg[b][5]);
-          lg[b][6] = fmaf(nbv.z, d[b][1][2], lg[b][6]);
-          lg[b][7] = fmaf(nbv.w, d[b][1][3], lg[b][7]);
-        }
-      }
+      floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+      if (r == 0) qk_rate<1>(S, r0, r1, r_nk[r], r_bit[r], r_kb[r], q, n, d0, d1);
+      if (r == 1) qk_rate<2>(S, r0, r1, r_nk[r], r_bit[r], r_kb[r], q, n, d0, d1);
+      if (r == 2) qk_rate<3>(S, r0, r1, r_nk[r], r_bit[r], r_kb[r], q, n, d0, d1);
+      if (r == 3) qk_rate<4>(S, r0, r1, r_nk[r], r_bit[r], r_kb[r], q, n, d0, d1);
+      const float4 na = *reinterpret_cast<const float4*>(&W.knt[r_grp[r]][8 * q]);
+      const float4 nb = *reinterpret_cast<const float4*>(&W.knt[r_grp[r]][8 * q + 4]);
+      lg[0] = fmaf(na.x, d0[0], lg[0]);
+      lg[1] = fmaf(na.y, d0[1], lg[1]);
+      lg[2] = fmaf(na.z, d0[2], lg[2]);
+      lg[3] = fmaf(na.w, d0[3], lg[3]);
+      lg[4] = fmaf(nb.x, d1[0], lg[4]);
+      lg[5] = fmaf(nb.y, d1[1], lg[5]);
+      lg[6] = fmaf(nb.z, d1[2], lg[6]);
+      lg[7] = fmaf(nb.w, d1[3], lg[7]);
     }
   }
   float mblk = -INFINITY;
+  const bool full = t0 + kBlk <= my_len;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int t0 = b ? t0b : t0a;
-    const bool full = b < nb && t0 + kBlk <= my_len;
+  for (int j = 0; j < 8; ++j) {
+    float v = lg[j] + dpp_row_mirror(lg[j]);
+    if (!full && t0 + 8 * q + j >= my_len) v = -INFINITY;
+    lg[j] = v;
+    mblk = fmaxf(mblk, v);
+  }
+  if (a.logits && n < 8) {
+    const int id = S.row_id[my_row];
+    if (id >= 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v = lg[b][j] + dpp_row_mirror(lg[b][j]);
-      if (!full && (b >= nb || t0 + 8 * q + j >= my_len)) v = -INFINITY;
-      lg[b][j] = v;
-      mblk = fmaxf(mblk, v);
-    }
-    if (a.logits && n < 8 && b < nb) {
-      const int id = S.row_id[my_row];
-      if (id >= 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int pos = t0 + 8 * q + j;
-          if (pos < my_len) a.logits[(size_t)id * a.logits_ld + pos] = lg[b][j] * LN2_F;
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int pos = t0 + 8 * q + j;
+        if (pos < my_len) a.logits[(size_t)id * a.logits_ld + pos] = lg[j] * LN2_F;
       }
     }
   }
@@ -786,36 +845,30 @@ __device__ inline void attn_blocks(const AttnShared& S, AttnWave (&W)[2], const 
     m_run = m_new;
   }
   const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-  // ---- probabilities times value norms, split high/low by column; PV over the 8 value
-  //      tiles (coordinate 8n + t of the rotated basis)
+  // ---- probabilities times value norms, split high/low by column
+  const float4 vna = *reinterpret_cast<const float4*>(W.vn + 8 * q);
+  const float4 vnb = *reinterpret_cast<const float4*>(W.vn + 8 * q + 4);
+  const float vn[8] = {vna.x, vna.y, vna.z, vna.w, vnb.x, vnb.y, vnb.z, vnb.w};
+  H8 pa;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if (b < nb) {
-      const float4 vna = *reinterpret_cast<const float4*>(W[b].vn + 8 * q);
-      const float4 vnb = *reinterpret_cast<const float4*>(W[b].vn + 8 * q + 4);
-      const float vn[8] = {vna.x, vna.y, vna.z, vna.w, vnb.x, vnb.y, vnb.z, vnb.w};
-      H8 pa;
+  for (int jj = 0; jj < 4; ++jj) {
+    float x[2];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float x[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = 2 * jj + u;
-          // lg - m_use <= 0: the hardware 2^x (denormal results flush to 0) is exact enough
-          const float p = (lg[b][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[b][j] - m_use);
-          l_run += p;
-          const float pv = (p == 0.f) ? 0.f : p * vn[j];
-          const float hi = (float)(_Float16)pv;
-          x[u] = n < 8 ? hi : pv - hi;
-        }
-        pa.u[jj] = pack2h(x[0], x[1]);
-      }
-      const BlockData<VB, KWL>& B = b ? B1 : B0;
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S, vfield<VB>(B.vw, t)), oacc[t], 0, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * jj + u;
+      // lg - m_use <= 0: the hardware 2^x (denormal results flush to 0) is exact enough
+      const float p = (lg[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[j] - m_use);
+      l_run += p;
+      const float pv = (p == 0.f) ? 0.f : p * vn[j];
+      const float hi = (float)(_Float16)pv;
+      x[u] = n < 8 ? hi : pv - hi;
     }
+    pa.u[jj] = pack2h(x[0], x[1]);
   }
+  // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S.lut, vfield<VB>(B.vw, t)), oacc[t], 0, 0, 0);
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -829,19 +882,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
   const int q = lane >> 4, n = lane & 15;
   const int chunk_idx = blockIdx.x;
   const int tile = blockIdx.y;
-
-  // ---- tile -> (sequence, KV head, rows)
   int seq, h, tr;
-  if (a.prefill) {
-    h = tile / a.tiles_per_kv;
-    tr = tile - h * a.tiles_per_kv;
-    seq = a.seq;
-  } else {
-    seq = tile / (a.n_kv * a.tiles_per_kv);
-    const int rem = tile - seq * a.n_kv * a.tiles_per_kv;
-    h = rem / a.tiles_per_kv;
-    tr = rem - h * a.tiles_per_kv;
-  }
+  tile_coords(a, tile, &seq, &h, &tr);
   const DevHead* __restrict__ hp = a.heads + h;
   const size_t sh = (size_t)seq * a.n_kv + h;
   const int kw = a.k_words;
@@ -850,189 +892,48 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
   const uint32_t* vc = a.v_codes + sh * (a.capacity / GTQ_VBLOCK) * (32 * VB);
   const float* vnp = a.v_norms + sh * a.capacity;
   const int c0 = chunk_idx * a.chunk;
-  const int cap_last = (int)(a.capacity - kBlk);
-  // ---- first: the loads of this wave's first kDepth blocks (clamped inside the cache;
-  //      unused when outside the tile's tokens), then everything else of the prologue
-  const int n_groups = hp->n_groups;
+  // ---- one round of independent loads: B operand, decode table, rows, first block
+  const uint4 qbv = a.qb[(size_t)tile * kQB + tid];  // kQB == kThreads
+  const uint32_t lutv = tid < kPairTable ? a.cb->pair[tid] : 0u;
   const int len_ld = a.prefill ? 0 : a.seq_len[seq];
-  // this wave's slices of the query rotation (group, first coordinate): slices are
-  // numbered over the groups in order, 16 coordinates each; wave w takes w and w + 8
-  int rg[2] = {-1, -1}, ri0[2] = {0, 0};
+  BlockData<VB, KWL> blk[kDepth];
+  load_block<VB, KWL>(blk[0], kc, knp, vc, vnp, (int)min<int64_t>(c0 + kBlk * wave, a.capacity - kBlk), kw, lane,
+                      q, n);
+  // per rate 1..4 (uniform, from the head table): K-blocks, group, record bit, first K-block
+  int r_nk[4] = {0, 0, 0, 0}, r_grp[4] = {0, 0, 0, 0}, r_bit[4] = {0, 0, 0, 0}, r_kb[4] = {0, 0, 0, 0};
   {
-    int t = 0;
+    const int n_groups = hp->n_groups;
+    int kbs = 0;
 #pragma unroll
     for (int g = 0; g < kMaxGroups; ++g) {
       if (g < n_groups) {
-        const int ns = (hp->dim[g] + 15) >> 4;
+        const int r = hp->rate[g] - 1, nk = hp->nkb_g[g];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int idx = wave + kWaves * j;
-          if (idx >= t && idx < t + ns) {
-            rg[j] = g;
-            ri0[j] = 16 * (idx - t);
+        for (int rr = 0; rr < 4; ++rr) {
+          if (rr == r) {
+            r_nk[rr] = nk;
+            r_grp[rr] = g;
+            r_bit[rr] = hp->bit_off[g];
+            r_kb[rr] = kbs;
           }
         }
-        t += ns;
+        kbs += nk;
       }
     }
   }
-  // Pi_g rows of the slices: lane (q, n) holds row i0 + n, columns k0 + 4q + 0..3 for
-  // k0 = 0, 16, ... (d is even: a pair of columns is wholly inside or outside)
-  float2 pa_[2][8][2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int g = rg[j] < 0 ? 0 : rg[j];
-    const int d = rg[j] < 0 ? 0 : hp->dim[g];
-    const float* R = a.rot + hp->krot_off[g];
-    const int i = ri0[j] + n;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int kk = 16 * u + 4 * q;
-      pa_[j][u][0] = (i < d && kk < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk) : make_float2(0.f, 0.f);
-      pa_[j][u][1] = (i < d && kk + 2 < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk + 2) : make_float2(0.f, 0.f);
-    }
-  }
-
-  // ---- row ids and lengths; query rows in natural order, and the head's record order
-  auto row_of = [&](int r, int* len) {
-    const int f = tr * 8 + r;
-    int id = -1, L = 0;
-    if (a.prefill) {
-      if (f < a.n_tok * a.g) {
-        const int t = f / a.g;
-        id = t * a.n_q + h * a.g + (f - t * a.g);
-        L = (int)(a.pos0 + t + 1);
-      }
-    } else if (f < a.g) {
-      id = seq * a.n_q + h * a.g + f;
-      L = min(max(len_ld, 0), a.max_len);
-    }
-    *len = L;
-    return id;
-  };
-  float qn[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + kThreads * u, r = e >> 7, c = e & (kD - 1);
-    int L;
-    const int id = row_of(r, &L);
-    qn[u] = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
-  }
-  const int crd = tid < kD ? hp->coord[tid] : 0;
-  // this wave's first block (clamped inside the cache; unused when outside the tile's
-  // tokens); the others follow once the prologue's own loads are out
-  BlockData<VB, KWL> blk[kDepth];
-  load_block<VB, KWL>(blk[0], kc, knp, vc, vnp, min(c0 + kBlk * wave, cap_last), kw, lane, q, n);
+  (&S.qb[0][0][0])[tid] = qbv;
+  if (tid < kPairTable) S.lut[tid] = lutv;
   if (tid < 8) {
     int L;
-    const int id = row_of(tid, &L);
-    S.row_id[tid] = id;
+    S.row_id[tid] = tile_row(a, seq, h, tr, tid, len_ld, &L);
     S.row_len[tid] = L;
   }
-  (&S.qb[0][0][0])[tid] = make_uint4(0, 0, 0, 0);  // kMaxKB * 64 == kThreads entries
-  {
-    // decode tables: byte (or 6 bits) -> binary16 centroids
-    const float* c1 = a.cbv[0];
-    const float* c2 = a.cbv[1];
-    const float* c3 = a.cbv[2];
-    const float* c4 = a.cbv[3];
-    for (int e = tid; e < 1024; e += kThreads) {
-      const int b = e >> 2, k = e & 3;
-      reinterpret_cast<uint32_t*>(S.lut1)[e] = pack2h(c1[(b >> (2 * k)) & 1], c1[(b >> (2 * k + 1)) & 1]);
-    }
-    {
-      const int b = tid >> 1, k = tid & 1;
-      reinterpret_cast<uint32_t*>(S.lut2)[tid] = pack2h(c2[(b >> (4 * k)) & 3], c2[(b >> (4 * k + 2)) & 3]);
-    }
-    if (tid < 64) S.lut3[tid] = pack2h(c3[tid & 7], c3[(tid >> 3) & 7]);
-    if (tid < 256) S.lut4[tid] = pack2h(c4[tid & 15], c4[(tid >> 4) & 15]);
-    if (tid < 4) {  // per rate: its group (at most one), K-blocks, record bit, first K-block
-      int nk = 0, grp = 0, bit = 0, kb = 0, kbs = 0;
-      for (int g = 0; g < n_groups; ++g) {
-        if (hp->rate[g] == tid + 1) {
-          nk = hp->nkb_g[g];
-          grp = g;
-          bit = hp->bit_off[g];
-          kb = kbs;
-        }
-        kbs += hp->nkb_g[g];
-      }
-      S.rate_nk[tid] = nk;
-      S.rate_grp[tid] = grp;
-      S.rate_bit[tid] = bit;
-      S.rate_kb[tid] = kb;
-    }
-  }
-  float* qnat = &S.u.slot[1][0][0];  // query rows in natural order [8][128]; clear of qrec
-  qnat[tid] = qn[0];
-  qnat[tid + kThreads] = qn[1];
   __syncthreads();
   int tile_len = 0;
 #pragma unroll
   for (int r = 0; r < 8; ++r) tile_len = max(tile_len, S.row_len[r]);
   if (c0 >= tile_len) return;  // no cached token of this tile in this split
   const int c1 = min(c0 + a.chunk, tile_len);
-  if (tid < kD) {  // record order: qrec[r][pos] = q[r][coord[pos]]
-#pragma unroll
-    for (int r = 0; r < 8; ++r) S.u.qrec[r][tid] = qnat[r * kD + crd];
-  }
-  __syncthreads();
-
-  // ---- query rotation on the matrix cores (fp32 MFMA 16x16x4): D[i][r] =
-  //      sum_k Pi_g[i0 + i][k] qrec[r][pos_off + k]; the 4 k of lane (q, n) per MFMA
-  //      are k0 + 4q + s
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (rg[j] >= 0) {
-      const int g = rg[j], i0 = ri0[j];
-      const int d = hp->dim[g], po = hp->pos_off[g], kp0 = hp->kp_off[g];
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (16 * u < d) {
-          const int kk = 16 * u + 4 * q;
-          float2 b0 = make_float2(0.f, 0.f), b1 = make_float2(0.f, 0.f);
-          if (n < 8 && kk < d) b0 = *reinterpret_cast<const float2*>(&S.u.qrec[n][po + kk]);
-          if (n < 8 && kk + 2 < d) b1 = *reinterpret_cast<const float2*>(&S.u.qrec[n][po + kk + 2]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa_[j][u][0].x, b0.x, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa_[j][u][0].y, b0.y, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa_[j][u][1].x, b1.x, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa_[j][u][1].y, b1.y, acc, 0, 0, 0);
-        }
-      }
-      // lane (q, n) holds D[4q + e][n]: coordinate i0 + 4q + e of row n
-      if (n < 8) {
-        const float sc = a.qscale / sqrtf((float)d);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ii = i0 + 4 * q + e;
-          if (ii < d) {
-            const float val = acc[e] * sc;
-            const _Float16 hi = (_Float16)val;
-            const _Float16 lo = (_Float16)(val - (float)hi);
-            const int kp = kp0 + ii;
-            reinterpret_cast<_Float16*>(&S.qb[kp >> 5][(kp >> 3) & 3][n])[kp & 7] = hi;
-            reinterpret_cast<_Float16*>(&S.qb[kp >> 5][(kp >> 3) & 3][15 - n])[kp & 7] = lo;
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();  // B operand ready; the query rows' space becomes the wave tiles
-
-  // ---- per rate 1..4 (uniform): K-blocks, group, record bit, first K-block
-  int r_nk[4], r_grp[4], r_bit[4], r_kb[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    r_nk[r] = __builtin_amdgcn_readfirstlane(S.rate_nk[r]);
-    r_grp[r] = __builtin_amdgcn_readfirstlane(S.rate_grp[r]);
-    r_bit[r] = __builtin_amdgcn_readfirstlane(S.rate_bit[r]);
-    r_kb[r] = __builtin_amdgcn_readfirstlane(S.rate_kb[r]);
-  }
-  const int my_row = n < 8 ? n : 15 - n;
-  const int my_len = S.row_len[my_row];
-  const int inv_kw = (65536 + kw - 1) / kw;  // floor(lw * inv_kw / 2^16) == lw / kw for lw < 512
-  AttnWave(&W)[2] = S.u.w[wave];
   constexpr int kStep = kBlk * kWaves;
 #pragma unroll
   for (int j = 1; j < kDepth; ++j) {
@@ -1040,25 +941,34 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
     if (t < c1) load_block<VB, KWL>(blk[j], kc, knp, vc, vnp, t, kw, lane, q, n);
   }
 
+  const int my_row = n < 8 ? n : 15 - n;
+  const int my_len = S.row_len[my_row];
+  AttnWave& W = S.u.w[wave];
+  int st[KWL];  // staging slot of word lane + 64 i: one pad word per token
+#pragma unroll
+  for (int i = 0; i < KWL; ++i) {
+    const int lw = lane + 64 * i;
+    st[i] = lw + lw / kw;
+  }
+  const int tau0 = 8 * (n >> 2) + (n & 3);  // A-row n of the two 16-token halves
+  const uint32_t* r0 = W.ktile + tau0 * (kw + 1);
+  const uint32_t* r1 = r0 + 4 * (kw + 1);
+
   floatx4 oacc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) oacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- main loop: kDepth blocks per round, two per step; each register set is
-  //      refilled kDepth blocks ahead
+  // ---- main loop: kDepth blocks per round, each register set refilled kDepth ahead
   for (int tb = c0 + kBlk * wave; tb < c1; tb += kStep * kDepth) {
 #pragma unroll
-    for (int j = 0; j < kDepth; j += 2) {
-      const int ta = tb + kStep * j, tb2 = ta + kStep;
-      if (ta < c1) {
-        attn_blocks<VB, KWL>(S, W, blk[j], blk[j + 1], tb2 < c1, a, ta, tb2, kw, inv_kw, lane, q, n, my_row,
-                             my_len, r_nk, r_grp, r_bit, r_kb, oacc, m_run, l_run);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int tn = ta + kStep * (u + kDepth);
-          if (tn < c1) load_block<VB, KWL>(blk[j + u], kc, knp, vc, vnp, tn, kw, lane, q, n);
-        }
+    for (int j = 0; j < kDepth; ++j) {
+      const int t0 = tb + kStep * j;
+      if (t0 < c1) {
+        attn_block<VB, KWL>(S, W, blk[j], a, t0, kw, lane, q, n, my_row, my_len, st, r0, r1, r_nk, r_grp, r_bit,
+                            r_kb, oacc, m_run, l_run);
+        const int tn = t0 + kStep * kDepth;
+        if (tn < c1) load_block<VB, KWL>(blk[j], kc, knp, vc, vnp, tn, kw, lane, q, n);
       }
     }
   }
@@ -1317,7 +1227,11 @@ int auto_chunk(int64_t max_len, int64_t tiles) {
   return (int)std::max<int64_t>(kRound, ch);
 }
 
-size_t attn_ws_bytes(int64_t rows, int64_t n_chunks) { return (size_t)rows * n_chunks * kPS * 4; }
+// workspace: the tiles' QK B operands, then the partials
+size_t attn_qb_bytes(int64_t n_tiles) { return (size_t)n_tiles * kQB * sizeof(uint4); }
+size_t attn_ws_bytes(int64_t rows, int64_t n_chunks, int64_t n_tiles) {
+  return attn_qb_bytes(n_tiles) + (size_t)rows * n_chunks * kPS * 4;
+}
 
 struct AttnLaunch {
   int64_t rows;
@@ -1327,16 +1241,17 @@ struct AttnLaunch {
   int n_chunks;
 };
 
-gtq_status launch_partials(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* q,
-                           AttnArgs& aa, const AttnLaunch& L, float scale, void* ws, hipStream_t stream) {
+void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnArgs& aa, const AttnLaunch& L,
+                    void* ws) {
   aa.heads = p->d_heads + (size_t)layer * p->n_kv;
   aa.rot = p->d_rot;
+  aa.cb = p->d_cb;
   aa.k_codes = c->k_codes;
   aa.k_norms = c->k_norms;
   aa.v_codes = c->v_codes;
   aa.v_norms = c->v_norms;
-  aa.q = q;
-  aa.partials = reinterpret_cast<float*>(ws);
+  aa.qb = reinterpret_cast<uint4*>(ws);
+  aa.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + attn_qb_bytes(L.n_tiles));
   aa.capacity = c->capacity;
   aa.n_kv = p->n_kv;
   aa.n_q = p->n_q;
@@ -1345,10 +1260,19 @@ gtq_status launch_partials(const gtq_plan* p, int layer, const gtq_cache_view* c
   aa.tiles_per_kv = L.tiles_per_kv;
   aa.chunk = L.chunk;
   aa.n_chunks = L.n_chunks;
+}
+
+gtq_status launch_qrot(AttnArgs& aa, const AttnLaunch& L, const float* q, float scale, hipStream_t stream) {
+  aa.q = q;
   aa.qscale = scale * LOG2E_F;
+  hipLaunchKernelGGL(attn_qrot_kernel, dim3(L.n_tiles), dim3(64 * kQrotWaves), 0, stream, aa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gtq attention query rotation: launch");
+  return ok();
+}
+
+gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L, hipStream_t stream) {
   if (p->k_words > 16) return fail(GTQ_EUNSUPPORTED, "gtq attention: more than 16 key code words per token");
-  for (int b = 1; b <= 4; ++b)
-    for (int k = 0; k < 16; ++k) aa.cbv[b - 1][k] = p->cb.c[b][k];
   dim3 grid(L.n_chunks, L.n_tiles);
   const bool wide = p->k_words > 8;  // key words per lane: 4 (k_words <= 8) or 8
 #define GTQ_LAUNCH(VB)                                                                          \
@@ -1369,7 +1293,8 @@ gtq_status launch_partials(const gtq_plan* p, int layer, const gtq_cache_view* c
 gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const int32_t* seq_len,
                         int64_t pos0, int prefill, int max_len, float* out, const void* ws,
                         hipStream_t stream) {
-  MergeArgs ma{p->d_heads + (size_t)layer * p->n_kv, p->d_rot, reinterpret_cast<const float*>(ws), seq_len,
+  MergeArgs ma{p->d_heads + (size_t)layer * p->n_kv, p->d_rot,
+               reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + attn_qb_bytes(L.n_tiles)), seq_len,
                out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill, max_len};
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows), dim3(256), 0, stream, ma);
   hipError_t e = hipGetLastError();
@@ -1509,7 +1434,7 @@ gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64
   AttnLaunch L;
   gtq_status st;
   if (!decode_shape(plan, batch, max_len, chunk, &L, &st, "gtq_decode_workspace_bytes")) return st;
-  *out = attn_ws_bytes(L.rows, L.n_chunks);
+  *out = attn_ws_bytes(L.rows, L.n_chunks, L.n_tiles);
   return ok();
 }
 
@@ -1523,28 +1448,43 @@ static gtq_status decode_check(const gtq_plan* plan, int32_t layer, const gtq_ca
   if (!ws) return fail(GTQ_EINVAL, std::string(fn) + ": workspace is NULL");
   if (max_len > cache->capacity) return fail(GTQ_ECAPACITY, std::string(fn) + ": max_len > capacity");
   if (!decode_shape(plan, cache->batch, max_len, chunk, L, &st, fn)) return st;
-  if (ws_bytes < attn_ws_bytes(L->rows, L->n_chunks))
+  if (ws_bytes < attn_ws_bytes(L->rows, L->n_chunks, L->n_tiles))
     return fail(GTQ_ECAPACITY, std::string(fn) + ": workspace too small");
   return GTQ_OK;
 }
 
+gtq_status gtq_decode_rotate_queries(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                     const float* q, int64_t max_len, float softmax_scale, int32_t chunk,
+                                     void* workspace, size_t ws_bytes, void* hip_stream) {
+  AttnLaunch L;
+  gtq_status st = decode_check(plan, layer, cache, max_len, chunk, ws_bytes, workspace, &L,
+                               "gtq_decode_rotate_queries");
+  if (st != GTQ_OK) return st;
+  if (!q) return fail(GTQ_EINVAL, "gtq_decode_rotate_queries: q is NULL");
+  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_decode_rotate_queries: softmax_scale not finite");
+  AttnArgs aa{};
+  fill_attn_args(plan, layer, cache, aa, L, workspace);
+  aa.prefill = 0;
+  aa.max_len = (int32_t)max_len;
+  return launch_qrot(aa, L, q, softmax_scale, (hipStream_t)hip_stream);
+}
+
 gtq_status gtq_decode_attn_partials(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
-                                    const float* q, const int32_t* seq_len, int64_t max_len,
-                                    float softmax_scale, int32_t chunk, float* logits, void* workspace,
-                                    size_t ws_bytes, void* hip_stream) {
+                                    const int32_t* seq_len, int64_t max_len, int32_t chunk, float* logits,
+                                    void* workspace, size_t ws_bytes, void* hip_stream) {
   AttnLaunch L;
   gtq_status st = decode_check(plan, layer, cache, max_len, chunk, ws_bytes, workspace, &L,
                                "gtq_decode_attn_partials");
   if (st != GTQ_OK) return st;
-  if (!q || !seq_len) return fail(GTQ_EINVAL, "gtq_decode_attn_partials: NULL pointer");
-  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_decode_attn_partials: softmax_scale not finite");
+  if (!seq_len) return fail(GTQ_EINVAL, "gtq_decode_attn_partials: seq_len is NULL");
   AttnArgs aa{};
+  fill_attn_args(plan, layer, cache, aa, L, workspace);
   aa.logits = logits;
   aa.logits_ld = max_len;
   aa.seq_len = seq_len;
   aa.prefill = 0;
   aa.max_len = (int32_t)max_len;
-  return launch_partials(plan, layer, cache, q, aa, L, softmax_scale, workspace, (hipStream_t)hip_stream);
+  return launch_partials(plan, aa, L, (hipStream_t)hip_stream);
 }
 
 gtq_status gtq_decode_attn_merge(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
@@ -1563,8 +1503,11 @@ gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_
                            float softmax_scale, int32_t chunk, float* out, float* logits,
                            void* workspace, size_t ws_bytes, void* hip_stream) {
   if (!out) return fail(GTQ_EINVAL, "gtq_decode_attn: out is NULL");
-  gtq_status st = gtq_decode_attn_partials(plan, layer, cache, q, seq_len, max_len, softmax_scale, chunk,
-                                           logits, workspace, ws_bytes, hip_stream);
+  gtq_status st = gtq_decode_rotate_queries(plan, layer, cache, q, max_len, softmax_scale, chunk, workspace,
+                                            ws_bytes, hip_stream);
+  if (st != GTQ_OK) return st;
+  st = gtq_decode_attn_partials(plan, layer, cache, seq_len, max_len, chunk, logits, workspace, ws_bytes,
+                                hip_stream);
   if (st != GTQ_OK) return st;
   return gtq_decode_attn_merge(plan, layer, cache, seq_len, max_len, chunk, out, workspace, ws_bytes,
                                hip_stream);
@@ -1604,7 +1547,7 @@ gtq_status gtq_prefill_workspace_bytes(const gtq_plan* plan, int64_t pos0, int64
   AttnLaunch L;
   gtq_status st;
   if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_workspace_bytes")) return st;
-  *out = attn_ws_bytes(L.rows, L.n_chunks);
+  *out = attn_ws_bytes(L.rows, L.n_chunks, L.n_tiles);
   return ok();
 }
 
@@ -1622,9 +1565,10 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
   AttnLaunch L;
   if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_attn")) return st;
   if (pos0 + n_tok > cache->capacity) return fail(GTQ_ECAPACITY, "gtq_prefill_attn: pos0 + n_tok > capacity");
-  if (ws_bytes < attn_ws_bytes(L.rows, L.n_chunks))
+  if (ws_bytes < attn_ws_bytes(L.rows, L.n_chunks, L.n_tiles))
     return fail(GTQ_ECAPACITY, "gtq_prefill_attn: workspace too small");
   AttnArgs aa{};
+  fill_attn_args(plan, layer, cache, aa, L, workspace);
   aa.logits = nullptr;
   aa.prefill = 1;
   aa.seq = seq;
@@ -1632,7 +1576,9 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
   aa.n_tok = (int32_t)n_tok;
   aa.max_len = (int32_t)(pos0 + n_tok);
   hipStream_t s = (hipStream_t)hip_stream;
-  st = launch_partials(plan, layer, cache, q, aa, L, softmax_scale, workspace, s);
+  st = launch_qrot(aa, L, q, softmax_scale, s);
+  if (st != GTQ_OK) return st;
+  st = launch_partials(plan, aa, L, s);
   if (st != GTQ_OK) return st;
   return launch_merge(plan, layer, L, nullptr, pos0, 1, (int)(pos0 + n_tok), out, workspace, s);
 }

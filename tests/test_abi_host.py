@@ -27,7 +27,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "gtq.h")).read()
     declared = set(re.findall(r"^\s*(?:gtq_status|const char\*)\s+(gtq_\w+)\s*\(", hdr, re.M))
-    assert len(declared) == len(G.EXPORTS) == 18
+    assert len(declared) == len(G.EXPORTS) == 19
     raw = C.CDLL(G.LIB_PATH)
     for name in sorted(declared):
         assert hasattr(raw, name), name
@@ -180,9 +180,10 @@ def test_error_paths(lib):
     assert lib.gtq_decode_workspace_bytes(p.handle, 2, 1000, 33, C.byref(ws)) == 1
     assert b"multiple of 32" in lib.gtq_last_error()
     assert lib.gtq_decode_workspace_bytes(p.handle, 2, 1000, 64, C.byref(ws)) == 0
-    # rows * chunks partial records of 132 floats (m, l, 2 pad, acc[128])
-    rows, chunks = 2 * 4, (1000 + 63) // 64
-    exp = rows * chunks * 132 * 4
+    # the rotated-query operand of each tile (batch x KV heads x ceil(g / 8) tiles of
+    # 8 KB), then rows * chunks partial records of 132 floats (m, l, 2 pad, acc[128])
+    rows, chunks, tiles = 2 * 4, (1000 + 63) // 64, 2 * 2
+    exp = tiles * 8192 + rows * chunks * 132 * 4
     assert ws.value == exp
     assert lib.gtq_decode_workspace_bytes(p.handle, 1, 100000, 32, C.byref(ws)) == 1
     assert b"256 splits" in lib.gtq_last_error()
