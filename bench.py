@@ -3,8 +3,9 @@
 One step = one decode step of one Llama-3.1-8B-shaped attention layer at batch 1:
 quantize-append the step's new key/value token (8 KV heads) into the packed cache,
 then split-K packed decode attention of the 32 query heads over the 32768 cached
-tokens (the query rotation, the per-split online-softmax partials, and the
-log-sum-exp merge with the inverse value rotation: three kernels). Inputs are seeded synthetic tensors with the pages' distributions,
+tokens: one launch appends the token and rotates the queries, one computes the
+per-split online-softmax partials, one does the log-sum-exp merge with the inverse
+value rotation. Inputs are seeded synthetic tensors with the pages' distributions,
 resident in HBM before timing. The cache is replicated into --copies layer caches
 that the steps cycle through (as a 32-layer stack would), so that each step reads
 its cache from HBM rather than from the 256 MB last-level cache.
@@ -164,8 +165,6 @@ def main():
     caches = [base] + [base.clone() for _ in range(args.copies - 1)]
     k_new = k_all[n - 1: n].contiguous()
     v_new = v_all[n - 1: n].contiguous()
-    seq_idx = torch.zeros(1, dtype=torch.int32, device=dev)
-    slot = torch.full((1,), n - 1, dtype=torch.int64, device=dev)
     q = torch.from_numpy(w["q"]).to(dev)
     seq_len = torch.full((1,), n, dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
@@ -175,8 +174,8 @@ def main():
 
     def step(i, ev=None):
         c = caches[i % len(caches)]
-        G.gtq_quantize_append(plan, 0, c, k_new, v_new, seq_idx, slot, stream=stream)
-        G.gtq_decode_rotate_queries(plan, 0, c, q, n, scale, ws, chunk=args.chunk, stream=stream)
+        # append the step's token at slot n - 1 and rotate the queries (one launch)
+        G.gtq_decode_prepare(plan, 0, c, k_new, v_new, q, seq_len, n, scale, ws, chunk=args.chunk, stream=stream)
         if ev is not None:
             ev[0].record(stream)
         G.gtq_decode_attn_partials(plan, 0, c, seq_len, n, ws, chunk=args.chunk, stream=stream)

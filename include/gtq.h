@@ -271,6 +271,23 @@ gtq_status gtq_decode_attn_merge(const gtq_plan* plan, int32_t layer, const gtq_
                                  const int32_t* seq_len, int64_t max_len, int32_t chunk, float* out,
                                  const void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* One decode step of a layer in three launches (the serving hot path): each sequence b
+ * appends its new token (k_new, v_new: device [batch][n_kv_heads][128] fp32, post-RoPE)
+ * at slot seq_len[b] - 1, then attends with its query to all seq_len[b] cached tokens.
+ * gtq_decode_prepare runs the append and the query rotation in one launch (they
+ * share no data); gtq_decode_step is prepare + partials + merge. seq_len counts the new
+ * token; a sequence with seq_len[b] < 1 or > capacity appends nothing (counted by
+ * gtq_plan_overflow_count) and, with seq_len 0, gets a zero output. Arguments and errors
+ * otherwise as for gtq_quantize_append and gtq_decode_attn. */
+gtq_status gtq_decode_prepare(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                              const float* k_new, const float* v_new, const float* q, const int32_t* seq_len,
+                              int64_t max_len, float softmax_scale, int32_t chunk, void* workspace,
+                              size_t ws_bytes, void* hip_stream);
+gtq_status gtq_decode_step(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                           const float* k_new, const float* v_new, const float* q, const int32_t* seq_len,
+                           int64_t max_len, float softmax_scale, int32_t chunk, float* out, void* workspace,
+                           size_t ws_bytes, void* hip_stream);
+
 /* Workspace bytes for gtq_prefill_attn on a chunk of n_tok queries whose last
  * position is pos0 + n_tok - 1 (no initialisation needed). */
 gtq_status gtq_prefill_workspace_bytes(const gtq_plan* plan, int64_t pos0, int64_t n_tok,

@@ -84,6 +84,12 @@ _SIGS = [
     ("gtq_decode_attn", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_void_p,
                                     C.c_int64, C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("gtq_decode_prepare", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_void_p,
+                                       C.c_void_p, C.c_void_p, C.c_int64, C.c_float, C.c_int32, C.c_void_p,
+                                       C.c_size_t, C.c_void_p]),
+    ("gtq_decode_step", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_void_p,
+                                    C.c_void_p, C.c_void_p, C.c_int64, C.c_float, C.c_int32, C.c_void_p,
+                                    C.c_void_p, C.c_size_t, C.c_void_p]),
     ("gtq_decode_rotate_queries", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p,
                                               C.c_int64, C.c_float, C.c_int32, C.c_void_p, C.c_size_t,
                                               C.c_void_p]),
@@ -307,6 +313,34 @@ def gtq_decode_attn(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_
                                _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
                                _stream(stream))
     _check(st, "gtq_decode_attn")
+    return out
+
+
+def gtq_decode_prepare(plan: Plan, layer: int, cache: PackedCache, k_new, v_new, q, seq_len, max_len: int,
+                       scale: float, workspace, chunk: int = 0, stream=None):
+    cv = cache.view()
+    st = lib().gtq_decode_prepare(plan.handle, layer, C.byref(cv), _dev(k_new, torch.float32, "k_new"),
+                                  _dev(v_new, torch.float32, "v_new"), _dev(q, torch.float32, "q"),
+                                  _dev(seq_len, torch.int32, "seq_len"), max_len, float(scale), chunk,
+                                  _dev(workspace, None, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gtq_decode_prepare")
+
+
+def gtq_decode_step(plan: Plan, layer: int, cache: PackedCache, k_new, v_new, q, seq_len, max_len: int,
+                    scale: float, chunk: int = 0, out=None, workspace=None, stream=None):
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(gtq_decode_workspace_bytes(plan, cache.batch, max_len, chunk), dtype=torch.uint8,
+                                device=q.device)
+    cv = cache.view()
+    st = lib().gtq_decode_step(plan.handle, layer, C.byref(cv), _dev(k_new, torch.float32, "k_new"),
+                               _dev(v_new, torch.float32, "v_new"), _dev(q, torch.float32, "q"),
+                               _dev(seq_len, torch.int32, "seq_len"), max_len, float(scale), chunk,
+                               _dev(out, torch.float32, "out"), _dev(workspace, None, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gtq_decode_step")
     return out
 
 

@@ -51,6 +51,7 @@ struct AppendArgs {
   const float* v;
   const int32_t* seq_idx;
   const int64_t* slot;
+  const int32_t* step_len;  // if set: token b goes to sequence b, slot step_len[b] - 1
   unsigned long long* overflow;
   int64_t capacity;
   int64_t n_tok;
@@ -310,45 +311,86 @@ __device__ inline double wave_sum_f64(double v) {
   return v;
 }
 
-__global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
-  __shared__ float xs[2 * kD];          // key (record order) then value coordinates
+// One workgroup (1024 threads) per (token, KV head). All global loads go out in one
+// round (the vectors in natural order, the rotation rows each thread needs, the
+// token's sequence and slot); the key is put in record order in LDS; the group norms
+// are fp64 wave reductions; thread (output o, quarter qq) forms a quarter of one
+// rotated coordinate.
+__device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h) {
+  __shared__ float xnat[2 * kD];        // key then value, natural order
+  __shared__ __align__(16) float xs[2 * kD];  // key (record order) then value coordinates
   __shared__ float red[4][2 * kD];
   __shared__ float nu_s[5], sc_s[5];
   __shared__ uint32_t krec[16];
   __shared__ uint32_t vblk[128], vmask[128];
   const int tid = threadIdx.x;
-  const int h = blockIdx.y;
-  const int64_t tok = blockIdx.x;
-  const DevHead& hd = a.heads[h];
-  const int seq = a.seq_idx[tok];
-  const int64_t slot = a.slot[tok];
+  const DevHead* __restrict__ hd = a.heads + h;
+  const int n_groups = hd->n_groups;
+  const size_t row = ((size_t)tok * a.n_kv + h) * kD;
+  float xv = 0.f;
+  if (tid < kD) xv = a.k[row + tid];
+  else if (tid < 2 * kD) xv = a.v[row + tid - kD];
+  const int crd = tid < kD ? hd->coord[tid] : 0;
+  // this thread's rotation entries: key output o < 128 (row i of its group, pair range
+  // of quarter qq) or value output o - 128 (32 columns of quarter qq)
+  const int o = tid & 255, qq = tid >> 8;
+  float2 pk[16];
+  float4 pv[8];
+  int kg = 0, klo = 0, khi = 0;
+  if (o < kD) {
+#pragma unroll
+    for (int gg = 1; gg < kMaxGroups; ++gg)
+      if (gg < n_groups && o >= hd->pos_off[gg]) kg = gg;
+    const int d = hd->dim[kg], i = o - hd->pos_off[kg], dp = d >> 1;
+    klo = (dp * qq) >> 2;
+    khi = (dp * (qq + 1)) >> 2;
+    const float2* pr = reinterpret_cast<const float2*>(a.rot + hd->krot_off[kg] + (size_t)i * d);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) pk[u] = (klo + u < khi) ? pr[klo + u] : make_float2(0.f, 0.f);
+  } else {
+    const float4* pr = reinterpret_cast<const float4*>(a.rot + hd->vrot_off + (size_t)(o - kD) * kD + 32 * qq);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pv[u] = pr[u];
+  }
+  const int seq = a.step_len ? (int)tok : a.seq_idx[tok];
+  const int64_t slot = a.step_len ? (int64_t)a.step_len[tok] - 1 : a.slot[tok];
   if (seq < 0 || seq >= a.batch || slot < 0 || slot >= a.capacity) {
     if (tid == 0 && h == 0) atomicAdd(a.overflow, 1ull);  // once per token
     return;
   }
-  const size_t row = ((size_t)tok * a.n_kv + h) * kD;
-  if (tid < kD) xs[tid] = a.k[row + hd.coord[tid]];
-  else if (tid < 2 * kD) xs[tid] = a.v[row + tid - kD];
+  if (tid < 2 * kD) xnat[tid] = xv;
   if (tid < 16) krec[tid] = 0u;
   if (tid < 128) {
     vblk[tid] = 0u;
     vmask[tid] = 0u;
   }
   __syncthreads();
-  // norms: wave 0 the key groups, wave 1 the value vector
+  if (tid < kD) xs[tid] = xnat[crd];
+  else if (tid < 2 * kD) xs[tid] = xnat[tid];
+  __syncthreads();
+  // norms: wave 0 the key groups (all four sums at once), wave 1 the value vector
   if (tid < 64) {
     const double x0 = xs[2 * tid], x1 = xs[2 * tid + 1];
     const double sq = x0 * x0 + x1 * x1;
     int mg = 0;
-    for (int g = 1; g < hd.n_groups; ++g)
-      if (2 * tid >= hd.pos_off[g]) mg = g;
 #pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g) {
-      const double s = wave_sum_f64(mg == g ? sq : 0.0);
-      if (tid == 0 && g < hd.n_groups) {
-        const double nu = sqrt(s);
-        nu_s[g] = (float)nu;
-        sc_s[g] = nu > 0.0 ? (float)(sqrt((double)hd.dim[g]) / nu) : 0.f;
+    for (int g = 1; g < kMaxGroups; ++g)
+      if (g < n_groups && 2 * tid >= hd->pos_off[g]) mg = g;
+    double s4[kMaxGroups];
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) s4[g] = (mg == g) ? sq : 0.0;
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1)
+#pragma unroll
+      for (int g = 0; g < kMaxGroups; ++g) s4[g] += __shfl_xor(s4[g], sft);
+    if (tid == 0) {
+#pragma unroll
+      for (int g = 0; g < kMaxGroups; ++g) {
+        if (g < n_groups) {
+          const double nu = sqrt(s4[g]);
+          nu_s[g] = (float)nu;
+          sc_s[g] = nu > 0.0 ? (float)(sqrt((double)hd->dim[g]) / nu) : 0.f;
+        }
       }
     }
   } else if (tid < 128) {
@@ -363,29 +405,25 @@ __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
   }
   // rotation partial sums
   {
-    const int o = tid & 255, qq = tid >> 8;
     float acc = 0.f;
     if (o < kD) {
-      int g = 0;
-      for (int gg = 1; gg < hd.n_groups; ++gg)
-        if (o >= hd.pos_off[gg]) g = gg;
-      const int d = hd.dim[g], i = o - hd.pos_off[g];
-      const int lo = (d * qq) >> 2, hi = (d * (qq + 1)) >> 2;
-      const float* pr = a.rot + hd.krot_off[g] + (size_t)i * d;
-      const float* x = xs + hd.pos_off[g];
-#pragma unroll 8
-      for (int j = lo; j < hi; ++j) acc = fmaf(pr[j], x[j], acc);
+      const float2* x = reinterpret_cast<const float2*>(xs + hd->pos_off[kg]);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (klo + u < khi) {
+          const float2 xx = x[klo + u];
+          acc = fmaf(pk[u].x, xx.x, acc);
+          acc = fmaf(pk[u].y, xx.y, acc);
+        }
+      }
     } else {
-      const int i = o - kD;
-      const float4* pr = reinterpret_cast<const float4*>(a.rot + hd.vrot_off + (size_t)i * kD + 32 * qq);
       const float* x = xs + kD + 32 * qq;
 #pragma unroll
-      for (int j4 = 0; j4 < 8; ++j4) {
-        const float4 w = pr[j4];
-        acc = fmaf(w.x, x[4 * j4], acc);
-        acc = fmaf(w.y, x[4 * j4 + 1], acc);
-        acc = fmaf(w.z, x[4 * j4 + 2], acc);
-        acc = fmaf(w.w, x[4 * j4 + 3], acc);
+      for (int u = 0; u < 8; ++u) {
+        acc = fmaf(pv[u].x, x[4 * u], acc);
+        acc = fmaf(pv[u].y, x[4 * u + 1], acc);
+        acc = fmaf(pv[u].z, x[4 * u + 2], acc);
+        acc = fmaf(pv[u].w, x[4 * u + 3], acc);
       }
     }
     red[qq][o] = acc;
@@ -396,12 +434,10 @@ __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
   if (tid < 2 * kD) {
     const float z0 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
     if (tid < kD) {
-      int g = 0;
-      for (int gg = 1; gg < hd.n_groups; ++gg)
-        if (tid >= hd.pos_off[gg]) g = gg;
-      const int b = hd.rate[g];
+      const int g = kg;
+      const int b = hd->rate[g];
       const uint32_t c = quantize(z0 * sc_s[g], a.cb->t[b], (1 << b) - 1);
-      const int bit = hd.bit_off[g] + (tid - hd.pos_off[g]) * b;
+      const int bit = hd->bit_off[g] + (tid - hd->pos_off[g]) * b;
       const uint64_t f = (uint64_t)c << (bit & 31);
       atomicOr(&krec[bit >> 5], (uint32_t)f);
       if (f >> 32) atomicOr(&krec[(bit >> 5) + 1], (uint32_t)(f >> 32));
@@ -424,7 +460,7 @@ __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
   if (tid < a.k_words) a.k_codes[(sh * a.capacity + slot) * a.k_words + tid] = krec[tid];
   if (tid >= 64 && tid < 64 + kNS) {
     const int g = tid - 64;
-    a.k_norms[(sh * a.capacity + slot) * kNS + g] = g < hd.n_groups ? nu_s[g] : 0.f;
+    a.k_norms[(sh * a.capacity + slot) * kNS + g] = g < n_groups ? nu_s[g] : 0.f;
   }
   if (tid == 128) a.v_norms[sh * a.capacity + slot] = nu_s[4];
   if (tid >= 256 && tid < 256 + 32 * vb) {
@@ -436,6 +472,10 @@ __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
       atomicOr(blk + w, vblk[w] & m);
     }
   }
+}
+
+__global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
+  append_token_body(a, blockIdx.x, blockIdx.y);
 }
 
 // ============================================================================
@@ -468,6 +508,7 @@ constexpr int kPS = 132;           // partial record: m, l, 2 pad, acc[128] (16-
 constexpr int kMaxChunks = 256;    // splits per row
 constexpr int kQB = kMaxKB * 64;   // uint4 entries of a tile's QK B operand (8 KB)
 constexpr int kDepth = 2;          // blocks of a wave in flight
+constexpr int kTargetWG = 256;     // partials workgroups the automatic split aims at
 
 struct AttnArgs {
   const DevHead* heads;
@@ -580,50 +621,82 @@ union H8 {
 // per group and 16-coordinate slice i0.. the fp32 MFMA 16x16x4 product
 // D[i][r] = sum_k Pi_g[i0 + i][k] qrec[r][pos_off + k] (the 4 k of lane (q, n) per MFMA
 // are k0 + 4q + s), written as the tile's B operand.
-constexpr int kQrotWaves = 4;
-__global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) {
-  __shared__ float qnat[8][kD];
-  __shared__ float qrec[8][kD];
+constexpr int kQrotWaves = 16;  // 1024 threads: one 16-coordinate slice per wave (at most 11)
+constexpr int kQrotSlices = 1;
+__device__ inline void qrot_body(const AttnArgs& a, int tile) {
+  __shared__ __align__(16) float qnat[8][kD];
+  __shared__ __align__(16) float qrec[8][kD];
   __shared__ uint4 qb[kMaxKB][4][16];
+  constexpr int kT = 64 * kQrotWaves;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, n = lane & 15;
-  const int tile = blockIdx.x;
   int seq, h, tr;
   tile_coords(a, tile, &seq, &h, &tr);
   const DevHead* __restrict__ hp = a.heads + h;
   const int n_groups = hp->n_groups;
+  // this wave's slices (group, first coordinate); slices are numbered over the groups
+  // in order, 16 coordinates each, and wave w takes w, w + 8, ...
+  int sg[kQrotSlices], si0[kQrotSlices];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = tid + 256 * u, r = e >> 7, c = e & (kD - 1);
+  for (int j = 0; j < kQrotSlices; ++j) sg[j] = -1, si0[j] = 0;
+  {
+    int t = 0;
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) {
+      if (g < n_groups) {
+        const int ns = (hp->dim[g] + 15) >> 4;
+#pragma unroll
+        for (int j = 0; j < kQrotSlices; ++j) {
+          const int idx = wave + kQrotWaves * j;
+          if (idx >= t && idx < t + ns) {
+            sg[j] = g;
+            si0[j] = 16 * (idx - t);
+          }
+        }
+        t += ns;
+      }
+    }
+  }
+  // one round of loads: the rotation rows of the slices (lane (q, n): row i0 + n,
+  // columns 16u + 4q + 0..3; d is even, so a pair of columns is wholly in or out), the
+  // tile's query rows in natural order and the head's record order
+  float2 pa[kQrotSlices][8][2];
+#pragma unroll
+  for (int j = 0; j < kQrotSlices; ++j) {
+    const int g = sg[j] < 0 ? 0 : sg[j];
+    const int d = sg[j] < 0 ? 0 : hp->dim[g];
+    const float* R = a.rot + hp->krot_off[g];
+    const int i = si0[j] + n;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kk = 16 * u + 4 * q;
+      pa[j][u][0] = (i < d && kk < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk) : make_float2(0.f, 0.f);
+      pa[j][u][1] = (i < d && kk + 2 < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk + 2)
+                                          : make_float2(0.f, 0.f);
+    }
+  }
+  float qv;
+  {
+    const int r = tid >> 7, c = tid & (kD - 1);  // 8 x 128 == kT
     int L;
     const int id = tile_row(a, seq, h, tr, r, 0, &L);
-    qnat[r][c] = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
+    qv = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
   }
   const int crd = tid < kD ? hp->coord[tid] : 0;
-  for (int e = tid; e < kQB; e += 256) (&qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
+  (&qnat[0][0])[tid] = qv;
+  for (int e = tid; e < kQB; e += kT) (&qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
   __syncthreads();
   if (tid < kD) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) qrec[r][tid] = qnat[r][crd];
   }
   __syncthreads();
-  int t = 0;
-  for (int g = 0; g < n_groups; ++g) {
-    const int d = hp->dim[g], po = hp->pos_off[g], kp0 = hp->kp_off[g];
-    const float* R = a.rot + hp->krot_off[g];
-    const float sc = a.qscale / sqrtf((float)d);
-    for (int i0 = 0; i0 < d; i0 += 16, ++t) {
-      if ((t & (kQrotWaves - 1)) != wave) continue;
-      const int i = i0 + n;
-      float2 pa[8][2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {  // all of the slice's rotation entries first
-        const int kk = 16 * u + 4 * q;  // d is even: a pair of columns is wholly in or out
-        pa[u][0] = (i < d && kk < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk) : make_float2(0.f, 0.f);
-        pa[u][1] = (i < d && kk + 2 < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk + 2)
-                                         : make_float2(0.f, 0.f);
-      }
+  for (int j = 0; j < kQrotSlices; ++j) {
+    if (sg[j] >= 0) {
+      const int g = sg[j], i0 = si0[j];
+      const int d = hp->dim[g], po = hp->pos_off[g], kp0 = hp->kp_off[g];
       floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -632,14 +705,15 @@ __global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) 
           float2 b0 = make_float2(0.f, 0.f), b1 = make_float2(0.f, 0.f);
           if (n < 8 && kk < d) b0 = *reinterpret_cast<const float2*>(&qrec[n][po + kk]);
           if (n < 8 && kk + 2 < d) b1 = *reinterpret_cast<const float2*>(&qrec[n][po + kk + 2]);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][0].x, b0.x, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][0].y, b0.y, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][1].x, b1.x, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[u][1].y, b1.y, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][0].x, b0.x, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][0].y, b0.y, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][1].x, b1.x, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][1].y, b1.y, acc[u & 1], 0, 0, 0);
         }
       }
       // lane (q, n) holds D[4q + e][n]: coordinate i0 + 4q + e of row n
       if (n < 8) {
+        const float sc = a.qscale / sqrtf((float)d);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ii = i0 + 4 * q + e;
@@ -656,7 +730,18 @@ __global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) 
     }
   }
   __syncthreads();
-  for (int e = tid; e < kQB; e += 256) a.qb[(size_t)tile * kQB + e] = (&qb[0][0][0])[e];
+  for (int e = tid; e < kQB; e += kT) a.qb[(size_t)tile * kQB + e] = (&qb[0][0][0])[e];
+}
+
+__global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) { qrot_body(a, blockIdx.x); }
+
+// Decode step preparation in one launch: workgroups [0, n_app) append the step's
+// tokens (token w / n_kv, KV head w % n_kv), the rest rotate the queries of one row
+// tile each; the two roles share no data.
+__global__ void __launch_bounds__(1024) decode_prep_kernel(AppendArgs ap, AttnArgs aa, int n_app) {
+  const int w = blockIdx.x;
+  if (w < n_app) append_token_body(ap, w / ap.n_kv, w % ap.n_kv);
+  else qrot_body(aa, w - n_app);
 }
 
 // ---------------------------------------------------------------- partials
@@ -893,8 +978,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
   const float* vnp = a.v_norms + sh * a.capacity;
   const int c0 = chunk_idx * a.chunk;
   // ---- one round of independent loads: B operand, decode table, rows, first block
-  const uint4 qbv = a.qb[(size_t)tile * kQB + tid];  // kQB == kThreads
-  const uint32_t lutv = tid < kPairTable ? a.cb->pair[tid] : 0u;
+  uint4 qbv[kQB / kThreads];
+#pragma unroll
+  for (int u = 0; u < kQB / kThreads; ++u) qbv[u] = a.qb[(size_t)tile * kQB + tid + kThreads * u];
+  uint32_t lutv[(kPairTable + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int u = 0; u < (kPairTable + kThreads - 1) / kThreads; ++u) {
+    const int e = tid + kThreads * u;
+    lutv[u] = e < kPairTable ? a.cb->pair[e] : 0u;
+  }
   const int len_ld = a.prefill ? 0 : a.seq_len[seq];
   BlockData<VB, KWL> blk[kDepth];
   load_block<VB, KWL>(blk[0], kc, knp, vc, vnp, (int)min<int64_t>(c0 + kBlk * wave, a.capacity - kBlk), kw, lane,
@@ -921,8 +1013,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
       }
     }
   }
-  (&S.qb[0][0][0])[tid] = qbv;
-  if (tid < kPairTable) S.lut[tid] = lutv;
+#pragma unroll
+  for (int u = 0; u < kQB / kThreads; ++u) (&S.qb[0][0][0])[tid + kThreads * u] = qbv[u];
+#pragma unroll
+  for (int u = 0; u < (kPairTable + kThreads - 1) / kThreads; ++u) {
+    const int e = tid + kThreads * u;
+    if (e < kPairTable) S.lut[e] = lutv[u];
+  }
   if (tid < 8) {
     int L;
     S.row_id[tid] = tile_row(a, seq, h, tr, tid, len_ld, &L);
@@ -1032,8 +1129,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
 // ============================================================================
 
 struct MergeArgs {
-  const DevHead* heads;
-  const float* rot;
+  const float* vrot_t;     // Pi_V^T of the layer's KV heads, 128 x 128 each, consecutive
   const float* partials;
   const int32_t* seq_len;
   float* out;
@@ -1041,16 +1137,20 @@ struct MergeArgs {
   int32_t n_q, g, n_chunks, chunk, prefill, max_len;
 };
 
+// One workgroup (256 threads) per row: thread (float4 column c4, chunk slice ks) loads
+// the accumulators of chunks ks, ks + 8, ... together with their (m, l) and its slice
+// of Pi_V^T in one round; then M = max m, weights 2^(m - M), the weighted sums over
+// the slices, normalisation by L sqrt(128) and the inverse rotation.
+constexpr int kMergeRegs = 4;  // chunks per thread kept in registers (32 splits)
 __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
-  __shared__ float wgt[kMaxChunks];
   __shared__ float4 red[8][32];
+  __shared__ float sm[8], sl[8];
   __shared__ float orot[kD];
   __shared__ float opart[2][kD];
-  __shared__ float rm[8], rl[8];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int c4 = tid & 31, ks = tid >> 5;
   const int hq = row % a.n_q;
-  const DevHead& hd = a.heads[hq / a.g];
   int len;
   if (a.prefill) len = (int)(a.pos0 + row / a.n_q + 1);
   else len = min(max(a.seq_len[row / a.n_q], 0), a.max_len);
@@ -1059,46 +1159,64 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   const int oi = tid & 127, oh = tid >> 7;
   float4 pvt[16];
   {
-    const float4* pt = reinterpret_cast<const float4*>(a.rot + hd.vrot_t_off + (size_t)oi * kD + 64 * oh);
+    const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)(hq / a.g) * kD * kD + (size_t)oi * kD + 64 * oh);
 #pragma unroll
     for (int u = 0; u < 16; ++u) pvt[u] = pt[u];
   }
   const float* pp = a.partials + (size_t)row * a.n_chunks * kPS;
-  // maximum over the chunks
-  const float mk = tid < nv ? pp[(size_t)tid * kPS] : -INFINITY;
-  const float lk = tid < nv ? pp[(size_t)tid * kPS + 1] : 0.f;
-  float M = mk;
+  float mk[kMergeRegs], lk[kMergeRegs];
+  float4 xk[kMergeRegs];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) rm[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
-  const float w = (mk == -INFINITY) ? 0.f : exp2f(mk - M);
-  float L = w * lk;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-  if ((tid & 63) == 0) rl[tid >> 6] = L;
-  if (tid < kMaxChunks) wgt[tid] = w;
-  __syncthreads();
-  L = (rl[0] + rl[1]) + (rl[2] + rl[3]);
-  // weighted sum of the accumulators: thread = (float4 column c4, chunk slice of 8)
-  {
-    const int c4 = tid & 31, ks = tid >> 5;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int k = ks; k < nv; k += 8) {
-      const float wk = wgt[k];
-      const float4 x = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS + 4 + 4 * c4);
-      acc.x = fmaf(wk, x.x, acc.x);
-      acc.y = fmaf(wk, x.y, acc.y);
-      acc.z = fmaf(wk, x.z, acc.z);
-      acc.w = fmaf(wk, x.w, acc.w);
+  for (int u = 0; u < kMergeRegs; ++u) {
+    const int k = ks + 8 * u;
+    mk[u] = -INFINITY;
+    lk[u] = 0.f;
+    xk[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < nv) {
+      const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)k * kPS);
+      mk[u] = ml.x;
+      lk[u] = ml.y;
+      xk[u] = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS + 4 + 4 * c4);
     }
-    red[ks][c4] = acc;
   }
+  float ms = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kMergeRegs; ++u) ms = fmaxf(ms, mk[u]);
+  for (int k = ks + 8 * kMergeRegs; k < nv; k += 8) ms = fmaxf(ms, pp[(size_t)k * kPS]);
+  if (c4 == 0) sm[ks] = ms;
+  __syncthreads();
+  float M = sm[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) M = fmaxf(M, sm[w]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int u = 0; u < kMergeRegs; ++u) {
+      const float w = (mk[u] == -INFINITY) ? 0.f : exp2f(mk[u] - M);
+      acc.x = fmaf(w, xk[u].x, acc.x);
+      acc.y = fmaf(w, xk[u].y, acc.y);
+      acc.z = fmaf(w, xk[u].z, acc.z);
+      acc.w = fmaf(w, xk[u].w, acc.w);
+      l = fmaf(w, lk[u], l);
+    }
+    for (int k = ks + 8 * kMergeRegs; k < nv; k += 8) {  // more than 32 splits
+      const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)k * kPS);
+      const float4 x = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS + 4 + 4 * c4);
+      const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+      acc.x = fmaf(w, x.x, acc.x);
+      acc.y = fmaf(w, x.y, acc.y);
+      acc.z = fmaf(w, x.z, acc.z);
+      acc.w = fmaf(w, x.w, acc.w);
+      l = fmaf(w, ml.y, l);
+    }
+  }
+  red[ks][c4] = acc;
+  if (c4 == 0) sl[ks] = l;
   __syncthreads();
   if (tid < 32) {
     float4 s = red[0][tid];
+    float L = sl[0];
 #pragma unroll
     for (int k2 = 1; k2 < 8; ++k2) {
       const float4 y = red[k2][tid];
@@ -1106,8 +1224,9 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
       s.y += y.y;
       s.z += y.z;
       s.w += y.w;
+      L += sl[k2];
     }
-    const float f = L > 0.f ? 0.08838834764831845f / L : 0.f;
+    const float f = L > 0.f ? 0.08838834764831845f / L : 0.f;  // 1 / (L sqrt(128))
     orot[4 * tid] = s.x * f;
     orot[4 * tid + 1] = s.y * f;
     orot[4 * tid + 2] = s.z * f;
@@ -1168,6 +1287,25 @@ int append_lds_bytes(const gtq_plan* p, int layer, int* krot_lds) {
   return (kD * kD + mx) * 4 + kAppendWaves * (int)sizeof(AppendWaveLds);
 }
 
+void fill_append_args(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* k, const float* v,
+                      AppendArgs& a) {
+  a.heads = p->d_heads + (size_t)layer * p->n_kv;
+  a.rot = p->d_rot;
+  a.cb = p->d_cb;
+  a.k_codes = c->k_codes;
+  a.k_norms = c->k_norms;
+  a.v_codes = c->v_codes;
+  a.v_norms = c->v_norms;
+  a.k = k;
+  a.v = v;
+  a.overflow = p->d_overflow;
+  a.capacity = c->capacity;
+  a.batch = c->batch;
+  a.n_kv = p->n_kv;
+  a.k_words = p->k_words;
+  a.v_bits = p->v_bits;
+}
+
 gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* k,
                          const float* v, const int32_t* seq_idx, const int64_t* slot, int32_t seq,
                          int64_t pos0, int64_t n_tok, bool chunk, hipStream_t stream) {
@@ -1220,7 +1358,7 @@ int auto_chunk(int64_t max_len, int64_t tiles) {
   // that ragged batches balance; splits of whole rounds of the main loop (8 waves x
   // 4 blocks x 32 tokens)
   constexpr int64_t kRound = kBlk * kWaves * kDepth;
-  int64_t target = std::max<int64_t>(4, 256 / std::max<int64_t>(1, tiles));
+  int64_t target = std::max<int64_t>(4, kTargetWG / std::max<int64_t>(1, tiles));
   target = std::min<int64_t>(kMaxChunks, target);
   int64_t ch = (max_len + target - 1) / target;
   ch = ((ch + kRound - 1) / kRound) * kRound;
@@ -1293,7 +1431,7 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
 gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const int32_t* seq_len,
                         int64_t pos0, int prefill, int max_len, float* out, const void* ws,
                         hipStream_t stream) {
-  MergeArgs ma{p->d_heads + (size_t)layer * p->n_kv, p->d_rot,
+  MergeArgs ma{p->d_rot + p->heads[(size_t)layer * p->n_kv].vrot_t_off,
                reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + attn_qb_bytes(L.n_tiles)), seq_len,
                out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill, max_len};
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows), dim3(256), 0, stream, ma);
@@ -1511,6 +1649,47 @@ gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_
   if (st != GTQ_OK) return st;
   return gtq_decode_attn_merge(plan, layer, cache, seq_len, max_len, chunk, out, workspace, ws_bytes,
                                hip_stream);
+}
+
+gtq_status gtq_decode_prepare(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                              const float* k_new, const float* v_new, const float* q, const int32_t* seq_len,
+                              int64_t max_len, float softmax_scale, int32_t chunk, void* workspace,
+                              size_t ws_bytes, void* hip_stream) {
+  AttnLaunch L;
+  gtq_status st = decode_check(plan, layer, cache, max_len, chunk, ws_bytes, workspace, &L, "gtq_decode_prepare");
+  if (st != GTQ_OK) return st;
+  if (!k_new || !v_new || !q || !seq_len) return fail(GTQ_EINVAL, "gtq_decode_prepare: NULL pointer");
+  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_decode_prepare: softmax_scale not finite");
+  AppendArgs ap{};
+  fill_append_args(plan, layer, cache, k_new, v_new, ap);
+  ap.step_len = seq_len;
+  ap.n_tok = cache->batch;
+  AttnArgs aa{};
+  fill_attn_args(plan, layer, cache, aa, L, workspace);
+  aa.prefill = 0;
+  aa.max_len = (int32_t)max_len;
+  aa.q = q;
+  aa.qscale = softmax_scale * LOG2E_F;
+  const int n_app = cache->batch * plan->n_kv;
+  hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)(n_app + L.n_tiles)), dim3(1024), 0, (hipStream_t)hip_stream,
+                     ap, aa, n_app);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gtq_decode_prepare: launch");
+  return ok();
+}
+
+gtq_status gtq_decode_step(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                           const float* k_new, const float* v_new, const float* q, const int32_t* seq_len,
+                           int64_t max_len, float softmax_scale, int32_t chunk, float* out, void* workspace,
+                           size_t ws_bytes, void* hip_stream) {
+  if (!out) return fail(GTQ_EINVAL, "gtq_decode_step: out is NULL");
+  gtq_status st = gtq_decode_prepare(plan, layer, cache, k_new, v_new, q, seq_len, max_len, softmax_scale, chunk,
+                                     workspace, ws_bytes, hip_stream);
+  if (st != GTQ_OK) return st;
+  st = gtq_decode_attn_partials(plan, layer, cache, seq_len, max_len, chunk, nullptr, workspace, ws_bytes,
+                                hip_stream);
+  if (st != GTQ_OK) return st;
+  return gtq_decode_attn_merge(plan, layer, cache, seq_len, max_len, chunk, out, workspace, ws_bytes, hip_stream);
 }
 
 static bool prefill_shape(const gtq_plan* p, int64_t pos0, int64_t n_tok, int32_t chunk,

@@ -168,6 +168,55 @@ def test_gqa_ragged_decode_on_oracle_cache(G, chunk):
         assert_close(out[b].cpu().numpy(), out_ref, f"out b{b}")
 
 
+def test_decode_step_fused(G):
+    """gtq_decode_step: every sequence appends its newest token at slot seq_len - 1 and
+    attends to seq_len tokens (lengths 1, 0, 300, 129; 4 KV heads x g=4, K2V2): cache
+    records and outputs against the oracle, and the same outputs as the separate
+    append + decode calls."""
+    _say("case: fused decode step (append + rotate, partials, merge)")
+    case = Case(5, 1, 4, 4, 300, 128, 2, batch=4)
+    plan = case.plan()
+    cap, lens = 320, [1, 0, 300, 129]
+    cache = G.PackedCache(plan, 4, cap)
+    for b, n in enumerate(lens):     # the prompt: all tokens but the step's newest
+        if n > 1:
+            k, v = case.kv(0, b, 0, n - 1)
+            G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k), _dev(v), b, 0)
+    ref_cache = cache.clone()
+    knew = np.zeros((4, case.H, 128), np.float32)
+    vnew = np.zeros((4, case.H, 128), np.float32)
+    for b, n in enumerate(lens):
+        if n > 0:
+            k, v = case.kv(0, b, n - 1, n)
+            knew[b], vnew[b] = k[0], v[0]
+    q = np.stack([case.q(0, b) for b in range(4)])
+    sl = _dev(np.array(lens, np.int32))
+    sc = scale_default()
+    out = G.gtq_decode_step(plan, 0, cache, _dev(knew), _dev(vnew), _dev(q), sl, cap, sc)
+    # the same step as separate calls
+    live = [b for b, n in enumerate(lens) if n > 0]
+    G.gtq_quantize_append(plan, 0, ref_cache, _dev(knew[live]), _dev(vnew[live]),
+                          _dev(np.array(live, np.int32)), _dev(np.array([lens[b] - 1 for b in live], np.int64)))
+    out_sep = G.gtq_decode_attn(plan, 0, ref_cache, _dev(q), sl, cap, sc)
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_norms", "v_codes", "v_norms"):
+        assert torch.equal(getattr(cache, name), getattr(ref_cache, name)), name
+    assert torch.equal(out, out_sep)
+    assert plan.overflow_count() == 1          # the sequence of length 0 appends nothing
+    ties = 0
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[b]) == 0
+            continue
+        enc = _encode(case, 0, b, n)
+        t, _ = _check_append(case, cache, 0, b, n, enc, f"step b{b}")
+        ties += t
+        if t == 0:
+            _, out_ref = _oracle_decode(case, 0, b, n, enc, q[b], sc)
+            assert_close(out[b].cpu().numpy(), out_ref, f"step out b{b}")
+    _say(f"  append ties={ties}")
+
+
 @pytest.mark.parametrize("k_budget,v_bits,g,layout", [(128, 1, 8, 0), (192, 3, 8, 0), (160, 4, 2, 0),
                                                       (64, 2, 8, 0), (256, 2, 4, 0), (192, 3, 2, 1),
                                                       (96, 1, 1, 1)])
