@@ -24,6 +24,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
+// An opaque copy of a register value: lane swaps take their second operand this way,
+// because handed the same value twice this compiler folds their two results into one.
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 gtq_status hip_fail(hipError_t e, const char* what) {
   return fail(GTQ_EDEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -305,6 +312,48 @@ __global__ void __launch_bounds__(64 * kAppendWaves) append_chunk_kernel(AppendA
 // fixed shuffle tree.
 // ============================================================================
 
+// fp64 sum over the 64 lanes of a wave with lane moves that stay in the VALU: DPP row
+// shifts inside each 16-lane row, then the gfx950 row swaps. Every lane gets the
+// total (in a fixed order; the stored fp32 norm of the square root may differ from
+// another summation order by at most one unit in the last place).
+__device__ inline double dpp_f64(double v, int ctrl) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+  switch (ctrl) {
+    case 0: lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false); hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false); break;  // quad [1,0,3,2]
+    case 1: lo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false); hi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false); break;  // quad [2,3,0,1]
+    case 2: lo = __builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, false); hi = __builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, false); break; // row half mirror
+    default: lo = __builtin_amdgcn_mov_dpp(lo, 0x140, 0xF, 0xF, false); hi = __builtin_amdgcn_mov_dpp(hi, 0x140, 0xF, 0xF, false); break; // row mirror
+  }
+  return __builtin_bit_cast(double, (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32));
+}
+__device__ inline double swap_f64(double v, bool x32) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  uint32_t rl, rh;
+  if (x32) {
+    auto a = __builtin_amdgcn_permlane32_swap(lo, opaque(lo), false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(hi, opaque(hi), false, false);
+    rl = (threadIdx.x & 32) ? a[0] : a[1];
+    rh = (threadIdx.x & 32) ? b[0] : b[1];
+  } else {
+    auto a = __builtin_amdgcn_permlane16_swap(lo, opaque(lo), false, false);
+    auto b = __builtin_amdgcn_permlane16_swap(hi, opaque(hi), false, false);
+    rl = (threadIdx.x & 16) ? a[0] : a[1];
+    rh = (threadIdx.x & 16) ? b[0] : b[1];
+  }
+  return __builtin_bit_cast(double, (uint64_t)rl | ((uint64_t)rh << 32));
+}
+__device__ inline double wave_sum_f64_fast(double v) {
+  v += dpp_f64(v, 0);  // pairs
+  v += dpp_f64(v, 1);  // quads
+  v += dpp_f64(v, 2);  // half rows (the mirror of a quad-uniform value is the other quad)
+  v += dpp_f64(v, 3);  // rows
+  v += swap_f64(v, false);
+  v += swap_f64(v, true);
+  return v;
+}
+
 __device__ inline double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -323,6 +372,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   __shared__ float nu_s[5], sc_s[5];
   __shared__ uint32_t krec[16];
   __shared__ uint32_t vblk[128], vmask[128];
+  __shared__ float thr[5][16];
   const int tid = threadIdx.x;
   const DevHead* __restrict__ hd = a.heads + h;
   const int n_groups = hd->n_groups;
@@ -331,6 +381,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   if (tid < kD) xv = a.k[row + tid];
   else if (tid < 2 * kD) xv = a.v[row + tid - kD];
   const int crd = tid < kD ? hd->coord[tid] : 0;
+  const float thv = tid < 80 ? (&a.cb->t[0][0])[tid] : 0.f;
   // this thread's rotation entries: key output o < 128 (row i of its group, pair range
   // of quarter qq) or value output o - 128 (32 columns of quarter qq)
   const int o = tid & 255, qq = tid >> 8;
@@ -359,6 +410,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     return;
   }
   if (tid < 2 * kD) xnat[tid] = xv;
+  if (tid < 80) (&thr[0][0])[tid] = thv;
   if (tid < 16) krec[tid] = 0u;
   if (tid < 128) {
     vblk[tid] = 0u;
@@ -380,23 +432,19 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
 #pragma unroll
     for (int g = 0; g < kMaxGroups; ++g) s4[g] = (mg == g) ? sq : 0.0;
 #pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1)
+    for (int g = 0; g < kMaxGroups; ++g) s4[g] = wave_sum_f64_fast(s4[g]);
+    if (tid < n_groups) {  // lane g finishes group g (every lane holds all four sums)
+      double sg = s4[0];
 #pragma unroll
-      for (int g = 0; g < kMaxGroups; ++g) s4[g] += __shfl_xor(s4[g], sft);
-    if (tid == 0) {
-#pragma unroll
-      for (int g = 0; g < kMaxGroups; ++g) {
-        if (g < n_groups) {
-          const double nu = sqrt(s4[g]);
-          nu_s[g] = (float)nu;
-          sc_s[g] = nu > 0.0 ? (float)(sqrt((double)hd->dim[g]) / nu) : 0.f;
-        }
-      }
+      for (int g = 1; g < kMaxGroups; ++g) sg = (tid == g) ? s4[g] : sg;
+      const double nu = sqrt(sg);
+      nu_s[tid] = (float)nu;
+      sc_s[tid] = nu > 0.0 ? (float)(sqrt((double)hd->dim[tid]) / nu) : 0.f;
     }
   } else if (tid < 128) {
     const int l = tid - 64;
     const double x0 = xs[kD + 2 * l], x1 = xs[kD + 2 * l + 1];
-    const double s = wave_sum_f64(x0 * x0 + x1 * x1);
+    const double s = wave_sum_f64_fast(x0 * x0 + x1 * x1);
     if (l == 0) {
       const double nu = sqrt(s);
       nu_s[4] = (float)nu;
@@ -436,14 +484,14 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     if (tid < kD) {
       const int g = kg;
       const int b = hd->rate[g];
-      const uint32_t c = quantize(z0 * sc_s[g], a.cb->t[b], (1 << b) - 1);
+      const uint32_t c = quantize(z0 * sc_s[g], thr[b], (1 << b) - 1);
       const int bit = hd->bit_off[g] + (tid - hd->pos_off[g]) * b;
       const uint64_t f = (uint64_t)c << (bit & 31);
       atomicOr(&krec[bit >> 5], (uint32_t)f);
       if (f >> 32) atomicOr(&krec[(bit >> 5) + 1], (uint32_t)(f >> 32));
     } else {
       const int cidx = tid - kD;
-      const uint32_t c = quantize(z0 * sc_s[4], a.cb->t[vb], (1 << vb) - 1);
+      const uint32_t c = quantize(z0 * sc_s[4], thr[vb], (1 << vb) - 1);
       const int bit = 8 * vb * cidx + vb * j0;
       const uint64_t f = (uint64_t)c << (bit & 31);
       const uint64_t m = (uint64_t)((1u << vb) - 1u) << (bit & 31);
@@ -580,12 +628,7 @@ __device__ inline float dpp_row_mirror(float x) {
 
 // Lane swaps of gfx950. v_permlane16_swap(x, y) exchanges the odd 16-lane rows of x
 // with the even rows of y (permlane32_swap: the upper half of x with the lower half of
-// y). The second operand is an opaque copy: handed the same value twice, this compiler
-// folds the two results into one.
-__device__ inline uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
+// y); the second operand is an opaque copy (see opaque()).
 // value of lane l ^ 16 and of lane l ^ 32
 __device__ inline float xor16(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -697,18 +740,25 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
     if (sg[j] >= 0) {
       const int g = sg[j], i0 = si0[j];
       const int d = hp->dim[g], po = hp->pos_off[g], kp0 = hp->kp_off[g];
+      // the B operands (row n of the record-order queries) first: reads at clamped
+      // addresses, zero outside the group or for n >= 8
+      float2 bq[8][2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int kk = 16 * u + 4 * q;
+        const float2 x0 = *reinterpret_cast<const float2*>(&qrec[n & 7][min(po + kk, kD - 2)]);
+        const float2 x1 = *reinterpret_cast<const float2*>(&qrec[n & 7][min(po + kk + 2, kD - 2)]);
+        bq[u][0] = (n < 8 && kk < d) ? x0 : make_float2(0.f, 0.f);
+        bq[u][1] = (n < 8 && kk + 2 < d) ? x1 : make_float2(0.f, 0.f);
+      }
       floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (16 * u < d) {
-          const int kk = 16 * u + 4 * q;
-          float2 b0 = make_float2(0.f, 0.f), b1 = make_float2(0.f, 0.f);
-          if (n < 8 && kk < d) b0 = *reinterpret_cast<const float2*>(&qrec[n][po + kk]);
-          if (n < 8 && kk + 2 < d) b1 = *reinterpret_cast<const float2*>(&qrec[n][po + kk + 2]);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][0].x, b0.x, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][0].y, b0.y, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][1].x, b1.x, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][1].y, b1.y, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][0].x, bq[u][0].x, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][0].y, bq[u][0].y, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][1].x, bq[u][1].x, acc[u & 1], 0, 0, 0);
+          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][1].y, bq[u][1].y, acc[u & 1], 0, 0, 0);
         }
       }
       // lane (q, n) holds D[4q + e][n]: coordinate i0 + 4q + e of row n
