@@ -229,7 +229,7 @@ def main():
                    "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "attn_partials_kernel<2>", "kernel_avg_us": round(kern_avg * 1e3, 3),
+                     "kernel": "attn_partials_kernel<2, 4>", "kernel_avg_us": round(kern_avg * 1e3, 3),
                      "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
                      "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
                      "alg_bytes_per_launch": int(alg_bytes)},
