@@ -19,6 +19,12 @@ using namespace gtq;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+union H8 {  // an MFMA f16 operand as a vector, dwords or one uint4
+  half8 h;
+  uint32_t u[4];
+  uint4 v;
+};
+
 #define LOG2E_F 1.4426950408889634f
 #define LN2_F 0.6931471805599453f
 
@@ -44,11 +50,10 @@ gtq_status hip_fail(hipError_t e, const char* what) {
 // in LDS.
 // ============================================================================
 
-constexpr int kAppendWaves = 2;
-
 struct AppendArgs {
   const DevHead* heads;  // this layer's heads [n_kv]
   const float* rot;
+  const uint16_t* rsplit;  // split rotations (binary16 hi, lo)
   const DevCodebook* cb;
   uint32_t* k_codes;
   float* k_norms;
@@ -62,24 +67,12 @@ struct AppendArgs {
   unsigned long long* overflow;
   int64_t capacity;
   int64_t n_tok;
-  int64_t n_items;
   int64_t pos0;
   int32_t seq;
   int32_t batch;
   int32_t n_kv;
   int32_t k_words;
   int32_t v_bits;
-  int32_t krot_lds;  // floats reserved for K rotations in LDS
-};
-
-struct AppendWaveLds {
-  float xk[kD][8];       // key coordinates in record order, [position][token]
-  float xv[kD][8];       // value coordinates, [coordinate][token]
-  float scale[8][5];     // sqrt(d)/nu per token and vector (4 = value)
-  float nu[8][5];
-  uint32_t krec[8][16];  // packed key records
-  uint32_t vblk[128];    // packed value block words
-  uint32_t vmask[128];   // bits of the value block written by this item
 };
 
 __device__ inline int quantize(float z, const float* thr, int n_thr) {
@@ -87,230 +80,6 @@ __device__ inline int quantize(float z, const float* thr, int n_thr) {
   for (int k = 0; k < n_thr; ++k) c += (z >= thr[k]) ? 1 : 0;
   return c;
 }
-
-__global__ void __launch_bounds__(64 * kAppendWaves) append_chunk_kernel(AppendArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* rotv_t = reinterpret_cast<float*>(smem);             // [j][i], 128 x 128
-  float* rotk_t = rotv_t + kD * kD;                            // per group [j][i]
-  AppendWaveLds* wl = reinterpret_cast<AppendWaveLds*>(rotk_t + a.krot_lds);
-
-  const int h = blockIdx.y;
-  const DevHead& hd = a.heads[h];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  AppendWaveLds& L = wl[wave];
-
-  // Stage the rotations transposed: rot_t[j*d + i] = Pi[i][j].
-  {
-    const float* pv = a.rot + hd.vrot_off;
-    for (int e = tid; e < kD * kD; e += blockDim.x) {
-      const int i = e >> 7, j = e & 127;
-      rotv_t[j * kD + i] = pv[e];
-    }
-    int base = 0;
-    for (int g = 0; g < hd.n_groups; ++g) {
-      const int d = hd.dim[g];
-      const float* pk = a.rot + hd.krot_off[g];
-      for (int e = tid; e < d * d; e += blockDim.x) {
-        const int i = e / d, j = e - i * d;
-        rotk_t[base + j * d + i] = pk[e];
-      }
-      base += d * d;
-    }
-  }
-  __syncthreads();
-
-  const int vb = a.v_bits;
-  const int kw = a.k_words;
-  // lane's pair of key record positions (2*lane, 2*lane+1): group, index in group
-  const int p0 = 2 * lane;
-  int kg = 0;
-  for (int g = 1; g < hd.n_groups; ++g)
-    if (p0 >= hd.pos_off[g]) kg = g;
-  const int kd = hd.dim[kg];
-  const int ki = p0 - hd.pos_off[kg];
-  int krot_base = 0;
-  for (int g = 0; g < kg; ++g) krot_base += hd.dim[g] * hd.dim[g];
-  const int kb = hd.rate[kg];
-  const float* kthr = a.cb->t[kb];
-  const float* vthr = a.cb->t[vb];
-
-  for (int64_t item = (int64_t)blockIdx.x * kAppendWaves + wave; item < a.n_items;
-       item += (int64_t)gridDim.x * kAppendWaves) {
-    // item = the part of value block (pos0/8 + item) that the chunk covers
-    const int64_t blk = a.pos0 / GTQ_VBLOCK + item;
-    const int64_t lo = max(a.pos0, blk * GTQ_VBLOCK);
-    const int64_t hi = min(a.pos0 + a.n_tok, (blk + 1) * GTQ_VBLOCK);
-    const int64_t s_first = lo;
-    const int nt = (int)(hi - lo);
-    const int64_t tok_first = lo - a.pos0;
-    const int seq = a.seq;
-    const int j0 = (int)(s_first & (GTQ_VBLOCK - 1));
-    const size_t sh = (size_t)seq * a.n_kv + h;
-
-    // -- stage inputs (record order for keys), zero the pack buffers
-    for (int t = 0; t < 8; ++t) {
-      float xk0 = 0.f, xk1 = 0.f, xv0 = 0.f, xv1 = 0.f;
-      if (t < nt) {
-        const size_t row = ((size_t)(tok_first + t) * a.n_kv + h) * kD;
-        xk0 = a.k[row + hd.coord[p0]];
-        xk1 = a.k[row + hd.coord[p0 + 1]];
-        const float2 vv = *reinterpret_cast<const float2*>(a.v + row + p0);
-        xv0 = vv.x;
-        xv1 = vv.y;
-      }
-      L.xk[p0][t] = xk0;
-      L.xk[p0 + 1][t] = xk1;
-      L.xv[p0][t] = xv0;
-      L.xv[p0 + 1][t] = xv1;
-    }
-    for (int e = lane; e < 8 * 16; e += 64) (&L.krec[0][0])[e] = 0u;
-    for (int e = lane; e < 128; e += 64) {
-      L.vblk[e] = 0u;
-      L.vmask[e] = 0u;
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // -- norms: one lane per (token, vector), fp64 sum of squares
-    if (lane < 40) {
-      const int t = lane / 5, vec = lane - 5 * (lane / 5);
-      if (t < nt && (vec == 4 || vec < hd.n_groups)) {
-        double s = 0.0;
-        int d;
-        if (vec == 4) {
-          d = kD;
-          for (int c = 0; c < kD; ++c) {
-            const double x = L.xv[c][t];
-            s = fma(x, x, s);
-          }
-        } else {
-          d = hd.dim[vec];
-          const int off = hd.pos_off[vec];
-          for (int c = 0; c < d; ++c) {
-            const double x = L.xk[off + c][t];
-            s = fma(x, x, s);
-          }
-        }
-        const double nu = sqrt(s);
-        L.nu[t][vec] = (float)nu;
-        L.scale[t][vec] = nu > 0.0 ? (float)(sqrt((double)d) / nu) : 0.f;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // -- key rotation: this lane's two outputs of its group, for all 8 tokens
-    {
-      float acc0[8], acc1[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc0[t] = acc1[t] = 0.f;
-      const float* rt = rotk_t + krot_base + ki;
-      const int xoff = hd.pos_off[kg];
-      for (int j = 0; j < kd; ++j) {
-        const float2 r = *reinterpret_cast<const float2*>(rt + j * kd);
-        const float4 xa = *reinterpret_cast<const float4*>(&L.xk[xoff + j][0]);
-        const float4 xb = *reinterpret_cast<const float4*>(&L.xk[xoff + j][4]);
-        const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          acc0[t] = fmaf(r.x, x[t], acc0[t]);
-          acc1[t] = fmaf(r.y, x[t], acc1[t]);
-        }
-      }
-      const int nthr = (1 << kb) - 1;
-      const int bitpos = hd.bit_off[kg] + ki * kb;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (t < nt) {
-          const float sc = L.scale[t][kg];
-          const uint32_t c0 = quantize(acc0[t] * sc, kthr, nthr);
-          const uint32_t c1 = quantize(acc1[t] * sc, kthr, nthr);
-          const uint64_t f = (uint64_t)(c0 | (c1 << kb)) << (bitpos & 31);
-          atomicOr(&L.krec[t][bitpos >> 5], (uint32_t)f);
-          if ((f >> 32) != 0) atomicOr(&L.krec[t][(bitpos >> 5) + 1], (uint32_t)(f >> 32));
-        }
-      }
-    }
-    // -- value rotation and packing into the 8-token block
-    {
-      float acc0[8], acc1[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc0[t] = acc1[t] = 0.f;
-      const float* rt = rotv_t + p0;
-      for (int j = 0; j < kD; ++j) {
-        const float2 r = *reinterpret_cast<const float2*>(rt + j * kD);
-        const float4 xa = *reinterpret_cast<const float4*>(&L.xv[j][0]);
-        const float4 xb = *reinterpret_cast<const float4*>(&L.xv[j][4]);
-        const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          acc0[t] = fmaf(r.x, x[t], acc0[t]);
-          acc1[t] = fmaf(r.y, x[t], acc1[t]);
-        }
-      }
-      const int nthr = (1 << vb) - 1;
-      const uint32_t ones = (1u << vb) - 1u;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (t < nt) {
-          const float sc = L.scale[t][4];
-          const uint32_t c[2] = {(uint32_t)quantize(acc0[t] * sc, vthr, nthr),
-                                 (uint32_t)quantize(acc1[t] * sc, vthr, nthr)};
-          const int j = j0 + t;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int bit = 8 * vb * (p0 + u) + vb * j;
-            const uint64_t f = (uint64_t)c[u] << (bit & 31);
-            const uint64_t m = (uint64_t)ones << (bit & 31);
-            atomicOr(&L.vblk[bit >> 5], (uint32_t)f);
-            atomicOr(&L.vmask[bit >> 5], (uint32_t)m);
-            if ((m >> 32) != 0) {
-              atomicOr(&L.vblk[(bit >> 5) + 1], (uint32_t)(f >> 32));
-              atomicOr(&L.vmask[(bit >> 5) + 1], (uint32_t)(m >> 32));
-            }
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // -- stores
-    for (int e = lane; e < nt * kw; e += 64) {
-      const int t = e / kw, w = e - t * kw;
-      a.k_codes[(sh * a.capacity + s_first + t) * kw + w] = L.krec[t][w];
-    }
-    if (lane < nt * kNS) {
-      const int t = lane / kNS, g = lane - kNS * (lane / kNS);
-      a.k_norms[(sh * a.capacity + s_first + t) * kNS + g] = g < hd.n_groups ? L.nu[t][g] : 0.f;
-    }
-    if (lane < nt) a.v_norms[sh * a.capacity + s_first + lane] = L.nu[lane][4];
-    {
-      const int vw = 32 * vb;
-      uint32_t* blk = a.v_codes + (sh * (size_t)(a.capacity / GTQ_VBLOCK) +
-                                   (size_t)(s_first / GTQ_VBLOCK)) * vw;
-      if (nt == GTQ_VBLOCK) {
-        for (int w = lane; w < vw; w += 64) blk[w] = L.vblk[w];
-      } else {
-        for (int w = lane; w < vw; w += 64) {
-          const uint32_t m = L.vmask[w];
-          if (m) {
-            atomicAnd(blk + w, ~m);
-            atomicOr(blk + w, L.vblk[w] & m);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-// ============================================================================
-// Append of scattered single tokens (decode steps): one 1024-thread workgroup per
-// (token, KV head); each of the 256 outputs (128 key record positions, 128 value
-// coordinates) is a dot product split over 4 thread groups so that the rotation rows
-// are read with many loads in flight. Norms: fp64 sums of squares, reduced by a
-// fixed shuffle tree.
-// ============================================================================
 
 // fp64 sum over the 64 lanes of a wave with lane moves that stay in the VALU: DPP row
 // shifts inside each 16-lane row, then the gfx950 row swaps. Every lane gets the
@@ -358,6 +127,296 @@ __device__ inline double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
+}
+
+// ============================================================================
+// Chunk append as a rotation GEMM on the matrix cores (TurboQuant diagram, "paper"
+// column: norm, rotation, per-coordinate quantization; Block-GTQ abstract, 5th
+// sentence: one TQ-MSE instance per equal-rate group).
+// Per token and vector (each key group, the value): nu = ||x|| in fp64, u = x / nu,
+// z = sqrt(d) Pi u, code = #{k : z >= t_k}. The product Pi u runs as MFMA 16x16x32
+// f16 on split operands: 16 Pi = P_hi + P_lo (plan tables) and 256 u = U_hi + U_lo
+// (binary16 each); P_hi U_hi + P_hi U_lo + P_lo U_hi leaves out a 2^-22-relative term,
+// so z carries fp32-grade error.
+// A workgroup (8 waves) takes one KV head and one role (keys or values); each wave
+// keeps the rotation operands of its output tiles (16 outputs x all inputs) in
+// registers, and the workgroup streams 16-token tiles through LDS: stage, norms,
+// split, products and codes, pack and store.
+// ============================================================================
+
+constexpr int kAppWaves = 8;
+constexpr int kAppThreads = 64 * kAppWaves;
+constexpr int kAppTile = 16;          // tokens per tile (MFMA rows)
+constexpr int kAppPitch = 264;        // halves per A row (256 padded inputs + 8: no bank conflicts)
+
+struct AppendGemmShared {
+  float x[kAppTile][kD + 4];          // staged inputs (keys in record order)
+  _Float16 ua[2][kAppTile][kAppPitch];  // U_hi, U_lo in the padded input order
+  uint8_t code[kAppTile][kD];         // codes by record position (keys) or coordinate (values)
+  float nu[kAppTile][5];              // fp32 norms per token: key groups 0..3, value 4
+  float thr[5][16];                   // quantizer thresholds by rate
+  double inv[kAppTile][5];            // 1 / nu
+};
+
+// fp64 sum over the 32 lanes l & ~31 .. l | 31 (one token): DPP inside each 16-lane row,
+// then the row swap
+__device__ inline double half_wave_sum_f64(double v) {
+  v += dpp_f64(v, 0);
+  v += dpp_f64(v, 1);
+  v += dpp_f64(v, 2);
+  v += dpp_f64(v, 3);
+  v += swap_f64(v, false);
+  return v;
+}
+
+__global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) {
+  __shared__ AppendGemmShared S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, n = lane & 15;
+  const int h = blockIdx.y;
+  const bool vrole = blockIdx.z != 0;
+  const DevHead* __restrict__ hp = a.heads + h;
+  const int n_groups = hp->n_groups;
+
+  // ---- this wave's output tiles: values: outputs 16 wave .. +15 over 4 input steps;
+  //      keys: tiles numbered over the groups (16 outputs each), wave w takes w, w + 8
+  int tg[2] = {-1, -1}, ti0[2] = {0, 0}, tsteps[2] = {0, 0}, trate[2] = {0, 0};
+  if (vrole) {
+    tg[0] = 4;
+    ti0[0] = 16 * wave;
+    tsteps[0] = 4;
+    trate[0] = a.v_bits;
+  } else {
+    int t = 0;
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) {
+      if (g < n_groups) {
+        const int d = hp->dim[g], ns = (d + 15) >> 4;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int idx = wave + kAppWaves * j;
+          if (idx >= t && idx < t + ns) {
+            tg[j] = g;
+            ti0[j] = 16 * (idx - t);
+            tsteps[j] = (d + 31) >> 5;
+            trate[j] = hp->rate[g];
+          }
+        }
+        t += ns;
+      }
+    }
+  }
+  // rotation operands: lane (q, n) holds rows i0 + n, inputs 32 s + 8q .. +7, hi and lo
+  uint4 bh[2][4], bl[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bh[j][s] = make_uint4(0, 0, 0, 0);
+      bl[j][s] = make_uint4(0, 0, 0, 0);
+      if (tg[j] >= 0 && s < tsteps[j]) {
+        int rows, cols;
+        int64_t off;
+        if (tg[j] == 4) {
+          rows = kD;
+          cols = kD;
+          off = hp->rsv_off;
+        } else {
+          const int d = hp->dim[tg[j]];
+          rows = (d + 15) >> 4 << 4;
+          cols = (d + 31) >> 5 << 5;
+          off = hp->rsk_off[tg[j]];
+        }
+        const uint16_t* base = a.rsplit + off + (size_t)(ti0[j] + n) * cols + 32 * s + 8 * q;
+        bh[j][s] = *reinterpret_cast<const uint4*>(base);
+        bl[j][s] = *reinterpret_cast<const uint4*>(base + (size_t)rows * cols);
+      }
+    }
+  }
+  if (tid < 80) (&S.thr[0][0])[tid] = (&a.cb->t[0][0])[tid];
+  // zero the A operands once: padding columns stay zero
+  for (int e = tid; e < 2 * kAppTile * kAppPitch / 8; e += kAppThreads)
+    reinterpret_cast<uint4*>(&S.ua[0][0][0])[e] = make_uint4(0, 0, 0, 0);
+
+  // ---- this thread's 4 staged elements: token tau = tid >> 5, columns c = (tid & 31) + 32 i
+  const int tau = tid >> 5, sub = tid & 31;
+  int src_col[4], kp_col[4], grp_of[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = sub + 32 * i;  // record position (keys) or coordinate (values)
+    if (vrole) {
+      src_col[i] = c;
+      kp_col[i] = c;
+      grp_of[i] = 4;
+    } else {
+      int g = 0;
+#pragma unroll
+      for (int gg = 1; gg < kMaxGroups; ++gg)
+        if (gg < n_groups && c >= hp->pos_off[gg]) g = gg;
+      src_col[i] = hp->coord[c];
+      kp_col[i] = hp->kp_off[g] + (c - hp->pos_off[g]);
+      grp_of[i] = g;
+    }
+  }
+  const float* src = vrole ? a.v : a.k;
+  const int64_t s_begin = a.pos0 & ~(int64_t)(GTQ_VBLOCK - 1), s_end = a.pos0 + a.n_tok;
+  const int64_t n_tiles = (s_end - s_begin + kAppTile - 1) / kAppTile;
+  const size_t sh = (size_t)a.seq * a.n_kv + h;
+  const int kw = a.k_words, vb = a.v_bits;
+
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int64_t ts = s_begin + tile * kAppTile;
+    // ---- stage (zeros for slots outside the chunk)
+    {
+      const int64_t s = ts + tau;
+      const bool ok = s >= a.pos0 && s < s_end;
+      const size_t row = ((size_t)(s - a.pos0) * a.n_kv + h) * kD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S.x[tau][sub + 32 * i] = ok ? src[row + src_col[i]] : 0.f;
+    }
+    __syncthreads();
+    // ---- norms (fp64): 4 key groups or the value, per token
+    {
+      double sg[kMaxGroups] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double xv = S.x[tau][sub + 32 * i];
+        const int g = vrole ? 0 : grp_of[i];
+#pragma unroll
+        for (int gg = 0; gg < kMaxGroups; ++gg) sg[gg] += (g == gg) ? xv * xv : 0.0;
+      }
+      const int ng = vrole ? 1 : kMaxGroups;
+#pragma unroll
+      for (int gg = 0; gg < kMaxGroups; ++gg)
+        if (gg < ng) sg[gg] = half_wave_sum_f64(sg[gg]);
+      const int nv = vrole ? 1 : n_groups;
+      if (sub < nv) {
+        double v = sg[0];
+#pragma unroll
+        for (int gg = 1; gg < kMaxGroups; ++gg) v = (sub == gg) ? sg[gg] : v;
+        const double nu = sqrt(v);
+        const int slot = vrole ? 4 : sub;
+        S.nu[tau][slot] = (float)nu;
+        S.inv[tau][slot] = nu > 0.0 ? 1.0 / nu : 0.0;
+      }
+    }
+    __syncthreads();
+    // ---- split u = x / nu: 256 u = U_hi + U_lo
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = vrole ? 4 : grp_of[i];
+      const float u = (float)((double)S.x[tau][sub + 32 * i] * S.inv[tau][slot]) * 256.f;
+      const _Float16 hi = (_Float16)u;
+      S.ua[0][tau][kp_col[i]] = hi;
+      S.ua[1][tau][kp_col[i]] = (_Float16)(u - (float)hi);
+    }
+    __syncthreads();
+    // ---- products and codes of this wave's tiles
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (tg[j] >= 0) {
+        const int g = tg[j];
+        const int kb0 = (g == 4) ? 0 : hp->kp_off[g];
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s < tsteps[j]) {
+            H8 ah, al, ph, pl;
+            ah.v = *reinterpret_cast<const uint4*>(&S.ua[0][n][kb0 + 32 * s + 8 * q]);
+            al.v = *reinterpret_cast<const uint4*>(&S.ua[1][n][kb0 + 32 * s + 8 * q]);
+            ph.v = bh[j][s];
+            pl.v = bl[j][s];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, ph.h, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al.h, ph.h, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, pl.h, acc, 0, 0, 0);
+          }
+        }
+        // lane (q, n) holds D[token 4q + e][output i0 + n]
+        const int d = (g == 4) ? kD : hp->dim[g];
+        const int i = ti0[j] + n;
+        if (i < d) {
+          const float zs = sqrtf((float)d) * (1.f / (kRotSplitScale * 256.f));
+          const int nthr = (1 << trate[j]) - 1;
+          const float* th = S.thr[trate[j]];
+          const int pos = (g == 4) ? i : hp->pos_off[g] + i;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = acc[e] * zs;
+            int c = 0;
+            for (int k = 0; k < nthr; ++k) c += (z >= th[k]) ? 1 : 0;
+            S.code[4 * q + e][pos] = (uint8_t)c;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- pack and store
+    if (!vrole) {
+      // key record word w of token t: the codes whose bits meet [32 w, 32 w + 32)
+      for (int e = tid; e < kAppTile * kw; e += kAppThreads) {
+        const int t = e / kw, w = e - t * kw;
+        const int64_t s = ts + t;
+        if (s < a.pos0 || s >= s_end) continue;
+        uint32_t word = 0;
+        for (int g = 0; g < n_groups; ++g) {
+          const int r = hp->rate[g], b0 = hp->bit_off[g], d = hp->dim[g], po = hp->pos_off[g];
+          const int lo = max(0, (32 * w - b0) / r - 1), hi = min(d, (32 * w + 32 - b0 + r - 1) / r);
+          for (int i = lo; i < hi; ++i) {
+            const int bit = b0 + i * r - 32 * w;
+            const uint32_t c = S.code[t][po + i];
+            if (bit >= 0 && bit < 32) word |= c << bit;
+            else if (bit < 0 && bit > -r) word |= c >> (-bit);
+          }
+        }
+        a.k_codes[(sh * a.capacity + s) * kw + w] = word;
+      }
+      if (tid < kAppTile * kNS) {
+        const int t = tid / kNS, g = tid - kNS * t;
+        const int64_t s = ts + t;
+        if (s >= a.pos0 && s < s_end) a.k_norms[(sh * a.capacity + s) * kNS + g] = g < n_groups ? S.nu[t][g] : 0.f;
+      }
+    } else {
+      // value block b (tokens 8b..8b+7 of the tile), word w: token j of coordinate c at
+      // bit 8 vb c + vb j
+      const int vw = 32 * vb;
+      for (int e = tid; e < 2 * vw; e += kAppThreads) {
+        const int b = e / vw, w = e - b * vw;
+        const int64_t sb = ts + 8 * b;
+        if (sb + 8 <= a.pos0 || sb >= s_end) continue;  // no token of this block in the chunk
+        uint32_t word = 0, mask = 0;
+        const int c_lo = (32 * w) / (8 * vb), c_hi = min(kD - 1, (32 * w + 31) / (8 * vb));
+        for (int c = c_lo; c <= c_hi; ++c) {
+          for (int jt = 0; jt < 8; ++jt) {
+            const int bit = 8 * vb * c + vb * jt - 32 * w;
+            if (bit <= -vb || bit >= 32) continue;
+            const int64_t s = sb + jt;
+            if (s < a.pos0 || s >= s_end) continue;
+            const uint32_t cv = S.code[8 * b + jt][c];
+            const uint32_t m = (1u << vb) - 1u;
+            if (bit >= 0) {
+              word |= cv << bit;
+              mask |= m << bit;
+            } else {
+              word |= cv >> (-bit);
+              mask |= m >> (-bit);
+            }
+          }
+        }
+        uint32_t* blk = a.v_codes + (sh * (size_t)(a.capacity / GTQ_VBLOCK) + (size_t)(sb / GTQ_VBLOCK)) * vw;
+        if (sb >= a.pos0 && sb + 8 <= s_end) {
+          blk[w] = word;
+        } else if (mask) {
+          atomicAnd(blk + w, ~mask);
+          atomicOr(blk + w, word);
+        }
+      }
+      if (tid < kAppTile) {
+        const int64_t s = ts + tid;
+        if (s >= a.pos0 && s < s_end) a.v_norms[sh * a.capacity + s] = S.nu[tid][4];
+      }
+    }
+  }
 }
 
 // One workgroup (1024 threads) per (token, KV head). All global loads go out in one
@@ -651,12 +710,6 @@ __device__ inline float sum_over_q(float x) {
 }
 // value of lane l ^ 48
 __device__ inline float swap_q3(float x) { return xor16(xor32(x)); }
-
-union H8 {
-  half8 h;
-  uint32_t u[4];
-  uint4 v;
-};
 
 // ---------------------------------------------------------------- query rotation
 
@@ -1326,21 +1379,11 @@ bool check_cache(const gtq_plan* p, const gtq_cache_view* c, const char* fn, gtq
   return true;
 }
 
-// rotations (V: 128^2, K: at most 128^2 floats) plus the per-wave staging
-constexpr int kAppendLdsMax = 2 * kD * kD * 4 + kAppendWaves * (int)sizeof(AppendWaveLds);
-
-int append_lds_bytes(const gtq_plan* p, int layer, int* krot_lds) {
-  int mx = 0;
-  for (int h = 0; h < p->n_kv; ++h) mx = std::max(mx, p->heads[(size_t)layer * p->n_kv + h].krot_floats);
-  mx = (mx + 3) & ~3;
-  *krot_lds = mx;
-  return (kD * kD + mx) * 4 + kAppendWaves * (int)sizeof(AppendWaveLds);
-}
-
 void fill_append_args(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* k, const float* v,
                       AppendArgs& a) {
   a.heads = p->d_heads + (size_t)layer * p->n_kv;
   a.rot = p->d_rot;
+  a.rsplit = p->d_rsplit;
   a.cb = p->d_cb;
   a.k_codes = c->k_codes;
   a.k_norms = c->k_norms;
@@ -1362,6 +1405,7 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   AppendArgs a{};
   a.heads = p->d_heads + (size_t)layer * p->n_kv;
   a.rot = p->d_rot;
+  a.rsplit = p->d_rsplit;
   a.cb = p->d_cb;
   a.k_codes = c->k_codes;
   a.k_norms = c->k_norms;
@@ -1387,18 +1431,16 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
     if (e != hipSuccess) return hip_fail(e, "gtq append: launch");
     return ok();
   }
-  a.n_items = (pos0 + n_tok - 1) / GTQ_VBLOCK - pos0 / GTQ_VBLOCK + 1;
-  const int lds = append_lds_bytes(p, layer, &a.krot_lds);
-  const int64_t wg_needed = (a.n_items + kAppendWaves - 1) / kAppendWaves;
-  const int gx = (int)std::min<int64_t>(wg_needed, std::max(1, 2048 / p->n_kv));
-  dim3 grid(gx, p->n_kv);
-  // allow the largest dynamic LDS any plan can need (set once)
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)append_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kAppendLdsMax);
-  hipError_t e = attr;
-  if (e != hipSuccess) return hip_fail(e, "gtq append: LDS attribute");
-  hipLaunchKernelGGL(append_chunk_kernel, grid, dim3(64 * kAppendWaves), lds, stream, a);
-  e = hipGetLastError();
+  a.n_tok = n_tok;
+  a.pos0 = pos0;
+  a.seq = seq;
+  const int64_t s_begin = pos0 & ~(int64_t)(GTQ_VBLOCK - 1);
+  const int64_t n_tiles = (pos0 + n_tok - s_begin + kAppTile - 1) / kAppTile;
+  // about four workgroups per compute unit, each over several tiles
+  const int64_t per_head = std::max<int64_t>(1, 1024 / (2 * (int64_t)p->n_kv));
+  const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(n_tiles, per_head));
+  hipLaunchKernelGGL(append_gemm_kernel, dim3(gx, p->n_kv, 2), dim3(kAppThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq append: launch");
   return ok();
 }
@@ -1515,7 +1557,9 @@ gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out) {
     }
     const size_t hb = p->heads.size() * sizeof(DevHead);
     const size_t rb = p->rot.size() * sizeof(float);
+    const size_t sb = p->rsplit.size() * sizeof(uint16_t);
     if ((e = hipMalloc(&p->d_heads, hb)) != hipSuccess || (e = hipMalloc(&p->d_rot, rb)) != hipSuccess ||
+        (e = hipMalloc(&p->d_rsplit, sb)) != hipSuccess ||
         (e = hipMalloc(&p->d_cb, sizeof(DevCodebook))) != hipSuccess ||
         (e = hipMalloc(&p->d_overflow, sizeof(unsigned long long))) != hipSuccess) {
       gtq_plan_destroy(p);
@@ -1523,6 +1567,7 @@ gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out) {
     }
     if ((e = hipMemcpy(p->d_heads, p->heads.data(), hb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(p->d_rot, p->rot.data(), rb, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(p->d_rsplit, p->rsplit.data(), sb, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(p->d_cb, &p->cb, sizeof(DevCodebook), hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemset(p->d_overflow, 0, sizeof(unsigned long long))) != hipSuccess) {
       gtq_plan_destroy(p);
@@ -1535,10 +1580,11 @@ gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out) {
 
 gtq_status gtq_plan_destroy(gtq_plan* p) {
   if (!p) return ok();
-  if (p->d_heads || p->d_rot || p->d_cb || p->d_overflow) {
+  if (p->d_heads || p->d_rot || p->d_rsplit || p->d_cb || p->d_overflow) {
     (void)hipDeviceSynchronize();
     (void)hipFree(p->d_heads);
     (void)hipFree(p->d_rot);
+    (void)hipFree(p->d_rsplit);
     (void)hipFree(p->d_cb);
     (void)hipFree(p->d_overflow);
   }

@@ -17,6 +17,7 @@ constexpr int kMaxKB = 8;             // sum_g ceil(d_g / 32) <= 4 + 128/32
 constexpr int kKP = kKB * kMaxKB;     // padded query length (halves)
 constexpr int kBlk = 32;              // tokens per decode block
 constexpr int kNS = GTQ_KNORM_STRIDE;
+constexpr float kRotSplitScale = 16.f;  // the split rotations hold 16 * Pi (lo parts stay normal)
 
 // Per (layer, KV head) tables, uploaded once per plan (plain data, same layout on
 // host and device).
@@ -34,6 +35,9 @@ struct DevHead {
   int64_t krot_off[kMaxGroups];   // float offset of Pi_g (row-major d x d) in the pool
   int64_t vrot_off;               // float offset of Pi_V (row-major 128 x 128)
   int64_t vrot_t_off;             // float offset of Pi_V^T (row-major, i.e. Pi_V column-major)
+  int64_t rsk_off[kMaxGroups];   // split K rotations of group g: binary16 hi then lo blocks of
+                                  // ceil16(d) rows x ceil32(d) columns (zero padded)
+  int64_t rsv_off;                // split V rotation: hi then lo, 128 x 128
   int32_t krot_floats;            // sum_g d_g^2
   int32_t pad_;
   uint8_t coord[kD];              // record position -> head coordinate
@@ -57,11 +61,13 @@ struct gtq_plan {
   std::vector<gtq::DevHead> heads;      // [L][H_kv]
   std::vector<gtq_head_layout> layouts; // [L][H_kv]
   std::vector<float> rot;               // rotation pool
+  std::vector<uint16_t> rsplit;         // rotations as binary16 (hi, lo) pairs, for the append GEMM
   gtq::DevCodebook cb{};
   // device copies (null for host-only plans)
   int device = -1;
   gtq::DevHead* d_heads = nullptr;
   float* d_rot = nullptr;
+  uint16_t* d_rsplit = nullptr;
   gtq::DevCodebook* d_cb = nullptr;
   unsigned long long* d_overflow = nullptr;
 };
