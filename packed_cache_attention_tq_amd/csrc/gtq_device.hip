@@ -146,26 +146,23 @@ __device__ inline double wave_sum_f64(double v) {
 
 constexpr int kAppWaves = 8;
 constexpr int kAppThreads = 64 * kAppWaves;
-constexpr int kAppTile = 16;          // tokens per tile (MFMA rows)
+constexpr int kAppTile = 32;          // tokens per tile (two MFMA row tiles)
 constexpr int kAppPitch = 264;        // halves per A row (256 padded inputs + 8: no bank conflicts)
 
 struct AppendGemmShared {
-  float x[kAppTile][kD + 4];          // staged inputs (keys in record order)
   _Float16 ua[2][kAppTile][kAppPitch];  // U_hi, U_lo in the padded input order
-  uint8_t code[kAppTile][kD];         // codes by record position (keys) or coordinate (values)
+  uint32_t pk[kAppTile][16];          // packed key records of the tile
+  uint32_t pv[4][128];                // packed value blocks of the tile (8 tokens each)
   float nu[kAppTile][5];              // fp32 norms per token: key groups 0..3, value 4
   float thr[5][16];                   // quantizer thresholds by rate
-  double inv[kAppTile][5];            // 1 / nu
 };
 
-// fp64 sum over the 32 lanes l & ~31 .. l | 31 (one token): DPP inside each 16-lane row,
-// then the row swap
-__device__ inline double half_wave_sum_f64(double v) {
+// fp64 sum over the 16 lanes of a row (one token): DPP row operations
+__device__ inline double row_sum_f64(double v) {
   v += dpp_f64(v, 0);
   v += dpp_f64(v, 1);
   v += dpp_f64(v, 2);
   v += dpp_f64(v, 3);
-  v += swap_f64(v, false);
   return v;
 }
 
@@ -181,7 +178,7 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
 
   // ---- this wave's output tiles: values: outputs 16 wave .. +15 over 4 input steps;
   //      keys: tiles numbered over the groups (16 outputs each), wave w takes w, w + 8
-  int tg[2] = {-1, -1}, ti0[2] = {0, 0}, tsteps[2] = {0, 0}, trate[2] = {0, 0};
+  int tg[2] = {-1, -1}, ti0[2] = {0, 0}, tsteps[2] = {0, 0}, trate[2] = {1, 1};
   if (vrole) {
     tg[0] = 4;
     ti0[0] = 16 * wave;
@@ -212,10 +209,10 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bh[j][s] = make_uint4(0, 0, 0, 0);
-      bl[j][s] = make_uint4(0, 0, 0, 0);
-      if (tg[j] >= 0 && s < tsteps[j]) {
+    for (int st = 0; st < 4; ++st) {
+      bh[j][st] = make_uint4(0, 0, 0, 0);
+      bl[j][st] = make_uint4(0, 0, 0, 0);
+      if (tg[j] >= 0 && st < tsteps[j]) {
         int rows, cols;
         int64_t off;
         if (tg[j] == 4) {
@@ -228,9 +225,9 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
           cols = (d + 31) >> 5 << 5;
           off = hp->rsk_off[tg[j]];
         }
-        const uint16_t* base = a.rsplit + off + (size_t)(ti0[j] + n) * cols + 32 * s + 8 * q;
-        bh[j][s] = *reinterpret_cast<const uint4*>(base);
-        bl[j][s] = *reinterpret_cast<const uint4*>(base + (size_t)rows * cols);
+        const uint16_t* base = a.rsplit + off + (size_t)(ti0[j] + n) * cols + 32 * st + 8 * q;
+        bh[j][st] = *reinterpret_cast<const uint4*>(base);
+        bl[j][st] = *reinterpret_cast<const uint4*>(base + (size_t)rows * cols);
       }
     }
   }
@@ -239,16 +236,17 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
   for (int e = tid; e < 2 * kAppTile * kAppPitch / 8; e += kAppThreads)
     reinterpret_cast<uint4*>(&S.ua[0][0][0])[e] = make_uint4(0, 0, 0, 0);
 
-  // ---- this thread's 4 staged elements: token tau = tid >> 5, columns c = (tid & 31) + 32 i
-  const int tau = tid >> 5, sub = tid & 31;
-  int src_col[4], kp_col[4], grp_of[4];
+  // ---- this thread's 8 inputs of a tile: token tau = tid >> 4 (one 16-lane row per
+  //      token), columns c = (tid & 15) + 16 i
+  const int tau = tid >> 4, sub = tid & 15;
+  int src_col[8], kp_col[8], grp_of[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = sub + 32 * i;  // record position (keys) or coordinate (values)
+  for (int i = 0; i < 8; ++i) {
+    const int c = sub + 16 * i;  // record position (keys) or coordinate (values)
     if (vrole) {
       src_col[i] = c;
       kp_col[i] = c;
-      grp_of[i] = 4;
+      grp_of[i] = 0;
     } else {
       int g = 0;
 #pragma unroll
@@ -264,112 +262,117 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
   const int64_t n_tiles = (s_end - s_begin + kAppTile - 1) / kAppTile;
   const size_t sh = (size_t)a.seq * a.n_kv + h;
   const int kw = a.k_words, vb = a.v_bits;
+  auto load_tile = [&](int64_t tile, float (&xr)[8]) {  // zeros outside the chunk
+    const int64_t s = s_begin + tile * kAppTile + tau;
+    const bool ok = tile < n_tiles && s >= a.pos0 && s < s_end;
+    const size_t row = ok ? ((size_t)(s - a.pos0) * a.n_kv + h) * kD : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xr[i] = ok ? src[row + src_col[i]] : 0.f;
+  };
+  float xr[8];
+  load_tile(blockIdx.x, xr);
 
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     const int64_t ts = s_begin + tile * kAppTile;
-    // ---- stage (zeros for slots outside the chunk)
-    {
-      const int64_t s = ts + tau;
-      const bool ok = s >= a.pos0 && s < s_end;
-      const size_t row = ((size_t)(s - a.pos0) * a.n_kv + h) * kD;
+    float x[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S.x[tau][sub + 32 * i] = ok ? src[row + src_col[i]] : 0.f;
+    for (int i = 0; i < 8; ++i) x[i] = xr[i];
+    load_tile(tile + gridDim.x, xr);  // next tile, in flight during this one
+    __syncthreads();                  // the previous tile's stores have read the buffers
+    if (tid < kAppTile * 16) (&S.pk[0][0])[tid] = 0u;
+    (&S.pv[0][0])[tid] = 0u;          // 4 x 128 == kAppThreads
+    // ---- norms (fp64, per token and group; every lane of the row gets all sums), then
+    //      u = x / nu split as 256 u = U_hi + U_lo
+    double sg[kMaxGroups] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double xv = x[i];
+#pragma unroll
+      for (int gg = 0; gg < kMaxGroups; ++gg) sg[gg] += (grp_of[i] == gg) ? xv * xv : 0.0;
     }
-    __syncthreads();
-    // ---- norms (fp64): 4 key groups or the value, per token
-    {
-      double sg[kMaxGroups] = {0.0, 0.0, 0.0, 0.0};
+    const int ng = vrole ? 1 : n_groups;
+    double inv[kMaxGroups];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double xv = S.x[tau][sub + 32 * i];
-        const int g = vrole ? 0 : grp_of[i];
-#pragma unroll
-        for (int gg = 0; gg < kMaxGroups; ++gg) sg[gg] += (g == gg) ? xv * xv : 0.0;
-      }
-      const int ng = vrole ? 1 : kMaxGroups;
-#pragma unroll
-      for (int gg = 0; gg < kMaxGroups; ++gg)
-        if (gg < ng) sg[gg] = half_wave_sum_f64(sg[gg]);
-      const int nv = vrole ? 1 : n_groups;
-      if (sub < nv) {
-        double v = sg[0];
-#pragma unroll
-        for (int gg = 1; gg < kMaxGroups; ++gg) v = (sub == gg) ? sg[gg] : v;
-        const double nu = sqrt(v);
-        const int slot = vrole ? 4 : sub;
-        S.nu[tau][slot] = (float)nu;
-        S.inv[tau][slot] = nu > 0.0 ? 1.0 / nu : 0.0;
+    for (int gg = 0; gg < kMaxGroups; ++gg) {
+      inv[gg] = 0.0;
+      if (gg < ng) {
+        const double nu = sqrt(row_sum_f64(sg[gg]));
+        inv[gg] = nu > 0.0 ? 1.0 / nu : 0.0;
+        if (sub == gg) S.nu[tau][vrole ? 4 : gg] = (float)nu;
       }
     }
-    __syncthreads();
-    // ---- split u = x / nu: 256 u = U_hi + U_lo
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = vrole ? 4 : grp_of[i];
-      const float u = (float)((double)S.x[tau][sub + 32 * i] * S.inv[tau][slot]) * 256.f;
+    for (int i = 0; i < 8; ++i) {
+      double iv = inv[0];
+#pragma unroll
+      for (int gg = 1; gg < kMaxGroups; ++gg) iv = (grp_of[i] == gg) ? inv[gg] : iv;
+      const float u = (float)((double)x[i] * iv) * 256.f;
       const _Float16 hi = (_Float16)u;
       S.ua[0][tau][kp_col[i]] = hi;
       S.ua[1][tau][kp_col[i]] = (_Float16)(u - (float)hi);
     }
     __syncthreads();
-    // ---- products and codes of this wave's tiles
+    // ---- products, codes and packing of this wave's tiles (both 16-token halves)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (tg[j] >= 0) {
         const int g = tg[j];
         const int kb0 = (g == 4) ? 0 : hp->kp_off[g];
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s < tsteps[j]) {
-            H8 ah, al, ph, pl;
-            ah.v = *reinterpret_cast<const uint4*>(&S.ua[0][n][kb0 + 32 * s + 8 * q]);
-            al.v = *reinterpret_cast<const uint4*>(&S.ua[1][n][kb0 + 32 * s + 8 * q]);
-            ph.v = bh[j][s];
-            pl.v = bl[j][s];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, ph.h, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al.h, ph.h, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, pl.h, acc, 0, 0, 0);
+        for (int st = 0; st < 4; ++st) {
+          if (st < tsteps[j]) {
+            H8 ph, pl;
+            ph.v = bh[j][st];
+            pl.v = bl[j][st];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              H8 ah, al;
+              ah.v = *reinterpret_cast<const uint4*>(&S.ua[0][16 * hf + n][kb0 + 32 * st + 8 * q]);
+              al.v = *reinterpret_cast<const uint4*>(&S.ua[1][16 * hf + n][kb0 + 32 * st + 8 * q]);
+              acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, ph.h, acc[hf], 0, 0, 0);
+              acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al.h, ph.h, acc[hf], 0, 0, 0);
+              acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, pl.h, acc[hf], 0, 0, 0);
+            }
           }
         }
-        // lane (q, n) holds D[token 4q + e][output i0 + n]
+        // lane (q, n) holds D[token 16 hf + 4q + e][output i0 + n]
         const int d = (g == 4) ? kD : hp->dim[g];
         const int i = ti0[j] + n;
         if (i < d) {
           const float zs = sqrtf((float)d) * (1.f / (kRotSplitScale * 256.f));
-          const int nthr = (1 << trate[j]) - 1;
-          const float* th = S.thr[trate[j]];
-          const int pos = (g == 4) ? i : hp->pos_off[g] + i;
+          const int r = trate[j];
+          const float* th = S.thr[r];
+          const int kbit = (g == 4) ? 0 : hp->bit_off[g] + i * r;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float z = acc[e] * zs;
-            int c = 0;
-            for (int k = 0; k < nthr; ++k) c += (z >= th[k]) ? 1 : 0;
-            S.code[4 * q + e][pos] = (uint8_t)c;
+          for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float z = acc[hf][e] * zs;
+              // code = #{k : z >= t_k} by binary search over the sorted thresholds
+              int cd = 0;
+              for (int step = 1 << (r - 1); step > 0; step >>= 1)
+                if (z >= th[cd + step - 1]) cd += step;
+              const int t = 16 * hf + 4 * q + e;
+              // values: token t & 7 of block t >> 3, coordinate i at bit 8 vb i + vb j;
+              // keys: the record bit of position i of the group
+              const int bit = (g == 4) ? 8 * r * i + r * (t & 7) : kbit;
+              uint32_t* dst = (g == 4) ? &S.pv[t >> 3][0] : &S.pk[t][0];
+              const uint64_t f = (uint64_t)cd << (bit & 31);
+              atomicOr(dst + (bit >> 5), (uint32_t)f);
+              if (f >> 32) atomicOr(dst + (bit >> 5) + 1, (uint32_t)(f >> 32));
+            }
           }
         }
       }
     }
     __syncthreads();
-    // ---- pack and store
+    // ---- store
     if (!vrole) {
-      // key record word w of token t: the codes whose bits meet [32 w, 32 w + 32)
       for (int e = tid; e < kAppTile * kw; e += kAppThreads) {
         const int t = e / kw, w = e - t * kw;
         const int64_t s = ts + t;
-        if (s < a.pos0 || s >= s_end) continue;
-        uint32_t word = 0;
-        for (int g = 0; g < n_groups; ++g) {
-          const int r = hp->rate[g], b0 = hp->bit_off[g], d = hp->dim[g], po = hp->pos_off[g];
-          const int lo = max(0, (32 * w - b0) / r - 1), hi = min(d, (32 * w + 32 - b0 + r - 1) / r);
-          for (int i = lo; i < hi; ++i) {
-            const int bit = b0 + i * r - 32 * w;
-            const uint32_t c = S.code[t][po + i];
-            if (bit >= 0 && bit < 32) word |= c << bit;
-            else if (bit < 0 && bit > -r) word |= c >> (-bit);
-          }
-        }
-        a.k_codes[(sh * a.capacity + s) * kw + w] = word;
+        if (s >= a.pos0 && s < s_end) a.k_codes[(sh * a.capacity + s) * kw + w] = S.pk[t][w];
       }
       if (tid < kAppTile * kNS) {
         const int t = tid / kNS, g = tid - kNS * t;
@@ -377,38 +380,31 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
         if (s >= a.pos0 && s < s_end) a.k_norms[(sh * a.capacity + s) * kNS + g] = g < n_groups ? S.nu[t][g] : 0.f;
       }
     } else {
-      // value block b (tokens 8b..8b+7 of the tile), word w: token j of coordinate c at
-      // bit 8 vb c + vb j
       const int vw = 32 * vb;
-      for (int e = tid; e < 2 * vw; e += kAppThreads) {
+      for (int e = tid; e < 4 * vw; e += kAppThreads) {
         const int b = e / vw, w = e - b * vw;
         const int64_t sb = ts + 8 * b;
         if (sb + 8 <= a.pos0 || sb >= s_end) continue;  // no token of this block in the chunk
-        uint32_t word = 0, mask = 0;
-        const int c_lo = (32 * w) / (8 * vb), c_hi = min(kD - 1, (32 * w + 31) / (8 * vb));
-        for (int c = c_lo; c <= c_hi; ++c) {
-          for (int jt = 0; jt < 8; ++jt) {
-            const int bit = 8 * vb * c + vb * jt - 32 * w;
-            if (bit <= -vb || bit >= 32) continue;
-            const int64_t s = sb + jt;
-            if (s < a.pos0 || s >= s_end) continue;
-            const uint32_t cv = S.code[8 * b + jt][c];
-            const uint32_t m = (1u << vb) - 1u;
-            if (bit >= 0) {
-              word |= cv << bit;
-              mask |= m << bit;
-            } else {
-              word |= cv >> (-bit);
-              mask |= m >> (-bit);
-            }
-          }
-        }
         uint32_t* blk = a.v_codes + (sh * (size_t)(a.capacity / GTQ_VBLOCK) + (size_t)(sb / GTQ_VBLOCK)) * vw;
         if (sb >= a.pos0 && sb + 8 <= s_end) {
-          blk[w] = word;
-        } else if (mask) {
-          atomicAnd(blk + w, ~mask);
-          atomicOr(blk + w, word);
+          blk[w] = S.pv[b][w];
+        } else {
+          // bits of the block's tokens inside the chunk only
+          uint32_t mask = 0;
+          for (int jt = 0; jt < 8; ++jt) {
+            if (sb + jt < a.pos0 || sb + jt >= s_end) continue;
+            const int c_lo = (32 * w) / (8 * vb), c_hi = min(kD - 1, (32 * w + 31) / (8 * vb));
+            for (int cc = c_lo; cc <= c_hi; ++cc) {
+              const int bit = 8 * vb * cc + vb * jt - 32 * w;
+              const uint32_t m = (1u << vb) - 1u;
+              if (bit >= 0 && bit < 32) mask |= m << bit;
+              else if (bit < 0 && bit > -vb) mask |= m >> (-bit);
+            }
+          }
+          if (mask) {
+            atomicAnd(blk + w, ~mask);
+            atomicOr(blk + w, S.pv[b][w] & mask);
+          }
         }
       }
       if (tid < kAppTile) {
