@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--chunk", type=int, default=0, help="split size (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--workload", default="decode-8b",
+                   choices=["decode-8b", "decode-3b-36L", "decode-70b-b32", "append-32b", "prefill-32b"],
+                   help="decode-8b (default, the headline): Llama-3.1-8B-shaped layer decode; the others "
+                        "measure the other workload shapes (one JSON line each)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run a plain device copy (torch.neg) of this many MiB three "
                         "times: a kernel of known traffic that calibrates the HBM byte counters")
@@ -93,6 +97,238 @@ def build_workload(seed, n_ctx=32768, h_kv=8, g=4, k_budget=128, v_bits=2):
     q = np.concatenate([i["q"][0] for i in inps])[None]   # [1, 32, 128]
     return dict(plan=plan, k=k, v=v, q=q, rates=rates, krot=krot, vrot=vrot, inps=inps,
                 n_ctx=n_ctx, h_kv=h_kv, g=g, k_budget=k_budget, v_bits=v_bits)
+
+
+def make_plan(seed, n_layers, h_kv, g, k_budget, v_bits, share_layer0=False):
+    """A plan with library-allocated rates (from each head's calibration set) and Haar
+    rotations; with share_layer0 every layer reuses layer 0's rates and rotations."""
+    import packed_cache_attention_tq_amd as G
+    from gtq_inputs import head_inputs, head_rotations
+
+    rates = np.zeros((n_layers, h_kv, 64), np.uint8)
+    krot, vrot = [], []
+    for l in range(n_layers):
+        if share_layer0 and l > 0:
+            rates[l] = rates[0]
+            krot.append(krot[0])
+            vrot.append(vrot[0])
+            continue
+        kl, vl = [], []
+        for h in range(h_kv):
+            inp = head_inputs(seed, l, h, g, 0)
+            r, _, _ = G.gtq_alloc_rates(inp["calib_q"], inp["calib_k"], 1, 4, k_budget)
+            rates[l, h] = r
+            kr, vr = head_rotations(seed, l, h, G.gtq_head_layout_from_rates(r)["dim"])
+            kl.append(kr)
+            vl.append(vr)
+        krot.append(kl)
+        vrot.append(vl)
+    return G.Plan(n_layers, h_kv, h_kv * g, k_budget, v_bits, rates, krot, np.array(vrot))
+
+
+def fill_layer(plan, layer, cache, seed, h_kv, g, lengths, gen_layer=None):
+    """Append seeded synthetic keys/values of every sequence (token n - 1 excluded: the
+    step appends it) and return the step's new tokens and queries."""
+    import torch
+
+    import packed_cache_attention_tq_amd as G
+    from gtq_inputs import head_inputs_device
+
+    dev = torch.device("cuda")
+    gl = layer if gen_layer is None else gen_layer
+    B = len(lengths)
+    knew = torch.zeros(B, h_kv, 128, device=dev)
+    vnew = torch.zeros(B, h_kv, 128, device=dev)
+    q = torch.zeros(B, h_kv * g, 128, device=dev)
+    for b, n in enumerate(lengths):
+        ks, vs = [], []
+        for h in range(h_kv):
+            d = head_inputs_device(seed, gl, h, g, int(n), dev, seq=b)
+            ks.append(d["k"])
+            vs.append(d["v"])
+            q[b, h * g:(h + 1) * g] = d["q"][0]
+        k = torch.stack(ks, 1)
+        v = torch.stack(vs, 1)
+        if n > 1:
+            G.gtq_quantize_append_chunk(plan, layer, cache, k[: n - 1].contiguous(), v[: n - 1].contiguous(), b, 0)
+        knew[b], vnew[b] = k[n - 1], v[n - 1]
+        del ks, vs, k, v
+    return knew, vnew, q
+
+
+def timed_graph(fn, steps, warmup):
+    """Capture fn (one step of kernel launches on the current stream) in a HIP graph,
+    replay it warmup + steps times; returns ms per step."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager run before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def bench_decode_stack(args, name):
+    """Multi-layer decode steps as one HIP graph per step: decode-3b-36L (Qwen2.5-3B shape:
+    36 layers, 16 query / 2 KV heads, batch 1, 131072 tokens, K3V3) or decode-70b-b32
+    (Llama-3-70B shape: 80 layers, 64 query / 8 KV heads, batch 32 with ragged lengths
+    uniform in [8192, 16384], K2V2; the 80 layer caches hold copies of one generated layer
+    and every layer uses that layer's rates and rotations)."""
+    import torch
+
+    import packed_cache_attention_tq_amd as G
+    from gtq_inputs import ragged_lengths
+
+    if name == "decode-3b-36L":
+        L, h_kv, g, kb, vb, lengths, share = 36, 2, 8, 192, 3, np.array([131072]), False
+    else:
+        L, h_kv, g, kb, vb, share = 80, 8, 8, 128, 2, True
+        lengths = ragged_lengths(args.seed, 32, 8192, 16384)
+    B, cap = len(lengths), int((lengths.max() + 31) // 32 * 32)
+    t_setup = time.perf_counter()
+    plan = make_plan(args.seed, L, h_kv, g, kb, vb, share_layer0=share)
+    caches, steps_in = [], []
+    for l in range(L):
+        if share and l > 0:
+            caches.append(caches[0].clone())
+            steps_in.append(steps_in[0])
+            continue
+        c = G.PackedCache(plan, B, cap)
+        steps_in.append(fill_layer(plan, l, c, args.seed, h_kv, g, lengths))
+        caches.append(c)
+    torch.cuda.synchronize()
+    sl = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    max_len = int(lengths.max())
+    ws = [torch.empty(G.gtq_decode_workspace_bytes(plan, B, max_len, 0), dtype=torch.uint8, device="cuda")
+          for _ in range(2)]
+    outs = [torch.empty(B, h_kv * g, 128, device="cuda") for _ in range(L)]
+    scale = 1.0 / math.sqrt(128)
+    log(f"{name}: setup {time.perf_counter() - t_setup:.1f}s, {L} layers, cache "
+        f"{sum(c.nbytes() for c in caches) / 1e9:.2f} GB")
+
+    def step():
+        for l in range(L):
+            kn, vn, q = steps_in[l]
+            G.gtq_decode_step(plan, l, caches[l], kn, vn, q, sl, max_len, scale,
+                              out=outs[l], workspace=ws[l & 1])
+
+    ms = timed_graph(step, args.steps, args.warmup)
+    kv_tok = L * int(lengths.sum())
+    sizes = caches[0].sizes
+    alg = L * (int(lengths.sum()) * h_kv * sizes.bytes_per_token)
+    return {
+        "metric": "packed-KV decode attention: KV tokens/s + achieved HBM GB/s (% of peak)",
+        "value": round(kv_tok / (ms / 1e3), 1), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (fp16 hi/lo split MFMA operands, fp32 accumulation; u32 packed codes)",
+        "data": "synthetic",
+        "config": {"workload": name, "layers": L, "global_batch": B, "kv_heads": h_kv, "q_heads": h_kv * g,
+                   "seq_len": [int(lengths.min()), int(lengths.max())], "k_bits_avg": kb / 64, "v_bits": vb,
+                   "graph": "one HIP graph per step (append + rotate, partials, merge per layer)"},
+        "step_hbm_gbs": round(alg / (ms / 1e3) / 1e9, 1), "step_hbm_frac": round(alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+
+def bench_append(args):
+    """append-32b: Qwen2.5-32B-shaped chunk append, 4096-token chunks x 8 KV heads, K3V2,
+    the 16 chunks of a 65536-token prompt in turn (one call = one chunk-layer)."""
+    import torch
+
+    import packed_cache_attention_tq_amd as G
+    from gtq_inputs import head_inputs_device
+
+    h_kv, g, kb, vb, chunk, total = 8, 5, 192, 2, 4096, 65536
+    plan = make_plan(args.seed, 1, h_kv, g, kb, vb)
+    cache = G.PackedCache(plan, 1, total)
+    ks = torch.stack([head_inputs_device(args.seed, 0, h, g, total, "cuda", with_q=False)["k"] for h in range(h_kv)], 1)
+    vs = torch.stack([head_inputs_device(args.seed, 0, h, g, total, "cuda", with_q=False)["v"] for h in range(h_kv)], 1)
+    chunks = [(ks[m * chunk:(m + 1) * chunk].contiguous(), vs[m * chunk:(m + 1) * chunk].contiguous())
+              for m in range(total // chunk)]
+    for m, (k, v) in enumerate(chunks):
+        G.gtq_quantize_append_chunk(plan, 0, cache, k, v, 0, m * chunk)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_steps = max(args.steps, 16)
+    t0.record()
+    for i in range(n_steps):
+        m = i % len(chunks)
+        G.gtq_quantize_append_chunk(plan, 0, cache, chunks[m][0], chunks[m][1], 0, m * chunk)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n_steps
+    per_tok = 2 * 128 * 4 + cache.sizes.bytes_per_token  # fp32 key + value in, packed record out
+    alg = chunk * h_kv * per_tok
+    return {
+        "metric": "fused rotate+quantize+pack append: tokens/s + achieved HBM GB/s (% of peak)",
+        "value": round(chunk / (ms / 1e3), 1), "unit": "tokens/s (x 8 KV heads)", "n_gpus": 1, "steps": n_steps,
+        "warmup": 16, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 in; binary16 hi/lo split MFMA; u32 packed codes", "data": "synthetic",
+        "config": {"workload": "append-32b", "chunk_tokens": chunk, "kv_heads": h_kv, "k_bits_avg": kb / 64,
+                   "v_bits": vb, "prompt": total},
+        "roofline": {"bound": "hbm", "achieved": round(alg / (ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "append_gemm_kernel", "alg_bytes_per_launch": int(alg)},
+    }
+
+
+def bench_prefill(args):
+    """prefill-32b: causal chunked-prefill attention of the last 4096-token chunk of a
+    65536-token prompt (Qwen2.5-32B shape: 40 query / 8 KV heads, K3V2) over the packed
+    cache; reported as TFLOP/s of the attention products (2 x 2 x 128 flop per visible
+    (query, key) pair and head)."""
+    import torch
+
+    import packed_cache_attention_tq_amd as G
+    from gtq_inputs import head_inputs_device
+
+    h_kv, g, kb, vb, chunk, total = 8, 5, 192, 2, 4096, 65536
+    pos0 = total - chunk
+    plan = make_plan(args.seed, 1, h_kv, g, kb, vb)
+    cache = G.PackedCache(plan, 1, total)
+    qpos = torch.arange(pos0, total, device="cuda")
+    ds = [head_inputs_device(args.seed, 0, h, g, total, "cuda", n_q_tok=chunk, q_positions=qpos) for h in range(h_kv)]
+    k = torch.stack([d["k"] for d in ds], 1)
+    v = torch.stack([d["v"] for d in ds], 1)
+    G.gtq_quantize_append_chunk(plan, 0, cache, k.contiguous(), v.contiguous(), 0, 0)
+    q = torch.cat([d["q"] for d in ds], 1).contiguous()  # [chunk, 40, 128]
+    del ds, k, v
+    ws = torch.empty(G.gtq_prefill_workspace_bytes(plan, pos0, chunk), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(128)
+    G.gtq_prefill_attn(plan, 0, cache, q, 0, pos0, scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_steps = max(1, min(args.steps, 5))
+    t0.record()
+    for _ in range(n_steps):
+        G.gtq_prefill_attn(plan, 0, cache, q, 0, pos0, scale, out=out, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n_steps
+    pairs = sum(pos0 + t + 1 for t in range(chunk)) * h_kv * g
+    flop = 4.0 * 128 * pairs
+    return {
+        "metric": "chunked prefill attention over the packed cache: TFLOP/s",
+        "value": round(flop / (ms / 1e3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": 1, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (fp16 hi/lo split MFMA operands, fp32 accumulation)", "data": "synthetic",
+        "config": {"workload": "prefill-32b", "chunk": chunk, "pos0": pos0, "q_heads": h_kv * g, "kv_heads": h_kv,
+                   "k_bits_avg": kb / 64, "v_bits": vb},
+    }
 
 
 def cpu_baseline(w, seed, min_seconds=10.0):
@@ -145,6 +381,12 @@ def main():
         raise SystemExit("bench.py needs a HIP device")
     G.lib()
     torch.cuda.set_device(0)
+    if args.workload != "decode-8b":
+        fn = {"decode-3b-36L": lambda: bench_decode_stack(args, "decode-3b-36L"),
+              "decode-70b-b32": lambda: bench_decode_stack(args, "decode-70b-b32"),
+              "append-32b": lambda: bench_append(args), "prefill-32b": lambda: bench_prefill(args)}[args.workload]
+        print(json.dumps(fn()), flush=True)
+        return
     t_setup = time.perf_counter()
     w = build_workload(args.seed)
     plan, n, h_kv, g = w["plan"], w["n_ctx"], w["h_kv"], w["g"]

@@ -125,6 +125,57 @@ def head_inputs(cfg_seed: int, layer: int, kv_head: int, g: int, n_cache: int,
                 k_pre=k_pre)
 
 
+def head_inputs_device(cfg_seed: int, layer: int, kv_head: int, g: int, n_cache: int, device,
+                       seq: int = 0, pos0: int = 0, n_q_tok: int = 1, q_positions=None, layout: int = HALF,
+                       with_q: bool = True) -> dict:
+    """The same recipe as head_inputs for large workloads, drawn on `device` with torch
+    generators seeded from the same (cfg_seed, layer, kv_head, stream) tuples (so the
+    numbers differ from head_inputs'): cache keys (post-RoPE, positions pos0 ..
+    pos0 + n_cache - 1), values, and n_q_tok x g queries (post-RoPE at q_positions,
+    default: position pos0 + n_cache). The calibration set is the small numpy one of
+    head_inputs (n_cache = 0)."""
+    import torch
+
+    D = HEAD_DIM
+    small = head_inputs(cfg_seed, layer, kv_head, g, 0, layout=layout)
+    sc = torch.tensor(coord_std(small["sigma"], layout), dtype=torch.float32, device=device)
+    so = 16 * seq
+
+    def gen(stream):
+        gg = torch.Generator(device=device)
+        gg.manual_seed(seed_int(cfg_seed, layer, kv_head, stream + so))
+        return gg
+
+    def rope(x, pos):
+        j = D // 2
+        theta = ROPE_BASE ** (-2.0 * torch.arange(j, dtype=torch.float64, device=device) / D)
+        ang = pos.to(torch.float64)[:, None] * theta[None, :]
+        c, sn = torch.cos(ang), torch.sin(ang)
+        xd = x.to(torch.float64)
+        if layout == HALF:
+            a, b = xd[..., :j], xd[..., j:]
+        else:
+            a, b = xd[..., 0::2], xd[..., 1::2]
+        out = torch.empty_like(xd)
+        if layout == HALF:
+            out[..., :j], out[..., j:] = a * c - b * sn, a * sn + b * c
+        else:
+            out[..., 0::2], out[..., 1::2] = a * c - b * sn, a * sn + b * c
+        return out.to(torch.float32)
+
+    pos = torch.arange(pos0, pos0 + n_cache, device=device)
+    k = rope(torch.randn(n_cache, D, generator=gen(S_CACHE_K), device=device) * sc, pos)
+    v = torch.randn(n_cache, D, generator=gen(S_CACHE_V), device=device)
+    out = dict(k=k, v=v, calib_q=small["calib_q"], calib_k=small["calib_k"], sigma=small["sigma"])
+    if with_q:
+        qp = torch.randn(n_q_tok, g, D, generator=gen(S_DEC_Q), device=device) * sc
+        if q_positions is None:
+            q_positions = torch.full((n_q_tok,), pos0 + n_cache, device=device)
+        qpos = torch.as_tensor(q_positions, device=device).repeat_interleave(g)
+        out["q"] = rope(qp.reshape(n_q_tok * g, D), qpos).reshape(n_q_tok, g, D)
+    return out
+
+
 def head_rotations(cfg_seed: int, layer: int, kv_head: int, group_dims: list[int]) -> tuple[list[np.ndarray], np.ndarray]:
     """Haar rotations for the K groups (in the order given) and the V rotation."""
     rng = rng_for(cfg_seed, layer, kv_head, S_ROT)
