@@ -99,6 +99,15 @@ def build_workload(seed, n_ctx=32768, h_kv=8, g=4, k_budget=128, v_bits=2):
                 n_ctx=n_ctx, h_kv=h_kv, g=g, k_budget=k_budget, v_bits=v_bits)
 
 
+def partials_kernel_name(plan, layer, h_kv, v_bits):
+    """The partials kernel instance a decode of this layer launches: value bits, key words
+    per lane (4 up to 8 key words, else 8) and the layer's largest K-block count."""
+    lays = [plan.layout(layer, h) for h in range(h_kv)]
+    nkb = max(sum((d + 31) // 32 for d in lay["dim"]) for lay in lays)
+    kwl = 4 if lays[0]["k_words"] <= 8 else 8
+    return f"attn_partials_kernel<{v_bits}, {kwl}, {nkb}>"
+
+
 def make_plan(seed, n_layers, h_kv, g, k_budget, v_bits, share_layer0=False):
     """A plan with library-allocated rates (from each head's calibration set) and Haar
     rotations; with share_layer0 every layer reuses layer 0's rates and rotations."""
@@ -471,7 +480,8 @@ def main():
                    "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "attn_partials_kernel<2, 4>", "kernel_avg_us": round(kern_avg * 1e3, 3),
+                     "kernel": partials_kernel_name(plan, 0, h_kv, w["v_bits"]),
+                     "kernel_avg_us": round(kern_avg * 1e3, 3),
                      "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
                      "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
                      "alg_bytes_per_launch": int(alg_bytes)},

@@ -163,7 +163,8 @@ gtq_status gtq_plan_overflow_count(const gtq_plan* plan, int64_t* out);
  *           [8*v_bits*c, 8*v_bits*(c+1)) and token j of the block the v_bits at
  *           8*v_bits*c + v_bits*j (little-endian u32 words)
  *   v_norms [batch][n_kv_heads][capacity]            fp32
- * capacity is a multiple of 32. */
+ * capacity is a multiple of 32 and at most 2^25 (calls on a larger cache return
+ * GTQ_EUNSUPPORTED). */
 typedef struct gtq_cache_view {
   uint32_t* k_codes;
   float* k_norms;

@@ -610,7 +610,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kPS = 132;           // partial record: m, l, 2 pad, acc[128] (16-byte aligned acc)
 constexpr int kMaxChunks = 256;    // splits per row
 constexpr int kQB = kMaxKB * 64;   // uint4 entries of a tile's QK B operand (8 KB)
-constexpr int kDepth = 2;          // blocks of a wave in flight
 constexpr int kTargetWG = 256;     // partials workgroups the automatic split aims at
 
 struct AttnArgs {
@@ -637,6 +636,7 @@ struct AttnArgs {
   int32_t chunk;           // tokens per split (multiple of 32)
   int32_t n_chunks;
   int32_t max_len;         // decode clamp
+  int32_t nkb_max;         // largest K-block count of the layer's heads
   float qscale;            // softmax scale * log2(e)
 };
 
@@ -845,10 +845,14 @@ __global__ void __launch_bounds__(1024) decode_prep_kernel(AppendArgs ap, AttnAr
 
 // ---------------------------------------------------------------- partials
 
+constexpr int kKPitch = 17;  // staged key record pitch in words (k_words <= 16): odd, so the
+                             // 16 A-rows of one read fall in distinct banks
+
 struct AttnWave {
-  uint32_t ktile[kBlk * 17];         // 32 key records at an odd pitch (kw + 1 words, kw <= 16)
+  uint32_t ktile[kBlk * kKPitch];    // 32 key records
   float knt[kMaxGroups][kBlk];       // group norms, group-major
   float vn[kBlk];
+  uint4 vcodes[2][64];               // value codes of the block, 2 v_bits words per lane
 };
 
 struct AttnShared {
@@ -876,26 +880,6 @@ __device__ inline half8 dequant8(const uint32_t* lut, uint32_t F) {
   return o.h;
 }
 
-// QK of the key group of rate R: its K-blocks (at most 4) into two accumulators
-// (tokens of A-rows n of the two 16-token halves)
-template <int R>
-__device__ inline void qk_rate(const AttnShared& S, const uint32_t* r0, const uint32_t* r1, int nk, int bit0,
-                               int kb0, int q, int n, floatx4& d0, floatx4& d1) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i < nk) {
-      const int bit = bit0 + R * (32 * i + 8 * q);
-      const int w = bit >> 5, sb = bit & 31;
-      const uint32_t f0 = __builtin_amdgcn_alignbit(r0[w + 1], r0[w], sb);
-      const uint32_t f1 = __builtin_amdgcn_alignbit(r1[w + 1], r1[w], sb);
-      H8 qv;
-      qv.v = S.qb[kb0 + i][q][n];
-      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<R>(S.lut, f0), qv.h, d0, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8<R>(S.lut, f1), qv.h, d1, 0, 0, 0);
-    }
-  }
-}
-
 template <int VB>
 __device__ inline uint32_t vfield(const uint32_t (&vw)[2 * VB], int t) {
   if (VB == 1) return (vw[t >> 2] >> (8 * (t & 3))) & 0xFFu;
@@ -919,42 +903,80 @@ struct BlockData {
   uint32_t vw[2 * VB];
 };
 
-// t0 is uniform, so every address is a scalar base plus a lane offset. Word lane + 64 i
-// exists when lane + 64 i < 32 kw.
+// Raw buffer views of one (sequence, KV head) slice of the cache: reads past the end
+// return zero, and every address is a scalar base plus a per-lane constant.
+struct SliceRsrc {
+  __amdgpu_buffer_rsrc_t kc, kn, vc, vn;
+};
+constexpr int kRawBufferWord3 = 0x00020000;  // untyped 32-bit buffer (gfx9 descriptor)
+constexpr int64_t kMaxCapacity = int64_t(1) << 25;  // tokens: 64 B a token per slice stays < 2 GiB
+
+// (the host keeps every slice under 2 GiB). The inputs are uniform; reading them from
+// the first lane keeps the descriptor in scalar registers.
+__device__ inline __amdgpu_buffer_rsrc_t slice_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* base = reinterpret_cast<void*>((uint64_t)hi << 32 | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRawBufferWord3);
+}
+
 template <int VB, int KWL>
-__device__ inline void load_block(BlockData<VB, KWL>& B, const uint32_t* kc, const float* knp, const uint32_t* vc,
-                                  const float* vnp, int t0, int kw, int lane, int q, int n) {
-  const uint32_t* ks = kc + (size_t)t0 * kw;
+__device__ inline void load_block(BlockData<VB, KWL>& B, const SliceRsrc& R, int t0, int kw, int lane, int voff_v) {
+  const int sk = t0 * kw * 4;
 #pragma unroll
-  for (int i = 0; i < KWL; ++i) {
-    if (2 * i + 1 < kw) B.kr[i] = ks[lane + 64 * i];
-    else if (2 * i < kw && lane < 32) B.kr[i] = ks[lane + 64 * i];
-  }
-  B.kn = *reinterpret_cast<const float2*>(knp + (size_t)t0 * kNS + 2 * lane);
-  B.vn = vnp[t0 + (lane & 31)];
-  const uint32_t* src = vc + ((size_t)(t0 / GTQ_VBLOCK) + q) * (32 * VB) + n * (2 * VB);
-  if (VB == 2) {
-    const uint4 x = *reinterpret_cast<const uint4*>(src);
+  for (int i = 0; i < KWL; ++i)
+    if (2 * i < kw) B.kr[i] = __builtin_amdgcn_raw_buffer_load_b32(R.kc, 4 * lane + 256 * i, sk, 0);
+  B.kn = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(R.kn, 8 * lane, t0 * (kNS * 4), 0));
+  B.vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.vn, 4 * (lane & 31), t0 * 4, 0));
+  const int sv = t0 * (4 * VB * 4);  // (t0 / 8) blocks of 32 VB words
+  // (vector results are bit-cast whole: element reads of them have been miscompiled)
+  if (VB == 1) {
+    const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.vc, voff_v, sv, 0));
+    B.vw[0] = x.x; B.vw[1] = x.y;
+  } else if (VB == 2) {
+    const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R.vc, voff_v, sv, 0));
     B.vw[0] = x.x; B.vw[1] = x.y; B.vw[2] = x.z; B.vw[3] = x.w;
-  } else if (VB == 4) {
-    const uint4 x = *reinterpret_cast<const uint4*>(src);
-    const uint4 y = *reinterpret_cast<const uint4*>(src + 4);
-    B.vw[0] = x.x; B.vw[1] = x.y; B.vw[2] = x.z; B.vw[3] = x.w;
-    B.vw[4] = y.x; B.vw[5] = y.y; B.vw[6] = y.z; B.vw[7] = y.w;
+  } else if (VB == 3) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.vc, voff_v + 8 * i, sv, 0));
+      B.vw[2 * i] = x.x; B.vw[2 * i + 1] = x.y;
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 2 * VB; ++i) B.vw[i] = src[i];
+    for (int i = 0; i < 2; ++i) {
+      const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R.vc, voff_v + 16 * i, sv, 0));
+      B.vw[4 * i] = x.x; B.vw[4 * i + 1] = x.y; B.vw[4 * i + 2] = x.z; B.vw[4 * i + 3] = x.w;
+    }
   }
 }
 
+__device__ inline uint32_t dpp_row_mirror_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);
+}
+
+__device__ inline uint32_t lds_u32(const char* base, uint32_t off) {
+  return *reinterpret_cast<const uint32_t*>(base + off);
+}
+
+// Per-lane and per-K-block constants of the QK (set once per workgroup): for K-block i,
+// ko = (byte offset in the shared block of the first staged record word this lane reads
+// for its half-0 token) << 5 | (bit shift of its first code in that word); the table
+// offset of the block's rate and the offset of its group's norm row.
+template <int NKB>
+struct QkConst {
+  uint32_t ko[NKB];
+  int w2[NKB];    // 2 R: bits per table index (uniform)
+  int lb[NKB];    // byte offset of the rate's pair table in the shared block (uniform)
+  int no[NKB];    // byte offset of the group's norm row within knt (uniform)
+};
+
 // One step of a wave's online softmax over one staged 32-token block.
+// Stage one block into the wave's shared area: key codes (pitch 17), group norms, value
+// norms and value codes. The registers are then free for the next block's loads.
 template <int VB, int KWL>
-__device__ inline void attn_block(const AttnShared& S, AttnWave& W, const BlockData<VB, KWL>& B, const AttnArgs& a,
-                                  int t0, int kw, int lane, int q, int n, int my_row, int my_len,
-                                  const int (&st)[KWL], const uint32_t* r0, const uint32_t* r1,
-                                  const int (&r_nk)[4], const int (&r_grp)[4], const int (&r_bit)[4],
-                                  const int (&r_kb)[4], floatx4 (&oacc)[8], float& m_run, float& l_run) {
-  // ---- stage the block's key codes (pitch kw + 1), group norms and value norms
+__device__ inline void stage_block(AttnWave& W, const BlockData<VB, KWL>& B, int kw, int lane, const int (&st)[KWL]) {
 #pragma unroll
   for (int i = 0; i < KWL; ++i) {
     if (2 * i + 1 < kw) W.ktile[st[i]] = B.kr[i];
@@ -963,52 +985,82 @@ __device__ inline void attn_block(const AttnShared& S, AttnWave& W, const BlockD
   W.knt[2 * (lane & 1)][lane >> 1] = B.kn.x;
   W.knt[2 * (lane & 1) + 1][lane >> 1] = B.kn.y;
   if (lane < 32) W.vn[lane] = B.vn;
-  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < (2 * VB + 3) / 4; ++i) {
+    uint4 x;
+    x.x = B.vw[4 * i];
+    x.y = 4 * i + 1 < 2 * VB ? B.vw[4 * i + 1] : 0u;
+    x.z = 4 * i + 2 < 2 * VB ? B.vw[4 * i + 2] : 0u;
+    x.w = 4 * i + 3 < 2 * VB ? B.vw[4 * i + 3] : 0u;
+    W.vcodes[i][lane] = x;
+  }
+}
 
-  // ---- QK per key group (one rate each), folded with the per-token group norm into
-  //      the logits of tokens 8q + j (j = 4 half + e)
+// One step of a wave's online softmax over the block staged in W.
+template <int VB, int NKB>
+__device__ inline void attn_block(const AttnShared& S, const AttnWave& W, const AttnArgs& a,
+                                  int t0, int lane, int q, int n, int my_row, int my_len,
+                                  const QkConst<NKB>& C, uint32_t nq_off, uint32_t vn_off,
+                                  floatx4 (&oacc)[8], float& m_run, float& l_run) {
+  const char* sb = reinterpret_cast<const char*>(&S);
+
+  // ---- QK per K-block (one rate and group each): A = the decoded codes of tokens
+  //      tau0 + 8 (n >> 2)... of the two 16-token halves, B = the rotated queries; the
+  //      product times the token's group norm adds into the logits of tokens 8q + j
   float lg[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) lg[j] = 0.f;
+  const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (r_nk[r] > 0) {
-      floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-      if (r == 0) qk_rate<1>(S, r0, r1, r_nk[r], r_bit[r], r_kb[r], q, n, d0, d1);
-      if (r == 1) qk_rate<2>(S, r0, r1, r_nk[r], r_bit[r], r_kb[r], q, n, d0, d1);
-      if (r == 2) qk_rate<3>(S, r0, r1, r_nk[r], r_bit[r], r_kb[r], q, n, d0, d1);
-      if (r == 3) qk_rate<4>(S, r0, r1, r_nk[r], r_bit[r], r_kb[r], q, n, d0, d1);
-      const float4 na = *reinterpret_cast<const float4*>(&W.knt[r_grp[r]][8 * q]);
-      const float4 nb = *reinterpret_cast<const float4*>(&W.knt[r_grp[r]][8 * q + 4]);
-      lg[0] = fmaf(na.x, d0[0], lg[0]);
-      lg[1] = fmaf(na.y, d0[1], lg[1]);
-      lg[2] = fmaf(na.z, d0[2], lg[2]);
-      lg[3] = fmaf(na.w, d0[3], lg[3]);
-      lg[4] = fmaf(nb.x, d1[0], lg[4]);
-      lg[5] = fmaf(nb.y, d1[1], lg[5]);
-      lg[6] = fmaf(nb.z, d1[2], lg[6]);
-      lg[7] = fmaf(nb.w, d1[3], lg[7]);
+  for (int i = 0; i < NKB; ++i) {
+    const char* rp = sb + (C.ko[i] >> 5);
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(rp);
+    const uint32_t f0 = __builtin_amdgcn_alignbit(r[1], r[0], C.ko[i]);
+    const uint32_t f1 = __builtin_amdgcn_alignbit(r[4 * kKPitch + 1], r[4 * kKPitch], C.ko[i]);
+    H8 a0, a1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a0.u[j] = lds_u32(sb, C.lb[i] + (__builtin_amdgcn_ubfe(f0, C.w2[i] * j, C.w2[i]) << 2));
+      a1.u[j] = lds_u32(sb, C.lb[i] + (__builtin_amdgcn_ubfe(f1, C.w2[i] * j, C.w2[i]) << 2));
     }
+    H8 qv;
+    qv.v = S.qb[i][q][n];
+    const floatx4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qv.h, z4, 0, 0, 0);
+    const floatx4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qv.h, z4, 0, 0, 0);
+    const float4 na = *reinterpret_cast<const float4*>(sb + nq_off + C.no[i]);
+    const float4 nb = *reinterpret_cast<const float4*>(sb + nq_off + C.no[i] + 16);
+    lg[0] = fmaf(na.x, d0[0], lg[0]);
+    lg[1] = fmaf(na.y, d0[1], lg[1]);
+    lg[2] = fmaf(na.z, d0[2], lg[2]);
+    lg[3] = fmaf(na.w, d0[3], lg[3]);
+    lg[4] = fmaf(nb.x, d1[0], lg[4]);
+    lg[5] = fmaf(nb.y, d1[1], lg[5]);
+    lg[6] = fmaf(nb.z, d1[2], lg[6]);
+    lg[7] = fmaf(nb.w, d1[3], lg[7]);
   }
-  float mblk = -INFINITY;
-  const bool full = t0 + kBlk <= my_len;
+  // ---- whole logits (lanes n and 15 - n hold the high and low parts of one row); each
+  //      of the two lanes then carries on with four of the eight tokens: the high lane
+  //      with tokens 8q..8q+3, the low lane with 8q+4..8q+7
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float v = lg[j] + dpp_row_mirror(lg[j]);
-    if (!full && t0 + 8 * q + j >= my_len) v = -INFINITY;
-    lg[j] = v;
-    mblk = fmaxf(mblk, v);
+  for (int j = 0; j < 8; ++j) lg[j] += dpp_row_mirror(lg[j]);
+  const bool lo = n >= 8;
+  const int tb = t0 + 8 * q + (lo ? 4 : 0);
+  float x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    x[u] = lo ? lg[4 + u] : lg[u];
+    if (tb + u >= my_len) x[u] = -INFINITY;
   }
-  if (a.logits && n < 8) {
+  if (a.logits) {
     const int id = S.row_id[my_row];
     if (id >= 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int pos = t0 + 8 * q + j;
-        if (pos < my_len) a.logits[(size_t)id * a.logits_ld + pos] = lg[j] * LN2_F;
-      }
+      for (int u = 0; u < 4; ++u)
+        if (tb + u < my_len) a.logits[(size_t)id * a.logits_ld + tb + u] = x[u] * LN2_F;
     }
   }
+  float mblk = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mblk = fmaxf(mblk, dpp_row_mirror(mblk));
   mblk = max_over_q(mblk);
   const bool grow = mblk > m_run;
   if (__any(grow)) {
@@ -1029,36 +1081,55 @@ __device__ inline void attn_block(const AttnShared& S, AttnWave& W, const BlockD
     m_run = m_new;
   }
   const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-  // ---- probabilities times value norms, split high/low by column
-  const float4 vna = *reinterpret_cast<const float4*>(W.vn + 8 * q);
-  const float4 vnb = *reinterpret_cast<const float4*>(W.vn + 8 * q + 4);
-  const float vn[8] = {vna.x, vna.y, vna.z, vna.w, vnb.x, vnb.y, vnb.z, vnb.w};
+  // ---- probabilities times value norms, split into binary16 high and low parts
+  const float4 vv = *reinterpret_cast<const float4*>(sb + vn_off);
+  const float vn[4] = {vv.x, vv.y, vv.z, vv.w};
+  float pv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    // x - m_use <= 0: the hardware 2^x (denormal results flush to 0) is exact enough
+    const float p = (x[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[u] - m_use);
+    l_run += p;
+    pv[u] = (p == 0.f) ? 0.f : p * vn[u];
+  }
+  H8 hv, lv;  // (only words 0 and 1 are used)
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(pv[2 * k], pv[2 * k + 1]);
+    const auto l = __builtin_amdgcn_cvt_pkrtz(pv[2 * k] - (float)h[0], pv[2 * k + 1] - (float)h[1]);
+    hv.u[k] = __builtin_bit_cast(uint32_t, h);
+    lv.u[k] = __builtin_bit_cast(uint32_t, l);
+  }
+  // A-row n < 8: high parts of row n; A-row n >= 8: low parts of row 15 - n. The high
+  // lane sends its low parts to its partner and takes the partner's high parts.
   H8 pa;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    float x[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = 2 * jj + u;
-      // lg - m_use <= 0: the hardware 2^x (denormal results flush to 0) is exact enough
-      const float p = (lg[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[j] - m_use);
-      l_run += p;
-      const float pv = (p == 0.f) ? 0.f : p * vn[j];
-      const float hi = (float)(_Float16)pv;
-      x[u] = n < 8 ? hi : pv - hi;
-    }
-    pa.u[jj] = pack2h(x[0], x[1]);
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t keep = lo ? lv.u[k] : hv.u[k];
+    const uint32_t recv = dpp_row_mirror_u(lo ? hv.u[k] : lv.u[k]);
+    pa.u[k] = lo ? recv : keep;
+    pa.u[2 + k] = lo ? keep : recv;
   }
   // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
+  uint32_t vw[2 * VB];
+#pragma unroll
+  for (int i = 0; i < (2 * VB + 3) / 4; ++i) {
+    const uint4 x = W.vcodes[i][lane];
+    vw[4 * i] = x.x;
+    if (4 * i + 1 < 2 * VB) vw[4 * i + 1] = x.y;
+    if (4 * i + 2 < 2 * VB) vw[4 * i + 2] = x.z;
+    if (4 * i + 3 < 2 * VB) vw[4 * i + 3] = x.w;
+  }
 #pragma unroll
   for (int t = 0; t < 8; ++t)
-    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S.lut, vfield<VB>(B.vw, t)), oacc[t], 0, 0, 0);
+    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S.lut, vfield<VB>(vw, t)), oacc[t], 0, 0, 0);
   __builtin_amdgcn_wave_barrier();
 }
 
 // Phase 1 of the attention: per (row tile, split) online-softmax partials.
-template <int VB, int KWL>
-__global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) {
+template <int VB, int KWL, int NKB>
+// (at most 128 registers: two workgroups per compute unit)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) attn_partials_kernel(AttnArgs a) {
   __shared__ AttnShared S;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1071,10 +1142,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
   const DevHead* __restrict__ hp = a.heads + h;
   const size_t sh = (size_t)seq * a.n_kv + h;
   const int kw = a.k_words;
-  const uint32_t* kc = a.k_codes + sh * a.capacity * kw;
-  const float* knp = a.k_norms + sh * a.capacity * kNS;
-  const uint32_t* vc = a.v_codes + sh * (a.capacity / GTQ_VBLOCK) * (32 * VB);
-  const float* vnp = a.v_norms + sh * a.capacity;
+  SliceRsrc R;
+  const uint32_t cap = (uint32_t)a.capacity;
+  R.kc = slice_rsrc(a.k_codes + sh * a.capacity * kw, cap * (uint32_t)kw * 4u);
+  R.kn = slice_rsrc(a.k_norms + sh * a.capacity * kNS, cap * (kNS * 4u));
+  R.vc = slice_rsrc(a.v_codes + sh * (a.capacity / GTQ_VBLOCK) * (32 * VB), cap * (16u * VB));
+  R.vn = slice_rsrc(a.v_norms + sh * a.capacity, cap * 4u);
+  const int voff_v = 4 * (q * (32 * VB) + n * (2 * VB));
   const int c0 = chunk_idx * a.chunk;
   // ---- one round of independent loads: B operand, decode table, rows, first block
   uint4 qbv[kQB / kThreads];
@@ -1087,31 +1161,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
     lutv[u] = e < kPairTable ? a.cb->pair[e] : 0u;
   }
   const int len_ld = a.prefill ? 0 : a.seq_len[seq];
-  BlockData<VB, KWL> blk[kDepth];
-  load_block<VB, KWL>(blk[0], kc, knp, vc, vnp, (int)min<int64_t>(c0 + kBlk * wave, a.capacity - kBlk), kw, lane,
-                      q, n);
-  // per rate 1..4 (uniform, from the head table): K-blocks, group, record bit, first K-block
-  int r_nk[4] = {0, 0, 0, 0}, r_grp[4] = {0, 0, 0, 0}, r_bit[4] = {0, 0, 0, 0}, r_kb[4] = {0, 0, 0, 0};
-  {
-    const int n_groups = hp->n_groups;
-    int kbs = 0;
-#pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g) {
-      if (g < n_groups) {
-        const int r = hp->rate[g] - 1, nk = hp->nkb_g[g];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if (rr == r) {
-            r_nk[rr] = nk;
-            r_grp[rr] = g;
-            r_bit[rr] = hp->bit_off[g];
-            r_kb[rr] = kbs;
-          }
-        }
-        kbs += nk;
-      }
-    }
-  }
+  BlockData<VB, KWL> blk[1];
+  load_block<VB, KWL>(blk[0], R, c0 + kBlk * wave, kw, lane, voff_v);
 #pragma unroll
   for (int u = 0; u < kQB / kThreads; ++u) (&S.qb[0][0][0])[tid + kThreads * u] = qbv[u];
 #pragma unroll
@@ -1131,45 +1182,50 @@ __global__ void __launch_bounds__(kThreads, 2) attn_partials_kernel(AttnArgs a) 
   if (c0 >= tile_len) return;  // no cached token of this tile in this split
   const int c1 = min(c0 + a.chunk, tile_len);
   constexpr int kStep = kBlk * kWaves;
-#pragma unroll
-  for (int j = 1; j < kDepth; ++j) {
-    const int t = c0 + kBlk * wave + kStep * j;
-    if (t < c1) load_block<VB, KWL>(blk[j], kc, knp, vc, vnp, t, kw, lane, q, n);
-  }
 
   const int my_row = n < 8 ? n : 15 - n;
   const int my_len = S.row_len[my_row];
   AttnWave& W = S.u.w[wave];
-  int st[KWL];  // staging slot of word lane + 64 i: one pad word per token
+  const char* sb = reinterpret_cast<const char*>(&S);
+  int st[KWL];  // staging slot of word lane + 64 i: token (lw / kw) at pitch 17
 #pragma unroll
   for (int i = 0; i < KWL; ++i) {
     const int lw = lane + 64 * i;
-    st[i] = lw + lw / kw;
+    st[i] = (lw / kw) * kKPitch + lw % kw;
   }
-  const int tau0 = 8 * (n >> 2) + (n & 3);  // A-row n of the two 16-token halves
-  const uint32_t* r0 = W.ktile + tau0 * (kw + 1);
-  const uint32_t* r1 = r0 + 4 * (kw + 1);
+  // QK constants: A-row n of the two 16-token halves is token tau0 (+ 4)
+  const int tau0 = 8 * (n >> 2) + (n & 3);
+  const uint32_t ktile_off = (uint32_t)(reinterpret_cast<const char*>(W.ktile) - sb);
+  const uint32_t lut_off = (uint32_t)(reinterpret_cast<const char*>(S.lut) - sb);
+  QkConst<NKB> C;
+#pragma unroll
+  for (int i = 0; i < NKB; ++i) {
+    const int rg = hp->kb_rg[i];
+    const int rate = rg & 0xFF, grp = rg >> 8;
+    const int bit = hp->kb_bit[i] + 8 * q * rate;
+    C.ko[i] = ((ktile_off + 4u * (uint32_t)(tau0 * kKPitch + (bit >> 5))) << 5) | (uint32_t)(bit & 31);
+    C.w2[i] = 2 * rate;
+    C.lb[i] = (int)lut_off + 4 * (((1 << (2 * rate)) - 4) / 3);
+    C.no[i] = grp * kBlk * 4;
+  }
+  const uint32_t nq_off = (uint32_t)(reinterpret_cast<const char*>(&W.knt[0][8 * q]) - sb);
+  const uint32_t vn_off = (uint32_t)(reinterpret_cast<const char*>(&W.vn[8 * q + (n >= 8 ? 4 : 0)]) - sb);
 
   floatx4 oacc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) oacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- main loop: kDepth blocks per round, each register set refilled kDepth ahead
-  for (int tb = c0 + kBlk * wave; tb < c1; tb += kStep * kDepth) {
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      const int t0 = tb + kStep * j;
-      if (t0 < c1) {
-        attn_block<VB, KWL>(S, W, blk[j], a, t0, kw, lane, q, n, my_row, my_len, st, r0, r1, r_nk, r_grp, r_bit,
-                            r_kb, oacc, m_run, l_run);
-        const int tn = t0 + kStep * kDepth;
-        if (tn < c1) load_block<VB, KWL>(blk[j], kc, knp, vc, vnp, tn, kw, lane, q, n);
-      }
-    }
+  // ---- main loop: stage the block, start the next block's loads, compute from the stage
+  for (int t0 = c0 + kBlk * wave; t0 < c1; t0 += kStep) {
+    stage_block<VB, KWL>(W, blk[0], kw, lane, st);
+    __builtin_amdgcn_wave_barrier();
+    if (t0 + kStep < c1) load_block<VB, KWL>(blk[0], R, t0 + kStep, kw, lane, voff_v);
+    attn_block<VB, NKB>(S, W, a, t0, lane, q, n, my_row, my_len, C, nq_off, vn_off, oacc, m_run, l_run);
   }
 
   // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves
+  l_run += dpp_row_mirror(l_run);  // the two lanes of a row summed different tokens
   l_run = sum_over_q(l_run);
   if (q == 0 && n < 8) {
     S.om[wave][n] = m_run;
@@ -1371,6 +1427,10 @@ bool check_cache(const gtq_plan* p, const gtq_cache_view* c, const char* fn, gtq
     *st = fail(GTQ_EINVAL, std::string(fn) + ": cache batch >= 1 and capacity a positive multiple of 32");
     return false;
   }
+  if (c->capacity > kMaxCapacity) {  // one (sequence, KV head) slice stays under 2 GiB
+    *st = fail(GTQ_EUNSUPPORTED, std::string(fn) + ": capacity above 2^25 tokens");
+    return false;
+  }
   (void)p;
   return true;
 }
@@ -1444,8 +1504,8 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
 int auto_chunk(int64_t max_len, int64_t tiles) {
   // one round of workgroups (one per compute unit), at least 4 splits per row tile so
   // that ragged batches balance; splits of whole rounds of the main loop (8 waves x
-  // 4 blocks x 32 tokens)
-  constexpr int64_t kRound = kBlk * kWaves * kDepth;
+  // 32 tokens)
+  constexpr int64_t kRound = kBlk * kWaves;
   int64_t target = std::max<int64_t>(4, kTargetWG / std::max<int64_t>(1, tiles));
   target = std::min<int64_t>(kMaxChunks, target);
   int64_t ch = (max_len + target - 1) / target;
@@ -1486,6 +1546,8 @@ void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnA
   aa.tiles_per_kv = L.tiles_per_kv;
   aa.chunk = L.chunk;
   aa.n_chunks = L.n_chunks;
+  aa.nkb_max = 0;
+  for (int h = 0; h < p->n_kv; ++h) aa.nkb_max = std::max(aa.nkb_max, (int32_t)p->heads[(size_t)layer * p->n_kv + h].nkb);
 }
 
 gtq_status launch_qrot(AttnArgs& aa, const AttnLaunch& L, const float* q, float scale, hipStream_t stream) {
@@ -1501,9 +1563,20 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
   if (p->k_words > 16) return fail(GTQ_EUNSUPPORTED, "gtq attention: more than 16 key code words per token");
   dim3 grid(L.n_chunks, L.n_tiles);
   const bool wide = p->k_words > 8;  // key words per lane: 4 (k_words <= 8) or 8
-#define GTQ_LAUNCH(VB)                                                                          \
-  if (wide) hipLaunchKernelGGL((attn_partials_kernel<VB, 8>), grid, dim3(kThreads), 0, stream, aa); \
-  else hipLaunchKernelGGL((attn_partials_kernel<VB, 4>), grid, dim3(kThreads), 0, stream, aa);
+  // K-blocks per head: sum_g ceil(d_g / 32), 4..7 for four groups; the kernel runs the
+  // layer's largest count (extra K-blocks of a head have zero query operands)
+  const int nkb = aa.nkb_max;
+  if (nkb < 4 || nkb > 7) return fail(GTQ_EUNSUPPORTED, "gtq attention: K-block count outside 4..7");
+#define GTQ_LAUNCH3(VB, KWL, NKB) hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB>), grid, dim3(kThreads), 0, stream, aa)
+#define GTQ_LAUNCH2(VB, KWL)                  \
+  switch (nkb) {                              \
+    case 4: GTQ_LAUNCH3(VB, KWL, 4); break;   \
+    case 5: GTQ_LAUNCH3(VB, KWL, 5); break;   \
+    case 6: GTQ_LAUNCH3(VB, KWL, 6); break;   \
+    default: GTQ_LAUNCH3(VB, KWL, 7); break;  \
+  }
+#define GTQ_LAUNCH(VB) \
+  if (wide) { GTQ_LAUNCH2(VB, 8) } else { GTQ_LAUNCH2(VB, 4) }
   switch (p->v_bits) {
     case 1: GTQ_LAUNCH(1) break;
     case 2: GTQ_LAUNCH(2) break;
@@ -1511,6 +1584,8 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
     default: GTQ_LAUNCH(4) break;
   }
 #undef GTQ_LAUNCH
+#undef GTQ_LAUNCH2
+#undef GTQ_LAUNCH3
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq attention partials: launch");
   return ok();
