@@ -1402,6 +1402,122 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   if (tid < kD) a.out[(size_t)row * kD + tid] = opart[0][tid] + opart[1][tid];
 }
 
+// Merge for up to 8 splits per row: one workgroup (256 threads) per row tile (the rows
+// of one sequence and KV head, as in the partials grid), so that Pi_V^T is read once per
+// tile. Thread (row r, float4 column c4) merges its row's splits in one round of loads;
+// then thread (column i, half) forms the inverse rotation's half sums for all 8 rows.
+constexpr int kMergeTileChunks = 8;
+struct MergeTileArgs {
+  const float* vrot_t;     // Pi_V^T of the layer's KV heads, 128 x 128 each, consecutive
+  const float* partials;
+  const int32_t* seq_len;
+  float* out;
+  int64_t pos0;
+  int32_t n_q, g, n_kv, tiles_per_kv, n_tok, n_chunks, chunk, prefill, max_len, seq;
+};
+
+__global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
+  __shared__ float4 accs[8][kD / 4];
+  __shared__ float part[2][8][kD];
+  __shared__ int32_t rid[8];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  int seq, h, tr;
+  if (a.prefill) {
+    h = tile / a.tiles_per_kv;
+    tr = tile - h * a.tiles_per_kv;
+    seq = a.seq;
+  } else {
+    seq = tile / (a.n_kv * a.tiles_per_kv);
+    const int rem = tile - seq * a.n_kv * a.tiles_per_kv;
+    h = rem / a.tiles_per_kv;
+    tr = rem - h * a.tiles_per_kv;
+  }
+  // the inverse rotation operand first: thread (i, half) holds Pi_V^T[i][64 half .. + 63]
+  const int oi = tid & 127, oh = tid >> 7;
+  float4 pvt[16];
+  {
+    const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)h * kD * kD + (size_t)oi * kD + 64 * oh);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) pvt[u] = pt[u];
+  }
+  // row r of the tile: global row id (-1 if absent) and visible length
+  const int r = tid >> 5, c4 = tid & 31;
+  const int f = tr * 8 + r;
+  int id = -1, len = 0;
+  if (a.prefill) {
+    if (f < a.n_tok * a.g) {
+      const int t = f / a.g;
+      id = t * a.n_q + h * a.g + (f - t * a.g);
+      len = (int)(a.pos0 + t + 1);
+    }
+  } else if (f < a.g) {
+    id = seq * a.n_q + h * a.g + f;
+    len = min(max(a.seq_len[seq], 0), a.max_len);
+  }
+  if (c4 == 0) rid[r] = id;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  if (id >= 0) {
+    const float* pp = a.partials + (size_t)id * a.n_chunks * kPS;
+    const int nv = min(a.n_chunks, (len + a.chunk - 1) / a.chunk);
+    float mk[kMergeTileChunks], lk[kMergeTileChunks];
+    float4 xk[kMergeTileChunks];
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeTileChunks; ++k) {
+      mk[k] = -INFINITY;
+      lk[k] = 0.f;
+      xk[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < nv) {
+        const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)k * kPS);
+        mk[k] = ml.x;
+        lk[k] = ml.y;
+        xk[k] = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS + 4 + 4 * c4);
+      }
+      M = fmaxf(M, mk[k]);
+    }
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < kMergeTileChunks; ++k) {
+        const float w = (mk[k] == -INFINITY) ? 0.f : exp2f(mk[k] - M);
+        acc.x = fmaf(w, xk[k].x, acc.x);
+        acc.y = fmaf(w, xk[k].y, acc.y);
+        acc.z = fmaf(w, xk[k].z, acc.z);
+        acc.w = fmaf(w, xk[k].w, acc.w);
+        L = fmaf(w, lk[k], L);
+      }
+    }
+  }
+  const float sc = L > 0.f ? 0.08838834764831845f / L : 0.f;  // 1 / (L sqrt(128))
+  accs[r][c4] = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+  __syncthreads();
+  float o[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) o[rr] = 0.f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const float4 x = accs[rr][16 * oh + u];
+      o[rr] = fmaf(pvt[u].x, x.x, o[rr]);
+      o[rr] = fmaf(pvt[u].y, x.y, o[rr]);
+      o[rr] = fmaf(pvt[u].z, x.z, o[rr]);
+      o[rr] = fmaf(pvt[u].w, x.w, o[rr]);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) part[oh][rr][oi] = o[rr];
+  __syncthreads();
+  const int orow = rid[r];
+  if (orow >= 0) {
+    const float4 p0 = *reinterpret_cast<const float4*>(&part[0][r][4 * c4]);
+    const float4 p1 = *reinterpret_cast<const float4*>(&part[1][r][4 * c4]);
+    *reinterpret_cast<float4*>(a.out + (size_t)orow * kD + 4 * c4) =
+        make_float4(p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w);
+  }
+}
+
 // ============================================================================
 // host helpers
 // ============================================================================
@@ -1594,10 +1710,17 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
 gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const int32_t* seq_len,
                         int64_t pos0, int prefill, int max_len, float* out, const void* ws,
                         hipStream_t stream) {
-  MergeArgs ma{p->d_rot + p->heads[(size_t)layer * p->n_kv].vrot_t_off,
-               reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + attn_qb_bytes(L.n_tiles)), seq_len,
-               out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill, max_len};
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows), dim3(256), 0, stream, ma);
+  const float* vrot_t = p->d_rot + p->heads[(size_t)layer * p->n_kv].vrot_t_off;
+  const float* partials = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + attn_qb_bytes(L.n_tiles));
+  if (L.n_chunks <= kMergeTileChunks) {  // one workgroup per row tile
+    MergeTileArgs mt{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, p->n_kv, L.tiles_per_kv,
+                     (int32_t)(L.rows / p->n_q), L.n_chunks, L.chunk, prefill, max_len, 0};
+    hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.n_tiles), dim3(256), 0, stream, mt);
+  } else {  // one workgroup per row
+    MergeArgs ma{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill,
+                 max_len};
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows), dim3(256), 0, stream, ma);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq attention merge: launch");
   return ok();
