@@ -157,6 +157,15 @@ struct AppendGemmShared {
   float thr[5][16];                   // quantizer thresholds by rate
 };
 
+// OR over the 16 lanes of a row: DPP row operations
+__device__ inline uint32_t row_or_u32(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // row mirror
+  return v;
+}
+
 // fp64 sum over the 16 lanes of a row (one token): DPP row operations
 __device__ inline double row_sum_f64(double v) {
   v += dpp_f64(v, 0);
@@ -339,28 +348,59 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
         // lane (q, n) holds D[token 16 hf + 4q + e][output i0 + n]
         const int d = (g == 4) ? kD : hp->dim[g];
         const int i = ti0[j] + n;
-        if (i < d) {
-          const float zs = sqrtf((float)d) * (1.f / (kRotSplitScale * 256.f));
-          const int r = trate[j];
-          const float* th = S.thr[r];
-          const int kbit = (g == 4) ? 0 : hp->bit_off[g] + i * r;
+        const float zs = sqrtf((float)d) * (1.f / (kRotSplitScale * 256.f));
+        const int r = trate[j];
+        const float* th = S.thr[r];
+        if (g == 4) {
+          if (i < d) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float z = acc[hf][e] * zs;
+                // code = #{k : z >= t_k} by binary search over the sorted thresholds
+                int cd = 0;
+                for (int step = 1 << (r - 1); step > 0; step >>= 1)
+                  if (z >= th[cd + step - 1]) cd += step;
+                const int t = 16 * hf + 4 * q + e;
+                // token t & 7 of block t >> 3, coordinate i at bit 8 vb i + vb (t & 7)
+                const int bit = 8 * r * i + r * (t & 7);
+                uint32_t* dst = &S.pv[t >> 3][0];
+                const uint64_t f = (uint64_t)cd << (bit & 31);
+                atomicOr(dst + (bit >> 5), (uint32_t)f);
+                if (f >> 32) atomicOr(dst + (bit >> 5) + 1, (uint32_t)(f >> 32));
+              }
+            }
+          }
+        } else {
+          // keys: the 16 lanes of a row hold consecutive positions i0..i0+15 of one group
+          // for one token, i.e. one run of 16 r record bits starting at bit b0. Each lane
+          // places its code in a 96-bit window, the row ORs the window together and three
+          // lanes OR its words into the record.
+          const int b0 = hp->bit_off[g] + ti0[j] * r;
+          const int w0 = b0 >> 5;
+          const int pos = (b0 & 31) + n * r;  // bit in the window (< 96)
+          const int kq = pos >> 5, sft = pos & 31;
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float z = acc[hf][e] * zs;
-              // code = #{k : z >= t_k} by binary search over the sorted thresholds
               int cd = 0;
               for (int step = 1 << (r - 1); step > 0; step >>= 1)
                 if (z >= th[cd + step - 1]) cd += step;
+              if (i >= d) cd = 0;  // padding outputs of the group's last tile
+              const uint32_t lo = (uint32_t)cd << sft;
+              const uint32_t hi = sft ? (uint32_t)cd >> (32 - sft) : 0u;
+              uint32_t v0 = kq == 0 ? lo : 0u;
+              uint32_t v1 = kq == 0 ? hi : (kq == 1 ? lo : 0u);
+              uint32_t v2 = kq == 1 ? hi : (kq == 2 ? lo : 0u);
+              v0 = row_or_u32(v0);
+              v1 = row_or_u32(v1);
+              v2 = row_or_u32(v2);
               const int t = 16 * hf + 4 * q + e;
-              // values: token t & 7 of block t >> 3, coordinate i at bit 8 vb i + vb j;
-              // keys: the record bit of position i of the group
-              const int bit = (g == 4) ? 8 * r * i + r * (t & 7) : kbit;
-              uint32_t* dst = (g == 4) ? &S.pv[t >> 3][0] : &S.pk[t][0];
-              const uint64_t f = (uint64_t)cd << (bit & 31);
-              atomicOr(dst + (bit >> 5), (uint32_t)f);
-              if (f >> 32) atomicOr(dst + (bit >> 5) + 1, (uint32_t)(f >> 32));
+              const uint32_t vv = n == 0 ? v0 : (n == 1 ? v1 : v2);
+              if (n < 3 && vv) atomicOr(&S.pk[t][w0 + n], vv);
             }
           }
         }
@@ -1296,7 +1336,7 @@ struct MergeArgs {
 // the accumulators of chunks ks, ks + 8, ... together with their (m, l) and its slice
 // of Pi_V^T in one round; then M = max m, weights 2^(m - M), the weighted sums over
 // the slices, normalisation by L sqrt(128) and the inverse rotation.
-constexpr int kMergeRegs = 4;  // chunks per thread kept in registers (32 splits)
+constexpr int kMergeRegs = 16;  // chunks per thread kept in registers (128 splits in one round)
 __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   __shared__ float4 red[8][32];
   __shared__ float sm[8], sl[8];
