@@ -351,17 +351,34 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
         const float zs = sqrtf((float)d) * (1.f / (kRotSplitScale * 256.f));
         const int r = trate[j];
         const float* th = S.thr[r];
+        // code = #{k : z >= t_k} by binary search over the sorted thresholds, one search
+        // level at a time for all 8 values of the lane (the threshold reads of a level go
+        // out together)
+        int cds[8];
+        float zv[8];
+#pragma unroll
+        for (int v8 = 0; v8 < 8; ++v8) {
+          zv[v8] = acc[v8 >> 2][v8 & 3] * zs;
+          cds[v8] = 0;
+        }
+#pragma unroll
+        for (int lvl = 3; lvl >= 0; --lvl) {
+          if (lvl < r) {
+            const int step = 1 << lvl;
+            float tv[8];
+#pragma unroll
+            for (int v8 = 0; v8 < 8; ++v8) tv[v8] = th[cds[v8] + step - 1];
+#pragma unroll
+            for (int v8 = 0; v8 < 8; ++v8) cds[v8] += zv[v8] >= tv[v8] ? step : 0;
+          }
+        }
         if (g == 4) {
           if (i < d) {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float z = acc[hf][e] * zs;
-                // code = #{k : z >= t_k} by binary search over the sorted thresholds
-                int cd = 0;
-                for (int step = 1 << (r - 1); step > 0; step >>= 1)
-                  if (z >= th[cd + step - 1]) cd += step;
+                const int cd = cds[4 * hf + e];
                 const int t = 16 * hf + 4 * q + e;
                 // token t & 7 of block t >> 3, coordinate i at bit 8 vb i + vb (t & 7)
                 const int bit = 8 * r * i + r * (t & 7);
@@ -385,11 +402,7 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
           for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float z = acc[hf][e] * zs;
-              int cd = 0;
-              for (int step = 1 << (r - 1); step > 0; step >>= 1)
-                if (z >= th[cd + step - 1]) cd += step;
-              if (i >= d) cd = 0;  // padding outputs of the group's last tile
+              const int cd = i >= d ? 0 : cds[4 * hf + e];  // zero: padding outputs of the group's last tile
               const uint32_t lo = (uint32_t)cd << sft;
               const uint32_t hi = sft ? (uint32_t)cd >> (32 - sft) : 0u;
               uint32_t v0 = kq == 0 ? lo : 0u;
