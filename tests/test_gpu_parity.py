@@ -346,3 +346,36 @@ def test_edge_cases(G):
     assert_close(o1[2].cpu().numpy(), np.repeat(vhat, 4, axis=0), "length-1 sequence returns its value")
     _, ref = _oracle_decode(case, 0, 0, n, [O.encode_kv(hp, k[:, 0], v[:, 0])], q[0], scale_default())
     assert_close(o1[0].cpu().numpy(), ref, "zero-vector sequence")
+
+
+def test_capacity_limit_and_merge_paths(G):
+    """A cache view above 2^25 tokens is refused before any launch (no memory behind it
+    is touched); both merge kernels (at most 8 splits per row: one workgroup per row
+    tile; more: one per row) give the oracle's outputs on the same cache."""
+    _say("case: capacity limit, merge paths")
+    import ctypes as C
+    case = Case(6, 1, 2, 8, 700, 128, 2, batch=2)
+    plan = case.plan()
+    big = G.CacheView(16, 16, 16, 16, 1, (1 << 25) + 32)  # dummy non-null pointers, never read
+    out = torch.empty(1, case.HQ, 128, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    q1 = torch.zeros(1, case.HQ, 128, device="cuda")
+    sl1 = torch.full((1,), 8, dtype=torch.int32, device="cuda")
+    st = G.lib().gtq_decode_attn(plan.handle, 0, C.byref(big), q1.data_ptr(), sl1.data_ptr(), 8, 0.1, 0,
+                                 out.data_ptr(), None, ws.data_ptr(), ws.numel(), None)
+    assert st == 2  # GTQ_EUNSUPPORTED
+    cache = G.PackedCache(plan, 2, 704)
+    lens = [700, 333]
+    encs = []
+    for b, n in enumerate(lens):
+        e = _encode(case, 0, b, n)
+        encs.append(e)
+        _upload_oracle_cache(case, cache, 0, b, n, e)
+    q = np.stack([case.q(0, b) for b in range(2)])
+    sc = scale_default()
+    for chunk in (96, 32):  # 8 splits (tile merge) and 22 splits (row merge) at 700 tokens
+        out = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(np.array(lens, np.int32)), 700, sc, chunk=chunk)
+        torch.cuda.synchronize()
+        for b, n in enumerate(lens):
+            _, ref = _oracle_decode(case, 0, b, n, encs[b], q[b], sc)
+            assert_close(out[b].cpu().numpy(), ref, f"chunk {chunk} out b{b}")
