@@ -45,7 +45,7 @@ typedef int32_t gtq_status;
 enum {
   GTQ_OK = 0,
   GTQ_EINVAL = 1,        /* bad argument (null pointer, out-of-range value)     */
-  GTQ_EUNSUPPORTED = 2,  /* valid but not supported by this build (head_dim)    */
+  GTQ_EUNSUPPORTED = 2,  /* valid but not supported (head_dim != 128, capacity > 2^25) */
   GTQ_ENOMEM = 3,        /* host or device allocation failed (plan creation)   */
   GTQ_EDEVICE = 4,       /* HIP runtime or kernel launch error                  */
   GTQ_ECAPACITY = 5      /* cache or workspace too small for the request        */

@@ -644,14 +644,18 @@ __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
 //                         columns 8..15: low parts of rows 7..0), kept in the workspace;
 //   attn_partials_kernel  per (row tile, split of `chunk` tokens) one online-softmax
 //                         partial (m, l, acc[128]) per row;
-//   attn_merge_kernel     log-sum-exp merge of the splits and o = Pi_V^T acc / sqrt(128).
+//   attn_merge_tile_kernel / attn_merge_kernel
+//                         log-sum-exp merge of the splits and o = Pi_V^T acc / sqrt(128).
 // Partials: a workgroup (8 waves) takes one row tile (up to 8 query rows of one sequence
-// and KV head) and one split; each wave walks 32-token blocks:
-//   QK: MFMA 16x16x32 f16 per 32-coordinate K-block of a key group; A = decoded key
-//       codes (exact binary16 codebook values, two codes per table read), 16 tokens per
-//       A tile. The per-token group norm multiplies each group's product; a row-mirror
-//       DPP then adds the high and low halves.
-//   online softmax in base 2 (the scale carries log2(e));
+// and KV head) and one split; each wave walks 32-token blocks, staging each block in its
+// LDS area and issuing the next block's loads before computing on the stage:
+//   QK: per 32-coordinate K-block (one rate and key group each; their count is a
+//       template parameter, so the loop is straight-line) one MFMA 16x16x32 f16 per
+//       16-token half; A = decoded key codes (exact binary16 codebook values, two codes
+//       per table read), B = the rotated queries. The per-token group norm multiplies
+//       each product; a row-mirror DPP then adds the high and low halves.
+//   online softmax in base 2 (the scale carries log2(e)), each of the two lanes of a
+//       row pair finishing four of the eight tokens;
 //   PV: MFMA with A = p * nu_V split into high/low parts (rows as above) and
 //       B = decoded value codes (8 tokens x 16 coordinates), accumulating in the value
 //       rotation's basis.
@@ -725,11 +729,6 @@ __device__ inline int tile_row(const AttnArgs& a, int seq, int h, int tr, int r,
   return id;
 }
 
-__device__ inline uint32_t pack2h(float a, float b) {
-  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
 __device__ inline float dpp_row_mirror(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
 }
@@ -762,7 +761,7 @@ __device__ inline float swap_q3(float x) { return xor16(xor32(x)); }
 
 // ---------------------------------------------------------------- query rotation
 
-// One workgroup (4 waves) per row tile: the tile's query rows in record order, then
+// One workgroup (16 waves) per row tile: the tile's query rows in record order, then
 // per group and 16-coordinate slice i0.. the fp32 MFMA 16x16x4 product
 // D[i][r] = sum_k Pi_g[i0 + i][k] qrec[r][pos_off + k] (the 4 k of lane (q, n) per MFMA
 // are k0 + 4q + s), written as the tile's B operand.
