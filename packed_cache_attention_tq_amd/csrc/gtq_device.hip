@@ -686,7 +686,7 @@ struct AttnArgs {
   int64_t logits_ld;
   int64_t pos0;            // prefill
   int32_t n_kv, n_q, g, k_words;
-  int32_t tiles_per_kv;    // ceil(rows per KV head / 8)
+  int32_t tiles_per_kv;    // row tiles per KV head (8 rows per tile in decode, 16 in prefill)
   int32_t prefill;         // 0 decode, 1 prefill
   int32_t seq;             // prefill sequence
   int32_t n_tok;           // prefill: tokens in chunk
@@ -711,9 +711,11 @@ __device__ inline void tile_coords(const AttnArgs& a, int tile, int* seq, int* h
   }
 }
 
-// query row r (0..7) of a tile: its global row id (-1 if absent) and visible length
+// query row r (0..RT-1) of a tile of RT rows: its global row id (-1 if absent) and
+// visible length
+template <int RT = 8>
 __device__ inline int tile_row(const AttnArgs& a, int seq, int h, int tr, int r, int len_ld, int* len) {
-  const int f = tr * 8 + r;
+  const int f = tr * RT + r;
   int id = -1, L = 0;
   if (a.prefill) {
     if (f < a.n_tok * a.g) {
@@ -764,13 +766,19 @@ __device__ inline float swap_q3(float x) { return xor16(xor32(x)); }
 // One workgroup (16 waves) per row tile: the tile's query rows in record order, then
 // per group and 16-coordinate slice i0.. the fp32 MFMA 16x16x4 product
 // D[i][r] = sum_k Pi_g[i0 + i][k] qrec[r][pos_off + k] (the 4 k of lane (q, n) per MFMA
-// are k0 + 4q + s), written as the tile's B operand.
+// are k0 + 4q + s), written as the tile's B operand. Tiles of 8 rows (RT = 8) put the
+// high parts in columns 0..7 and the low parts of rows 7..0 in columns 8..15; tiles of
+// 16 rows (RT = 16, prefill) write two operands, high parts then low parts, with row n
+// in column n.
 constexpr int kQrotWaves = 16;  // 1024 threads: one 16-coordinate slice per wave (at most 11)
 constexpr int kQrotSlices = 1;
+template <int RT>
 __device__ inline void qrot_body(const AttnArgs& a, int tile) {
-  __shared__ __align__(16) float qnat[8][kD];
-  __shared__ __align__(16) float qrec[8][kD];
-  __shared__ uint4 qb[kMaxKB][4][16];
+  constexpr int kParts = RT / 8;       // B operands per tile (1, or 2 for hi and lo)
+  constexpr int kTileQB = kParts * kQB;
+  __shared__ __align__(16) float qnat[RT][kD];
+  __shared__ __align__(16) float qrec[RT][kD];
+  __shared__ uint4 qb[kParts * kMaxKB][4][16];
   constexpr int kT = 64 * kQrotWaves;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -820,20 +828,22 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
                                           : make_float2(0.f, 0.f);
     }
   }
-  float qv;
-  {
-    const int r = tid >> 7, c = tid & (kD - 1);  // 8 x 128 == kT
+  float qv[kParts];
+#pragma unroll
+  for (int pp = 0; pp < kParts; ++pp) {
+    const int r = (tid >> 7) + 8 * pp, c = tid & (kD - 1);  // 8 x 128 == kT
     int L;
-    const int id = tile_row(a, seq, h, tr, r, 0, &L);
-    qv = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
+    const int id = tile_row<RT>(a, seq, h, tr, r, 0, &L);
+    qv[pp] = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
   }
   const int crd = tid < kD ? hp->coord[tid] : 0;
-  (&qnat[0][0])[tid] = qv;
-  for (int e = tid; e < kQB; e += kT) (&qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int pp = 0; pp < kParts; ++pp) (&qnat[0][0])[tid + kT * pp] = qv[pp];
+  for (int e = tid; e < kTileQB; e += kT) (&qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
   __syncthreads();
   if (tid < kD) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) qrec[r][tid] = qnat[r][crd];
+    for (int r = 0; r < RT; ++r) qrec[r][tid] = qnat[r][crd];
   }
   __syncthreads();
 #pragma unroll
@@ -842,15 +852,15 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
       const int g = sg[j], i0 = si0[j];
       const int d = hp->dim[g], po = hp->pos_off[g], kp0 = hp->kp_off[g];
       // the B operands (row n of the record-order queries) first: reads at clamped
-      // addresses, zero outside the group or for n >= 8
+      // addresses, zero outside the group or for rows past the tile
       float2 bq[8][2];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int kk = 16 * u + 4 * q;
-        const float2 x0 = *reinterpret_cast<const float2*>(&qrec[n & 7][min(po + kk, kD - 2)]);
-        const float2 x1 = *reinterpret_cast<const float2*>(&qrec[n & 7][min(po + kk + 2, kD - 2)]);
-        bq[u][0] = (n < 8 && kk < d) ? x0 : make_float2(0.f, 0.f);
-        bq[u][1] = (n < 8 && kk + 2 < d) ? x1 : make_float2(0.f, 0.f);
+        const float2 x0 = *reinterpret_cast<const float2*>(&qrec[n % RT][min(po + kk, kD - 2)]);
+        const float2 x1 = *reinterpret_cast<const float2*>(&qrec[n % RT][min(po + kk + 2, kD - 2)]);
+        bq[u][0] = (n < RT && kk < d) ? x0 : make_float2(0.f, 0.f);
+        bq[u][1] = (n < RT && kk + 2 < d) ? x1 : make_float2(0.f, 0.f);
       }
       floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -863,7 +873,7 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
         }
       }
       // lane (q, n) holds D[4q + e][n]: coordinate i0 + 4q + e of row n
-      if (n < 8) {
+      if (n < RT) {
         const float sc = a.qscale / sqrtf((float)d);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -873,18 +883,24 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
             const _Float16 hi = (_Float16)val;
             const _Float16 lo = (_Float16)(val - (float)hi);
             const int kp = kp0 + ii;
-            reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][n])[kp & 7] = hi;
-            reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][15 - n])[kp & 7] = lo;
+            if (RT == 8) {
+              reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][n])[kp & 7] = hi;
+              reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][15 - n])[kp & 7] = lo;
+            } else {
+              reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][n])[kp & 7] = hi;
+              reinterpret_cast<_Float16*>(&qb[kMaxKB + (kp >> 5)][(kp >> 3) & 3][n])[kp & 7] = lo;
+            }
           }
         }
       }
     }
   }
   __syncthreads();
-  for (int e = tid; e < kQB; e += kT) a.qb[(size_t)tile * kQB + e] = (&qb[0][0][0])[e];
+  for (int e = tid; e < kTileQB; e += kT) a.qb[(size_t)tile * kTileQB + e] = (&qb[0][0][0])[e];
 }
 
-__global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) { qrot_body(a, blockIdx.x); }
+template <int RT>
+__global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) { qrot_body<RT>(a, blockIdx.x); }
 
 // Decode step preparation in one launch: workgroups [0, n_app) append the step's
 // tokens (token w / n_kv, KV head w % n_kv), the rest rotate the queries of one row
@@ -892,7 +908,7 @@ __global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) 
 __global__ void __launch_bounds__(1024) decode_prep_kernel(AppendArgs ap, AttnArgs aa, int n_app) {
   const int w = blockIdx.x;
   if (w < n_app) append_token_body(ap, w / ap.n_kv, w % ap.n_kv);
-  else qrot_body(aa, w - n_app);
+  else qrot_body<8>(aa, w - n_app);
 }
 
 // ---------------------------------------------------------------- partials
@@ -907,18 +923,22 @@ struct AttnWave {
   uint4 vcodes[2][64];               // value codes of the block, 2 v_bits words per lane
 };
 
-struct AttnShared {
+// Shared block of a partials workgroup whose row tile has RT rows (8: high/low query
+// parts share one B operand; 16: separate high and low B operands).
+template <int RT>
+struct AttnSharedT {
   uint32_t lut[kPairTable + 4];      // decode table (DevCodebook::pair)
-  uint4 qb[kMaxKB][4][16];           // QK B operand per K-block and lane
-  int32_t row_id[8];
-  int32_t row_len[8];
-  float om[kWaves][8];
-  float ol[kWaves][8];
+  uint4 qb[(RT / 8) * kMaxKB][4][16];  // QK B operand(s) per K-block and lane
+  int32_t row_id[RT];
+  int32_t row_len[RT];
+  float om[kWaves][RT];
+  float ol[kWaves][RT];
   union alignas(16) {
     AttnWave w[kWaves];              // main loop
-    float slot[kWaves][8][kD];       // epilogue: accumulator rows of each wave
+    float slot[kWaves][8][kD];       // epilogue: 8 accumulator rows of each wave at a time
   } u;
 };
+using AttnShared = AttnSharedT<8>;
 
 // 8 codes of rate R (code k at bits [k R, (k + 1) R) of F) -> 8 binary16 centroids, two
 // codes per table read
@@ -1178,11 +1198,162 @@ __device__ inline void attn_block(const AttnShared& S, const AttnWave& W, const 
   __builtin_amdgcn_wave_barrier();
 }
 
-// Phase 1 of the attention: per (row tile, split) online-softmax partials.
-template <int VB, int KWL, int NKB>
+// The same step for a 16-row tile: separate MFMAs for the high and the low query parts
+// (and for the high and low parts of p * nu_V), so that lane (q, n) carries row n alone:
+// no row-mirror adds and no duplicated softmax lanes. Used where many query rows share a
+// KV head (prefill).
+template <int VB, int NKB>
+__device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W, const AttnArgs& a,
+                                    int t0, int lane, int q, int n, int my_len,
+                                    const QkConst<NKB>& C, uint32_t nq_off, uint32_t vn_off,
+                                    floatx4 (&oacc)[8], float& m_run, float& l_run) {
+  const char* sb = reinterpret_cast<const char*>(&S);
+  float lg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lg[j] = 0.f;
+  const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NKB; ++i) {
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(sb + (C.ko[i] >> 5));
+    const uint32_t f0 = __builtin_amdgcn_alignbit(r[1], r[0], C.ko[i]);
+    const uint32_t f1 = __builtin_amdgcn_alignbit(r[4 * kKPitch + 1], r[4 * kKPitch], C.ko[i]);
+    H8 a0, a1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a0.u[j] = lds_u32(sb, C.lb[i] + (__builtin_amdgcn_ubfe(f0, C.w2[i] * j, C.w2[i]) << 2));
+      a1.u[j] = lds_u32(sb, C.lb[i] + (__builtin_amdgcn_ubfe(f1, C.w2[i] * j, C.w2[i]) << 2));
+    }
+    H8 qh, ql;
+    qh.v = S.qb[i][q][n];
+    ql.v = S.qb[kMaxKB + i][q][n];
+    floatx4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qh.h, z4, 0, 0, 0);
+    floatx4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qh.h, z4, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, ql.h, d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, ql.h, d1, 0, 0, 0);
+    const float4 na = *reinterpret_cast<const float4*>(sb + nq_off + C.no[i]);
+    const float4 nb = *reinterpret_cast<const float4*>(sb + nq_off + C.no[i] + 16);
+    lg[0] = fmaf(na.x, d0[0], lg[0]);
+    lg[1] = fmaf(na.y, d0[1], lg[1]);
+    lg[2] = fmaf(na.z, d0[2], lg[2]);
+    lg[3] = fmaf(na.w, d0[3], lg[3]);
+    lg[4] = fmaf(nb.x, d1[0], lg[4]);
+    lg[5] = fmaf(nb.y, d1[1], lg[5]);
+    lg[6] = fmaf(nb.z, d1[2], lg[6]);
+    lg[7] = fmaf(nb.w, d1[3], lg[7]);
+  }
+  // ---- online softmax of row n over tokens t0 + 8q + j
+  const int tb = t0 + 8 * q;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (tb + j >= my_len) lg[j] = -INFINITY;
+  if (a.logits) {
+    const int id = S.row_id[n];
+    if (id >= 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (tb + j < my_len) a.logits[(size_t)id * a.logits_ld + tb + j] = lg[j] * LN2_F;
+    }
+  }
+  float mblk = lg[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mblk = fmaxf(mblk, lg[j]);
+  mblk = max_over_q(mblk);
+  const bool grow = mblk > m_run;
+  if (__any(grow)) {
+    const float m_new = grow ? mblk : m_run;
+    const bool rescale = grow && m_run != -INFINITY;
+    if (__any(rescale)) {
+      const float f = rescale ? exp2f(m_run - m_new) : 1.f;
+      l_run *= f;
+      // accumulator rows 4q + e live in lanes with n == row: fetch their factors
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fe = __shfl(f, 4 * q + e);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) oacc[t][e] *= fe;
+      }
+    }
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  const float4 va = *reinterpret_cast<const float4*>(sb + vn_off);
+  const float4 vb4 = *reinterpret_cast<const float4*>(sb + vn_off + 16);
+  const float vn[8] = {va.x, va.y, va.z, va.w, vb4.x, vb4.y, vb4.z, vb4.w};
+  float pv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = (lg[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[j] - m_use);
+    l_run += p;
+    pv[j] = (p == 0.f) ? 0.f : p * vn[j];
+  }
+  H8 ph, pl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto hh = __builtin_amdgcn_cvt_pkrtz(pv[2 * k], pv[2 * k + 1]);
+    const auto ll = __builtin_amdgcn_cvt_pkrtz(pv[2 * k] - (float)hh[0], pv[2 * k + 1] - (float)hh[1]);
+    ph.u[k] = __builtin_bit_cast(uint32_t, hh);
+    pl.u[k] = __builtin_bit_cast(uint32_t, ll);
+  }
+  // ---- PV over the 8 value tiles, high and low parts of p * nu_V
+  uint32_t vw[2 * VB];
+#pragma unroll
+  for (int i = 0; i < (2 * VB + 3) / 4; ++i) {
+    const uint4 x = W.vcodes[i][lane];
+    vw[4 * i] = x.x;
+    if (4 * i + 1 < 2 * VB) vw[4 * i + 1] = x.y;
+    if (4 * i + 2 < 2 * VB) vw[4 * i + 2] = x.z;
+    if (4 * i + 3 < 2 * VB) vw[4 * i + 3] = x.w;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const half8 bv = dequant8<VB>(S.lut, vfield<VB>(vw, t));
+    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph.h, bv, oacc[t], 0, 0, 0);
+    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl.h, bv, oacc[t], 0, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One partial (m, l, acc) per row for this split, for rows r0 .. r0 + 7 of the tile: the
+// waves' (m, l) and accumulator rows (staged in the shared slots) merged by their
+// log-sum-exp weights.
+template <int RT>
+__device__ inline void write_partials(const AttnArgs& a, const AttnSharedT<RT>& S, int tid, int r0, int chunk_idx) {
+  if (tid < 8 * (kD / 4)) {
+    const int r8 = tid >> 5, c4 = tid & 31;
+    const int r = r0 + r8;
+    const int id = S.row_id[r];
+    if (id >= 0) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.om[w][r]);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float l = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = S.om[w][r];
+          const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+          const float4 x = *reinterpret_cast<const float4*>(&S.u.slot[w][r8][4 * c4]);
+          acc.x = fmaf(sw, x.x, acc.x);
+          acc.y = fmaf(sw, x.y, acc.y);
+          acc.z = fmaf(sw, x.z, acc.z);
+          acc.w = fmaf(sw, x.w, acc.w);
+          l = fmaf(sw, S.ol[w][r], l);
+        }
+      }
+      float* dst = a.partials + ((size_t)id * a.n_chunks + chunk_idx) * kPS;
+      *reinterpret_cast<float4*>(dst + 4 + 4 * c4) = acc;
+      if (c4 == 0) *reinterpret_cast<float4*>(dst) = make_float4(M, l, 0.f, 0.f);
+    }
+  }
+}
+
+// Phase 1 of the attention: per (row tile of RT rows, split) online-softmax partials.
 // (at most 128 registers: two workgroups per compute unit)
+template <int VB, int KWL, int NKB, int RT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) attn_partials_kernel(AttnArgs a) {
-  __shared__ AttnShared S;
+  constexpr int kTileQB = (RT / 8) * kQB;
+  __shared__ AttnSharedT<RT> S;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
@@ -1203,9 +1374,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const int voff_v = 4 * (q * (32 * VB) + n * (2 * VB));
   const int c0 = chunk_idx * a.chunk;
   // ---- one round of independent loads: B operand, decode table, rows, first block
-  uint4 qbv[kQB / kThreads];
+  uint4 qbv[kTileQB / kThreads];
 #pragma unroll
-  for (int u = 0; u < kQB / kThreads; ++u) qbv[u] = a.qb[(size_t)tile * kQB + tid + kThreads * u];
+  for (int u = 0; u < kTileQB / kThreads; ++u) qbv[u] = a.qb[(size_t)tile * kTileQB + tid + kThreads * u];
   uint32_t lutv[(kPairTable + kThreads - 1) / kThreads];
 #pragma unroll
   for (int u = 0; u < (kPairTable + kThreads - 1) / kThreads; ++u) {
@@ -1216,26 +1387,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   BlockData<VB, KWL> blk[1];
   load_block<VB, KWL>(blk[0], R, c0 + kBlk * wave, kw, lane, voff_v);
 #pragma unroll
-  for (int u = 0; u < kQB / kThreads; ++u) (&S.qb[0][0][0])[tid + kThreads * u] = qbv[u];
+  for (int u = 0; u < kTileQB / kThreads; ++u) (&S.qb[0][0][0])[tid + kThreads * u] = qbv[u];
 #pragma unroll
   for (int u = 0; u < (kPairTable + kThreads - 1) / kThreads; ++u) {
     const int e = tid + kThreads * u;
     if (e < kPairTable) S.lut[e] = lutv[u];
   }
-  if (tid < 8) {
+  if (tid < RT) {
     int L;
-    S.row_id[tid] = tile_row(a, seq, h, tr, tid, len_ld, &L);
+    S.row_id[tid] = tile_row<RT>(a, seq, h, tr, tid, len_ld, &L);
     S.row_len[tid] = L;
   }
   __syncthreads();
   int tile_len = 0;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) tile_len = max(tile_len, S.row_len[r]);
+  for (int r = 0; r < RT; ++r) tile_len = max(tile_len, S.row_len[r]);
   if (c0 >= tile_len) return;  // no cached token of this tile in this split
   const int c1 = min(c0 + a.chunk, tile_len);
   constexpr int kStep = kBlk * kWaves;
 
-  const int my_row = n < 8 ? n : 15 - n;
+  const int my_row = RT == 16 ? n : (n < 8 ? n : 15 - n);
   const int my_len = S.row_len[my_row];
   AttnWave& W = S.u.w[wave];
   const char* sb = reinterpret_cast<const char*>(&S);
@@ -1261,7 +1432,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     C.no[i] = grp * kBlk * 4;
   }
   const uint32_t nq_off = (uint32_t)(reinterpret_cast<const char*>(&W.knt[0][8 * q]) - sb);
-  const uint32_t vn_off = (uint32_t)(reinterpret_cast<const char*>(&W.vn[8 * q + (n >= 8 ? 4 : 0)]) - sb);
+  // value norms: the four tokens this lane finishes (8-row tiles) or all eight (16-row)
+  const uint32_t vn_off =
+      (uint32_t)(reinterpret_cast<const char*>(&W.vn[8 * q + (RT == 8 && n >= 8 ? 4 : 0)]) - sb);
 
   floatx4 oacc[8];
 #pragma unroll
@@ -1273,59 +1446,59 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     stage_block<VB, KWL>(W, blk[0], kw, lane, st);
     __builtin_amdgcn_wave_barrier();
     if (t0 + kStep < c1) load_block<VB, KWL>(blk[0], R, t0 + kStep, kw, lane, voff_v);
-    attn_block<VB, NKB>(S, W, a, t0, lane, q, n, my_row, my_len, C, nq_off, vn_off, oacc, m_run, l_run);
+    if constexpr (RT == 8)
+      attn_block<VB, NKB>(S, W, a, t0, lane, q, n, my_row, my_len, C, nq_off, vn_off, oacc, m_run, l_run);
+    else
+      attn_block16<VB, NKB>(S, W, a, t0, lane, q, n, my_len, C, nq_off, vn_off, oacc, m_run, l_run);
   }
 
-  // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves
-  l_run += dpp_row_mirror(l_run);  // the two lanes of a row summed different tokens
-  l_run = sum_over_q(l_run);
-  if (q == 0 && n < 8) {
-    S.om[wave][n] = m_run;
-    S.ol[wave][n] = l_run;
-  }
-  // combined rows 4q + e (q < 2): own high row plus the low row held by lane l ^ 48
-  float vrow[8][4];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
-  }
-  __syncthreads();  // every wave is done with its key tile
-  if (q < 2) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float* dst = &S.u.slot[wave][4 * q + e][8 * n];
-      *reinterpret_cast<float4*>(dst) = make_float4(vrow[0][e], vrow[1][e], vrow[2][e], vrow[3][e]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(vrow[4][e], vrow[5][e], vrow[6][e], vrow[7][e]);
+  if constexpr (RT == 8) {
+    // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves
+    l_run += dpp_row_mirror(l_run);  // the two lanes of a row summed different tokens
+    l_run = sum_over_q(l_run);
+    if (q == 0 && n < 8) {
+      S.om[wave][n] = m_run;
+      S.ol[wave][n] = l_run;
     }
-  }
-  __syncthreads();
-  // ---- one partial (m, l, acc) per row for this split
-  if (tid < 8 * (kD / 4)) {
-    const int r = tid >> 5, c4 = tid & 31;
-    const int id = S.row_id[r];
-    if (id >= 0) {
-      float M = -INFINITY;
+    // combined rows 4q + e (q < 2): own high row plus the low row held by lane l ^ 48
+    float vrow[8][4];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.om[w][r]);
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      float l = 0.f;
-      if (M != -INFINITY) {
+    for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float mw = S.om[w][r];
-          const float s = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-          const float4 x = *reinterpret_cast<const float4*>(&S.u.slot[w][r][4 * c4]);
-          acc.x = fmaf(s, x.x, acc.x);
-          acc.y = fmaf(s, x.y, acc.y);
-          acc.z = fmaf(s, x.z, acc.z);
-          acc.w = fmaf(s, x.w, acc.w);
-          l = fmaf(s, S.ol[w][r], l);
+      for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
+    }
+    __syncthreads();  // every wave is done with its key tile
+    if (q < 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float* dst = &S.u.slot[wave][4 * q + e][8 * n];
+        *reinterpret_cast<float4*>(dst) = make_float4(vrow[0][e], vrow[1][e], vrow[2][e], vrow[3][e]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(vrow[4][e], vrow[5][e], vrow[6][e], vrow[7][e]);
+      }
+    }
+    __syncthreads();
+    write_partials<RT>(a, S, tid, 0, chunk_idx);
+  } else {
+    // ---- epilogue, 16 rows: lane (q, n) holds row n (its l over its own tokens) and the
+    //      accumulator rows 4q + e; two rounds of 8 rows through the shared slots
+    l_run = sum_over_q(l_run);
+    if (q == 0) {
+      S.om[wave][n] = m_run;
+      S.ol[wave][n] = l_run;
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      __syncthreads();  // hf 0: every wave is done with its stage; hf 1: round 0 was read
+      if ((q >> 1) == hf) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float* dst = &S.u.slot[wave][4 * (q & 1) + e][8 * n];
+          *reinterpret_cast<float4*>(dst) = make_float4(oacc[0][e], oacc[1][e], oacc[2][e], oacc[3][e]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(oacc[4][e], oacc[5][e], oacc[6][e], oacc[7][e]);
         }
       }
-      float* dst = a.partials + ((size_t)id * a.n_chunks + chunk_idx) * kPS;
-      *reinterpret_cast<float4*>(dst + 4 + 4 * c4) = acc;
-      if (c4 == 0) *reinterpret_cast<float4*>(dst) = make_float4(M, l, 0.f, 0.f);
+      __syncthreads();
+      write_partials<RT>(a, S, tid, 8 * hf, chunk_idx);
     }
   }
 }
@@ -1682,15 +1855,20 @@ int auto_chunk(int64_t max_len, int64_t tiles) {
 }
 
 // workspace: the tiles' QK B operands, then the partials
-size_t attn_qb_bytes(int64_t n_tiles) { return (size_t)n_tiles * kQB * sizeof(uint4); }
-size_t attn_ws_bytes(int64_t rows, int64_t n_chunks, int64_t n_tiles) {
-  return attn_qb_bytes(n_tiles) + (size_t)rows * n_chunks * kPS * 4;
+// rotated-query operands of n_tiles row tiles of rt rows (8 KB per 8 rows)
+size_t attn_qb_bytes(int64_t n_tiles, int rt) { return (size_t)n_tiles * (rt / 8) * kQB * sizeof(uint4); }
+size_t attn_ws_bytes(int64_t rows, int64_t n_chunks, size_t qb_bytes) {
+  return qb_bytes + (size_t)rows * n_chunks * kPS * 4;
 }
 
 struct AttnLaunch {
   int64_t rows;
-  int tiles_per_kv;
+  int rt;                  // rows per partials tile: 8 (decode) or 16 (prefill)
+  int tiles_per_kv;        // partials / query-rotation tiles
   int n_tiles;
+  int merge_tiles_per_kv;  // 8-row tiles of the merge
+  int merge_n_tiles;
+  size_t qb_bytes;         // rotated-query operands at the start of the workspace
   int chunk;
   int n_chunks;
 };
@@ -1705,7 +1883,7 @@ void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnA
   aa.v_codes = c->v_codes;
   aa.v_norms = c->v_norms;
   aa.qb = reinterpret_cast<uint4*>(ws);
-  aa.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + attn_qb_bytes(L.n_tiles));
+  aa.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + L.qb_bytes);
   aa.capacity = c->capacity;
   aa.n_kv = p->n_kv;
   aa.n_q = p->n_q;
@@ -1721,7 +1899,10 @@ void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnA
 gtq_status launch_qrot(AttnArgs& aa, const AttnLaunch& L, const float* q, float scale, hipStream_t stream) {
   aa.q = q;
   aa.qscale = scale * LOG2E_F;
-  hipLaunchKernelGGL(attn_qrot_kernel, dim3(L.n_tiles), dim3(64 * kQrotWaves), 0, stream, aa);
+  if (L.rt == 16)
+    hipLaunchKernelGGL(attn_qrot_kernel<16>, dim3(L.n_tiles), dim3(64 * kQrotWaves), 0, stream, aa);
+  else
+    hipLaunchKernelGGL(attn_qrot_kernel<8>, dim3(L.n_tiles), dim3(64 * kQrotWaves), 0, stream, aa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq attention query rotation: launch");
   return ok();
@@ -1735,7 +1916,9 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
   // layer's largest count (extra K-blocks of a head have zero query operands)
   const int nkb = aa.nkb_max;
   if (nkb < 4 || nkb > 7) return fail(GTQ_EUNSUPPORTED, "gtq attention: K-block count outside 4..7");
-#define GTQ_LAUNCH3(VB, KWL, NKB) hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB>), grid, dim3(kThreads), 0, stream, aa)
+#define GTQ_LAUNCH3(VB, KWL, NKB)                                                                              \
+  if (L.rt == 16) hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 16>), grid, dim3(kThreads), 0, stream, aa); \
+  else hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 8>), grid, dim3(kThreads), 0, stream, aa)
 #define GTQ_LAUNCH2(VB, KWL)                  \
   switch (nkb) {                              \
     case 4: GTQ_LAUNCH3(VB, KWL, 4); break;   \
@@ -1763,11 +1946,11 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
                         int64_t pos0, int prefill, int max_len, float* out, const void* ws,
                         hipStream_t stream) {
   const float* vrot_t = p->d_rot + p->heads[(size_t)layer * p->n_kv].vrot_t_off;
-  const float* partials = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + attn_qb_bytes(L.n_tiles));
+  const float* partials = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + L.qb_bytes);
   if (L.n_chunks <= kMergeTileChunks) {  // one workgroup per row tile
-    MergeTileArgs mt{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, p->n_kv, L.tiles_per_kv,
+    MergeTileArgs mt{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, p->n_kv, L.merge_tiles_per_kv,
                      (int32_t)(L.rows / p->n_q), L.n_chunks, L.chunk, prefill, max_len, 0};
-    hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.n_tiles), dim3(256), 0, stream, mt);
+    hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.merge_n_tiles), dim3(256), 0, stream, mt);
   } else {  // one workgroup per row
     MergeArgs ma{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill,
                  max_len};
@@ -1896,8 +2079,12 @@ static bool decode_shape(const gtq_plan* p, int32_t batch, int64_t max_len, int3
   }
   const int g = p->n_q / p->n_kv;
   L->rows = (int64_t)batch * p->n_q;
+  L->rt = 8;
   L->tiles_per_kv = (g + 7) / 8;
   L->n_tiles = batch * p->n_kv * L->tiles_per_kv;
+  L->merge_tiles_per_kv = L->tiles_per_kv;
+  L->merge_n_tiles = L->n_tiles;
+  L->qb_bytes = attn_qb_bytes(L->n_tiles, L->rt);
   L->chunk = chunk ? chunk : auto_chunk(max_len, L->n_tiles);
   L->n_chunks = (int)std::max<int64_t>(1, (max_len + L->chunk - 1) / L->chunk);
   if (L->n_chunks > kMaxChunks) {
@@ -1914,7 +2101,7 @@ gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64
   AttnLaunch L;
   gtq_status st;
   if (!decode_shape(plan, batch, max_len, chunk, &L, &st, "gtq_decode_workspace_bytes")) return st;
-  *out = attn_ws_bytes(L.rows, L.n_chunks, L.n_tiles);
+  *out = attn_ws_bytes(L.rows, L.n_chunks, L.qb_bytes);
   return ok();
 }
 
@@ -1928,7 +2115,7 @@ static gtq_status decode_check(const gtq_plan* plan, int32_t layer, const gtq_ca
   if (!ws) return fail(GTQ_EINVAL, std::string(fn) + ": workspace is NULL");
   if (max_len > cache->capacity) return fail(GTQ_ECAPACITY, std::string(fn) + ": max_len > capacity");
   if (!decode_shape(plan, cache->batch, max_len, chunk, L, &st, fn)) return st;
-  if (ws_bytes < attn_ws_bytes(L->rows, L->n_chunks, L->n_tiles))
+  if (ws_bytes < attn_ws_bytes(L->rows, L->n_chunks, L->qb_bytes))
     return fail(GTQ_ECAPACITY, std::string(fn) + ": workspace too small");
   return GTQ_OK;
 }
@@ -2051,8 +2238,13 @@ static bool prefill_shape(const gtq_plan* p, int64_t pos0, int64_t n_tok, int32_
   const int g = p->n_q / p->n_kv;
   const int64_t total = pos0 + n_tok;
   L->rows = n_tok * p->n_q;
-  L->tiles_per_kv = (int)((n_tok * g + 7) / 8);
+  // prefill: tiles of 16 query rows (a KV head's rows are many), merged in tiles of 8
+  L->rt = 16;
+  L->tiles_per_kv = (int)((n_tok * g + 15) / 16);
   L->n_tiles = p->n_kv * L->tiles_per_kv;
+  L->merge_tiles_per_kv = (int)((n_tok * g + 7) / 8);
+  L->merge_n_tiles = p->n_kv * L->merge_tiles_per_kv;
+  L->qb_bytes = attn_qb_bytes(L->n_tiles, L->rt);
   L->chunk = chunk ? chunk : auto_chunk(total, L->n_tiles);
   L->n_chunks = (int)((total + L->chunk - 1) / L->chunk);
   if (L->n_chunks > kMaxChunks) {
@@ -2068,7 +2260,7 @@ gtq_status gtq_prefill_workspace_bytes(const gtq_plan* plan, int64_t pos0, int64
   AttnLaunch L;
   gtq_status st;
   if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_workspace_bytes")) return st;
-  *out = attn_ws_bytes(L.rows, L.n_chunks, L.n_tiles);
+  *out = attn_ws_bytes(L.rows, L.n_chunks, L.qb_bytes);
   return ok();
 }
 
@@ -2086,7 +2278,7 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
   AttnLaunch L;
   if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_attn")) return st;
   if (pos0 + n_tok > cache->capacity) return fail(GTQ_ECAPACITY, "gtq_prefill_attn: pos0 + n_tok > capacity");
-  if (ws_bytes < attn_ws_bytes(L.rows, L.n_chunks, L.n_tiles))
+  if (ws_bytes < attn_ws_bytes(L.rows, L.n_chunks, L.qb_bytes))
     return fail(GTQ_ECAPACITY, "gtq_prefill_attn: workspace too small");
   AttnArgs aa{};
   fill_attn_args(plan, layer, cache, aa, L, workspace);
