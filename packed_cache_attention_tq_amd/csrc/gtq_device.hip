@@ -157,12 +157,14 @@ struct AppendGemmShared {
   float thr[5][16];                   // quantizer thresholds by rate
 };
 
-// OR over the 16 lanes of a row: DPP row operations
+// OR over the 16 lanes of a row: DPP row operations. update_dpp with bound_ctrl (every
+// source lane of these patterns is inside the row) lets the compiler fuse each step
+// into one v_or_b32_dpp.
 __device__ inline uint32_t row_or_u32(uint32_t v) {
-  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
-  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
-  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
-  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // row mirror
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);   // quad [1,0,3,2]
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);   // quad [2,3,0,1]
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true);  // half-row mirror
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true);  // row mirror
   return v;
 }
 
@@ -731,8 +733,9 @@ __device__ inline int tile_row(const AttnArgs& a, int seq, int h, int tr, int r,
   return id;
 }
 
+// value of lane 15 - i of the same 16-lane row (fusable into the consuming VALU op)
 __device__ inline float dpp_row_mirror(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
 }
 
 // Lane swaps of gfx950. v_permlane16_swap(x, y) exchanges the odd 16-lane rows of x
