@@ -46,7 +46,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--workload", default="decode-8b",
-                   choices=["decode-8b", "decode-3b-36L", "decode-70b-b32", "append-32b", "prefill-32b"],
+                   choices=["decode-8b", "decode-3b-36L", "decode-70b-b32", "append-32b", "prefill-32b",
+                            "logit-mae"],
                    help="decode-8b (default, the headline): Llama-3.1-8B-shaped layer decode; the others "
                         "measure the other workload shapes (one JSON line each)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -340,6 +341,63 @@ def bench_prefill(args):
     }
 
 
+def bench_logit_mae(args):
+    """K-only logit error of Block-GTQ (greedy per-block rates) against uniform TQ-MSE
+    (every block at the same rate), at 2 and 3 average key bits: one Llama-3.1-8B-shaped
+    layer (8 KV heads, g = 4), 8192 cached tokens. The logits come from the packed-cache
+    decode kernel's logits output and are compared with exact fp32 logits of the
+    unquantized keys (mean absolute error over queries and tokens)."""
+    import torch
+
+    import packed_cache_attention_tq_amd as G
+    from gtq_inputs import head_inputs, head_inputs_device, head_rotations
+
+    h_kv, g, n, vb = 8, 4, 8192, 2
+    scale = 1.0 / math.sqrt(128)
+    D = G.gtq_rate_distortion(4)
+    out = {}
+    for bits in (2, 3):
+        for mode in ("block-gtq", "uniform"):
+            rates, krot, vrot, prox = [], [], [], 0.0
+            for h in range(h_kv):
+                inp = head_inputs(args.seed, 0, h, g, 0)
+                r, sc, px = G.gtq_alloc_rates(inp["calib_q"], inp["calib_k"], 1, 4, 64 * bits)
+                if mode == "uniform":
+                    r = np.full(64, bits, np.uint8)
+                    px = float(np.sum(sc * D[bits]))
+                prox += px
+                kr, vr = head_rotations(args.seed, 0, h, G.gtq_head_layout_from_rates(r)["dim"])
+                rates.append(r)
+                krot.append(kr)
+                vrot.append(vr)
+            plan = G.Plan(1, h_kv, h_kv * g, 64 * bits, vb, np.array(rates)[None], [krot], np.array(vrot)[None])
+            cache = G.PackedCache(plan, 1, n)
+            ds = [head_inputs_device(args.seed, 0, h, g, n, "cuda") for h in range(h_kv)]
+            k = torch.stack([d["k"] for d in ds], 1).contiguous()
+            v = torch.stack([d["v"] for d in ds], 1).contiguous()
+            q = torch.cat([d["q"][0] for d in ds], 0)[None].contiguous()
+            G.gtq_quantize_append_chunk(plan, 0, cache, k, v, 0, 0)
+            logits = torch.zeros(1, h_kv * g, n, device="cuda")
+            G.gtq_decode_attn(plan, 0, cache, q, torch.full((1,), n, dtype=torch.int32, device="cuda"), n, scale,
+                              logits=logits)
+            exact = torch.cat([(q[0, h * g:(h + 1) * g] @ k[:, h].T) * scale for h in range(h_kv)], 0)
+            err = (logits[0] - exact).abs()
+            out[f"K{bits}_{mode}"] = {"logit_mae": round(float(err.mean()), 6),
+                                      "logit_max_err": round(float(err.max()), 5),
+                                      "proxy_sum_s_D": round(prox, 6)}
+            del cache, k, v, logits, exact
+            plan.destroy()
+    ratio = out["K2_uniform"]["logit_mae"] / out["K2_block-gtq"]["logit_mae"]
+    return {
+        "metric": "K-only logit MAE, Block-GTQ rates vs uniform TQ-MSE (ratio uniform / Block-GTQ at 2 bits)",
+        "value": round(ratio, 4), "unit": "x", "n_gpus": 1, "steps": 1, "warmup": 0, "ms_per_step": None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 logits from the packed cache vs f32 exact", "data": "synthetic",
+        "config": {"workload": "logit-mae", "kv_heads": h_kv, "q_heads": h_kv * g, "tokens": n},
+        "results": out,
+    }
+
+
 def cpu_baseline(w, seed, min_seconds=10.0):
     """The fp64 oracle on the whole step (1-token encode + decode of all 32 query heads over
     every cached token, 8 KV heads), repeated until at least min_seconds of CPU time."""
@@ -393,7 +451,8 @@ def main():
     if args.workload != "decode-8b":
         fn = {"decode-3b-36L": lambda: bench_decode_stack(args, "decode-3b-36L"),
               "decode-70b-b32": lambda: bench_decode_stack(args, "decode-70b-b32"),
-              "append-32b": lambda: bench_append(args), "prefill-32b": lambda: bench_prefill(args)}[args.workload]
+              "append-32b": lambda: bench_append(args), "prefill-32b": lambda: bench_prefill(args),
+              "logit-mae": lambda: bench_logit_mae(args)}[args.workload]
         print(json.dumps(fn()), flush=True)
         return
     t_setup = time.perf_counter()
