@@ -189,11 +189,18 @@ def groups_from_rates(rates, layout: int = HALF) -> list[tuple[int, np.ndarray]]
 # TQ-MSE encode / dequantize  [TQ-diag input -> rotate -> scalar-MSE], [BGTQ s5]
 # --------------------------------------------------------------------------
 
-def encode(x: np.ndarray, rot: np.ndarray, bits: int):
+def encode(x: np.ndarray, rot: np.ndarray, bits: int, nc: bool = False):
     """Encode rows of x [n, d] (fp32 input) with rotation rot [d, d] (fp32 entries).
 
     nu = sqrt(sum x_i^2) in fp64, stored fp32; u = x / nu; z = sqrt(d) * rot @ u;
-    code_i = #{k : z_i >= t_k}. Returns (nu fp32 [n], codes int64 [n, d], z fp64 [n, d])."""
+    code_i = #{k : z_i >= t_k}. Returns (stored norm fp32 [n], codes int64 [n, d],
+    z fp64 [n, d]).
+
+    nc (the norm-corrected variant named in the TurboQuant page's vLLM preset column):
+    the stored norm is nu * sqrt(d) / ||C[code]|| instead of nu, so that the decoded
+    vector nu_stored * rot^T C[code] / sqrt(d) has norm nu exactly (rot is orthogonal).
+    It is evaluated in fp64 as (nu * sqrt(d)) / sqrt(sum_i C[code_i]^2) and rounded to
+    fp32; the sum is exact in any order (binary16 centroids, at most 128 terms)."""
     x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
     if x64.ndim == 1:
         x64 = x64[None, :]
@@ -207,6 +214,11 @@ def encode(x: np.ndarray, rot: np.ndarray, bits: int):
     codes = np.zeros((n, d), dtype=np.int64)
     for tk in t:
         codes += (z >= tk)
+    if nc:
+        c16, _ = codebook(bits)
+        ssq = np.sum(c16[codes] ** 2, axis=1)
+        stored = np.where(nu > 0.0, nu * math.sqrt(d) / np.sqrt(ssq), 0.0)
+        return stored.astype(np.float32), codes, z
     return nu.astype(np.float32), codes, z
 
 
@@ -272,9 +284,10 @@ class HeadPlan:
     """Rates, groups, rotations and V rate of one (layer, KV head)."""
 
     def __init__(self, rates, k_rots: list[np.ndarray], v_rot: np.ndarray, v_bits: int,
-                 layout: int = HALF):
+                 layout: int = HALF, nc: bool = False):
         self.rates = np.asarray(rates, dtype=np.int64)
         self.layout = layout
+        self.nc = bool(nc)  # norm-corrected stored norms (see encode)
         self.groups = groups_from_rates(self.rates, layout)
         if len(k_rots) != len(self.groups):
             raise ValueError("one K rotation per group")
@@ -299,11 +312,11 @@ def encode_kv(plan: HeadPlan, k: np.ndarray, v: np.ndarray) -> dict:
     (K words, K norms per group, V words, V norm) [BGTQ s5], [TQ-diag]."""
     kn, kc, kz = [], [], []
     for (r, coords), rot in zip(plan.groups, plan.k_rots):
-        nu, codes, z = encode(np.asarray(k)[:, coords], rot, r)
+        nu, codes, z = encode(np.asarray(k)[:, coords], rot, r, nc=plan.nc)
         kn.append(nu)
         kc.append(codes)
         kz.append(z)
-    vn, vc, vz = encode(v, plan.v_rot, plan.v_bits)
+    vn, vc, vz = encode(v, plan.v_rot, plan.v_bits, nc=plan.nc)
     return dict(k_words=pack_codes(kc, plan.group_rates), k_norms=np.stack(kn, axis=1),
                 v_words=pack_codes([vc], [plan.v_bits]), v_norms=vn,
                 k_codes=kc, k_z=kz, v_codes=vc, v_z=vz)

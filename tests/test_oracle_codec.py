@@ -147,6 +147,42 @@ def test_unit_vector_distortion_near_gaussian(bits):
     assert np.mean(err) == pytest.approx(O.rate_distortion()[bits], rel=0.03)
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_norm_corrected_reconstruction_keeps_the_norm(bits):
+    """Norm-corrected variant: the decoded vector has the input's norm (up to the fp32
+    rounding of the stored norm), the codes are those of the plain variant, and the
+    plain variant's reconstruction is shorter on average (a Lloyd-Max quantizer keeps
+    E[C^2] = 1 - D(b) of the energy)."""
+    rng = np.random.default_rng(200 + bits)
+    d = 40
+    rot = haar_rotation(d, rng)
+    x = (rng.standard_normal((200, d)) * 2.5).astype(np.float32)
+    nu_p, c_p, _ = O.encode(x, rot, bits)
+    nu_c, c_c, _ = O.encode(x, rot, bits, nc=True)
+    assert np.array_equal(c_p, c_c)
+    x64 = x.astype(np.float64)
+    true = np.linalg.norm(x64, axis=1)
+    rec_c = np.linalg.norm(O.dequantize(nu_c, c_c, rot, bits), axis=1)
+    rec_p = np.linalg.norm(O.dequantize(nu_p, c_p, rot, bits), axis=1)
+    assert np.allclose(rec_c, true, rtol=2e-7, atol=0)
+    assert np.mean(rec_p ** 2 / true ** 2) == pytest.approx(1 - O.rate_distortion()[bits], abs=0.04)
+
+
+def test_norm_corrected_one_bit_closed_form():
+    """At 1 bit every centroid has magnitude c1, so ||C[code]|| = sqrt(d) c1 and the
+    stored norm is nu / c1 whatever the codes are."""
+    rng = np.random.default_rng(9)
+    d = 24
+    rot = haar_rotation(d, rng)
+    x = rng.standard_normal((64, d)).astype(np.float32)
+    nu_c, _, _ = O.encode(x, rot, 1, nc=True)
+    c1 = O.codebook(1)[0][1]
+    ref = (np.linalg.norm(x.astype(np.float64), axis=1) / c1).astype(np.float32)
+    d_ulp = np.abs(nu_c.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert d_ulp.max() <= 1
+    assert O.encode(np.zeros((1, d), np.float32), rot, 1, nc=True)[0][0] == 0.0
+
+
 def test_haar_rotations_orthogonal():
     rng = np.random.default_rng(5)
     for d in (2, 6, 40, 128):
