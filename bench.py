@@ -50,6 +50,8 @@ def parse():
                             "logit-mae"],
                    help="decode-8b (default, the headline): Llama-3.1-8B-shaped layer decode; the others "
                         "measure the other workload shapes (one JSON line each)")
+    p.add_argument("--norm-correct", action="store_true",
+                   help="append-32b: plan with norm-corrected stored norms (GTQ_PLAN_NORM_CORRECT)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run a plain device copy (torch.neg) of this many MiB three "
                         "times: a kernel of known traffic that calibrates the HBM byte counters")
@@ -109,7 +111,7 @@ def partials_kernel_name(plan, layer, h_kv, v_bits):
     return f"attn_partials_kernel<{v_bits}, {kwl}, {nkb}>"
 
 
-def make_plan(seed, n_layers, h_kv, g, k_budget, v_bits, share_layer0=False):
+def make_plan(seed, n_layers, h_kv, g, k_budget, v_bits, share_layer0=False, nc=False):
     """A plan with library-allocated rates (from each head's calibration set) and Haar
     rotations; with share_layer0 every layer reuses layer 0's rates and rotations."""
     import packed_cache_attention_tq_amd as G
@@ -133,7 +135,7 @@ def make_plan(seed, n_layers, h_kv, g, k_budget, v_bits, share_layer0=False):
             vl.append(vr)
         krot.append(kl)
         vrot.append(vl)
-    return G.Plan(n_layers, h_kv, h_kv * g, k_budget, v_bits, rates, krot, np.array(vrot))
+    return G.Plan(n_layers, h_kv, h_kv * g, k_budget, v_bits, rates, krot, np.array(vrot), norm_correct=nc)
 
 
 def fill_layer(plan, layer, cache, seed, h_kv, g, lengths, gen_layer=None):
@@ -262,7 +264,7 @@ def bench_append(args):
     from gtq_inputs import head_inputs_device
 
     h_kv, g, kb, vb, chunk, total = 8, 5, 192, 2, 4096, 65536
-    plan = make_plan(args.seed, 1, h_kv, g, kb, vb)
+    plan = make_plan(args.seed, 1, h_kv, g, kb, vb, nc=args.norm_correct)
     cache = G.PackedCache(plan, 1, total)
     ks = torch.stack([head_inputs_device(args.seed, 0, h, g, total, "cuda", with_q=False)["k"] for h in range(h_kv)], 1)
     vs = torch.stack([head_inputs_device(args.seed, 0, h, g, total, "cuda", with_q=False)["v"] for h in range(h_kv)], 1)
@@ -288,7 +290,7 @@ def bench_append(args):
         "warmup": 16, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32 in; binary16 hi/lo split MFMA; u32 packed codes", "data": "synthetic",
         "config": {"workload": "append-32b", "chunk_tokens": chunk, "kv_heads": h_kv, "k_bits_avg": kb / 64,
-                   "v_bits": vb, "prompt": total},
+                   "v_bits": vb, "prompt": total, "norm_correct": bool(args.norm_correct)},
         "roofline": {"bound": "hbm", "achieved": round(alg / (ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "append_gemm_kernel", "alg_bytes_per_launch": int(alg)},

@@ -120,7 +120,15 @@ gtq_status gtq_head_layout_from_rates(const uint8_t* rates, int32_t rope_layout,
 
 /* ---------------------------------------------------------------- plans */
 
-enum { GTQ_PLAN_HOST_ONLY = 1 /* build and validate on the host, no device copy */ };
+enum {
+  GTQ_PLAN_HOST_ONLY = 1,     /* build and validate on the host, no device copy           */
+  GTQ_PLAN_NORM_CORRECT = 2   /* norm-corrected variant ("TurboQuant: paper algorithm
+                                 and vLLM engineering" diagram, vLLM column, NC box): the
+                                 stored norm of every key group and of the value is
+                                 nu * sqrt(d) / ||C[code]|| (fp64, rounded to fp32), so
+                                 that the decoded vector keeps the input's norm; codes and
+                                 the attention are unchanged                               */
+};
 
 typedef struct gtq_plan_desc {
   int32_t n_layers, n_kv_heads, n_q_heads; /* n_q_heads a multiple of n_kv_heads      */
@@ -128,7 +136,7 @@ typedef struct gtq_plan_desc {
   int32_t rope_layout;                     /* GTQ_ROPE_HALF | GTQ_ROPE_INTERLEAVED     */
   int32_t k_budget;                        /* sum_j b_j of every head (128 = K2, 192 = K3) */
   int32_t v_bits;                          /* 1..4, values are one 128-dim group       */
-  int32_t flags;                           /* GTQ_PLAN_HOST_ONLY or 0                 */
+  int32_t flags;                           /* GTQ_PLAN_HOST_ONLY | GTQ_PLAN_NORM_CORRECT */
   const uint8_t* k_rates; /* host [n_layers][n_kv_heads][64], each head summing to k_budget */
   const float* k_rot;     /* host: for l, h, groups in ascending rate: the group's d x d
                              rotation, row-major fp32, concatenated (each head's slice is

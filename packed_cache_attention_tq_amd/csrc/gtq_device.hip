@@ -73,6 +73,7 @@ struct AppendArgs {
   int32_t n_kv;
   int32_t k_words;
   int32_t v_bits;
+  int32_t nc;  // norm-corrected stored norms: nu * sqrt(d) / ||C[code]||
 };
 
 __device__ inline int quantize(float z, const float* thr, int n_thr) {
@@ -155,7 +156,17 @@ struct AppendGemmShared {
   uint32_t pv[4][128];                // packed value blocks of the tile (8 tokens each)
   float nu[kAppTile][5];              // fp32 norms per token: key groups 0..3, value 4
   float thr[5][16];                   // quantizer thresholds by rate
+  float cen[5][16];                   // centroids by rate (norm-corrected variant)
+  double nu64[kAppTile][5];           // fp64 norms (norm-corrected variant)
+  double cs[kAppTile][5];             // sum of C[code]^2 per token and group (exact in fp64)
 };
+
+// Norm-corrected stored norm: nu sqrt(d) / sqrt(sum C[code]^2), evaluated in fp64. The
+// sum is exact whatever the order (binary16 centroids, at most 128 terms), so only nu
+// carries summation-order rounding.
+__device__ inline float corrected_norm(double nu, double csum, int d) {
+  return nu > 0.0 ? (float)(nu * sqrt((double)d) / sqrt(csum)) : 0.f;
+}
 
 // OR over the 16 lanes of a row: DPP row operations. update_dpp with bound_ctrl (every
 // source lane of these patterns is inside the row) lets the compiler fuse each step
@@ -242,7 +253,10 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       }
     }
   }
-  if (tid < 80) (&S.thr[0][0])[tid] = (&a.cb->t[0][0])[tid];
+  if (tid < 80) {
+    (&S.thr[0][0])[tid] = (&a.cb->t[0][0])[tid];
+    (&S.cen[0][0])[tid] = (&a.cb->c[0][0])[tid];
+  }
   // zero the A operands once: padding columns stay zero
   for (int e = tid; e < 2 * kAppTile * kAppPitch / 8; e += kAppThreads)
     reinterpret_cast<uint4*>(&S.ua[0][0][0])[e] = make_uint4(0, 0, 0, 0);
@@ -292,6 +306,7 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
     __syncthreads();                  // the previous tile's stores have read the buffers
     if (tid < kAppTile * 16) (&S.pk[0][0])[tid] = 0u;
     (&S.pv[0][0])[tid] = 0u;          // 4 x 128 == kAppThreads
+    if (a.nc && tid < kAppTile * 5) (&S.cs[0][0])[tid] = 0.0;
     // ---- norms (fp64, per token and group; every lane of the row gets all sums), then
     //      u = x / nu split as 256 u = U_hi + U_lo
     double sg[kMaxGroups] = {0.0, 0.0, 0.0, 0.0};
@@ -309,7 +324,10 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       if (gg < ng) {
         const double nu = sqrt(row_sum_f64(sg[gg]));
         inv[gg] = nu > 0.0 ? 1.0 / nu : 0.0;
-        if (sub == gg) S.nu[tau][vrole ? 4 : gg] = (float)nu;
+        if (sub == gg) {
+          S.nu[tau][vrole ? 4 : gg] = (float)nu;
+          if (a.nc) S.nu64[tau][vrole ? 4 : gg] = nu;
+        }
       }
     }
 #pragma unroll
@@ -374,6 +392,16 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
             for (int v8 = 0; v8 < 8; ++v8) cds[v8] += zv[v8] >= tv[v8] ? step : 0;
           }
         }
+        if (a.nc) {
+          // sum of C[code]^2 over the row's 16 outputs for each of the lane's 8 tokens
+          const float* cr = S.cen[r];
+#pragma unroll
+          for (int v8 = 0; v8 < 8; ++v8) {
+            const double c = i < d ? (double)cr[cds[v8]] : 0.0;
+            const double rs = row_sum_f64(c * c);
+            if (n == 0) atomicAdd(&S.cs[16 * (v8 >> 2) + 4 * q + (v8 & 3)][g], rs);
+          }
+        }
         if (g == 4) {
           if (i < d) {
 #pragma unroll
@@ -432,7 +460,9 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       if (tid < kAppTile * kNS) {
         const int t = tid / kNS, g = tid - kNS * t;
         const int64_t s = ts + t;
-        if (s >= a.pos0 && s < s_end) a.k_norms[(sh * a.capacity + s) * kNS + g] = g < n_groups ? S.nu[t][g] : 0.f;
+        if (s >= a.pos0 && s < s_end)
+          a.k_norms[(sh * a.capacity + s) * kNS + g] =
+              g >= n_groups ? 0.f : (a.nc ? corrected_norm(S.nu64[t][g], S.cs[t][g], hp->dim[g]) : S.nu[t][g]);
       }
     } else {
       const int vw = 32 * vb;
@@ -464,7 +494,8 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       }
       if (tid < kAppTile) {
         const int64_t s = ts + tid;
-        if (s >= a.pos0 && s < s_end) a.v_norms[sh * a.capacity + s] = S.nu[tid][4];
+        if (s >= a.pos0 && s < s_end)
+          a.v_norms[sh * a.capacity + s] = a.nc ? corrected_norm(S.nu64[tid][4], S.cs[tid][4], kD) : S.nu[tid][4];
       }
     }
   }
@@ -480,9 +511,10 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   __shared__ __align__(16) float xs[2 * kD];  // key (record order) then value coordinates
   __shared__ float red[4][2 * kD];
   __shared__ float nu_s[5], sc_s[5];
+  __shared__ double nu64_s[5], cs_s[5];  // norm-corrected variant: fp64 norms, sums of C[code]^2
   __shared__ uint32_t krec[16];
   __shared__ uint32_t vblk[128], vmask[128];
-  __shared__ float thr[5][16];
+  __shared__ float thr[5][16], cen[5][16];
   const int tid = threadIdx.x;
   const DevHead* __restrict__ hd = a.heads + h;
   const int n_groups = hd->n_groups;
@@ -492,6 +524,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   else if (tid < 2 * kD) xv = a.v[row + tid - kD];
   const int crd = tid < kD ? hd->coord[tid] : 0;
   const float thv = tid < 80 ? (&a.cb->t[0][0])[tid] : 0.f;
+  const float cev = tid < 80 ? (&a.cb->c[0][0])[tid] : 0.f;
   // this thread's rotation entries: key output o < 128 (row i of its group, pair range
   // of quarter qq) or value output o - 128 (32 columns of quarter qq)
   const int o = tid & 255, qq = tid >> 8;
@@ -520,7 +553,11 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     return;
   }
   if (tid < 2 * kD) xnat[tid] = xv;
-  if (tid < 80) (&thr[0][0])[tid] = thv;
+  if (tid < 80) {
+    (&thr[0][0])[tid] = thv;
+    (&cen[0][0])[tid] = cev;
+  }
+  if (tid < 5) cs_s[tid] = 0.0;
   if (tid < 16) krec[tid] = 0u;
   if (tid < 128) {
     vblk[tid] = 0u;
@@ -549,6 +586,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
       for (int g = 1; g < kMaxGroups; ++g) sg = (tid == g) ? s4[g] : sg;
       const double nu = sqrt(sg);
       nu_s[tid] = (float)nu;
+      nu64_s[tid] = nu;
       sc_s[tid] = nu > 0.0 ? (float)(sqrt((double)hd->dim[tid]) / nu) : 0.f;
     }
   } else if (tid < 128) {
@@ -558,6 +596,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     if (l == 0) {
       const double nu = sqrt(s);
       nu_s[4] = (float)nu;
+      nu64_s[4] = nu;
       sc_s[4] = nu > 0.0 ? (float)(sqrt((double)kD) / nu) : 0.f;
     }
   }
@@ -599,9 +638,25 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
       const uint64_t f = (uint64_t)c << (bit & 31);
       atomicOr(&krec[bit >> 5], (uint32_t)f);
       if (f >> 32) atomicOr(&krec[(bit >> 5) + 1], (uint32_t)(f >> 32));
+      if (a.nc) {  // per-group sums of C[code]^2 (waves 0 and 1 hold the key outputs)
+        const double c2 = (double)cen[b][c] * (double)cen[b][c];
+        double s4[kMaxGroups];
+#pragma unroll
+        for (int gg = 0; gg < kMaxGroups; ++gg) s4[gg] = wave_sum_f64_fast(g == gg ? c2 : 0.0);
+        if ((tid & 63) < n_groups) {
+          double sv = s4[0];
+#pragma unroll
+          for (int gg = 1; gg < kMaxGroups; ++gg) sv = ((tid & 63) == gg) ? s4[gg] : sv;
+          atomicAdd(&cs_s[tid & 63], sv);
+        }
+      }
     } else {
       const int cidx = tid - kD;
       const uint32_t c = quantize(z0 * sc_s[4], thr[vb], (1 << vb) - 1);
+      if (a.nc) {
+        const double c2 = wave_sum_f64_fast((double)cen[vb][c] * (double)cen[vb][c]);
+        if ((tid & 63) == 0) atomicAdd(&cs_s[4], c2);
+      }
       const int bit = 8 * vb * cidx + vb * j0;
       const uint64_t f = (uint64_t)c << (bit & 31);
       const uint64_t m = (uint64_t)((1u << vb) - 1u) << (bit & 31);
@@ -618,9 +673,10 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   if (tid < a.k_words) a.k_codes[(sh * a.capacity + slot) * a.k_words + tid] = krec[tid];
   if (tid >= 64 && tid < 64 + kNS) {
     const int g = tid - 64;
-    a.k_norms[(sh * a.capacity + slot) * kNS + g] = g < n_groups ? nu_s[g] : 0.f;
+    a.k_norms[(sh * a.capacity + slot) * kNS + g] =
+        g >= n_groups ? 0.f : (a.nc ? corrected_norm(nu64_s[g], cs_s[g], hd->dim[g]) : nu_s[g]);
   }
-  if (tid == 128) a.v_norms[sh * a.capacity + slot] = nu_s[4];
+  if (tid == 128) a.v_norms[sh * a.capacity + slot] = a.nc ? corrected_norm(nu64_s[4], cs_s[4], kD) : nu_s[4];
   if (tid >= 256 && tid < 256 + 32 * vb) {
     const int w = tid - 256;
     const uint32_t m = vmask[w];
@@ -1797,6 +1853,7 @@ void fill_append_args(const gtq_plan* p, int layer, const gtq_cache_view* c, con
   a.n_kv = p->n_kv;
   a.k_words = p->k_words;
   a.v_bits = p->v_bits;
+  a.nc = (p->flags & GTQ_PLAN_NORM_CORRECT) ? 1 : 0;
 }
 
 gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* k,
@@ -1824,6 +1881,7 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   a.n_kv = p->n_kv;
   a.k_words = p->k_words;
   a.v_bits = p->v_bits;
+  a.nc = (p->flags & GTQ_PLAN_NORM_CORRECT) ? 1 : 0;
   if (!chunk) {
     if (n_tok > 0x7FFFFFFF) return fail(GTQ_EUNSUPPORTED, "gtq_quantize_append: too many tokens");
     hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)n_tok, p->n_kv), dim3(1024), 0, stream, a);

@@ -331,7 +331,8 @@ gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
   if (d->v_bits < 1 || d->v_bits > 4) return fail(GTQ_EINVAL, "gtq_plan_create: v_bits must be in [1, 4]");
   if (d->k_budget < kJ || d->k_budget > 4 * kJ || d->k_budget % 16)
     return fail(GTQ_EINVAL, "gtq_plan_create: k_budget must be a multiple of 16 in [64, 256]");
-  if (d->flags & ~GTQ_PLAN_HOST_ONLY) return fail(GTQ_EINVAL, "gtq_plan_create: unknown flags");
+  if (d->flags & ~(GTQ_PLAN_HOST_ONLY | GTQ_PLAN_NORM_CORRECT))
+    return fail(GTQ_EINVAL, "gtq_plan_create: unknown flags");
   if (!d->k_rates || !d->k_rot || !d->v_rot) return fail(GTQ_EINVAL, "gtq_plan_create: NULL table");
   p->n_layers = d->n_layers;
   p->n_kv = d->n_kv_heads;

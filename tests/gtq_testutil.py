@@ -31,11 +31,12 @@ class Case:
     """Plans (oracle + library) and per-sequence inputs for n_layers x h_kv heads."""
 
     def __init__(self, seed, n_layers, h_kv, g, n_cache, k_budget, v_bits, batch=1, layout=O.HALF,
-                 n_dec_q=1, b_min=1, b_max=4):
+                 n_dec_q=1, b_min=1, b_max=4, nc=False):
         import packed_cache_attention_tq_amd as G
         self.seed, self.L, self.H, self.g = seed, n_layers, h_kv, g
         self.HQ = h_kv * g
         self.n, self.k_budget, self.v_bits, self.batch, self.layout = n_cache, k_budget, v_bits, batch, layout
+        self.nc = nc
         self.rates = np.zeros((n_layers, h_kv, 64), np.uint8)
         self.heads = {}
         k_rot_all, v_rot_all = [], []
@@ -55,7 +56,7 @@ class Case:
                 self.rates[l, h] = r_lib
                 dims = [len(c) for _, c in O.groups_from_rates(r, layout)]
                 kr, vr = head_rotations(seed, l, h, dims)
-                self.heads[l, h] = O.HeadPlan(r, kr, vr, v_bits, layout)
+                self.heads[l, h] = O.HeadPlan(r, kr, vr, v_bits, layout, nc=nc)
                 kl.append(kr)
                 vl.append(vr)
             k_rot_all.append(kl)
@@ -65,7 +66,7 @@ class Case:
     def plan(self, host_only=False):
         import packed_cache_attention_tq_amd as G
         return G.Plan(self.L, self.H, self.HQ, self.k_budget, self.v_bits, self.rates, self.k_rot,
-                      self.v_rot, rope_layout=self.layout, host_only=host_only)
+                      self.v_rot, rope_layout=self.layout, host_only=host_only, norm_correct=self.nc)
 
     def kv(self, l, b, lo=0, hi=None):
         """k, v [n_tok, H_kv, 128] of sequence b, tokens lo..hi-1."""

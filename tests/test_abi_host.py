@@ -162,6 +162,12 @@ def test_error_paths(lib):
     with pytest.raises(G.GtqError) as e:
         G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True, head_dim=64)
     _expect(e, 2, "head_dim")
+    # the norm-corrected flag is accepted, any other bit is not
+    G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True, norm_correct=True).destroy()
+    desc = G.PlanDesc(2, 2, 4, 128, 0, 128, 2, G.PLAN_HOST_ONLY | 4, None, None, None)
+    h = C.c_void_p()
+    assert lib.gtq_plan_create(C.byref(desc), C.byref(h)) == 1
+    assert b"flags" in lib.gtq_last_error()
     p = G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True)
     with pytest.raises(G.GtqError) as e:
         p.layout(2, 0)

@@ -168,13 +168,14 @@ def test_gqa_ragged_decode_on_oracle_cache(G, chunk):
         assert_close(out[b].cpu().numpy(), out_ref, f"out b{b}")
 
 
-def test_decode_step_fused(G):
+@pytest.mark.parametrize("nc", [False, True])
+def test_decode_step_fused(G, nc):
     """gtq_decode_step: every sequence appends its newest token at slot seq_len - 1 and
     attends to seq_len tokens (lengths 1, 0, 300, 129; 4 KV heads x g=4, K2V2): cache
     records and outputs against the oracle, and the same outputs as the separate
-    append + decode calls."""
-    _say("case: fused decode step (append + rotate, partials, merge)")
-    case = Case(5, 1, 4, 4, 300, 128, 2, batch=4)
+    append + decode calls; plain and norm-corrected stored norms."""
+    _say(f"case: fused decode step (append + rotate, partials, merge), nc={nc}")
+    case = Case(5, 1, 4, 4, 300, 128, 2, batch=4, nc=nc)
     plan = case.plan()
     cap, lens = 320, [1, 0, 300, 129]
     cache = G.PackedCache(plan, 4, cap)
@@ -283,6 +284,45 @@ def test_scatter_append_random_order_and_overflow(G):
                 torch.cuda.synchronize()
                 _, out_ref = _oracle_decode(case, l, b, n, _encode(case, l, b, n), q[0], scale_default())
                 assert_close(out[b].cpu().numpy(), out_ref, f"end-to-end out l{l} b{b}")
+
+
+def test_norm_corrected_append(G):
+    """Norm-corrected stored norms through both append kernels (the tiled chunk kernel and
+    the per-token scatter kernel): codes as in the plain variant, norms within 1 ulp of
+    the oracle's corrected norms, and the decode over the corrected cache matching the
+    oracle's."""
+    _say("case: norm-corrected append (chunk + scatter)")
+    n = 150
+    case = Case(4, 1, 2, 4, n, 160, 2, batch=2, nc=True)
+    plain = Case(4, 1, 2, 4, n, 160, 2, batch=2)
+    plan = case.plan()
+    cache = G.PackedCache(plan, 2, 160)
+    # sequence 0: chunks (one tile-aligned, one ragged); sequence 1: scatter in random order
+    k, v = case.kv(0, 0)
+    for lo, hi in [(0, 64), (64, 101), (101, n)]:
+        G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k[lo:hi]), _dev(v[lo:hi]), 0, lo)
+    k1, v1 = case.kv(0, 1)
+    perm = np.random.default_rng(5).permutation(n)
+    G.gtq_quantize_append(plan, 0, cache, _dev(k1[perm]), _dev(v1[perm]), _dev(np.ones(n, np.int32)),
+                          _dev(perm.astype(np.int64)))
+    torch.cuda.synchronize()
+    for b, what in ((0, "nc chunk"), (1, "nc scatter")):
+        enc = _encode(case, 0, b, n)
+        enc_plain = _encode(plain, 0, b, n)
+        ties, ulps = _check_append(case, cache, 0, b, n, enc, what)
+        _say(f"  {what}: ties={ties} norm-ulps={ulps}")
+        for h in range(case.H):  # the correction changes the norms only
+            for gi in range(len(enc[h]["k_codes"])):
+                assert np.array_equal(enc[h]["k_codes"][gi], enc_plain[h]["k_codes"][gi])
+            assert not np.array_equal(enc[h]["v_norms"], enc_plain[h]["v_norms"])
+        if ties == 0:
+            q = case.q(0, b)[None]
+            qq = np.concatenate([q, q])
+            out = G.gtq_decode_attn(plan, 0, cache, _dev(qq), _dev(np.array([n, n], np.int32)), n,
+                                    scale_default())
+            torch.cuda.synchronize()
+            _, out_ref = _oracle_decode(case, 0, b, n, enc, q[0], scale_default())
+            assert_close(out[b].cpu().numpy(), out_ref, f"{what} decode out")
 
 
 def test_prefill_chunk(G):
