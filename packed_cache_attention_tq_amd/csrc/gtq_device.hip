@@ -986,6 +986,8 @@ struct AttnWave {
 // parts share one B operand; 16: separate high and low B operands).
 template <int RT>
 struct AttnSharedT {
+  uint4 oct1[256];                   // byte-indexed decode tables (DevCodebook::oct1, quad2)
+  uint2 quad2[256];
   uint32_t lut[kPairTable + 4];      // decode table (DevCodebook::pair)
   uint4 qb[(RT / 8) * kMaxKB][4][16];  // QK B operand(s) per K-block and lane
   int32_t row_id[RT];
@@ -999,15 +1001,26 @@ struct AttnSharedT {
 };
 using AttnShared = AttnSharedT<8>;
 
-// 8 codes of rate R (code k at bits [k R, (k + 1) R) of F) -> 8 binary16 centroids, two
-// codes per table read
-template <int R>
-__device__ inline half8 dequant8(const uint32_t* lut, uint32_t F) {
-  constexpr int base = ((1 << (2 * R)) - 4) / 3;
-  constexpr uint32_t m = (1u << (2 * R)) - 1;
+// 8 codes of rate R (code k at bits [k R, (k + 1) R) of F) -> 8 binary16 centroids: one
+// table read of the byte of 1-bit codes, two of the bytes of 2-bit codes, else two
+// codes per read of the pair table
+template <int R, int RT>
+__device__ inline half8 dequant8(const AttnSharedT<RT>& S, uint32_t F) {
   H8 o;
+  if constexpr (R == 1) {
+    o.v = S.oct1[F & 0xFFu];
+  } else if constexpr (R == 2) {
+    const uint2 x = S.quad2[F & 0xFFu], y = S.quad2[(F >> 8) & 0xFFu];
+    o.u[0] = x.x;
+    o.u[1] = x.y;
+    o.u[2] = y.x;
+    o.u[3] = y.y;
+  } else {
+    constexpr int base = ((1 << (2 * R)) - 4) / 3;
+    constexpr uint32_t m = (1u << (2 * R)) - 1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) o.u[j] = lut[base + ((F >> (2 * R * j)) & m)];
+    for (int j = 0; j < 4; ++j) o.u[j] = S.lut[base + ((F >> (2 * R * j)) & m)];
+  }
   return o.h;
 }
 
@@ -1056,8 +1069,8 @@ template <int VB, int KWL>
 __device__ inline void load_block(BlockData<VB, KWL>& B, const SliceRsrc& R, int t0, int kw, int lane, int voff_v) {
   const int sk = t0 * kw * 4;
 #pragma unroll
-  for (int i = 0; i < KWL; ++i)
-    if (2 * i < kw) B.kr[i] = __builtin_amdgcn_raw_buffer_load_b32(R.kc, 4 * lane + 256 * i, sk, 0);
+  for (int i = 0; i < KWL; ++i)  // (words past the block's records are staged to a pad slot)
+    B.kr[i] = __builtin_amdgcn_raw_buffer_load_b32(R.kc, 4 * lane + 256 * i, sk, 0);
   B.kn = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(R.kn, 8 * lane, t0 * (kNS * 4), 0));
   B.vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.vn, 4 * (lane & 31), t0 * 4, 0));
   const int sv = t0 * (4 * VB * 4);  // (t0 / 8) blocks of 32 VB words
@@ -1109,13 +1122,10 @@ struct QkConst {
 template <int VB, int KWL>
 __device__ inline void stage_block(AttnWave& W, const BlockData<VB, KWL>& B, int kw, int lane, const int (&st)[KWL]) {
 #pragma unroll
-  for (int i = 0; i < KWL; ++i) {
-    if (2 * i + 1 < kw) W.ktile[st[i]] = B.kr[i];
-    else if (2 * i < kw && lane < 32) W.ktile[st[i]] = B.kr[i];
-  }
+  for (int i = 0; i < KWL; ++i) W.ktile[st[i]] = B.kr[i];
   W.knt[2 * (lane & 1)][lane >> 1] = B.kn.x;
   W.knt[2 * (lane & 1) + 1][lane >> 1] = B.kn.y;
-  if (lane < 32) W.vn[lane] = B.vn;
+  W.vn[lane & 31] = B.vn;  // (lanes l and l + 32 hold the same norm)
 #pragma unroll
   for (int i = 0; i < (2 * VB + 3) / 4; ++i) {
     uint4 x;
@@ -1253,7 +1263,7 @@ __device__ inline void attn_block(const AttnShared& S, const AttnWave& W, const 
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t)
-    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S.lut, vfield<VB>(vw, t)), oacc[t], 0, 0, 0);
+    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB, 8>(S, vfield<VB>(vw, t)), oacc[t], 0, 0, 0);
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -1273,7 +1283,8 @@ __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W,
   const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NKB; ++i) {
-    const uint32_t* r = reinterpret_cast<const uint32_t*>(sb + (C.ko[i] >> 5));
+    const char* rp = sb + (C.ko[i] >> 5);
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(rp);
     const uint32_t f0 = __builtin_amdgcn_alignbit(r[1], r[0], C.ko[i]);
     const uint32_t f1 = __builtin_amdgcn_alignbit(r[4 * kKPitch + 1], r[4 * kKPitch], C.ko[i]);
     H8 a0, a1;
@@ -1365,7 +1376,7 @@ __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W,
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const half8 bv = dequant8<VB>(S.lut, vfield<VB>(vw, t));
+    const half8 bv = dequant8<VB, 16>(S, vfield<VB>(vw, t));
     oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph.h, bv, oacc[t], 0, 0, 0);
     oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl.h, bv, oacc[t], 0, 0, 0);
   }
@@ -1442,6 +1453,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const int e = tid + kThreads * u;
     lutv[u] = e < kPairTable ? a.cb->pair[e] : 0u;
   }
+  static_assert(kThreads == 512, "one byte-table entry per thread");
+  uint4 tabv;  // threads 0..255: oct1[tid]; 256..511: quad2[tid - 256]
+  if (tid < 256) tabv = *reinterpret_cast<const uint4*>(a.cb->oct1[tid]);
+  else tabv = make_uint4(a.cb->quad2[tid - 256][0], a.cb->quad2[tid - 256][1], 0u, 0u);
   const int len_ld = a.prefill ? 0 : a.seq_len[seq];
   BlockData<VB, KWL> blk[1];
   load_block<VB, KWL>(blk[0], R, c0 + kBlk * wave, kw, lane, voff_v);
@@ -1452,6 +1467,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const int e = tid + kThreads * u;
     if (e < kPairTable) S.lut[e] = lutv[u];
   }
+  if (tid < 256) S.oct1[tid] = tabv;
+  else S.quad2[tid - 256] = make_uint2(tabv.x, tabv.y);
   if (tid < RT) {
     int L;
     S.row_id[tid] = tile_row<RT>(a, seq, h, tr, tid, len_ld, &L);
@@ -1469,11 +1486,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const int my_len = S.row_len[my_row];
   AttnWave& W = S.u.w[wave];
   const char* sb = reinterpret_cast<const char*>(&S);
-  int st[KWL];  // staging slot of word lane + 64 i: token (lw / kw) at pitch 17
+  int st[KWL];  // staging slot of word lane + 64 i: token (lw / kw) at pitch 17; words past
+                // the block's 32 records go to the pad column of token 0, whose bits no
+                // decoded code uses
 #pragma unroll
   for (int i = 0; i < KWL; ++i) {
     const int lw = lane + 64 * i;
-    st[i] = (lw / kw) * kKPitch + lw % kw;
+    st[i] = lw < kBlk * kw ? (lw / kw) * kKPitch + lw % kw : kKPitch - 1;
   }
   // QK constants: A-row n of the two 16-token halves is token tau0 (+ 4)
   const int tau0 = 8 * (n >> 2) + (n & 3);

@@ -112,6 +112,10 @@ void fill_codebook(DevCodebook* cb) {
     for (int x = 0; x < (1 << (2 * b)); ++x)
       cb->pair[base + x] = half_bits(t.cent[b][x & m]) | (half_bits(t.cent[b][x >> b]) << 16);
   }
+  for (int x = 0; x < 256; ++x) {
+    for (int j = 0; j < 4; ++j) cb->oct1[x][j] = cb->pair[0 + ((x >> (2 * j)) & 3)];
+    for (int j = 0; j < 2; ++j) cb->quad2[x][j] = cb->pair[4 + ((x >> (4 * j)) & 15)];
+  }
 }
 
 // ---------------------------------------------------------------- layouts

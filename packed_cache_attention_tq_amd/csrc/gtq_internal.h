@@ -51,6 +51,11 @@ struct DevCodebook {
   // decode table: entry (4^b - 4) / 3 + (k0 | k1 << b) holds the binary16 centroids
   // k0 (low half) and k1 (high half) of rate b
   uint32_t pair[kPairTable + 4];
+  // byte-indexed tables of the two lowest rates: oct1[x] = the 8 binary16 centroids of
+  // the eight 1-bit codes in byte x (code k at bit k; entry word j = codes 2j, 2j + 1),
+  // quad2[x] = the 4 centroids of the four 2-bit codes in byte x (code k at bits 2k..)
+  uint32_t oct1[256][4];
+  uint32_t quad2[256][2];
 };
 
 }  // namespace gtq
