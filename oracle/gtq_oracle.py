@@ -35,6 +35,10 @@ Readings where the pages are silent (each also listed in the design notes):
       and every code 2^(b-1).
   R12 greedy ties go to the smallest block index.
   R13 the budget counts code bits only: sum_j b_j = (average key bits) * 64.
+  R22 fp16 sink and recent-token buffers ([BGTQ s8] names the variant as one its K3V2
+      result does without): the first n_sink positions and the last n_recent
+      positions of a sequence attend through fp16 copies of their K and V (binary16,
+      round to nearest even), every other position through the packed cache.
 """
 from __future__ import annotations
 
@@ -377,6 +381,41 @@ def decode_attention(plan: HeadPlan, q: np.ndarray, k_words, k_norms, v_words, v
     o_rot = p @ vrot
     out = o_rot @ plan.v_rot.astype(np.float64)          # (Pi^T o_rot^T)^T
     return logits, out
+
+
+def window_positions(length: int, n_sink: int, n_recent: int) -> np.ndarray:
+    """Boolean mask [length]: True where position p reads the fp16 buffers (R22): the
+    sink p < n_sink, or the recent window p >= length - n_recent."""
+    p = np.arange(int(length))
+    return (p < n_sink) | (p >= int(length) - n_recent)
+
+
+def decode_attention_window(plan: HeadPlan, q: np.ndarray, k_words, k_norms, v_words, v_norms,
+                            k_full, v_full, n_sink: int, n_recent: int, scale: float, length: int):
+    """Decode attention with fp16 sink and recent-token buffers (R22) [BGTQ s8]: the
+    logit of a window position is scale * q . fp16(k) and its value fp16(v); every
+    other position uses the packed cache (packed_logits, and the value decoded as
+    nu Pi_V^T C[code] / sqrt(128)). Softmax over all `length` positions in fp64.
+    k_full, v_full [>= length, 128] are the fp32 inputs the buffers were filled from.
+    Returns (logits [m, length], out [m, 128])."""
+    n = int(length)
+    win = window_positions(n, n_sink, n_recent)
+    q64 = np.asarray(q, np.float32).astype(np.float64)
+    k16 = np.asarray(k_full, np.float32)[:n].astype(np.float16).astype(np.float64)
+    v16 = np.asarray(v_full, np.float32)[:n].astype(np.float16).astype(np.float64)
+    logits = np.empty((q64.shape[0], n))
+    if (~win).any():
+        logits[:, ~win] = packed_logits(plan, q, np.asarray(k_words)[:n][~win], np.asarray(k_norms)[:n][~win], scale)
+    if win.any():
+        logits[:, win] = scale * (q64 @ k16[win].T)
+    values = np.empty((n, HEAD_DIM))
+    if (~win).any():
+        values[~win] = dequantized_values(plan, np.asarray(v_words)[:n][~win], np.asarray(v_norms)[:n][~win])
+    values[win] = v16[win]
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    return logits, p @ values
 
 
 def prefill_attention(plan: HeadPlan, q: np.ndarray, pos0: int, k_words, k_norms, v_words,

@@ -120,3 +120,68 @@ def test_prefill_reduces_to_decode_and_is_causal():
     out2 = O.prefill_attention(plan, q, pos0, kw, enc["k_norms"], enc["v_words"], enc["v_norms"], sc)
     assert np.array_equal(out2[:3], out[:3])
     assert not np.allclose(out2[3:], out[3:])
+
+
+# ---------------------------------------------------------------- fp16 sink + recent window
+
+def test_window_positions_by_hand():
+    """Length 20, 3 sink and 5 recent positions: 0, 1, 2 and 15..19 read the fp16
+    buffers; a window longer than the sequence covers everything; none when both are 0."""
+    assert np.flatnonzero(O.window_positions(20, 3, 5)).tolist() == [0, 1, 2, 15, 16, 17, 18, 19]
+    assert O.window_positions(6, 4, 4).all()
+    assert not O.window_positions(9, 0, 0).any()
+    assert np.flatnonzero(O.window_positions(10, 0, 1)).tolist() == [9]
+
+
+def test_window_without_buffers_is_the_packed_decode():
+    inp, plan, enc = _plan_and_cache(n=150)
+    q = inp["q"].reshape(-1, 128)
+    sc = 1 / math.sqrt(128)
+    args = (enc["k_words"], enc["k_norms"], enc["v_words"], enc["v_norms"])
+    lg0, o0 = O.decode_attention(plan, q, *args, sc, length=150)
+    lg1, o1 = O.decode_attention_window(plan, q, *args, inp["k"], inp["v"], 0, 0, sc, 150)
+    assert np.array_equal(lg0, lg1)
+    assert np.allclose(o0, o1, rtol=1e-13, atol=1e-15)
+
+
+def test_window_covering_everything_is_fp16_attention():
+    """Sink + recent >= length: plain softmax attention over the binary16-rounded K, V."""
+    inp, plan, enc = _plan_and_cache(n=96)
+    q = inp["q"].reshape(-1, 128).astype(np.float64)
+    sc = 0.07
+    args = (enc["k_words"], enc["k_norms"], enc["v_words"], enc["v_norms"])
+    for ns, nr in ((96, 0), (0, 96), (40, 60)):
+        _, o = O.decode_attention_window(plan, q, *args, inp["k"], inp["v"], ns, nr, sc, 96)
+        k16 = inp["k"].astype(np.float16).astype(np.float64)
+        v16 = inp["v"].astype(np.float16).astype(np.float64)
+        ref = softmax(sc * q @ k16.T, axis=1) @ v16
+        assert np.allclose(o, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_window_brute_force_small():
+    """Position by position in plain Python: fp16 key/value inside the window,
+    dequantized packed key/value outside; softmax with math.exp."""
+    inp, plan, enc = _plan_and_cache(n=23, n_q=1)
+    q = inp["q"].reshape(-1, 128)[:2].astype(np.float64)
+    sc = 0.09
+    n, ns, nr = 23, 2, 6
+    kh = O.dequantized_keys(plan, enc["k_words"], enc["k_norms"])
+    vh = O.dequantized_values(plan, enc["v_words"], enc["v_norms"])
+    lg, o = O.decode_attention_window(plan, q, enc["k_words"], enc["k_norms"], enc["v_words"], enc["v_norms"],
+                                      inp["k"], inp["v"], ns, nr, sc, n)
+    for r in range(2):
+        logit, val = [], []
+        for pos in range(n):
+            if pos < ns or pos >= n - nr:
+                kk = [float(np.float16(x)) for x in inp["k"][pos]]
+                vv = [float(np.float16(x)) for x in inp["v"][pos]]
+            else:
+                kk, vv = list(kh[pos]), list(vh[pos])
+            logit.append(sc * sum(a * b for a, b in zip(q[r], kk)))
+            val.append(vv)
+        mx = max(logit)
+        w = [math.exp(x - mx) for x in logit]
+        tot = sum(w)
+        ref = [sum(w[p] * val[p][c] for p in range(n)) / tot for c in range(128)]
+        assert np.allclose(lg[r], logit, rtol=1e-12, atol=1e-12)
+        assert np.allclose(o[r], ref, rtol=1e-11, atol=1e-13)
