@@ -312,6 +312,61 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
                             float softmax_scale, int32_t chunk, float* out, void* workspace,
                             size_t ws_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------- fp16 window */
+
+/* fp16 sink and recent-token buffers beside the packed cache ("Block-GTQ" abstract,
+ * 8th sentence, names them as the variant its K3V2 result does without): positions
+ * p < n_sink and p >= seq_len - n_recent of a sequence attend through binary16 copies
+ * of their key and value (round to nearest even), every other position through the
+ * packed cache. Device buffers, caller-owned, one set per layer:
+ *   k_sink   [batch][n_kv_heads][sink_slots][128]      binary16, token-major
+ *   v_sink   [batch][n_kv_heads][sink_slots / 8][128][8] binary16: blocks of 8 tokens,
+ *            coordinate-major inside a block (slot s: block s / 8, lane s % 8)
+ *   k_recent [batch][n_kv_heads][n_recent][128]        ring: position p at slot p % n_recent
+ *   v_recent [batch][n_kv_heads][n_recent / 8][128][8] the same ring, V block layout
+ * with sink_slots = n_sink rounded up to a multiple of 32. n_sink in [0, 256];
+ * n_recent a multiple of 32 in [0, 8192]. Slots that no token has filled may hold
+ * anything: the kernels never read their values into a result. */
+typedef struct {
+  uint16_t* k_sink;
+  uint16_t* v_sink;
+  uint16_t* k_recent;
+  uint16_t* v_recent;
+  int32_t batch;
+  int32_t n_sink;
+  int32_t n_recent;
+} gtq_window_view;
+
+/* Copy tokens into the fp16 buffers: token t (k, v device [n_tok][n_kv_heads][128]
+ * fp32) of sequence seq_idx[t] at position pos[t] (device int32 / int64) goes to sink
+ * slot pos when pos < n_sink, else to recent slot pos % n_recent (nowhere if
+ * n_recent is 0). Tokens of one call that map to the same slot race: pass each slot
+ * at most once per call (for a prompt, its sink positions and its last n_recent
+ * positions). The packed cache is filled separately (gtq_quantize_append), for every
+ * position. Tokens with seq_idx outside [0, batch) or pos < 0 are skipped and
+ * counted (gtq_plan_overflow_count). Errors: EINVAL (NULL, layer, window sizes,
+ * host-only plan). */
+gtq_status gtq_window_append(const gtq_plan* plan, int32_t layer, const gtq_window_view* window,
+                             const float* k, const float* v, const int32_t* seq_idx, const int64_t* pos,
+                             int64_t n_tok, void* hip_stream);
+
+/* Workspace bytes of gtq_decode_attn_window: gtq_decode_workspace_bytes plus one more
+ * partial per query row (the fp16 window's). */
+gtq_status gtq_decode_window_workspace_bytes(const gtq_plan* plan, int32_t batch, int64_t max_len,
+                                             int32_t chunk, size_t* out);
+
+/* gtq_decode_attn with the fp16 window: for sequence b of length L = seq_len[b] the
+ * packed partials cover positions [n_sink, max(n_sink, L - n_recent)); the fp16
+ * positions (sink p < min(n_sink, L), recent p >= max(n_sink, L - n_recent)) form one
+ * more split computed in the original basis and carried into the rotated value basis
+ * before the merge. logits (optional) get every visible position's logit, packed or
+ * fp16. window->batch must equal cache->batch. Errors: as gtq_decode_attn, plus EINVAL
+ * for window sizes. */
+gtq_status gtq_decode_attn_window(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                  const gtq_window_view* window, const float* q, const int32_t* seq_len,
+                                  int64_t max_len, float softmax_scale, int32_t chunk, float* out,
+                                  float* logits, void* workspace, size_t ws_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

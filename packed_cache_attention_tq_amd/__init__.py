@@ -52,6 +52,11 @@ class CacheView(C.Structure):
                 ("v_norms", C.c_void_p), ("batch", C.c_int32), ("capacity", C.c_int64)]
 
 
+class WindowView(C.Structure):
+    _fields_ = [("k_sink", C.c_void_p), ("v_sink", C.c_void_p), ("k_recent", C.c_void_p),
+                ("v_recent", C.c_void_p), ("batch", C.c_int32), ("n_sink", C.c_int32), ("n_recent", C.c_int32)]
+
+
 class CacheSizes(C.Structure):
     _fields_ = [("k_codes_bytes", C.c_size_t), ("k_norms_bytes", C.c_size_t),
                 ("v_codes_bytes", C.c_size_t), ("v_norms_bytes", C.c_size_t),
@@ -103,6 +108,13 @@ _SIGS = [
     ("gtq_prefill_attn", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_int32,
                                      C.c_int64, C.c_int64, C.c_float, C.c_int32, C.c_void_p,
                                      C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("gtq_window_append", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(WindowView), C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
+    ("gtq_decode_window_workspace_bytes", C.c_int32, [C.c_void_p, C.c_int32, C.c_int64, C.c_int32,
+                                                      C.POINTER(C.c_size_t)]),
+    ("gtq_decode_attn_window", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.POINTER(WindowView),
+                                           C.c_void_p, C.c_void_p, C.c_int64, C.c_float, C.c_int32, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
 ]
 EXPORTS = [s[0] for s in _SIGS]
 
@@ -397,4 +409,63 @@ def gtq_prefill_attn(plan: Plan, layer: int, cache: PackedCache, q, seq: int, po
                                 _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
                                 _stream(stream))
     _check(st, "gtq_prefill_attn")
+    return out
+
+
+# ------------------------------------------------------------------ fp16 window
+
+class WindowCache:
+    """One layer's fp16 sink and recent-token buffers (see gtq_window_view): binary16
+    K [batch, n_kv, slots, 128] token-major, V [batch, n_kv, slots / 8, 128, 8] in
+    8-token blocks; sink slots = n_sink rounded up to 32, the recent ring has n_recent
+    slots (position p at p % n_recent)."""
+
+    def __init__(self, plan: Plan, batch: int, n_sink: int, n_recent: int, device="cuda"):
+        self.batch, self.n_sink, self.n_recent = batch, n_sink, n_recent
+        ss = (n_sink + 31) // 32 * 32
+        h = plan.n_kv
+        # never-written slots are masked by the kernels; fill with NaN so a test notices
+        # any read of them into a result
+        nan = float("nan")
+        self.k_sink = torch.full((batch, h, max(ss, 1), 128), nan, dtype=torch.float16, device=device)
+        self.v_sink = torch.full((batch, h, max(ss, 8) // 8, 128, 8), nan, dtype=torch.float16, device=device)
+        self.k_recent = torch.full((batch, h, max(n_recent, 1), 128), nan, dtype=torch.float16, device=device)
+        self.v_recent = torch.full((batch, h, max(n_recent, 8) // 8, 128, 8), nan, dtype=torch.float16,
+                                   device=device)
+
+    def view(self) -> WindowView:
+        return WindowView(self.k_sink.data_ptr(), self.v_sink.data_ptr(), self.k_recent.data_ptr(),
+                          self.v_recent.data_ptr(), self.batch, self.n_sink, self.n_recent)
+
+
+def gtq_window_append(plan: Plan, layer: int, win: WindowCache, k, v, seq_idx, pos, stream=None):
+    wv = win.view()
+    st = lib().gtq_window_append(plan.handle, layer, C.byref(wv), _dev(k, torch.float32, "k"),
+                                 _dev(v, torch.float32, "v"), _dev(seq_idx, torch.int32, "seq_idx"),
+                                 _dev(pos, torch.int64, "pos"), k.shape[0], _stream(stream))
+    _check(st, "gtq_window_append")
+
+
+def gtq_decode_window_workspace_bytes(plan: Plan, batch: int, max_len: int, chunk: int = 0) -> int:
+    out = C.c_size_t(0)
+    _check(lib().gtq_decode_window_workspace_bytes(plan.handle, batch, max_len, chunk, C.byref(out)),
+           "gtq_decode_window_workspace_bytes")
+    return out.value
+
+
+def gtq_decode_attn_window(plan: Plan, layer: int, cache: PackedCache, win: WindowCache, q, seq_len,
+                           max_len: int, scale: float, chunk: int = 0, out=None, logits=None, workspace=None,
+                           stream=None):
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nb = gtq_decode_window_workspace_bytes(plan, cache.batch, max_len, chunk)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    cv, wv = cache.view(), win.view()
+    st = lib().gtq_decode_attn_window(plan.handle, layer, C.byref(cv), C.byref(wv), _dev(q, torch.float32, "q"),
+                                      _dev(seq_len, torch.int32, "seq_len"), max_len, float(scale), chunk,
+                                      _dev(out, torch.float32, "out"), _dev(logits, torch.float32, "logits"),
+                                      _dev(workspace, None, "workspace"),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gtq_decode_attn_window")
     return out

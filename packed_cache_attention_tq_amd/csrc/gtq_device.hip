@@ -753,7 +753,20 @@ struct AttnArgs {
   int32_t max_len;         // decode clamp
   int32_t nkb_max;         // largest K-block count of the layer's heads
   float qscale;            // softmax scale * log2(e)
+  // fp16 sink and recent-token buffers (decode only): their split is the last one
+  const uint16_t* wk_sink;
+  const uint16_t* wv_sink;
+  const uint16_t* wk_rec;
+  const uint16_t* wv_rec;
+  int32_t win;             // 1: split n_chunks - 1 is the fp16 window's
+  int32_t n_sink, sink_slots, n_recent;
 };
+
+// End of the packed positions of a sequence of length L with n_sink sink and n_recent
+// recent fp16 positions: the packed ones are [n_sink, packed_end).
+__host__ __device__ inline int packed_end(int L, int n_sink, int n_recent) {
+  return L > n_sink + n_recent ? L - n_recent : min(L, n_sink);
+}
 
 // tile -> (sequence, KV head, tile within the head)
 __device__ inline void tile_coords(const AttnArgs& a, int tile, int* seq, int* h, int* tr) {
@@ -784,6 +797,7 @@ __device__ inline int tile_row(const AttnArgs& a, int seq, int h, int tr, int r,
   } else if (f < a.g) {
     id = seq * a.n_q + h * a.g + f;
     L = min(max(len_ld, 0), a.max_len);
+    if (a.win) L = packed_end(L, a.n_sink, a.n_recent);
   }
   *len = L;
   return id;
@@ -970,6 +984,52 @@ __global__ void __launch_bounds__(1024) decode_prep_kernel(AppendArgs ap, AttnAr
   else qrot_body<8>(aa, w - n_app);
 }
 
+// fp16 window copies: token t / KV head h (one 128-thread workgroup) to its sink slot
+// (pos < n_sink) or its recent ring slot pos % n_recent, binary16 round to nearest even.
+struct WindowAppendArgs {
+  uint16_t* k_sink;
+  uint16_t* v_sink;
+  uint16_t* k_rec;
+  uint16_t* v_rec;
+  const float* k;
+  const float* v;
+  const int32_t* seq_idx;
+  const int64_t* pos;
+  unsigned long long* overflow;
+  int32_t batch, n_kv, n_sink, sink_slots, n_recent;
+};
+
+__global__ void __launch_bounds__(kD) window_append_kernel(WindowAppendArgs w) {
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y, c = threadIdx.x;
+  const int seq = w.seq_idx[t];
+  const int64_t pos = w.pos[t];
+  if (seq < 0 || seq >= w.batch || pos < 0) {
+    if (c == 0 && h == 0) atomicAdd(w.overflow, 1ull);
+    return;
+  }
+  const size_t row = ((size_t)t * w.n_kv + h) * kD + c;
+  const _Float16 kh = (_Float16)w.k[row], vh = (_Float16)w.v[row];
+  const size_t sh = (size_t)seq * w.n_kv + h;
+  uint16_t *kd, *vd;
+  int slot, slots;
+  if (pos < w.n_sink) {
+    kd = w.k_sink;
+    vd = w.v_sink;
+    slot = (int)pos;
+    slots = w.sink_slots;
+  } else if (w.n_recent > 0) {
+    kd = w.k_rec;
+    vd = w.v_rec;
+    slot = (int)(pos % w.n_recent);
+    slots = w.n_recent;
+  } else {
+    return;
+  }
+  kd[(sh * slots + slot) * kD + c] = __builtin_bit_cast(uint16_t, kh);
+  vd[((sh * (slots / 8) + slot / 8) * kD + c) * 8 + (slot & 7)] = __builtin_bit_cast(uint16_t, vh);
+}
+
 // ---------------------------------------------------------------- partials
 
 constexpr int kKPitch = 17;  // staged key record pitch in words (k_words <= 16): odd, so the
@@ -1140,7 +1200,7 @@ __device__ inline void stage_block(AttnWave& W, const BlockData<VB, KWL>& B, int
 // One step of a wave's online softmax over the block staged in W.
 template <int VB, int NKB>
 __device__ inline void attn_block(const AttnShared& S, const AttnWave& W, const AttnArgs& a,
-                                  int t0, int lane, int q, int n, int my_row, int my_len,
+                                  int t0, int lane, int q, int n, int my_row, int my_len, int my_lo,
                                   const QkConst<NKB>& C, uint32_t nq_off, uint32_t vn_off,
                                   floatx4 (&oacc)[8], float& m_run, float& l_run) {
   const char* sb = reinterpret_cast<const char*>(&S);
@@ -1190,14 +1250,14 @@ __device__ inline void attn_block(const AttnShared& S, const AttnWave& W, const 
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     x[u] = lo ? lg[4 + u] : lg[u];
-    if (tb + u >= my_len) x[u] = -INFINITY;
+    if (tb + u >= my_len || tb + u < my_lo) x[u] = -INFINITY;
   }
   if (a.logits) {
     const int id = S.row_id[my_row];
     if (id >= 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (tb + u < my_len) a.logits[(size_t)id * a.logits_ld + tb + u] = x[u] * LN2_F;
+        if (tb + u < my_len && tb + u >= my_lo) a.logits[(size_t)id * a.logits_ld + tb + u] = x[u] * LN2_F;
     }
   }
   float mblk = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -1418,6 +1478,271 @@ __device__ inline void write_partials(const AttnArgs& a, const AttnSharedT<RT>& 
   }
 }
 
+// The fp16 window's split of one 8-row tile (decode with sink and recent buffers), in
+// the original basis: QK with A = the binary16 keys (four 32-coordinate K-blocks) and
+// B = the queries split into binary16 high and low parts (rows as in the packed
+// tiles), the same online softmax, PV with B = the binary16 values, then the waves'
+// merge and acc_rot = sqrt(128) Pi_V acc, so that the merge treats it as a packed split.
+// Slots that hold no visible position are masked, and their values zeroed before the
+// products (unfilled slots may hold anything). Runs in workgroups of the query-rotation
+// launch (1024 threads): waves 0..7 do the work, the others only join the barriers.
+__device__ inline bool window_slot(const AttnArgs& a, bool sink, int slot, int L, int* pos) {
+  if (sink) {
+    *pos = slot;
+    return slot < a.n_sink && slot < L;
+  }
+  const int base = L - a.n_recent;  // recent slot r holds the position in [L - W, L) congruent to r
+  int d = (slot - base) % a.n_recent;
+  if (d < 0) d += a.n_recent;
+  *pos = base + d;
+  return *pos >= a.n_sink && *pos >= 0;
+}
+
+__device__ inline void window_split(const AttnArgs& a, AttnShared& S, int tile) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, n = lane & 15;
+  int seq, h, tr;
+  tile_coords(a, tile, &seq, &h, &tr);
+  const DevHead* __restrict__ hp = a.heads + h;
+  const int L = min(max(a.seq_len[seq], 0), a.max_len);
+  const size_t sh = (size_t)seq * a.n_kv + h;
+  const bool lo = n >= 8;
+  const int my_row = lo ? 15 - n : n;
+  const int f = tr * 8 + my_row;
+  const int qid = f < a.g ? seq * a.n_q + h * a.g + f : -1;
+  const bool active = wave < kWaves;
+  if (tid < 8) {
+    const int fr = tr * 8 + tid;
+    S.row_id[tid] = fr < a.g ? seq * a.n_q + h * a.g + fr : -1;
+  }
+  // B operands (kept in the shared block): column n < 8 the high parts of row n, column
+  // n >= 8 the low parts of row 15 - n; lane (q, n) holds coordinates 32 i + 8 q .. + 7
+  // of K-block i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    H8 qb;
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (qid >= 0 && wave == 0) {
+      const float4* qp = reinterpret_cast<const float4*>(a.q + (size_t)qid * kD + 32 * i + 8 * q);
+      x0 = qp[0];
+      x1 = qp[1];
+    }
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float val = xv[j] * a.qscale;
+      const _Float16 hi = (_Float16)val;
+      qb.h[j] = lo ? (_Float16)(val - (float)hi) : hi;
+    }
+    if (wave == 0) S.qb[i][q][n] = qb.v;
+  }
+  __syncthreads();
+  const int nb_sink = a.sink_slots / kBlk, nb = nb_sink + a.n_recent / kBlk;
+  const int tau0 = 8 * (n >> 2) + (n & 3);
+  floatx4 oacc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) oacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+  for (int b = wave; active && b < nb; b += kWaves) {
+    const bool sink = b < nb_sink;
+    const int s0 = sink ? kBlk * b : kBlk * (b - nb_sink);
+    const uint16_t* kb = sink ? a.wk_sink + (sh * a.sink_slots + s0) * kD : a.wk_rec + (sh * a.n_recent + s0) * kD;
+    const uint16_t* vb = sink ? a.wv_sink + (sh * (a.sink_slots / 8) + s0 / 8) * (kD * 8)
+                              : a.wv_rec + (sh * (a.n_recent / 8) + s0 / 8) * (kD * 8);
+    // QK over the four K-blocks, both 16-token halves (A-row n: token tau0, tau0 + 4)
+    H8 ka[4], kc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ka[i].v = *reinterpret_cast<const uint4*>(kb + (size_t)tau0 * kD + 32 * i + 8 * q);
+      kc[i].v = *reinterpret_cast<const uint4*>(kb + (size_t)(tau0 + 4) * kD + 32 * i + 8 * q);
+    }
+    floatx4 d0 = z4, d1 = z4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      H8 qv;
+      qv.v = S.qb[i][q][n];
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i].h, qv.h, d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[i].h, qv.h, d1, 0, 0, 0);
+    }
+    float lg[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lg[j] += dpp_row_mirror(lg[j]);
+    const int tb = 8 * q + (lo ? 4 : 0);
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int pos;
+      const bool ok = window_slot(a, sink, s0 + tb + u, L, &pos);
+      x[u] = ok ? (lo ? lg[4 + u] : lg[u]) : -INFINITY;
+      if (ok && a.logits) {
+        const int id = S.row_id[my_row];
+        if (id >= 0) a.logits[(size_t)id * a.logits_ld + pos] = x[u] * LN2_F;
+      }
+    }
+    float mblk = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mblk = fmaxf(mblk, dpp_row_mirror(mblk));
+    mblk = max_over_q(mblk);
+    const bool grow = mblk > m_run;
+    if (__any(grow)) {
+      const float m_new = grow ? mblk : m_run;
+      const bool rescale = grow && m_run != -INFINITY;
+      if (__any(rescale)) {
+        const float fac = rescale ? exp2f(m_run - m_new) : 1.f;
+        l_run *= fac;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float fe = __shfl(fac, 4 * q + e);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) oacc[t][e] *= fe;
+        }
+      }
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float pv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pv[u] = (x[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[u] - m_use);
+      l_run += pv[u];
+    }
+    H8 hv, lv;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const auto hh = __builtin_amdgcn_cvt_pkrtz(pv[2 * k], pv[2 * k + 1]);
+      const auto ll = __builtin_amdgcn_cvt_pkrtz(pv[2 * k] - (float)hh[0], pv[2 * k + 1] - (float)hh[1]);
+      hv.u[k] = __builtin_bit_cast(uint32_t, hh);
+      lv.u[k] = __builtin_bit_cast(uint32_t, ll);
+    }
+    H8 pa;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t keep = lo ? lv.u[k] : hv.u[k];
+      const uint32_t recv = dpp_row_mirror_u(lo ? hv.u[k] : lv.u[k]);
+      pa.u[k] = lo ? recv : keep;
+      pa.u[2 + k] = lo ? keep : recv;
+    }
+    // zero the value halves of slots without a visible position
+    uint32_t vm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int pos;
+      const bool ok0 = window_slot(a, sink, s0 + 8 * q + 2 * j, L, &pos);
+      const bool ok1 = window_slot(a, sink, s0 + 8 * q + 2 * j + 1, L, &pos);
+      vm[j] = (ok0 ? 0x0000FFFFu : 0u) | (ok1 ? 0xFFFF0000u : 0u);
+    }
+    // value operands of the 8 tiles: tokens 8q .. 8q + 7 x coordinate 8n + t
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      H8 bv;
+      bv.v = *reinterpret_cast<const uint4*>(vb + ((size_t)q * kD + 8 * n + t) * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv.u[j] &= vm[j];
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, bv.h, oacc[t], 0, 0, 0);
+    }
+  }
+  // ---- waves' merge (as in the packed epilogue), then the rotation into the Pi_V basis
+  l_run += dpp_row_mirror(l_run);
+  l_run = sum_over_q(l_run);
+  if (active && q == 0 && n < 8) {
+    S.om[wave][n] = m_run;
+    S.ol[wave][n] = l_run;
+  }
+  float vrow[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
+  }
+  if (active && q < 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float* dst = &S.u.slot[wave][4 * q + e][8 * n];
+      *reinterpret_cast<float4*>(dst) = make_float4(vrow[0][e], vrow[1][e], vrow[2][e], vrow[3][e]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(vrow[4][e], vrow[5][e], vrow[6][e], vrow[7][e]);
+    }
+  }
+  // this thread's quarter of a row of Pi_V: output i = tid & 127, inputs 32 qq .. + 31
+  const int oi = tid & 127, qq = (tid >> 7) & 3;
+  float4 pr[8];
+  {
+    const float4* pp = reinterpret_cast<const float4*>(a.rot + hp->vrot_off + (size_t)oi * kD + 32 * qq);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pr[u] = active ? pp[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+  float* acc_o = reinterpret_cast<float*>(&S.qb[0][0][0]);  // [8][128] merged rows, then M[8], l[8]
+  if (tid < 8 * (kD / 4)) {
+    const int r8 = tid >> 5, c4 = tid & 31;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.om[w][r8]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = S.om[w][r8];
+        const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        const float4 xx = *reinterpret_cast<const float4*>(&S.u.slot[w][r8][4 * c4]);
+        acc.x = fmaf(sw, xx.x, acc.x);
+        acc.y = fmaf(sw, xx.y, acc.y);
+        acc.z = fmaf(sw, xx.z, acc.z);
+        acc.w = fmaf(sw, xx.w, acc.w);
+        l = fmaf(sw, S.ol[w][r8], l);
+      }
+    }
+    *reinterpret_cast<float4*>(acc_o + r8 * kD + 4 * c4) = acc;
+    if (c4 == 0) {
+      acc_o[8 * kD + r8] = M;
+      acc_o[8 * kD + 8 + r8] = l;
+    }
+  }
+  __syncthreads();
+  float* part = &S.u.slot[0][0][0];  // [4][8][128] quarter sums
+#pragma unroll
+  for (int r = 0; r < 8 && active; ++r) {
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 xx = *reinterpret_cast<const float4*>(acc_o + r * kD + 32 * qq + 4 * u);
+      sum = fmaf(pr[u].x, xx.x, sum);
+      sum = fmaf(pr[u].y, xx.y, sum);
+      sum = fmaf(pr[u].z, xx.z, sum);
+      sum = fmaf(pr[u].w, xx.w, sum);
+    }
+    part[(qq * 8 + r) * kD + oi] = sum;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = tid + kThreads * k;  // 8 rows x 128 outputs
+    const int r = e >> 7, i = e & 127;
+    const int id = active ? S.row_id[r] : -1;
+    if (id >= 0) {
+      float* dst = a.partials + ((size_t)id * a.n_chunks + (a.n_chunks - 1)) * kPS;
+      const float v = part[(0 * 8 + r) * kD + i] + part[(1 * 8 + r) * kD + i] + part[(2 * 8 + r) * kD + i] +
+                      part[(3 * 8 + r) * kD + i];
+      dst[4 + i] = v * 11.313708498984761f;  // sqrt(128): the merge divides by it
+      if (i == 0) {
+        dst[0] = acc_o[8 * kD + r];
+        dst[1] = acc_o[8 * kD + 8 + r];
+      }
+    }
+  }
+}
+
+// Decode with the fp16 window: workgroups [0, n_tiles) rotate the queries of one row
+// tile each, the rest compute the window split of one tile (the two roles share no
+// data, and neither reads the packed partials).
+__global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_window_kernel(AttnArgs a, int n_tiles) {
+  static_assert(64 * kQrotWaves >= kThreads, "the window split needs 8 waves");
+  __shared__ AttnShared S;
+  if ((int)blockIdx.x < n_tiles) qrot_body<8>(a, blockIdx.x);
+  else window_split(a, S, blockIdx.x - n_tiles);
+}
+
 // Phase 1 of the attention: per (row tile of RT rows, split) online-softmax partials.
 // (at most 128 registers: two workgroups per compute unit)
 template <int VB, int KWL, int NKB, int RT>
@@ -1484,6 +1809,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 
   const int my_row = RT == 16 ? n : (n < 8 ? n : 15 - n);
   const int my_len = S.row_len[my_row];
+  const int my_lo = a.win ? a.n_sink : 0;  // sink positions read the fp16 buffers
   AttnWave& W = S.u.w[wave];
   const char* sb = reinterpret_cast<const char*>(&S);
   int st[KWL];  // staging slot of word lane + 64 i: token (lw / kw) at pitch 17; words past
@@ -1525,7 +1851,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     __builtin_amdgcn_wave_barrier();
     if (t0 + kStep < c1) load_block<VB, KWL>(blk[0], R, t0 + kStep, kw, lane, voff_v);
     if constexpr (RT == 8)
-      attn_block<VB, NKB>(S, W, a, t0, lane, q, n, my_row, my_len, C, nq_off, vn_off, oacc, m_run, l_run);
+      attn_block<VB, NKB>(S, W, a, t0, lane, q, n, my_row, my_len, my_lo, C, nq_off, vn_off, oacc, m_run, l_run);
     else
       attn_block16<VB, NKB>(S, W, a, t0, lane, q, n, my_len, C, nq_off, vn_off, oacc, m_run, l_run);
   }
@@ -1593,6 +1919,7 @@ struct MergeArgs {
   float* out;
   int64_t pos0;
   int32_t n_q, g, n_chunks, chunk, prefill, max_len;
+  int32_t win, n_sink, n_recent;  // fp16 window: its split is the last slot
 };
 
 // One workgroup (256 threads) per row: thread (float4 column c4, chunk slice ks) loads
@@ -1612,7 +1939,9 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   int len;
   if (a.prefill) len = (int)(a.pos0 + row / a.n_q + 1);
   else len = min(max(a.seq_len[row / a.n_q], 0), a.max_len);
-  const int nv = (len + a.chunk - 1) / a.chunk;
+  const int len_p = a.win ? packed_end(len, a.n_sink, a.n_recent) : len;
+  const int nv = (len_p + a.chunk - 1) / a.chunk + a.win;  // packed splits, then the window's
+  auto slot = [&](int k) { return (a.win && k == nv - 1) ? a.n_chunks - 1 : k; };
   // inverse rotation operand: thread (i, half) holds Pi_V^T[i][64 half .. + 63]
   const int oi = tid & 127, oh = tid >> 7;
   float4 pvt[16];
@@ -1631,16 +1960,16 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
     lk[u] = 0.f;
     xk[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (k < nv) {
-      const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)k * kPS);
+      const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)slot(k) * kPS);
       mk[u] = ml.x;
       lk[u] = ml.y;
-      xk[u] = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS + 4 + 4 * c4);
+      xk[u] = *reinterpret_cast<const float4*>(pp + (size_t)slot(k) * kPS + 4 + 4 * c4);
     }
   }
   float ms = -INFINITY;
 #pragma unroll
   for (int u = 0; u < kMergeRegs; ++u) ms = fmaxf(ms, mk[u]);
-  for (int k = ks + 8 * kMergeRegs; k < nv; k += 8) ms = fmaxf(ms, pp[(size_t)k * kPS]);
+  for (int k = ks + 8 * kMergeRegs; k < nv; k += 8) ms = fmaxf(ms, pp[(size_t)slot(k) * kPS]);
   if (c4 == 0) sm[ks] = ms;
   __syncthreads();
   float M = sm[0];
@@ -1659,8 +1988,8 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
       l = fmaf(w, lk[u], l);
     }
     for (int k = ks + 8 * kMergeRegs; k < nv; k += 8) {  // more than 32 splits
-      const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)k * kPS);
-      const float4 x = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS + 4 + 4 * c4);
+      const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)slot(k) * kPS);
+      const float4 x = *reinterpret_cast<const float4*>(pp + (size_t)slot(k) * kPS + 4 + 4 * c4);
       const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
       acc.x = fmaf(w, x.x, acc.x);
       acc.y = fmaf(w, x.y, acc.y);
@@ -1717,6 +2046,7 @@ struct MergeTileArgs {
   float* out;
   int64_t pos0;
   int32_t n_q, g, n_kv, tiles_per_kv, n_tok, n_chunks, chunk, prefill, max_len, seq;
+  int32_t win, n_sink, n_recent;  // fp16 window: its split is the last slot
 };
 
 __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
@@ -1763,7 +2093,9 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
   float L = 0.f;
   if (id >= 0) {
     const float* pp = a.partials + (size_t)id * a.n_chunks * kPS;
-    const int nv = min(a.n_chunks, (len + a.chunk - 1) / a.chunk);
+    const int len_p = a.win ? packed_end(len, a.n_sink, a.n_recent) : len;
+    const int nv = min(a.n_chunks, (len_p + a.chunk - 1) / a.chunk + a.win);  // packed, then the window
+    auto slot = [&](int k) { return (a.win && k == nv - 1) ? a.n_chunks - 1 : k; };
     float mk[kMergeTileChunks], lk[kMergeTileChunks];
     float4 xk[kMergeTileChunks];
     float M = -INFINITY;
@@ -1773,10 +2105,10 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
       lk[k] = 0.f;
       xk[k] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (k < nv) {
-        const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)k * kPS);
+        const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)slot(k) * kPS);
         mk[k] = ml.x;
         lk[k] = ml.y;
-        xk[k] = *reinterpret_cast<const float4*>(pp + (size_t)k * kPS + 4 + 4 * c4);
+        xk[k] = *reinterpret_cast<const float4*>(pp + (size_t)slot(k) * kPS + 4 + 4 * c4);
       }
       M = fmaxf(M, mk[k]);
     }
@@ -1990,7 +2322,7 @@ gtq_status launch_qrot(AttnArgs& aa, const AttnLaunch& L, const float* q, float 
 
 gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L, hipStream_t stream) {
   if (p->k_words > 16) return fail(GTQ_EUNSUPPORTED, "gtq attention: more than 16 key code words per token");
-  dim3 grid(L.n_chunks, L.n_tiles);
+  dim3 grid(L.n_chunks - aa.win, L.n_tiles);  // (the window's split comes from its own launch)
   const bool wide = p->k_words > 8;  // key words per lane: 4 (k_words <= 8) or 8
   // K-blocks per head: sum_g ceil(d_g / 32), 4..7 for four groups; the kernel runs the
   // layer's largest count (extra K-blocks of a head have zero query operands)
@@ -2024,16 +2356,26 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
 
 gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const int32_t* seq_len,
                         int64_t pos0, int prefill, int max_len, float* out, const void* ws,
-                        hipStream_t stream) {
+                        hipStream_t stream, const gtq_window_view* w = nullptr) {
   const float* vrot_t = p->d_rot + p->heads[(size_t)layer * p->n_kv].vrot_t_off;
   const float* partials = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + L.qb_bytes);
   if (L.n_chunks <= kMergeTileChunks) {  // one workgroup per row tile
     MergeTileArgs mt{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, p->n_kv, L.merge_tiles_per_kv,
                      (int32_t)(L.rows / p->n_q), L.n_chunks, L.chunk, prefill, max_len, 0};
+    if (w) {
+      mt.win = 1;
+      mt.n_sink = w->n_sink;
+      mt.n_recent = w->n_recent;
+    }
     hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.merge_n_tiles), dim3(256), 0, stream, mt);
   } else {  // one workgroup per row
     MergeArgs ma{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill,
                  max_len};
+    if (w) {
+      ma.win = 1;
+      ma.n_sink = w->n_sink;
+      ma.n_recent = w->n_recent;
+    }
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows), dim3(256), 0, stream, ma);
   }
   hipError_t e = hipGetLastError();
@@ -2144,7 +2486,7 @@ gtq_status gtq_quantize_append_chunk(const gtq_plan* plan, int32_t layer,
 }
 
 static bool decode_shape(const gtq_plan* p, int32_t batch, int64_t max_len, int32_t chunk,
-                         AttnLaunch* L, gtq_status* st, const char* fn) {
+                         AttnLaunch* L, gtq_status* st, const char* fn, int win = 0) {
   if (max_len < 0) {
     *st = fail(GTQ_EINVAL, std::string(fn) + ": max_len < 0");
     return false;
@@ -2171,6 +2513,7 @@ static bool decode_shape(const gtq_plan* p, int32_t batch, int64_t max_len, int3
     *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk too small (more than 256 splits per sequence)");
     return false;
   }
+  L->n_chunks += win;  // the fp16 window's split
   return true;
 }
 
@@ -2187,14 +2530,14 @@ gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64
 
 static gtq_status decode_check(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
                                int64_t max_len, int32_t chunk, size_t ws_bytes, const void* ws,
-                               AttnLaunch* L, const char* fn) {
+                               AttnLaunch* L, const char* fn, int win = 0) {
   gtq_status st;
   if (!check_device_plan(plan, fn, &st)) return st;
   if (!check_cache(plan, cache, fn, &st)) return st;
   if (layer < 0 || layer >= plan->n_layers) return fail(GTQ_EINVAL, std::string(fn) + ": layer out of range");
   if (!ws) return fail(GTQ_EINVAL, std::string(fn) + ": workspace is NULL");
   if (max_len > cache->capacity) return fail(GTQ_ECAPACITY, std::string(fn) + ": max_len > capacity");
-  if (!decode_shape(plan, cache->batch, max_len, chunk, L, &st, fn)) return st;
+  if (!decode_shape(plan, cache->batch, max_len, chunk, L, &st, fn, win)) return st;
   if (ws_bytes < attn_ws_bytes(L->rows, L->n_chunks, L->qb_bytes))
     return fail(GTQ_ECAPACITY, std::string(fn) + ": workspace too small");
   return GTQ_OK;
@@ -2374,6 +2717,100 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
   st = launch_partials(plan, aa, L, s);
   if (st != GTQ_OK) return st;
   return launch_merge(plan, layer, L, nullptr, pos0, 1, (int)(pos0 + n_tok), out, workspace, s);
+}
+
+static bool check_window(const gtq_plan* plan, int32_t layer, const gtq_window_view* w, int32_t batch,
+                         const char* fn, gtq_status* st) {
+  if (!w || !w->k_sink || !w->v_sink || !w->k_recent || !w->v_recent) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": window view or one of its buffers is NULL");
+    return false;
+  }
+  if (w->n_sink < 0 || w->n_sink > 256 || w->n_recent < 0 || w->n_recent > 8192 || w->n_recent % kBlk) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": n_sink in [0, 256], n_recent a multiple of 32 in [0, 8192]");
+    return false;
+  }
+  if (w->batch != batch) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": window batch differs from the cache's");
+    return false;
+  }
+  if (layer < 0 || layer >= plan->n_layers) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": layer out of range");
+    return false;
+  }
+  return true;
+}
+
+static int sink_slots_of(const gtq_window_view* w) { return (w->n_sink + kBlk - 1) / kBlk * kBlk; }
+
+gtq_status gtq_window_append(const gtq_plan* plan, int32_t layer, const gtq_window_view* window,
+                             const float* k, const float* v, const int32_t* seq_idx, const int64_t* pos,
+                             int64_t n_tok, void* hip_stream) {
+  gtq_status st;
+  if (!check_device_plan(plan, "gtq_window_append", &st)) return st;
+  if (!window) return fail(GTQ_EINVAL, "gtq_window_append: window view is NULL");
+  if (!check_window(plan, layer, window, window->batch, "gtq_window_append", &st)) return st;
+  if (window->batch < 1) return fail(GTQ_EINVAL, "gtq_window_append: batch < 1");
+  if (n_tok < 0) return fail(GTQ_EINVAL, "gtq_window_append: n_tok < 0");
+  if (n_tok == 0) return ok();
+  if (!k || !v || !seq_idx || !pos) return fail(GTQ_EINVAL, "gtq_window_append: NULL pointer");
+  if (n_tok > 0x7FFFFFFF) return fail(GTQ_EUNSUPPORTED, "gtq_window_append: too many tokens");
+  WindowAppendArgs wa{window->k_sink, window->v_sink, window->k_recent, window->v_recent, k, v, seq_idx, pos,
+                      plan->d_overflow, window->batch, plan->n_kv, window->n_sink, sink_slots_of(window),
+                      window->n_recent};
+  hipLaunchKernelGGL(window_append_kernel, dim3((unsigned)n_tok, plan->n_kv), dim3(kD), 0, (hipStream_t)hip_stream,
+                     wa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gtq_window_append: launch");
+  return ok();
+}
+
+gtq_status gtq_decode_window_workspace_bytes(const gtq_plan* plan, int32_t batch, int64_t max_len,
+                                             int32_t chunk, size_t* out) {
+  if (!plan || !out) return fail(GTQ_EINVAL, "gtq_decode_window_workspace_bytes: NULL pointer");
+  if (batch < 1) return fail(GTQ_EINVAL, "gtq_decode_window_workspace_bytes: batch < 1");
+  AttnLaunch L;
+  gtq_status st;
+  if (!decode_shape(plan, batch, max_len, chunk, &L, &st, "gtq_decode_window_workspace_bytes", 1)) return st;
+  *out = attn_ws_bytes(L.rows, L.n_chunks, L.qb_bytes);
+  return ok();
+}
+
+gtq_status gtq_decode_attn_window(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                  const gtq_window_view* window, const float* q, const int32_t* seq_len,
+                                  int64_t max_len, float softmax_scale, int32_t chunk, float* out,
+                                  float* logits, void* workspace, size_t ws_bytes, void* hip_stream) {
+  const char* fn = "gtq_decode_attn_window";
+  AttnLaunch L;
+  gtq_status st = decode_check(plan, layer, cache, max_len, chunk, ws_bytes, workspace, &L, fn, 1);
+  if (st != GTQ_OK) return st;
+  if (!check_window(plan, layer, window, cache->batch, fn, &st)) return st;
+  if (!q || !seq_len || !out) return fail(GTQ_EINVAL, "gtq_decode_attn_window: NULL pointer");
+  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_decode_attn_window: softmax_scale not finite");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  AttnArgs aa{};
+  fill_attn_args(plan, layer, cache, aa, L, workspace);
+  aa.prefill = 0;
+  aa.max_len = (int32_t)max_len;
+  aa.q = q;
+  aa.qscale = softmax_scale * LOG2E_F;
+  aa.logits = logits;
+  aa.logits_ld = max_len;
+  aa.seq_len = seq_len;
+  aa.win = 1;
+  aa.wk_sink = window->k_sink;
+  aa.wv_sink = window->v_sink;
+  aa.wk_rec = window->k_recent;
+  aa.wv_rec = window->v_recent;
+  aa.n_sink = window->n_sink;
+  aa.sink_slots = sink_slots_of(window);
+  aa.n_recent = window->n_recent;
+  hipLaunchKernelGGL(attn_qrot_window_kernel, dim3((unsigned)(2 * L.n_tiles)), dim3(64 * kQrotWaves), 0, stream, aa,
+                     L.n_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gtq_decode_attn_window: launch");
+  st = launch_partials(plan, aa, L, stream);
+  if (st != GTQ_OK) return st;
+  return launch_merge(plan, layer, L, seq_len, 0, 0, (int)max_len, out, workspace, stream, window);
 }
 
 }  // extern "C"

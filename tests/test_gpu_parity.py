@@ -419,3 +419,93 @@ def test_capacity_limit_and_merge_paths(G):
         for b, n in enumerate(lens):
             _, ref = _oracle_decode(case, 0, b, n, encs[b], q[b], sc)
             assert_close(out[b].cpu().numpy(), ref, f"chunk {chunk} out b{b}")
+
+
+def _window_positions_to_fill(L, ns, nr):
+    pos = [p for p in range(min(ns, L))] + [p for p in range(max(ns, L - nr), L)]
+    return np.array(sorted(set(pos)), np.int64)
+
+
+@pytest.mark.parametrize("ns,nr,chunk", [(4, 64, 0), (4, 64, 64), (0, 96, 0), (40, 32, 96), (0, 0, 0)])
+def test_window_decode(G, ns, nr, chunk):
+    """fp16 sink + recent buffers beside the packed cache: sequences shorter than the
+    window, one that wraps the ring (filled in two calls, the second overwriting), and a
+    plain one; logits of every position and outputs against the oracle; the buffers
+    hold binary16 of the inputs exactly; unfilled slots (NaN) never reach a result."""
+    _say(f"case: fp16 window decode n_sink={ns} n_recent={nr} chunk={chunk}")
+    lens = [300, 37, 150]
+    case = Case(6, 1, 2, 4, 300, 128, 2, batch=3)
+    plan = case.plan()
+    cap = 320
+    cache = G.PackedCache(plan, 3, cap)
+    win = G.WindowCache(plan, 3, ns, nr)
+    encs = []
+    for b, L in enumerate(lens):
+        enc = _encode(case, 0, b, L)
+        _upload_oracle_cache(case, cache, 0, b, L, enc)
+        encs.append(enc)
+        k, v = case.kv(0, b, 0, L)
+        pos = _window_positions_to_fill(L, ns, nr)
+        if b == 0 and nr:  # ring wrap: positions nr earlier first, then the real window
+            early = np.arange(max(ns, L - nr - 20), L - 20, dtype=np.int64)
+            G.gtq_window_append(plan, 0, win, _dev(k[early]), _dev(v[early]), _dev(np.full(len(early), b, np.int32)),
+                                _dev(early))
+        if len(pos):
+            G.gtq_window_append(plan, 0, win, _dev(k[pos]), _dev(v[pos]), _dev(np.full(len(pos), b, np.int32)),
+                                _dev(pos))
+    torch.cuda.synchronize()
+    # buffer contents: binary16 of the inputs, bit for bit
+    for b, L in enumerate(lens):
+        k, v = case.kv(0, b, 0, L)
+        for p in _window_positions_to_fill(L, ns, nr):
+            if p < ns:
+                kb, vb = win.k_sink[b, :, p], win.v_sink[b, :, p // 8, :, p % 8]
+            else:
+                s_ = p % nr
+                kb, vb = win.k_recent[b, :, s_], win.v_recent[b, :, s_ // 8, :, s_ % 8]
+            assert np.array_equal(kb.cpu().numpy().view(np.uint16), k[p].astype(np.float16).view(np.uint16))
+            assert np.array_equal(vb.cpu().numpy().view(np.uint16), v[p].astype(np.float16).view(np.uint16))
+    q = np.stack([case.q(0, b) for b in range(3)])
+    sc = scale_default()
+    logits = torch.full((3, case.HQ, cap), float("nan"), device="cuda")
+    out = G.gtq_decode_attn_window(plan, 0, cache, win, _dev(q), _dev(np.array(lens, np.int32)), cap, sc,
+                                   chunk=chunk, logits=logits)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all()
+    for b, L in enumerate(lens):
+        for h in range(case.H):
+            e = encs[b][h]
+            sl = slice(h * case.g, (h + 1) * case.g)
+            inp = case.inputs[0, h][b]
+            lg_ref, o_ref = O.decode_attention_window(case.heads[0, h], q[b, sl], e["k_words"], e["k_norms"],
+                                                      e["v_words"], e["v_norms"], inp["k"], inp["v"], ns, nr,
+                                                      sc, L)
+            assert_close(lg[b, sl, :L], lg_ref, f"window logits b{b} h{h}")
+            assert_close(o[b, sl], o_ref, f"window out b{b} h{h}")
+    if ns == 0 and nr == 0:  # no window: the plain decode
+        ref = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(np.array(lens, np.int32)), cap, sc, chunk=chunk)
+        torch.cuda.synchronize()
+        assert_close(o, ref.cpu().numpy(), "empty window vs plain decode")
+    plan.destroy()
+
+
+def test_window_errors(G):
+    _say("case: fp16 window argument errors")
+    case = Case(7, 1, 2, 4, 64, 128, 2, batch=1)
+    plan = case.plan()
+    cache = G.PackedCache(plan, 1, 64)
+    q = _dev(np.stack([case.q(0, 0)]))
+    sl = _dev(np.array([64], np.int32))
+    for ns, nr, what in ((0, 48, "multiple of 32"), (300, 32, "n_sink"), (0, 8224, "n_recent")):
+        win = G.WindowCache(plan, 1, 4, 32)
+        win.n_sink, win.n_recent = ns, nr
+        with pytest.raises(G.GtqError) as e:
+            G.gtq_decode_attn_window(plan, 0, cache, win, q, sl, 64, 0.1)
+        assert e.value.status == 1 and what in str(e.value)
+    win = G.WindowCache(plan, 2, 4, 32)
+    with pytest.raises(G.GtqError) as e:
+        G.gtq_decode_attn_window(plan, 0, cache, win, q, sl, 64, 0.1)
+    assert "batch" in str(e.value)
+    plan.destroy()
