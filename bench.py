@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--workload", default="decode-8b",
                    choices=["decode-8b", "decode-3b-36L", "decode-70b-b32", "append-32b", "prefill-32b",
-                            "logit-mae"],
+                            "logit-mae", "decode-8b-window"],
                    help="decode-8b (default, the headline): Llama-3.1-8B-shaped layer decode; the others "
                         "measure the other workload shapes (one JSON line each)")
     p.add_argument("--norm-correct", action="store_true",
@@ -400,6 +400,69 @@ def bench_logit_mae(args):
     }
 
 
+def bench_window(args, n_sink=4, n_recent=128):
+    """decode-8b-window: the Llama-3.1-8B-shaped layer decode (32768 cached tokens, K2V2,
+    32 query / 8 KV heads) with fp16 sink and recent-token buffers: a step appends its
+    token to the packed cache and to the fp16 ring, then attends (window split in the
+    query-rotation launch, packed partials over positions [n_sink, L - n_recent), merge)."""
+    import torch
+
+    import packed_cache_attention_tq_amd as G
+
+    w = build_workload(args.seed)
+    plan, n, h_kv, g = w["plan"], w["n_ctx"], w["h_kv"], w["g"]
+    dev = torch.device("cuda")
+    k_all = torch.from_numpy(w["k"]).to(dev)
+    v_all = torch.from_numpy(w["v"]).to(dev)
+    base = G.PackedCache(plan, 1, n)
+    G.gtq_quantize_append_chunk(plan, 0, base, k_all[: n - 1].contiguous(), v_all[: n - 1].contiguous(), 0, 0)
+    win = G.WindowCache(plan, 1, n_sink, n_recent)
+    pos = torch.cat([torch.arange(n_sink), torch.arange(n - 1 - n_recent, n - 1)]).to(dev)
+    G.gtq_window_append(plan, 0, win, k_all[pos].contiguous(), v_all[pos].contiguous(),
+                        torch.zeros(len(pos), dtype=torch.int32, device=dev), pos.to(torch.int64))
+    caches = [base] + [base.clone() for _ in range(args.copies - 1)]
+    k_new, v_new = k_all[n - 1: n].contiguous(), v_all[n - 1: n].contiguous()
+    q = torch.from_numpy(w["q"]).to(dev)
+    seq_len = torch.full((1,), n, dtype=torch.int32, device=dev)
+    sidx = torch.zeros(1, dtype=torch.int32, device=dev)
+    slot = torch.full((1,), n - 1, dtype=torch.int64, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(G.gtq_decode_window_workspace_bytes(plan, 1, n, args.chunk), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(128)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = caches[i % len(caches)]
+        G.gtq_quantize_append(plan, 0, c, k_new, v_new, sidx, slot, stream=stream)
+        G.gtq_window_append(plan, 0, win, k_new, v_new, sidx, slot, stream=stream)
+        G.gtq_decode_attn_window(plan, 0, c, win, q, seq_len, n, scale, chunk=args.chunk, out=out, workspace=ws,
+                                 stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    packed = n - n_sink - n_recent
+    alg = packed * h_kv * base.sizes.bytes_per_token + (n_sink + n_recent) * h_kv * 512
+    return {
+        "metric": "packed-KV decode attention with fp16 sink + recent window: KV tokens/s",
+        "value": round(n / (ms / 1e3), 1), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (fp16 hi/lo split MFMA operands; binary16 window K/V)",
+        "data": "synthetic",
+        "config": {"workload": "decode-8b-window", "seq_len": n, "n_sink": n_sink, "n_recent": n_recent,
+                   "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches),
+                   "step": "packed append + window append (1 token) + window decode (3 launches)"},
+        "step_hbm_gbs": round(alg / (ms / 1e3) / 1e9, 1),
+    }
+
+
 def cpu_baseline(w, seed, min_seconds=10.0):
     """The fp64 oracle on the whole step (1-token encode + decode of all 32 query heads over
     every cached token, 8 KV heads), repeated until at least min_seconds of CPU time."""
@@ -454,7 +517,8 @@ def main():
         fn = {"decode-3b-36L": lambda: bench_decode_stack(args, "decode-3b-36L"),
               "decode-70b-b32": lambda: bench_decode_stack(args, "decode-70b-b32"),
               "append-32b": lambda: bench_append(args), "prefill-32b": lambda: bench_prefill(args),
-              "logit-mae": lambda: bench_logit_mae(args)}[args.workload]
+              "logit-mae": lambda: bench_logit_mae(args),
+              "decode-8b-window": lambda: bench_window(args)}[args.workload]
         print(json.dumps(fn()), flush=True)
         return
     t_setup = time.perf_counter()
