@@ -52,6 +52,8 @@ def parse():
                         "measure the other workload shapes (one JSON line each)")
     p.add_argument("--norm-correct", action="store_true",
                    help="append-32b: plan with norm-corrected stored norms (GTQ_PLAN_NORM_CORRECT)")
+    p.add_argument("--paged", type=int, default=0,
+                   help="decode-8b: a paged cache of this many tokens per page (pool pages in shuffled order)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run a plain device copy (torch.neg) of this many MiB three "
                         "times: a kernel of known traffic that calibrates the HBM byte counters")
@@ -528,7 +530,13 @@ def main():
     dev = torch.device("cuda")
     k_all = torch.from_numpy(w["k"]).to(dev)
     v_all = torch.from_numpy(w["v"]).to(dev)
-    base = G.PackedCache(plan, 1, n)
+    if args.paged:
+        n_pages = (n + args.paged - 1) // args.paged
+        base = G.PagedCache(plan, 1, n_pages, args.paged, n_pages)
+        base.block_table.copy_(torch.from_numpy(
+            np.random.default_rng(args.seed).permutation(n_pages).astype(np.int32)[None]))
+    else:
+        base = G.PackedCache(plan, 1, n)
     # fill the cache: tokens 0..n-2 as one prompt; the step appends token n-1
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -602,7 +610,8 @@ def main():
         "config": {"workload": "llama3.1-8b-shaped layer decode, batch 1, 32768 cached tokens, K2V2 "
                                "packed cache, 32 query / 8 KV heads, head_dim 128",
                    "global_batch": 1, "seq_len": n, "parallelism": "none (1 GPU)",
-                   "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches)},
+                   "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches),
+                   **({"page_tokens": args.paged} if args.paged else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                      "kernel": partials_kernel_name(plan, 0, h_kv, w["v_bits"]),

@@ -157,7 +157,7 @@ gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out);
 gtq_status gtq_plan_destroy(gtq_plan* plan);
 gtq_status gtq_plan_layout(const gtq_plan* plan, int32_t layer, int32_t kv_head,
                            gtq_head_layout* out);
-/* Number of device-side overruns (slot >= capacity, seq >= batch) skipped by append
+/* Number of device-side overruns (slot >= capacity, seq >= batch, an absent page) skipped by append
  * kernels since the plan was created. Synchronizes the device. */
 gtq_status gtq_plan_overflow_count(const gtq_plan* plan, int64_t* out);
 
@@ -172,7 +172,20 @@ gtq_status gtq_plan_overflow_count(const gtq_plan* plan, int64_t* out);
  *           8*v_bits*c + v_bits*j (little-endian u32 words)
  *   v_norms [batch][n_kv_heads][capacity]            fp32
  * capacity is a multiple of 32 and at most 2^25 (calls on a larger cache return
- * GTQ_EUNSUPPORTED). */
+ * GTQ_EUNSUPPORTED).
+ *
+ * Paged layout (block_table non-NULL), for serving ("Block-GTQ" abstract, 9th sentence,
+ * reports packed serving; the block-table organisation is this library's): the four
+ * buffers are a pool
+ * of n_pages pages of page_tokens tokens, each page laid out like a contiguous cache
+ * with batch = n_pages and capacity = page_tokens (size it with gtq_cache_bytes(plan,
+ * n_pages, page_tokens)). Position p of sequence b lives in pool page
+ * block_table[b * table_stride + p / page_tokens] (device int32) at p % page_tokens.
+ * capacity is then the per-sequence limit (at most table_stride * page_tokens);
+ * page_tokens is a multiple of 32 in [32, 2^25]. Table entries outside [0, n_pages):
+ * appends there are skipped and counted (gtq_plan_overflow_count) and reads return
+ * zero codes and norms, so every page that covers a visible position must be valid.
+ * With block_table NULL the last three fields are ignored. */
 typedef struct gtq_cache_view {
   uint32_t* k_codes;
   float* k_norms;
@@ -180,6 +193,10 @@ typedef struct gtq_cache_view {
   float* v_norms;
   int32_t batch;
   int64_t capacity;
+  const int32_t* block_table;
+  int32_t page_tokens;
+  int32_t n_pages;
+  int32_t table_stride;
 } gtq_cache_view;
 
 typedef struct gtq_cache_sizes {

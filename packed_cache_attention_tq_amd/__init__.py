@@ -49,7 +49,9 @@ class PlanDesc(C.Structure):
 
 class CacheView(C.Structure):
     _fields_ = [("k_codes", C.c_void_p), ("k_norms", C.c_void_p), ("v_codes", C.c_void_p),
-                ("v_norms", C.c_void_p), ("batch", C.c_int32), ("capacity", C.c_int64)]
+                ("v_norms", C.c_void_p), ("batch", C.c_int32), ("capacity", C.c_int64),
+                ("block_table", C.c_void_p), ("page_tokens", C.c_int32), ("n_pages", C.c_int32),
+                ("table_stride", C.c_int32)]
 
 
 class WindowView(C.Structure):
@@ -284,6 +286,32 @@ class PackedCache:
     def nbytes(self) -> int:
         s = self.sizes
         return s.k_codes_bytes + s.k_norms_bytes + s.v_codes_bytes + s.v_norms_bytes
+
+
+class PagedCache(PackedCache):
+    """One layer's paged cache: a pool of n_pages pages of page_tokens tokens (each laid
+    out like a contiguous cache of batch n_pages and capacity page_tokens) and a block
+    table [batch, max_pages] int32 (entry -1 = absent); sequence capacity
+    max_pages * page_tokens."""
+
+    def __init__(self, plan: Plan, batch: int, n_pages: int, page_tokens: int, max_pages: int, device="cuda"):
+        super().__init__(plan, n_pages, page_tokens, device)
+        self.n_pages, self.page_tokens, self.max_pages = n_pages, page_tokens, max_pages
+        self.batch, self.capacity = batch, max_pages * page_tokens
+        self.block_table = torch.full((batch, max_pages), -1, dtype=torch.int32, device=device)
+
+    def clone(self) -> "PagedCache":
+        c = PagedCache.__new__(PagedCache)
+        c.__dict__.update(self.__dict__)
+        c.k_codes, c.k_norms = self.k_codes.clone(), self.k_norms.clone()
+        c.v_codes, c.v_norms = self.v_codes.clone(), self.v_norms.clone()
+        c.block_table = self.block_table.clone()
+        return c
+
+    def view(self) -> CacheView:
+        return CacheView(self.k_codes.data_ptr(), self.k_norms.data_ptr(), self.v_codes.data_ptr(),
+                         self.v_norms.data_ptr(), self.batch, self.capacity, self.block_table.data_ptr(),
+                         self.page_tokens, self.n_pages, self.max_pages)
 
 
 # ------------------------------------------------------------------ GPU calls

@@ -50,6 +50,22 @@ gtq_status hip_fail(hipError_t e, const char* what) {
 // in LDS.
 // ============================================================================
 
+// Paged caches: position s of sequence seq lives in pool page table[seq * tstride +
+// s / P] at s % P; a contiguous cache (table NULL) is slice (seq, h) of `capacity`.
+struct PageMap {
+  const int32_t* table;
+  int32_t P, log2P, n_pages, tstride;  // P = 2^log2P tokens per page
+};
+
+// Flat token index of position s of (seq, KV head h) in the cache buffers, or -1 when
+// the page is absent (a table entry outside [0, n_pages)).
+__device__ inline int64_t token_index(const PageMap& m, int64_t capacity, int n_kv, int seq, int h, int64_t s) {
+  if (!m.table) return ((int64_t)seq * n_kv + h) * capacity + s;
+  const int pg = m.table[(int64_t)seq * m.tstride + (s >> m.log2P)];
+  if (pg < 0 || pg >= m.n_pages) return -1;
+  return ((int64_t)pg * n_kv + h) * m.P + (s & (m.P - 1));
+}
+
 struct AppendArgs {
   const DevHead* heads;  // this layer's heads [n_kv]
   const float* rot;
@@ -74,6 +90,7 @@ struct AppendArgs {
   int32_t k_words;
   int32_t v_bits;
   int32_t nc;  // norm-corrected stored norms: nu * sqrt(d) / ||C[code]||
+  PageMap pm;
 };
 
 __device__ inline int quantize(float z, const float* thr, int n_thr) {
@@ -455,14 +472,22 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       for (int e = tid; e < kAppTile * kw; e += kAppThreads) {
         const int t = e / kw, w = e - t * kw;
         const int64_t s = ts + t;
-        if (s >= a.pos0 && s < s_end) a.k_codes[(sh * a.capacity + s) * kw + w] = S.pk[t][w];
+        if (s >= a.pos0 && s < s_end) {
+          const int64_t ti = token_index(a.pm, a.capacity, a.n_kv, a.seq, h, s);
+          if (ti >= 0) a.k_codes[ti * kw + w] = S.pk[t][w];
+        }
       }
       if (tid < kAppTile * kNS) {
         const int t = tid / kNS, g = tid - kNS * t;
         const int64_t s = ts + t;
-        if (s >= a.pos0 && s < s_end)
-          a.k_norms[(sh * a.capacity + s) * kNS + g] =
-              g >= n_groups ? 0.f : (a.nc ? corrected_norm(S.nu64[t][g], S.cs[t][g], hp->dim[g]) : S.nu[t][g]);
+        if (s >= a.pos0 && s < s_end) {
+          const int64_t ti = token_index(a.pm, a.capacity, a.n_kv, a.seq, h, s);
+          if (ti >= 0)
+            a.k_norms[ti * kNS + g] =
+                g >= n_groups ? 0.f : (a.nc ? corrected_norm(S.nu64[t][g], S.cs[t][g], hp->dim[g]) : S.nu[t][g]);
+          else if (g == 0 && h == 0)
+            atomicAdd(a.overflow, 1ull);  // once per token in an absent page
+        }
       }
     } else {
       const int vw = 32 * vb;
@@ -470,7 +495,9 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
         const int b = e / vw, w = e - b * vw;
         const int64_t sb = ts + 8 * b;
         if (sb + 8 <= a.pos0 || sb >= s_end) continue;  // no token of this block in the chunk
-        uint32_t* blk = a.v_codes + (sh * (size_t)(a.capacity / GTQ_VBLOCK) + (size_t)(sb / GTQ_VBLOCK)) * vw;
+        const int64_t bi = token_index(a.pm, a.capacity, a.n_kv, a.seq, h, sb);  // (8-aligned: a block index x 8)
+        if (bi < 0) continue;
+        uint32_t* blk = a.v_codes + (size_t)(bi / GTQ_VBLOCK) * vw;
         if (sb >= a.pos0 && sb + 8 <= s_end) {
           blk[w] = S.pv[b][w];
         } else {
@@ -494,8 +521,8 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       }
       if (tid < kAppTile) {
         const int64_t s = ts + tid;
-        if (s >= a.pos0 && s < s_end)
-          a.v_norms[sh * a.capacity + s] = a.nc ? corrected_norm(S.nu64[tid][4], S.cs[tid][4], kD) : S.nu[tid][4];
+        const int64_t ti = (s >= a.pos0 && s < s_end) ? token_index(a.pm, a.capacity, a.n_kv, a.seq, h, s) : -1;
+        if (ti >= 0) a.v_norms[ti] = a.nc ? corrected_norm(S.nu64[tid][4], S.cs[tid][4], kD) : S.nu[tid][4];
       }
     }
   }
@@ -548,7 +575,9 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   }
   const int seq = a.step_len ? (int)tok : a.seq_idx[tok];
   const int64_t slot = a.step_len ? (int64_t)a.step_len[tok] - 1 : a.slot[tok];
-  if (seq < 0 || seq >= a.batch || slot < 0 || slot >= a.capacity) {
+  const int64_t ti = (seq < 0 || seq >= a.batch || slot < 0 || slot >= a.capacity)
+                         ? -1 : token_index(a.pm, a.capacity, a.n_kv, seq, h, slot);
+  if (ti < 0) {
     if (tid == 0 && h == 0) atomicAdd(a.overflow, 1ull);  // once per token
     return;
   }
@@ -669,19 +698,18 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     }
   }
   __syncthreads();
-  const size_t sh = (size_t)seq * a.n_kv + h;
-  if (tid < a.k_words) a.k_codes[(sh * a.capacity + slot) * a.k_words + tid] = krec[tid];
+  if (tid < a.k_words) a.k_codes[ti * a.k_words + tid] = krec[tid];
   if (tid >= 64 && tid < 64 + kNS) {
     const int g = tid - 64;
-    a.k_norms[(sh * a.capacity + slot) * kNS + g] =
+    a.k_norms[ti * kNS + g] =
         g >= n_groups ? 0.f : (a.nc ? corrected_norm(nu64_s[g], cs_s[g], hd->dim[g]) : nu_s[g]);
   }
-  if (tid == 128) a.v_norms[sh * a.capacity + slot] = a.nc ? corrected_norm(nu64_s[4], cs_s[4], kD) : nu_s[4];
+  if (tid == 128) a.v_norms[ti] = a.nc ? corrected_norm(nu64_s[4], cs_s[4], kD) : nu_s[4];
   if (tid >= 256 && tid < 256 + 32 * vb) {
     const int w = tid - 256;
     const uint32_t m = vmask[w];
     if (m) {
-      uint32_t* blk = a.v_codes + (sh * (size_t)(a.capacity / GTQ_VBLOCK) + (size_t)(slot / GTQ_VBLOCK)) * (32 * vb);
+      uint32_t* blk = a.v_codes + (size_t)(ti / GTQ_VBLOCK) * (32 * vb);  // (slices hold whole blocks)
       atomicAnd(blk + w, ~m);
       atomicOr(blk + w, vblk[w] & m);
     }
@@ -760,6 +788,7 @@ struct AttnArgs {
   const uint16_t* wv_rec;
   int32_t win;             // 1: split n_chunks - 1 is the fp16 window's
   int32_t n_sink, sink_slots, n_recent;
+  PageMap pm;              // paged cache (pm.table set) or contiguous
 };
 
 // End of the packed positions of a sequence of length L with n_sink sink and n_recent
@@ -1745,7 +1774,7 @@ __global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_window_kernel(AttnA
 
 // Phase 1 of the attention: per (row tile of RT rows, split) online-softmax partials.
 // (at most 128 registers: two workgroups per compute unit)
-template <int VB, int KWL, int NKB, int RT>
+template <int VB, int KWL, int NKB, int RT, bool PAGED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) attn_partials_kernel(AttnArgs a) {
   constexpr int kTileQB = (RT / 8) * kQB;
   __shared__ AttnSharedT<RT> S;
@@ -1760,12 +1789,31 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const DevHead* __restrict__ hp = a.heads + h;
   const size_t sh = (size_t)seq * a.n_kv + h;
   const int kw = a.k_words;
+  // buffer views of one slice: (sequence, KV head) of a contiguous cache, or (pool page,
+  // KV head) of a paged one (an absent page reads as zeros)
+  auto slice_views = [&](size_t slice, uint32_t len) {
+    SliceRsrc V;
+    V.kc = slice_rsrc(a.k_codes + slice * len * kw, len * (uint32_t)kw * 4u);
+    V.kn = slice_rsrc(a.k_norms + slice * len * kNS, len * (kNS * 4u));
+    V.vc = slice_rsrc(a.v_codes + slice * (len / GTQ_VBLOCK) * (32 * VB), len * (16u * VB));
+    V.vn = slice_rsrc(a.v_norms + slice * len, len * 4u);
+    return V;
+  };
+  auto page_views = [&](int pg) {
+    const bool ok = pg >= 0 && pg < a.pm.n_pages;
+    SliceRsrc V = slice_views((size_t)(ok ? pg : 0) * a.n_kv + h, (uint32_t)a.pm.P);
+    if (!ok) V = slice_views(0, 0u);
+    return V;
+  };
+  // the sequence's row of the block table; the page of position t (a vector load, so
+  // that it waits with the block loads)
+  const __amdgpu_buffer_rsrc_t Rt =
+      PAGED ? slice_rsrc(a.pm.table + (size_t)seq * a.pm.tstride, (uint32_t)a.pm.tstride * 4u) : slice_rsrc(a.k_codes, 0u);
+  auto page_of = [&](int t) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(Rt, 0, (t >> a.pm.log2P) * 4, 0);
+  };
   SliceRsrc R;
-  const uint32_t cap = (uint32_t)a.capacity;
-  R.kc = slice_rsrc(a.k_codes + sh * a.capacity * kw, cap * (uint32_t)kw * 4u);
-  R.kn = slice_rsrc(a.k_norms + sh * a.capacity * kNS, cap * (kNS * 4u));
-  R.vc = slice_rsrc(a.v_codes + sh * (a.capacity / GTQ_VBLOCK) * (32 * VB), cap * (16u * VB));
-  R.vn = slice_rsrc(a.v_norms + sh * a.capacity, cap * 4u);
+  if constexpr (!PAGED) R = slice_views(sh, (uint32_t)a.capacity);
   const int voff_v = 4 * (q * (32 * VB) + n * (2 * VB));
   const int c0 = chunk_idx * a.chunk;
   // ---- one round of independent loads: B operand, decode table, rows, first block
@@ -1784,7 +1832,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   else tabv = make_uint4(a.cb->quad2[tid - 256][0], a.cb->quad2[tid - 256][1], 0u, 0u);
   const int len_ld = a.prefill ? 0 : a.seq_len[seq];
   BlockData<VB, KWL> blk[1];
-  load_block<VB, KWL>(blk[0], R, c0 + kBlk * wave, kw, lane, voff_v);
+  int pg_next = 0;
+  if constexpr (PAGED) {
+    const int t_first = c0 + kBlk * wave;
+    load_block<VB, KWL>(blk[0], page_views(__builtin_amdgcn_readfirstlane(page_of(t_first))),
+                        t_first & (a.pm.P - 1), kw, lane, voff_v);
+    pg_next = page_of(t_first + kBlk * kWaves);
+  } else {
+    load_block<VB, KWL>(blk[0], R, c0 + kBlk * wave, kw, lane, voff_v);
+  }
 #pragma unroll
   for (int u = 0; u < kTileQB / kThreads; ++u) (&S.qb[0][0][0])[tid + kThreads * u] = qbv[u];
 #pragma unroll
@@ -1849,7 +1905,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   for (int t0 = c0 + kBlk * wave; t0 < c1; t0 += kStep) {
     stage_block<VB, KWL>(W, blk[0], kw, lane, st);
     __builtin_amdgcn_wave_barrier();
-    if (t0 + kStep < c1) load_block<VB, KWL>(blk[0], R, t0 + kStep, kw, lane, voff_v);
+    if (t0 + kStep < c1) {
+      if constexpr (PAGED) {  // (each 32-token block lies in one page: P is a multiple of 32)
+        load_block<VB, KWL>(blk[0], page_views(__builtin_amdgcn_readfirstlane(pg_next)),
+                            (t0 + kStep) & (a.pm.P - 1), kw, lane, voff_v);
+        pg_next = page_of(t0 + 2 * kStep);
+      } else {
+        load_block<VB, KWL>(blk[0], R, t0 + kStep, kw, lane, voff_v);
+      }
+    }
     if constexpr (RT == 8)
       attn_block<VB, NKB>(S, W, a, t0, lane, q, n, my_row, my_len, my_lo, C, nq_off, vn_off, oacc, m_run, l_run);
     else
@@ -2178,12 +2242,32 @@ bool check_cache(const gtq_plan* p, const gtq_cache_view* c, const char* fn, gtq
     *st = fail(GTQ_EINVAL, std::string(fn) + ": cache batch >= 1 and capacity a positive multiple of 32");
     return false;
   }
-  if (c->capacity > kMaxCapacity) {  // one (sequence, KV head) slice stays under 2 GiB
+  if (c->block_table) {
+    const int P = c->page_tokens;
+    if (P < 32 || (P & (P - 1)) || P > kMaxCapacity || c->n_pages < 1 || c->table_stride < 1 ||
+        c->capacity > (int64_t)c->table_stride * P) {
+      *st = fail(GTQ_EINVAL, std::string(fn) + ": paged cache needs page_tokens a power of two in [32, 2^25], "
+                                             "n_pages >= 1, table_stride >= 1, capacity <= table_stride * page_tokens");
+      return false;
+    }
+  } else if (c->capacity > kMaxCapacity) {  // one (sequence, KV head) slice stays under 2 GiB
     *st = fail(GTQ_EUNSUPPORTED, std::string(fn) + ": capacity above 2^25 tokens");
     return false;
   }
   (void)p;
   return true;
+}
+
+PageMap page_map(const gtq_cache_view* c) {
+  PageMap m{};
+  if (c->block_table) {
+    m.table = c->block_table;
+    m.P = c->page_tokens;
+    m.log2P = __builtin_ctz((unsigned)c->page_tokens);
+    m.n_pages = c->n_pages;
+    m.tstride = c->table_stride;
+  }
+  return m;
 }
 
 void fill_append_args(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* k, const float* v,
@@ -2205,6 +2289,7 @@ void fill_append_args(const gtq_plan* p, int layer, const gtq_cache_view* c, con
   a.k_words = p->k_words;
   a.v_bits = p->v_bits;
   a.nc = (p->flags & GTQ_PLAN_NORM_CORRECT) ? 1 : 0;
+  a.pm = page_map(c);
 }
 
 gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, const float* k,
@@ -2233,6 +2318,7 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   a.k_words = p->k_words;
   a.v_bits = p->v_bits;
   a.nc = (p->flags & GTQ_PLAN_NORM_CORRECT) ? 1 : 0;
+  a.pm = page_map(c);
   if (!chunk) {
     if (n_tok > 0x7FFFFFFF) return fail(GTQ_EUNSUPPORTED, "gtq_quantize_append: too many tokens");
     hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)n_tok, p->n_kv), dim3(1024), 0, stream, a);
@@ -2304,6 +2390,7 @@ void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnA
   aa.tiles_per_kv = L.tiles_per_kv;
   aa.chunk = L.chunk;
   aa.n_chunks = L.n_chunks;
+  aa.pm = page_map(c);
   aa.nkb_max = 0;
   for (int h = 0; h < p->n_kv; ++h) aa.nkb_max = std::max(aa.nkb_max, (int32_t)p->heads[(size_t)layer * p->n_kv + h].nkb);
 }
@@ -2328,9 +2415,11 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
   // layer's largest count (extra K-blocks of a head have zero query operands)
   const int nkb = aa.nkb_max;
   if (nkb < 4 || nkb > 7) return fail(GTQ_EUNSUPPORTED, "gtq attention: K-block count outside 4..7");
-#define GTQ_LAUNCH3(VB, KWL, NKB)                                                                              \
-  if (L.rt == 16) hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 16>), grid, dim3(kThreads), 0, stream, aa); \
-  else hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 8>), grid, dim3(kThreads), 0, stream, aa)
+#define GTQ_LAUNCH4(VB, KWL, NKB, PG)                                                                             \
+  if (L.rt == 16) hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 16, PG>), grid, dim3(kThreads), 0, stream, aa); \
+  else hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 8, PG>), grid, dim3(kThreads), 0, stream, aa)
+#define GTQ_LAUNCH3(VB, KWL, NKB) \
+  if (aa.pm.table) { GTQ_LAUNCH4(VB, KWL, NKB, true); } else { GTQ_LAUNCH4(VB, KWL, NKB, false); }
 #define GTQ_LAUNCH2(VB, KWL)                  \
   switch (nkb) {                              \
     case 4: GTQ_LAUNCH3(VB, KWL, 4); break;   \
@@ -2349,6 +2438,7 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
 #undef GTQ_LAUNCH
 #undef GTQ_LAUNCH2
 #undef GTQ_LAUNCH3
+#undef GTQ_LAUNCH4
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq attention partials: launch");
   return ok();

@@ -509,3 +509,102 @@ def test_window_errors(G):
         G.gtq_decode_attn_window(plan, 0, cache, win, q, sl, 64, 0.1)
     assert "batch" in str(e.value)
     plan.destroy()
+
+
+def _gather_paged(case, pc, b, n):
+    """Records of sequence b, positions 0..n-1, gathered from a paged cache through its
+    block table: (k words, k norms, v codes [n][128], v norms)."""
+    s = pc.sizes
+    P, H = pc.page_tokens, case.H
+    kc = pc.k_codes.cpu().numpy().view(np.uint32).reshape(pc.n_pages, H, P, s.k_words)
+    kn = pc.k_norms.cpu().numpy().reshape(pc.n_pages, H, P, 4)
+    vc = pc.v_codes.cpu().numpy().view(np.uint32).reshape(pc.n_pages, H, P // 8, s.v_words_per_block)
+    vn = pc.v_norms.cpu().numpy().reshape(pc.n_pages, H, P)
+    tab = pc.block_table.cpu().numpy()
+    out = []
+    for h in range(H):
+        pages = [tab[b, p // P] for p in range(n)]
+        kw = np.stack([kc[pg, h, p % P] for p, pg in zip(range(n), pages)])
+        knn = np.stack([kn[pg, h, p % P] for p, pg in zip(range(n), pages)])
+        vnn = np.array([vn[pg, h, p % P] for p, pg in zip(range(n), pages)])
+        vcodes = np.concatenate([v_codes_from_physical(vc[tab[b, j], h], P, case.v_bits)
+                                 for j in range((n + P - 1) // P)])[:n]
+        out.append((kw, knn, vcodes, vnn))
+    return out
+
+
+def test_paged_cache(G):
+    """A paged cache (64-token pages, shuffled pool pages, absent entries -1) filled by
+    the chunk append (across page boundaries), the scatter append and the fused decode
+    step holds the same records as a contiguous cache filled the same way; decode,
+    window decode and prefill give the same outputs, and match the oracle; appends into
+    an absent page are skipped and counted."""
+    _say("case: paged cache (block table) vs contiguous")
+    lens, P, maxp = [300, 150], 64, 5
+    case = Case(8, 1, 2, 4, 300, 128, 2, batch=2)
+    plan = case.plan()
+    cont = G.PackedCache(plan, 2, P * maxp)
+    pc = G.PagedCache(plan, 2, 12, P, maxp)
+    perm = np.random.default_rng(3).permutation(12)
+    tab = np.full((2, maxp), -1, np.int32)
+    tab[0, :5] = perm[:5]
+    tab[1, :3] = perm[5:8]
+    pc.block_table.copy_(torch.from_numpy(tab))
+    k0, v0 = case.kv(0, 0)
+    k1, v1 = case.kv(0, 1)
+    for c in (cont, pc):
+        for lo, hi in [(0, 77), (77, 200)]:  # chunks across page boundaries
+            G.gtq_quantize_append_chunk(plan, 0, c, _dev(k0[lo:hi]), _dev(v0[lo:hi]), 0, lo)
+        idx = np.concatenate([np.stack([np.zeros(99, int), np.arange(200, 299)], 1),
+                              np.stack([np.ones(149, int), np.arange(149)], 1)])
+        idx = idx[np.random.default_rng(9).permutation(len(idx))]
+        kk = np.stack([(k0 if b == 0 else k1)[p] for b, p in idx])
+        vv = np.stack([(v0 if b == 0 else v1)[p] for b, p in idx])
+        G.gtq_quantize_append(plan, 0, c, _dev(kk), _dev(vv), _dev(idx[:, 0].astype(np.int32)),
+                              _dev(idx[:, 1].astype(np.int64)))
+    before = plan.overflow_count()
+    # positions 192.. of sequence 1 lie in its absent page 3
+    G.gtq_quantize_append(plan, 0, pc, _dev(k1[250:251]), _dev(v1[250:251]), _dev(np.ones(1, np.int32)),
+                          _dev(np.array([250], np.int64)))
+    G.gtq_quantize_append_chunk(plan, 0, pc, _dev(k1[192:200]), _dev(v1[192:200]), 1, 192)
+    torch.cuda.synchronize()
+    assert plan.overflow_count() - before == 1 + 8
+    # the step: both sequences append their last token and attend (fused prepare)
+    q = np.stack([case.q(0, 0), case.q(0, 1)])
+    knew = np.stack([k0[299], k1[149]])
+    vnew = np.stack([v0[299], v1[149]])
+    sl = _dev(np.array(lens, np.int32))
+    sc = scale_default()
+    o_c = G.gtq_decode_step(plan, 0, cont, _dev(knew), _dev(vnew), _dev(q), sl, P * maxp, sc)
+    o_p = G.gtq_decode_step(plan, 0, pc, _dev(knew), _dev(vnew), _dev(q), sl, P * maxp, sc)
+    torch.cuda.synchronize()
+    kc, kn, vc, vn = _cache_arrays(cont, case)
+    for b, n in enumerate(lens):
+        for h, (kw, knn, vcodes, vnn) in enumerate(_gather_paged(case, pc, b, n)):
+            assert np.array_equal(kw, kc[b, h, :n]), f"paged K codes b{b} h{h}"
+            assert np.array_equal(knn, kn[b, h, :n]), f"paged K norms b{b} h{h}"
+            assert np.array_equal(vnn, vn[b, h, :n]), f"paged V norms b{b} h{h}"
+            assert np.array_equal(vcodes, v_codes_from_physical(vc[b, h], n, case.v_bits)), f"paged V b{b} h{h}"
+    assert torch.equal(o_c, o_p)
+    for b, n in enumerate(lens):
+        enc = _encode(case, 0, b, n)
+        t, _ = _check_append(case, cont, 0, b, n, enc, f"contiguous b{b}")
+        if t == 0:
+            _, ref = _oracle_decode(case, 0, b, n, enc, q[b], sc)
+            assert_close(o_p[b].cpu().numpy(), ref, f"paged step out b{b}")
+    # window decode and prefill over the paged cache equal the contiguous ones
+    win = G.WindowCache(plan, 2, 4, 64)
+    for b, n in enumerate(lens):
+        kx, vx = case.kv(0, b, 0, n)
+        pos = _window_positions_to_fill(n, 4, 64)
+        G.gtq_window_append(plan, 0, win, _dev(kx[pos]), _dev(vx[pos]), _dev(np.full(len(pos), b, np.int32)),
+                            _dev(pos))
+    w_c = G.gtq_decode_attn_window(plan, 0, cont, win, _dev(q), sl, P * maxp, sc, chunk=64)
+    w_p = G.gtq_decode_attn_window(plan, 0, pc, win, _dev(q), sl, P * maxp, sc, chunk=64)
+    qp = (np.random.default_rng(4).standard_normal((40, case.HQ, 128)) * 2).astype(np.float32)
+    p_c = G.gtq_prefill_attn(plan, 0, cont, _dev(qp), 0, 260, sc, chunk=64)
+    p_p = G.gtq_prefill_attn(plan, 0, pc, _dev(qp), 0, 260, sc, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(w_c, w_p)
+    assert torch.equal(p_c, p_p)
+    plan.destroy()
