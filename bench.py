@@ -54,6 +54,8 @@ def parse():
                    help="append-32b: plan with norm-corrected stored norms (GTQ_PLAN_NORM_CORRECT)")
     p.add_argument("--paged", type=int, default=0,
                    help="decode-8b: a paged cache of this many tokens per page (pool pages in shuffled order)")
+    p.add_argument("--v-hadamard", action="store_true",
+                   help="decode-8b: randomized Hadamard value rotations (applied as fast transforms)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run a plain device copy (torch.neg) of this many MiB three "
                         "times: a kernel of known traffic that calibrates the HBM byte counters")
@@ -79,7 +81,7 @@ def measured_traffic():
         return None
 
 
-def build_workload(seed, n_ctx=32768, h_kv=8, g=4, k_budget=128, v_bits=2):
+def build_workload(seed, n_ctx=32768, h_kv=8, g=4, k_budget=128, v_bits=2, v_hadamard=False):
     import torch
 
     import packed_cache_attention_tq_amd as G
@@ -92,7 +94,7 @@ def build_workload(seed, n_ctx=32768, h_kv=8, g=4, k_budget=128, v_bits=2):
         r, _, _ = G.gtq_alloc_rates(inp["calib_q"], inp["calib_k"], 1, 4, k_budget)
         rates[0, h] = r
         lay = G.gtq_head_layout_from_rates(r)
-        kr, vr = head_rotations(seed, 0, h, lay["dim"])
+        kr, vr = head_rotations(seed, 0, h, lay["dim"], v_hadamard=v_hadamard)
         krot[0].append(kr)
         vrot[0].append(vr)
         inps.append(inp)
@@ -524,7 +526,7 @@ def main():
         print(json.dumps(fn()), flush=True)
         return
     t_setup = time.perf_counter()
-    w = build_workload(args.seed)
+    w = build_workload(args.seed, v_hadamard=args.v_hadamard)
     plan, n, h_kv, g = w["plan"], w["n_ctx"], w["h_kv"], w["g"]
     hq = h_kv * g
     dev = torch.device("cuda")
@@ -611,7 +613,8 @@ def main():
                                "packed cache, 32 query / 8 KV heads, head_dim 128",
                    "global_batch": 1, "seq_len": n, "parallelism": "none (1 GPU)",
                    "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches),
-                   **({"page_tokens": args.paged} if args.paged else {})},
+                   **({"page_tokens": args.paged} if args.paged else {}),
+                   **({"v_rotation": "randomized Hadamard"} if args.v_hadamard else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                      "kernel": partials_kernel_name(plan, 0, h_kv, w["v_bits"]),

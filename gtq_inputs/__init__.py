@@ -176,11 +176,26 @@ def head_inputs_device(cfg_seed: int, layer: int, kv_head: int, g: int, n_cache:
     return out
 
 
-def head_rotations(cfg_seed: int, layer: int, kv_head: int, group_dims: list[int]) -> tuple[list[np.ndarray], np.ndarray]:
-    """Haar rotations for the K groups (in the order given) and the V rotation."""
+def hadamard_rotation(d: int, rng: np.random.Generator) -> np.ndarray:
+    """Randomized Hadamard rotation H_d diag(s) / sqrt(d) (d a power of two): H_d the
+    Sylvester matrix, H[i][j] = (-1)^popcount(i & j), s a seeded random sign vector;
+    entries +-fp32(1/sqrt(d))."""
+    if d & (d - 1):
+        raise ValueError("d must be a power of two")
+    i = np.arange(d)
+    h = np.where(np.vectorize(lambda x: bin(x).count("1") % 2)(i[:, None] & i[None, :]) == 1, -1.0, 1.0)
+    s = np.where(rng.integers(0, 2, size=d) == 1, -1.0, 1.0)
+    c = np.float32(1.0 / np.sqrt(d))
+    return (h * s[None, :]).astype(np.float32) * c
+
+
+def head_rotations(cfg_seed: int, layer: int, kv_head: int, group_dims: list[int],
+                   v_hadamard: bool = False) -> tuple[list[np.ndarray], np.ndarray]:
+    """Haar rotations for the K groups (in the order given) and the V rotation (Haar, or
+    a randomized Hadamard one with v_hadamard)."""
     rng = rng_for(cfg_seed, layer, kv_head, S_ROT)
     k_rots = [haar_rotation(d, rng) for d in group_dims]
-    v_rot = haar_rotation(HEAD_DIM, rng)
+    v_rot = hadamard_rotation(HEAD_DIM, rng) if v_hadamard else haar_rotation(HEAD_DIM, rng)
     return k_rots, v_rot
 
 

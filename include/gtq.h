@@ -111,6 +111,13 @@ typedef struct gtq_head_layout {
                                          this head's slice of gtq_plan_desc.k_rot   */
   int32_t k_words;                  /* u32 words of one token's key record          */
   int32_t coord[GTQ_HEAD_DIM];      /* head coordinate of each record position      */
+  int32_t v_hadamard;               /* gtq_plan_layout only: 1 when the head's value
+                                       rotation is H_128 diag(s) / sqrt(128) for a sign
+                                       vector s (Sylvester H, entries exactly
+                                       +-fp32(1/sqrt(128))): the library then applies
+                                       it as a fast Walsh-Hadamard transform where it
+                                       can ("TurboQuant" diagram, rotate box: random
+                                       rotation or Hadamard)                          */
 } gtq_head_layout;
 
 /* Computes the layout from rates[64] (each in [1, 4]). Host only.

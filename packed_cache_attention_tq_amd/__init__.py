@@ -30,13 +30,13 @@ class GtqError(RuntimeError):
 class HeadLayout(C.Structure):
     _fields_ = [("n_groups", C.c_int32), ("rate", C.c_int32 * 4), ("dim", C.c_int32 * 4),
                 ("bit_offset", C.c_int32 * 4), ("rot_offset", C.c_int32 * 4),
-                ("k_words", C.c_int32), ("coord", C.c_int32 * 128)]
+                ("k_words", C.c_int32), ("coord", C.c_int32 * 128), ("v_hadamard", C.c_int32)]
 
     def as_dict(self) -> dict:
         n = self.n_groups
         return dict(n_groups=n, rate=list(self.rate)[:n], dim=list(self.dim)[:n],
                     bit_offset=list(self.bit_offset)[:n], rot_offset=list(self.rot_offset)[:n],
-                    k_words=self.k_words, coord=list(self.coord))
+                    k_words=self.k_words, coord=list(self.coord), v_hadamard=self.v_hadamard)
 
 
 class PlanDesc(C.Structure):

@@ -205,6 +205,27 @@ __device__ inline double row_sum_f64(double v) {
   return v;
 }
 
+// Walsh-Hadamard transform (unnormalised, Sylvester order: H[i][j] = (-1)^popcount(i & j))
+// of a 128-vector held one element per thread, element e by the thread with e = tid - t0
+// for two whole waves starting at t0. Strides 1..32 move inside a wave; stride 64 goes
+// through buf (128 floats of LDS). Every thread of the workgroup must call it (one
+// barrier); only the 128 owners' results mean anything.
+__device__ inline float wht128(float x, int e, bool owner, float* buf) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float y = __shfl_xor(x, m);
+    x = (e & m) ? y - x : x + y;
+  }
+  if (owner) buf[e] = x;
+  __syncthreads();
+  if (owner) {
+    const float y = buf[e ^ 64];
+    x = (e & 64) ? y - x : x + y;
+  }
+  return x;
+}
+constexpr float kInvSqrt128 = 0.0883883461356163f;  // fp32 nearest to 1/sqrt(128)
+
 __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) {
   __shared__ AppendGemmShared S;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -571,7 +592,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   } else {
     const float4* pr = reinterpret_cast<const float4*>(a.rot + hd->vrot_off + (size_t)(o - kD) * kD + 32 * qq);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) pv[u] = pr[u];
+    for (int u = 0; u < 8; ++u) pv[u] = hd->v_hadamard ? make_float4(0.f, 0.f, 0.f, 0.f) : pr[u];
   }
   const int seq = a.step_len ? (int)tok : a.seq_idx[tok];
   const int64_t slot = a.step_len ? (int64_t)a.step_len[tok] - 1 : a.slot[tok];
@@ -642,7 +663,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
           acc = fmaf(pk[u].y, xx.y, acc);
         }
       }
-    } else {
+    } else if (!hd->v_hadamard) {
       const float* x = xs + kD + 32 * qq;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -653,6 +674,14 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
       }
     }
     red[qq][o] = acc;
+  }
+  if (hd->v_hadamard) {  // Pi_V v = c H (s * v): threads 128..255 own coordinate tid - 128
+    __shared__ float hbuf[kD];
+    const bool owner = tid >= kD && tid < 2 * kD;
+    const int e = tid - kD;
+    const float x = owner ? hd->vsign[e] * xs[kD + e] : 0.f;
+    const float y = wht128(x, e & (kD - 1), owner, hbuf);
+    if (owner) red[0][tid] = y * kInvSqrt128;
   }
   __syncthreads();
   const int vb = a.v_bits;
@@ -1977,6 +2006,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 // ============================================================================
 
 struct MergeArgs {
+  const DevHead* heads;    // this layer's heads (Hadamard value rotations)
   const float* vrot_t;     // Pi_V^T of the layer's KV heads, 128 x 128 each, consecutive
   const float* partials;
   const int32_t* seq_len;
@@ -2006,13 +2036,16 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   const int len_p = a.win ? packed_end(len, a.n_sink, a.n_recent) : len;
   const int nv = (len_p + a.chunk - 1) / a.chunk + a.win;  // packed splits, then the window's
   auto slot = [&](int k) { return (a.win && k == nv - 1) ? a.n_chunks - 1 : k; };
-  // inverse rotation operand: thread (i, half) holds Pi_V^T[i][64 half .. + 63]
+  // inverse rotation operand: thread (i, half) holds Pi_V^T[i][64 half .. + 63] (none
+  // for a Hadamard Pi_V, applied as a transform)
   const int oi = tid & 127, oh = tid >> 7;
+  const DevHead* __restrict__ hp = a.heads + hq / a.g;
+  const bool had = hp->v_hadamard != 0;
   float4 pvt[16];
   {
     const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)(hq / a.g) * kD * kD + (size_t)oi * kD + 64 * oh);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) pvt[u] = pt[u];
+    for (int u = 0; u < 16; ++u) pvt[u] = had ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
   }
   const float* pp = a.partials + (size_t)row * a.n_chunks * kPS;
   float mk[kMergeRegs], lk[kMergeRegs];
@@ -2084,6 +2117,11 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
     orot[4 * tid + 3] = s.w * f;
   }
   __syncthreads();
+  if (had) {  // o = s * (c H o_rot)
+    const float y = wht128(tid < kD ? orot[tid] : 0.f, tid & (kD - 1), tid < kD, opart[0]);
+    if (tid < kD) a.out[(size_t)row * kD + tid] = hp->vsign[tid] * kInvSqrt128 * y;
+    return;
+  }
   float o = 0.f;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
@@ -2104,6 +2142,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
 // then thread (column i, half) forms the inverse rotation's half sums for all 8 rows.
 constexpr int kMergeTileChunks = 8;
 struct MergeTileArgs {
+  const DevHead* heads;    // this layer's heads (Hadamard value rotations)
   const float* vrot_t;     // Pi_V^T of the layer's KV heads, 128 x 128 each, consecutive
   const float* partials;
   const int32_t* seq_len;
@@ -2131,12 +2170,15 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
     tr = rem - h * a.tiles_per_kv;
   }
   // the inverse rotation operand first: thread (i, half) holds Pi_V^T[i][64 half .. + 63]
+  // (none for a Hadamard Pi_V, applied as a transform)
   const int oi = tid & 127, oh = tid >> 7;
+  const DevHead* __restrict__ hp = a.heads + h;
+  const bool had = hp->v_hadamard != 0;
   float4 pvt[16];
   {
     const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)h * kD * kD + (size_t)oi * kD + 64 * oh);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) pvt[u] = pt[u];
+    for (int u = 0; u < 16; ++u) pvt[u] = had ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
   }
   // row r of the tile: global row id (-1 if absent) and visible length
   const int r = tid >> 5, c4 = tid & 31;
@@ -2189,6 +2231,31 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
     }
   }
   const float sc = L > 0.f ? 0.08838834764831845f / L : 0.f;  // 1 / (L sqrt(128))
+  if (had) {
+    // o = s * (c H o_rot): the thread holds elements 4 c4 .. + 3 of its row; strides 1, 2
+    // in registers, 4 .. 64 across the row's 32 lanes
+    float v[4] = {acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc};
+    const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+    v[0] = a0 + a2;
+    v[1] = a1 + a3;
+    v[2] = a0 - a2;
+    v[3] = a1 - a3;
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y = __shfl_xor(v[j], m);
+        v[j] = (c4 & m) ? y - v[j] : v[j] + y;
+      }
+    }
+    if (id >= 0) {
+      const float* sg = hp->vsign + 4 * c4;
+      *reinterpret_cast<float4*>(a.out + (size_t)id * kD + 4 * c4) =
+          make_float4(sg[0] * kInvSqrt128 * v[0], sg[1] * kInvSqrt128 * v[1], sg[2] * kInvSqrt128 * v[2],
+                      sg[3] * kInvSqrt128 * v[3]);
+    }
+    return;
+  }
   accs[r][c4] = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
   __syncthreads();
   float o[8];
@@ -2450,7 +2517,7 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
   const float* vrot_t = p->d_rot + p->heads[(size_t)layer * p->n_kv].vrot_t_off;
   const float* partials = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + L.qb_bytes);
   if (L.n_chunks <= kMergeTileChunks) {  // one workgroup per row tile
-    MergeTileArgs mt{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, p->n_kv, L.merge_tiles_per_kv,
+    MergeTileArgs mt{p->d_heads + (size_t)layer * p->n_kv, vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, p->n_kv, L.merge_tiles_per_kv,
                      (int32_t)(L.rows / p->n_q), L.n_chunks, L.chunk, prefill, max_len, 0};
     if (w) {
       mt.win = 1;
@@ -2459,7 +2526,7 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
     }
     hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.merge_n_tiles), dim3(256), 0, stream, mt);
   } else {  // one workgroup per row
-    MergeArgs ma{vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill,
+    MergeArgs ma{p->d_heads + (size_t)layer * p->n_kv, vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill,
                  max_len};
     if (w) {
       ma.win = 1;

@@ -386,6 +386,23 @@ gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
     off += dh.krot_floats;
     dh.vrot_off = (int64_t)(krot_total + h * vsz);
     dh.vrot_t_off = (int64_t)(krot_total + nh * vsz + h * vsz);
+    // a randomized Hadamard Pi_V: every entry is +-c, c = fp32(1/sqrt(128)), with the
+    // Sylvester sign pattern times a per-column sign (read off row 0)
+    {
+      const float c = 0.0883883461356163f;  // fp32 nearest to 1/sqrt(128)
+      const float* v = d->v_rot + h * vsz;
+      bool had = true;
+      for (int j = 0; j < kD && had; ++j) had = (v[j] == c || v[j] == -c);
+      for (int i = 0; i < kD && had; ++i)
+        for (int j = 0; j < kD && had; ++j) {
+          const float sj = v[j] > 0.f ? 1.f : -1.f;
+          const float hij = (__builtin_popcount((unsigned)(i & j)) & 1) ? -1.f : 1.f;
+          had = v[(size_t)i * kD + j] == sj * hij * c;
+        }
+      dh.v_hadamard = had ? 1 : 0;
+      for (int j = 0; j < kD; ++j) dh.vsign[j] = v[j] > 0.f ? 1.f : -1.f;
+      p->layouts[h].v_hadamard = dh.v_hadamard;
+    }
     for (size_t i = 0; i < (size_t)dh.krot_floats; ++i)
       if (!isfinite(p->rot[dh.krot_off[0] + i]))
         return fail(GTQ_EINVAL, "gtq_plan_create: non-finite K rotation");

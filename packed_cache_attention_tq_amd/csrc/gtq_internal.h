@@ -39,8 +39,9 @@ struct DevHead {
                                   // ceil16(d) rows x ceil32(d) columns (zero padded)
   int64_t rsv_off;                // split V rotation: hi then lo, 128 x 128
   int32_t krot_floats;            // sum_g d_g^2
-  int32_t pad_;
+  int32_t v_hadamard;             // 1: Pi_V = H_128 diag(vsign) / sqrt(128) exactly (fast transform)
   uint8_t coord[kD];              // record position -> head coordinate
+  float vsign[kD];                // the sign vector of a Hadamard Pi_V
 };
 
 constexpr int kPairTable = 340;  // (code, code) pairs of rates 1..4: 4 + 16 + 64 + 256 entries

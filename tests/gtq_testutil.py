@@ -31,7 +31,7 @@ class Case:
     """Plans (oracle + library) and per-sequence inputs for n_layers x h_kv heads."""
 
     def __init__(self, seed, n_layers, h_kv, g, n_cache, k_budget, v_bits, batch=1, layout=O.HALF,
-                 n_dec_q=1, b_min=1, b_max=4, nc=False):
+                 n_dec_q=1, b_min=1, b_max=4, nc=False, v_hadamard=False):
         import packed_cache_attention_tq_amd as G
         self.seed, self.L, self.H, self.g = seed, n_layers, h_kv, g
         self.HQ = h_kv * g
@@ -55,7 +55,7 @@ class Case:
                 assert np.array_equal(r_lib, r), f"rate allocation differs at layer {l} head {h}"
                 self.rates[l, h] = r_lib
                 dims = [len(c) for _, c in O.groups_from_rates(r, layout)]
-                kr, vr = head_rotations(seed, l, h, dims)
+                kr, vr = head_rotations(seed, l, h, dims, v_hadamard=v_hadamard)
                 self.heads[l, h] = O.HeadPlan(r, kr, vr, v_bits, layout, nc=nc)
                 kl.append(kr)
                 vl.append(vr)

@@ -196,3 +196,16 @@ def test_error_paths(lib):
     assert lib.gtq_prefill_workspace_bytes(p.handle, 0, 0, 0, C.byref(ws)) == 1
     p.destroy()
     assert lib.gtq_plan_destroy(None) == 0
+
+
+def test_plan_detects_hadamard_value_rotations():
+    import packed_cache_attention_tq_amd as G
+    from gtq_inputs import hadamard_rotation
+    rates, krot, vrot = _small_plan_inputs()
+    vrot = np.array(vrot, np.float32).copy()
+    vrot[0, 1] = hadamard_rotation(128, np.random.default_rng(1))
+    vrot[1, 0] = hadamard_rotation(128, np.random.default_rng(2))
+    vrot[1, 0, 5, 7] = -vrot[1, 0, 5, 7]          # no longer a Hadamard pattern
+    p = G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True)
+    assert [p.layout(l, h)["v_hadamard"] for l in range(2) for h in range(2)] == [0, 1, 0, 0]
+    p.destroy()

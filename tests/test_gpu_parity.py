@@ -608,3 +608,37 @@ def test_paged_cache(G):
     assert torch.equal(w_c, w_p)
     assert torch.equal(p_c, p_p)
     plan.destroy()
+
+
+@pytest.mark.parametrize("chunk", [0, 32])
+def test_hadamard_value_rotation(G, chunk):
+    """Randomized Hadamard value rotations (detected at plan creation): the chunk append
+    (dense split rotation), the scatter append and the decode step (fast transform), and
+    the merge's inverse rotation (fast transform; tile merge and row merge) against the
+    oracle's dense Pi_V."""
+    _say(f"case: Hadamard value rotation, chunk={chunk}")
+    lens = [290, 64]
+    case = Case(10, 1, 2, 4, 290, 128, 2, batch=2, v_hadamard=True)
+    plan = case.plan()
+    assert all(plan.layout(0, h)["v_hadamard"] == 1 for h in range(case.H))
+    cache = G.PackedCache(plan, 2, 320)
+    k0, v0 = case.kv(0, 0)
+    k1, v1 = case.kv(0, 1)
+    G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k0[:200]), _dev(v0[:200]), 0, 0)
+    idx = np.random.default_rng(2).permutation(89) + 200
+    G.gtq_quantize_append(plan, 0, cache, _dev(k0[idx]), _dev(v0[idx]), _dev(np.zeros(89, np.int32)), _dev(idx))
+    G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k1[:63]), _dev(v1[:63]), 1, 0)
+    q = np.stack([case.q(0, 0), case.q(0, 1)])
+    sl = _dev(np.array(lens, np.int32))
+    sc = scale_default()
+    out = G.gtq_decode_step(plan, 0, cache, _dev(np.stack([k0[289], k1[63]])), _dev(np.stack([v0[289], v1[63]])),
+                            _dev(q), sl, 320, sc, chunk=chunk)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        enc = _encode(case, 0, b, n)
+        ties, ulps = _check_append(case, cache, 0, b, n, enc, f"hadamard b{b}")
+        _say(f"  b{b}: ties={ties} norm-ulps={ulps}")
+        if ties == 0:
+            _, ref = _oracle_decode(case, 0, b, n, enc, q[b], sc)
+            assert_close(out[b].cpu().numpy(), ref, f"hadamard out b{b}")
+    plan.destroy()

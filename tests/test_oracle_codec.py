@@ -229,3 +229,18 @@ def test_pack_round_trip_and_record_size():
         back = O.unpack_codes(w, [len(c) for _, c in gs], [r for r, _ in gs])
         for a, b in zip(cg, back):
             assert np.array_equal(a, b)
+
+
+def test_hadamard_rotation_is_sylvester_times_signs():
+    """The randomized Hadamard generator: scipy's Sylvester Hadamard matrix with a +-1
+    column scaling, entries exactly +-fp32(1/sqrt(128)), orthogonal."""
+    from scipy.linalg import hadamard
+    from gtq_inputs import hadamard_rotation
+    r = hadamard_rotation(128, np.random.default_rng(3))
+    c = np.float32(1 / np.sqrt(128))
+    h = hadamard(128)
+    s = np.sign(r[0])
+    assert np.array_equal(r, (h * s[None, :]).astype(np.float32) * c)
+    assert set(np.unique(np.abs(r)).tolist()) == {float(c)}
+    r64 = r.astype(np.float64)
+    assert np.max(np.abs(r64 @ r64.T - np.eye(128))) < 1e-6
