@@ -560,6 +560,11 @@ def main():
 
     def step(i, ev=None):
         c = caches[i % len(caches)]
+        if ev is None:  # the fused step: prepare + partials + merge in one library call
+            G.gtq_decode_step(plan, 0, c, k_new, v_new, q, seq_len, n, scale, chunk=args.chunk, out=out,
+                              workspace=ws, stream=stream)
+            return
+        # the same three launches as separate calls, with timing events around the partials:
         # append the step's token at slot n - 1 and rotate the queries (one launch)
         G.gtq_decode_prepare(plan, 0, c, k_new, v_new, q, seq_len, n, scale, ws, chunk=args.chunk, stream=stream)
         if ev is not None:
@@ -575,14 +580,17 @@ def main():
     log(f"setup {time.perf_counter() - t_setup:.1f}s; cache fill (append of {n - 1} tokens x {h_kv} heads) "
         f"{fill_ms:.3f} ms; cache {base.nbytes() / 1e6:.2f} MB x {len(caches)} copies")
 
+    # the partials kernel's duration is sampled with HIP events on every EVERY-th timed step
+    # (events and separate calls on every step would make the loop host-bound)
+    EVERY = 8
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range((args.steps + EVERY - 1) // EVERY)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs[i // EVERY] if i % EVERY == 0 else None)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
