@@ -549,12 +549,16 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
   }
 }
 
-// One workgroup (1024 threads) per (token, KV head). All global loads go out in one
-// round (the vectors in natural order, the rotation rows each thread needs, the
-// token's sequence and slot); the key is put in record order in LDS; the group norms
-// are fp64 wave reductions; thread (output o, quarter qq) forms a quarter of one
-// rotated coordinate.
-__device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h) {
+// Three workgroups (1024 threads each) per (token, KV head), one per role: the key
+// (role 0), value coordinates 0..63 (role 1) and 64..127 (role 2), so that each loads a
+// third of the rotation rows; a value rotation that needs all 128 coordinates at once
+// (a Hadamard transform, or the norm-corrected sum over all codes) stays in role 1.
+// All global loads go out in one round (the vectors in natural order, the rotation rows
+// each thread needs, the token's sequence and slot); the key is put in record order in
+// LDS; the norms are fp64 wave reductions; thread (output o, quarter qq) forms a
+// quarter of one rotated coordinate. The two value halves write disjoint words of the
+// token's value block.
+__device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h, int role) {
   __shared__ float xnat[2 * kD];        // key then value, natural order
   __shared__ __align__(16) float xs[2 * kD];  // key (record order) then value coordinates
   __shared__ float red[4][2 * kD];
@@ -574,8 +578,11 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   const float thv = tid < 80 ? (&a.cb->t[0][0])[tid] : 0.f;
   const float cev = tid < 80 ? (&a.cb->c[0][0])[tid] : 0.f;
   // this thread's rotation entries: key output o < 128 (row i of its group, pair range
-  // of quarter qq) or value output o - 128 (32 columns of quarter qq)
+  // of quarter qq) or value output o - 128 (32 columns of quarter qq), if its role's
   const int o = tid & 255, qq = tid >> 8;
+  const bool vsplit = !a.nc && !hd->v_hadamard;
+  const int vlo = role == 2 ? kD / 2 : 0, vhi = (role == 1 && vsplit) ? kD / 2 : kD;
+  const bool mine = role == 0 ? o < kD : (o >= kD + vlo && o < kD + vhi);
   float2 pk[16];
   float4 pv[8];
   int kg = 0, klo = 0, khi = 0;
@@ -586,22 +593,24 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     const int d = hd->dim[kg], i = o - hd->pos_off[kg], dp = d >> 1;
     klo = (dp * qq) >> 2;
     khi = (dp * (qq + 1)) >> 2;
+    if (!mine) khi = klo;  // (no key work outside role 0)
     const float2* pr = reinterpret_cast<const float2*>(a.rot + hd->krot_off[kg] + (size_t)i * d);
 #pragma unroll
     for (int u = 0; u < 16; ++u) pk[u] = (klo + u < khi) ? pr[klo + u] : make_float2(0.f, 0.f);
   } else {
     const float4* pr = reinterpret_cast<const float4*>(a.rot + hd->vrot_off + (size_t)(o - kD) * kD + 32 * qq);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) pv[u] = hd->v_hadamard ? make_float4(0.f, 0.f, 0.f, 0.f) : pr[u];
+    for (int u = 0; u < 8; ++u) pv[u] = (hd->v_hadamard || !mine) ? make_float4(0.f, 0.f, 0.f, 0.f) : pr[u];
   }
   const int seq = a.step_len ? (int)tok : a.seq_idx[tok];
   const int64_t slot = a.step_len ? (int64_t)a.step_len[tok] - 1 : a.slot[tok];
   const int64_t ti = (seq < 0 || seq >= a.batch || slot < 0 || slot >= a.capacity)
                          ? -1 : token_index(a.pm, a.capacity, a.n_kv, seq, h, slot);
   if (ti < 0) {
-    if (tid == 0 && h == 0) atomicAdd(a.overflow, 1ull);  // once per token
+    if (tid == 0 && h == 0 && role == 0) atomicAdd(a.overflow, 1ull);  // once per token
     return;
   }
+  if (role == 2 && !vsplit) return;  // role 1 does the whole value
   if (tid < 2 * kD) xnat[tid] = xv;
   if (tid < 80) {
     (&thr[0][0])[tid] = thv;
@@ -686,7 +695,8 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   __syncthreads();
   const int vb = a.v_bits;
   const int j0 = (int)(slot & (GTQ_VBLOCK - 1));
-  if (tid < 2 * kD) {
+  const bool qown = role == 0 ? tid < kD : (tid >= kD + vlo && tid < kD + vhi);
+  if (tid < 2 * kD && qown) {  // (whole waves: 0-1 keys, 2 and/or 3 values)
     const float z0 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
     if (tid < kD) {
       const int g = kg;
@@ -727,14 +737,14 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     }
   }
   __syncthreads();
-  if (tid < a.k_words) a.k_codes[ti * a.k_words + tid] = krec[tid];
-  if (tid >= 64 && tid < 64 + kNS) {
+  if (role == 0 && tid < a.k_words) a.k_codes[ti * a.k_words + tid] = krec[tid];
+  if (role == 0 && tid >= 64 && tid < 64 + kNS) {
     const int g = tid - 64;
     a.k_norms[ti * kNS + g] =
         g >= n_groups ? 0.f : (a.nc ? corrected_norm(nu64_s[g], cs_s[g], hd->dim[g]) : nu_s[g]);
   }
-  if (tid == 128) a.v_norms[ti] = a.nc ? corrected_norm(nu64_s[4], cs_s[4], kD) : nu_s[4];
-  if (tid >= 256 && tid < 256 + 32 * vb) {
+  if (role == 1 && tid == 128) a.v_norms[ti] = a.nc ? corrected_norm(nu64_s[4], cs_s[4], kD) : nu_s[4];
+  if (role != 0 && tid >= 256 && tid < 256 + 32 * vb) {
     const int w = tid - 256;
     const uint32_t m = vmask[w];
     if (m) {
@@ -746,7 +756,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
 }
 
 __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
-  append_token_body(a, blockIdx.x, blockIdx.y);
+  append_token_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ============================================================================
@@ -894,15 +904,15 @@ __device__ inline float swap_q3(float x) { return xor16(xor32(x)); }
 
 // ---------------------------------------------------------------- query rotation
 
-// One workgroup (16 waves) per row tile: the tile's query rows in record order, then
-// per group and 16-coordinate slice i0.. the fp32 MFMA 16x16x4 product
-// D[i][r] = sum_k Pi_g[i0 + i][k] qrec[r][pos_off + k] (the 4 k of lane (q, n) per MFMA
-// are k0 + 4q + s), written as the tile's B operand. Tiles of 8 rows (RT = 8) put the
-// high parts in columns 0..7 and the low parts of rows 7..0 in columns 8..15; tiles of
-// 16 rows (RT = 16, prefill) write two operands, high parts then low parts, with row n
-// in column n.
-constexpr int kQrotWaves = 16;  // 1024 threads: one 16-coordinate slice per wave (at most 11)
-constexpr int kQrotSlices = 1;
+// One workgroup (1024 threads) per row tile: the tile's query rows in record order, then
+// r_g = Pi_g q_g on the VALU: thread (record position i, part p of 8) sums its eighth of
+// row i - pos_off[g] of Pi_g against every row of the tile (one round of rotation loads
+// per thread, the query pairs broadcast from LDS), the 8 parts add up through lane
+// shuffles, and part 0 writes the scaled high and low binary16 halves into the tile's B
+// operand. Tiles of 8 rows (RT = 8) put the high parts in columns 0..7 and the low parts
+// of rows 7..0 in columns 8..15; tiles of 16 rows (RT = 16, prefill) write two operands,
+// high parts then low parts, with row n in column n.
+constexpr int kQrotWaves = 16;
 template <int RT>
 __device__ inline void qrot_body(const AttnArgs& a, int tile) {
   constexpr int kParts = RT / 8;       // B operands per tile (1, or 2 for hi and lo)
@@ -911,65 +921,39 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
   __shared__ __align__(16) float qrec[RT][kD];
   __shared__ uint4 qb[kParts * kMaxKB][4][16];
   constexpr int kT = 64 * kQrotWaves;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x;
   int seq, h, tr;
   tile_coords(a, tile, &seq, &h, &tr);
   const DevHead* __restrict__ hp = a.heads + h;
   const int n_groups = hp->n_groups;
-  // this wave's slices (group, first coordinate); slices are numbered over the groups
-  // in order, 16 coordinates each, and wave w takes w, w + 8, ...
-  int sg[kQrotSlices], si0[kQrotSlices];
+  // this thread's output: record position i, its group g, row ii of Pi_g, and its
+  // eighth [plo, phi) of the d / 2 column pairs
+  const int i = tid >> 3, part = tid & 7;
+  int g = 0;
 #pragma unroll
-  for (int j = 0; j < kQrotSlices; ++j) sg[j] = -1, si0[j] = 0;
+  for (int gg = 1; gg < kMaxGroups; ++gg)
+    if (gg < n_groups && i >= hp->pos_off[gg]) g = gg;
+  const int d = hp->dim[g], po = hp->pos_off[g], ii = i - po, dp = d >> 1;
+  const int plo = (dp * part) >> 3, phi = (dp * (part + 1)) >> 3;
+  // one round of loads: the rotation pairs, the tile's query rows (natural order) and
+  // the head's record order
+  float2 pr[8];
   {
-    int t = 0;
+    const float2* row = reinterpret_cast<const float2*>(a.rot + hp->krot_off[g] + (size_t)ii * d);
 #pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g) {
-      if (g < n_groups) {
-        const int ns = (hp->dim[g] + 15) >> 4;
-#pragma unroll
-        for (int j = 0; j < kQrotSlices; ++j) {
-          const int idx = wave + kQrotWaves * j;
-          if (idx >= t && idx < t + ns) {
-            sg[j] = g;
-            si0[j] = 16 * (idx - t);
-          }
-        }
-        t += ns;
-      }
-    }
+    for (int u = 0; u < 8; ++u) pr[u] = (plo + u < phi) ? row[plo + u] : make_float2(0.f, 0.f);
   }
-  // one round of loads: the rotation rows of the slices (lane (q, n): row i0 + n,
-  // columns 16u + 4q + 0..3; d is even, so a pair of columns is wholly in or out), the
-  // tile's query rows in natural order and the head's record order
-  float2 pa[kQrotSlices][8][2];
+  float qv[RT * kD / kT > 0 ? RT * kD / kT : 1];
 #pragma unroll
-  for (int j = 0; j < kQrotSlices; ++j) {
-    const int g = sg[j] < 0 ? 0 : sg[j];
-    const int d = sg[j] < 0 ? 0 : hp->dim[g];
-    const float* R = a.rot + hp->krot_off[g];
-    const int i = si0[j] + n;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int kk = 16 * u + 4 * q;
-      pa[j][u][0] = (i < d && kk < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk) : make_float2(0.f, 0.f);
-      pa[j][u][1] = (i < d && kk + 2 < d) ? *reinterpret_cast<const float2*>(R + (size_t)i * d + kk + 2)
-                                          : make_float2(0.f, 0.f);
-    }
-  }
-  float qv[kParts];
-#pragma unroll
-  for (int pp = 0; pp < kParts; ++pp) {
-    const int r = (tid >> 7) + 8 * pp, c = tid & (kD - 1);  // 8 x 128 == kT
+  for (int pp = 0; pp < RT * kD / kT; ++pp) {
+    const int r = (tid >> 7) + (kT / kD) * pp, c = tid & (kD - 1);
     int L;
     const int id = tile_row<RT>(a, seq, h, tr, r, 0, &L);
     qv[pp] = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
   }
   const int crd = tid < kD ? hp->coord[tid] : 0;
 #pragma unroll
-  for (int pp = 0; pp < kParts; ++pp) (&qnat[0][0])[tid + kT * pp] = qv[pp];
+  for (int pp = 0; pp < RT * kD / kT; ++pp) (&qnat[0][0])[tid + kT * pp] = qv[pp];
   for (int e = tid; e < kTileQB; e += kT) (&qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
   __syncthreads();
   if (tid < kD) {
@@ -977,52 +961,42 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
     for (int r = 0; r < RT; ++r) qrec[r][tid] = qnat[r][crd];
   }
   __syncthreads();
+  float acc[RT];
 #pragma unroll
-  for (int j = 0; j < kQrotSlices; ++j) {
-    if (sg[j] >= 0) {
-      const int g = sg[j], i0 = si0[j];
-      const int d = hp->dim[g], po = hp->pos_off[g], kp0 = hp->kp_off[g];
-      // the B operands (row n of the record-order queries) first: reads at clamped
-      // addresses, zero outside the group or for rows past the tile
-      float2 bq[8][2];
+  for (int r = 0; r < RT; ++r) {
+    const float2* x = reinterpret_cast<const float2*>(&qrec[r][po]);
+    float s = 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int kk = 16 * u + 4 * q;
-        const float2 x0 = *reinterpret_cast<const float2*>(&qrec[n % RT][min(po + kk, kD - 2)]);
-        const float2 x1 = *reinterpret_cast<const float2*>(&qrec[n % RT][min(po + kk + 2, kD - 2)]);
-        bq[u][0] = (n < RT && kk < d) ? x0 : make_float2(0.f, 0.f);
-        bq[u][1] = (n < RT && kk + 2 < d) ? x1 : make_float2(0.f, 0.f);
+    for (int u = 0; u < 8; ++u) {
+      if (plo + u < phi) {
+        const float2 xx = x[plo + u];
+        s = fmaf(pr[u].x, xx.x, s);
+        s = fmaf(pr[u].y, xx.y, s);
       }
-      floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    }
+    acc[r] = s;
+  }
+  // sum the 8 parts (consecutive lanes)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (16 * u < d) {
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][0].x, bq[u][0].x, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][0].y, bq[u][0].y, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][1].x, bq[u][1].x, acc[u & 1], 0, 0, 0);
-          acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[j][u][1].y, bq[u][1].y, acc[u & 1], 0, 0, 0);
-        }
-      }
-      // lane (q, n) holds D[4q + e][n]: coordinate i0 + 4q + e of row n
-      if (n < RT) {
-        const float sc = a.qscale / sqrtf((float)d);
+  for (int r = 0; r < RT; ++r) {
+    acc[r] += __shfl_xor(acc[r], 1);
+    acc[r] += __shfl_xor(acc[r], 2);
+    acc[r] += __shfl_xor(acc[r], 4);
+  }
+  if (part == 0) {
+    const float sc = a.qscale / sqrtf((float)d);
+    const int kp = hp->kp_off[g] + ii;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ii = i0 + 4 * q + e;
-          if (ii < d) {
-            const float val = (acc[0][e] + acc[1][e]) * sc;
-            const _Float16 hi = (_Float16)val;
-            const _Float16 lo = (_Float16)(val - (float)hi);
-            const int kp = kp0 + ii;
-            if (RT == 8) {
-              reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][n])[kp & 7] = hi;
-              reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][15 - n])[kp & 7] = lo;
-            } else {
-              reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][n])[kp & 7] = hi;
-              reinterpret_cast<_Float16*>(&qb[kMaxKB + (kp >> 5)][(kp >> 3) & 3][n])[kp & 7] = lo;
-            }
-          }
-        }
+    for (int r = 0; r < RT; ++r) {
+      const float val = acc[r] * sc;
+      const _Float16 hi = (_Float16)val;
+      const _Float16 lo = (_Float16)(val - (float)hi);
+      if (RT == 8) {
+        reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][r])[kp & 7] = hi;
+        reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][15 - r])[kp & 7] = lo;
+      } else {
+        reinterpret_cast<_Float16*>(&qb[kp >> 5][(kp >> 3) & 3][r])[kp & 7] = hi;
+        reinterpret_cast<_Float16*>(&qb[kMaxKB + (kp >> 5)][(kp >> 3) & 3][r])[kp & 7] = lo;
       }
     }
   }
@@ -1034,11 +1008,11 @@ template <int RT>
 __global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) { qrot_body<RT>(a, blockIdx.x); }
 
 // Decode step preparation in one launch: workgroups [0, n_app) append the step's
-// tokens (token w / n_kv, KV head w % n_kv), the rest rotate the queries of one row
-// tile each; the two roles share no data.
+// tokens (token w / (3 n_kv), KV head (w / 3) % n_kv, role w % 3: key, value halves),
+// the rest rotate the queries of one row tile each; the two kinds share no data.
 __global__ void __launch_bounds__(1024) decode_prep_kernel(AppendArgs ap, AttnArgs aa, int n_app) {
   const int w = blockIdx.x;
-  if (w < n_app) append_token_body(ap, w / ap.n_kv, w % ap.n_kv);
+  if (w < n_app) append_token_body(ap, w / (3 * ap.n_kv), (w / 3) % ap.n_kv, w % 3);
   else qrot_body<8>(aa, w - n_app);
 }
 
@@ -2388,7 +2362,7 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   a.pm = page_map(c);
   if (!chunk) {
     if (n_tok > 0x7FFFFFFF) return fail(GTQ_EUNSUPPORTED, "gtq_quantize_append: too many tokens");
-    hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)n_tok, p->n_kv), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)n_tok, p->n_kv, 3), dim3(1024), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "gtq append: launch");
     return ok();
@@ -2779,7 +2753,7 @@ gtq_status gtq_decode_prepare(const gtq_plan* plan, int32_t layer, const gtq_cac
   aa.max_len = (int32_t)max_len;
   aa.q = q;
   aa.qscale = softmax_scale * LOG2E_F;
-  const int n_app = cache->batch * plan->n_kv;
+  const int n_app = cache->batch * plan->n_kv * 3;  // key, value low half, value high half
   hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)(n_app + L.n_tiles)), dim3(1024), 0, (hipStream_t)hip_stream,
                      ap, aa, n_app);
   hipError_t e = hipGetLastError();
