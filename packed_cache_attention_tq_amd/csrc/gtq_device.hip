@@ -549,10 +549,12 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
   }
 }
 
-// Three workgroups (1024 threads each) per (token, KV head), one per role: the key
-// (role 0), value coordinates 0..63 (role 1) and 64..127 (role 2), so that each loads a
-// third of the rotation rows; a value rotation that needs all 128 coordinates at once
-// (a Hadamard transform, or the norm-corrected sum over all codes) stays in role 1.
+// One workgroup (1024 threads) per (token, KV head) doing everything (role 3), or, when
+// few tokens leave most of the chip idle, three per (token, KV head), one per role: the
+// key (role 0), value coordinates 0..63 (role 1) and 64..127 (role 2), so that each
+// loads a third of the rotation rows; a value rotation that needs all 128 coordinates
+// at once (a Hadamard transform, or the norm-corrected sum over all codes) stays in
+// role 1.
 // All global loads go out in one round (the vectors in natural order, the rotation rows
 // each thread needs, the token's sequence and slot); the key is put in record order in
 // LDS; the norms are fp64 wave reductions; thread (output o, quarter qq) forms a
@@ -582,7 +584,8 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   const int o = tid & 255, qq = tid >> 8;
   const bool vsplit = !a.nc && !hd->v_hadamard;
   const int vlo = role == 2 ? kD / 2 : 0, vhi = (role == 1 && vsplit) ? kD / 2 : kD;
-  const bool mine = role == 0 ? o < kD : (o >= kD + vlo && o < kD + vhi);
+  const bool mine = role == 3 || (role == 0 ? o < kD : (o >= kD + vlo && o < kD + vhi));
+  const bool do_k = role == 0 || role == 3, do_v = role != 0;
   float2 pk[16];
   float4 pv[8];
   int kg = 0, klo = 0, khi = 0;
@@ -607,7 +610,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   const int64_t ti = (seq < 0 || seq >= a.batch || slot < 0 || slot >= a.capacity)
                          ? -1 : token_index(a.pm, a.capacity, a.n_kv, seq, h, slot);
   if (ti < 0) {
-    if (tid == 0 && h == 0 && role == 0) atomicAdd(a.overflow, 1ull);  // once per token
+    if (tid == 0 && h == 0 && do_k) atomicAdd(a.overflow, 1ull);  // once per token
     return;
   }
   if (role == 2 && !vsplit) return;  // role 1 does the whole value
@@ -695,7 +698,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   __syncthreads();
   const int vb = a.v_bits;
   const int j0 = (int)(slot & (GTQ_VBLOCK - 1));
-  const bool qown = role == 0 ? tid < kD : (tid >= kD + vlo && tid < kD + vhi);
+  const bool qown = tid < kD ? do_k : (do_v && tid >= kD + vlo && tid < kD + vhi);
   if (tid < 2 * kD && qown) {  // (whole waves: 0-1 keys, 2 and/or 3 values)
     const float z0 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
     if (tid < kD) {
@@ -737,14 +740,14 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     }
   }
   __syncthreads();
-  if (role == 0 && tid < a.k_words) a.k_codes[ti * a.k_words + tid] = krec[tid];
-  if (role == 0 && tid >= 64 && tid < 64 + kNS) {
+  if (do_k && tid < a.k_words) a.k_codes[ti * a.k_words + tid] = krec[tid];
+  if (do_k && tid >= 64 && tid < 64 + kNS) {
     const int g = tid - 64;
     a.k_norms[ti * kNS + g] =
         g >= n_groups ? 0.f : (a.nc ? corrected_norm(nu64_s[g], cs_s[g], hd->dim[g]) : nu_s[g]);
   }
-  if (role == 1 && tid == 128) a.v_norms[ti] = a.nc ? corrected_norm(nu64_s[4], cs_s[4], kD) : nu_s[4];
-  if (role != 0 && tid >= 256 && tid < 256 + 32 * vb) {
+  if ((role == 1 || role == 3) && tid == 128) a.v_norms[ti] = a.nc ? corrected_norm(nu64_s[4], cs_s[4], kD) : nu_s[4];
+  if (do_v && tid >= 256 && tid < 256 + 32 * vb) {
     const int w = tid - 256;
     const uint32_t m = vmask[w];
     if (m) {
@@ -755,9 +758,14 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   }
 }
 
+// grid (tokens, KV heads, 1 or 3 roles)
 __global__ void __launch_bounds__(1024) append_token_kernel(AppendArgs a) {
-  append_token_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  append_token_body(a, blockIdx.x, blockIdx.y, gridDim.z == 1 ? 3 : (int)blockIdx.z);
 }
+
+// roles per (token, KV head) of the per-token append: 3 while n token-heads leave most of
+// the compute units idle, else 1
+inline int append_roles(int64_t n_token_heads) { return n_token_heads < 128 ? 3 : 1; }
 
 // ============================================================================
 // Split-K attention over the packed cache (Block-GTQ page, abstract, 5th
@@ -1008,11 +1016,15 @@ template <int RT>
 __global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) { qrot_body<RT>(a, blockIdx.x); }
 
 // Decode step preparation in one launch: workgroups [0, n_app) append the step's
-// tokens (token w / (3 n_kv), KV head (w / 3) % n_kv, role w % 3: key, value halves),
-// the rest rotate the queries of one row tile each; the two kinds share no data.
-__global__ void __launch_bounds__(1024) decode_prep_kernel(AppendArgs ap, AttnArgs aa, int n_app) {
+// tokens (with 3 roles: token w / (3 n_kv), KV head (w / 3) % n_kv, role w % 3; with 1:
+// token w / n_kv, KV head w % n_kv), the rest rotate the queries of one row tile each;
+// the two kinds share no data.
+__global__ void __launch_bounds__(1024) decode_prep_kernel(AppendArgs ap, AttnArgs aa, int n_app, int roles) {
   const int w = blockIdx.x;
-  if (w < n_app) append_token_body(ap, w / (3 * ap.n_kv), (w / 3) % ap.n_kv, w % 3);
+  if (w < n_app) {
+    if (roles == 1) append_token_body(ap, w / ap.n_kv, w % ap.n_kv, 3);
+    else append_token_body(ap, w / (3 * ap.n_kv), (w / 3) % ap.n_kv, w % 3);
+  }
   else qrot_body<8>(aa, w - n_app);
 }
 
@@ -2362,7 +2374,8 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   a.pm = page_map(c);
   if (!chunk) {
     if (n_tok > 0x7FFFFFFF) return fail(GTQ_EUNSUPPORTED, "gtq_quantize_append: too many tokens");
-    hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)n_tok, p->n_kv, 3), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)n_tok, p->n_kv, append_roles(n_tok * p->n_kv)), dim3(1024),
+                       0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "gtq append: launch");
     return ok();
@@ -2753,9 +2766,10 @@ gtq_status gtq_decode_prepare(const gtq_plan* plan, int32_t layer, const gtq_cac
   aa.max_len = (int32_t)max_len;
   aa.q = q;
   aa.qscale = softmax_scale * LOG2E_F;
-  const int n_app = cache->batch * plan->n_kv * 3;  // key, value low half, value high half
+  const int roles = append_roles((int64_t)cache->batch * plan->n_kv);
+  const int n_app = cache->batch * plan->n_kv * roles;
   hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)(n_app + L.n_tiles)), dim3(1024), 0, (hipStream_t)hip_stream,
-                     ap, aa, n_app);
+                     ap, aa, n_app, roles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq_decode_prepare: launch");
   return ok();
