@@ -2002,17 +2002,20 @@ struct MergeArgs {
   int32_t win, n_sink, n_recent;  // fp16 window: its split is the last slot
 };
 
-// One workgroup (256 threads) per row: thread (float4 column c4, chunk slice ks) loads
-// the accumulators of chunks ks, ks + 8, ... together with their (m, l) and its slice
-// of Pi_V^T in one round; then M = max m, weights 2^(m - M), the weighted sums over
-// the slices, normalisation by L sqrt(128) and the inverse rotation.
+// Four workgroups (256 threads each) per row, one per quarter of the output coordinates:
+// thread (float4 column c4, chunk slice ks) loads the accumulators of chunks ks, ks + 8,
+// ... together with their (m, l), and thread (output i of the quarter, eighth e) its
+// 16 entries of row i of Pi_V^T, in one round; then M = max m, weights 2^(m - M), the
+// weighted sums over the slices, normalisation by L sqrt(128) and the quarter's outputs
+// of the inverse rotation (eighths added by lane shuffles). Each quarter repeats the
+// merge of all 128 accumulator columns and reads only its 16 KB of Pi_V^T.
 constexpr int kMergeRegs = 16;  // chunks per thread kept in registers (128 splits in one round)
 __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   __shared__ float4 red[8][32];
   __shared__ float sm[8], sl[8];
   __shared__ float orot[kD];
   __shared__ float opart[2][kD];
-  const int row = blockIdx.x;
+  const int row = blockIdx.x, oq = blockIdx.y;
   const int tid = threadIdx.x;
   const int c4 = tid & 31, ks = tid >> 5;
   const int hq = row % a.n_q;
@@ -2022,16 +2025,18 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   const int len_p = a.win ? packed_end(len, a.n_sink, a.n_recent) : len;
   const int nv = (len_p + a.chunk - 1) / a.chunk + a.win;  // packed splits, then the window's
   auto slot = [&](int k) { return (a.win && k == nv - 1) ? a.n_chunks - 1 : k; };
-  // inverse rotation operand: thread (i, half) holds Pi_V^T[i][64 half .. + 63] (none
-  // for a Hadamard Pi_V, applied as a transform)
-  const int oi = tid & 127, oh = tid >> 7;
+  // inverse rotation operand: thread (output oi of this quarter, eighth e) holds
+  // Pi_V^T[oi][16 e .. + 15] (none for a Hadamard Pi_V, applied as a transform by the
+  // first quarter alone)
   const DevHead* __restrict__ hp = a.heads + hq / a.g;
   const bool had = hp->v_hadamard != 0;
-  float4 pvt[16];
+  if (had && oq != 0) return;
+  const int oe = tid & 7, oi = 32 * oq + (tid >> 3);
+  float4 pvt[4];
   {
-    const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)(hq / a.g) * kD * kD + (size_t)oi * kD + 64 * oh);
+    const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)(hq / a.g) * kD * kD + (size_t)oi * kD + 16 * oe);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) pvt[u] = had ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
+    for (int u = 0; u < 4; ++u) pvt[u] = had ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
   }
   const float* pp = a.partials + (size_t)row * a.n_chunks * kPS;
   float mk[kMergeRegs], lk[kMergeRegs];
@@ -2110,16 +2115,17 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   }
   float o = 0.f;
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const float4 x = *reinterpret_cast<const float4*>(&orot[64 * oh + 4 * u]);
+  for (int u = 0; u < 4; ++u) {
+    const float4 x = *reinterpret_cast<const float4*>(&orot[16 * oe + 4 * u]);
     o = fmaf(pvt[u].x, x.x, o);
     o = fmaf(pvt[u].y, x.y, o);
     o = fmaf(pvt[u].z, x.z, o);
     o = fmaf(pvt[u].w, x.w, o);
   }
-  opart[oh][oi] = o;
-  __syncthreads();
-  if (tid < kD) a.out[(size_t)row * kD + tid] = opart[0][tid] + opart[1][tid];
+  o += __shfl_xor(o, 1);
+  o += __shfl_xor(o, 2);
+  o += __shfl_xor(o, 4);
+  if (oe == 0) a.out[(size_t)row * kD + oi] = o;
 }
 
 // Merge for up to 8 splits per row: one workgroup (256 threads) per row tile (the rows
@@ -2520,7 +2526,7 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
       ma.n_sink = w->n_sink;
       ma.n_recent = w->n_recent;
     }
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows), dim3(256), 0, stream, ma);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows, 4), dim3(256), 0, stream, ma);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq attention merge: launch");
