@@ -2031,12 +2031,15 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   const DevHead* __restrict__ hp = a.heads + hq / a.g;
   const bool had = hp->v_hadamard != 0;
   if (had && oq != 0) return;
-  const int oe = tid & 7, oi = 32 * oq + (tid >> 3);
-  float4 pvt[4];
-  {
+  const int nqw = gridDim.y;  // workgroups per row: 4 (one quarter each) or 1 (all four)
+  const int oe = tid & 7;
+  float4 pvt[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int qo = oq + j * nqw, oi = 32 * qo + (tid >> 3);
     const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)(hq / a.g) * kD * kD + (size_t)oi * kD + 16 * oe);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pvt[u] = had ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
+    for (int u = 0; u < 4; ++u) pvt[j][u] = (had || qo >= 4) ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
   }
   const float* pp = a.partials + (size_t)row * a.n_chunks * kPS;
   float mk[kMergeRegs], lk[kMergeRegs];
@@ -2113,25 +2116,32 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
     if (tid < kD) a.out[(size_t)row * kD + tid] = hp->vsign[tid] * kInvSqrt128 * y;
     return;
   }
-  float o = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float4 x = *reinterpret_cast<const float4*>(&orot[16 * oe + 4 * u]);
-    o = fmaf(pvt[u].x, x.x, o);
-    o = fmaf(pvt[u].y, x.y, o);
-    o = fmaf(pvt[u].z, x.z, o);
-    o = fmaf(pvt[u].w, x.w, o);
+  for (int j = 0; j < 4; ++j) {
+    const int qo = oq + j * nqw, oi = 32 * qo + (tid >> 3);
+    if (qo >= 4) break;
+    float o = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 x = *reinterpret_cast<const float4*>(&orot[16 * oe + 4 * u]);
+      o = fmaf(pvt[j][u].x, x.x, o);
+      o = fmaf(pvt[j][u].y, x.y, o);
+      o = fmaf(pvt[j][u].z, x.z, o);
+      o = fmaf(pvt[j][u].w, x.w, o);
+    }
+    o += __shfl_xor(o, 1);
+    o += __shfl_xor(o, 2);
+    o += __shfl_xor(o, 4);
+    if (oe == 0) a.out[(size_t)row * kD + oi] = o;
   }
-  o += __shfl_xor(o, 1);
-  o += __shfl_xor(o, 2);
-  o += __shfl_xor(o, 4);
-  if (oe == 0) a.out[(size_t)row * kD + oi] = o;
 }
 
-// Merge for up to 8 splits per row: one workgroup (256 threads) per row tile (the rows
-// of one sequence and KV head, as in the partials grid), so that Pi_V^T is read once per
-// tile. Thread (row r, float4 column c4) merges its row's splits in one round of loads;
-// then thread (column i, half) forms the inverse rotation's half sums for all 8 rows.
+// Merge for up to 8 splits per row: four workgroups (256 threads) per row tile (the rows
+// of one sequence and KV head, as in the partials grid), one per quarter of the output
+// coordinates, so that each quarter of Pi_V^T is read once per tile. Thread (row r,
+// float4 column c4) merges its row's splits in one round of loads; then thread (output
+// i of the quarter, eighth e) forms its eighth of the inverse rotation for all 8 rows,
+// and lane shuffles add the eighths.
 constexpr int kMergeTileChunks = 8;
 struct MergeTileArgs {
   const DevHead* heads;    // this layer's heads (Hadamard value rotations)
@@ -2146,10 +2156,9 @@ struct MergeTileArgs {
 
 __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
   __shared__ float4 accs[8][kD / 4];
-  __shared__ float part[2][8][kD];
   __shared__ int32_t rid[8];
   const int tid = threadIdx.x;
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.x, oq = blockIdx.y;
   int seq, h, tr;
   if (a.prefill) {
     h = tile / a.tiles_per_kv;
@@ -2161,16 +2170,21 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
     h = rem / a.tiles_per_kv;
     tr = rem - h * a.tiles_per_kv;
   }
-  // the inverse rotation operand first: thread (i, half) holds Pi_V^T[i][64 half .. + 63]
-  // (none for a Hadamard Pi_V, applied as a transform)
-  const int oi = tid & 127, oh = tid >> 7;
+  // the inverse rotation operand first: thread (output oi of this quarter, eighth e)
+  // holds Pi_V^T[oi][16 e .. + 15] (none for a Hadamard Pi_V, applied as a transform by
+  // the first quarter alone)
   const DevHead* __restrict__ hp = a.heads + h;
   const bool had = hp->v_hadamard != 0;
-  float4 pvt[16];
-  {
-    const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)h * kD * kD + (size_t)oi * kD + 64 * oh);
+  if (had && oq != 0) return;
+  const int nqw = gridDim.y;  // workgroups per tile: 4 (one quarter each) or 1 (all four)
+  const int oe = tid & 7;
+  float4 pvt[4][4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) pvt[u] = had ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
+  for (int j = 0; j < 4; ++j) {
+    const int qo = oq + j * nqw, oi = 32 * qo + (tid >> 3);
+    const float4* pt = reinterpret_cast<const float4*>(a.vrot_t + (size_t)h * kD * kD + (size_t)oi * kD + 16 * oe);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pvt[j][u] = (had || qo >= 4) ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
   }
   // row r of the tile: global row id (-1 if absent) and visible length
   const int r = tid >> 5, c4 = tid & 31;
@@ -2250,29 +2264,32 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
   }
   accs[r][c4] = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
   __syncthreads();
-  float o[8];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) o[rr] = 0.f;
+  for (int j = 0; j < 4; ++j) {
+    const int qo = oq + j * nqw, oi = 32 * qo + (tid >> 3);
+    if (qo >= 4) break;
+    float o[8];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
+    for (int rr = 0; rr < 8; ++rr) o[rr] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const float4 x = accs[rr][4 * oe + u];
+        o[rr] = fmaf(pvt[j][u].x, x.x, o[rr]);
+        o[rr] = fmaf(pvt[j][u].y, x.y, o[rr]);
+        o[rr] = fmaf(pvt[j][u].z, x.z, o[rr]);
+        o[rr] = fmaf(pvt[j][u].w, x.w, o[rr]);
+      }
+    }
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
-      const float4 x = accs[rr][16 * oh + u];
-      o[rr] = fmaf(pvt[u].x, x.x, o[rr]);
-      o[rr] = fmaf(pvt[u].y, x.y, o[rr]);
-      o[rr] = fmaf(pvt[u].z, x.z, o[rr]);
-      o[rr] = fmaf(pvt[u].w, x.w, o[rr]);
+      o[rr] += __shfl_xor(o[rr], 1);
+      o[rr] += __shfl_xor(o[rr], 2);
+      o[rr] += __shfl_xor(o[rr], 4);
+      const int orow = rid[rr];
+      if (oe == 0 && orow >= 0) a.out[(size_t)orow * kD + oi] = o[rr];
     }
-  }
-#pragma unroll
-  for (int rr = 0; rr < 8; ++rr) part[oh][rr][oi] = o[rr];
-  __syncthreads();
-  const int orow = rid[r];
-  if (orow >= 0) {
-    const float4 p0 = *reinterpret_cast<const float4*>(&part[0][r][4 * c4]);
-    const float4 p1 = *reinterpret_cast<const float4*>(&part[1][r][4 * c4]);
-    *reinterpret_cast<float4*>(a.out + (size_t)orow * kD + 4 * c4) =
-        make_float4(p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w);
   }
 }
 
@@ -2504,6 +2521,10 @@ gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L,
   return ok();
 }
 
+// merge workgroups per row (tile): one per quarter of the inverse rotation while few rows
+// (tiles) leave most compute units idle, else one
+inline unsigned merge_quarters(int64_t n) { return n < 256 ? 4u : 1u; }
+
 gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const int32_t* seq_len,
                         int64_t pos0, int prefill, int max_len, float* out, const void* ws,
                         hipStream_t stream, const gtq_window_view* w = nullptr) {
@@ -2517,7 +2538,8 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
       mt.n_sink = w->n_sink;
       mt.n_recent = w->n_recent;
     }
-    hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.merge_n_tiles), dim3(256), 0, stream, mt);
+    hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.merge_n_tiles, merge_quarters(L.merge_n_tiles)),
+                       dim3(256), 0, stream, mt);
   } else {  // one workgroup per row
     MergeArgs ma{p->d_heads + (size_t)layer * p->n_kv, vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, L.n_chunks, L.chunk, prefill,
                  max_len};
@@ -2526,7 +2548,7 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
       ma.n_sink = w->n_sink;
       ma.n_recent = w->n_recent;
     }
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows, 4), dim3(256), 0, stream, ma);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows, merge_quarters(L.rows)), dim3(256), 0, stream, ma);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq attention merge: launch");
