@@ -642,3 +642,22 @@ def test_hadamard_value_rotation(G, chunk):
             _, ref = _oracle_decode(case, 0, b, n, enc, q[b], sc)
             assert_close(out[b].cpu().numpy(), ref, f"hadamard out b{b}")
     plan.destroy()
+
+
+def test_paged_view_errors(G):
+    """Paged views that the host rejects before any launch: a page size that is not a
+    power of two of at least 32, an empty pool, a capacity beyond the table."""
+    _say("case: paged view argument errors")
+    case = Case(11, 1, 2, 4, 64, 128, 2, batch=1)
+    plan = case.plan()
+    q = _dev(np.stack([case.q(0, 0)]))
+    sl = _dev(np.array([64], np.int32))
+    for P, n_pages, maxp in ((48, 4, 2), (16, 4, 4), (64, 4, 2)):
+        pc = G.PagedCache(plan, 1, n_pages, P if P % 32 == 0 else 64, maxp)
+        pc.page_tokens = P
+        if P == 64:
+            pc.capacity = 64 * maxp + 64  # beyond table_stride * page_tokens
+        with pytest.raises(G.GtqError) as e:
+            G.gtq_decode_attn(plan, 0, pc, q, sl, 64, 0.1)
+        assert e.value.status == 1 and "paged cache" in str(e.value)
+    plan.destroy()
