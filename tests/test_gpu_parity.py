@@ -661,3 +661,40 @@ def test_paged_view_errors(G):
             G.gtq_decode_attn(plan, 0, pc, q, sl, 64, 0.1)
         assert e.value.status == 1 and "paged cache" in str(e.value)
     plan.destroy()
+
+
+@pytest.mark.parametrize("g", [12, 16])
+def test_wide_gqa_groups(G, g):
+    """More than 8 query heads per KV head (two row tiles per KV head): append, decode
+    (tile and row merges), the fused step and the fp16 window decode against the oracle."""
+    _say(f"case: GQA group of {g} query heads")
+    n = 170
+    case = Case(12, 1, 2, g, n, 128, 2, batch=1)
+    plan = case.plan()
+    cache = G.PackedCache(plan, 1, 192)
+    enc = _encode(case, 0, 0, n)
+    _upload_oracle_cache(case, cache, 0, 0, n, enc)
+    q = case.q(0, 0)[None]
+    sc = scale_default()
+    for chunk in (0, 32):
+        lg = torch.zeros((1, case.HQ, n), device="cuda")
+        out = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(np.array([n], np.int32)), n, sc, chunk=chunk,
+                                logits=lg)
+        torch.cuda.synchronize()
+        lg_ref, out_ref = _oracle_decode(case, 0, 0, n, enc, q[0], sc)
+        assert_close(lg[0].cpu().numpy(), lg_ref, f"g{g} logits chunk {chunk}")
+        assert_close(out[0].cpu().numpy(), out_ref, f"g{g} out chunk {chunk}")
+    win = G.WindowCache(plan, 1, 4, 32)
+    k, v = case.kv(0, 0)
+    pos = _window_positions_to_fill(n, 4, 32)
+    G.gtq_window_append(plan, 0, win, _dev(k[pos]), _dev(v[pos]), _dev(np.zeros(len(pos), np.int32)), _dev(pos))
+    ow = G.gtq_decode_attn_window(plan, 0, cache, win, _dev(q), _dev(np.array([n], np.int32)), n, sc)
+    torch.cuda.synchronize()
+    for h in range(case.H):
+        e = enc[h]
+        sl = slice(h * g, (h + 1) * g)
+        inp = case.inputs[0, h][0]
+        _, o_ref = O.decode_attention_window(case.heads[0, h], q[0, sl], e["k_words"], e["k_norms"], e["v_words"],
+                                             e["v_norms"], inp["k"], inp["v"], 4, 32, sc, n)
+        assert_close(ow[0, sl].cpu().numpy(), o_ref, f"g{g} window out h{h}")
+    plan.destroy()
