@@ -325,11 +325,13 @@ def test_norm_corrected_append(G):
             assert_close(out[b].cpu().numpy(), out_ref, f"{what} decode out")
 
 
-def test_prefill_chunk(G):
-    """g = 5 (Qwen2.5-32B ratio): append 176 tokens, then a 60-token chunk appended and
-    attended causally over the packed cache."""
-    _say("case: chunked prefill g=5")
-    n0, T = 176, 60
+@pytest.mark.parametrize("T", [60, 61, 7])
+def test_prefill_chunk(G, T):
+    """g = 5 (Qwen2.5-32B ratio): append 176 tokens, then a T-token chunk appended and
+    attended causally over the packed cache (T g = 300, 305, 35 query rows per KV head: the
+    last 16-row tile holds 12, 1 and 3 rows)."""
+    _say(f"case: chunked prefill g=5 T={T}")
+    n0 = 176
     case = Case(4, 1, 2, 5, n0 + T, 192, 2, batch=1)
     plan = case.plan()
     cache = G.PackedCache(plan, 1, 256)
