@@ -320,27 +320,42 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       grp_of[i] = g;
     }
   }
+  // head fields the tile loop needs, read once: the loop's global stores could alias
+  // them, so reads inside it would be repeated (and waited for) on every tile
+  int kb0j[2], dj[2], b0j[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int g = tg[j] < 0 ? 0 : tg[j];
+    kb0j[j] = (g == 4) ? 0 : hp->kp_off[g];
+    dj[j] = (g == 4) ? kD : hp->dim[g];
+    b0j[j] = (g == 4) ? 0 : hp->bit_off[g] + ti0[j] * trate[j];
+  }
+  const int nd_store = (tid < kAppTile * kNS && tid % kNS < n_groups) ? hp->dim[tid % kNS] : 1;
   const float* src = vrole ? a.v : a.k;
   const int64_t s_begin = a.pos0 & ~(int64_t)(GTQ_VBLOCK - 1), s_end = a.pos0 + a.n_tok;
   const int64_t n_tiles = (s_end - s_begin + kAppTile - 1) / kAppTile;
   const size_t sh = (size_t)a.seq * a.n_kv + h;
   const int kw = a.k_words, vb = a.v_bits;
-  auto load_tile = [&](int64_t tile, float (&xr)[8]) {  // zeros outside the chunk
+  // the thread's 8 inputs of a tile: unconditional loads (token 0 of the chunk stands in
+  // for tokens outside it) whose validity is applied where they are used, so that the
+  // next tile's loads stay in flight during this one
+  auto load_tile = [&](int64_t tile, float (&xr)[8]) {
     const int64_t s = s_begin + tile * kAppTile + tau;
     const bool ok = tile < n_tiles && s >= a.pos0 && s < s_end;
-    const size_t row = ok ? ((size_t)(s - a.pos0) * a.n_kv + h) * kD : 0;
+    const size_t row = ok ? ((size_t)(s - a.pos0) * a.n_kv + h) * kD : (size_t)h * kD;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xr[i] = ok ? src[row + src_col[i]] : 0.f;
+    for (int i = 0; i < 8; ++i) xr[i] = src[row + src_col[i]];
+    return ok;
   };
   float xr[8];
-  load_tile(blockIdx.x, xr);
+  bool xok = load_tile(blockIdx.x, xr);
 
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     const int64_t ts = s_begin + tile * kAppTile;
     float x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = xr[i];
-    load_tile(tile + gridDim.x, xr);  // next tile, in flight during this one
+    for (int i = 0; i < 8; ++i) x[i] = xok ? xr[i] : 0.f;
+    xok = load_tile(tile + gridDim.x, xr);  // next tile, in flight during this one
     __syncthreads();                  // the previous tile's stores have read the buffers
     if (tid < kAppTile * 16) (&S.pk[0][0])[tid] = 0u;
     (&S.pv[0][0])[tid] = 0u;          // 4 x 128 == kAppThreads
@@ -384,7 +399,7 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
     for (int j = 0; j < 2; ++j) {
       if (tg[j] >= 0) {
         const int g = tg[j];
-        const int kb0 = (g == 4) ? 0 : hp->kp_off[g];
+        const int kb0 = kb0j[j];
         floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
@@ -404,7 +419,7 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
           }
         }
         // lane (q, n) holds D[token 16 hf + 4q + e][output i0 + n]
-        const int d = (g == 4) ? kD : hp->dim[g];
+        const int d = dj[j];
         const int i = ti0[j] + n;
         const float zs = sqrtf((float)d) * (1.f / (kRotSplitScale * 256.f));
         const int r = trate[j];
@@ -462,7 +477,7 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
           // for one token, i.e. one run of 16 r record bits starting at bit b0. Each lane
           // places its code in a 96-bit window, the row ORs the window together and three
           // lanes OR its words into the record.
-          const int b0 = hp->bit_off[g] + ti0[j] * r;
+          const int b0 = b0j[j];
           const int w0 = b0 >> 5;
           const int pos = (b0 & 31) + n * r;  // bit in the window (< 96)
           const int kq = pos >> 5, sft = pos & 31;
@@ -505,7 +520,7 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
           const int64_t ti = token_index(a.pm, a.capacity, a.n_kv, a.seq, h, s);
           if (ti >= 0)
             a.k_norms[ti * kNS + g] =
-                g >= n_groups ? 0.f : (a.nc ? corrected_norm(S.nu64[t][g], S.cs[t][g], hp->dim[g]) : S.nu[t][g]);
+                g >= n_groups ? 0.f : (a.nc ? corrected_norm(S.nu64[t][g], S.cs[t][g], nd_store) : S.nu[t][g]);
           else if (g == 0 && h == 0)
             atomicAdd(a.overflow, 1ull);  // once per token in an absent page
         }
