@@ -156,19 +156,21 @@ __device__ inline double wave_sum_f64(double v) {
 // f16 on split operands: 16 Pi = P_hi + P_lo (plan tables) and 256 u = U_hi + U_lo
 // (binary16 each); P_hi U_hi + P_hi U_lo + P_lo U_hi leaves out a 2^-22-relative term,
 // so z carries fp32-grade error.
-// A workgroup (8 waves) takes one KV head and one role (keys or values); each wave
-// keeps the rotation operands of its output tiles (16 outputs x all inputs) in
-// registers, and the workgroup streams 16-token tiles through LDS: stage, norms,
-// split, products and codes, pack and store.
+// A workgroup (8 waves) takes one KV head and one role (keys or values); wave w keeps
+// the rotation operands of outputs 16 w .. 16 w + 15 (x all 128 inputs) in registers:
+// the key groups' rotations form one block-diagonal matrix in record position order,
+// so a tile may hold outputs of two groups (rate, dimension and record bit are per
+// lane). The workgroup streams 32-token tiles through LDS: stage, norms, split,
+// products and codes, pack and store.
 // ============================================================================
 
 constexpr int kAppWaves = 8;
 constexpr int kAppThreads = 64 * kAppWaves;
 constexpr int kAppTile = 32;          // tokens per tile (two MFMA row tiles)
-constexpr int kAppPitch = 264;        // halves per A row (256 padded inputs + 8: no bank conflicts)
+constexpr int kAppPitch = 136;        // halves per A row (128 inputs + 8: no bank conflicts)
 
 struct AppendGemmShared {
-  _Float16 ua[2][kAppTile][kAppPitch];  // U_hi, U_lo in the padded input order
+  _Float16 ua[2][kAppTile][kAppPitch];  // U_hi, U_lo in record position (key) or coordinate order
   uint32_t pk[kAppTile][16];          // packed key records of the tile
   uint32_t pv[4][128];                // packed value blocks of the tile (8 tokens each)
   float nu[kAppTile][5];              // fp32 norms per token: key groups 0..3, value 4
@@ -236,79 +238,50 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
   const DevHead* __restrict__ hp = a.heads + h;
   const int n_groups = hp->n_groups;
 
-  // ---- this wave's output tiles: values: outputs 16 wave .. +15 over 4 input steps;
-  //      keys: tiles numbered over the groups (16 outputs each), wave w takes w, w + 8
-  int tg[2] = {-1, -1}, ti0[2] = {0, 0}, tsteps[2] = {0, 0}, trate[2] = {1, 1};
-  if (vrole) {
-    tg[0] = 4;
-    ti0[0] = 16 * wave;
-    tsteps[0] = 4;
-    trate[0] = a.v_bits;
-  } else {
-    int t = 0;
+  // ---- this wave's output tile: outputs 16 wave .. 16 wave + 15 (record positions of the
+  //      key, coordinates of the value) over all 128 inputs in 4 steps of 32; lane (q, n)
+  //      owns output p_out and its group's rate and dimension
+  const int p_out = 16 * wave + n;
+  int gp = 0;
+  if (!vrole) {
 #pragma unroll
-    for (int g = 0; g < kMaxGroups; ++g) {
-      if (g < n_groups) {
-        const int d = hp->dim[g], ns = (d + 15) >> 4;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int idx = wave + kAppWaves * j;
-          if (idx >= t && idx < t + ns) {
-            tg[j] = g;
-            ti0[j] = 16 * (idx - t);
-            tsteps[j] = (d + 31) >> 5;
-            trate[j] = hp->rate[g];
-          }
-        }
-        t += ns;
-      }
-    }
+    for (int gg = 1; gg < kMaxGroups; ++gg)
+      if (gg < n_groups && p_out >= hp->pos_off[gg]) gp = gg;
   }
-  // rotation operands: lane (q, n) holds rows i0 + n, inputs 32 s + 8q .. +7, hi and lo
-  uint4 bh[2][4], bl[2][4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  const int rp = vrole ? a.v_bits : hp->rate[gp];
+  const int dp = vrole ? kD : hp->dim[gp];
+  // key record: the lane's code bit; a row's 16 outputs are one run of at most 64 bits
+  // from the bit of output 16 wave (lane 0), inside words w0 .. w0 + 2
+  const int bitp = vrole ? 0 : hp->bit_off[gp] + (p_out - hp->pos_off[gp]) * rp;
+  const int w0 = __builtin_amdgcn_readfirstlane(bitp) >> 5;
+  const int g_lo = __builtin_amdgcn_readfirstlane(gp), g_hi = __builtin_amdgcn_readlane(gp, 15);
+  // rotation operands: lane (q, n) holds row p_out, inputs 32 s + 8q .. +7, hi and lo
+  uint4 bh[4], bl[4];
+  {
+    const uint16_t* base = a.rsplit + (vrole ? hp->rsv_off : hp->rsk_off) + (size_t)p_out * kD + 8 * q;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      bh[j][st] = make_uint4(0, 0, 0, 0);
-      bl[j][st] = make_uint4(0, 0, 0, 0);
-      if (tg[j] >= 0 && st < tsteps[j]) {
-        int rows, cols;
-        int64_t off;
-        if (tg[j] == 4) {
-          rows = kD;
-          cols = kD;
-          off = hp->rsv_off;
-        } else {
-          const int d = hp->dim[tg[j]];
-          rows = (d + 15) >> 4 << 4;
-          cols = (d + 31) >> 5 << 5;
-          off = hp->rsk_off[tg[j]];
-        }
-        const uint16_t* base = a.rsplit + off + (size_t)(ti0[j] + n) * cols + 32 * st + 8 * q;
-        bh[j][st] = *reinterpret_cast<const uint4*>(base);
-        bl[j][st] = *reinterpret_cast<const uint4*>(base + (size_t)rows * cols);
-      }
+      bh[st] = *reinterpret_cast<const uint4*>(base + 32 * st);
+      bl[st] = *reinterpret_cast<const uint4*>(base + kD * kD + 32 * st);
     }
   }
   if (tid < 80) {
     (&S.thr[0][0])[tid] = (&a.cb->t[0][0])[tid];
     (&S.cen[0][0])[tid] = (&a.cb->c[0][0])[tid];
   }
-  // zero the A operands once: padding columns stay zero
+  // zero the A operands once (the pitch's pad columns are never read)
   for (int e = tid; e < 2 * kAppTile * kAppPitch / 8; e += kAppThreads)
     reinterpret_cast<uint4*>(&S.ua[0][0][0])[e] = make_uint4(0, 0, 0, 0);
 
   // ---- this thread's 8 inputs of a tile: token tau = tid >> 4 (one 16-lane row per
   //      token), columns c = (tid & 15) + 16 i
   const int tau = tid >> 4, sub = tid & 15;
-  int src_col[8], kp_col[8], grp_of[8];
+  int src_col[8], grp_of[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = sub + 16 * i;  // record position (keys) or coordinate (values)
     if (vrole) {
       src_col[i] = c;
-      kp_col[i] = c;
       grp_of[i] = 0;
     } else {
       int g = 0;
@@ -316,20 +289,11 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       for (int gg = 1; gg < kMaxGroups; ++gg)
         if (gg < n_groups && c >= hp->pos_off[gg]) g = gg;
       src_col[i] = hp->coord[c];
-      kp_col[i] = hp->kp_off[g] + (c - hp->pos_off[g]);
       grp_of[i] = g;
     }
   }
-  // head fields the tile loop needs, read once: the loop's global stores could alias
-  // them, so reads inside it would be repeated (and waited for) on every tile
-  int kb0j[2], dj[2], b0j[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int g = tg[j] < 0 ? 0 : tg[j];
-    kb0j[j] = (g == 4) ? 0 : hp->kp_off[g];
-    dj[j] = (g == 4) ? kD : hp->dim[g];
-    b0j[j] = (g == 4) ? 0 : hp->bit_off[g] + ti0[j] * trate[j];
-  }
+  // (head fields the tile loop needs are all read before it: the loop's global stores
+  // could alias them, so reads inside it would be repeated and waited for on every tile)
   const int nd_store = (tid < kAppTile * kNS && tid % kNS < n_groups) ? hp->dim[tid % kNS] : 1;
   const float* src = vrole ? a.v : a.k;
   const int64_t s_begin = a.pos0 & ~(int64_t)(GTQ_VBLOCK - 1), s_end = a.pos0 + a.n_tok;
@@ -390,115 +354,101 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
       for (int gg = 1; gg < kMaxGroups; ++gg) iv = (grp_of[i] == gg) ? inv[gg] : iv;
       const float u = (float)((double)x[i] * iv) * 256.f;
       const _Float16 hi = (_Float16)u;
-      S.ua[0][tau][kp_col[i]] = hi;
-      S.ua[1][tau][kp_col[i]] = (_Float16)(u - (float)hi);
+      S.ua[0][tau][sub + 16 * i] = hi;
+      S.ua[1][tau][sub + 16 * i] = (_Float16)(u - (float)hi);
     }
     __syncthreads();
-    // ---- products, codes and packing of this wave's tiles (both 16-token halves)
+    // ---- products, codes and packing of this wave's tile (both 16-token halves)
+    floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (tg[j] >= 0) {
-        const int g = tg[j];
-        const int kb0 = kb0j[j];
-        floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int st = 0; st < 4; ++st) {
+      H8 ph, pl;
+      ph.v = bh[st];
+      pl.v = bl[st];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          if (st < tsteps[j]) {
-            H8 ph, pl;
-            ph.v = bh[j][st];
-            pl.v = bl[j][st];
+      for (int hf = 0; hf < 2; ++hf) {
+        H8 ah, al;
+        ah.v = *reinterpret_cast<const uint4*>(&S.ua[0][16 * hf + n][32 * st + 8 * q]);
+        al.v = *reinterpret_cast<const uint4*>(&S.ua[1][16 * hf + n][32 * st + 8 * q]);
+        acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, ph.h, acc[hf], 0, 0, 0);
+        acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al.h, ph.h, acc[hf], 0, 0, 0);
+        acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, pl.h, acc[hf], 0, 0, 0);
+      }
+    }
+    // lane (q, n) holds D[token 16 hf + 4q + e][output p_out]
+    const float zs = sqrtf((float)dp) * (1.f / (kRotSplitScale * 256.f));
+    const float* th = S.thr[rp];
+    // code = #{k : z >= t_k} by binary search over the sorted thresholds of the lane's
+    // rate, one search level at a time for all 8 values of the lane (the threshold reads
+    // of a level go out together)
+    int cds[8];
+    float zv[8];
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              H8 ah, al;
-              ah.v = *reinterpret_cast<const uint4*>(&S.ua[0][16 * hf + n][kb0 + 32 * st + 8 * q]);
-              al.v = *reinterpret_cast<const uint4*>(&S.ua[1][16 * hf + n][kb0 + 32 * st + 8 * q]);
-              acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, ph.h, acc[hf], 0, 0, 0);
-              acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al.h, ph.h, acc[hf], 0, 0, 0);
-              acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah.h, pl.h, acc[hf], 0, 0, 0);
-            }
-          }
+    for (int v8 = 0; v8 < 8; ++v8) {
+      zv[v8] = acc[v8 >> 2][v8 & 3] * zs;
+      cds[v8] = 0;
+    }
+#pragma unroll
+    for (int lvl = 3; lvl >= 0; --lvl) {
+      if (lvl < rp) {
+        const int step = 1 << lvl;
+        float tv[8];
+#pragma unroll
+        for (int v8 = 0; v8 < 8; ++v8) tv[v8] = th[cds[v8] + step - 1];
+#pragma unroll
+        for (int v8 = 0; v8 < 8; ++v8) cds[v8] += zv[v8] >= tv[v8] ? step : 0;
+      }
+    }
+    if (a.nc) {
+      // sum of C[code]^2 over each group's outputs in the row, for each of the lane's 8
+      // tokens (the row's groups are g_lo .. g_hi)
+      const float* cr = S.cen[rp];
+#pragma unroll
+      for (int v8 = 0; v8 < 8; ++v8) {
+        const double c = (double)cr[cds[v8]];
+        for (int g = g_lo; g <= g_hi; ++g) {
+          const double rs = row_sum_f64(gp == g ? c * c : 0.0);
+          if (n == 0) atomicAdd(&S.cs[16 * (v8 >> 2) + 4 * q + (v8 & 3)][vrole ? 4 : g], rs);
         }
-        // lane (q, n) holds D[token 16 hf + 4q + e][output i0 + n]
-        const int d = dj[j];
-        const int i = ti0[j] + n;
-        const float zs = sqrtf((float)d) * (1.f / (kRotSplitScale * 256.f));
-        const int r = trate[j];
-        const float* th = S.thr[r];
-        // code = #{k : z >= t_k} by binary search over the sorted thresholds, one search
-        // level at a time for all 8 values of the lane (the threshold reads of a level go
-        // out together)
-        int cds[8];
-        float zv[8];
+      }
+    }
+    if (vrole) {
+      const int r = rp, i = p_out;
 #pragma unroll
-        for (int v8 = 0; v8 < 8; ++v8) {
-          zv[v8] = acc[v8 >> 2][v8 & 3] * zs;
-          cds[v8] = 0;
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cd = cds[4 * hf + e];
+          const int t = 16 * hf + 4 * q + e;
+          // token t & 7 of block t >> 3, coordinate i at bit 8 vb i + vb (t & 7)
+          const int bit = 8 * r * i + r * (t & 7);
+          uint32_t* dst = &S.pv[t >> 3][0];
+          const uint64_t f = (uint64_t)cd << (bit & 31);
+          atomicOr(dst + (bit >> 5), (uint32_t)f);
+          if (f >> 32) atomicOr(dst + (bit >> 5) + 1, (uint32_t)(f >> 32));
         }
+      }
+    } else {
+      // keys: each lane places its code in the row's 96-bit window from word w0, the row
+      // ORs the window together and three lanes OR its words into the record
+      const int pos = bitp - 32 * w0;
+      const int kq = pos >> 5, sft = pos & 31;
 #pragma unroll
-        for (int lvl = 3; lvl >= 0; --lvl) {
-          if (lvl < r) {
-            const int step = 1 << lvl;
-            float tv[8];
+      for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-            for (int v8 = 0; v8 < 8; ++v8) tv[v8] = th[cds[v8] + step - 1];
-#pragma unroll
-            for (int v8 = 0; v8 < 8; ++v8) cds[v8] += zv[v8] >= tv[v8] ? step : 0;
-          }
-        }
-        if (a.nc) {
-          // sum of C[code]^2 over the row's 16 outputs for each of the lane's 8 tokens
-          const float* cr = S.cen[r];
-#pragma unroll
-          for (int v8 = 0; v8 < 8; ++v8) {
-            const double c = i < d ? (double)cr[cds[v8]] : 0.0;
-            const double rs = row_sum_f64(c * c);
-            if (n == 0) atomicAdd(&S.cs[16 * (v8 >> 2) + 4 * q + (v8 & 3)][g], rs);
-          }
-        }
-        if (g == 4) {
-          if (i < d) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int cd = cds[4 * hf + e];
-                const int t = 16 * hf + 4 * q + e;
-                // token t & 7 of block t >> 3, coordinate i at bit 8 vb i + vb (t & 7)
-                const int bit = 8 * r * i + r * (t & 7);
-                uint32_t* dst = &S.pv[t >> 3][0];
-                const uint64_t f = (uint64_t)cd << (bit & 31);
-                atomicOr(dst + (bit >> 5), (uint32_t)f);
-                if (f >> 32) atomicOr(dst + (bit >> 5) + 1, (uint32_t)(f >> 32));
-              }
-            }
-          }
-        } else {
-          // keys: the 16 lanes of a row hold consecutive positions i0..i0+15 of one group
-          // for one token, i.e. one run of 16 r record bits starting at bit b0. Each lane
-          // places its code in a 96-bit window, the row ORs the window together and three
-          // lanes OR its words into the record.
-          const int b0 = b0j[j];
-          const int w0 = b0 >> 5;
-          const int pos = (b0 & 31) + n * r;  // bit in the window (< 96)
-          const int kq = pos >> 5, sft = pos & 31;
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int cd = i >= d ? 0 : cds[4 * hf + e];  // zero: padding outputs of the group's last tile
-              const uint32_t lo = (uint32_t)cd << sft;
-              const uint32_t hi = sft ? (uint32_t)cd >> (32 - sft) : 0u;
-              uint32_t v0 = kq == 0 ? lo : 0u;
-              uint32_t v1 = kq == 0 ? hi : (kq == 1 ? lo : 0u);
-              uint32_t v2 = kq == 1 ? hi : (kq == 2 ? lo : 0u);
-              v0 = row_or_u32(v0);
-              v1 = row_or_u32(v1);
-              v2 = row_or_u32(v2);
-              const int t = 16 * hf + 4 * q + e;
-              const uint32_t vv = n == 0 ? v0 : (n == 1 ? v1 : v2);
-              if (n < 3 && vv) atomicOr(&S.pk[t][w0 + n], vv);
-            }
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int cd = cds[4 * hf + e];
+          const uint32_t lo = (uint32_t)cd << sft;
+          const uint32_t hi = sft ? (uint32_t)cd >> (32 - sft) : 0u;
+          uint32_t v0 = kq == 0 ? lo : 0u;
+          uint32_t v1 = kq == 0 ? hi : (kq == 1 ? lo : 0u);
+          uint32_t v2 = kq == 1 ? hi : (kq == 2 ? lo : 0u);
+          v0 = row_or_u32(v0);
+          v1 = row_or_u32(v1);
+          v2 = row_or_u32(v2);
+          const int t = 16 * hf + 4 * q + e;
+          const uint32_t vv = n == 0 ? v0 : (n == 1 ? v1 : v2);
+          if (n < 3 && vv) atomicOr(&S.pk[t][w0 + n], vv);
         }
       }
     }

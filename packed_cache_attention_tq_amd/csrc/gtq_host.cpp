@@ -407,17 +407,15 @@ gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
       if (!isfinite(p->rot[dh.krot_off[0] + i]))
         return fail(GTQ_EINVAL, "gtq_plan_create: non-finite K rotation");
   }
-  // split rotations: 16 Pi = hi + lo + O(2^-24), both binary16, padded to whole MFMA
-  // tiles (16 output rows, 32 input columns) with zeros
+  // split rotations: 16 Pi = hi + lo + O(2^-24), both binary16, as 128 x 128 matrices
+  // (the key groups' Pi_g on the diagonal blocks of record position order, zeros across
+  // groups), so that the append's MFMA tiles of 16 outputs need no per-group padding
   {
     size_t total = 0;
     for (size_t h = 0; h < nh; ++h) {
       DevHead& dh = p->heads[h];
-      for (int g = 0; g < dh.n_groups; ++g) {
-        const int d = dh.dim[g];
-        dh.rsk_off[g] = (int64_t)total;
-        total += 2 * (size_t)((d + 15) / 16 * 16) * ((d + 31) / 32 * 32);
-      }
+      dh.rsk_off = (int64_t)total;
+      total += 2 * vsz;
       dh.rsv_off = (int64_t)total;
       total += 2 * vsz;
     }
@@ -426,21 +424,23 @@ gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
     } catch (...) {
       return fail(GTQ_ENOMEM, "gtq_plan_create: host allocation failed");
     }
-    auto put = [&](const float* src, int d, size_t off) {
-      const int rows = (d + 15) / 16 * 16, cols = (d + 31) / 32 * 32;
+    // Pi (d x d, row-major) into rows and columns [p0, p0 + d) of the 128 x 128 pair at off
+    auto put = [&](const float* src, int d, int p0, size_t off) {
       for (int i = 0; i < d; ++i)
         for (int j = 0; j < d; ++j) {
           const float x = kRotSplitScale * src[(size_t)i * d + j];
           const _Float16 hi = (_Float16)x;
           const _Float16 lo = (_Float16)(x - (float)hi);
-          memcpy(&p->rsplit[off + (size_t)i * cols + j], &hi, 2);
-          memcpy(&p->rsplit[off + (size_t)rows * cols + (size_t)i * cols + j], &lo, 2);
+          const size_t e = (size_t)(p0 + i) * kD + (p0 + j);
+          memcpy(&p->rsplit[off + e], &hi, 2);
+          memcpy(&p->rsplit[off + vsz + e], &lo, 2);
         }
     };
     for (size_t h = 0; h < nh; ++h) {
       const DevHead& dh = p->heads[h];
-      for (int g = 0; g < dh.n_groups; ++g) put(p->rot.data() + dh.krot_off[g], dh.dim[g], dh.rsk_off[g]);
-      put(p->rot.data() + dh.vrot_off, kD, dh.rsv_off);
+      for (int g = 0; g < dh.n_groups; ++g)
+        put(p->rot.data() + dh.krot_off[g], dh.dim[g], dh.pos_off[g], dh.rsk_off);
+      put(p->rot.data() + dh.vrot_off, kD, 0, dh.rsv_off);
     }
   }
   fill_codebook(&p->cb);

@@ -35,8 +35,9 @@ struct DevHead {
   int64_t krot_off[kMaxGroups];   // float offset of Pi_g (row-major d x d) in the pool
   int64_t vrot_off;               // float offset of Pi_V (row-major 128 x 128)
   int64_t vrot_t_off;             // float offset of Pi_V^T (row-major, i.e. Pi_V column-major)
-  int64_t rsk_off[kMaxGroups];   // split K rotations of group g: binary16 hi then lo blocks of
-                                  // ceil16(d) rows x ceil32(d) columns (zero padded)
+  int64_t rsk_off;                // split K rotation: the block-diagonal 128 x 128 matrix of the
+                                  // Pi_g in record position order (zeros across groups), binary16
+                                  // hi then lo
   int64_t rsv_off;                // split V rotation: hi then lo, 128 x 128
   int32_t krot_floats;            // sum_g d_g^2
   int32_t v_hadamard;             // 1: Pi_V = H_128 diag(vsign) / sqrt(128) exactly (fast transform)
