@@ -228,7 +228,9 @@ __device__ inline float wht128(float x, int e, bool owner, float* buf) {
 }
 constexpr float kInvSqrt128 = 0.0883883461356163f;  // fp32 nearest to 1/sqrt(128)
 
-__global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) {
+// (at most 128 VGPRs, a few spilled: two workgroups per compute unit, so that one's
+// barriers and LDS round trips overlap the other's work)
+__global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_eu(4))) append_gemm_kernel(AppendArgs a) {
   __shared__ AppendGemmShared S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -327,25 +329,39 @@ __global__ void __launch_bounds__(kAppThreads) append_gemm_kernel(AppendArgs a) 
     // ---- norms (fp64, per token and group; every lane of the row gets all sums), then
     //      u = x / nu split as 256 u = U_hi + U_lo
     double sg[kMaxGroups] = {0.0, 0.0, 0.0, 0.0};
+    if (vrole) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double xv = x[i];
+      for (int i = 0; i < 8; ++i) sg[0] = fma((double)x[i], (double)x[i], sg[0]);
+    } else {
 #pragma unroll
-      for (int gg = 0; gg < kMaxGroups; ++gg) sg[gg] += (grp_of[i] == gg) ? xv * xv : 0.0;
+      for (int i = 0; i < 8; ++i) {
+        const double xv = x[i];
+#pragma unroll
+        for (int gg = 0; gg < kMaxGroups; ++gg) sg[gg] += (grp_of[i] == gg) ? xv * xv : 0.0;
+      }
     }
+    // every lane gets each group's sum; the stored norm is the correctly rounded fp64
+    // sqrt (lane sub computes group sub's), the scaling 1 / nu takes the hardware
+    // reciprocal square root and one Newton step (relative error far below the split
+    // products' 2^-22)
     const int ng = vrole ? 1 : n_groups;
-    double inv[kMaxGroups];
+    double inv[kMaxGroups], own = 0.0;
 #pragma unroll
     for (int gg = 0; gg < kMaxGroups; ++gg) {
       inv[gg] = 0.0;
       if (gg < ng) {
-        const double nu = sqrt(row_sum_f64(sg[gg]));
-        inv[gg] = nu > 0.0 ? 1.0 / nu : 0.0;
-        if (sub == gg) {
-          S.nu[tau][vrole ? 4 : gg] = (float)nu;
-          if (a.nc) S.nu64[tau][vrole ? 4 : gg] = nu;
+        const double t = row_sum_f64(sg[gg]);
+        if (sub == gg) own = t;
+        if (t > 0.0) {
+          const double y = __builtin_amdgcn_rsq(t);
+          inv[gg] = y * fma(-0.5 * t, y * y, 1.5);
         }
       }
+    }
+    if (sub < ng) {
+      const double nu = sqrt(own);
+      S.nu[tau][vrole ? 4 : sub] = (float)nu;
+      if (a.nc) S.nu64[tau][vrole ? 4 : sub] = nu;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
