@@ -541,6 +541,41 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
 // LDS; the norms are fp64 wave reductions; thread (output o, quarter qq) forms a
 // quarter of one rotated coordinate. The two value halves write disjoint words of the
 // token's value block.
+// A head's key group layout, read in one round of uniform loads (none waits on another;
+// short-circuit tests on n_groups would chain them), and selection by group index
+// without indexed (per-lane) loads.
+struct GroupLayout {
+  int n;
+  int pos[kMaxGroups], dim[kMaxGroups], rate[kMaxGroups], bit[kMaxGroups], kp[kMaxGroups];
+  int64_t krot[kMaxGroups];
+};
+// (written out without loops: every array index is a constant from the start, so the
+// struct lives in registers)
+static_assert(kMaxGroups == 4, "the layout helpers are written for four groups");
+__device__ inline GroupLayout load_layout(const DevHead* hd) {
+  GroupLayout L;
+  L.n = hd->n_groups;
+  L.pos[0] = hd->pos_off[0], L.pos[1] = hd->pos_off[1], L.pos[2] = hd->pos_off[2], L.pos[3] = hd->pos_off[3];
+  L.dim[0] = hd->dim[0], L.dim[1] = hd->dim[1], L.dim[2] = hd->dim[2], L.dim[3] = hd->dim[3];
+  L.rate[0] = hd->rate[0], L.rate[1] = hd->rate[1], L.rate[2] = hd->rate[2], L.rate[3] = hd->rate[3];
+  L.bit[0] = hd->bit_off[0], L.bit[1] = hd->bit_off[1], L.bit[2] = hd->bit_off[2], L.bit[3] = hd->bit_off[3];
+  L.kp[0] = hd->kp_off[0], L.kp[1] = hd->kp_off[1], L.kp[2] = hd->kp_off[2], L.kp[3] = hd->kp_off[3];
+  L.krot[0] = hd->krot_off[0], L.krot[1] = hd->krot_off[1], L.krot[2] = hd->krot_off[2], L.krot[3] = hd->krot_off[3];
+  return L;
+}
+// group of record position p
+__device__ inline int group_of(const GroupLayout& L, int p) {
+  int g = 0;
+  g = (1 < L.n && p >= L.pos[1]) ? 1 : g;
+  g = (2 < L.n && p >= L.pos[2]) ? 2 : g;
+  g = (3 < L.n && p >= L.pos[3]) ? 3 : g;
+  return g;
+}
+template <typename T>
+__device__ inline T pick(const T (&v)[kMaxGroups], int g) {
+  return g == 3 ? v[3] : (g == 2 ? v[2] : (g == 1 ? v[1] : v[0]));
+}
+
 __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h, int role) {
   __shared__ float xnat[2 * kD];        // key then value, natural order
   __shared__ __align__(16) float xs[2 * kD];  // key (record order) then value coordinates
@@ -552,7 +587,8 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   __shared__ float thr[5][16], cen[5][16];
   const int tid = threadIdx.x;
   const DevHead* __restrict__ hd = a.heads + h;
-  const int n_groups = hd->n_groups;
+  const GroupLayout GL = load_layout(hd);
+  const int n_groups = GL.n;
   const size_t row = ((size_t)tok * a.n_kv + h) * kD;
   float xv = 0.f;
   if (tid < kD) xv = a.k[row + tid];
@@ -571,14 +607,12 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   float4 pv[8];
   int kg = 0, klo = 0, khi = 0;
   if (o < kD) {
-#pragma unroll
-    for (int gg = 1; gg < kMaxGroups; ++gg)
-      if (gg < n_groups && o >= hd->pos_off[gg]) kg = gg;
-    const int d = hd->dim[kg], i = o - hd->pos_off[kg], dp = d >> 1;
+    kg = group_of(GL, o);
+    const int d = pick(GL.dim, kg), i = o - pick(GL.pos, kg), dp = d >> 1;
     klo = (dp * qq) >> 2;
     khi = (dp * (qq + 1)) >> 2;
     if (!mine) khi = klo;  // (no key work outside role 0)
-    const float2* pr = reinterpret_cast<const float2*>(a.rot + hd->krot_off[kg] + (size_t)i * d);
+    const float2* pr = reinterpret_cast<const float2*>(a.rot + pick(GL.krot, kg) + (size_t)i * d);
 #pragma unroll
     for (int u = 0; u < 16; ++u) pk[u] = (klo + u < khi) ? pr[klo + u] : make_float2(0.f, 0.f);
   } else {
@@ -614,10 +648,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   if (tid < 64) {
     const double x0 = xs[2 * tid], x1 = xs[2 * tid + 1];
     const double sq = x0 * x0 + x1 * x1;
-    int mg = 0;
-#pragma unroll
-    for (int g = 1; g < kMaxGroups; ++g)
-      if (g < n_groups && 2 * tid >= hd->pos_off[g]) mg = g;
+    const int mg = group_of(GL, 2 * tid);
     double s4[kMaxGroups];
 #pragma unroll
     for (int g = 0; g < kMaxGroups; ++g) s4[g] = (mg == g) ? sq : 0.0;
@@ -630,7 +661,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
       const double nu = sqrt(sg);
       nu_s[tid] = (float)nu;
       nu64_s[tid] = nu;
-      sc_s[tid] = nu > 0.0 ? (float)(sqrt((double)hd->dim[tid]) / nu) : 0.f;
+      sc_s[tid] = nu > 0.0 ? (float)(sqrt((double)pick(GL.dim, tid)) / nu) : 0.f;
     }
   } else if (tid < 128) {
     const int l = tid - 64;
@@ -647,7 +678,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   {
     float acc = 0.f;
     if (o < kD) {
-      const float2* x = reinterpret_cast<const float2*>(xs + hd->pos_off[kg]);
+      const float2* x = reinterpret_cast<const float2*>(xs + pick(GL.pos, kg));
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         if (klo + u < khi) {
@@ -684,9 +715,9 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     const float z0 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
     if (tid < kD) {
       const int g = kg;
-      const int b = hd->rate[g];
+      const int b = pick(GL.rate, g);
       const uint32_t c = quantize(z0 * sc_s[g], thr[b], (1 << b) - 1);
-      const int bit = hd->bit_off[g] + (tid - hd->pos_off[g]) * b;
+      const int bit = pick(GL.bit, g) + (tid - pick(GL.pos, g)) * b;
       const uint64_t f = (uint64_t)c << (bit & 31);
       atomicOr(&krec[bit >> 5], (uint32_t)f);
       if (f >> 32) atomicOr(&krec[(bit >> 5) + 1], (uint32_t)(f >> 32));
@@ -725,7 +756,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   if (do_k && tid >= 64 && tid < 64 + kNS) {
     const int g = tid - 64;
     a.k_norms[ti * kNS + g] =
-        g >= n_groups ? 0.f : (a.nc ? corrected_norm(nu64_s[g], cs_s[g], hd->dim[g]) : nu_s[g]);
+        g >= n_groups ? 0.f : (a.nc ? corrected_norm(nu64_s[g], cs_s[g], pick(GL.dim, g)) : nu_s[g]);
   }
   if ((role == 1 || role == 3) && tid == 128) a.v_norms[ti] = a.nc ? corrected_norm(nu64_s[4], cs_s[4], kD) : nu_s[4];
   if (do_v && tid >= 256 && tid < 256 + 32 * vb) {
@@ -914,21 +945,18 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
   int seq, h, tr;
   tile_coords(a, tile, &seq, &h, &tr);
   const DevHead* __restrict__ hp = a.heads + h;
-  const int n_groups = hp->n_groups;
+  const GroupLayout GL = load_layout(hp);
   // this thread's output: record position i, its group g, row ii of Pi_g, and its
   // eighth [plo, phi) of the d / 2 column pairs
   const int i = tid >> 3, part = tid & 7;
-  int g = 0;
-#pragma unroll
-  for (int gg = 1; gg < kMaxGroups; ++gg)
-    if (gg < n_groups && i >= hp->pos_off[gg]) g = gg;
-  const int d = hp->dim[g], po = hp->pos_off[g], ii = i - po, dp = d >> 1;
+  const int g = group_of(GL, i);
+  const int d = pick(GL.dim, g), po = pick(GL.pos, g), ii = i - po, dp = d >> 1;
   const int plo = (dp * part) >> 3, phi = (dp * (part + 1)) >> 3;
   // one round of loads: the rotation pairs, the tile's query rows (natural order) and
   // the head's record order
   float2 pr[8];
   {
-    const float2* row = reinterpret_cast<const float2*>(a.rot + hp->krot_off[g] + (size_t)ii * d);
+    const float2* row = reinterpret_cast<const float2*>(a.rot + pick(GL.krot, g) + (size_t)ii * d);
 #pragma unroll
     for (int u = 0; u < 8; ++u) pr[u] = (plo + u < phi) ? row[plo + u] : make_float2(0.f, 0.f);
   }
@@ -974,7 +1002,7 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
   }
   if (part == 0) {
     const float sc = a.qscale / sqrtf((float)d);
-    const int kp = hp->kp_off[g] + ii;
+    const int kp = pick(GL.kp, g) + ii;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const float val = acc[r] * sc;
