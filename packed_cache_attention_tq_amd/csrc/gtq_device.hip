@@ -2417,8 +2417,9 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   a.seq = seq;
   const int64_t s_begin = pos0 & ~(int64_t)(GTQ_VBLOCK - 1);
   const int64_t n_tiles = (pos0 + n_tok - s_begin + kAppTile - 1) / kAppTile;
-  // about four workgroups per compute unit, each over several tiles
-  const int64_t per_head = std::max<int64_t>(1, 1024 / (2 * (int64_t)p->n_kv));
+  // one round of workgroups, two per compute unit (512), each over several tiles with the
+  // next tile's inputs in flight
+  const int64_t per_head = std::max<int64_t>(1, 512 / (2 * (int64_t)p->n_kv));
   const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(n_tiles, per_head));
   hipLaunchKernelGGL(append_gemm_kernel, dim3(gx, p->n_kv, 2), dim3(kAppThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
