@@ -158,6 +158,17 @@ def _dev(t: torch.Tensor | None, dtype=None, name="tensor"):
     return C.c_void_p(t.data_ptr())
 
 
+def _need(t, numel: int, name: str, at_least: bool = False):
+    """Host-side size check before a tensor's pointer reaches a kernel: the C ABI takes
+    plain pointers and cannot see how much memory lies behind them."""
+    if t is None:
+        return
+    n = t.numel()
+    if (n < numel) if at_least else (n != numel):
+        raise ValueError(f"{name} holds {n} elements, {'at least ' if at_least else ''}{numel} expected "
+                         f"(shape {tuple(t.shape)})")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -318,6 +329,10 @@ class PagedCache(PackedCache):
 
 def gtq_quantize_append(plan: Plan, layer: int, cache: PackedCache, k, v, seq_idx, slot, stream=None):
     n = k.shape[0]
+    for t, nm in ((k, "k"), (v, "v")):
+        _need(t, n * plan.n_kv * HEAD_DIM, nm)
+    _need(seq_idx, n, "seq_idx")
+    _need(slot, n, "slot")
     cv = cache.view()
     st = lib().gtq_quantize_append(plan.handle, layer, C.byref(cv), _dev(k, torch.float32, "k"),
                                    _dev(v, torch.float32, "v"), _dev(seq_idx, torch.int32, "seq_idx"),
@@ -328,6 +343,8 @@ def gtq_quantize_append(plan: Plan, layer: int, cache: PackedCache, k, v, seq_id
 def gtq_quantize_append_chunk(plan: Plan, layer: int, cache: PackedCache, k, v, seq: int, pos0: int,
                               stream=None):
     n = k.shape[0]
+    for t, nm in ((k, "k"), (v, "v")):
+        _need(t, n * plan.n_kv * HEAD_DIM, nm)
     cv = cache.view()
     st = lib().gtq_quantize_append_chunk(plan.handle, layer, C.byref(cv), _dev(k, torch.float32, "k"),
                                          _dev(v, torch.float32, "v"), seq, pos0, n, _stream(stream))
@@ -341,10 +358,23 @@ def gtq_decode_workspace_bytes(plan: Plan, batch: int, max_len: int, chunk: int 
     return out.value
 
 
+def _decode_sizes(plan, cache, q, seq_len, max_len, logits=None, k_new=None, v_new=None):
+    B = cache.batch
+    if q is not None:
+        _need(q, B * plan.n_q * HEAD_DIM, "q")
+    _need(seq_len, B, "seq_len")
+    if logits is not None:
+        _need(logits, B * plan.n_q * max(int(max_len), 0), "logits")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, B * plan.n_kv * HEAD_DIM, nm)
+
+
 def gtq_decode_attn(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_len: int, scale: float,
                     chunk: int = 0, out=None, logits=None, workspace=None, stream=None):
+    _decode_sizes(plan, cache, q, seq_len, max_len, logits)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, q.numel(), "out")
     if workspace is None:
         nb = gtq_decode_workspace_bytes(plan, cache.batch, max_len, chunk)
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
@@ -360,6 +390,7 @@ def gtq_decode_attn(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_
 
 def gtq_decode_prepare(plan: Plan, layer: int, cache: PackedCache, k_new, v_new, q, seq_len, max_len: int,
                        scale: float, workspace, chunk: int = 0, stream=None):
+    _decode_sizes(plan, cache, q, seq_len, max_len, k_new=k_new, v_new=v_new)
     cv = cache.view()
     st = lib().gtq_decode_prepare(plan.handle, layer, C.byref(cv), _dev(k_new, torch.float32, "k_new"),
                                   _dev(v_new, torch.float32, "v_new"), _dev(q, torch.float32, "q"),
@@ -371,8 +402,10 @@ def gtq_decode_prepare(plan: Plan, layer: int, cache: PackedCache, k_new, v_new,
 
 def gtq_decode_step(plan: Plan, layer: int, cache: PackedCache, k_new, v_new, q, seq_len, max_len: int,
                     scale: float, chunk: int = 0, out=None, workspace=None, stream=None):
+    _decode_sizes(plan, cache, q, seq_len, max_len, k_new=k_new, v_new=v_new)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, q.numel(), "out")
     if workspace is None:
         workspace = torch.empty(gtq_decode_workspace_bytes(plan, cache.batch, max_len, chunk), dtype=torch.uint8,
                                 device=q.device)
@@ -388,6 +421,7 @@ def gtq_decode_step(plan: Plan, layer: int, cache: PackedCache, k_new, v_new, q,
 
 def gtq_decode_rotate_queries(plan: Plan, layer: int, cache: PackedCache, q, max_len: int, scale: float,
                               workspace, chunk: int = 0, stream=None):
+    _decode_sizes(plan, cache, q, None, max_len)
     cv = cache.view()
     st = lib().gtq_decode_rotate_queries(plan.handle, layer, C.byref(cv), _dev(q, torch.float32, "q"), max_len,
                                          float(scale), chunk, _dev(workspace, None, "workspace"),
@@ -397,6 +431,7 @@ def gtq_decode_rotate_queries(plan: Plan, layer: int, cache: PackedCache, q, max
 
 def gtq_decode_attn_partials(plan: Plan, layer: int, cache: PackedCache, seq_len, max_len: int, workspace,
                              chunk: int = 0, logits=None, stream=None):
+    _decode_sizes(plan, cache, None, seq_len, max_len, logits)
     cv = cache.view()
     st = lib().gtq_decode_attn_partials(plan.handle, layer, C.byref(cv), _dev(seq_len, torch.int32, "seq_len"),
                                         max_len, chunk, _dev(logits, torch.float32, "logits"),
@@ -407,6 +442,8 @@ def gtq_decode_attn_partials(plan: Plan, layer: int, cache: PackedCache, seq_len
 
 def gtq_decode_attn_merge(plan: Plan, layer: int, cache: PackedCache, seq_len, max_len: int, out, workspace,
                           chunk: int = 0, stream=None):
+    _decode_sizes(plan, cache, None, seq_len, max_len)
+    _need(out, cache.batch * plan.n_q * HEAD_DIM, "out")
     cv = cache.view()
     st = lib().gtq_decode_attn_merge(plan.handle, layer, C.byref(cv), _dev(seq_len, torch.int32, "seq_len"),
                                      max_len, chunk, _dev(out, torch.float32, "out"),
@@ -426,8 +463,10 @@ def gtq_prefill_workspace_bytes(plan: Plan, pos0: int, n_tok: int, chunk: int = 
 def gtq_prefill_attn(plan: Plan, layer: int, cache: PackedCache, q, seq: int, pos0: int, scale: float,
                      chunk: int = 0, out=None, workspace=None, stream=None):
     n = q.shape[0]
+    _need(q, n * plan.n_q * HEAD_DIM, "q")
     if out is None:
         out = torch.empty_like(q)
+    _need(out, q.numel(), "out")
     if workspace is None:
         nb = gtq_prefill_workspace_bytes(plan, pos0, n, chunk)
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
@@ -467,6 +506,11 @@ class WindowCache:
 
 
 def gtq_window_append(plan: Plan, layer: int, win: WindowCache, k, v, seq_idx, pos, stream=None):
+    n = k.shape[0]
+    for t, nm in ((k, "k"), (v, "v")):
+        _need(t, n * plan.n_kv * HEAD_DIM, nm)
+    _need(seq_idx, n, "seq_idx")
+    _need(pos, n, "pos")
     wv = win.view()
     st = lib().gtq_window_append(plan.handle, layer, C.byref(wv), _dev(k, torch.float32, "k"),
                                  _dev(v, torch.float32, "v"), _dev(seq_idx, torch.int32, "seq_idx"),
@@ -484,8 +528,10 @@ def gtq_decode_window_workspace_bytes(plan: Plan, batch: int, max_len: int, chun
 def gtq_decode_attn_window(plan: Plan, layer: int, cache: PackedCache, win: WindowCache, q, seq_len,
                            max_len: int, scale: float, chunk: int = 0, out=None, logits=None, workspace=None,
                            stream=None):
+    _decode_sizes(plan, cache, q, seq_len, max_len, logits)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, q.numel(), "out")
     if workspace is None:
         nb = gtq_decode_window_workspace_bytes(plan, cache.batch, max_len, chunk)
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)

@@ -13,6 +13,9 @@ from oracle import gtq_oracle as O
 TOL_REL, TOL_ABS = 2e-3, 1e-4     # |gpu - ref| <= TOL_ABS + TOL_REL * |ref|
 TIE_WINDOW = 1e-6
 
+# running totals of what the parity checks compared (printed at the end of the session)
+STATS = {"attn_values": 0, "attn_checks": 0, "codes": 0, "code_ties": 0, "norms": 0, "norm_mismatches": 0}
+
 
 def assert_close(gpu, ref, what):
     gpu = np.asarray(gpu, np.float64)
@@ -20,6 +23,8 @@ def assert_close(gpu, ref, what):
     err = np.abs(gpu - ref)
     lim = TOL_ABS + TOL_REL * np.abs(ref)
     bad = ~(err <= lim)
+    STATS["attn_checks"] += 1
+    STATS["attn_values"] += int(err.size)
     if bad.any():
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at {tuple(i)}: "
@@ -128,6 +133,8 @@ def compare_codes(gpu_codes, ref_codes, ref_z, bits, what):
     mism = gpu_codes != ref_codes
     ties = tie_mask(ref_z, bits)
     hard = mism & ~ties
+    STATS["codes"] += int(mism.size)
+    STATS["code_ties"] += int((mism & ties).sum())
     if hard.any():
         i = tuple(np.argwhere(hard)[0])
         raise AssertionError(f"{what}: {hard.sum()} code mismatches outside the tie window; first at {i}: "
@@ -136,14 +143,19 @@ def compare_codes(gpu_codes, ref_codes, ref_z, bits, what):
 
 
 def compare_norms(gpu, ref, what):
-    """fp32 norms equal, or 1 ulp apart (fp64 summation order); returns ulp-off count."""
+    """Stored fp32 norms must equal the oracle's bit for bit (both sides accumulate in
+    fp64 and round once to fp32). Returns 0, the number of norms off (kept so that the
+    callers' summaries print it)."""
     gpu = np.asarray(gpu, np.float32)
     ref = np.asarray(ref, np.float32)
     d = np.abs(gpu.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
-    if (d > 1).any():
-        i = tuple(np.argwhere(d > 1)[0])
-        raise AssertionError(f"{what}: norm off by {d[i]} ulp at {i}: gpu={gpu[i]!r} ref={ref[i]!r}")
-    return int((d == 1).sum())
+    STATS["norms"] += int(d.size)
+    STATS["norm_mismatches"] += int((d > 0).sum())
+    if (d > 0).any():
+        i = tuple(np.argwhere(d > 0)[0])
+        raise AssertionError(f"{what}: {(d > 0).sum()} norms differ; first off by {d[i]} ulp at {i}: "
+                             f"gpu={gpu[i]!r} ref={ref[i]!r}")
+    return 0
 
 
 def scale_default():

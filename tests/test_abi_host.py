@@ -209,3 +209,39 @@ def test_plan_detects_hadamard_value_rotations():
     p = G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True)
     assert [p.layout(l, h)["v_hadamard"] for l in range(2) for h in range(2)] == [0, 1, 0, 0]
     p.destroy()
+
+
+def test_binding_rejects_undersized_tensors(lib):
+    """The binding checks every tensor's element count against the plan and cache before
+    a pointer reaches the library (CPU tensors: the size check comes before the device
+    check, so no GPU is needed and nothing is launched)."""
+    import torch
+    inp = head_inputs(0, 0, 0, 4, 8)
+    r, _, _ = G.gtq_alloc_rates(inp["calib_q"], inp["calib_k"], 1, 4, 128)
+    dims = G.gtq_head_layout_from_rates(r)["dim"]
+    kr, vr = head_rotations(0, 0, 0, dims)
+    H, g = 2, 4
+    plan = G.Plan(1, H, H * g, 128, 2, np.stack([r, r])[None], [[kr, kr]], np.stack([vr, vr])[None],
+                  host_only=True)
+    cache = G.PackedCache(plan, 3, 64, device="cpu")
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, dtype=dt)
+    cases = [
+        (lambda: G.gtq_decode_attn(plan, 0, cache, z(3, H * g - 1, 128), z(3, dt=torch.int32), 64, 0.1), "q"),
+        (lambda: G.gtq_decode_attn(plan, 0, cache, z(3, H * g, 128), z(2, dt=torch.int32), 64, 0.1), "seq_len"),
+        (lambda: G.gtq_decode_attn(plan, 0, cache, z(3, H * g, 128), z(3, dt=torch.int32), 64, 0.1,
+                                   logits=z(3, H * g, 63)), "logits"),
+        (lambda: G.gtq_decode_attn(plan, 0, cache, z(3, H * g, 128), z(3, dt=torch.int32), 64, 0.1,
+                                   out=z(3, H * g, 127)), "out"),
+        (lambda: G.gtq_quantize_append(plan, 0, cache, z(5, H, 128), z(5, H - 1, 128), z(5, dt=torch.int32),
+                                       z(5, dt=torch.int64)), "v"),
+        (lambda: G.gtq_quantize_append(plan, 0, cache, z(5, H, 128), z(5, H, 128), z(4, dt=torch.int32),
+                                       z(5, dt=torch.int64)), "seq_idx"),
+        (lambda: G.gtq_quantize_append_chunk(plan, 0, cache, z(5, H, 64), z(5, H, 128), 0, 0), "k"),
+        (lambda: G.gtq_decode_step(plan, 0, cache, z(3, H, 128), z(2, H, 128), z(3, H * g, 128),
+                                   z(3, dt=torch.int32), 64, 0.1), "v_new"),
+        (lambda: G.gtq_prefill_attn(plan, 0, cache, z(7, H * g + 1, 128), 0, 0, 0.1), "q"),
+    ]
+    for fn, name in cases:
+        with pytest.raises(ValueError, match=rf"^{name} holds"):
+            fn()
+    plan.destroy()

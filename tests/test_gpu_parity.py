@@ -1,10 +1,12 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Append: codes bit-exact except values whose oracle z lies within 1e-6 of a
-threshold (counted), fp32 norms equal or 1 ulp apart (counted). Attention:
-logits and outputs within 1e-4 + 2e-3 |ref| element-wise. Decode parity feeds the
-GPU the oracle's own packed cache (written into the library's layout), so that
-append tie cases cannot leak into it; the end-to-end tests run append then decode.
+threshold (counted and printed), fp32 norms bit-exact. Attention: logits and outputs
+within 1e-4 + 2e-3 |ref| element-wise. Decode-only tests feed the GPU the oracle's
+own packed cache (written into the library's layout). The end-to-end tests (append
+then decode) compare the decode with the oracle's decode over the records the GPU
+itself wrote, read back and converted to the canonical stream: every such comparison
+runs, whether or not the append produced tie codes.
 """
 import math
 import sys
@@ -101,6 +103,19 @@ def _oracle_decode(case, l, b, n, enc_by_head, q, scale):
     return lg, out
 
 
+def _records_from_gpu(case, cache, l, b, n):
+    """The packed records of sequence b, positions 0..n-1, as the GPU wrote them, in the
+    oracle's canonical form (key words, key norms per group, value words, value norms)."""
+    kc, kn, vc, vn = _cache_arrays(cache, case)
+    recs = []
+    for h in range(case.H):
+        ng = len(case.heads[l, h].groups)
+        vcodes = v_codes_from_physical(vc[b, h], n, case.v_bits)
+        recs.append(dict(k_words=kc[b, h, :n].copy(), k_norms=kn[b, h, :n, :ng].copy(),
+                         v_words=O.pack_codes([vcodes], [case.v_bits]), v_norms=vn[b, h, :n].copy()))
+    return recs
+
+
 def _encode(case, l, b, n):
     return [O.encode_kv(case.heads[l, h], case.inputs[l, h][b]["k"][:n], case.inputs[l, h][b]["v"][:n])
             for h in range(case.H)]
@@ -135,11 +150,12 @@ def test_config0_tiny_single_head(G):
                             logits=logits)
     torch.cuda.synchronize()
     for b in range(4):
-        lg_ref, out_ref = O.decode_attention(case.heads[0, 0], q[b], enc[0]["k_words"], enc[0]["k_norms"],
-                                             enc[0]["v_words"], enc[0]["v_norms"], sc)
-        if ties == 0:
-            assert_close(logits[b].cpu().numpy(), lg_ref, f"config0 logits q{b}")
-            assert_close(out[b].cpu().numpy(), out_ref, f"config0 out q{b}")
+        rec = _records_from_gpu(case, cache, 0, b, 1024)[0]
+        lg_ref, out_ref = O.decode_attention(case.heads[0, 0], q[b], rec["k_words"], rec["k_norms"],
+                                             rec["v_words"], rec["v_norms"], sc)
+        assert_close(logits[b].cpu().numpy(), lg_ref, f"config0 logits q{b}")
+        assert_close(out[b].cpu().numpy(), out_ref, f"config0 out q{b}")
+    _say(f"  config0: decode of 4 queries compared (append ties={ties})")
 
 
 @pytest.mark.parametrize("chunk", [32, 96, 512, 0])
@@ -212,10 +228,9 @@ def test_decode_step_fused(G, nc):
         enc = _encode(case, 0, b, n)
         t, _ = _check_append(case, cache, 0, b, n, enc, f"step b{b}")
         ties += t
-        if t == 0:
-            _, out_ref = _oracle_decode(case, 0, b, n, enc, q[b], sc)
-            assert_close(out[b].cpu().numpy(), out_ref, f"step out b{b}")
-    _say(f"  append ties={ties}")
+        _, out_ref = _oracle_decode(case, 0, b, n, _records_from_gpu(case, cache, 0, b, n), q[b], sc)
+        assert_close(out[b].cpu().numpy(), out_ref, f"step out b{b}")
+    _say(f"  append ties={ties}; decode of 3 sequences compared")
 
 
 @pytest.mark.parametrize("k_budget,v_bits,g,layout", [(128, 1, 8, 0), (192, 3, 8, 0), (160, 4, 2, 0),
@@ -276,20 +291,21 @@ def test_scatter_append_random_order_and_overflow(G):
         assert plan.overflow_count() - before == 3
         for b in range(2):
             ties, _ = _check_append(case, cache, l, b, n, _encode(case, l, b, n), f"scatter l{l} b{b}")
-            if ties == 0:
-                q = case.q(l, b)[None]
-                lens = np.array([n, n], np.int32)
-                out = G.gtq_decode_attn(plan, l, cache, _dev(np.concatenate([q, q])), _dev(lens), n,
+            q = case.q(l, b)[None]
+            lens = np.array([n, n], np.int32)
+            out = G.gtq_decode_attn(plan, l, cache, _dev(np.concatenate([q, q])), _dev(lens), n,
+                                    scale_default())
+            torch.cuda.synchronize()
+            _, out_ref = _oracle_decode(case, l, b, n, _records_from_gpu(case, cache, l, b, n), q[0],
                                         scale_default())
-                torch.cuda.synchronize()
-                _, out_ref = _oracle_decode(case, l, b, n, _encode(case, l, b, n), q[0], scale_default())
-                assert_close(out[b].cpu().numpy(), out_ref, f"end-to-end out l{l} b{b}")
+            assert_close(out[b].cpu().numpy(), out_ref, f"end-to-end out l{l} b{b}")
+            _say(f"  scatter l{l} b{b}: append ties={ties}; decode compared")
 
 
 def test_norm_corrected_append(G):
     """Norm-corrected stored norms through both append kernels (the tiled chunk kernel and
-    the per-token scatter kernel): codes as in the plain variant, norms within 1 ulp of
-    the oracle's corrected norms, and the decode over the corrected cache matching the
+    the per-token scatter kernel): codes as in the plain variant, norms bit-exact to the
+    oracle's corrected norms, and the decode over the corrected cache matching the
     oracle's."""
     _say("case: norm-corrected append (chunk + scatter)")
     n = 150
@@ -315,14 +331,13 @@ def test_norm_corrected_append(G):
             for gi in range(len(enc[h]["k_codes"])):
                 assert np.array_equal(enc[h]["k_codes"][gi], enc_plain[h]["k_codes"][gi])
             assert not np.array_equal(enc[h]["v_norms"], enc_plain[h]["v_norms"])
-        if ties == 0:
-            q = case.q(0, b)[None]
-            qq = np.concatenate([q, q])
-            out = G.gtq_decode_attn(plan, 0, cache, _dev(qq), _dev(np.array([n, n], np.int32)), n,
-                                    scale_default())
-            torch.cuda.synchronize()
-            _, out_ref = _oracle_decode(case, 0, b, n, enc, q[0], scale_default())
-            assert_close(out[b].cpu().numpy(), out_ref, f"{what} decode out")
+        q = case.q(0, b)[None]
+        qq = np.concatenate([q, q])
+        out = G.gtq_decode_attn(plan, 0, cache, _dev(qq), _dev(np.array([n, n], np.int32)), n,
+                                scale_default())
+        torch.cuda.synchronize()
+        _, out_ref = _oracle_decode(case, 0, b, n, _records_from_gpu(case, cache, 0, b, n), q[0], scale_default())
+        assert_close(out[b].cpu().numpy(), out_ref, f"{what} decode out")
 
 
 @pytest.mark.parametrize("T", [60, 61, 7])
@@ -352,7 +367,7 @@ def test_prefill_chunk(G, T):
     G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k[n0:]), _dev(v[n0:]), 0, n0)
     torch.cuda.synchronize()
     ties, _ = _check_append(case, cache, 0, 0, n0 + T, enc, "prefill-chunk append")
-    assert ties == 0 or ties < 3
+    _say(f"  prefill chunk append ties={ties}")
 
 
 def test_edge_cases(G):
@@ -591,9 +606,9 @@ def test_paged_cache(G):
     for b, n in enumerate(lens):
         enc = _encode(case, 0, b, n)
         t, _ = _check_append(case, cont, 0, b, n, enc, f"contiguous b{b}")
-        if t == 0:
-            _, ref = _oracle_decode(case, 0, b, n, enc, q[b], sc)
-            assert_close(o_p[b].cpu().numpy(), ref, f"paged step out b{b}")
+        _, ref = _oracle_decode(case, 0, b, n, _records_from_gpu(case, cont, 0, b, n), q[b], sc)
+        assert_close(o_p[b].cpu().numpy(), ref, f"paged step out b{b}")
+        _say(f"  paged b{b}: append ties={t}; step output compared")
     # window decode and prefill over the paged cache equal the contiguous ones
     win = G.WindowCache(plan, 2, 4, 64)
     for b, n in enumerate(lens):
@@ -639,10 +654,9 @@ def test_hadamard_value_rotation(G, chunk):
     for b, n in enumerate(lens):
         enc = _encode(case, 0, b, n)
         ties, ulps = _check_append(case, cache, 0, b, n, enc, f"hadamard b{b}")
-        _say(f"  b{b}: ties={ties} norm-ulps={ulps}")
-        if ties == 0:
-            _, ref = _oracle_decode(case, 0, b, n, enc, q[b], sc)
-            assert_close(out[b].cpu().numpy(), ref, f"hadamard out b{b}")
+        _say(f"  b{b}: ties={ties} norm-ulps={ulps}; decode compared")
+        _, ref = _oracle_decode(case, 0, b, n, _records_from_gpu(case, cache, 0, b, n), q[b], sc)
+        assert_close(out[b].cpu().numpy(), ref, f"hadamard out b{b}")
     plan.destroy()
 
 
