@@ -1,23 +1,32 @@
 """Benchmark: packed-KV decode attention over a Block-GTQ (mixed-rate TQ-MSE) cache.
 
-One step = one decode step of one Llama-3.1-8B-shaped attention layer at batch 1:
-quantize-append the step's new key/value token (8 KV heads) into the packed cache,
-then split-K packed decode attention of the 32 query heads over the 32768 cached
-tokens: one launch appends the token and rotates the queries, one computes the
-per-split online-softmax partials, one does the log-sum-exp merge with the inverse
-value rotation. Inputs are seeded synthetic tensors with the pages' distributions,
-resident in HBM before timing. The cache is replicated into --copies layer caches
-that the steps cycle through (as a 32-layer stack would), so that each step reads
-its cache from HBM rather than from the 256 MB last-level cache.
+Default workload (the headline): one decode step of a Llama-3-70B-shaped model on one
+GPU: 80 layers, 64 query / 8 KV heads, head_dim 128, batch 32 sequences with ragged
+lengths uniform in [8192, 16384], K2V2 packed cache (about 28 GB resident). A step runs,
+for every layer, the three launches of gtq_decode_step: prepare (append each sequence's
+new token into the packed cache + rotate the queries), split-K packed decode partials,
+log-sum-exp merge with the inverse value rotation. The 80 layers are captured in one
+HIP graph; the graph is replayed --steps times after --warmup replays.
 
-Prints one JSON line (metric, value = KV tokens/s, roofline of the attention
-(partials) kernel measured with HIP events around each of its launches in the timed
-region, cpu_baseline = the
-fp64 oracle timed on a bounded slice of the same workload on this host).
+Inputs are seeded synthetic tensors with the pages' distributions, resident in HBM
+before timing. The 80 layer caches are copies of one generated layer (same rates and
+rotations; every layer reads its own copy from HBM).
+
+Prints one JSON line: value = KV tokens/s (layers x cached positions attended per
+second), roofline = the split-K partials kernel (algorithmic bytes of one launch, i.e.
+the packed records of every attended (token, KV head), over its average duration,
+measured with HIP events around a graph of back-to-back partials launches on the same
+stream), cpu_baseline = the fp64 CPU oracle timed on a bounded slice of the same
+workload on this host (all BLAS threads, and one thread).
+
+Other workloads (--workload NAME) print one line each: decode-8b (Llama-3.1-8B layer,
+batch 1, 32768 tokens, K2V2), decode-3b-36L (Qwen2.5-3B, 36 layers, batch 1, 131072
+tokens, K3V3), append-32b, prefill-32b, logit-mae, decode-8b-window.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -30,6 +39,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0   # dense fp16 MFMA
+METRIC = "packed-KV decode attention: KV tokens/s + achieved HBM GB/s (% of peak)"
+KERNEL_SRC = os.path.join(ROOT, "packed_cache_attention_tq_amd", "csrc", "gtq_device.hip")
 
 
 def log(*a):
@@ -39,17 +51,17 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--copies", type=int, default=32, help="layer caches the steps cycle through")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--chunk", type=int, default=0, help="split size (0 = automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="CPU time of each oracle leg (all threads, one thread)")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--workload", default="decode-8b",
-                   choices=["decode-8b", "decode-3b-36L", "decode-70b-b32", "append-32b", "prefill-32b",
-                            "logit-mae", "decode-8b-window"],
-                   help="decode-8b (default, the headline): Llama-3.1-8B-shaped layer decode; the others "
-                        "measure the other workload shapes (one JSON line each)")
+    p.add_argument("--workload", default="decode-70b-b32",
+                   choices=["decode-70b-b32", "decode-8b", "decode-3b-36L", "append-32b", "prefill-32b",
+                            "logit-mae", "decode-8b-window"])
+    p.add_argument("--copies", type=int, default=32, help="decode-8b: layer caches the steps cycle through")
     p.add_argument("--norm-correct", action="store_true",
                    help="append-32b: plan with norm-corrected stored norms (GTQ_PLAN_NORM_CORRECT)")
     p.add_argument("--paged", type=int, default=0,
@@ -62,16 +74,15 @@ def parse():
     return p.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_partials_k2v2_32k_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "packed_cache_attention_tq_amd", "csrc", "gtq_device.hip")
+# ---------------------------------------------------------------- measured traffic
 
-
-def measured_traffic():
-    """HBM bytes per launch of the attention (partials) kernel from the committed counter
-    summary, or None when the kernel source has changed since the counters were taken."""
-    import hashlib
+def measured_traffic(name):
+    """Calibrated HBM bytes per launch of a workload's dominant kernel from its committed
+    counter summary profiles/<name>_traffic.txt, or None when the kernel source has
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
     try:
-        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE).read().splitlines()
+        kv = dict(line.split(":", 1) for line in open(path).read().splitlines()
                   if ":" in line and not line.startswith("#"))
         sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
         if kv["kernel_source_sha256"].strip() != sha:
@@ -81,41 +92,19 @@ def measured_traffic():
         return None
 
 
-def build_workload(seed, n_ctx=32768, h_kv=8, g=4, k_budget=128, v_bits=2, v_hadamard=False):
-    import torch
-
-    import packed_cache_attention_tq_amd as G
-    from gtq_inputs import head_inputs, head_rotations
-
-    rates = np.zeros((1, h_kv, 64), np.uint8)
-    krot, vrot, inps = [[]], [[]], []
-    for h in range(h_kv):
-        inp = head_inputs(seed, 0, h, g, n_ctx)   # the last token is the step's new token
-        r, _, _ = G.gtq_alloc_rates(inp["calib_q"], inp["calib_k"], 1, 4, k_budget)
-        rates[0, h] = r
-        lay = G.gtq_head_layout_from_rates(r)
-        kr, vr = head_rotations(seed, 0, h, lay["dim"], v_hadamard=v_hadamard)
-        krot[0].append(kr)
-        vrot[0].append(vr)
-        inps.append(inp)
-    plan = G.Plan(1, h_kv, h_kv * g, k_budget, v_bits, rates, krot, np.array(vrot))
-    k = np.stack([i["k"] for i in inps], axis=1)          # [n_ctx+1, H, 128]
-    v = np.stack([i["v"] for i in inps], axis=1)
-    q = np.concatenate([i["q"][0] for i in inps])[None]   # [1, 32, 128]
-    return dict(plan=plan, k=k, v=v, q=q, rates=rates, krot=krot, vrot=vrot, inps=inps,
-                n_ctx=n_ctx, h_kv=h_kv, g=g, k_budget=k_budget, v_bits=v_bits)
+def hbm_roofline(kernel, alg_bytes, avg_ms, traffic_name, extra=None):
+    achieved = alg_bytes / (avg_ms / 1e3) / 1e9
+    r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(traffic_name),
+         "kernel": kernel, "kernel_avg_us": round(avg_ms * 1e3, 3), "alg_bytes_per_launch": int(alg_bytes)}
+    if extra:
+        r.update(extra)
+    return r
 
 
-def partials_kernel_name(plan, layer, h_kv, v_bits):
-    """The partials kernel instance a decode of this layer launches: value bits, key words
-    per lane (4 up to 8 key words, else 8) and the layer's largest K-block count."""
-    lays = [plan.layout(layer, h) for h in range(h_kv)]
-    nkb = max(sum((d + 31) // 32 for d in lay["dim"]) for lay in lays)
-    kwl = 4 if lays[0]["k_words"] <= 8 else 8
-    return f"attn_partials_kernel<{v_bits}, {kwl}, {nkb}>"
+# ---------------------------------------------------------------- plans and caches
 
-
-def make_plan(seed, n_layers, h_kv, g, k_budget, v_bits, share_layer0=False, nc=False):
+def make_plan(seed, n_layers, h_kv, g, k_budget, v_bits, share_layer0=False, nc=False, v_hadamard=False):
     """A plan with library-allocated rates (from each head's calibration set) and Haar
     rotations; with share_layer0 every layer reuses layer 0's rates and rotations."""
     import packed_cache_attention_tq_amd as G
@@ -134,12 +123,13 @@ def make_plan(seed, n_layers, h_kv, g, k_budget, v_bits, share_layer0=False, nc=
             inp = head_inputs(seed, l, h, g, 0)
             r, _, _ = G.gtq_alloc_rates(inp["calib_q"], inp["calib_k"], 1, 4, k_budget)
             rates[l, h] = r
-            kr, vr = head_rotations(seed, l, h, G.gtq_head_layout_from_rates(r)["dim"])
+            kr, vr = head_rotations(seed, l, h, G.gtq_head_layout_from_rates(r)["dim"], v_hadamard=v_hadamard)
             kl.append(kr)
             vl.append(vr)
         krot.append(kl)
         vrot.append(vl)
-    return G.Plan(n_layers, h_kv, h_kv * g, k_budget, v_bits, rates, krot, np.array(vrot), norm_correct=nc)
+    plan = G.Plan(n_layers, h_kv, h_kv * g, k_budget, v_bits, rates, krot, np.array(vrot), norm_correct=nc)
+    return plan, rates, krot, vrot
 
 
 def fill_layer(plan, layer, cache, seed, h_kv, g, lengths, gen_layer=None):
@@ -172,9 +162,9 @@ def fill_layer(plan, layer, cache, seed, h_kv, g, lengths, gen_layer=None):
     return knew, vnew, q
 
 
-def timed_graph(fn, steps, warmup):
-    """Capture fn (one step of kernel launches on the current stream) in a HIP graph,
-    replay it warmup + steps times; returns ms per step."""
+def graph_ms(fn, reps, warmup, per=1):
+    """Capture fn (kernel launches on the current stream) in a HIP graph, replay it
+    warmup + reps times; returns ms per replay / per (HIP events around the replays)."""
     import torch
 
     s = torch.cuda.Stream()
@@ -189,75 +179,214 @@ def timed_graph(fn, steps, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
+    t0.record(stream)
+    for _ in range(reps):
         g.replay()
-    t1.record()
+    t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    ms = t0.elapsed_time(t1) / reps / per
+    del g
+    return ms
 
 
-def bench_decode_stack(args, name):
-    """Multi-layer decode steps as one HIP graph per step: decode-3b-36L (Qwen2.5-3B shape:
-    36 layers, 16 query / 2 KV heads, batch 1, 131072 tokens, K3V3) or decode-70b-b32
-    (Llama-3-70B shape: 80 layers, 64 query / 8 KV heads, batch 32 with ragged lengths
-    uniform in [8192, 16384], K2V2; the 80 layer caches hold copies of one generated layer
-    and every layer uses that layer's rates and rotations)."""
+def partials_kernel_name(plan, layer, h_kv, v_bits):
+    """The partials kernel instance a decode of this layer launches: value bits, key words
+    per lane (4 up to 8 key words, else 8) and the layer's largest K-block count."""
+    lays = [plan.layout(layer, h) for h in range(h_kv)]
+    nkb = max(sum((d + 31) // 32 for d in lay["dim"]) for lay in lays)
+    kwl = 4 if lays[0]["k_words"] <= 8 else 8
+    return f"attn_partials_kernel<{v_bits}, {kwl}, {nkb}, 8, false>"
+
+
+# ---------------------------------------------------------------- decode workloads
+
+DECODE = {
+    # name: layers, KV heads, g, key budget, value bits, lengths, shared layer plan, cache copies
+    "decode-70b-b32": dict(L=80, h_kv=8, g=8, kb=128, vb=2, batch=32, lens=(8192, 16384), share=True,
+                           desc="Llama-3-70B-shaped decode step: 80 layers, 64 query / 8 KV heads, head_dim 128, "
+                                "batch 32, ragged lengths U[8192, 16384], K2V2 packed cache"),
+    "decode-3b-36L": dict(L=36, h_kv=2, g=8, kb=192, vb=3, batch=1, lens=131072, share=False,
+                          desc="Qwen2.5-3B-shaped decode step: 36 layers, 16 query / 2 KV heads, head_dim 128, "
+                               "batch 1, 131072 cached tokens per layer, K3V3 packed cache"),
+    "decode-8b": dict(L=1, h_kv=8, g=4, kb=128, vb=2, batch=1, lens=32768, share=False,
+                      desc="Llama-3.1-8B-shaped layer decode: 32 query / 8 KV heads, head_dim 128, batch 1, "
+                           "32768 cached tokens, K2V2 packed cache"),
+}
+
+
+def bench_decode(args, name):
     import torch
 
     import packed_cache_attention_tq_amd as G
     from gtq_inputs import ragged_lengths
 
-    if name == "decode-3b-36L":
-        L, h_kv, g, kb, vb, lengths, share = 36, 2, 8, 192, 3, np.array([131072]), False
+    c = DECODE[name]
+    L, h_kv, g, kb, vb = c["L"], c["h_kv"], c["g"], c["kb"], c["vb"]
+    if isinstance(c["lens"], tuple):
+        lengths = ragged_lengths(args.seed, c["batch"], *c["lens"])
     else:
-        L, h_kv, g, kb, vb, share = 80, 8, 8, 128, 2, True
-        lengths = ragged_lengths(args.seed, 32, 8192, 16384)
-    B, cap = len(lengths), int((lengths.max() + 31) // 32 * 32)
+        lengths = np.full(c["batch"], c["lens"], np.int32)
+    B = len(lengths)
+    cap = int((lengths.max() + 31) // 32 * 32)
     t_setup = time.perf_counter()
-    plan = make_plan(args.seed, L, h_kv, g, kb, vb, share_layer0=share)
-    caches, steps_in = [], []
-    for l in range(L):
-        if share and l > 0:
+    plan, rates, krot, vrot = make_plan(args.seed, L, h_kv, g, kb, vb, share_layer0=c["share"],
+                                        v_hadamard=args.v_hadamard)
+    # cache entries: one per layer; the single-layer shape cycles through --copies copies of
+    # its layer (a step is one layer-step, the graph holds one step per copy)
+    n_ent = L if L > 1 else args.copies
+    caches, step_in = [], []
+    for i in range(n_ent):
+        li = i if L > 1 else 0
+        if i > 0 and (c["share"] or L == 1):
             caches.append(caches[0].clone())
-            steps_in.append(steps_in[0])
+            step_in.append(step_in[0])
             continue
-        c = G.PackedCache(plan, B, cap)
-        steps_in.append(fill_layer(plan, l, c, args.seed, h_kv, g, lengths))
-        caches.append(c)
+        if args.paged and L == 1:
+            n_pages = (cap + args.paged - 1) // args.paged
+            cc = G.PagedCache(plan, B, n_pages * B, args.paged, n_pages)
+            perm = np.random.default_rng(args.seed).permutation(n_pages * B).astype(np.int32).reshape(B, n_pages)
+            cc.block_table.copy_(torch.from_numpy(perm))
+        else:
+            cc = G.PackedCache(plan, B, cap)
+        step_in.append(fill_layer(plan, li, cc, args.seed, h_kv, g, lengths))
+        caches.append(cc)
     torch.cuda.synchronize()
     sl = torch.tensor(lengths, dtype=torch.int32, device="cuda")
     max_len = int(lengths.max())
-    ws = [torch.empty(G.gtq_decode_workspace_bytes(plan, B, max_len, 0), dtype=torch.uint8, device="cuda")
-          for _ in range(2)]
-    outs = [torch.empty(B, h_kv * g, 128, device="cuda") for _ in range(L)]
+    wsb = G.gtq_decode_workspace_bytes(plan, B, max_len, args.chunk)
+    ws = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(n_ent)]
+    outs = [torch.empty(B, h_kv * g, 128, device="cuda") for _ in range(n_ent)]
     scale = 1.0 / math.sqrt(128)
-    log(f"{name}: setup {time.perf_counter() - t_setup:.1f}s, {L} layers, cache "
-        f"{sum(c.nbytes() for c in caches) / 1e9:.2f} GB")
+    log(f"{name}: setup {time.perf_counter() - t_setup:.1f}s, {n_ent} cache entries, "
+        f"{sum(x.nbytes() for x in caches) / 1e9:.2f} GB")
+
+    def layer_of(i):
+        return i if L > 1 else 0
 
     def step():
-        for l in range(L):
-            kn, vn, q = steps_in[l]
-            G.gtq_decode_step(plan, l, caches[l], kn, vn, q, sl, max_len, scale,
-                              out=outs[l], workspace=ws[l & 1])
+        for i in range(n_ent):
+            kn, vn, q = step_in[i]
+            G.gtq_decode_step(plan, layer_of(i), caches[i], kn, vn, q, sl, max_len, scale, chunk=args.chunk,
+                              out=outs[i], workspace=ws[i])
 
-    ms = timed_graph(step, args.steps, args.warmup)
-    kv_tok = L * int(lengths.sum())
-    sizes = caches[0].sizes
-    alg = L * (int(lengths.sum()) * h_kv * sizes.bytes_per_token)
-    return {
-        "metric": "packed-KV decode attention: KV tokens/s + achieved HBM GB/s (% of peak)",
-        "value": round(kv_tok / (ms / 1e3), 1), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 (fp16 hi/lo split MFMA operands, fp32 accumulation; u32 packed codes)",
+    def partials_only():
+        for i in range(n_ent):
+            G.gtq_decode_attn_partials(plan, layer_of(i), caches[i], sl, max_len, ws[i], chunk=args.chunk)
+
+    per_step = n_ent if L == 1 else 1            # graph replays hold this many model steps
+    ms = graph_ms(step, args.steps, args.warmup, per=per_step)
+    part_ms = graph_ms(partials_only, args.steps, min(args.warmup, 2), per=n_ent)
+    tok_per_step = (L if L > 1 else 1) * int(lengths.sum())
+    bpt = caches[0].sizes.bytes_per_token
+    alg_launch = int(lengths.sum()) * h_kv * bpt      # packed records one partials launch reads
+    step_alg = (L if L > 1 else 1) * alg_launch
+    res = {
+        "metric": METRIC, "value": round(tok_per_step / (ms / 1e3), 1), "unit": "KV tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32 packed codes; f16 hi/lo MFMA operands, f32 accumulation",
         "data": "synthetic",
-        "config": {"workload": name, "layers": L, "global_batch": B, "kv_heads": h_kv, "q_heads": h_kv * g,
-                   "seq_len": [int(lengths.min()), int(lengths.max())], "k_bits_avg": kb / 64, "v_bits": vb,
-                   "graph": "one HIP graph per step (append + rotate, partials, merge per layer)"},
-        "step_hbm_gbs": round(alg / (ms / 1e3) / 1e9, 1), "step_hbm_frac": round(alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        "config": {"workload": c["desc"], "layers": L, "global_batch": B, "q_heads": h_kv * g, "kv_heads": h_kv,
+                   "head_dim": 128, "seq_len": [int(lengths.min()), int(lengths.max())],
+                   "k_bits_avg": kb / 64, "v_bits": vb, "parallelism": "none (1 GPU)",
+                   "step": "one HIP graph: per layer prepare (token append + query rotation), partials, merge",
+                   **({"cache_copies": n_ent} if L == 1 else {}),
+                   **({"page_tokens": args.paged} if args.paged else {}),
+                   **({"v_rotation": "randomized Hadamard"} if args.v_hadamard else {})},
+        "roofline": hbm_roofline(partials_kernel_name(plan, 0, h_kv, vb), alg_launch, part_ms, name,
+                                 {"timing": "HIP events around a graph of back-to-back partials launches"}),
+        "step_hbm_gbs": round(step_alg / (ms / 1e3) / 1e9, 1),
+        "step_hbm_frac": round(step_alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
     }
+    if args.calib_copy_mib > 0:
+        calib_copy(args.calib_copy_mib)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded slice ...")
+        res["cpu_baseline"] = cpu_baseline_decode(args, c, lengths, rates, krot, vrot)
+    return res
 
+
+def calib_copy(mib):
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- CPU oracle baselines
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _two_legs(run_leg, seconds):
+    """run_leg(seconds) -> (units, elapsed, detail) with all BLAS threads, then one."""
+    from threadpoolctl import threadpool_limits
+    out = {}
+    u, t, det = run_leg(seconds)
+    out["all"] = (u / t, _blas_threads(), det, t)
+    with threadpool_limits(1):
+        u, t, det = run_leg(seconds)
+        out["one"] = (u / t, 1, det, t)
+    return out
+
+
+def cpu_baseline_decode(args, c, lengths, rates, krot, vrot):
+    """The fp64 oracle on slices of one (layer, sequence, KV head): the step's one-token
+    encode plus the decode of the KV head's g query heads over the sequence's cached
+    tokens, repeated over sequences (and heads) until `seconds` of CPU time. KV tokens/s
+    = attended positions / (KV heads x time), since a KV token holds all KV heads."""
+    from gtq_inputs import head_inputs
+    from oracle import gtq_oracle as O
+
+    h_kv, g, vb = c["h_kv"], c["g"], c["vb"]
+    scale = 1 / math.sqrt(128)
+    order = [(b % len(lengths), (b // len(lengths) + b) % h_kv) for b in range(128)]
+    prepared = {}
+
+    def slice_inputs(b, h):        # generation and the cache's encode are setup (untimed, shared by the legs)
+        if (b, h) not in prepared:
+            n = int(lengths[b])
+            inp = head_inputs(args.seed, 0, h, g, n, seq=b)
+            hp = O.HeadPlan(rates[0, h], krot[0][h], vrot[0][h], vb)
+            prepared[b, h] = (n, inp, hp, O.encode_kv(hp, inp["k"][: n - 1], inp["v"][: n - 1]))
+        return prepared[b, h]
+
+    def leg(seconds):
+        done, t_total, slices = 0, 0.0, 0
+        for b, h in order:
+            n, inp, hp, enc = slice_inputs(b, h)
+            t0 = time.perf_counter()
+            new = O.encode_kv(hp, inp["k"][n - 1: n], inp["v"][n - 1: n])
+            O.decode_attention(hp, inp["q"][0], np.concatenate([enc["k_words"], new["k_words"]]),
+                               np.concatenate([enc["k_norms"], new["k_norms"]]),
+                               np.concatenate([enc["v_words"], new["v_words"]]),
+                               np.concatenate([enc["v_norms"], new["v_norms"]]), scale)
+            t_total += time.perf_counter() - t0
+            done += n
+            slices += 1
+            if t_total >= seconds:
+                break
+        return done / h_kv, t_total, f"{slices} slice(s) of 1 layer x 1 sequence x 1 KV head ({g} query heads)"
+
+    legs = _two_legs(leg, args.cpu_seconds)
+    v, cores, det, t = legs["all"]
+    v1, _, det1, t1 = legs["one"]
+    return {"value": round(v, 1), "unit": "KV tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{det}, encode of the step's token + decode, {t:.1f} s; extrapolated to the step by "
+                      f"rate (the work is linear in tokens and heads)",
+            "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round(v1, 1), "cores": 1, "sample": f"{det1}, {t1:.1f} s"}}
+
+
+# ---------------------------------------------------------------- append / prefill
 
 def bench_append(args):
     """append-32b: Qwen2.5-32B-shaped chunk append, 4096-token chunks x 8 KV heads, K3V2,
@@ -268,37 +397,65 @@ def bench_append(args):
     from gtq_inputs import head_inputs_device
 
     h_kv, g, kb, vb, chunk, total = 8, 5, 192, 2, 4096, 65536
-    plan = make_plan(args.seed, 1, h_kv, g, kb, vb, nc=args.norm_correct)
+    plan, rates, krot, vrot = make_plan(args.seed, 1, h_kv, g, kb, vb, nc=args.norm_correct)
     cache = G.PackedCache(plan, 1, total)
     ks = torch.stack([head_inputs_device(args.seed, 0, h, g, total, "cuda", with_q=False)["k"] for h in range(h_kv)], 1)
     vs = torch.stack([head_inputs_device(args.seed, 0, h, g, total, "cuda", with_q=False)["v"] for h in range(h_kv)], 1)
     chunks = [(ks[m * chunk:(m + 1) * chunk].contiguous(), vs[m * chunk:(m + 1) * chunk].contiguous())
               for m in range(total // chunk)]
-    for m, (k, v) in enumerate(chunks):
-        G.gtq_quantize_append_chunk(plan, 0, cache, k, v, 0, m * chunk)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_steps = max(args.steps, 16)
-    t0.record()
-    for i in range(n_steps):
-        m = i % len(chunks)
-        G.gtq_quantize_append_chunk(plan, 0, cache, chunks[m][0], chunks[m][1], 0, m * chunk)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / n_steps
+
+    def run():
+        for m, (k, v) in enumerate(chunks):
+            G.gtq_quantize_append_chunk(plan, 0, cache, k, v, 0, m * chunk)
+
+    ms = graph_ms(run, max(1, args.steps // 4), 1, per=len(chunks))
     per_tok = 2 * 128 * 4 + cache.sizes.bytes_per_token  # fp32 key + value in, packed record out
     alg = chunk * h_kv * per_tok
-    return {
+    res = {
         "metric": "fused rotate+quantize+pack append: tokens/s + achieved HBM GB/s (% of peak)",
-        "value": round(chunk / (ms / 1e3), 1), "unit": "tokens/s (x 8 KV heads)", "n_gpus": 1, "steps": n_steps,
-        "warmup": 16, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 in; binary16 hi/lo split MFMA; u32 packed codes", "data": "synthetic",
-        "config": {"workload": "append-32b", "chunk_tokens": chunk, "kv_heads": h_kv, "k_bits_avg": kb / 64,
-                   "v_bits": vb, "prompt": total, "norm_correct": bool(args.norm_correct)},
-        "roofline": {"bound": "hbm", "achieved": round(alg / (ms / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "append_gemm_kernel", "alg_bytes_per_launch": int(alg)},
+        "value": round(chunk / (ms / 1e3), 1), "unit": "tokens/s (x 8 KV heads)", "n_gpus": 1,
+        "steps": max(1, args.steps // 4) * len(chunks), "warmup": len(chunks), "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 in; f16 hi/lo split MFMA rotation; u32 packed codes", "data": "synthetic",
+        "config": {"workload": "Qwen2.5-32B-shaped prompt append: 4096-token chunk x 8 KV heads, K3V2 "
+                               "(the 16 chunks of a 65536-token prompt in turn)",
+                   "chunk_tokens": chunk, "kv_heads": h_kv, "k_bits_avg": kb / 64, "v_bits": vb, "prompt": total,
+                   "norm_correct": bool(args.norm_correct)},
+        "roofline": hbm_roofline("append_gemm_kernel", alg, ms, "append-32b",
+                                 {"timing": "HIP events around a graph of the 16 chunk launches"}),
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_append(args, rates, krot, vrot, kb, vb, chunk, h_kv, g)
+    return res
+
+
+def cpu_baseline_append(args, rates, krot, vrot, kb, vb, chunk, h_kv, g):
+    """The oracle's encode + pack of one chunk of one KV head, repeated over heads until
+    `seconds`; tokens/s of the whole 8-head chunk = tokens / (heads x time)."""
+    from gtq_inputs import head_inputs
+    from oracle import gtq_oracle as O
+
+    def leg(seconds):
+        done, t_total, n_sl = 0, 0.0, 0
+        for i in range(64):
+            h = i % h_kv
+            inp = head_inputs(args.seed, 0, h, g, chunk)
+            hp = O.HeadPlan(rates[0, h], krot[0][h], vrot[0][h], vb, nc=args.norm_correct)
+            t0 = time.perf_counter()
+            O.encode_kv(hp, inp["k"], inp["v"])
+            t_total += time.perf_counter() - t0
+            done += chunk
+            n_sl += 1
+            if t_total >= seconds:
+                break
+        return done / h_kv, t_total, f"{n_sl} chunk(s) of {chunk} tokens x 1 KV head"
+
+    legs = _two_legs(leg, args.cpu_seconds)
+    v, cores, det, t = legs["all"]
+    v1, _, det1, t1 = legs["one"]
+    return {"value": round(v, 1), "unit": "tokens/s (x 8 KV heads)", "cores": int(cores), "kind": "oracle",
+            "sample": f"{det}, {t:.1f} s", "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round(v1, 1), "cores": 1, "sample": f"{det1}, {t1:.1f} s"}}
 
 
 def bench_prefill(args):
@@ -313,7 +470,7 @@ def bench_prefill(args):
 
     h_kv, g, kb, vb, chunk, total = 8, 5, 192, 2, 4096, 65536
     pos0 = total - chunk
-    plan = make_plan(args.seed, 1, h_kv, g, kb, vb)
+    plan, rates, krot, vrot = make_plan(args.seed, 1, h_kv, g, kb, vb)
     cache = G.PackedCache(plan, 1, total)
     qpos = torch.arange(pos0, total, device="cuda")
     ds = [head_inputs_device(args.seed, 0, h, g, total, "cuda", n_q_tok=chunk, q_positions=qpos) for h in range(h_kv)]
@@ -337,15 +494,61 @@ def bench_prefill(args):
     ms = t0.elapsed_time(t1) / n_steps
     pairs = sum(pos0 + t + 1 for t in range(chunk)) * h_kv * g
     flop = 4.0 * 128 * pairs
-    return {
+    tf = flop / (ms / 1e3) / 1e12
+    res = {
         "metric": "chunked prefill attention over the packed cache: TFLOP/s",
-        "value": round(flop / (ms / 1e3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": n_steps,
+        "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": n_steps,
         "warmup": 1, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 (fp16 hi/lo split MFMA operands, fp32 accumulation)", "data": "synthetic",
-        "config": {"workload": "prefill-32b", "chunk": chunk, "pos0": pos0, "q_heads": h_kv * g, "kv_heads": h_kv,
-                   "k_bits_avg": kb / 64, "v_bits": vb},
+        "vs_baseline": None, "dtype": "f16 hi/lo split MFMA operands, f32 accumulation", "data": "synthetic",
+        "config": {"workload": "Qwen2.5-32B-shaped chunked prefill: the last 4096-token chunk of a 65536-token "
+                               "prompt, 40 query / 8 KV heads, K3V2", "chunk": chunk, "pos0": pos0,
+                   "q_heads": h_kv * g, "kv_heads": h_kv, "k_bits_avg": kb / 64, "v_bits": vb},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "kernel": "gtq_prefill_attn (query rotation, partials, merge)",
+                     "alg_flop_per_call": flop, "note": "algorithmic flop: 4 x 128 per visible (query, key) pair and "
+                                                        "query head; the split operands execute twice that"},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(args, rates, krot, vrot, vb, g, pos0, chunk)
+    return res
 
+
+def cpu_baseline_prefill(args, rates, krot, vrot, vb, g, pos0, chunk):
+    """The oracle's causal attention of a few query tokens of the chunk (one KV head, its g
+    query heads) over the packed cache; TFLOP/s of the attention products."""
+    from gtq_inputs import head_inputs
+    from oracle import gtq_oracle as O
+
+    total = pos0 + chunk
+    inp = head_inputs(args.seed, 0, 0, g, total)
+    hp = O.HeadPlan(rates[0, 0], krot[0][0], vrot[0][0], vb)
+    enc = O.encode_kv(hp, inp["k"], inp["v"])
+    q = np.random.default_rng(args.seed).standard_normal((chunk, g, 128)).astype(np.float32)
+
+    def leg(seconds):
+        fl, t_total, n = 0.0, 0.0, 0
+        for t in range(chunk):
+            p = pos0 + t
+            t0 = time.perf_counter()
+            O.decode_attention(hp, q[t], enc["k_words"], enc["k_norms"], enc["v_words"], enc["v_norms"],
+                               1 / math.sqrt(128), length=p + 1)
+            t_total += time.perf_counter() - t0
+            fl += 4.0 * 128 * (p + 1) * g
+            n += 1
+            if t_total >= seconds:
+                break
+        return fl / 1e12, t_total, f"{n} query token(s) x {g} query heads of one KV head over ~{total} positions"
+
+    legs = _two_legs(leg, args.cpu_seconds)
+    v, cores, det, t = legs["all"]
+    v1, _, det1, t1 = legs["one"]
+    return {"value": round(v, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{det}, {t:.1f} s", "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round(v1, 6), "cores": 1, "sample": f"{det1}, {t1:.1f} s"}}
+
+
+# ---------------------------------------------------------------- diagnostics
 
 def bench_logit_mae(args):
     """K-only logit error of Block-GTQ (greedy per-block rates) against uniform TQ-MSE
@@ -412,12 +615,14 @@ def bench_window(args, n_sink=4, n_recent=128):
     import torch
 
     import packed_cache_attention_tq_amd as G
+    from gtq_inputs import head_inputs, head_rotations
 
-    w = build_workload(args.seed)
-    plan, n, h_kv, g = w["plan"], w["n_ctx"], w["h_kv"], w["g"]
+    h_kv, g, n, kb, vb = 8, 4, 32768, 128, 2
+    plan, rates, krot, vrot = make_plan(args.seed, 1, h_kv, g, kb, vb)
     dev = torch.device("cuda")
-    k_all = torch.from_numpy(w["k"]).to(dev)
-    v_all = torch.from_numpy(w["v"]).to(dev)
+    inps = [head_inputs(args.seed, 0, h, g, n) for h in range(h_kv)]
+    k_all = torch.from_numpy(np.stack([i["k"] for i in inps], axis=1)).to(dev)
+    v_all = torch.from_numpy(np.stack([i["v"] for i in inps], axis=1)).to(dev)
     base = G.PackedCache(plan, 1, n)
     G.gtq_quantize_append_chunk(plan, 0, base, k_all[: n - 1].contiguous(), v_all[: n - 1].contiguous(), 0, 0)
     win = G.WindowCache(plan, 1, n_sink, n_recent)
@@ -426,81 +631,34 @@ def bench_window(args, n_sink=4, n_recent=128):
                         torch.zeros(len(pos), dtype=torch.int32, device=dev), pos.to(torch.int64))
     caches = [base] + [base.clone() for _ in range(args.copies - 1)]
     k_new, v_new = k_all[n - 1: n].contiguous(), v_all[n - 1: n].contiguous()
-    q = torch.from_numpy(w["q"]).to(dev)
+    q = torch.from_numpy(np.concatenate([i["q"][0] for i in inps])[None]).to(dev)
     seq_len = torch.full((1,), n, dtype=torch.int32, device=dev)
     sidx = torch.zeros(1, dtype=torch.int32, device=dev)
     slot = torch.full((1,), n - 1, dtype=torch.int64, device=dev)
     out = torch.empty_like(q)
     ws = torch.empty(G.gtq_decode_window_workspace_bytes(plan, 1, n, args.chunk), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(128)
-    stream = torch.cuda.current_stream()
 
-    def step(i):
-        c = caches[i % len(caches)]
-        G.gtq_quantize_append(plan, 0, c, k_new, v_new, sidx, slot, stream=stream)
-        G.gtq_window_append(plan, 0, win, k_new, v_new, sidx, slot, stream=stream)
-        G.gtq_decode_attn_window(plan, 0, c, win, q, seq_len, n, scale, chunk=args.chunk, out=out, workspace=ws,
-                                 stream=stream)
+    def run():
+        for c in caches:
+            G.gtq_quantize_append(plan, 0, c, k_new, v_new, sidx, slot)
+            G.gtq_window_append(plan, 0, win, k_new, v_new, sidx, slot)
+            G.gtq_decode_attn_window(plan, 0, c, win, q, seq_len, n, scale, chunk=args.chunk, out=out, workspace=ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = graph_ms(run, args.steps, args.warmup, per=len(caches))
     packed = n - n_sink - n_recent
     alg = packed * h_kv * base.sizes.bytes_per_token + (n_sink + n_recent) * h_kv * 512
     return {
         "metric": "packed-KV decode attention with fp16 sink + recent window: KV tokens/s",
         "value": round(n / (ms / 1e3), 1), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 (fp16 hi/lo split MFMA operands; binary16 window K/V)",
+        "vs_baseline": None, "dtype": "u32 packed codes; f16 hi/lo MFMA operands; binary16 window K/V",
         "data": "synthetic",
         "config": {"workload": "decode-8b-window", "seq_len": n, "n_sink": n_sink, "n_recent": n_recent,
-                   "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches),
+                   "k_bits_avg": kb / 64, "v_bits": vb, "cache_copies": len(caches),
                    "step": "packed append + window append (1 token) + window decode (3 launches)"},
         "step_hbm_gbs": round(alg / (ms / 1e3) / 1e9, 1),
     }
-
-
-def cpu_baseline(w, seed, min_seconds=10.0):
-    """The fp64 oracle on the whole step (1-token encode + decode of all 32 query heads over
-    every cached token, 8 KV heads), repeated until at least min_seconds of CPU time."""
-    from oracle import gtq_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    n, g, h_kv = w["n_ctx"], w["g"], w["h_kv"]
-    heads, caches = [], []
-    for h in range(h_kv):                                    # cache fill (untimed setup)
-        inp = w["inps"][h]
-        hp = O.HeadPlan(w["rates"][0, h], w["krot"][0][h], w["vrot"][0][h], w["v_bits"])
-        heads.append(hp)
-        caches.append(O.encode_kv(hp, inp["k"][: n - 1], inp["v"][: n - 1]))
-    reps, t_total = 0, 0.0
-    while t_total < min_seconds and reps < 100:
-        t0 = time.perf_counter()
-        for h in range(h_kv):
-            inp, enc, hp = w["inps"][h], caches[h], heads[h]
-            new = O.encode_kv(hp, inp["k"][n - 1: n], inp["v"][n - 1: n])
-            kw = np.concatenate([enc["k_words"], new["k_words"]])
-            kn = np.concatenate([enc["k_norms"], new["k_norms"]])
-            vw = np.concatenate([enc["v_words"], new["v_words"]])
-            vn = np.concatenate([enc["v_norms"], new["v_norms"]])
-            O.decode_attention(hp, inp["q"][0], kw, kn, vw, vn, 1 / math.sqrt(128))
-        t_total += time.perf_counter() - t0
-        reps += 1
-    t_step = t_total / reps
-    return {"value": n / t_step, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the whole step (1-token encode + decode of {h_kv * g} query heads over {n} tokens, "
-                      f"{h_kv} KV heads), {reps} step(s), {t_total:.1f} s",
-            "seconds": round(t_total, 2)}
 
 
 def main():
@@ -517,130 +675,12 @@ def main():
         raise SystemExit("bench.py needs a HIP device")
     G.lib()
     torch.cuda.set_device(0)
-    if args.workload != "decode-8b":
-        fn = {"decode-3b-36L": lambda: bench_decode_stack(args, "decode-3b-36L"),
-              "decode-70b-b32": lambda: bench_decode_stack(args, "decode-70b-b32"),
-              "append-32b": lambda: bench_append(args), "prefill-32b": lambda: bench_prefill(args),
-              "logit-mae": lambda: bench_logit_mae(args),
-              "decode-8b-window": lambda: bench_window(args)}[args.workload]
-        print(json.dumps(fn()), flush=True)
-        return
-    t_setup = time.perf_counter()
-    w = build_workload(args.seed, v_hadamard=args.v_hadamard)
-    plan, n, h_kv, g = w["plan"], w["n_ctx"], w["h_kv"], w["g"]
-    hq = h_kv * g
-    dev = torch.device("cuda")
-    k_all = torch.from_numpy(w["k"]).to(dev)
-    v_all = torch.from_numpy(w["v"]).to(dev)
-    if args.paged:
-        n_pages = (n + args.paged - 1) // args.paged
-        base = G.PagedCache(plan, 1, n_pages, args.paged, n_pages)
-        base.block_table.copy_(torch.from_numpy(
-            np.random.default_rng(args.seed).permutation(n_pages).astype(np.int32)[None]))
+    if args.workload in DECODE:
+        res = bench_decode(args, args.workload)
     else:
-        base = G.PackedCache(plan, 1, n)
-    # fill the cache: tokens 0..n-2 as one prompt; the step appends token n-1
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    G.gtq_quantize_append_chunk(plan, 0, base, k_all[: n - 1].contiguous(), v_all[: n - 1].contiguous(), 0, 0)
-    t1.record()
-    torch.cuda.synchronize()
-    fill_ms = t0.elapsed_time(t1)
-    sizes = base.sizes
-    caches = [base] + [base.clone() for _ in range(args.copies - 1)]
-    k_new = k_all[n - 1: n].contiguous()
-    v_new = v_all[n - 1: n].contiguous()
-    q = torch.from_numpy(w["q"]).to(dev)
-    seq_len = torch.full((1,), n, dtype=torch.int32, device=dev)
-    out = torch.empty_like(q)
-    ws = torch.empty(G.gtq_decode_workspace_bytes(plan, 1, n, args.chunk), dtype=torch.uint8, device=dev)
-    scale = 1.0 / math.sqrt(128)
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        c = caches[i % len(caches)]
-        if ev is None:  # the fused step: prepare + partials + merge in one library call
-            G.gtq_decode_step(plan, 0, c, k_new, v_new, q, seq_len, n, scale, chunk=args.chunk, out=out,
-                              workspace=ws, stream=stream)
-            return
-        # the same three launches as separate calls, with timing events around the partials:
-        # append the step's token at slot n - 1 and rotate the queries (one launch)
-        G.gtq_decode_prepare(plan, 0, c, k_new, v_new, q, seq_len, n, scale, ws, chunk=args.chunk, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        G.gtq_decode_attn_partials(plan, 0, c, seq_len, n, ws, chunk=args.chunk, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        G.gtq_decode_attn_merge(plan, 0, c, seq_len, n, out, ws, chunk=args.chunk, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"setup {time.perf_counter() - t_setup:.1f}s; cache fill (append of {n - 1} tokens x {h_kv} heads) "
-        f"{fill_ms:.3f} ms; cache {base.nbytes() / 1e6:.2f} MB x {len(caches)} copies")
-
-    # the partials kernel's duration is sampled with HIP events on every EVERY-th timed step
-    # (events and separate calls on every step would make the loop host-bound)
-    EVERY = 8
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range((args.steps + EVERY - 1) // EVERY)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i // EVERY] if i % EVERY == 0 else None)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    ms_per_step = total_ms / args.steps
-    value = n / (ms_per_step / 1e3)
-
-    # algorithmic bytes of one launch of the attention (partials) kernel: the packed
-    # records of every attended (token, KV head), the key-group rotations, the queries
-    krot_bytes = sum(sum(int(np.prod(m.shape)) for m in hh) for hh in w["krot"][0]) * 4
-    alg_bytes = n * h_kv * sizes.bytes_per_token + krot_bytes + hq * 128 * 4
-    kern_avg = float(kern_ms.mean())
-    achieved = alg_bytes / (kern_avg / 1e3) / 1e9
-    res = {
-        "metric": "packed-KV decode attention: KV tokens/s + achieved HBM GB/s (% of peak)",
-        "value": round(value, 1),
-        "unit": "KV tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32 (fp16 hi/lo split MFMA operands, fp32 accumulation; u32 packed codes)",
-        "data": "synthetic",
-        "config": {"workload": "llama3.1-8b-shaped layer decode, batch 1, 32768 cached tokens, K2V2 "
-                               "packed cache, 32 query / 8 KV heads, head_dim 128",
-                   "global_batch": 1, "seq_len": n, "parallelism": "none (1 GPU)",
-                   "k_bits_avg": w["k_budget"] / 64, "v_bits": w["v_bits"], "cache_copies": len(caches),
-                   **({"page_tokens": args.paged} if args.paged else {}),
-                   **({"v_rotation": "randomized Hadamard"} if args.v_hadamard else {})},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": partials_kernel_name(plan, 0, h_kv, w["v_bits"]),
-                     "kernel_avg_us": round(kern_avg * 1e3, 3),
-                     "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
-                     "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
-                     "alg_bytes_per_launch": int(alg_bytes)},
-    }
-    if args.calib_copy_mib > 0:
-        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded slice ...")
-        res["cpu_baseline"] = cpu_baseline(w, args.seed)
+        res = {"append-32b": lambda: bench_append(args), "prefill-32b": lambda: bench_prefill(args),
+               "logit-mae": lambda: bench_logit_mae(args),
+               "decode-8b-window": lambda: bench_window(args)}[args.workload]()
     print(json.dumps(res), flush=True)
 
 
