@@ -191,13 +191,20 @@ def graph_ms(fn, reps, warmup, per=1):
     return ms
 
 
-def partials_kernel_name(plan, layer, h_kv, v_bits):
-    """The partials kernel instance a decode of this layer launches: value bits, key words
-    per lane (4 up to 8 key words, else 8) and the layer's largest K-block count."""
+def partials_kernel_name(plan, layer, h_kv, v_bits, paged=False):
+    """The decode partials kernel instance a decode of this layer launches: value bits, key
+    words per lane (4 up to 8 key words, else 8) and the layer's specialized K-block slot
+    counts (leading rate-1 and rate-4 blocks common to every head, at most 3 each and 4
+    together; none for paged caches)."""
     lays = [plan.layout(layer, h) for h in range(h_kv)]
-    nkb = max(sum((d + 31) // 32 for d in lay["dim"]) for lay in lays)
     kwl = 4 if lays[0]["k_words"] <= 8 else 8
-    return f"attn_partials_kernel<{v_bits}, {kwl}, {nkb}, 8, false>"
+    n1 = min((lay["dim"][0] + 31) // 32 if lay["rate"][0] == 1 else 0 for lay in lays)
+    n4 = min((lay["dim"][-1] + 31) // 32 if lay["rate"][-1] == 4 else 0 for lay in lays)
+    n1 = min(n1, 3)
+    n4 = min(n4, 3, 4 - n1)
+    if paged:
+        n1 = n4 = 0
+    return f"attn_decode_kernel<{v_bits}, {kwl}, {n1}, {n4}, {'true' if paged else 'false'}>"
 
 
 # ---------------------------------------------------------------- decode workloads
@@ -294,7 +301,7 @@ def bench_decode(args, name):
                    **({"cache_copies": n_ent} if L == 1 else {}),
                    **({"page_tokens": args.paged} if args.paged else {}),
                    **({"v_rotation": "randomized Hadamard"} if args.v_hadamard else {})},
-        "roofline": hbm_roofline(partials_kernel_name(plan, 0, h_kv, vb), alg_launch, part_ms, name,
+        "roofline": hbm_roofline(partials_kernel_name(plan, 0, h_kv, vb, bool(args.paged)), alg_launch, part_ms, name,
                                  {"timing": "HIP events around a graph of back-to-back partials launches"}),
         "step_hbm_gbs": round(step_alg / (ms / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),

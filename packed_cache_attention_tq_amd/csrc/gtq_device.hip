@@ -826,6 +826,7 @@ struct AttnArgs {
   float* logits;           // decode only, optional
   const int32_t* seq_len;  // decode
   uint4* qb;               // [tiles][kQB] QK B operands
+  float* tile_xs;          // [tiles]: 2^sq, the factor that undoes the operands' range scaling
   float* partials;         // [rows][n_chunks][kPS]
   int64_t capacity;
   int64_t logits_ld;
@@ -978,6 +979,7 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
     for (int r = 0; r < RT; ++r) qrec[r][tid] = qnat[r][crd];
   }
   __syncthreads();
+  __shared__ float wmax[kQrotWaves];
   float acc[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
@@ -1000,9 +1002,34 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
     acc[r] += __shfl_xor(acc[r], 2);
     acc[r] += __shfl_xor(acc[r], 4);
   }
+  // Range of the binary16 high parts: if the tile's largest scaled component exceeds
+  // 2^14, every operand of the tile is scaled by the power of two 2^-sq that brings it
+  // under (exact); the attention kernels multiply the tile's logits by 2^sq.
+  float sc = a.qscale / sqrtf((float)d);
+  {
+    float lm = 0.f;
+    if (part == 0) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) lm = fmaxf(lm, fabsf(acc[r] * sc));
+    }
+#pragma unroll
+    for (int o = 8; o < 64; o <<= 1) lm = fmaxf(lm, __shfl_xor(lm, o));
+    if ((tid & 63) == 0) wmax[tid >> 6] = lm;
+    __syncthreads();
+    float tm = 0.f;
+#pragma unroll
+    for (int w = 0; w < kQrotWaves; ++w) tm = fmaxf(tm, wmax[w]);
+    int sq = 0;
+    if (tm > 16384.f) {  // (NaN or inf inputs keep sq = 0 and propagate)
+      int e;
+      frexpf(tm / 16384.f, &e);
+      sq = e;
+    }
+    sc = ldexpf(sc, -sq);
+    if (tid == 0) a.tile_xs[tile] = ldexpf(1.f, sq);
+  }
   if (part == 0) {
-    const float sc = a.qscale / sqrtf((float)d);
-    const int kp = pick(GL.kp, g) + ii;
+    const int kp = hp->kp_pos[i];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const float val = acc[r] * sc;
@@ -1117,8 +1144,8 @@ using AttnShared = AttnSharedT<8>;
 // 8 codes of rate R (code k at bits [k R, (k + 1) R) of F) -> 8 binary16 centroids: one
 // table read of the byte of 1-bit codes, two of the bytes of 2-bit codes, else two
 // codes per read of the pair table
-template <int R, int RT>
-__device__ inline half8 dequant8(const AttnSharedT<RT>& S, uint32_t F) {
+template <int R, typename SH>
+__device__ inline half8 dequant8(const SH& S, uint32_t F) {
   H8 o;
   if constexpr (R == 1) {
     o.v = S.oct1[F & 0xFFu];
@@ -1376,7 +1403,7 @@ __device__ inline void attn_block(const AttnShared& S, const AttnWave& W, const 
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t)
-    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB, 8>(S, vfield<VB>(vw, t)), oacc[t], 0, 0, 0);
+    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S, vfield<VB>(vw, t)), oacc[t], 0, 0, 0);
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -1386,7 +1413,7 @@ __device__ inline void attn_block(const AttnShared& S, const AttnWave& W, const 
 // KV head (prefill).
 template <int VB, int NKB>
 __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W, const AttnArgs& a,
-                                    int t0, int lane, int q, int n, int my_len,
+                                    int t0, int lane, int q, int n, int my_len, float xs,
                                     const QkConst<NKB>& C, uint32_t nq_off, uint32_t vn_off,
                                     floatx4 (&oacc)[8], float& m_run, float& l_run) {
   const char* sb = reinterpret_cast<const char*>(&S);
@@ -1424,11 +1451,11 @@ __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W,
     lg[6] = fmaf(nb.z, d1[2], lg[6]);
     lg[7] = fmaf(nb.w, d1[3], lg[7]);
   }
-  // ---- online softmax of row n over tokens t0 + 8q + j
+  // ---- online softmax of row n over tokens t0 + 8q + j (logits back in true units: the
+  //      tile's operands were scaled by 2^-sq, xs = 2^sq)
   const int tb = t0 + 8 * q;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (tb + j >= my_len) lg[j] = -INFINITY;
+  for (int j = 0; j < 8; ++j) lg[j] = (tb + j >= my_len) ? -INFINITY : lg[j] * xs;
   if (a.logits) {
     const int id = S.row_id[n];
     if (id >= 0) {
@@ -1489,7 +1516,7 @@ __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W,
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const half8 bv = dequant8<VB, 16>(S, vfield<VB>(vw, t));
+    const half8 bv = dequant8<VB>(S, vfield<VB>(vw, t));
     oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph.h, bv, oacc[t], 0, 0, 0);
     oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl.h, bv, oacc[t], 0, 0, 0);
   }
@@ -1499,8 +1526,8 @@ __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W,
 // One partial (m, l, acc) per row for this split, for rows r0 .. r0 + 7 of the tile: the
 // waves' (m, l) and accumulator rows (staged in the shared slots) merged by their
 // log-sum-exp weights.
-template <int RT>
-__device__ inline void write_partials(const AttnArgs& a, const AttnSharedT<RT>& S, int tid, int r0, int chunk_idx) {
+template <typename SH>
+__device__ inline void write_partials(const AttnArgs& a, const SH& S, int tid, int r0, int chunk_idx) {
   if (tid < 8 * (kD / 4)) {
     const int r8 = tid >> 5, c4 = tid & 31;
     const int r = r0 + r8;
@@ -1855,6 +1882,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   if (tid < 256) tabv = *reinterpret_cast<const uint4*>(a.cb->oct1[tid]);
   else tabv = make_uint4(a.cb->quad2[tid - 256][0], a.cb->quad2[tid - 256][1], 0u, 0u);
   const int len_ld = a.prefill ? 0 : a.seq_len[seq];
+  const float xs = a.tile_xs[tile];
   BlockData<VB, KWL> blk[1];
   int pg_next = 0;
   if constexpr (PAGED) {
@@ -1941,7 +1969,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     if constexpr (RT == 8)
       attn_block<VB, NKB>(S, W, a, t0, lane, q, n, my_row, my_len, my_lo, C, nq_off, vn_off, oacc, m_run, l_run);
     else
-      attn_block16<VB, NKB>(S, W, a, t0, lane, q, n, my_len, C, nq_off, vn_off, oacc, m_run, l_run);
+      attn_block16<VB, NKB>(S, W, a, t0, lane, q, n, my_len, xs, C, nq_off, vn_off, oacc, m_run, l_run);
   }
 
   if constexpr (RT == 8) {
@@ -1969,7 +1997,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
       }
     }
     __syncthreads();
-    write_partials<RT>(a, S, tid, 0, chunk_idx);
+    write_partials(a, S, tid, 0, chunk_idx);
   } else {
     // ---- epilogue, 16 rows: lane (q, n) holds row n (its l over its own tokens) and the
     //      accumulator rows 4q + e; two rounds of 8 rows through the shared slots
@@ -1990,9 +2018,486 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         }
       }
       __syncthreads();
-      write_partials<RT>(a, S, tid, 8 * hf, chunk_idx);
+      write_partials(a, S, tid, 8 * hf, chunk_idx);
     }
   }
+}
+
+// ============================================================================
+// Decode partials: tiles of up to 8 query rows of one sequence and KV head (the g query
+// heads of the KV head; more than 8 take several tiles).
+//
+// Products as in the kernel above (QK: A = decoded key codes of 16 tokens, B = the
+// tile's rotated queries as binary16 high/low columns; PV: A = probability times value
+// norm in binary16 high/low rows, B = decoded value codes), organised for decode:
+//   * K-block slots: the layer's heads order their K-blocks so that the first N1 slots
+//     hold rate-1 blocks and the next N4 slots rate-4 blocks in every head of the layer
+//     (order_kblocks). A rate-1 slot reads one record byte (eight 1-bit codes) and one
+//     entry of the byte table (eight centroids); a rate-4 slot takes four bytes of its
+//     32-bit field, one pair-table entry each. The products of such a run accumulate in
+//     one MFMA chain and meet the group norm once. The remaining slots (rates 2 and 3,
+//     blocks past the specialized counts) decode through the pair table with the slot's
+//     rate, each scaled by its group norm; slots past the head's count are skipped.
+//   * the query operands stay in registers; the value codes and value norms of a block
+//     go from the loads straight to the products (double-buffered registers); only the
+//     key records and key norms are staged in the wave's LDS area.
+//   * softmax against a lazily moved reference: a row's reference m moves only when a
+//     logit exceeds it by more than kLazyT (base 2) or p * nu_V would leave the range
+//     of the binary16 high parts; that block then takes the exact row maximum, raises
+//     m further if a value norm demands it, and rescales. Every other block computes
+//     p = 2^(x - m) <= 2^kLazyT with no cross-lane reduction. The partial stores m
+//     with l and acc relative to it, which is all the log-sum-exp merge needs.
+//   * masking only in blocks that straddle the visible range.
+// ============================================================================
+constexpr float kLazyT = 10.f;
+constexpr float kPvLimit = 16384.f;  // p * nu_V <= 2^14 keeps the binary16 high parts finite
+
+struct DecWave {
+  uint32_t ktile[kBlk * kKPitch];    // 32 key records, pitch 17 words
+  float knt[kMaxGroups][kBlk];       // key group norms, group-major
+  float vn[kBlk];                    // value norms
+};
+struct DecShared {
+  uint4 oct1[256];                   // byte-indexed tables (DevCodebook::oct1, quad2)
+  uint2 quad2[256];
+  uint32_t lut[kPairTable + 4];      // pair table (DevCodebook::pair)
+  uint4 qb[kMaxKB - 1][4][16];       // query operands of the slots kept out of registers
+  int32_t row_id[8];
+  int32_t row_len[8];
+  float om[kWaves][8];
+  float ol[kWaves][8];
+  union alignas(16) {
+    DecWave w[kWaves];               // main loop (reads of partial K-blocks may run a few
+                                     // words past a wave's records: still inside S)
+    float slot[kWaves][8][kD];       // epilogue
+  } u;
+};
+
+template <int VB, int KWL>
+struct DecBlock {
+  uint32_t kr[KWL];
+  float2 kn;
+  float vn;
+  uint32_t vw[2 * VB];
+};
+
+// Loads of one 32-token block (raw buffer views: reads past the slice return 0). Key
+// words lane + 64 i of the block's records (lanes past the records load nothing), key
+// norms 2 lane, 2 lane + 1 of the [32][4] block, the value norm of token lane & 31 and
+// this lane's value words (tokens 8q..8q+7 x coordinates 8n..8n+7).
+template <int VB, int KWL>
+__device__ inline void dec_load(DecBlock<VB, KWL>& B, const SliceRsrc& R, int t0, int kw, int lane, int voff_v) {
+  const int sk = t0 * kw * 4;
+#pragma unroll
+  for (int i = 0; i < KWL; ++i) {
+    // a lane past the block's records re-reads a word of the first half (its cache lines
+    // are being read anyway; the value goes to the pad slot). The first half always lies
+    // inside: a record has at least 4 words for 4 words per lane, 9 for 8.
+    const int lw = lane + 64 * i;
+    const int off = (i < KWL / 2 || lw < kBlk * kw) ? 4 * lw : 4 * (lw - 32 * KWL);
+    B.kr[i] = __builtin_amdgcn_raw_buffer_load_b32(R.kc, off, sk, 0);
+  }
+  B.kn = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(R.kn, 8 * lane, t0 * (kNS * 4), 0));
+  B.vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.vn, 4 * (lane & 31), t0 * 4, 0));
+  const int sv = t0 * (4 * VB * 4);
+  if (VB == 1) {
+    const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.vc, voff_v, sv, 0));
+    B.vw[0] = x.x; B.vw[1] = x.y;
+  } else if (VB == 2) {
+    const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R.vc, voff_v, sv, 0));
+    B.vw[0] = x.x; B.vw[1] = x.y; B.vw[2] = x.z; B.vw[3] = x.w;
+  } else if (VB == 3) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.vc, voff_v + 8 * i, sv, 0));
+      B.vw[2 * i] = x.x; B.vw[2 * i + 1] = x.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(R.vc, voff_v + 16 * i, sv, 0));
+      B.vw[4 * i] = x.x; B.vw[4 * i + 1] = x.y; B.vw[4 * i + 2] = x.z; B.vw[4 * i + 3] = x.w;
+    }
+  }
+}
+
+// max over the lanes of a row: lanes n, 15 - n (row mirror) and q = 0..3
+__device__ inline float row_max(float x) {
+  x = fmaxf(x, dpp_row_mirror(x));
+  return max_over_q(x);
+}
+
+template <int VB, int KWL, int N1, int N4, bool PAGED>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) attn_decode_kernel(AttnArgs a) {
+  constexpr int NS = kMaxKB - 1;  // K-block slots (a head has at most 7)
+  __shared__ DecShared S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, n = lane & 15;
+  const int chunk_idx = blockIdx.x;
+  const int tile = blockIdx.y;
+  int seq, h, tr;
+  tile_coords(a, tile, &seq, &h, &tr);
+  const DevHead* __restrict__ hp = a.heads + h;
+  const size_t sh = (size_t)seq * a.n_kv + h;
+  const int kw = a.k_words;
+  constexpr bool paged = PAGED;
+  auto slice_views = [&](size_t slice, uint32_t len) {
+    SliceRsrc V;
+    V.kc = slice_rsrc(a.k_codes + slice * len * kw, len * (uint32_t)kw * 4u);
+    V.kn = slice_rsrc(a.k_norms + slice * len * kNS, len * (kNS * 4u));
+    V.vc = slice_rsrc(a.v_codes + slice * (len / GTQ_VBLOCK) * (32 * VB), len * (16u * VB));
+    V.vn = slice_rsrc(a.v_norms + slice * len, len * 4u);
+    return V;
+  };
+  auto page_views = [&](int pg) {
+    const bool ok = pg >= 0 && pg < a.pm.n_pages;
+    SliceRsrc V = slice_views((size_t)(ok ? pg : 0) * a.n_kv + h, (uint32_t)a.pm.P);
+    if (!ok) V = slice_views(0, 0u);
+    return V;
+  };
+  const __amdgpu_buffer_rsrc_t Rt =
+      paged ? slice_rsrc(a.pm.table + (size_t)seq * a.pm.tstride, (uint32_t)a.pm.tstride * 4u) : slice_rsrc(a.k_codes, 0u);
+  auto page_of = [&](int t) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(Rt, 0, (t >> a.pm.log2P) * 4, 0);
+  };
+  SliceRsrc R;
+  if constexpr (!PAGED) R = slice_views(sh, (uint32_t)a.capacity);
+  const int voff_v = 4 * (q * (32 * VB) + n * (2 * VB));
+  const bool lo = n >= 8;
+  const int c0 = chunk_idx * a.chunk;
+  // ---- one round of independent loads: query operands (registers for the specialized
+  //      slots, LDS for the others), tables, rows, first block
+  constexpr int NR = N1 + N4;
+  H8 qv[NR > 0 ? NR : 1];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) qv[i].v = a.qb[(size_t)tile * kQB + i * 64 + lane];
+  uint4 qg[(NS * 64 + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int u = 0; u < (NS * 64 + kThreads - 1) / kThreads; ++u) {
+    const int e = tid + kThreads * u;
+    qg[u] = e < NS * 64 ? a.qb[(size_t)tile * kQB + e] : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t lutv[(kPairTable + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int u = 0; u < (kPairTable + kThreads - 1) / kThreads; ++u) {
+    const int e = tid + kThreads * u;
+    lutv[u] = e < kPairTable ? a.cb->pair[e] : 0u;
+  }
+  static_assert(kThreads == 512, "one byte-table entry per thread");
+  uint4 tabv;
+  if (tid < 256) tabv = *reinterpret_cast<const uint4*>(a.cb->oct1[tid]);
+  else tabv = make_uint4(a.cb->quad2[tid - 256][0], a.cb->quad2[tid - 256][1], 0u, 0u);
+  const int len_ld = a.seq_len[seq];
+  const float xs = a.tile_xs[tile];
+  DecBlock<VB, KWL> blk;
+  int pg_next = 0;
+  {
+    const int t_first = c0 + kBlk * wave;
+    if constexpr (PAGED) {
+      dec_load<VB, KWL>(blk, page_views(__builtin_amdgcn_readfirstlane(page_of(t_first))), t_first & (a.pm.P - 1),
+                        kw, lane, voff_v);
+      pg_next = page_of(t_first + kBlk * kWaves);
+    } else {
+      dec_load<VB, KWL>(blk, R, t_first, kw, lane, voff_v);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < (kPairTable + kThreads - 1) / kThreads; ++u) {
+    const int e = tid + kThreads * u;
+    if (e < kPairTable) S.lut[e] = lutv[u];
+  }
+  if (tid < 256) S.oct1[tid] = tabv;
+  else S.quad2[tid - 256] = make_uint2(tabv.x, tabv.y);
+#pragma unroll
+  for (int u = 0; u < (NS * 64 + kThreads - 1) / kThreads; ++u) {
+    const int e = tid + kThreads * u;
+    if (e < NS * 64) (&S.qb[0][0][0])[e] = qg[u];
+  }
+  if (tid < 8) {
+    int L;
+    S.row_id[tid] = tile_row<8>(a, seq, h, tr, tid, len_ld, &L);
+    S.row_len[tid] = L;
+  }
+  __syncthreads();
+  // every present row of a decode tile has the sequence's length
+  int tile_len = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) tile_len = max(tile_len, S.row_len[r]);
+  if (c0 >= tile_len) return;  // no cached token of this tile in this split
+  const int c1 = min(c0 + a.chunk, tile_len);
+  const int lo_vis = a.win ? a.n_sink : 0;  // sink positions read the fp16 buffers
+  constexpr int kStep = kBlk * kWaves;
+  const int my_row = lo ? 15 - n : n;
+  DecWave& W = S.u.w[wave];
+  const char* sb = reinterpret_cast<const char*>(&S);
+  int st[KWL];
+#pragma unroll
+  for (int i = 0; i < KWL; ++i) {
+    const int lw = lane + 64 * i;
+    st[i] = lw < kBlk * kw ? (lw / kw) * kKPitch + lw % kw : kKPitch - 1;
+  }
+  // A-row n of the two 16-token halves: token tau0 and tau0 + 4
+  const int tau0 = 8 * (n >> 2) + (n & 3);
+  const uint32_t ktile_off = (uint32_t)(reinterpret_cast<const char*>(W.ktile) - sb);
+  const uint32_t row0 = ktile_off + 4u * (uint32_t)(tau0 * kKPitch);  // byte offset of token tau0's record
+  constexpr uint32_t kHalf = 4u * 4u * kKPitch;                       // token tau0 + 4
+  const uint32_t lut_off = (uint32_t)(reinterpret_cast<const char*>(S.lut) - sb);
+  const int nkb = hp->nkb;
+  const int gl = hp->n_groups - 1;
+  // rate-4 slots: the lane's field starts at word (bit >> 5) + q, shift bit & 31 (uniform)
+  uint32_t a4[N4 > 0 ? N4 : 1];
+  int sh4[N4 > 0 ? N4 : 1];
+#pragma unroll
+  for (int j = 0; j < N4; ++j) {
+    const int bit = hp->kb_bit[N1 + j];
+    a4[j] = row0 + 4u * (uint32_t)((bit >> 5) + q);
+    sh4[j] = bit & 31;
+  }
+  // other slots: per-lane LDS address << 5 | shift of the first code; one uniform word
+  // with the index width 2R (bits 0..3), the group (bits 4..5) and the table's byte
+  // offset in the shared block (bits 8..)
+  constexpr int NG = NS - N1 - N4;
+  uint32_t gko[NG > 0 ? NG : 1];
+  uint32_t gpk[NG > 0 ? NG : 1];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int rg = hp->kb_rg[N1 + N4 + i];
+    const int rate = rg & 0xFF;
+    const int bit = hp->kb_bit[N1 + N4 + i] + 8 * q * rate;
+    gko[i] = ((row0 + 4u * (uint32_t)(bit >> 5)) << 5) | (uint32_t)(bit & 31);
+    gpk[i] = (uint32_t)(2 * rate) | (uint32_t)(rg >> 8) << 4 |
+             (lut_off + 4u * (uint32_t)(((1 << (2 * rate)) - 4) / 3)) << 8;
+  }
+  // this lane's key norms: knt[g][8q .. 8q + 7]
+  const uint32_t nq_off = (uint32_t)(reinterpret_cast<const char*>(&W.knt[0][8 * q]) - sb);
+  auto knorm4 = [&](int g, int hf) { return *reinterpret_cast<const float4*>(sb + nq_off + g * (kBlk * 4) + 16 * hf); };
+  const uint8_t* sb8 = reinterpret_cast<const uint8_t*>(sb);
+
+  floatx4 oacc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) oacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f, thr = -INFINITY;
+  const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = c0 + kBlk * wave; t0 < c1; t0 += kStep) {
+    // ---- stage the key records and key norms; the value words and norms stay in registers
+#pragma unroll
+    for (int i = 0; i < KWL; ++i) W.ktile[st[i]] = blk.kr[i];
+    W.knt[2 * (lane & 1)][lane >> 1] = blk.kn.x;
+    W.knt[2 * (lane & 1) + 1][lane >> 1] = blk.kn.y;
+    uint32_t vw[2 * VB];
+#pragma unroll
+    for (int i = 0; i < 2 * VB; ++i) vw[i] = blk.vw[i];
+    W.vn[lane & 31] = blk.vn;  // (lanes l and l + 32 hold the same norm)
+    __builtin_amdgcn_wave_barrier();
+    if (t0 + kStep < c1) {
+      if constexpr (PAGED) {  // (a 32-token block lies in one page: P is a multiple of 32)
+        dec_load<VB, KWL>(blk, page_views(__builtin_amdgcn_readfirstlane(pg_next)), (t0 + kStep) & (a.pm.P - 1), kw,
+                          lane, voff_v);
+        pg_next = page_of(t0 + 2 * kStep);
+      } else {
+        dec_load<VB, KWL>(blk, R, t0 + kStep, kw, lane, voff_v);
+      }
+    }
+    // ---- QK: lg[4 hf + e] = logit (high or low column part) of token 8q + 4 hf + e
+    float lg[8];
+    if constexpr (N1 > 0) {
+      floatx4 d0 = z4, d1 = z4;
+#pragma unroll
+      for (int i = 0; i < N1; ++i) {
+        H8 a0, a1;
+        a0.v = S.oct1[sb8[row0 + 4 * i + q]];
+        a1.v = S.oct1[sb8[row0 + kHalf + 4 * i + q]];
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qv[i].h, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qv[i].h, d1, 0, 0, 0);
+      }
+      const float4 na = knorm4(0, 0), nb = knorm4(0, 1);
+      lg[0] = na.x * d0[0]; lg[1] = na.y * d0[1]; lg[2] = na.z * d0[2]; lg[3] = na.w * d0[3];
+      lg[4] = nb.x * d1[0]; lg[5] = nb.y * d1[1]; lg[6] = nb.z * d1[2]; lg[7] = nb.w * d1[3];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lg[j] = 0.f;
+    }
+    if constexpr (N4 > 0) {
+      floatx4 d0 = z4, d1 = z4;
+#pragma unroll
+      for (int j = 0; j < N4; ++j) {
+        const uint32_t* r = reinterpret_cast<const uint32_t*>(sb + a4[j]);
+        const uint32_t f0 = __builtin_amdgcn_alignbit(r[1], r[0], sh4[j]);
+        const uint32_t f1 = __builtin_amdgcn_alignbit(r[4 * kKPitch + 1], r[4 * kKPitch], sh4[j]);
+        H8 a0, a1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a0.u[k] = S.lut[84 + ((f0 >> (8 * k)) & 0xFFu)];
+          a1.u[k] = S.lut[84 + ((f1 >> (8 * k)) & 0xFFu)];
+        }
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qv[N1 + j].h, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qv[N1 + j].h, d1, 0, 0, 0);
+      }
+      const float4 na = knorm4(gl, 0), nb = knorm4(gl, 1);
+      lg[0] = fmaf(na.x, d0[0], lg[0]); lg[1] = fmaf(na.y, d0[1], lg[1]);
+      lg[2] = fmaf(na.z, d0[2], lg[2]); lg[3] = fmaf(na.w, d0[3], lg[3]);
+      lg[4] = fmaf(nb.x, d1[0], lg[4]); lg[5] = fmaf(nb.y, d1[1], lg[5]);
+      lg[6] = fmaf(nb.z, d1[2], lg[6]); lg[7] = fmaf(nb.w, d1[3], lg[7]);
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (N1 + N4 + i < nkb) {
+        const uint32_t* r = reinterpret_cast<const uint32_t*>(sb + (gko[i] >> 5));
+        const uint32_t f0 = __builtin_amdgcn_alignbit(r[1], r[0], gko[i]);
+        const uint32_t f1 = __builtin_amdgcn_alignbit(r[4 * kKPitch + 1], r[4 * kKPitch], gko[i]);
+        const uint32_t w2 = gpk[i] & 15u, lb = gpk[i] >> 8;
+        H8 a0, a1, bq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a0.u[j] = lds_u32(sb, lb + (__builtin_amdgcn_ubfe(f0, w2 * j, w2) << 2));
+          a1.u[j] = lds_u32(sb, lb + (__builtin_amdgcn_ubfe(f1, w2 * j, w2) << 2));
+        }
+        bq.v = S.qb[N1 + N4 + i][q][n];
+        const floatx4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, bq.h, z4, 0, 0, 0);
+        const floatx4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, bq.h, z4, 0, 0, 0);
+        const int grp = (int)((gpk[i] >> 4) & 3u);
+        const float4 na = knorm4(grp, 0), nb = knorm4(grp, 1);
+        lg[0] = fmaf(na.x, d0[0], lg[0]); lg[1] = fmaf(na.y, d0[1], lg[1]);
+        lg[2] = fmaf(na.z, d0[2], lg[2]); lg[3] = fmaf(na.w, d0[3], lg[3]);
+        lg[4] = fmaf(nb.x, d1[0], lg[4]); lg[5] = fmaf(nb.y, d1[1], lg[5]);
+        lg[6] = fmaf(nb.z, d1[2], lg[6]); lg[7] = fmaf(nb.w, d1[3], lg[7]);
+      }
+    }
+    // ---- whole logits (high + low columns); this lane finishes tokens 8q + 4 lo + u of
+    //      row my_row, in units of 2^-sq (xs = 2^sq)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lg[j] += dpp_row_mirror(lg[j]);
+    const int tb = t0 + 8 * q + (lo ? 4 : 0);
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = lo ? lg[4 + u] : lg[u];
+    const bool edge = (t0 + kBlk > c1) || (t0 < lo_vis);  // uniform
+    if (edge) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (tb + u >= c1 || tb + u < lo_vis) x[u] = -INFINITY;
+    }
+    if (a.logits) {
+      const int id = S.row_id[my_row];
+      if (id >= 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (tb + u < c1 && tb + u >= lo_vis) a.logits[(size_t)id * a.logits_ld + tb + u] = x[u] * xs * LN2_F;
+      }
+    }
+    // ---- softmax against the lazily moved reference m_ref (base 2)
+    const float4 vn4 = *reinterpret_cast<const float4*>(&W.vn[8 * q + (lo ? 4 : 0)]);
+    const float vn[4] = {vn4.x, vn4.y, vn4.z, vn4.w};
+    float p[4], pv[4];
+    {
+      const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float xm = -INFINITY, pm = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xm = fmaxf(xm, x[u]);
+        p[u] = __builtin_amdgcn_exp2f(fmaf(x[u], xs, -mu));
+        pv[u] = p[u] * vn[u];
+        pm = fmaxf(pm, pv[u]);
+      }
+      if (edge) {  // masked tokens contribute nothing, whatever their value norm holds
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pv[u] = (x[u] == -INFINITY) ? 0.f : pv[u];
+      }
+      if (__any(xm > thr || !(pm <= kPvLimit))) {
+        // exact row maximum of this block; the reference moves to the larger of it and
+        // the old one, then further by the power of two that keeps p * nu_V <= 2^14
+        float mb = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mb = fmaxf(mb, x[u] * xs);
+        mb = row_max(mb);
+        float m_new = fmaxf(m_ref, mb);
+        const float mu2 = (m_new == -INFINITY) ? 0.f : m_new;
+        float pvm = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          p[u] = __builtin_amdgcn_exp2f(fmaf(x[u], xs, -mu2));
+          pv[u] = (x[u] == -INFINITY) ? 0.f : p[u] * vn[u];
+          pvm = fmaxf(pvm, pv[u]);
+        }
+        pvm = row_max(pvm);
+        if (pvm > kPvLimit && m_new != -INFINITY) {  // (a NaN value norm stays NaN)
+          int e;
+          frexpf(pvm / kPvLimit, &e);
+          m_new += (float)e;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            p[u] = ldexpf(p[u], -e);
+            pv[u] = ldexpf(pv[u], -e);
+          }
+        }
+        // rescale by each row's factor (1 where the reference stays); the accumulator
+        // rows 4q + e of a lane belong to other rows than its own, so every lane takes
+        // part (a uniform step: the factors come from the lanes n == row)
+        const float f = (m_ref != -INFINITY && m_new != m_ref) ? exp2f(m_ref - m_new) : 1.f;
+        l_run *= f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float fe = __shfl(f, 4 * q + e);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) oacc[t][e] *= fe;
+        }
+        m_ref = m_new;
+        thr = (m_ref == -INFINITY) ? -INFINITY : (m_ref + kLazyT) / xs;
+      }
+    }
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    // ---- p * nu_V split into binary16 high and low parts; A-row n < 8: high parts of
+    //      row n, A-row n >= 8: low parts of row 15 - n
+    H8 hv, lv;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const auto hh = __builtin_amdgcn_cvt_pkrtz(pv[2 * k], pv[2 * k + 1]);
+      const auto ll = __builtin_amdgcn_cvt_pkrtz(pv[2 * k] - (float)hh[0], pv[2 * k + 1] - (float)hh[1]);
+      hv.u[k] = __builtin_bit_cast(uint32_t, hh);
+      lv.u[k] = __builtin_bit_cast(uint32_t, ll);
+    }
+    H8 pa;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t keep = lo ? lv.u[k] : hv.u[k];
+      const uint32_t recv = dpp_row_mirror_u(lo ? hv.u[k] : lv.u[k]);
+      pa.u[k] = lo ? recv : keep;
+      pa.u[2 + k] = lo ? keep : recv;
+    }
+    // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S, vfield<VB>(vw, t)), oacc[t], 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves
+  l_run += dpp_row_mirror(l_run);  // the two lanes of a row summed different tokens
+  l_run = sum_over_q(l_run);
+  if (q == 0 && n < 8) {
+    S.om[wave][n] = m_ref;
+    S.ol[wave][n] = l_run;
+  }
+  float vrow[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
+  }
+  __syncthreads();  // every wave is done with its key tile
+  if (q < 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float* dst = &S.u.slot[wave][4 * q + e][8 * n];
+      *reinterpret_cast<float4*>(dst) = make_float4(vrow[0][e], vrow[1][e], vrow[2][e], vrow[3][e]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(vrow[4][e], vrow[5][e], vrow[6][e], vrow[7][e]);
+    }
+  }
+  __syncthreads();
+  write_partials(a, S, tid, 0, chunk_idx);
 }
 
 // ============================================================================
@@ -2441,7 +2946,10 @@ int auto_chunk(int64_t max_len, int64_t tiles) {
 
 // workspace: the tiles' QK B operands, then the partials
 // rotated-query operands of n_tiles row tiles of rt rows (8 KB per 8 rows)
-size_t attn_qb_bytes(int64_t n_tiles, int rt) { return (size_t)n_tiles * (rt / 8) * kQB * sizeof(uint4); }
+// (followed by one float per tile: the factor 2^sq that undoes the operands' range scaling)
+size_t attn_qb_bytes(int64_t n_tiles, int rt) {
+  return (size_t)n_tiles * (rt / 8) * kQB * sizeof(uint4) + ((size_t)n_tiles * 4 + 15) / 16 * 16;
+}
 size_t attn_ws_bytes(int64_t rows, int64_t n_chunks, size_t qb_bytes) {
   return qb_bytes + (size_t)rows * n_chunks * kPS * 4;
 }
@@ -2468,6 +2976,7 @@ void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnA
   aa.v_codes = c->v_codes;
   aa.v_norms = c->v_norms;
   aa.qb = reinterpret_cast<uint4*>(ws);
+  aa.tile_xs = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (size_t)L.n_tiles * (L.rt / 8) * kQB * sizeof(uint4));
   aa.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + L.qb_bytes);
   aa.capacity = c->capacity;
   aa.n_kv = p->n_kv;
@@ -2494,17 +3003,58 @@ gtq_status launch_qrot(AttnArgs& aa, const AttnLaunch& L, const float* q, float 
   return ok();
 }
 
-gtq_status launch_partials(const gtq_plan* p, AttnArgs& aa, const AttnLaunch& L, hipStream_t stream) {
+// decode tiles: attn_decode_kernel<VB, KWL, N1, N4> with the layer's specialized slot
+// counts (N1 <= 3, N4 <= min(3, 4 - N1))
+template <int VB, int KWL>
+void launch_decode(dim3 grid, int n1, int n4, const AttnArgs& aa, hipStream_t stream) {
+  if (aa.pm.table) {  // paged caches: every slot through the generic path
+    hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, 0, 0, true>), grid, dim3(kThreads), 0, stream, aa);
+    return;
+  }
+#define GTQ_DEC(A, B) hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, A, B, false>), grid, dim3(kThreads), 0, stream, aa)
+  switch (n1 * 4 + n4) {
+    case 0: GTQ_DEC(0, 0); break;
+    case 1: GTQ_DEC(0, 1); break;
+    case 2: GTQ_DEC(0, 2); break;
+    case 3: GTQ_DEC(0, 3); break;
+    case 4: GTQ_DEC(1, 0); break;
+    case 5: GTQ_DEC(1, 1); break;
+    case 6: GTQ_DEC(1, 2); break;
+    case 7: GTQ_DEC(1, 3); break;
+    case 8: GTQ_DEC(2, 0); break;
+    case 9: GTQ_DEC(2, 1); break;
+    case 10: GTQ_DEC(2, 2); break;
+    case 12: GTQ_DEC(3, 0); break;
+    default: GTQ_DEC(3, 1); break;
+  }
+#undef GTQ_DEC
+}
+
+gtq_status launch_partials(const gtq_plan* p, int layer, AttnArgs& aa, const AttnLaunch& L, hipStream_t stream) {
   if (p->k_words > 16) return fail(GTQ_EUNSUPPORTED, "gtq attention: more than 16 key code words per token");
   dim3 grid(L.n_chunks - aa.win, L.n_tiles);  // (the window's split comes from its own launch)
   const bool wide = p->k_words > 8;  // key words per lane: 4 (k_words <= 8) or 8
+  if (L.rt == 8) {
+    const int n1 = p->layer_n1[layer], n4 = p->layer_n4[layer];
+#define GTQ_DECV(VB) \
+  if (wide) launch_decode<VB, 8>(grid, n1, n4, aa, stream); else launch_decode<VB, 4>(grid, n1, n4, aa, stream)
+    switch (p->v_bits) {
+      case 1: GTQ_DECV(1); break;
+      case 2: GTQ_DECV(2); break;
+      case 3: GTQ_DECV(3); break;
+      default: GTQ_DECV(4); break;
+    }
+#undef GTQ_DECV
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "gtq attention partials: launch");
+    return ok();
+  }
   // K-blocks per head: sum_g ceil(d_g / 32), 4..7 for four groups; the kernel runs the
   // layer's largest count (extra K-blocks of a head have zero query operands)
   const int nkb = aa.nkb_max;
   if (nkb < 4 || nkb > 7) return fail(GTQ_EUNSUPPORTED, "gtq attention: K-block count outside 4..7");
-#define GTQ_LAUNCH4(VB, KWL, NKB, PG)                                                                             \
-  if (L.rt == 16) hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 16, PG>), grid, dim3(kThreads), 0, stream, aa); \
-  else hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 8, PG>), grid, dim3(kThreads), 0, stream, aa)
+#define GTQ_LAUNCH4(VB, KWL, NKB, PG) \
+  hipLaunchKernelGGL((attn_partials_kernel<VB, KWL, NKB, 16, PG>), grid, dim3(kThreads), 0, stream, aa)
 #define GTQ_LAUNCH3(VB, KWL, NKB) \
   if (aa.pm.table) { GTQ_LAUNCH4(VB, KWL, NKB, true); } else { GTQ_LAUNCH4(VB, KWL, NKB, false); }
 #define GTQ_LAUNCH2(VB, KWL)                  \
@@ -2756,7 +3306,7 @@ gtq_status gtq_decode_attn_partials(const gtq_plan* plan, int32_t layer, const g
   aa.seq_len = seq_len;
   aa.prefill = 0;
   aa.max_len = (int32_t)max_len;
-  return launch_partials(plan, aa, L, (hipStream_t)hip_stream);
+  return launch_partials(plan, layer, aa, L, (hipStream_t)hip_stream);
 }
 
 gtq_status gtq_decode_attn_merge(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
@@ -2897,7 +3447,7 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
   hipStream_t s = (hipStream_t)hip_stream;
   st = launch_qrot(aa, L, q, softmax_scale, s);
   if (st != GTQ_OK) return st;
-  st = launch_partials(plan, aa, L, s);
+  st = launch_partials(plan, layer, aa, L, s);
   if (st != GTQ_OK) return st;
   return launch_merge(plan, layer, L, nullptr, pos0, 1, (int)(pos0 + n_tok), out, workspace, s);
 }
@@ -2991,7 +3541,7 @@ gtq_status gtq_decode_attn_window(const gtq_plan* plan, int32_t layer, const gtq
                      L.n_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq_decode_attn_window: launch");
-  st = launch_partials(plan, aa, L, stream);
+  st = launch_partials(plan, layer, aa, L, stream);
   if (st != GTQ_OK) return st;
   return launch_merge(plan, layer, L, seq_len, 0, 0, (int)max_len, out, workspace, stream, window);
 }

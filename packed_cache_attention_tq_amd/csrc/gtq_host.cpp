@@ -181,6 +181,39 @@ void build_head(const uint8_t* rates, int layout, gtq_head_layout* lay, DevHead*
   }
   dh->krot_floats = rot;
   lay->k_words = (bit + 31) / 32;
+  for (int g = 0; g < dh->n_groups; ++g)
+    for (int i = 0; i < dh->dim[g]; ++i) dh->kp_pos[dh->pos_off[g] + i] = (uint8_t)(dh->kp_off[g] + i);
+}
+
+// Puts a head's K-blocks in the slot order the decode kernel specializes on: the first
+// n1 blocks of the rate-1 group (group 0), then the first n4 blocks of the rate-4 group
+// (the last group), then the remaining blocks in group order. Every head of a layer
+// gets the layer's (n1, n4), so that these slots have the same rate in every head.
+void order_kblocks(DevHead* dh, int n1, int n4) {
+  int src[kMaxKB], ns = 0;
+  int first[kMaxGroups], k = 0;
+  for (int g = 0; g < dh->n_groups; ++g) {
+    first[g] = k;
+    k += dh->nkb_g[g];
+  }
+  const int gl = dh->n_groups - 1;
+  for (int i = 0; i < n1; ++i) src[ns++] = first[0] + i;
+  for (int i = 0; i < n4; ++i) src[ns++] = first[gl] + i;
+  for (int g = 0; g < dh->n_groups; ++g)
+    for (int i = (g == 0 ? n1 : 0) + (g == gl ? n4 : 0); i < dh->nkb_g[g]; ++i) src[ns++] = first[g] + i;
+  int bit[kMaxKB], rg[kMaxKB], slot_of[kMaxKB];
+  for (int s = 0; s < ns; ++s) {
+    bit[s] = dh->kb_bit[src[s]];
+    rg[s] = dh->kb_rg[src[s]];
+    slot_of[src[s]] = s;
+  }
+  for (int s = 0; s < kMaxKB; ++s) {
+    dh->kb_bit[s] = s < ns ? bit[s] : bit[0];
+    dh->kb_rg[s] = s < ns ? rg[s] : rg[0];
+  }
+  for (int g = 0; g < dh->n_groups; ++g)
+    for (int i = 0; i < dh->dim[g]; ++i)
+      dh->kp_pos[dh->pos_off[g] + i] = (uint8_t)(kKB * slot_of[first[g] + i / kKB] + i % kKB);
 }
 
 }  // namespace gtq
@@ -362,6 +395,22 @@ gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
                                   std::to_string(h) + ")");
     build_head(r, d->rope_layout, &p->layouts[h], &p->heads[h]);
     krot_total += p->heads[h].krot_floats;
+  }
+  // per layer: how many leading rate-1 and rate-4 K-blocks every head has (at most 3
+  // each and 4 together: the decode kernel is compiled for these counts)
+  p->layer_n1.assign(d->n_layers, 0);
+  p->layer_n4.assign(d->n_layers, 0);
+  for (int l = 0; l < d->n_layers; ++l) {
+    int n1 = 3, n4 = 3;
+    for (int h = 0; h < d->n_kv_heads; ++h) {
+      const DevHead& dh = p->heads[(size_t)l * d->n_kv_heads + h];
+      n1 = std::min(n1, dh.rate[0] == 1 ? dh.nkb_g[0] : 0);
+      n4 = std::min(n4, dh.rate[dh.n_groups - 1] == 4 ? dh.nkb_g[dh.n_groups - 1] : 0);
+    }
+    n4 = std::min(n4, 4 - n1);
+    p->layer_n1[l] = n1;
+    p->layer_n4[l] = n4;
+    for (int h = 0; h < d->n_kv_heads; ++h) order_kblocks(&p->heads[(size_t)l * d->n_kv_heads + h], n1, n4);
   }
   // rotation pool: all K group rotations (as given), all V rotations, then the V
   // rotations transposed (read column-wise by the attention kernel's last step)

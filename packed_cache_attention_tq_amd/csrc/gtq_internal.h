@@ -30,6 +30,8 @@ struct DevHead {
   int32_t pos_off[kMaxGroups];    // group start in record position order (0..127)
   int32_t kp_off[kMaxGroups];     // group start in the padded K-block order
   int32_t nkb_g[kMaxGroups];      // K-blocks of each group
+  // K-blocks in slot order: first the layer's n1 leading rate-1 blocks, then its n4
+  // leading rate-4 blocks, then every other block in group order (see order_kblocks)
   int32_t kb_bit[kMaxKB];         // record bit of each K-block's first coordinate
   int32_t kb_rg[kMaxKB];          // rate | group << 8 of each K-block; slots past nkb repeat slot 0
   int64_t krot_off[kMaxGroups];   // float offset of Pi_g (row-major d x d) in the pool
@@ -42,6 +44,8 @@ struct DevHead {
   int32_t krot_floats;            // sum_g d_g^2
   int32_t v_hadamard;             // 1: Pi_V = H_128 diag(vsign) / sqrt(128) exactly (fast transform)
   uint8_t coord[kD];              // record position -> head coordinate
+  uint8_t kp_pos[kD];             // record position -> its place in the K-block operands
+                                  // (slot * 32 + coordinate within the block)
   float vsign[kD];                // the sign vector of a Hadamard Pi_V
 };
 
@@ -66,6 +70,7 @@ struct gtq_plan {
   int32_t n_layers = 0, n_kv = 0, n_q = 0, rope_layout = 0, k_budget = 0, v_bits = 0;
   int32_t k_words = 0, flags = 0;
   std::vector<gtq::DevHead> heads;      // [L][H_kv]
+  std::vector<int32_t> layer_n1, layer_n4;  // [L]: specialized rate-1 / rate-4 K-block slots
   std::vector<gtq_head_layout> layouts; // [L][H_kv]
   std::vector<float> rot;               // rotation pool
   std::vector<uint16_t> rsplit;         // rotations as binary16 (hi, lo) pairs, for the append GEMM
@@ -85,6 +90,7 @@ gtq_status ok();
 // host math shared by the host entry points
 void lloyd_max(int bits, double* centroids, double* mse);
 void build_head(const uint8_t* rates, int rope_layout, gtq_head_layout* lay, DevHead* dh);
+void order_kblocks(DevHead* dh, int n1, int n4);
 void fill_codebook(DevCodebook* cb);
 gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p);
 }  // namespace gtq
