@@ -251,11 +251,14 @@ gtq_status gtq_quantize_append_chunk(const gtq_plan* plan, int32_t layer,
 /* ---------------------------------------------------------------- attention */
 
 /* Workspace bytes that gtq_decode_attn needs for `batch` sequences of at most
- * max_len cached tokens with split size `chunk` (0 = automatic; else a multiple of
- * 32, at most 256 splits per sequence). The workspace holds the rotated queries
- * (8 KB per tile of up to 8 query rows of one sequence and KV head) and the split-K
- * partials (m, l, acc[128] per query row and split); its contents need no
- * initialisation.
+ * max_len cached tokens with split parameter `chunk` (0 = automatic; else a multiple
+ * of 32 giving at most 256 splits of max_len). The partials phase runs G workgroups
+ * that share the batch's 32-token blocks (of every tile of up to 8 query rows of one
+ * sequence and KV head) equally: G = the device's compute units for chunk 0, else
+ * tiles x ceil(max_len / chunk). The workspace holds the rotated queries (8 KB per
+ * tile) and the split-K partials (m, l, acc[128] of 8 rows per piece of a tile that
+ * one workgroup runs, G + tiles - 1 at most, plus one per tile for a window split);
+ * its contents need no initialisation.
  * Calls that share a workspace must be ordered on one stream. */
 gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64_t max_len,
                                       int32_t chunk, size_t* out);
@@ -272,9 +275,10 @@ gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64
  *            every visible token; entries >= seq_len untouched), for tests.
  * Logit of token n, query head h: scale * sum_g nu_{n,g} / sqrt(d_g) *
  * sum_{i in g} (Pi_g q_g)_i C_{b_g}[code_{n,i}]; softmax over n < seq_len; output
- * Pi_V^T sum_n p_n nu^V_n C_{b_V}[vcode_n] / sqrt(128). Split-K over `chunk`-token
- * pieces (gtq_decode_attn_partials) followed by a log-sum-exp merge and the inverse
- * value rotation (gtq_decode_attn_merge). A sequence with seq_len 0 gets a zero output.
+ * Pi_V^T sum_n p_n nu^V_n C_{b_V}[vcode_n] / sqrt(128). Split-K over the pieces of
+ * the workgroups' equal shares of blocks (gtq_decode_attn_partials; see
+ * gtq_decode_workspace_bytes) followed by a log-sum-exp merge and the inverse value
+ * rotation (gtq_decode_attn_merge). A sequence with seq_len 0 gets a zero output.
  * Errors: EINVAL (NULL, layer, scale not finite, chunk not a multiple of 32 or more than
  * 256 splits, host-only plan, max_len < 0); ECAPACITY (workspace too small,
  * max_len > capacity). */
@@ -290,9 +294,10 @@ gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_
  *   (the query side of the logit above), scaled by softmax_scale * log2(e) / sqrt(d_g),
  *   stored in the workspace as the operand the partials phase reads. Errors as for
  *   gtq_decode_attn.
- * gtq_decode_attn_partials: per query row and split, the running maximum m (base 2),
+ * gtq_decode_attn_partials: per query row and piece, the running maximum m (base 2),
  *   the sum l of 2^(logit*log2(e) - m) and the accumulator of p * nu_V * C[vcode] in
- *   the value rotation's basis, into the workspace (needs the rotated queries).
+ *   the value rotation's basis, into the workspace (needs the rotated queries; the
+ *   merge must see the same seq_len, max_len and chunk).
  * gtq_decode_attn_merge: combines the splits and writes `out`. */
 gtq_status gtq_decode_rotate_queries(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
                                      const float* q, int64_t max_len, float softmax_scale, int32_t chunk,

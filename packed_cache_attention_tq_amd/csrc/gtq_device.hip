@@ -7,6 +7,7 @@
 // column: norm, random rotation, per-coordinate Lloyd-Max quantization).
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 #include <string.h>
 
 #include <algorithm>
@@ -849,12 +850,56 @@ struct AttnArgs {
   int32_t win;             // 1: split n_chunks - 1 is the fp16 window's
   int32_t n_sink, sink_slots, n_recent;
   PageMap pm;              // paged cache (pm.table set) or contiguous
+  // decode: the partials kernel's workgroups (sk_G) share the (tile, 32-token block)
+  // units of the batch equally; partial record of segment s (workgroup w on tile t:
+  // s = w + t; the window split of tile t: s = sk_G + n_tiles + t), row r of the tile:
+  // partials + (8 s + r) kPS
+  int32_t batch, n_tiles, sk_G;
 };
 
 // End of the packed positions of a sequence of length L with n_sink sink and n_recent
 // recent fp16 positions: the packed ones are [n_sink, packed_end).
 __host__ __device__ inline int packed_end(int L, int n_sink, int n_recent) {
   return L > n_sink + n_recent ? L - n_recent : min(L, n_sink);
+}
+
+// Decode work units: the 32-token blocks of each row tile's packed range (every tile of a
+// sequence has the sequence's length). Workgroup w of G takes units [w U / G, (w + 1) U / G).
+__device__ inline int seq_blocks(const int32_t* seq_len, int b, int max_len, int win, int n_sink, int n_recent) {
+  int L = min(max(seq_len[b], 0), max_len);
+  if (win) L = packed_end(L, n_sink, n_recent);
+  return (L + 31) >> 5;
+}
+// the workgroup whose range holds unit u (0 <= u < U)
+__device__ inline int sk_owner(int64_t u, int G, int64_t U) { return (int)(((u + 1) * G - 1) / U); }
+// whether workgroup w has units (with fewer units than workgroups some have none, and
+// write no partial)
+__device__ inline bool sk_live(int64_t w, int G, int64_t U) { return (w + 1) * U / G > w * U / G; }
+
+// U and the units of the sequences before `seq`, summed by the 256 threads of a merge
+// workgroup (every thread gets both)
+__device__ inline void sk_sums256(const int32_t* seq_len, int batch, int seq, int tps, int max_len, int win,
+                                  int n_sink, int n_recent, long long* U, long long* P) {
+  __shared__ long long red_u[4], red_p[4];
+  const int tid = threadIdx.x;
+  long long u = 0, pb = 0;
+  for (int b = tid; b < batch; b += 256) {
+    const long long x = (long long)tps * seq_blocks(seq_len, b, max_len, win, n_sink, n_recent);
+    u += x;
+    if (b < seq) pb += x;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    u += __shfl_xor(u, m);
+    pb += __shfl_xor(pb, m);
+  }
+  if ((tid & 63) == 0) {
+    red_u[tid >> 6] = u;
+    red_p[tid >> 6] = pb;
+  }
+  __syncthreads();
+  *U = red_u[0] + red_u[1] + red_u[2] + red_u[3];
+  *P = red_p[0] + red_p[1] + red_p[2] + red_p[3];
 }
 
 // tile -> (sequence, KV head, tile within the head)
@@ -1526,7 +1571,7 @@ __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W,
 // One partial (m, l, acc) per row for this split, for rows r0 .. r0 + 7 of the tile: the
 // waves' (m, l) and accumulator rows (staged in the shared slots) merged by their
 // log-sum-exp weights.
-template <typename SH>
+template <int NW = kWaves, typename SH>
 __device__ inline void write_partials(const AttnArgs& a, const SH& S, int tid, int r0, int chunk_idx) {
   if (tid < 8 * (kD / 4)) {
     const int r8 = tid >> 5, c4 = tid & 31;
@@ -1535,12 +1580,12 @@ __device__ inline void write_partials(const AttnArgs& a, const SH& S, int tid, i
     if (id >= 0) {
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.om[w][r]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, S.om[w][r]);
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       float l = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
           const float mw = S.om[w][r];
           const float sw = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
           const float4 x = *reinterpret_cast<const float4*>(&S.u.slot[w][r8][4 * c4]);
@@ -1801,7 +1846,7 @@ __device__ inline void window_split(const AttnArgs& a, AttnShared& S, int tile) 
     const int r = e >> 7, i = e & 127;
     const int id = active ? S.row_id[r] : -1;
     if (id >= 0) {
-      float* dst = a.partials + ((size_t)id * a.n_chunks + (a.n_chunks - 1)) * kPS;
+      float* dst = a.partials + ((size_t)(a.sk_G + a.n_tiles + tile) * 8 + r) * kPS;
       const float v = part[(0 * 8 + r) * kD + i] + part[(1 * 8 + r) * kD + i] + part[(2 * 8 + r) * kD + i] +
                       part[(3 * 8 + r) * kD + i];
       dst[4 + i] = v * 11.313708498984761f;  // sqrt(128): the merge divides by it
@@ -2027,20 +2072,31 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 // Decode partials: tiles of up to 8 query rows of one sequence and KV head (the g query
 // heads of the KV head; more than 8 take several tiles).
 //
+// Work split: the units are the 32-token blocks of every tile's packed range, U in all.
+// The launch has G workgroups of 16 waves (one per compute unit by default); workgroup w
+// takes units [w U / G, (w + 1) U / G), i.e. the same number of blocks whatever the
+// lengths of a ragged batch. Its range crosses tile boundaries: each piece (segment) is
+// run by the 16 waves (block b of the segment to wave b mod 16), merged over the waves
+// and written as one partial record of its 8 rows at index w + t (unique: a workgroup's
+// tiles follow the previous workgroup's last one). The merge finds the segments of a
+// tile from the same arithmetic.
+//
 // Products as in the kernel above (QK: A = decoded key codes of 16 tokens, B = the
 // tile's rotated queries as binary16 high/low columns; PV: A = probability times value
 // norm in binary16 high/low rows, B = decoded value codes), organised for decode:
 //   * K-block slots: the layer's heads order their K-blocks so that the first N1 slots
 //     hold rate-1 blocks and the next N4 slots rate-4 blocks in every head of the layer
-//     (order_kblocks). A rate-1 slot reads one record byte (eight 1-bit codes) and one
-//     entry of the byte table (eight centroids); a rate-4 slot takes four bytes of its
-//     32-bit field, one pair-table entry each. The products of such a run accumulate in
-//     one MFMA chain and meet the group norm once. The remaining slots (rates 2 and 3,
-//     blocks past the specialized counts) decode through the pair table with the slot's
-//     rate, each scaled by its group norm; slots past the head's count are skipped.
-//   * the query operands stay in registers; the value codes and value norms of a block
-//     go from the loads straight to the products (double-buffered registers); only the
-//     key records and key norms are staged in the wave's LDS area.
+//     (order_kblocks). A rate-1 slot reads one record byte (eight 1-bit codes) and two
+//     entries of the nibble table; a rate-4 slot takes four bytes of its 32-bit field,
+//     one pair-table entry each. The products of such a run accumulate in one MFMA chain
+//     and meet the group norm once. The remaining slots (rates 2 and 3, blocks past the
+//     specialized counts) decode through the pair table of the slot's rate, each scaled
+//     by its group norm; slots past the head's count are skipped.
+//   * decode tables repeated across the LDS banks (DecTables): random lookups by a wave
+//     run at the rate of contiguous reads. They fill most of the 160 KB, hence one
+//     workgroup per compute unit.
+//   * the query operands and key records / norms are staged in LDS; the value codes go
+//     from their loads (issued after the previous block's products) to the products.
 //   * softmax against a lazily moved reference: a row's reference m moves only when a
 //     logit exceeds it by more than kLazyT (base 2) or p * nu_V would leave the range
 //     of the binary16 high parts; that block then takes the exact row maximum, raises
@@ -2051,27 +2107,83 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 // ============================================================================
 constexpr float kLazyT = 10.f;
 constexpr float kPvLimit = 16384.f;  // p * nu_V <= 2^14 keeps the binary16 high parts finite
+constexpr int kDecWaves = 16;        // one 1024-thread workgroup per compute unit
+constexpr int kDecThreads = 64 * kDecWaves;
 
 struct DecWave {
   uint32_t ktile[kBlk * kKPitch];    // 32 key records, pitch 17 words
   float knt[kMaxGroups][kBlk];       // key group norms, group-major
   float vn[kBlk];                    // value norms
 };
+// Decode tables in LDS, each entry repeated so that a wave's random lookups fall in
+// distinct banks: entry e of a table kept R times sits at (e R + r) x its size and lane
+// l reads copy r = l mod R. The copy counts are the smallest a random wave-wide read of
+// that width needs to run at the rate of a contiguous one on gfx950 (b32: 64, b64: 32;
+// the rate-4 pairs keep 16 for space). Byte offsets are fixed (the lookups put them in
+// the instruction's offset field).
+constexpr uint32_t kDecT1 = 4096, kDecP3 = 8192, kDecP4 = 24576, kDecQ2 = 40960;
+struct DecTables {
+  uint32_t lut[1024];                // all pair tables once (DevCodebook::pair); the rate-1
+                                     // and rate-2 ones (4 and 16 entries) read conflict-free
+  uint2 t1[16][32];                  // 4 rate-1 centroids of each nibble, 32 copies
+  uint32_t p3[64][64];               // rate-3 pairs, 64 copies
+  uint32_t p4[256][16];              // rate-4 pairs, 16 copies
+  uint2 q2[256][32];                 // 4 rate-2 centroids of each byte, 32 copies
+};
+static_assert(offsetof(DecTables, t1) == kDecT1 && offsetof(DecTables, p3) == kDecP3 &&
+                  offsetof(DecTables, p4) == kDecP4 && offsetof(DecTables, q2) == kDecQ2,
+              "decode table offsets");
 struct DecShared {
-  uint4 oct1[256];                   // byte-indexed tables (DevCodebook::oct1, quad2)
-  uint2 quad2[256];
-  uint32_t lut[kPairTable + 4];      // pair table (DevCodebook::pair)
+  union alignas(16) {
+    DecTables t;
+  } u;
+  DecWave w[kDecWaves];              // main loop (reads of partial K-blocks may run a few words
+                                     // past a wave's records: still inside S); between a
+                                     // segment's loop and its partial, eight merge slots
+  long long sk_u0, sk_u1, sk_P;      // this workgroup's next unit, its end, the units before sk_b
+  int32_t sk_b;                      // the sequence of the next unit (or an earlier, empty one)
+  int32_t sk_tile;                   // the current segment's row tile
   uint4 qb[kMaxKB - 1][4][16];       // query operands of the slots kept out of registers
   int32_t row_id[8];
   int32_t row_len[8];
-  float om[kWaves][8];
-  float ol[kWaves][8];
-  union alignas(16) {
-    DecWave w[kWaves];               // main loop (reads of partial K-blocks may run a few
-                                     // words past a wave's records: still inside S)
-    float slot[kWaves][8][kD];       // epilogue
-  } u;
+  float om[kDecWaves][8];
+  float ol[kDecWaves][8];
 };
+static_assert(offsetof(DecShared, u) == 0, "tables at the start of the shared block");
+
+// Lane base offsets of the replicated tables: copy lane mod 32 of an 8-byte table
+// (t1, q2), lane mod 64 and lane mod 16 of a 4-byte one (p3, p4)
+struct DecLanes {
+  uint32_t l8, l4, l4_16;
+};
+
+__device__ inline uint2 lds_u64(const char* base, uint32_t off) {
+  return *reinterpret_cast<const uint2*>(base + off);
+}
+
+// the 8 binary16 centroids of the 8 codes of rate R in F (code k at bits R k) from the
+// replicated tables: nibbles through t1 (R = 1), bytes through q2 (R = 2), code pairs
+// through p3 / p4 (R = 3, 4)
+template <int R>
+__device__ inline half8 dec_dequant8(const char* sb, const DecLanes& L, uint32_t F) {
+  H8 o;
+  if constexpr (R == 1) {
+    const uint2 x = lds_u64(sb, kDecT1 + (((F << 8) & 0xF00u) | L.l8));
+    const uint2 y = lds_u64(sb, kDecT1 + (((F << 4) & 0xF00u) | L.l8));
+    o.u[0] = x.x; o.u[1] = x.y; o.u[2] = y.x; o.u[3] = y.y;
+  } else if constexpr (R == 2) {
+    const uint2 x = lds_u64(sb, kDecQ2 + (((F << 8) & 0xFF00u) | L.l8));
+    const uint2 y = lds_u64(sb, kDecQ2 + ((F & 0xFF00u) | L.l8));
+    o.u[0] = x.x; o.u[1] = x.y; o.u[2] = y.x; o.u[3] = y.y;
+  } else if constexpr (R == 3) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.u[j] = lds_u32(sb, kDecP3 + ((__builtin_amdgcn_ubfe(F, 6 * j, 6) << 8) | L.l4));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.u[j] = lds_u32(sb, kDecP4 + ((__builtin_amdgcn_ubfe(F, 8 * j, 8) << 6) | L.l4_16));
+  }
+  return o.h;
+}
 
 template <int VB, int KWL>
 struct DecBlock {
@@ -2082,23 +2194,23 @@ struct DecBlock {
 };
 
 // Loads of one 32-token block (raw buffer views: reads past the slice return 0). Key
-// words lane + 64 i of the block's records (lanes past the records load nothing), key
-// norms 2 lane, 2 lane + 1 of the [32][4] block, the value norm of token lane & 31 and
-// this lane's value words (tokens 8q..8q+7 x coordinates 8n..8n+7).
+// words: with W = 2 KWL words per record row, lane l takes word l mod W of tokens
+// l / W + (64 / W) i (kvo = its byte offset in the block's records; lanes with
+// l mod W >= kw read the next record's first words, which land in the pad of their row).
+// Key norms 2 lane, 2 lane + 1 of the [32][4] block and the value norm of token lane & 31
+// (dec_load_k); this lane's value words, tokens 8q..8q+7 x coordinates 8n..8n+7
+// (dec_load_v: issued once the products of the previous block have read them).
 template <int VB, int KWL>
-__device__ inline void dec_load(DecBlock<VB, KWL>& B, const SliceRsrc& R, int t0, int kw, int lane, int voff_v) {
+__device__ inline void dec_load_k(DecBlock<VB, KWL>& B, const SliceRsrc& R, int t0, int kw, int lane, int kvo) {
   const int sk = t0 * kw * 4;
+  constexpr int kTok = 64 / (2 * KWL);  // tokens per load instruction
 #pragma unroll
-  for (int i = 0; i < KWL; ++i) {
-    // a lane past the block's records re-reads a word of the first half (its cache lines
-    // are being read anyway; the value goes to the pad slot). The first half always lies
-    // inside: a record has at least 4 words for 4 words per lane, 9 for 8.
-    const int lw = lane + 64 * i;
-    const int off = (i < KWL / 2 || lw < kBlk * kw) ? 4 * lw : 4 * (lw - 32 * KWL);
-    B.kr[i] = __builtin_amdgcn_raw_buffer_load_b32(R.kc, off, sk, 0);
-  }
+  for (int i = 0; i < KWL; ++i) B.kr[i] = __builtin_amdgcn_raw_buffer_load_b32(R.kc, kvo, sk + i * kTok * kw * 4, 0);
   B.kn = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(R.kn, 8 * lane, t0 * (kNS * 4), 0));
   B.vn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.vn, 4 * (lane & 31), t0 * 4, 0));
+}
+template <int VB, int KWL>
+__device__ inline void dec_load_v(DecBlock<VB, KWL>& B, const SliceRsrc& R, int t0, int voff_v) {
   const int sv = t0 * (4 * VB * 4);
   if (VB == 1) {
     const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.vc, voff_v, sv, 0));
@@ -2128,21 +2240,28 @@ __device__ inline float row_max(float x) {
 }
 
 template <int VB, int KWL, int N1, int N4, bool PAGED>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) attn_decode_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) attn_decode_kernel(AttnArgs a) {
   constexpr int NS = kMaxKB - 1;  // K-block slots (a head has at most 7)
   __shared__ DecShared S;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, n = lane & 15;
-  const int chunk_idx = blockIdx.x;
-  const int tile = blockIdx.y;
-  int seq, h, tr;
-  tile_coords(a, tile, &seq, &h, &tr);
-  const DevHead* __restrict__ hp = a.heads + h;
-  const size_t sh = (size_t)seq * a.n_kv + h;
   const int kw = a.k_words;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int tps = a.n_kv * a.tiles_per_kv;  // row tiles per sequence
+  int seq = 0, h = 0;                        // of the current segment (the views read them)
   constexpr bool paged = PAGED;
+  using KArgs = const __attribute__((address_space(4))) AttnArgs;
+  KArgs* const ka0 = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  auto slice_views_of = [&](const AttnArgs& A, size_t slice, uint32_t len) {
+    SliceRsrc V;
+    V.kc = slice_rsrc(A.k_codes + slice * len * kw, len * (uint32_t)kw * 4u);
+    V.kn = slice_rsrc(A.k_norms + slice * len * kNS, len * (kNS * 4u));
+    V.vc = slice_rsrc(A.v_codes + slice * (len / GTQ_VBLOCK) * (32 * VB), len * (16u * VB));
+    V.vn = slice_rsrc(A.v_norms + slice * len, len * 4u);
+    return V;
+  };
   auto slice_views = [&](size_t slice, uint32_t len) {
     SliceRsrc V;
     V.kc = slice_rsrc(a.k_codes + slice * len * kw, len * (uint32_t)kw * 4u);
@@ -2157,93 +2276,184 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     if (!ok) V = slice_views(0, 0u);
     return V;
   };
-  const __amdgpu_buffer_rsrc_t Rt =
-      paged ? slice_rsrc(a.pm.table + (size_t)seq * a.pm.tstride, (uint32_t)a.pm.tstride * 4u) : slice_rsrc(a.k_codes, 0u);
   auto page_of = [&](int t) {
+    const __amdgpu_buffer_rsrc_t Rt = slice_rsrc(a.pm.table + (size_t)seq * a.pm.tstride, (uint32_t)a.pm.tstride * 4u);
     return (int)__builtin_amdgcn_raw_buffer_load_b32(Rt, 0, (t >> a.pm.log2P) * 4, 0);
   };
-  SliceRsrc R;
-  if constexpr (!PAGED) R = slice_views(sh, (uint32_t)a.capacity);
-  const int voff_v = 4 * (q * (32 * VB) + n * (2 * VB));
-  const bool lo = n >= 8;
-  const int c0 = chunk_idx * a.chunk;
-  // ---- one round of independent loads: query operands (registers for the specialized
-  //      slots, LDS for the others), tables, rows, first block
-  constexpr int NR = N1 + N4;
-  H8 qv[NR > 0 ? NR : 1];
+  constexpr int kRowW = 2 * KWL;  // record words a lane row covers (>= kw)
+  // ---- the replicated tables (entries through registers), and this workgroup's units
+  const DevCodebook* __restrict__ cb = a.cb;
+  static_assert(kPairTable <= kDecThreads && 16 * 32 <= kDecThreads, "one entry per thread");
+  constexpr int kU3 = 64 * 64 / kDecThreads, kU2 = 256 * 32 / kDecThreads;
+  const uint32_t lutv = tid < kPairTable ? cb->pair[tid] : 0u;
+  const uint2 t1v = *reinterpret_cast<const uint2*>(cb->oct1[(tid >> 5) & 15]);
+  uint32_t p3v[kU3], p4v[kU3];
+  uint2 q2v[kU2];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) qv[i].v = a.qb[(size_t)tile * kQB + i * 64 + lane];
-  uint4 qg[(NS * 64 + kThreads - 1) / kThreads];
-#pragma unroll
-  for (int u = 0; u < (NS * 64 + kThreads - 1) / kThreads; ++u) {
-    const int e = tid + kThreads * u;
-    qg[u] = e < NS * 64 ? a.qb[(size_t)tile * kQB + e] : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < kU3; ++u) {
+    const int e = tid + kDecThreads * u;
+    p3v[u] = cb->pair[20 + (e >> 6)];
+    p4v[u] = cb->pair[84 + (e >> 4)];
   }
-  uint32_t lutv[(kPairTable + kThreads - 1) / kThreads];
 #pragma unroll
-  for (int u = 0; u < (kPairTable + kThreads - 1) / kThreads; ++u) {
-    const int e = tid + kThreads * u;
-    lutv[u] = e < kPairTable ? a.cb->pair[e] : 0u;
-  }
-  static_assert(kThreads == 512, "one byte-table entry per thread");
-  uint4 tabv;
-  if (tid < 256) tabv = *reinterpret_cast<const uint4*>(a.cb->oct1[tid]);
-  else tabv = make_uint4(a.cb->quad2[tid - 256][0], a.cb->quad2[tid - 256][1], 0u, 0u);
-  const int len_ld = a.seq_len[seq];
-  const float xs = a.tile_xs[tile];
-  DecBlock<VB, KWL> blk;
-  int pg_next = 0;
-  {
-    const int t_first = c0 + kBlk * wave;
-    if constexpr (PAGED) {
-      dec_load<VB, KWL>(blk, page_views(__builtin_amdgcn_readfirstlane(page_of(t_first))), t_first & (a.pm.P - 1),
-                        kw, lane, voff_v);
-      pg_next = page_of(t_first + kBlk * kWaves);
-    } else {
-      dec_load<VB, KWL>(blk, R, t_first, kw, lane, voff_v);
+  for (int u = 0; u < kU2; ++u) q2v[u] = *reinterpret_cast<const uint2*>(cb->quad2[(tid + kDecThreads * u) >> 5]);
+  if (wave == 0) {
+    // U = all units; this workgroup's range [u0, u1); the first sequence b with units at
+    // or past u0 and P = the units before it
+    long long U = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+      const int b = b0 + lane;
+      long long x = b < a.batch ? (long long)tps * seq_blocks(a.seq_len, b, a.max_len, a.win, a.n_sink, a.n_recent) : 0;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+      U += x;
+    }
+    const long long u0 = (long long)wg * U / G, u1 = (long long)(wg + 1) * U / G;
+    long long P = 0, Ps = 0;
+    int bs = -1;
+    for (int b0 = 0; b0 < a.batch && bs < 0; b0 += 64) {
+      const int b = b0 + lane;
+      const long long x =
+          b < a.batch ? (long long)tps * seq_blocks(a.seq_len, b, a.max_len, a.win, a.n_sink, a.n_recent) : 0;
+      long long incl = x;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const long long y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      incl += P;
+      const unsigned long long hit = __ballot(b < a.batch && incl > u0);
+      if (hit) {
+        const int f = __ffsll((long long)hit) - 1;
+        bs = b0 + f;
+        Ps = __shfl(incl - x, f);
+      }
+      P = __shfl(incl, 63);
+    }
+    if (lane == 0) {
+      S.sk_u0 = u0;
+      S.sk_u1 = u1;
+      S.sk_P = Ps;
+      S.sk_b = bs;
     }
   }
+  if (tid < kPairTable) S.u.t.lut[tid] = lutv;
+  if (tid < 16 * 32) S.u.t.t1[tid >> 5][tid & 31] = t1v;
 #pragma unroll
-  for (int u = 0; u < (kPairTable + kThreads - 1) / kThreads; ++u) {
-    const int e = tid + kThreads * u;
-    if (e < kPairTable) S.lut[e] = lutv[u];
+  for (int u = 0; u < kU3; ++u) {
+    const int e = tid + kDecThreads * u;
+    S.u.t.p3[e >> 6][e & 63] = p3v[u];
+    S.u.t.p4[e >> 4][e & 15] = p4v[u];
   }
-  if (tid < 256) S.oct1[tid] = tabv;
-  else S.quad2[tid - 256] = make_uint2(tabv.x, tabv.y);
 #pragma unroll
-  for (int u = 0; u < (NS * 64 + kThreads - 1) / kThreads; ++u) {
-    const int e = tid + kThreads * u;
-    if (e < NS * 64) (&S.qb[0][0][0])[e] = qg[u];
-  }
-  if (tid < 8) {
-    int L;
-    S.row_id[tid] = tile_row<8>(a, seq, h, tr, tid, len_ld, &L);
-    S.row_len[tid] = L;
+  for (int u = 0; u < kU2; ++u) {
+    const int e = tid + kDecThreads * u;
+    S.u.t.q2[e >> 5][e & 31] = q2v[u];
   }
   __syncthreads();
-  // every present row of a decode tile has the sequence's length
-  int tile_len = 0;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) tile_len = max(tile_len, S.row_len[r]);
-  if (c0 >= tile_len) return;  // no cached token of this tile in this split
-  const int c1 = min(c0 + a.chunk, tile_len);
-  const int lo_vis = a.win ? a.n_sink : 0;  // sink positions read the fp16 buffers
-  constexpr int kStep = kBlk * kWaves;
-  const int my_row = lo ? 15 - n : n;
-  DecWave& W = S.u.w[wave];
+  constexpr int kStep = kBlk * kDecWaves;
   const char* sb = reinterpret_cast<const char*>(&S);
-  int st[KWL];
+  const uint8_t* sb8 = reinterpret_cast<const uint8_t*>(sb);
+  const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+  float* const slots = reinterpret_cast<float*>(&S.w[0]);  // [8][8][kD] in the wave areas (epilogue)
+  DecWave& W = S.w[wave];
+
+  // ---- the segments: blocks [bb, be) of row tile `tile`, one partial each. The position
+  //      (next unit, sequence, units before it) lives in the shared block between segments.
+  auto rfl64 = [](long long x) {
+    const int lo32 = __builtin_amdgcn_readfirstlane((int)(x & 0xFFFFFFFFll));
+    const int hi32 = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+    return (long long)(((unsigned long long)(unsigned)hi32 << 32) | (unsigned)lo32);
+  };
+  for (;;) {
+    // the arguments the segment set-up reads are loaded again here rather than held in
+    // registers across the main loop
+    KArgs* kap = ka0;
+    asm volatile("" : "+s"(kap));
+    const AttnArgs& A = *(const AttnArgs*)kap;
+    // the lane's constants, from an opaque copy of the thread index: derived again for each
+    // segment rather than held in registers across the segment loop
+    int tid_v = threadIdx.x;
+    asm volatile("" : "+v"(tid_v));
+    const int tid = tid_v, lane = tid & 63, q = lane >> 4, n = lane & 15;
+    const int voff_v = 4 * (q * (32 * VB) + n * (2 * VB));
+    const int kvo = 4 * ((lane / kRowW) * kw + lane % kRowW);
+    const bool lo = n >= 8;
+    const int lo_vis = A.win ? A.n_sink : 0;  // sink positions read the fp16 buffers
+    const int my_row = lo ? 15 - n : n;
+    const int kst = (lane / kRowW) * kKPitch + lane % kRowW;  // LDS word of the lane's first key word
+    // A-row n of the two 16-token halves: token tau0 and tau0 + 4
+    const int tau0 = 8 * (n >> 2) + (n & 3);
+    const uint32_t ktile_off = (uint32_t)(reinterpret_cast<const char*>(W.ktile) - sb);
+    const uint32_t row0 = ktile_off + 4u * (uint32_t)(tau0 * kKPitch);  // byte offset of token tau0's record
+    constexpr uint32_t kHalf = 4u * 4u * kKPitch;                       // token tau0 + 4
+    DecLanes DL;
+    DL.l8 = (uint32_t)(lane & 31) << 3;
+    DL.l4 = (uint32_t)lane << 2;
+    DL.l4_16 = (uint32_t)(lane & 15) << 2;
+    // this lane's key norms: knt[g][8q .. 8q + 7]
+    const uint32_t nq_off = (uint32_t)(reinterpret_cast<const char*>(&W.knt[0][8 * q]) - sb);
+    auto knorm4 = [&](int g, int hf) { return *reinterpret_cast<const float4*>(sb + nq_off + g * (kBlk * 4) + 16 * hf); };
+    long long u = rfl64(S.sk_u0);
+    const long long u_end = rfl64(S.sk_u1);
+    if (u >= u_end) break;
+    long long Pb = rfl64(S.sk_P);
+    int b = __builtin_amdgcn_readfirstlane(S.sk_b);
+    int nb = seq_blocks(A.seq_len, b, A.max_len, A.win, A.n_sink, A.n_recent);
+    while (nb == 0) nb = seq_blocks(A.seq_len, ++b, A.max_len, A.win, A.n_sink, A.n_recent);  // (no units)
+    const int tis = (int)(u - Pb) / nb;  // (the units of one sequence fit in 31 bits)
+    const int tile = b * tps + tis;
+    const long long Ut = Pb + (long long)tis * nb;
+    const int bb = (int)(u - Ut);
+    const int be = (int)min((long long)nb, u_end - Ut);
+    u = Ut + be;
+    if (be == nb && tis == tps - 1) {
+      Pb += (long long)tps * nb;
+      ++b;
+    }
+    int tr;
+    tile_coords(A, tile, &seq, &h, &tr);
+    const DevHead* __restrict__ hp = A.heads + h;
+    SliceRsrc R;
+    if constexpr (!PAGED) R = slice_views_of(A, (size_t)seq * A.n_kv + h, (uint32_t)A.capacity);
+    const int c0 = bb * kBlk;
+    // one round of independent loads: query operands (to LDS), rows, the first block
+    static_assert(NS * 64 <= kDecThreads, "one query operand per thread");
+    const uint4 qg = tid < NS * 64 ? A.qb[(size_t)tile * kQB + tid] : make_uint4(0, 0, 0, 0);
+    const int len_ld = A.seq_len[seq];
+    const float xs = A.tile_xs[tile];
+    DecBlock<VB, KWL> blk;
+    int pg_next = 0;
+    {
+      const int t_first = c0 + kBlk * wave;
+      if constexpr (PAGED) {
+        const SliceRsrc R0 = page_views(__builtin_amdgcn_readfirstlane(page_of(t_first)));
+        dec_load_k<VB, KWL>(blk, R0, t_first & (A.pm.P - 1), kw, lane, kvo);
+        dec_load_v<VB, KWL>(blk, R0, t_first & (A.pm.P - 1), voff_v);
+        pg_next = page_of(t_first + kBlk * kDecWaves);
+      } else {
+        dec_load_k<VB, KWL>(blk, R, t_first, kw, lane, kvo);
+        dec_load_v<VB, KWL>(blk, R, t_first, voff_v);
+      }
+    }
+    if (tid < NS * 64) (&S.qb[0][0][0])[tid] = qg;
+    if (tid < 8) {
+      int L;
+      S.row_id[tid] = tile_row<8>(A, seq, h, tr, tid, len_ld, &L);
+      S.row_len[tid] = L;
+    }
+    __syncthreads();  // (every thread has read the position)
+    if (tid == 0) {
+      S.sk_u0 = u;
+      S.sk_P = Pb;
+      S.sk_b = b;
+      S.sk_tile = tile;
+    }
+    // every present row of a decode tile has the sequence's length (c0 lies inside it)
+    int tile_len = 0;
 #pragma unroll
-  for (int i = 0; i < KWL; ++i) {
-    const int lw = lane + 64 * i;
-    st[i] = lw < kBlk * kw ? (lw / kw) * kKPitch + lw % kw : kKPitch - 1;
-  }
-  // A-row n of the two 16-token halves: token tau0 and tau0 + 4
-  const int tau0 = 8 * (n >> 2) + (n & 3);
-  const uint32_t ktile_off = (uint32_t)(reinterpret_cast<const char*>(W.ktile) - sb);
-  const uint32_t row0 = ktile_off + 4u * (uint32_t)(tau0 * kKPitch);  // byte offset of token tau0's record
-  constexpr uint32_t kHalf = 4u * 4u * kKPitch;                       // token tau0 + 4
-  const uint32_t lut_off = (uint32_t)(reinterpret_cast<const char*>(S.lut) - sb);
+    for (int r = 0; r < 8; ++r) tile_len = max(tile_len, S.row_len[r]);
+    const int c1 = min(be * kBlk, tile_len);
   const int nkb = hp->nkb;
   const int gl = hp->n_groups - 1;
   // rate-4 slots: the lane's field starts at word (bit >> 5) + q, shift bit & 31 (uniform)
@@ -2256,8 +2466,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     sh4[j] = bit & 31;
   }
   // other slots: per-lane LDS address << 5 | shift of the first code; one uniform word
-  // with the index width 2R (bits 0..3), the group (bits 4..5) and the table's byte
-  // offset in the shared block (bits 8..)
+  // with the index width 2R (bits 0..3), the group (bits 4..5), the copy stride shift
+  // (bits 6..9: 2 for the single pair tables of rates 1 and 2, 8 for p3, 6 for p4) and
+  // the table's byte offset (bits 12..)
   constexpr int NG = NS - N1 - N4;
   uint32_t gko[NG > 0 ? NG : 1];
   uint32_t gpk[NG > 0 ? NG : 1];
@@ -2267,39 +2478,31 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const int rate = rg & 0xFF;
     const int bit = hp->kb_bit[N1 + N4 + i] + 8 * q * rate;
     gko[i] = ((row0 + 4u * (uint32_t)(bit >> 5)) << 5) | (uint32_t)(bit & 31);
-    gpk[i] = (uint32_t)(2 * rate) | (uint32_t)(rg >> 8) << 4 |
-             (lut_off + 4u * (uint32_t)(((1 << (2 * rate)) - 4) / 3)) << 8;
+    const uint32_t tb = rate == 3 ? kDecP3 : rate == 4 ? kDecP4 : 4u * (uint32_t)(((1 << (2 * rate)) - 4) / 3);
+    const uint32_t ts = rate == 3 ? 8u : rate == 4 ? 6u : 2u;
+    gpk[i] = (uint32_t)(2 * rate) | (uint32_t)(rg >> 8) << 4 | ts << 6 | tb << 12;
   }
-  // this lane's key norms: knt[g][8q .. 8q + 7]
-  const uint32_t nq_off = (uint32_t)(reinterpret_cast<const char*>(&W.knt[0][8 * q]) - sb);
-  auto knorm4 = [&](int g, int hf) { return *reinterpret_cast<const float4*>(sb + nq_off + g * (kBlk * 4) + 16 * hf); };
-  const uint8_t* sb8 = reinterpret_cast<const uint8_t*>(sb);
 
   floatx4 oacc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) oacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f, thr = -INFINITY;
-  const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
 
   for (int t0 = c0 + kBlk * wave; t0 < c1; t0 += kStep) {
     // ---- stage the key records and key norms; the value words and norms stay in registers
 #pragma unroll
-    for (int i = 0; i < KWL; ++i) W.ktile[st[i]] = blk.kr[i];
+    for (int i = 0; i < KWL; ++i) W.ktile[kst + i * (64 / kRowW) * kKPitch] = blk.kr[i];
     W.knt[2 * (lane & 1)][lane >> 1] = blk.kn.x;
     W.knt[2 * (lane & 1) + 1][lane >> 1] = blk.kn.y;
-    uint32_t vw[2 * VB];
-#pragma unroll
-    for (int i = 0; i < 2 * VB; ++i) vw[i] = blk.vw[i];
     W.vn[lane & 31] = blk.vn;  // (lanes l and l + 32 hold the same norm)
     __builtin_amdgcn_wave_barrier();
-    if (t0 + kStep < c1) {
-      if constexpr (PAGED) {  // (a 32-token block lies in one page: P is a multiple of 32)
-        dec_load<VB, KWL>(blk, page_views(__builtin_amdgcn_readfirstlane(pg_next)), (t0 + kStep) & (a.pm.P - 1), kw,
-                          lane, voff_v);
-        pg_next = page_of(t0 + 2 * kStep);
-      } else {
-        dec_load<VB, KWL>(blk, R, t0 + kStep, kw, lane, voff_v);
-      }
+    // the next block: key part now, value words after this block's products
+    // (a 32-token block lies in one page: P is a multiple of 32)
+    const bool more = t0 + kStep < c1;
+    const int t_next = PAGED ? (t0 + kStep) & (a.pm.P - 1) : t0 + kStep;
+    if (more) {
+      if constexpr (PAGED) dec_load_k<VB, KWL>(blk, page_views(__builtin_amdgcn_readfirstlane(pg_next)), t_next, kw, lane, kvo);
+      else dec_load_k<VB, KWL>(blk, R, t_next, kw, lane, kvo);
     }
     // ---- QK: lg[4 hf + e] = logit (high or low column part) of token 8q + 4 hf + e
     float lg[8];
@@ -2308,10 +2511,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
       for (int i = 0; i < N1; ++i) {
         H8 a0, a1;
-        a0.v = S.oct1[sb8[row0 + 4 * i + q]];
-        a1.v = S.oct1[sb8[row0 + kHalf + 4 * i + q]];
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qv[i].h, d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qv[i].h, d1, 0, 0, 0);
+        a0.h = dec_dequant8<1>(sb, DL, sb8[row0 + 4 * i + q]);
+        a1.h = dec_dequant8<1>(sb, DL, sb8[row0 + kHalf + 4 * i + q]);
+        H8 bq;
+        bq.v = S.qb[i][q][n];
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, bq.h, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, bq.h, d1, 0, 0, 0);
       }
       const float4 na = knorm4(0, 0), nb = knorm4(0, 1);
       lg[0] = na.x * d0[0]; lg[1] = na.y * d0[1]; lg[2] = na.z * d0[2]; lg[3] = na.w * d0[3];
@@ -2330,11 +2535,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         H8 a0, a1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          a0.u[k] = S.lut[84 + ((f0 >> (8 * k)) & 0xFFu)];
-          a1.u[k] = S.lut[84 + ((f1 >> (8 * k)) & 0xFFu)];
+          a0.u[k] = lds_u32(sb, kDecP4 + ((__builtin_amdgcn_ubfe(f0, 8 * k, 8) << 6) | DL.l4_16));
+          a1.u[k] = lds_u32(sb, kDecP4 + ((__builtin_amdgcn_ubfe(f1, 8 * k, 8) << 6) | DL.l4_16));
         }
-        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qv[N1 + j].h, d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qv[N1 + j].h, d1, 0, 0, 0);
+        H8 bq;
+        bq.v = S.qb[N1 + j][q][n];
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, bq.h, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, bq.h, d1, 0, 0, 0);
       }
       const float4 na = knorm4(gl, 0), nb = knorm4(gl, 1);
       lg[0] = fmaf(na.x, d0[0], lg[0]); lg[1] = fmaf(na.y, d0[1], lg[1]);
@@ -2348,12 +2555,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         const uint32_t* r = reinterpret_cast<const uint32_t*>(sb + (gko[i] >> 5));
         const uint32_t f0 = __builtin_amdgcn_alignbit(r[1], r[0], gko[i]);
         const uint32_t f1 = __builtin_amdgcn_alignbit(r[4 * kKPitch + 1], r[4 * kKPitch], gko[i]);
-        const uint32_t w2 = gpk[i] & 15u, lb = gpk[i] >> 8;
+        const uint32_t w2 = gpk[i] & 15u, ts = (gpk[i] >> 6) & 15u;
+        const uint32_t lb = (gpk[i] >> 12) + (ts == 8u ? DL.l4 : ts == 6u ? DL.l4_16 : 0u);
         H8 a0, a1, bq;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          a0.u[j] = lds_u32(sb, lb + (__builtin_amdgcn_ubfe(f0, w2 * j, w2) << 2));
-          a1.u[j] = lds_u32(sb, lb + (__builtin_amdgcn_ubfe(f1, w2 * j, w2) << 2));
+          a0.u[j] = lds_u32(sb, lb + (__builtin_amdgcn_ubfe(f0, w2 * j, w2) << ts));
+          a1.u[j] = lds_u32(sb, lb + (__builtin_amdgcn_ubfe(f1, w2 * j, w2) << ts));
         }
         bq.v = S.qb[N1 + N4 + i][q][n];
         const floatx4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, bq.h, z4, 0, 0, 0);
@@ -2470,17 +2678,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S, vfield<VB>(vw, t)), oacc[t], 0, 0, 0);
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dec_dequant8<VB>(sb, DL, vfield<VB>(blk.vw, t)), oacc[t], 0, 0, 0);
+    if (more) {
+      if constexpr (PAGED) {
+        dec_load_v<VB, KWL>(blk, page_views(__builtin_amdgcn_readfirstlane(pg_next)), t_next, voff_v);
+        pg_next = page_of(t0 + 2 * kStep);
+      } else {
+        dec_load_v<VB, KWL>(blk, R, t_next, voff_v);
+      }
+    }
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves
+  // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves into
+  //      eight pre-weighted slots in the wave areas, then one partial for the segment
   l_run += dpp_row_mirror(l_run);  // the two lanes of a row summed different tokens
   l_run = sum_over_q(l_run);
-  if (q == 0 && n < 8) {
-    S.om[wave][n] = m_ref;
-    S.ol[wave][n] = l_run;
-  }
+  // (lane indices again opaque: the merge's addresses stay in the epilogue)
+  int tid_x = tid;
+  asm volatile("" : "+v"(tid_x));
+  const int q_x = (tid_x >> 4) & 3, n_x = tid_x & 15;
   float vrow[8][4];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -2488,17 +2705,78 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
   }
   __syncthreads();  // every wave is done with its key tile
-  if (q < 2) {
+  if (q_x == 0 && n_x < 8) {
+    S.om[wave][n_x] = m_ref;
+    S.ol[wave][n_x] = l_run;
+  }
+  __syncthreads();
+  float wt[4];  // 2^(m_wave - M) of rows 4 (q_x & 1) + e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * (q_x & 1) + e;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, S.om[w][r]);
+    const float mw = S.om[wave][r];
+    wt[e] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+  }
+  if (wave >= 8 && q_x < 2) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float* dst = &S.u.slot[wave][4 * q + e][8 * n];
-      *reinterpret_cast<float4*>(dst) = make_float4(vrow[0][e], vrow[1][e], vrow[2][e], vrow[3][e]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(vrow[4][e], vrow[5][e], vrow[6][e], vrow[7][e]);
+      float* dst = slots + ((wave - 8) * 8 + 4 * q_x + e) * kD + 8 * n_x;
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(wt[e] * vrow[0][e], wt[e] * vrow[1][e], wt[e] * vrow[2][e], wt[e] * vrow[3][e]);
+      *reinterpret_cast<float4*>(dst + 4) =
+          make_float4(wt[e] * vrow[4][e], wt[e] * vrow[5][e], wt[e] * vrow[6][e], wt[e] * vrow[7][e]);
     }
   }
   __syncthreads();
-  write_partials(a, S, tid, 0, chunk_idx);
+  if (wave < 8 && q_x < 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float* dst = slots + (wave * 8 + 4 * q_x + e) * kD + 8 * n_x;
+      const float4 x0 = *reinterpret_cast<const float4*>(dst), x1 = *reinterpret_cast<const float4*>(dst + 4);
+      *reinterpret_cast<float4*>(dst) = make_float4(fmaf(wt[e], vrow[0][e], x0.x), fmaf(wt[e], vrow[1][e], x0.y),
+                                                    fmaf(wt[e], vrow[2][e], x0.z), fmaf(wt[e], vrow[3][e], x0.w));
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(fmaf(wt[e], vrow[4][e], x1.x), fmaf(wt[e], vrow[5][e], x1.y),
+                                                        fmaf(wt[e], vrow[6][e], x1.z), fmaf(wt[e], vrow[7][e], x1.w));
+    }
+  }
+  __syncthreads();
+  if (tid_x < 8 * (kD / 4)) {
+    const int r = tid_x >> 5, c4 = tid_x & 31;
+    const int id = S.row_id[r];
+    if (id >= 0) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, S.om[w][r]);
+      float l = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) {
+          const float mw = S.om[w][r];
+          l = fmaf((mw == -INFINITY) ? 0.f : exp2f(mw - M), S.ol[w][r], l);
+        }
+      }
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 x = *reinterpret_cast<const float4*>(slots + (i * 8 + r) * kD + 4 * c4);
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+      }
+      float* dst = a.partials + ((size_t)(wg + S.sk_tile) * 8 + r) * kPS;
+      *reinterpret_cast<float4*>(dst + 4 + 4 * c4) = acc;
+      if (c4 == 0) *reinterpret_cast<float4*>(dst) = make_float4(M, l, 0.f, 0.f);
+    }
+  }
+  __syncthreads();  // the next segment rewrites the wave areas, rows and query operands
+  }
 }
+
+
 
 // ============================================================================
 // Phase 2: per row, log-sum-exp merge of its chunk partials, then
@@ -2514,6 +2792,7 @@ struct MergeArgs {
   int64_t pos0;
   int32_t n_q, g, n_chunks, chunk, prefill, max_len;
   int32_t win, n_sink, n_recent;  // fp16 window: its split is the last slot
+  int32_t batch, n_kv, tiles_per_kv, n_tiles, sk_G;  // decode: the partials' segments (AttnArgs)
 };
 
 // Four workgroups (256 threads each) per row, one per quarter of the output coordinates:
@@ -2537,8 +2816,34 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   if (a.prefill) len = (int)(a.pos0 + row / a.n_q + 1);
   else len = min(max(a.seq_len[row / a.n_q], 0), a.max_len);
   const int len_p = a.win ? packed_end(len, a.n_sink, a.n_recent) : len;
-  const int nv = (len_p + a.chunk - 1) / a.chunk + a.win;  // packed splits, then the window's
-  auto slot = [&](int k) { return (a.win && k == nv - 1) ? a.n_chunks - 1 : k; };
+  // the row's partials: prefill, one per split of its row; decode, one per segment of the
+  // partials' workgroups on its row tile, then the window's
+  int nv, first = 0, tile = 0, r8 = 0, w0 = 0;
+  long long U = 0;
+  if (a.prefill) {
+    nv = (len_p + a.chunk - 1) / a.chunk;
+  } else {
+    const int seq = row / a.n_q, f = hq % a.g, tps = a.n_kv * a.tiles_per_kv;
+    tile = (seq * a.n_kv + hq / a.g) * a.tiles_per_kv + f / 8;
+    r8 = f & 7;
+    long long P;
+    sk_sums256(a.seq_len, a.batch, seq, tps, a.max_len, a.win, a.n_sink, a.n_recent, &U, &P);
+    const int nb = (len_p + 31) >> 5;
+    int nseg = 0;
+    if (nb > 0) {
+      const long long Ut = P + (long long)(tile - seq * tps) * nb;
+      w0 = sk_owner(Ut, a.sk_G, U);
+      first = w0 + tile;
+      nseg = sk_owner(Ut + nb - 1, a.sk_G, U) - w0 + 1;
+    }
+    nv = nseg + a.win;
+  }
+  auto part = [&](int k) -> const float* {
+    if (a.prefill) return a.partials + ((size_t)row * a.n_chunks + k) * kPS;
+    const int sg = (a.win && k == nv - 1) ? a.sk_G + a.n_tiles + tile : first + k;
+    return a.partials + ((size_t)sg * 8 + r8) * kPS;
+  };
+  auto live = [&](int k) { return a.prefill || (a.win && k == nv - 1) || sk_live(w0 + k, a.sk_G, U); };
   // inverse rotation operand: thread (output oi of this quarter, eighth e) holds
   // Pi_V^T[oi][16 e .. + 15] (none for a Hadamard Pi_V, applied as a transform by the
   // first quarter alone)
@@ -2555,7 +2860,6 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) pvt[j][u] = (had || qo >= 4) ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
   }
-  const float* pp = a.partials + (size_t)row * a.n_chunks * kPS;
   float mk[kMergeRegs], lk[kMergeRegs];
   float4 xk[kMergeRegs];
 #pragma unroll
@@ -2564,17 +2868,18 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
     mk[u] = -INFINITY;
     lk[u] = 0.f;
     xk[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < nv) {
-      const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)slot(k) * kPS);
+    if (k < nv && live(k)) {
+      const float2 ml = *reinterpret_cast<const float2*>(part(k));
       mk[u] = ml.x;
       lk[u] = ml.y;
-      xk[u] = *reinterpret_cast<const float4*>(pp + (size_t)slot(k) * kPS + 4 + 4 * c4);
+      xk[u] = *reinterpret_cast<const float4*>(part(k) + 4 + 4 * c4);
     }
   }
   float ms = -INFINITY;
 #pragma unroll
   for (int u = 0; u < kMergeRegs; ++u) ms = fmaxf(ms, mk[u]);
-  for (int k = ks + 8 * kMergeRegs; k < nv; k += 8) ms = fmaxf(ms, pp[(size_t)slot(k) * kPS]);
+  for (int k = ks + 8 * kMergeRegs; k < nv; k += 8)
+    if (live(k)) ms = fmaxf(ms, part(k)[0]);
   if (c4 == 0) sm[ks] = ms;
   __syncthreads();
   float M = sm[0];
@@ -2592,9 +2897,10 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
       acc.w = fmaf(w, xk[u].w, acc.w);
       l = fmaf(w, lk[u], l);
     }
-    for (int k = ks + 8 * kMergeRegs; k < nv; k += 8) {  // more than 32 splits
-      const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)slot(k) * kPS);
-      const float4 x = *reinterpret_cast<const float4*>(pp + (size_t)slot(k) * kPS + 4 + 4 * c4);
+    for (int k = ks + 8 * kMergeRegs; k < nv; k += 8) {  // more than 128 partials
+      if (!live(k)) continue;
+      const float2 ml = *reinterpret_cast<const float2*>(part(k));
+      const float4 x = *reinterpret_cast<const float4*>(part(k) + 4 + 4 * c4);
       const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
       acc.x = fmaf(w, x.x, acc.x);
       acc.y = fmaf(w, x.y, acc.y);
@@ -2666,6 +2972,7 @@ struct MergeTileArgs {
   int64_t pos0;
   int32_t n_q, g, n_kv, tiles_per_kv, n_tok, n_chunks, chunk, prefill, max_len, seq;
   int32_t win, n_sink, n_recent;  // fp16 window: its split is the last slot
+  int32_t batch, n_tiles, sk_G;   // decode: the partials' segments (AttnArgs)
 };
 
 __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
@@ -2700,6 +3007,22 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) pvt[j][u] = (had || qo >= 4) ? make_float4(0.f, 0.f, 0.f, 0.f) : pt[u];
   }
+  // decode: the partials of this row tile, one per segment of the partials' workgroups on
+  // it, then the window's
+  int first = 0, nseg = 0, w0 = 0;
+  long long U = 0;
+  if (!a.prefill) {
+    const int tps = a.n_kv * a.tiles_per_kv;
+    long long P;
+    sk_sums256(a.seq_len, a.batch, seq, tps, a.max_len, a.win, a.n_sink, a.n_recent, &U, &P);
+    const int nb = seq_blocks(a.seq_len, seq, a.max_len, a.win, a.n_sink, a.n_recent);
+    if (nb > 0) {
+      const long long Ut = P + (long long)(tile - seq * tps) * nb;
+      w0 = sk_owner(Ut, a.sk_G, U);
+      first = w0 + tile;
+      nseg = sk_owner(Ut + nb - 1, a.sk_G, U) - w0 + 1;
+    }
+  }
   // row r of the tile: global row id (-1 if absent) and visible length
   const int r = tid >> 5, c4 = tid & 31;
   const int f = tr * 8 + r;
@@ -2718,10 +3041,13 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
   if (id >= 0) {
-    const float* pp = a.partials + (size_t)id * a.n_chunks * kPS;
-    const int len_p = a.win ? packed_end(len, a.n_sink, a.n_recent) : len;
-    const int nv = min(a.n_chunks, (len_p + a.chunk - 1) / a.chunk + a.win);  // packed, then the window
-    auto slot = [&](int k) { return (a.win && k == nv - 1) ? a.n_chunks - 1 : k; };
+    const int nv = a.prefill ? min(a.n_chunks, (len + a.chunk - 1) / a.chunk) : nseg + a.win;
+    auto part = [&](int k) -> const float* {
+      if (a.prefill) return a.partials + ((size_t)id * a.n_chunks + k) * kPS;
+      const int sg = (a.win && k == nv - 1) ? a.sk_G + a.n_tiles + tile : first + k;
+      return a.partials + ((size_t)sg * 8 + r) * kPS;
+    };
+    auto live = [&](int k) { return a.prefill || (a.win && k == nv - 1) || sk_live(w0 + k, a.sk_G, U); };
     float mk[kMergeTileChunks], lk[kMergeTileChunks];
     float4 xk[kMergeTileChunks];
     float M = -INFINITY;
@@ -2730,14 +3056,16 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
       mk[k] = -INFINITY;
       lk[k] = 0.f;
       xk[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < nv) {
-        const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)slot(k) * kPS);
+      if (k < nv && live(k)) {
+        const float2 ml = *reinterpret_cast<const float2*>(part(k));
         mk[k] = ml.x;
         lk[k] = ml.y;
-        xk[k] = *reinterpret_cast<const float4*>(pp + (size_t)slot(k) * kPS + 4 + 4 * c4);
+        xk[k] = *reinterpret_cast<const float4*>(part(k) + 4 + 4 * c4);
       }
       M = fmaxf(M, mk[k]);
     }
+    for (int k = kMergeTileChunks; k < nv; ++k)
+      if (live(k)) M = fmaxf(M, part(k)[0]);
     if (M != -INFINITY) {
 #pragma unroll
       for (int k = 0; k < kMergeTileChunks; ++k) {
@@ -2747,6 +3075,17 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
         acc.z = fmaf(w, xk[k].z, acc.z);
         acc.w = fmaf(w, xk[k].w, acc.w);
         L = fmaf(w, lk[k], L);
+      }
+      for (int k = kMergeTileChunks; k < nv; ++k) {  // more partials than registers
+        if (!live(k)) continue;
+        const float2 ml = *reinterpret_cast<const float2*>(part(k));
+        const float4 x = *reinterpret_cast<const float4*>(part(k) + 4 + 4 * c4);
+        const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+        acc.x = fmaf(w, x.x, acc.x);
+        acc.y = fmaf(w, x.y, acc.y);
+        acc.z = fmaf(w, x.z, acc.z);
+        acc.w = fmaf(w, x.w, acc.w);
+        L = fmaf(w, ml.y, L);
       }
     }
   }
@@ -2932,11 +3271,10 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   return ok();
 }
 
-int auto_chunk(int64_t max_len, int64_t tiles) {
+int auto_chunk(int64_t max_len, int64_t tiles, int64_t kRound) {
   // one round of workgroups (one per compute unit), at least 4 splits per row tile so
-  // that ragged batches balance; splits of whole rounds of the main loop (8 waves x
-  // 32 tokens)
-  constexpr int64_t kRound = kBlk * kWaves;
+  // that ragged batches balance; splits of whole rounds of the main loop (waves x 32
+  // tokens: 16 waves for the decode tiles, 8 for the prefill tiles)
   int64_t target = std::max<int64_t>(4, kTargetWG / std::max<int64_t>(1, tiles));
   target = std::min<int64_t>(kMaxChunks, target);
   int64_t ch = (max_len + target - 1) / target;
@@ -2953,9 +3291,15 @@ size_t attn_qb_bytes(int64_t n_tiles, int rt) {
 size_t attn_ws_bytes(int64_t rows, int64_t n_chunks, size_t qb_bytes) {
   return qb_bytes + (size_t)rows * n_chunks * kPS * 4;
 }
+// decode: one 8-row partial per (workgroup, tile) segment, w + t < sk_G + n_tiles, then
+// one per tile for the window's split
+size_t decode_ws_bytes(int64_t n_tiles, int sk_G, size_t qb_bytes) {
+  return qb_bytes + (size_t)(sk_G + 2 * n_tiles) * 8 * kPS * 4;
+}
 
 struct AttnLaunch {
   int64_t rows;
+  int sk_G;                // decode: partials workgroups (each an equal share of the batch's units)
   int rt;                  // rows per partials tile: 8 (decode) or 16 (prefill)
   int tiles_per_kv;        // partials / query-rotation tiles
   int n_tiles;
@@ -2986,6 +3330,9 @@ void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnA
   aa.tiles_per_kv = L.tiles_per_kv;
   aa.chunk = L.chunk;
   aa.n_chunks = L.n_chunks;
+  aa.batch = (int32_t)(L.rows / p->n_q);
+  aa.n_tiles = L.n_tiles;
+  aa.sk_G = L.sk_G;
   aa.pm = page_map(c);
   aa.nkb_max = 0;
   for (int h = 0; h < p->n_kv; ++h) aa.nkb_max = std::max(aa.nkb_max, (int32_t)p->heads[(size_t)layer * p->n_kv + h].nkb);
@@ -3008,10 +3355,10 @@ gtq_status launch_qrot(AttnArgs& aa, const AttnLaunch& L, const float* q, float 
 template <int VB, int KWL>
 void launch_decode(dim3 grid, int n1, int n4, const AttnArgs& aa, hipStream_t stream) {
   if (aa.pm.table) {  // paged caches: every slot through the generic path
-    hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, 0, 0, true>), grid, dim3(kThreads), 0, stream, aa);
+    hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, 0, 0, true>), grid, dim3(kDecThreads), 0, stream, aa);
     return;
   }
-#define GTQ_DEC(A, B) hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, A, B, false>), grid, dim3(kThreads), 0, stream, aa)
+#define GTQ_DEC(A, B) hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, A, B, false>), grid, dim3(kDecThreads), 0, stream, aa)
   switch (n1 * 4 + n4) {
     case 0: GTQ_DEC(0, 0); break;
     case 1: GTQ_DEC(0, 1); break;
@@ -3035,6 +3382,7 @@ gtq_status launch_partials(const gtq_plan* p, int layer, AttnArgs& aa, const Att
   dim3 grid(L.n_chunks - aa.win, L.n_tiles);  // (the window's split comes from its own launch)
   const bool wide = p->k_words > 8;  // key words per lane: 4 (k_words <= 8) or 8
   if (L.rt == 8) {
+    grid = dim3((unsigned)L.sk_G);
     const int n1 = p->layer_n1[layer], n4 = p->layer_n4[layer];
 #define GTQ_DECV(VB) \
   if (wide) launch_decode<VB, 8>(grid, n1, n4, aa, stream); else launch_decode<VB, 4>(grid, n1, n4, aa, stream)
@@ -3090,7 +3438,10 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
                         hipStream_t stream, const gtq_window_view* w = nullptr) {
   const float* vrot_t = p->d_rot + p->heads[(size_t)layer * p->n_kv].vrot_t_off;
   const float* partials = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + L.qb_bytes);
-  if (L.n_chunks <= kMergeTileChunks) {  // one workgroup per row tile
+  // one workgroup per row tile when few partials per row are expected (prefill: at most
+  // kMergeTileChunks splits; decode: about sk_G / n_tiles + 2 segments per tile)
+  const bool tile_merge = prefill ? L.n_chunks <= kMergeTileChunks : L.sk_G <= 4 * L.n_tiles;
+  if (tile_merge) {
     MergeTileArgs mt{p->d_heads + (size_t)layer * p->n_kv, vrot_t, partials, seq_len, out, pos0, p->n_q, p->n_q / p->n_kv, p->n_kv, L.merge_tiles_per_kv,
                      (int32_t)(L.rows / p->n_q), L.n_chunks, L.chunk, prefill, max_len, 0};
     if (w) {
@@ -3098,6 +3449,9 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
       mt.n_sink = w->n_sink;
       mt.n_recent = w->n_recent;
     }
+    mt.batch = (int32_t)(L.rows / p->n_q);
+    mt.n_tiles = L.n_tiles;
+    mt.sk_G = L.sk_G;
     hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.merge_n_tiles, merge_quarters(L.merge_n_tiles)),
                        dim3(256), 0, stream, mt);
   } else {  // one workgroup per row
@@ -3108,6 +3462,11 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
       ma.n_sink = w->n_sink;
       ma.n_recent = w->n_recent;
     }
+    ma.batch = (int32_t)(L.rows / p->n_q);
+    ma.n_kv = p->n_kv;
+    ma.tiles_per_kv = L.merge_tiles_per_kv;
+    ma.n_tiles = L.n_tiles;
+    ma.sk_G = L.sk_G;
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows, merge_quarters(L.rows)), dim3(256), 0, stream, ma);
   }
   hipError_t e = hipGetLastError();
@@ -3138,6 +3497,12 @@ gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out) {
       delete p;
       return hip_fail(e, "gtq_plan_create: no HIP device");
     }
+    int n_cu = 0;
+    if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, p->device)) != hipSuccess) {
+      delete p;
+      return hip_fail(e, "gtq_plan_create: device query");
+    }
+    p->n_cu = std::max(1, n_cu);
     const size_t hb = p->heads.size() * sizeof(DevHead);
     const size_t rb = p->rot.size() * sizeof(float);
     const size_t sb = p->rsplit.size() * sizeof(uint16_t);
@@ -3239,12 +3604,20 @@ static bool decode_shape(const gtq_plan* p, int32_t batch, int64_t max_len, int3
   L->merge_tiles_per_kv = L->tiles_per_kv;
   L->merge_n_tiles = L->n_tiles;
   L->qb_bytes = attn_qb_bytes(L->n_tiles, L->rt);
-  L->chunk = chunk ? chunk : auto_chunk(max_len, L->n_tiles);
+  L->chunk = chunk ? chunk : auto_chunk(max_len, L->n_tiles, kBlk * kDecWaves);
   L->n_chunks = (int)std::max<int64_t>(1, (max_len + L->chunk - 1) / L->chunk);
   if (L->n_chunks > kMaxChunks) {
     *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk too small (more than 256 splits per sequence)");
     return false;
   }
+  // partials workgroups: one per compute unit, or with an explicit chunk as many as the
+  // splits of a batch at max_len (chunk / 32 blocks each when every row has max_len)
+  const int64_t g_req = chunk ? (int64_t)L->n_tiles * L->n_chunks : (int64_t)p->n_cu;
+  if (g_req > (int64_t)1 << 20) {
+    *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk too small for this batch");
+    return false;
+  }
+  L->sk_G = (int)std::max<int64_t>(1, g_req);
   L->n_chunks += win;  // the fp16 window's split
   return true;
 }
@@ -3256,7 +3629,7 @@ gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64
   AttnLaunch L;
   gtq_status st;
   if (!decode_shape(plan, batch, max_len, chunk, &L, &st, "gtq_decode_workspace_bytes")) return st;
-  *out = attn_ws_bytes(L.rows, L.n_chunks, L.qb_bytes);
+  *out = decode_ws_bytes(L.n_tiles, L.sk_G, L.qb_bytes);
   return ok();
 }
 
@@ -3270,7 +3643,7 @@ static gtq_status decode_check(const gtq_plan* plan, int32_t layer, const gtq_ca
   if (!ws) return fail(GTQ_EINVAL, std::string(fn) + ": workspace is NULL");
   if (max_len > cache->capacity) return fail(GTQ_ECAPACITY, std::string(fn) + ": max_len > capacity");
   if (!decode_shape(plan, cache->batch, max_len, chunk, L, &st, fn, win)) return st;
-  if (ws_bytes < attn_ws_bytes(L->rows, L->n_chunks, L->qb_bytes))
+  if (ws_bytes < decode_ws_bytes(L->n_tiles, L->sk_G, L->qb_bytes))
     return fail(GTQ_ECAPACITY, std::string(fn) + ": workspace too small");
   return GTQ_OK;
 }
@@ -3401,7 +3774,7 @@ static bool prefill_shape(const gtq_plan* p, int64_t pos0, int64_t n_tok, int32_
   L->merge_tiles_per_kv = (int)((n_tok * g + 7) / 8);
   L->merge_n_tiles = p->n_kv * L->merge_tiles_per_kv;
   L->qb_bytes = attn_qb_bytes(L->n_tiles, L->rt);
-  L->chunk = chunk ? chunk : auto_chunk(total, L->n_tiles);
+  L->chunk = chunk ? chunk : auto_chunk(total, L->n_tiles, kBlk * kWaves);
   L->n_chunks = (int)((total + L->chunk - 1) / L->chunk);
   if (L->n_chunks > kMaxChunks) {
     *st = fail(GTQ_EINVAL, std::string(fn) + ": chunk too small (more than 256 splits per sequence)");
@@ -3504,7 +3877,7 @@ gtq_status gtq_decode_window_workspace_bytes(const gtq_plan* plan, int32_t batch
   AttnLaunch L;
   gtq_status st;
   if (!decode_shape(plan, batch, max_len, chunk, &L, &st, "gtq_decode_window_workspace_bytes", 1)) return st;
-  *out = attn_ws_bytes(L.rows, L.n_chunks, L.qb_bytes);
+  *out = decode_ws_bytes(L.n_tiles, L.sk_G, L.qb_bytes);
   return ok();
 }
 

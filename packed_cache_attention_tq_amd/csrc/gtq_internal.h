@@ -77,6 +77,7 @@ struct gtq_plan {
   gtq::DevCodebook cb{};
   // device copies (null for host-only plans)
   int device = -1;
+  int n_cu = 256;                       // compute units of the device (decode partials workgroups)
   gtq::DevHead* d_heads = nullptr;
   float* d_rot = nullptr;
   uint16_t* d_rsplit = nullptr;

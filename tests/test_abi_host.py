@@ -187,10 +187,13 @@ def test_error_paths(lib):
     assert b"multiple of 32" in lib.gtq_last_error()
     assert lib.gtq_decode_workspace_bytes(p.handle, 2, 1000, 64, C.byref(ws)) == 0
     # the rotated-query operand of each tile (batch x KV heads x ceil(g / 8) tiles of
-    # 8 KB) and one range factor per tile (padded to 16 bytes), then rows * chunks
-    # partial records of 132 floats (m, l, 2 pad, acc[128])
-    rows, chunks, tiles = 2 * 4, (1000 + 63) // 64, 2 * 2
-    exp = tiles * 8192 + (tiles * 4 + 15) // 16 * 16 + rows * chunks * 132 * 4
+    # 8 KB) and one range factor per tile (padded to 16 bytes), then 8-row partials of
+    # 132 floats (m, l, 2 pad, acc[128]): one per (workgroup, tile) segment, i.e. G +
+    # tiles - 1 of them with G = tiles * chunks workgroups for an explicit chunk, and one
+    # per tile for the window's split
+    chunks, tiles = (1000 + 63) // 64, 2 * 2
+    n_wg = tiles * chunks
+    exp = tiles * 8192 + (tiles * 4 + 15) // 16 * 16 + (n_wg + 2 * tiles) * 8 * 132 * 4
     assert ws.value == exp
     assert lib.gtq_decode_workspace_bytes(p.handle, 1, 100000, 32, C.byref(ws)) == 1
     assert b"256 splits" in lib.gtq_last_error()

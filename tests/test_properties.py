@@ -202,7 +202,8 @@ def test_packed_decode_splits_over_heads_and_chunks(seed, n, g, budget, v_bits, 
     for h in range(g):
         _, oh = O.decode_attention(plan, q[h:h + 1], rec["k_words"], rec["k_norms"], rec["v_words"],
                                    rec["v_norms"], scale)
-        assert np.allclose(oh[0], out[h], rtol=1e-12, atol=1e-14)
+        # (a different BLAS blocking moves logits of size ~100 by an ulp: compare at the scale of the outputs)
+        assert np.abs(oh[0] - out[h]).max() <= 1e-11 * max(1.0, np.abs(out).max())
     bounds = sorted({0, n, *[c for c in cuts if c < n]})
     ms, ls, accs = [], [], []
     for a, b in zip(bounds[:-1], bounds[1:]):
@@ -216,4 +217,4 @@ def test_packed_decode_splits_over_heads_and_chunks(seed, n, g, budget, v_bits, 
     w = [np.exp(m - M) for m in ms]
     L = sum(wi * li for wi, li in zip(w, ls))
     merged = sum(wi[:, None] * ai for wi, ai in zip(w, accs)) / L[:, None]
-    assert np.allclose(merged, out, rtol=1e-11, atol=1e-13)
+    assert np.abs(merged - out).max() <= 1e-11 * max(1.0, np.abs(out).max())
