@@ -287,6 +287,23 @@ gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_
                            float softmax_scale, int32_t chunk, float* out, float* logits,
                            void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* gtq_decode_attn for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation
+ * and arguments without the workspace, which is a device array of 16 MiB inside the
+ * library instead (one copy per device, held until the process ends; its address is
+ * taken when a plan is created on that device). Calls no allocating routine. The plan's
+ * device must be current. Every call on a device shares that one array: calls that
+ * overlap on a device (other streams, other threads) race and give wrong results; calls
+ * ordered on one stream are safe. The array needs no initialisation (each call writes
+ * what it reads). Errors: those of gtq_decode_attn; ECAPACITY when the workspace that
+ * gtq_decode_workspace_bytes gives for (batch, max_len, chunk) exceeds 16 MiB (e.g.
+ * more than about 900 tiles of 8 query rows at the automatic split on 256 compute
+ * units); EINVAL when the plan's device is not current. */
+gtq_status gtq_decode_attn_static(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                  const float* q, const int32_t* seq_len, int64_t max_len,
+                                  float softmax_scale, int32_t chunk, float* out, float* logits,
+                                  void* hip_stream);
+
 /* The three phases of gtq_decode_attn, for callers that interleave other work between
  * them or time them separately; all three take the same (cache, max_len, chunk) and
  * workspace, ordered on one stream.

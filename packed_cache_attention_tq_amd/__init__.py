@@ -91,6 +91,8 @@ _SIGS = [
     ("gtq_decode_attn", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_void_p,
                                     C.c_int64, C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("gtq_decode_attn_static", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_void_p,
+                                           C.c_int64, C.c_float, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     ("gtq_decode_prepare", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_void_p, C.c_int64, C.c_float, C.c_int32, C.c_void_p,
                                        C.c_size_t, C.c_void_p]),
@@ -385,6 +387,21 @@ def gtq_decode_attn(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_
                                _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
                                _stream(stream))
     _check(st, "gtq_decode_attn")
+    return out
+
+
+def gtq_decode_attn_static(plan: Plan, layer: int, cache: PackedCache, q, seq_len, max_len: int, scale: float,
+                           out, chunk: int = 0, logits=None, stream=None):
+    """gtq_decode_attn on the library's static scratch (no workspace); `out` is the
+    caller's [batch][n_q][128] fp32 tensor."""
+    _decode_sizes(plan, cache, q, seq_len, max_len, logits)
+    _need(out, q.numel(), "out")
+    cv = cache.view()
+    st = lib().gtq_decode_attn_static(plan.handle, layer, C.byref(cv), _dev(q, torch.float32, "q"),
+                                      _dev(seq_len, torch.int32, "seq_len"), max_len, float(scale), chunk,
+                                      _dev(out, torch.float32, "out"), _dev(logits, torch.float32, "logits"),
+                                      _stream(stream))
+    _check(st, "gtq_decode_attn_static")
     return out
 
 

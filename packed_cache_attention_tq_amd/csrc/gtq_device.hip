@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "gtq_internal.h"
@@ -3474,6 +3475,28 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
   return ok();
 }
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of gtq_decode_attn_static: a device array of fixed size in the library
+// (each device holds its own copy until the process ends). Host code uses only the
+// address that hipGetSymbolAddress returns for it on each device, taken once per device
+// at plan creation with that device current.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+gtq_status scratch_init(int device) {
+  if (device < 0 || device >= kMaxScratchDevices) return fail(GTQ_EUNSUPPORTED, "gtq_plan_create: device index too large");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[device]) return ok();
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "gtq_plan_create: scratch address");
+  g_scratch_ptr[device] = ptr;
+  return ok();
+}
+
 }  // namespace
 
 // ============================================================================
@@ -3503,6 +3526,10 @@ gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out) {
       return hip_fail(e, "gtq_plan_create: device query");
     }
     p->n_cu = std::max(1, n_cu);
+    if ((st = scratch_init(p->device)) != GTQ_OK) {
+      delete p;
+      return st;
+    }
     const size_t hb = p->heads.size() * sizeof(DevHead);
     const size_t rb = p->rot.size() * sizeof(float);
     const size_t sb = p->rsplit.size() * sizeof(uint16_t);
@@ -3706,6 +3733,33 @@ gtq_status gtq_decode_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_
   if (st != GTQ_OK) return st;
   return gtq_decode_attn_merge(plan, layer, cache, seq_len, max_len, chunk, out, workspace, ws_bytes,
                                hip_stream);
+}
+
+gtq_status gtq_decode_attn_static(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                  const float* q, const int32_t* seq_len, int64_t max_len, float softmax_scale,
+                                  int32_t chunk, float* out, float* logits, void* hip_stream) {
+  const char* fn = "gtq_decode_attn_static";
+  gtq_status st;
+  if (!check_device_plan(plan, fn, &st)) return st;
+  if (!cache) return fail(GTQ_EINVAL, std::string(fn) + ": cache is NULL");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+    return fail(GTQ_EINVAL, std::string(fn) + ": the plan's device must be the current device");
+  AttnLaunch L;
+  if (!decode_shape(plan, cache->batch, max_len, chunk, &L, &st, fn)) return st;
+  const size_t need = decode_ws_bytes(L.n_tiles, L.sk_G, L.qb_bytes);
+  if (need > kScratchBytes)
+    return fail(GTQ_ECAPACITY, std::string(fn) + ": needs " + std::to_string(need) +
+                                   " bytes of workspace, more than the static scratch (" +
+                                   std::to_string(kScratchBytes) + ")");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    ws = (dev >= 0 && dev < kMaxScratchDevices) ? g_scratch_ptr[dev] : nullptr;
+  }
+  if (!ws) return fail(GTQ_EINVAL, std::string(fn) + ": no scratch address for this device");
+  return gtq_decode_attn(plan, layer, cache, q, seq_len, max_len, softmax_scale, chunk, out, logits, ws,
+                         kScratchBytes, hip_stream);
 }
 
 gtq_status gtq_decode_prepare(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
