@@ -809,6 +809,7 @@ inline int append_roles(int64_t n_token_heads) { return n_token_heads < 128 ? 3 
 // The waves merge through LDS into one partial per row.
 // ============================================================================
 
+constexpr float kPvLimit = 16384.f;  // p * nu_V <= 2^14 keeps the binary16 high parts finite
 constexpr int kWaves = 8;          // waves per partials workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPS = 132;           // partial record: m, l, 2 pad, acc[128] (16-byte aligned acc)
@@ -1535,13 +1536,37 @@ __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W,
   const float4 va = *reinterpret_cast<const float4*>(sb + vn_off);
   const float4 vb4 = *reinterpret_cast<const float4*>(sb + vn_off + 16);
   const float vn[8] = {va.x, va.y, va.z, va.w, vb4.x, vb4.y, vb4.z, vb4.w};
-  float pv[8];
+  float p[8], pv[8], pvm = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float p = (lg[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[j] - m_use);
-    l_run += p;
-    pv[j] = (p == 0.f) ? 0.f : p * vn[j];
+    p[j] = (lg[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[j] - m_use);
+    pv[j] = (p[j] == 0.f) ? 0.f : p[j] * vn[j];
+    pvm = fmaxf(pvm, pv[j]);
   }
+  // p * nu_V goes to binary16 high and low parts: a row where it passes 2^14 moves its
+  // reference up by the power of two that brings it back (an exact rescale of l, acc
+  // and this block's p; every lane takes part in the factor exchange)
+  pvm = max_over_q(pvm);
+  if (__any(pvm > kPvLimit)) {
+    int e = 0;
+    if (pvm > kPvLimit) frexpf(pvm / kPvLimit, &e);
+    const float f = ldexpf(1.f, -e);
+    m_run += (float)e;
+    l_run *= f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] *= f;
+      pv[j] *= f;
+    }
+#pragma unroll
+    for (int ee = 0; ee < 4; ++ee) {
+      const float fe = __shfl(f, 4 * q + ee);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) oacc[t][ee] *= fe;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) l_run += p[j];
   H8 ph, pl;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -2107,7 +2132,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 //   * masking only in blocks that straddle the visible range.
 // ============================================================================
 constexpr float kLazyT = 10.f;
-constexpr float kPvLimit = 16384.f;  // p * nu_V <= 2^14 keeps the binary16 high parts finite
 constexpr int kDecWaves = 16;        // one 1024-thread workgroup per compute unit
 constexpr int kDecThreads = 64 * kDecWaves;
 

@@ -370,6 +370,57 @@ def test_prefill_chunk(G, T):
     _say(f"  prefill chunk append ties={ties}")
 
 
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_binary16_operand_ranges(G, mode):
+    """Operands that leave the binary16 range unless rescaled: value norms near 1e5 (p *
+    nu_V above 65504 without the moved softmax reference) and a softmax scale of 2e4 on
+    keys shrunk by 1e-5 (scaled rotated queries above 16384 without the per-tile power
+    of two), against the oracle on the same records; decode (ragged batch, explicit and
+    automatic split) and causal prefill. Outputs are compared in units of the value scale
+    (divided by 1e4): the bar's absolute term is meant for values of order one, and an
+    output that cancels terms of order 1e5 carries their fp32 rounding."""
+    _say(f"case: binary16 operand ranges, {mode}")
+    n = 300
+    case = Case(21, 1, 2, 4, n, 128, 2, batch=2)
+    for h in range(case.H):
+        for b in range(2):
+            inp = case.inputs[0, h][b]
+            inp["k"] = (inp["k"] * 1e-5).astype(np.float32)
+            inp["v"] = (inp["v"] * 1e4).astype(np.float32)
+    plan = case.plan()
+    sc = 2e4
+    if mode == "decode":
+        lens = [n, 157]
+        cache = G.PackedCache(plan, 2, 320)
+        encs = [_encode(case, 0, b, lens[b]) for b in range(2)]
+        for b in range(2):
+            _upload_oracle_cache(case, cache, 0, b, lens[b], encs[b])
+        q = np.stack([case.q(0, b) for b in range(2)])
+        assert np.abs(q).max() * sc > 16384 * 4
+        for chunk in (64, 0):
+            out = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(np.array(lens, np.int32)), n, sc, chunk=chunk)
+            torch.cuda.synchronize()
+            for b in range(2):
+                _, ref = _oracle_decode(case, 0, b, lens[b], encs[b], q[b], sc)
+                assert np.abs(ref).max() > 1e3
+                assert_close(out[b].cpu().numpy() / 1e4, ref / 1e4, f"decode b{b} chunk={chunk}")
+    else:
+        n0, T = 240, 60
+        cache = G.PackedCache(plan, 1, 320)
+        enc = _encode(case, 0, 0, n0 + T)
+        _upload_oracle_cache(case, cache, 0, 0, n0 + T, enc)
+        rng = np.random.default_rng(21)
+        q = (rng.standard_normal((T, case.HQ, 128)) * 3).astype(np.float32)
+        out = G.gtq_prefill_attn(plan, 0, cache, _dev(q), 0, n0, sc, chunk=64)
+        torch.cuda.synchronize()
+        for h in range(case.H):
+            sl = slice(h * case.g, (h + 1) * case.g)
+            ref = O.prefill_attention(case.heads[0, h], q[:, sl], n0, enc[h]["k_words"], enc[h]["k_norms"],
+                                      enc[h]["v_words"], enc[h]["v_norms"], sc)
+            assert np.abs(ref).max() > 1e3
+            assert_close(out[:, sl].cpu().numpy() / 1e4, ref / 1e4, f"prefill out h{h}")
+
+
 def test_edge_cases(G):
     """Zero vectors (norm 0, codes 2^(b-1)), sequences of length 0 and 1, determinism."""
     _say("case: edge cases")
