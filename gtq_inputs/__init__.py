@@ -30,7 +30,7 @@ ROPE_BASE = 500000.0
 N_CALIB = 256
 
 # stream ids of the SeedSequence tuple
-S_SIGMA, S_CACHE_K, S_CACHE_V, S_DEC_Q, S_CAL_Q, S_CAL_K, S_LENGTHS, S_ROT = range(8)
+S_SIGMA, S_CACHE_K, S_CACHE_V, S_DEC_Q, S_CAL_Q, S_CAL_K, S_LENGTHS, S_ROT, S_QJL = range(9)
 
 HALF, INTERLEAVED = 0, 1
 
@@ -197,6 +197,11 @@ def head_rotations(cfg_seed: int, layer: int, kv_head: int, group_dims: list[int
     k_rots = [haar_rotation(d, rng) for d in group_dims]
     v_rot = hadamard_rotation(HEAD_DIM, rng) if v_hadamard else haar_rotation(HEAD_DIM, rng)
     return k_rots, v_rot
+
+
+def qjl_matrix(cfg_seed: int, layer: int, kv_head: int, m: int = HEAD_DIM) -> np.ndarray:
+    """The residual sketch's matrix of one (layer, KV head): m x 128 entries N(0, 1), fp32."""
+    return rng_for(cfg_seed, layer, kv_head, S_QJL).standard_normal((m, HEAD_DIM)).astype(np.float32)
 
 
 def ragged_lengths(cfg_seed: int, batch: int, lo: int, hi: int) -> np.ndarray:

@@ -19,8 +19,10 @@ Sources (cited as [short tag] in each function):
              01_turboquant_pipeline), left ("paper") column, box X:
              input (vector x of a head's K or V), rotate (random rotation /
              Hadamard), scalar-MSE (per-coordinate MSE scalar quantization with a
-             few centroids), residual, QJL (not used: TQ-MSE is the variant
-             without it).
+             few centroids), residual (r = x - x_hat: the MSE-optimal code is not
+             inner-product unbiased), QJL (a 1-bit sign sketch of the residual that
+             corrects the attention inner products; TQ-MSE is the variant without
+             it, TurboQuant-prod the one with it).
 
 Readings where the pages are silent (each also listed in the design notes):
   R1  RoPE pairing: half-split, block j = coordinates (j, j+64); interleaved
@@ -39,6 +41,15 @@ Readings where the pages are silent (each also listed in the design notes):
       result does without): the first n_sink positions and the last n_recent
       positions of a sequence attend through fp16 copies of their K and V (binary16,
       round to nearest even), every other position through the packed cache.
+  R23 QJL residual sketch (TurboQuant-prod): keys only (it corrects q . k); the
+      residual is r = k - k_hat in head coordinates, k_hat the TQ-MSE reconstruction of
+      the stored record (fp64); S is an m x 128 matrix of N(0,1) entries (m = 128, one
+      bit per coordinate), drawn per (layer, KV head) and passed in like the rotations;
+      the sketch stores sign(S r) (a zero projection counts as +) and gamma = ||r||
+      (fp64, stored fp32); the estimate is q . k_hat + gamma sqrt(pi/2) / m *
+      sum_j (S q)_j sign_j, unbiased over S. The sketch bits and gamma's fp32 bits
+      follow the MSE words of the key record (4 + 1 words). A prod key at b bits is the
+      MSE key at b - 1 bits plus the sketch.
 """
 from __future__ import annotations
 
@@ -281,14 +292,56 @@ def unpack_codes(words: np.ndarray, dims: list[int], rates: list[int]) -> list[n
 
 
 # --------------------------------------------------------------------------
+# 1-bit QJL residual sketch (TurboQuant-prod)  [TQ-diag residual, QJL], R23
+# --------------------------------------------------------------------------
+
+QJL_M = 128  # sketch rows: one sign bit per key coordinate
+
+
+def qjl_encode(r: np.ndarray, S: np.ndarray):
+    """Residual rows r [n, d] (fp64) and S [m, d] (fp32 entries): (gamma = ||r|| fp64
+    stored fp32 [n], sign bits [n, m] (1 where (S r)_j >= 0), the projections S r fp64)."""
+    r64 = np.asarray(r, np.float64)
+    if r64.ndim == 1:
+        r64 = r64[None, :]
+    gamma = np.sqrt(np.sum(r64 * r64, axis=1))
+    proj = r64 @ np.asarray(S, np.float32).astype(np.float64).T
+    bits = (proj >= 0.0).astype(np.int64)
+    return gamma.astype(np.float32), bits, proj
+
+
+def qjl_inner(y: np.ndarray, bits, gamma, S: np.ndarray) -> np.ndarray:
+    """The sketch's estimate of y . r for rows y [k, d] and sketches (bits [n, m],
+    gamma [n]): gamma sqrt(pi/2) / m * sum_j (S y)_j (2 bit_j - 1), fp64 [k, n]."""
+    y64 = np.atleast_2d(np.asarray(y, np.float32)).astype(np.float64)
+    S64 = np.asarray(S, np.float32).astype(np.float64)
+    m = S64.shape[0]
+    sy = y64 @ S64.T                                   # [k, m]
+    sigma = 2.0 * np.asarray(bits, np.float64) - 1.0   # [n, m]
+    g = np.asarray(gamma, np.float32).astype(np.float64)
+    return (sy @ sigma.T) * (g * math.sqrt(math.pi / 2.0) / m)[None, :]
+
+
+def qjl_fields(plan, k_words):
+    """The sketch bits [n, m] and gamma (fp32) [n] stored after the MSE words of key
+    records [n, words]."""
+    w = np.atleast_2d(np.asarray(k_words, np.uint32))
+    mw = plan.mse_words
+    (bits,) = unpack_codes(w[:, mw:mw + QJL_M // 32], [QJL_M], [1])
+    gamma = np.ascontiguousarray(w[:, mw + QJL_M // 32]).view(np.float32)
+    return bits, gamma
+
+
+# --------------------------------------------------------------------------
 # A head's plan and its packed cache
 # --------------------------------------------------------------------------
 
 class HeadPlan:
-    """Rates, groups, rotations and V rate of one (layer, KV head)."""
+    """Rates, groups, rotations and V rate of one (layer, KV head); qjl: the residual
+    sketch matrix S [128, 128] (R23) or None."""
 
     def __init__(self, rates, k_rots: list[np.ndarray], v_rot: np.ndarray, v_bits: int,
-                 layout: int = HALF, nc: bool = False):
+                 layout: int = HALF, nc: bool = False, qjl=None):
         self.rates = np.asarray(rates, dtype=np.int64)
         self.layout = layout
         self.nc = bool(nc)  # norm-corrected stored norms (see encode)
@@ -301,6 +354,14 @@ class HeadPlan:
         self.k_rots = [np.asarray(r, np.float32) for r in k_rots]
         self.v_rot = np.asarray(v_rot, np.float32)
         self.v_bits = int(v_bits)
+        self.qjl = None if qjl is None else np.asarray(qjl, np.float32)
+        if self.qjl is not None and self.qjl.shape != (QJL_M, HEAD_DIM):
+            raise ValueError("the QJL matrix is 128 x 128")
+
+    @property
+    def mse_words(self):
+        """Words of the MSE part of a key record."""
+        return (sum(len(c) * r for r, c in self.groups) + 31) // 32
 
     @property
     def group_rates(self):
@@ -313,7 +374,9 @@ class HeadPlan:
 
 def encode_kv(plan: HeadPlan, k: np.ndarray, v: np.ndarray) -> dict:
     """Encode tokens k, v [n, 128] of one KV head into the packed record
-    (K words, K norms per group, V words, V norm) [BGTQ s5], [TQ-diag]."""
+    (K words, K norms per group, V words, V norm) [BGTQ s5], [TQ-diag]. With a QJL plan
+    the key record goes on with the residual's sketch words and gamma's bits (R23)
+    [TQ-diag residual, QJL]."""
     kn, kc, kz = [], [], []
     for (r, coords), rot in zip(plan.groups, plan.k_rots):
         nu, codes, z = encode(np.asarray(k)[:, coords], rot, r, nc=plan.nc)
@@ -321,9 +384,18 @@ def encode_kv(plan: HeadPlan, k: np.ndarray, v: np.ndarray) -> dict:
         kc.append(codes)
         kz.append(z)
     vn, vc, vz = encode(v, plan.v_rot, plan.v_bits, nc=plan.nc)
-    return dict(k_words=pack_codes(kc, plan.group_rates), k_norms=np.stack(kn, axis=1),
-                v_words=pack_codes([vc], [plan.v_bits]), v_norms=vn,
-                k_codes=kc, k_z=kz, v_codes=vc, v_z=vz)
+    k_words = pack_codes(kc, plan.group_rates)
+    k_norms = np.stack(kn, axis=1)
+    out = dict(k_norms=k_norms, v_words=pack_codes([vc], [plan.v_bits]), v_norms=vn,
+               k_codes=kc, k_z=kz, v_codes=vc, v_z=vz)
+    if plan.qjl is not None:
+        k64 = np.asarray(k, np.float32).astype(np.float64)
+        r = k64 - dequantized_keys(plan, k_words, k_norms)
+        gamma, bits, proj = qjl_encode(r, plan.qjl)
+        k_words = np.concatenate([k_words, pack_codes([bits], [1]), gamma.view(np.uint32)[:, None]], axis=1)
+        out.update(qjl_bits=bits, qjl_gamma=gamma, qjl_proj=proj)
+    out["k_words"] = k_words
+    return out
 
 
 def rotate_query(plan: HeadPlan, q: np.ndarray) -> list[np.ndarray]:
@@ -334,8 +406,8 @@ def rotate_query(plan: HeadPlan, q: np.ndarray) -> list[np.ndarray]:
 
 def packed_logits(plan: HeadPlan, q: np.ndarray, k_words, k_norms, scale: float) -> np.ndarray:
     """Logits straight from the packed record: for each group,
-    nu_g / sqrt(d_g) * sum_i r_{g,i} * C_b[code_i], summed over groups, times scale.
-    q [m, 128] -> [m, n]."""
+    nu_g / sqrt(d_g) * sum_i r_{g,i} * C_b[code_i], summed over groups, plus (QJL plans)
+    the sketch's estimate of q . r, times scale. q [m, 128] -> [m, n]."""
     q = np.atleast_2d(q)
     codes = unpack_codes(k_words, plan.group_dims, plan.group_rates)
     r = rotate_query(plan, q)
@@ -345,6 +417,9 @@ def packed_logits(plan: HeadPlan, q: np.ndarray, k_words, k_norms, scale: float)
         c16, _ = codebook(b)
         vals = c16[cg]                                   # [n, d_g]
         out += (r[g] @ vals.T) * (kn[:, g] / math.sqrt(len(coords)))[None, :]
+    if plan.qjl is not None:
+        bits, gamma = qjl_fields(plan, k_words)
+        out += qjl_inner(q, bits, gamma, plan.qjl)
     return scale * out
 
 
