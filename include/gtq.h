@@ -129,12 +129,24 @@ gtq_status gtq_head_layout_from_rates(const uint8_t* rates, int32_t rope_layout,
 
 enum {
   GTQ_PLAN_HOST_ONLY = 1,     /* build and validate on the host, no device copy           */
-  GTQ_PLAN_NORM_CORRECT = 2   /* norm-corrected variant ("TurboQuant: paper algorithm
+  GTQ_PLAN_NORM_CORRECT = 2,  /* norm-corrected variant ("TurboQuant: paper algorithm
                                  and vLLM engineering" diagram, vLLM column, NC box): the
                                  stored norm of every key group and of the value is
                                  nu * sqrt(d) / ||C[code]|| (fp64, rounded to fp32), so
                                  that the decoded vector keeps the input's norm; codes and
                                  the attention are unchanged                               */
+  GTQ_PLAN_QJL = 4            /* 1-bit QJL residual sketch of the keys (TurboQuant-prod;
+                                 "TurboQuant: paper algorithm and vLLM engineering"
+                                 diagram, paper column, residual and QJL boxes): each key
+                                 record goes on after its MSE words with sign(S r) for the
+                                 residual r = k - k_hat (128 bits, 4 words; a zero
+                                 projection counts as +) and gamma = ||r|| (fp64, stored
+                                 as fp32 bits, 1 word); the attention logit adds
+                                 gamma sqrt(pi/2) / 128 * sum_j (S q)_j sign_j. Needs
+                                 desc.qjl and k_budget <= 176 (records of at most 16
+                                 words); a prod key at b bits is k_budget = 64 (b - 1).
+                                 Decode only (gtq_prefill_attn returns EUNSUPPORTED); chunk
+                                 appends run through the per-token kernel.                 */
 };
 
 typedef struct gtq_plan_desc {
@@ -143,12 +155,15 @@ typedef struct gtq_plan_desc {
   int32_t rope_layout;                     /* GTQ_ROPE_HALF | GTQ_ROPE_INTERLEAVED     */
   int32_t k_budget;                        /* sum_j b_j of every head (128 = K2, 192 = K3) */
   int32_t v_bits;                          /* 1..4, values are one 128-dim group       */
-  int32_t flags;                           /* GTQ_PLAN_HOST_ONLY | GTQ_PLAN_NORM_CORRECT */
+  int32_t flags;                           /* GTQ_PLAN_HOST_ONLY | _NORM_CORRECT | _QJL */
   const uint8_t* k_rates; /* host [n_layers][n_kv_heads][64], each head summing to k_budget */
   const float* k_rot;     /* host: for l, h, groups in ascending rate: the group's d x d
                              rotation, row-major fp32, concatenated (each head's slice is
                              sum_g d_g^2 floats)                                     */
   const float* v_rot;     /* host [n_layers][n_kv_heads][128][128] row-major fp32      */
+  const float* qjl;       /* host [n_layers][n_kv_heads][128][128] row-major fp32, the
+                             sketch matrices S (entries N(0,1)) of GTQ_PLAN_QJL; else
+                             NULL                                                    */
 } gtq_plan_desc;
 
 typedef struct gtq_plan gtq_plan;

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgtq.so")
 
 HEAD_DIM = 128
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
-PLAN_HOST_ONLY, PLAN_NORM_CORRECT = 1, 2
+PLAN_HOST_ONLY, PLAN_NORM_CORRECT, PLAN_QJL = 1, 2, 4
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "EDEVICE", 5: "ECAPACITY"}
 
 
@@ -44,7 +44,7 @@ class PlanDesc(C.Structure):
                 ("head_dim", C.c_int32), ("rope_layout", C.c_int32), ("k_budget", C.c_int32),
                 ("v_bits", C.c_int32), ("flags", C.c_int32),
                 ("k_rates", C.POINTER(C.c_uint8)), ("k_rot", C.POINTER(C.c_float)),
-                ("v_rot", C.POINTER(C.c_float))]
+                ("v_rot", C.POINTER(C.c_float)), ("qjl", C.POINTER(C.c_float))]
 
 
 class CacheView(C.Structure):
@@ -220,10 +220,11 @@ def gtq_head_layout_from_rates(rates, rope_layout: int = ROPE_HALF) -> dict:
 class Plan:
     """Owner of a gtq_plan*. k_rot[l][h] is the list of group rotations (ascending
     rate) of (layer l, KV head h); v_rot is [L][H_kv][128][128]. norm_correct selects
-    the norm-corrected stored norms (GTQ_PLAN_NORM_CORRECT)."""
+    the norm-corrected stored norms (GTQ_PLAN_NORM_CORRECT); qjl, [L][H_kv][128][128]
+    sketch matrices, the QJL residual sketch of the keys (GTQ_PLAN_QJL)."""
 
     def __init__(self, n_layers, n_kv_heads, n_q_heads, k_budget, v_bits, k_rates, k_rot, v_rot,
-                 rope_layout=ROPE_HALF, host_only=False, head_dim=HEAD_DIM, norm_correct=False):
+                 rope_layout=ROPE_HALF, host_only=False, head_dim=HEAD_DIM, norm_correct=False, qjl=None):
         self.n_layers, self.n_kv, self.n_q = n_layers, n_kv_heads, n_q_heads
         self.k_budget, self.v_bits = k_budget, v_bits
         self.norm_correct = bool(norm_correct)
@@ -231,9 +232,14 @@ class Plan:
         flat = [np.asarray(m, np.float32).reshape(-1) for lh in k_rot for hh in lh for m in hh]
         krot = np.ascontiguousarray(np.concatenate(flat) if flat else np.zeros(1, np.float32))
         vrot = np.ascontiguousarray(v_rot, dtype=np.float32).reshape(-1)
+        self.qjl = qjl is not None
+        qm = None if qjl is None else np.ascontiguousarray(qjl, dtype=np.float32).reshape(-1)
+        self._keep = (rates, krot, vrot, qm)
         d = PlanDesc(n_layers, n_kv_heads, n_q_heads, head_dim, rope_layout, k_budget, v_bits,
-                     (PLAN_HOST_ONLY if host_only else 0) | (PLAN_NORM_CORRECT if norm_correct else 0),
-                     rates.ctypes.data_as(C.POINTER(C.c_uint8)), _fptr(krot), _fptr(vrot))
+                     (PLAN_HOST_ONLY if host_only else 0) | (PLAN_NORM_CORRECT if norm_correct else 0)
+                     | (PLAN_QJL if qjl is not None else 0),
+                     rates.ctypes.data_as(C.POINTER(C.c_uint8)), _fptr(krot), _fptr(vrot),
+                     _fptr(qm) if qm is not None else None)
         h = C.c_void_p()
         self._h = None
         _check(lib().gtq_plan_create(C.byref(d), C.byref(h)), "gtq_plan_create")

@@ -586,6 +586,8 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   __shared__ double nu64_s[5], cs_s[5];  // norm-corrected variant: fp64 norms, sums of C[code]^2
   __shared__ uint32_t krec[16];
   __shared__ uint32_t vblk[128], vmask[128];
+  __shared__ float kcen[kD];            // QJL: the decoded centroid of each key record position
+  __shared__ double rnat[kD];           // QJL: the residual in head coordinates
   __shared__ float thr[5][16], cen[5][16];
   const int tid = threadIdx.x;
   const DevHead* __restrict__ hd = a.heads + h;
@@ -622,8 +624,9 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
 #pragma unroll
     for (int u = 0; u < 8; ++u) pv[u] = (hd->v_hadamard || !mine) ? make_float4(0.f, 0.f, 0.f, 0.f) : pr[u];
   }
-  const int seq = a.step_len ? (int)tok : a.seq_idx[tok];
-  const int64_t slot = a.step_len ? (int64_t)a.step_len[tok] - 1 : a.slot[tok];
+  // (a chunk through this kernel: no index arrays, token tok of sequence a.seq at pos0 + tok)
+  const int seq = a.step_len ? (int)tok : (a.seq_idx ? a.seq_idx[tok] : a.seq);
+  const int64_t slot = a.step_len ? (int64_t)a.step_len[tok] - 1 : (a.slot ? a.slot[tok] : a.pos0 + tok);
   const int64_t ti = (seq < 0 || seq >= a.batch || slot < 0 || slot >= a.capacity)
                          ? -1 : token_index(a.pm, a.capacity, a.n_kv, seq, h, slot);
   if (ti < 0) {
@@ -719,6 +722,7 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
       const int g = kg;
       const int b = pick(GL.rate, g);
       const uint32_t c = quantize(z0 * sc_s[g], thr[b], (1 << b) - 1);
+      kcen[tid] = cen[b][c];
       const int bit = pick(GL.bit, g) + (tid - pick(GL.pos, g)) * b;
       const uint64_t f = (uint64_t)c << (bit & 31);
       atomicOr(&krec[bit >> 5], (uint32_t)f);
@@ -754,6 +758,57 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     }
   }
   __syncthreads();
+  if (hd->qjl && do_k) {
+    // 1-bit QJL residual sketch (TurboQuant-prod; diagram residual and QJL boxes): the
+    // decoded key k_hat (stored norms), r = k - k_hat and gamma = |r| in fp64, then
+    // sign(S r) into record words mse .. mse + 3 and gamma's fp32 bits into mse + 4.
+    // Thread (record position p, eighth e) sums its sixteenth of column p of Pi_g.
+    const int p = tid >> 3, e = tid & 7;
+    const int g = group_of(GL, p);
+    const int d = pick(GL.dim, g), po = pick(GL.pos, g), ii = p - po;
+    const float* col = a.rot + pick(GL.krot, g) + ii;
+    double s = 0.0;
+    for (int i = 16 * e; i < min(d, 16 * e + 16); ++i) s += (double)col[(size_t)i * d] * (double)kcen[po + i];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    const double nu = a.nc ? (double)corrected_norm(nu64_s[g], cs_s[g], d) : (double)nu_s[g];
+    const double r = (double)xs[p] - nu * (s / sqrt((double)d));
+    if (e == 0) rnat[hd->coord[p]] = r;
+    __syncthreads();
+    // gamma: threads 0..127 take the residual's coordinate tid
+    __shared__ double gsum[2];
+    if (tid < kD) {
+      const double w = wave_sum_f64_fast(rnat[tid] * rnat[tid]);
+      if ((tid & 63) == 0) gsum[tid >> 6] = w;
+    }
+    // projections: thread (row j, eighth e) sums its sixteenth of row j of S
+    const float4* srow = reinterpret_cast<const float4*>(a.rot + hd->qjl_off + (size_t)p * kD + 16 * e);
+    double pj = 0.0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 sv = srow[u];
+      pj += (double)sv.x * rnat[16 * e + 4 * u] + (double)sv.y * rnat[16 * e + 4 * u + 1] +
+            (double)sv.z * rnat[16 * e + 4 * u + 2] + (double)sv.w * rnat[16 * e + 4 * u + 3];
+    }
+    pj += __shfl_xor(pj, 1);
+    pj += __shfl_xor(pj, 2);
+    pj += __shfl_xor(pj, 4);
+    // bits j of the wave (lanes with e == 0): 8 per wave, 32 per word
+    const unsigned long long bal = __ballot(e == 0 && pj >= 0.0);
+    __shared__ uint32_t sbits[16];  // (1024 threads: 16 waves)
+    if ((tid & 63) == 0) {
+      uint32_t b8 = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) b8 |= (uint32_t)((bal >> (8 * k)) & 1ull) << k;
+      sbits[tid >> 6] = b8;
+    }
+    __syncthreads();
+    const int mw = hd->mse_words;
+    if (tid < 4) krec[mw + tid] = sbits[4 * tid] | sbits[4 * tid + 1] << 8 | sbits[4 * tid + 2] << 16 | sbits[4 * tid + 3] << 24;
+    if (tid == 4) krec[mw + 4] = __builtin_bit_cast(uint32_t, (float)sqrt(gsum[0] + gsum[1]));
+    __syncthreads();
+  }
   if (do_k && tid < a.k_words) a.k_codes[ti * a.k_words + tid] = krec[tid];
   if (do_k && tid >= 64 && tid < 64 + kNS) {
     const int g = tid - 64;
@@ -830,6 +885,8 @@ struct AttnArgs {
   const int32_t* seq_len;  // decode
   uint4* qb;               // [tiles][kQB] QK B operands
   float* tile_xs;          // [tiles]: 2^sq, the factor that undoes the operands' range scaling
+  uint4* qjl_qb;           // QJL plans: [tiles][4 * 64] B operands of the residual sketch (S q)
+  int32_t qjl, mse_words;  // QJL plan; words of a key record's MSE part
   float* partials;         // [rows][n_chunks][kPS]
   int64_t capacity;
   int64_t logits_ld;
@@ -1017,9 +1074,19 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
     qv[pp] = id >= 0 ? a.q[(size_t)id * kD + c] : 0.f;
   }
   const int crd = tid < kD ? hp->coord[tid] : 0;
+  // QJL plans (decode tiles): this thread's sixteenth of row i of the sketch matrix S
+  const bool qjl = RT == 8 && a.qjl;
+  float4 sr[4];
+  {
+    const float4* row = reinterpret_cast<const float4*>(a.rot + hp->qjl_off + (size_t)i * kD + 16 * part);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sr[u] = qjl ? row[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __shared__ uint4 qjb[4][4][16];
 #pragma unroll
   for (int pp = 0; pp < RT * kD / kT; ++pp) (&qnat[0][0])[tid + kT * pp] = qv[pp];
   for (int e = tid; e < kTileQB; e += kT) (&qb[0][0][0])[e] = make_uint4(0, 0, 0, 0);
+  if (qjl && tid < 4 * 4 * 16) (&qjb[0][0][0])[tid] = make_uint4(0, 0, 0, 0);
   __syncthreads();
   if (tid < kD) {
 #pragma unroll
@@ -1042,13 +1109,37 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
     }
     acc[r] = s;
   }
+  // the sketch's projection (S q)_i of each row, natural coordinate order
+  float aq[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float s = 0.f;
+    if (qjl) {
+      const float4* x = reinterpret_cast<const float4*>(&qnat[r][16 * part]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 xx = x[u];
+        s = fmaf(sr[u].x, xx.x, s);
+        s = fmaf(sr[u].y, xx.y, s);
+        s = fmaf(sr[u].z, xx.z, s);
+        s = fmaf(sr[u].w, xx.w, s);
+      }
+    }
+    aq[r] = s;
+  }
   // sum the 8 parts (consecutive lanes)
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     acc[r] += __shfl_xor(acc[r], 1);
     acc[r] += __shfl_xor(acc[r], 2);
     acc[r] += __shfl_xor(acc[r], 4);
+    aq[r] += __shfl_xor(aq[r], 1);
+    aq[r] += __shfl_xor(aq[r], 2);
+    aq[r] += __shfl_xor(aq[r], 4);
   }
+  // the sketch operand: the key's factor is gamma and its codes decode to c1 sign_j (the
+  // rate-1 centroids), so B = (S q)_j qscale sqrt(pi/2) / (128 c1)
+  const float sq_scale = qjl ? a.qscale * 1.2533141373155003f / (128.f * a.cb->c[1][1]) : 0.f;
   // Range of the binary16 high parts: if the tile's largest scaled component exceeds
   // 2^14, every operand of the tile is scaled by the power of two 2^-sq that brings it
   // under (exact); the attention kernels multiply the tile's logits by 2^sq.
@@ -1057,7 +1148,7 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
     float lm = 0.f;
     if (part == 0) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r) lm = fmaxf(lm, fabsf(acc[r] * sc));
+      for (int r = 0; r < RT; ++r) lm = fmaxf(lm, fmaxf(fabsf(acc[r] * sc), fabsf(aq[r] * sq_scale)));
     }
 #pragma unroll
     for (int o = 8; o < 64; o <<= 1) lm = fmaxf(lm, __shfl_xor(lm, o));
@@ -1074,6 +1165,17 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
     }
     sc = ldexpf(sc, -sq);
     if (tid == 0) a.tile_xs[tile] = ldexpf(1.f, sq);
+    if (qjl && part == 0) {  // (RT == 8: columns r high, 15 - r low)
+      const float qs = ldexpf(sq_scale, -sq);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float val = aq[r] * qs;
+        const _Float16 hi = (_Float16)val;
+        const _Float16 lo = (_Float16)(val - (float)hi);
+        reinterpret_cast<_Float16*>(&qjb[i >> 5][(i >> 3) & 3][r])[i & 7] = hi;
+        reinterpret_cast<_Float16*>(&qjb[i >> 5][(i >> 3) & 3][15 - r])[i & 7] = lo;
+      }
+    }
   }
   if (part == 0) {
     const int kp = hp->kp_pos[i];
@@ -1093,6 +1195,7 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
   }
   __syncthreads();
   for (int e = tid; e < kTileQB; e += kT) a.qb[(size_t)tile * kTileQB + e] = (&qb[0][0][0])[e];
+  if (qjl && tid < 4 * 64) a.qjl_qb[(size_t)tile * 256 + tid] = (&qjb[0][0][0])[tid];
 }
 
 template <int RT>
@@ -2137,21 +2240,21 @@ constexpr int kDecThreads = 64 * kDecWaves;
 
 struct DecWave {
   uint32_t ktile[kBlk * kKPitch];    // 32 key records, pitch 17 words
-  float knt[kMaxGroups][kBlk];       // key group norms, group-major
+  float knt[kMaxGroups + 1][kBlk];   // key group norms, group-major, then the QJL gamma
   float vn[kBlk];                    // value norms
 };
 // Decode tables in LDS, each entry repeated so that a wave's random lookups fall in
 // distinct banks: entry e of a table kept R times sits at (e R + r) x its size and lane
 // l reads copy r = l mod R. The copy counts are the smallest a random wave-wide read of
-// that width needs to run at the rate of a contiguous one on gfx950 (b32: 64, b64: 32;
-// the rate-4 pairs keep 16 for space). Byte offsets are fixed (the lookups put them in
-// the instruction's offset field).
-constexpr uint32_t kDecT1 = 4096, kDecP3 = 8192, kDecP4 = 24576, kDecQ2 = 40960;
+// that width needs to run at the rate of a contiguous one on gfx950 (b64: 32; the b32
+// pair tables of rates 3 and 4 keep 32 and 16 for space). Byte offsets are fixed (the
+// lookups put them in the instruction's offset field).
+constexpr uint32_t kDecT1 = 4096, kDecP3 = 8192, kDecP4 = 16384, kDecQ2 = 32768;
 struct DecTables {
   uint32_t lut[1024];                // all pair tables once (DevCodebook::pair); the rate-1
                                      // and rate-2 ones (4 and 16 entries) read conflict-free
   uint2 t1[16][32];                  // 4 rate-1 centroids of each nibble, 32 copies
-  uint32_t p3[64][64];               // rate-3 pairs, 64 copies
+  uint32_t p3[64][32];               // rate-3 pairs, 32 copies
   uint32_t p4[256][16];              // rate-4 pairs, 16 copies
   uint2 q2[256][32];                 // 4 rate-2 centroids of each byte, 32 copies
 };
@@ -2168,7 +2271,8 @@ struct DecShared {
   long long sk_u0, sk_u1, sk_P;      // this workgroup's next unit, its end, the units before sk_b
   int32_t sk_b;                      // the sequence of the next unit (or an earlier, empty one)
   int32_t sk_tile;                   // the current segment's row tile
-  uint4 qb[kMaxKB - 1][4][16];       // query operands of the slots kept out of registers
+  uint4 qb[kMaxKB - 1][4][16];       // query operands of the K-block slots
+  uint4 qjlb[4][4][16];              // QJL plans: the residual sketch's operands
   int32_t row_id[8];
   int32_t row_len[8];
   float om[kDecWaves][8];
@@ -2177,9 +2281,9 @@ struct DecShared {
 static_assert(offsetof(DecShared, u) == 0, "tables at the start of the shared block");
 
 // Lane base offsets of the replicated tables: copy lane mod 32 of an 8-byte table
-// (t1, q2), lane mod 64 and lane mod 16 of a 4-byte one (p3, p4)
+// (t1, q2), lane mod 32 and lane mod 16 of a 4-byte one (p3, p4)
 struct DecLanes {
-  uint32_t l8, l4, l4_16;
+  uint32_t l8, l4_32, l4_16;
 };
 
 __device__ inline uint2 lds_u64(const char* base, uint32_t off) {
@@ -2202,7 +2306,7 @@ __device__ inline half8 dec_dequant8(const char* sb, const DecLanes& L, uint32_t
     o.u[0] = x.x; o.u[1] = x.y; o.u[2] = y.x; o.u[3] = y.y;
   } else if constexpr (R == 3) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.u[j] = lds_u32(sb, kDecP3 + ((__builtin_amdgcn_ubfe(F, 6 * j, 6) << 8) | L.l4));
+    for (int j = 0; j < 4; ++j) o.u[j] = lds_u32(sb, kDecP3 + ((__builtin_amdgcn_ubfe(F, 6 * j, 6) << 7) | L.l4_32));
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) o.u[j] = lds_u32(sb, kDecP4 + ((__builtin_amdgcn_ubfe(F, 8 * j, 8) << 6) | L.l4_16));
@@ -2317,7 +2421,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
 #pragma unroll
   for (int u = 0; u < kU3; ++u) {
     const int e = tid + kDecThreads * u;
-    p3v[u] = cb->pair[20 + (e >> 6)];
+    p3v[u] = cb->pair[20 + (e >> 5)];  // (the first kU3 / 2 rounds; the rest unused)
     p4v[u] = cb->pair[84 + (e >> 4)];
   }
 #pragma unroll
@@ -2367,7 +2471,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
 #pragma unroll
   for (int u = 0; u < kU3; ++u) {
     const int e = tid + kDecThreads * u;
-    S.u.t.p3[e >> 6][e & 63] = p3v[u];
+    if (e < 64 * 32) S.u.t.p3[e >> 5][e & 31] = p3v[u];
     S.u.t.p4[e >> 4][e & 15] = p4v[u];
   }
 #pragma unroll
@@ -2414,7 +2518,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
     constexpr uint32_t kHalf = 4u * 4u * kKPitch;                       // token tau0 + 4
     DecLanes DL;
     DL.l8 = (uint32_t)(lane & 31) << 3;
-    DL.l4 = (uint32_t)lane << 2;
+    DL.l4_32 = (uint32_t)(lane & 31) << 2;
     DL.l4_16 = (uint32_t)(lane & 15) << 2;
     // this lane's key norms: knt[g][8q .. 8q + 7]
     const uint32_t nq_off = (uint32_t)(reinterpret_cast<const char*>(&W.knt[0][8 * q]) - sb);
@@ -2445,6 +2549,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
     // one round of independent loads: query operands (to LDS), rows, the first block
     static_assert(NS * 64 <= kDecThreads, "one query operand per thread");
     const uint4 qg = tid < NS * 64 ? A.qb[(size_t)tile * kQB + tid] : make_uint4(0, 0, 0, 0);
+    const uint4 qjg = (A.qjl && tid < 4 * 64) ? A.qjl_qb[(size_t)tile * 256 + tid] : make_uint4(0, 0, 0, 0);
     const int len_ld = A.seq_len[seq];
     const float xs = A.tile_xs[tile];
     DecBlock<VB, KWL> blk;
@@ -2462,6 +2567,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
       }
     }
     if (tid < NS * 64) (&S.qb[0][0][0])[tid] = qg;
+    if (A.qjl && tid < 4 * 64) (&S.qjlb[0][0][0])[tid] = qjg;
     if (tid < 8) {
       int L;
       S.row_id[tid] = tile_row<8>(A, seq, h, tr, tid, len_ld, &L);
@@ -2492,7 +2598,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
   }
   // other slots: per-lane LDS address << 5 | shift of the first code; one uniform word
   // with the index width 2R (bits 0..3), the group (bits 4..5), the copy stride shift
-  // (bits 6..9: 2 for the single pair tables of rates 1 and 2, 8 for p3, 6 for p4) and
+  // (bits 6..9: 2 for the single pair tables of rates 1 and 2, 7 for p3, 6 for p4) and
   // the table's byte offset (bits 12..)
   constexpr int NG = NS - N1 - N4;
   uint32_t gko[NG > 0 ? NG : 1];
@@ -2504,7 +2610,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
     const int bit = hp->kb_bit[N1 + N4 + i] + 8 * q * rate;
     gko[i] = ((row0 + 4u * (uint32_t)(bit >> 5)) << 5) | (uint32_t)(bit & 31);
     const uint32_t tb = rate == 3 ? kDecP3 : rate == 4 ? kDecP4 : 4u * (uint32_t)(((1 << (2 * rate)) - 4) / 3);
-    const uint32_t ts = rate == 3 ? 8u : rate == 4 ? 6u : 2u;
+    const uint32_t ts = rate == 3 ? 7u : rate == 4 ? 6u : 2u;
     gpk[i] = (uint32_t)(2 * rate) | (uint32_t)(rg >> 8) << 4 | ts << 6 | tb << 12;
   }
 
@@ -2517,6 +2623,10 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
     // ---- stage the key records and key norms; the value words and norms stay in registers
 #pragma unroll
     for (int i = 0; i < KWL; ++i) W.ktile[kst + i * (64 / kRowW) * kKPitch] = blk.kr[i];
+    if (a.qjl && lane % kRowW == a.mse_words + 4) {  // the QJL gamma (record word mse + 4)
+#pragma unroll
+      for (int i = 0; i < KWL; ++i) W.knt[kMaxGroups][lane / kRowW + i * (64 / kRowW)] = __builtin_bit_cast(float, blk.kr[i]);
+    }
     W.knt[2 * (lane & 1)][lane >> 1] = blk.kn.x;
     W.knt[2 * (lane & 1) + 1][lane >> 1] = blk.kn.y;
     W.vn[lane & 31] = blk.vn;  // (lanes l and l + 32 hold the same norm)
@@ -2574,6 +2684,26 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
       lg[4] = fmaf(nb.x, d1[0], lg[4]); lg[5] = fmaf(nb.y, d1[1], lg[5]);
       lg[6] = fmaf(nb.z, d1[2], lg[6]); lg[7] = fmaf(nb.w, d1[3], lg[7]);
     }
+    if (a.qjl) {
+      // the residual sketch: four 32-bit slots after the MSE words, decoded like rate-1
+      // codes (centroids c1 sign_j) against B = S q scaled, times gamma
+      floatx4 d0 = z4, d1 = z4;
+      const uint32_t sk0 = row0 + 4u * (uint32_t)a.mse_words;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        H8 a0, a1, bq;
+        a0.h = dec_dequant8<1>(sb, DL, sb8[sk0 + 4 * i + q]);
+        a1.h = dec_dequant8<1>(sb, DL, sb8[sk0 + kHalf + 4 * i + q]);
+        bq.v = S.qjlb[i][q][n];
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, bq.h, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, bq.h, d1, 0, 0, 0);
+      }
+      const float4 na = knorm4(kMaxGroups, 0), nb = knorm4(kMaxGroups, 1);
+      lg[0] = fmaf(na.x, d0[0], lg[0]); lg[1] = fmaf(na.y, d0[1], lg[1]);
+      lg[2] = fmaf(na.z, d0[2], lg[2]); lg[3] = fmaf(na.w, d0[3], lg[3]);
+      lg[4] = fmaf(nb.x, d1[0], lg[4]); lg[5] = fmaf(nb.y, d1[1], lg[5]);
+      lg[6] = fmaf(nb.z, d1[2], lg[6]); lg[7] = fmaf(nb.w, d1[3], lg[7]);
+    }
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       if (N1 + N4 + i < nkb) {
@@ -2581,7 +2711,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
         const uint32_t f0 = __builtin_amdgcn_alignbit(r[1], r[0], gko[i]);
         const uint32_t f1 = __builtin_amdgcn_alignbit(r[4 * kKPitch + 1], r[4 * kKPitch], gko[i]);
         const uint32_t w2 = gpk[i] & 15u, ts = (gpk[i] >> 6) & 15u;
-        const uint32_t lb = (gpk[i] >> 12) + (ts == 8u ? DL.l4 : ts == 6u ? DL.l4_16 : 0u);
+        const uint32_t lb = (gpk[i] >> 12) + (ts == 7u ? DL.l4_32 : ts == 6u ? DL.l4_16 : 0u);
         H8 a0, a1, bq;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -3273,8 +3403,10 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   a.v_bits = p->v_bits;
   a.nc = (p->flags & GTQ_PLAN_NORM_CORRECT) ? 1 : 0;
   a.pm = page_map(c);
-  if (!chunk) {
+  // QJL plans append through the per-token kernel (chunks included: no index arrays)
+  if (!chunk || (p->flags & GTQ_PLAN_QJL)) {
     if (n_tok > 0x7FFFFFFF) return fail(GTQ_EUNSUPPORTED, "gtq_quantize_append: too many tokens");
+    if (n_tok == 0) return ok();
     hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)n_tok, p->n_kv, append_roles(n_tok * p->n_kv)), dim3(1024),
                        0, stream, a);
     hipError_t e = hipGetLastError();
@@ -3310,8 +3442,10 @@ int auto_chunk(int64_t max_len, int64_t tiles, int64_t kRound) {
 // workspace: the tiles' QK B operands, then the partials
 // rotated-query operands of n_tiles row tiles of rt rows (8 KB per 8 rows)
 // (followed by one float per tile: the factor 2^sq that undoes the operands' range scaling)
-size_t attn_qb_bytes(int64_t n_tiles, int rt) {
-  return (size_t)n_tiles * (rt / 8) * kQB * sizeof(uint4) + ((size_t)n_tiles * 4 + 15) / 16 * 16;
+// (QJL plans: then the residual sketch's operands, 4 KB per tile)
+size_t attn_qb_bytes(int64_t n_tiles, int rt, bool qjl = false) {
+  return (size_t)n_tiles * (rt / 8) * kQB * sizeof(uint4) + ((size_t)n_tiles * 4 + 15) / 16 * 16 +
+         (qjl ? (size_t)n_tiles * 256 * sizeof(uint4) : 0);
 }
 size_t attn_ws_bytes(int64_t rows, int64_t n_chunks, size_t qb_bytes) {
   return qb_bytes + (size_t)rows * n_chunks * kPS * 4;
@@ -3346,6 +3480,10 @@ void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnA
   aa.v_norms = c->v_norms;
   aa.qb = reinterpret_cast<uint4*>(ws);
   aa.tile_xs = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (size_t)L.n_tiles * (L.rt / 8) * kQB * sizeof(uint4));
+  aa.qjl = (p->flags & GTQ_PLAN_QJL) ? 1 : 0;
+  aa.mse_words = 2 * p->k_budget / 32;
+  aa.qjl_qb = aa.qjl ? reinterpret_cast<uint4*>(reinterpret_cast<char*>(aa.tile_xs) + ((size_t)L.n_tiles * 4 + 15) / 16 * 16)
+                     : nullptr;
   aa.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + L.qb_bytes);
   aa.capacity = c->capacity;
   aa.n_kv = p->n_kv;
@@ -3654,7 +3792,7 @@ static bool decode_shape(const gtq_plan* p, int32_t batch, int64_t max_len, int3
   L->n_tiles = batch * p->n_kv * L->tiles_per_kv;
   L->merge_tiles_per_kv = L->tiles_per_kv;
   L->merge_n_tiles = L->n_tiles;
-  L->qb_bytes = attn_qb_bytes(L->n_tiles, L->rt);
+  L->qb_bytes = attn_qb_bytes(L->n_tiles, L->rt, (p->flags & GTQ_PLAN_QJL) != 0);
   L->chunk = chunk ? chunk : auto_chunk(max_len, L->n_tiles, kBlk * kDecWaves);
   L->n_chunks = (int)std::max<int64_t>(1, (max_len + L->chunk - 1) / L->chunk);
   if (L->n_chunks > kMaxChunks) {
@@ -3882,6 +4020,7 @@ gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache
   if (seq < 0 || seq >= cache->batch) return fail(GTQ_EINVAL, "gtq_prefill_attn: seq out of range");
   if (!q || !out || !workspace) return fail(GTQ_EINVAL, "gtq_prefill_attn: NULL pointer");
   if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_prefill_attn: softmax_scale not finite");
+  if (plan->flags & GTQ_PLAN_QJL) return fail(GTQ_EUNSUPPORTED, "gtq_prefill_attn: QJL plans are decode only");
   AttnLaunch L;
   if (!prefill_shape(plan, pos0, n_tok, chunk, &L, &st, "gtq_prefill_attn")) return st;
   if (pos0 + n_tok > cache->capacity) return fail(GTQ_ECAPACITY, "gtq_prefill_attn: pos0 + n_tok > capacity");

@@ -347,7 +347,7 @@ gtq_status gtq_cache_bytes(const gtq_plan* plan, int32_t batch, int64_t capacity
   out->k_norms_bytes = bh * capacity * kNS * 4;
   out->v_codes_bytes = bh * (capacity / GTQ_VBLOCK) * 32 * plan->v_bits * 4;
   out->v_norms_bytes = bh * capacity * 4;
-  out->logical_bits_per_token = 2 * plan->k_budget + kD * plan->v_bits;
+  out->logical_bits_per_token = 2 * plan->k_budget + kD * plan->v_bits + ((plan->flags & GTQ_PLAN_QJL) ? kD : 0);
   out->bytes_per_token = plan->k_words * 4 + kNS * 4 + 16 * plan->v_bits + 4;
   return ok();
 }
@@ -368,16 +368,21 @@ gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
   if (d->v_bits < 1 || d->v_bits > 4) return fail(GTQ_EINVAL, "gtq_plan_create: v_bits must be in [1, 4]");
   if (d->k_budget < kJ || d->k_budget > 4 * kJ || d->k_budget % 16)
     return fail(GTQ_EINVAL, "gtq_plan_create: k_budget must be a multiple of 16 in [64, 256]");
-  if (d->flags & ~(GTQ_PLAN_HOST_ONLY | GTQ_PLAN_NORM_CORRECT))
+  if (d->flags & ~(GTQ_PLAN_HOST_ONLY | GTQ_PLAN_NORM_CORRECT | GTQ_PLAN_QJL))
     return fail(GTQ_EINVAL, "gtq_plan_create: unknown flags");
   if (!d->k_rates || !d->k_rot || !d->v_rot) return fail(GTQ_EINVAL, "gtq_plan_create: NULL table");
+  const bool qjl = (d->flags & GTQ_PLAN_QJL) != 0;
+  if (qjl != (d->qjl != nullptr))
+    return fail(GTQ_EINVAL, "gtq_plan_create: GTQ_PLAN_QJL and the qjl matrices go together");
+  if (qjl && 2 * d->k_budget / 32 + 5 > 16)
+    return fail(GTQ_EUNSUPPORTED, "gtq_plan_create: QJL needs k_budget <= 176 (records of at most 16 words)");
   p->n_layers = d->n_layers;
   p->n_kv = d->n_kv_heads;
   p->n_q = d->n_q_heads;
   p->rope_layout = d->rope_layout;
   p->k_budget = d->k_budget;
   p->v_bits = d->v_bits;
-  p->k_words = 2 * d->k_budget / 32;
+  p->k_words = 2 * d->k_budget / 32 + (qjl ? 5 : 0);  // MSE words, then the sketch and gamma
   p->flags = d->flags;
   const size_t nh = (size_t)d->n_layers * d->n_kv_heads;
   p->heads.resize(nh);
@@ -416,7 +421,7 @@ gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
   // rotations transposed (read column-wise by the attention kernel's last step)
   const size_t vsz = (size_t)kD * kD;
   try {
-    p->rot.resize(krot_total + 2 * nh * vsz);
+    p->rot.resize(krot_total + (qjl ? 3 : 2) * nh * vsz);  // (and the sketch matrices)
   } catch (...) {
     return fail(GTQ_ENOMEM, "gtq_plan_create: host allocation failed");
   }
@@ -435,6 +440,15 @@ gtq_status plan_build_host(const gtq_plan_desc* d, gtq_plan* p) {
     off += dh.krot_floats;
     dh.vrot_off = (int64_t)(krot_total + h * vsz);
     dh.vrot_t_off = (int64_t)(krot_total + nh * vsz + h * vsz);
+    dh.mse_words = 2 * d->k_budget / 32;
+    dh.qjl = qjl ? 1 : 0;
+    dh.qjl_off = qjl ? (int64_t)(krot_total + 2 * nh * vsz + h * vsz) : 0;
+    if (qjl) {
+      const float* src = d->qjl + h * vsz;
+      for (size_t e = 0; e < vsz; ++e)
+        if (!isfinite(src[e])) return fail(GTQ_EINVAL, "gtq_plan_create: non-finite QJL matrix");
+      memcpy(p->rot.data() + dh.qjl_off, src, vsz * sizeof(float));
+    }
     // a randomized Hadamard Pi_V: every entry is +-c, c = fp32(1/sqrt(128)), with the
     // Sylvester sign pattern times a per-column sign (read off row 0)
     {

@@ -43,6 +43,9 @@ struct DevHead {
   int64_t rsv_off;                // split V rotation: hi then lo, 128 x 128
   int32_t krot_floats;            // sum_g d_g^2
   int32_t v_hadamard;             // 1: Pi_V = H_128 diag(vsign) / sqrt(128) exactly (fast transform)
+  int32_t mse_words;              // words of the MSE part of a key record
+  int32_t qjl;                    // 1: the record goes on with the residual sketch (4 words) and gamma
+  int64_t qjl_off;                // float offset of the sketch matrix S (row-major 128 x 128)
   uint8_t coord[kD];              // record position -> head coordinate
   uint8_t kp_pos[kD];             // record position -> its place in the K-block operands
                                   // (slot * 32 + coordinate within the block)

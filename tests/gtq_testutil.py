@@ -7,7 +7,7 @@ import math
 
 import numpy as np
 
-from gtq_inputs import head_inputs, head_rotations
+from gtq_inputs import head_inputs, head_rotations, qjl_matrix
 from oracle import gtq_oracle as O
 
 TOL_REL, TOL_ABS = 2e-3, 1e-4     # |gpu - ref| <= TOL_ABS + TOL_REL * |ref|
@@ -36,12 +36,14 @@ class Case:
     """Plans (oracle + library) and per-sequence inputs for n_layers x h_kv heads."""
 
     def __init__(self, seed, n_layers, h_kv, g, n_cache, k_budget, v_bits, batch=1, layout=O.HALF,
-                 n_dec_q=1, b_min=1, b_max=4, nc=False, v_hadamard=False):
+                 n_dec_q=1, b_min=1, b_max=4, nc=False, v_hadamard=False, qjl=False):
         import packed_cache_attention_tq_amd as G
         self.seed, self.L, self.H, self.g = seed, n_layers, h_kv, g
         self.HQ = h_kv * g
         self.n, self.k_budget, self.v_bits, self.batch, self.layout = n_cache, k_budget, v_bits, batch, layout
         self.nc = nc
+        self.qjl = np.stack([np.stack([qjl_matrix(seed, l, h) for h in range(h_kv)]) for l in range(n_layers)]) \
+            if qjl else None
         self.rates = np.zeros((n_layers, h_kv, 64), np.uint8)
         self.heads = {}
         k_rot_all, v_rot_all = [], []
@@ -61,7 +63,8 @@ class Case:
                 self.rates[l, h] = r_lib
                 dims = [len(c) for _, c in O.groups_from_rates(r, layout)]
                 kr, vr = head_rotations(seed, l, h, dims, v_hadamard=v_hadamard)
-                self.heads[l, h] = O.HeadPlan(r, kr, vr, v_bits, layout, nc=nc)
+                self.heads[l, h] = O.HeadPlan(r, kr, vr, v_bits, layout, nc=nc,
+                                              qjl=None if self.qjl is None else self.qjl[l, h])
                 kl.append(kr)
                 vl.append(vr)
             k_rot_all.append(kl)
@@ -71,7 +74,8 @@ class Case:
     def plan(self, host_only=False):
         import packed_cache_attention_tq_amd as G
         return G.Plan(self.L, self.H, self.HQ, self.k_budget, self.v_bits, self.rates, self.k_rot,
-                      self.v_rot, rope_layout=self.layout, host_only=host_only, norm_correct=self.nc)
+                      self.v_rot, rope_layout=self.layout, host_only=host_only, norm_correct=self.nc,
+                      qjl=self.qjl)
 
     def kv(self, l, b, lo=0, hi=None):
         """k, v [n_tok, H_kv, 128] of sequence b, tokens lo..hi-1."""
@@ -140,6 +144,38 @@ def compare_codes(gpu_codes, ref_codes, ref_z, bits, what):
         raise AssertionError(f"{what}: {hard.sum()} code mismatches outside the tie window; first at {i}: "
                              f"gpu={gpu_codes[i]} ref={ref_codes[i]} z={ref_z[i]!r}")
     return int((mism & ties).sum())
+
+
+def compare_qjl(gpu_words, gpu_norms, k, enc, plan, what, rel_window=1e-9):
+    """The residual sketch of GPU records [n, words] against the oracle's encoding: sign
+    bits equal except where the oracle's projection lies within rel_window * |S| |r| of
+    zero (both sides compute S r in fp64, in different orders), gamma bit for bit. A token
+    whose MSE codes took the other side of a tie has another residual: for such tokens
+    the oracle sketches k minus the key decoded from the GPU's own MSE record (k [n, 128]
+    the fp32 keys, gpu_norms [n, groups]). Returns the number of near-zero sign
+    differences."""
+    gpu_words = np.asarray(gpu_words, np.uint32)
+    mw = plan.mse_words
+    bits_ref = enc["qjl_bits"].copy()
+    gamma_ref = enc["qjl_gamma"].copy()
+    proj_ref = enc["qjl_proj"].copy()
+    moved = np.flatnonzero((gpu_words[:, :mw] != enc["k_words"][:, :mw]).any(axis=1))
+    if moved.size:
+        k64 = np.asarray(k, np.float32)[moved].astype(np.float64)
+        r = k64 - O.dequantized_keys(plan, gpu_words[moved, :mw], np.asarray(gpu_norms)[moved])
+        gamma_ref[moved], bits_ref[moved], proj_ref[moved] = O.qjl_encode(r, plan.qjl)
+    bits, gamma = O.qjl_fields(plan, gpu_words)
+    mism = bits != bits_ref
+    scale = np.abs(plan.qjl).max() * np.maximum(gamma_ref.astype(np.float64), 1e-30) * 128
+    near = np.abs(proj_ref) < rel_window * scale[:, None]
+    hard = mism & ~near
+    STATS["codes"] += int(mism.size)
+    STATS["code_ties"] += int((mism & near).sum())
+    if hard.any():
+        i = tuple(np.argwhere(hard)[0])
+        raise AssertionError(f"{what}: {hard.sum()} sketch bits differ; first at {i}: proj={proj_ref[i]!r}")
+    compare_norms(gamma, gamma_ref, f"{what} gamma")
+    return int((mism & near).sum())
 
 
 def compare_norms(gpu, ref, what):

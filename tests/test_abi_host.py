@@ -162,12 +162,33 @@ def test_error_paths(lib):
     with pytest.raises(G.GtqError) as e:
         G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True, head_dim=64)
     _expect(e, 2, "head_dim")
-    # the norm-corrected flag is accepted, any other bit is not
+    # the norm-corrected and QJL flags are accepted, any other bit is not
     G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True, norm_correct=True).destroy()
-    desc = G.PlanDesc(2, 2, 4, 128, 0, 128, 2, G.PLAN_HOST_ONLY | 4, None, None, None)
+    S = np.ones((2, 2, 128, 128), np.float32)
+    qp = G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True, qjl=S)
+    qs = qp.cache_sizes(1, 64)
+    assert qs.k_words == 8 + 5
+    assert qs.logical_bits_per_token == 2 * 128 + 128 * 2 + 128
+    qp.destroy()
+    desc = G.PlanDesc(2, 2, 4, 128, 0, 128, 2, G.PLAN_HOST_ONLY | 8, None, None, None)
     h = C.c_void_p()
     assert lib.gtq_plan_create(C.byref(desc), C.byref(h)) == 1
     assert b"flags" in lib.gtq_last_error()
+    # the QJL flag and its matrices go together; its records hold at most 16 words
+    rq = rates.copy()
+    rq[:, :, :] = 1
+    rq[:, :, :56] = 3
+    krq = [[[np.eye(len(c), dtype=np.float32) for _, c in O.groups_from_rates(rq[l, h], O.HALF)]
+            for h in range(2)] for l in range(2)]
+    G.Plan(2, 2, 4, 176, 2, rq, krq, vrot, host_only=True, qjl=S).destroy()   # 11 + 5 words
+    rq[:, :, 56:64] = 3
+    krq = [[[np.eye(len(c), dtype=np.float32) for _, c in O.groups_from_rates(rq[l, h], O.HALF)]
+            for h in range(2)] for l in range(2)]
+    with pytest.raises(G.GtqError) as e:
+        G.Plan(2, 2, 4, 192, 2, rq, krq, vrot, host_only=True, qjl=S)
+    _expect(e, 2, "176")
+    desc = G.PlanDesc(2, 2, 4, 128, 0, 128, 2, G.PLAN_HOST_ONLY | G.PLAN_QJL, None, None, None)
+    assert lib.gtq_plan_create(C.byref(desc), C.byref(h)) == 1
     p = G.Plan(2, 2, 4, 128, 2, rates, krot, vrot, host_only=True)
     with pytest.raises(G.GtqError) as e:
         p.layout(2, 0)

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from oracle import gtq_oracle as O
-from gtq_testutil import (Case, assert_close, compare_codes, compare_norms, scale_default,
+from gtq_testutil import (Case, assert_close, compare_codes, compare_norms, compare_qjl, scale_default,
                           unpack_key_record, v_codes_from_physical, v_codes_to_physical)
 
 pytestmark = pytest.mark.gpu
@@ -419,6 +419,54 @@ def test_binary16_operand_ranges(G, mode):
                                       enc[h]["v_words"], enc[h]["v_norms"], sc)
             assert np.abs(ref).max() > 1e3
             assert_close(out[:, sl].cpu().numpy() / 1e4, ref / 1e4, f"prefill out h{h}")
+
+
+@pytest.mark.parametrize("k_budget", [64, 128])
+def test_qjl_residual_sketch(G, k_budget):
+    """TurboQuant-prod keys (QJL residual sketch, GTQ_PLAN_QJL) at 2 and 3 bits (K1 / K2
+    MSE part + one sketch bit per coordinate): records from the chunk append (through the
+    per-token kernel) and from the fused decode step against the oracle (MSE codes, norms
+    and gamma bit-exact, sketch signs except at near-zero projections), then decode over
+    the GPU's records against the oracle: ragged batch, explicit and automatic split."""
+    _say(f"case: QJL residual sketch, k_budget={k_budget}")
+    case = Case(31, 1, 2, 4, 300, k_budget, 2, batch=2, qjl=True)
+    plan = case.plan()
+    lens = [300, 171]
+    cache = G.PackedCache(plan, 2, 320)
+    ties = 0
+    for b, n in enumerate(lens):
+        k, v = case.kv(0, b, 0, n - 1)
+        G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k), _dev(v), b, 0)
+    # the newest token through the fused step (decode_prep's per-token append)
+    knew = np.stack([case.kv(0, b, n - 1, n)[0][0] for b, n in enumerate(lens)])
+    vnew = np.stack([case.kv(0, b, n - 1, n)[1][0] for b, n in enumerate(lens)])
+    q = np.stack([case.q(0, b) for b in range(2)])
+    sc = scale_default()
+    out_step = G.gtq_decode_step(plan, 0, cache, _dev(knew), _dev(vnew), _dev(q),
+                                 _dev(np.array(lens, np.int32)), 320, sc)
+    torch.cuda.synchronize()
+    kc, kn, vc, vn = _cache_arrays(cache, case)
+    for b, n in enumerate(lens):
+        encs = _encode(case, 0, b, n)
+        t, _ = _check_append(case, cache, 0, b, n, encs, f"qjl append b{b}")
+        ties += t
+        for h in range(case.H):
+            ng = len(case.heads[0, h].groups)
+            ties += compare_qjl(kc[b, h, :n], kn[b, h, :n, :ng], case.inputs[0, h][b]["k"][:n], encs[h],
+                                case.heads[0, h], f"qjl sketch b{b} h{h}")
+    recs = [_records_from_gpu(case, cache, 0, b, n) for b, n in enumerate(lens)]
+    for chunk in (64, 0):
+        out = G.gtq_decode_attn(plan, 0, cache, _dev(q), _dev(np.array(lens, np.int32)), 320, sc, chunk=chunk)
+        torch.cuda.synchronize()
+        for b, n in enumerate(lens):
+            _, ref = _oracle_decode(case, 0, b, n, recs[b], q[b], sc)
+            assert_close(out[b].cpu().numpy(), ref, f"qjl decode b{b} chunk={chunk}")
+    for b, n in enumerate(lens):
+        _, ref = _oracle_decode(case, 0, b, n, recs[b], q[b], sc)
+        assert_close(out_step[b].cpu().numpy(), ref, f"qjl decode step b{b}")
+    _say(f"  qjl: sketch sign ties={ties}")
+    with pytest.raises(G.GtqError, match="decode only"):
+        G.gtq_prefill_attn(plan, 0, cache, _dev(np.zeros((4, case.HQ, 128), np.float32)), 0, 100, sc)
 
 
 def test_edge_cases(G):
