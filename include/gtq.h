@@ -169,11 +169,17 @@ typedef struct gtq_plan_desc {
 typedef struct gtq_plan gtq_plan;
 
 /* Builds a plan: group layouts, codebooks, decode tables; copies the rotations and
- * uploads everything to the current HIP device (unless GTQ_PLAN_HOST_ONLY). The plan
+ * uploads everything to the current HIP device (unless GTQ_PLAN_HOST_ONLY). The pages
+ * have no passage for this step as a call of its own; what it sets up is the grouping of
+ * equal-rate blocks ("Block-GTQ" abstract, 5th sentence) and the rotate / per-coordinate
+ * quantizer pair of each group ("TurboQuant: paper algorithm and vLLM engineering"
+ * diagram, paper column, rotate and scalar-MSE boxes). The plan
  * is immutable afterwards and may be used from several streams at once.
  * Errors: EINVAL (NULL, counts < 1, rates outside [1,4] or not summing to k_budget,
- * k_budget not a multiple of 16, v_bits outside [1,4], bad flags/layout);
- * EUNSUPPORTED (head_dim != 128); ENOMEM; EDEVICE (no device / upload failed). */
+ * k_budget not a multiple of 16, v_bits outside [1,4], bad flags/layout, GTQ_PLAN_QJL
+ * without the qjl matrices or the matrices without the flag);
+ * EUNSUPPORTED (head_dim != 128; GTQ_PLAN_QJL with k_budget > 176); ENOMEM; EDEVICE (no
+ * device / upload failed). */
 gtq_status gtq_plan_create(const gtq_plan_desc* desc, gtq_plan** out);
 /* Frees the plan (host and device copies). Synchronizes the device. NULL is a no-op. */
 gtq_status gtq_plan_destroy(gtq_plan* plan);
@@ -363,11 +369,15 @@ gtq_status gtq_decode_step(const gtq_plan* plan, int32_t layer, const gtq_cache_
 gtq_status gtq_prefill_workspace_bytes(const gtq_plan* plan, int64_t pos0, int64_t n_tok,
                                        int32_t chunk, size_t* out);
 
-/* Causal attention of a prompt chunk over the packed cache of sequence `seq`:
+/* Causal attention of a prompt chunk over the packed cache of sequence `seq`. No passage
+ * of the pages describes prefill; it is the attention over packed caches of the
+ * "Block-GTQ" abstract (5th sentence) applied to the query rows of a prompt chunk, each
+ * seeing the cached positions up to its own:
  * q device [n_tok][n_q_heads][128] fp32 (post-RoPE) at positions pos0 .. pos0+n_tok-1;
  * the chunk's own keys/values must already be appended (gtq_quantize_append_chunk).
  * Query t sees cached positions 0 .. pos0 + t. out device [n_tok][n_q_heads][128].
- * Errors: as gtq_decode_attn; ECAPACITY if pos0 + n_tok > capacity. */
+ * Errors: as gtq_decode_attn; ECAPACITY if pos0 + n_tok > capacity; EUNSUPPORTED for a
+ * GTQ_PLAN_QJL plan. */
 gtq_status gtq_prefill_attn(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
                             const float* q, int32_t seq, int64_t pos0, int64_t n_tok,
                             float softmax_scale, int32_t chunk, float* out, void* workspace,

@@ -41,7 +41,7 @@ Readings where the pages are silent (each also listed in the design notes):
       result does without): the first n_sink positions and the last n_recent
       positions of a sequence attend through fp16 copies of their K and V (binary16,
       round to nearest even), every other position through the packed cache.
-  R23 QJL residual sketch (TurboQuant-prod): keys only (it corrects q . k); the
+  R24 QJL residual sketch (TurboQuant-prod): keys only (it corrects q . k); the
       residual is r = k - k_hat in head coordinates, k_hat the TQ-MSE reconstruction of
       the stored record (fp64); S is an m x 128 matrix of N(0,1) entries (m = 128, one
       bit per coordinate), drawn per (layer, KV head) and passed in like the rotations;
@@ -292,7 +292,7 @@ def unpack_codes(words: np.ndarray, dims: list[int], rates: list[int]) -> list[n
 
 
 # --------------------------------------------------------------------------
-# 1-bit QJL residual sketch (TurboQuant-prod)  [TQ-diag residual, QJL], R23
+# 1-bit QJL residual sketch (TurboQuant-prod)  [TQ-diag residual, QJL], R24
 # --------------------------------------------------------------------------
 
 QJL_M = 128  # sketch rows: one sign bit per key coordinate
@@ -338,7 +338,7 @@ def qjl_fields(plan, k_words):
 
 class HeadPlan:
     """Rates, groups, rotations and V rate of one (layer, KV head); qjl: the residual
-    sketch matrix S [128, 128] (R23) or None."""
+    sketch matrix S [128, 128] (R24) or None."""
 
     def __init__(self, rates, k_rots: list[np.ndarray], v_rot: np.ndarray, v_bits: int,
                  layout: int = HALF, nc: bool = False, qjl=None):
@@ -375,7 +375,7 @@ class HeadPlan:
 def encode_kv(plan: HeadPlan, k: np.ndarray, v: np.ndarray) -> dict:
     """Encode tokens k, v [n, 128] of one KV head into the packed record
     (K words, K norms per group, V words, V norm) [BGTQ s5], [TQ-diag]. With a QJL plan
-    the key record goes on with the residual's sketch words and gamma's bits (R23)
+    the key record goes on with the residual's sketch words and gamma's bits (R24)
     [TQ-diag residual, QJL]."""
     kn, kc, kz = [], [], []
     for (r, coords), rot in zip(plan.groups, plan.k_rots):
