@@ -204,7 +204,7 @@ def partials_kernel_name(plan, layer, h_kv, v_bits, paged=False):
     n4 = min(n4, 3, 4 - n1)
     if paged:
         n1 = n4 = 0
-    return f"attn_decode_kernel<{v_bits}, {kwl}, {n1}, {n4}, {'true' if paged else 'false'}>"
+    return f"attn_decode_kernel<{v_bits}, {kwl}, {n1}, {n4}, {'true' if paged else 'false'}, false>"
 
 
 # ---------------------------------------------------------------- decode workloads

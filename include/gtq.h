@@ -278,8 +278,9 @@ gtq_status gtq_quantize_append_chunk(const gtq_plan* plan, int32_t layer,
  * sequence and KV head) equally: G = the device's compute units for chunk 0, else
  * tiles x ceil(max_len / chunk). The workspace holds the rotated queries (8 KB per
  * tile) and the split-K partials (m, l, acc[128] of 8 rows per piece of a tile that
- * one workgroup runs, G + tiles - 1 at most, plus one per tile for a window split);
- * its contents need no initialisation.
+ * one workgroup runs, G + tiles - 1 at most, plus one per tile for a window split) and
+ * 16 bytes per tile that tell the merge where the tile's pieces are; its contents need
+ * no initialisation.
  * Calls that share a workspace must be ordered on one stream. */
 gtq_status gtq_decode_workspace_bytes(const gtq_plan* plan, int32_t batch, int64_t max_len,
                                       int32_t chunk, size_t* out);

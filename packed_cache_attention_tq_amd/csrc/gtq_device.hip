@@ -607,8 +607,8 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
   const int vlo = role == 2 ? kD / 2 : 0, vhi = (role == 1 && vsplit) ? kD / 2 : kD;
   const bool mine = role == 3 || (role == 0 ? o < kD : (o >= kD + vlo && o < kD + vhi));
   const bool do_k = role == 0 || role == 3, do_v = role != 0;
-  float2 pk[16];
-  float4 pv[8];
+  // (key: column pairs klo + 2u and klo + 2u + 1 in rv[u]; value: columns 32 qq + 4u ..)
+  float4 rv[8];
   int kg = 0, klo = 0, khi = 0;
   if (o < kD) {
     kg = group_of(GL, o);
@@ -618,11 +618,15 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     if (!mine) khi = klo;  // (no key work outside role 0)
     const float2* pr = reinterpret_cast<const float2*>(a.rot + pick(GL.krot, kg) + (size_t)i * d);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) pk[u] = (klo + u < khi) ? pr[klo + u] : make_float2(0.f, 0.f);
+    for (int u = 0; u < 8; ++u) {
+      const float2 p0 = (klo + 2 * u < khi) ? pr[klo + 2 * u] : make_float2(0.f, 0.f);
+      const float2 p1 = (klo + 2 * u + 1 < khi) ? pr[klo + 2 * u + 1] : make_float2(0.f, 0.f);
+      rv[u] = make_float4(p0.x, p0.y, p1.x, p1.y);
+    }
   } else {
     const float4* pr = reinterpret_cast<const float4*>(a.rot + hd->vrot_off + (size_t)(o - kD) * kD + 32 * qq);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) pv[u] = (hd->v_hadamard || !mine) ? make_float4(0.f, 0.f, 0.f, 0.f) : pr[u];
+    for (int u = 0; u < 8; ++u) rv[u] = (hd->v_hadamard || !mine) ? make_float4(0.f, 0.f, 0.f, 0.f) : pr[u];
   }
   // (a chunk through this kernel: no index arrays, token tok of sequence a.seq at pos0 + tok)
   const int seq = a.step_len ? (int)tok : (a.seq_idx ? a.seq_idx[tok] : a.seq);
@@ -685,21 +689,26 @@ __device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h
     if (o < kD) {
       const float2* x = reinterpret_cast<const float2*>(xs + pick(GL.pos, kg));
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (klo + u < khi) {
-          const float2 xx = x[klo + u];
-          acc = fmaf(pk[u].x, xx.x, acc);
-          acc = fmaf(pk[u].y, xx.y, acc);
+      for (int u = 0; u < 8; ++u) {
+        if (klo + 2 * u < khi) {
+          const float2 xx = x[klo + 2 * u];
+          acc = fmaf(rv[u].x, xx.x, acc);
+          acc = fmaf(rv[u].y, xx.y, acc);
+        }
+        if (klo + 2 * u + 1 < khi) {
+          const float2 xx = x[klo + 2 * u + 1];
+          acc = fmaf(rv[u].z, xx.x, acc);
+          acc = fmaf(rv[u].w, xx.y, acc);
         }
       }
     } else if (!hd->v_hadamard) {
       const float* x = xs + kD + 32 * qq;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        acc = fmaf(pv[u].x, x[4 * u], acc);
-        acc = fmaf(pv[u].y, x[4 * u + 1], acc);
-        acc = fmaf(pv[u].z, x[4 * u + 2], acc);
-        acc = fmaf(pv[u].w, x[4 * u + 3], acc);
+        acc = fmaf(rv[u].x, x[4 * u], acc);
+        acc = fmaf(rv[u].y, x[4 * u + 1], acc);
+        acc = fmaf(rv[u].z, x[4 * u + 2], acc);
+        acc = fmaf(rv[u].w, x[4 * u + 3], acc);
       }
     }
     red[qq][o] = acc;
@@ -914,6 +923,9 @@ struct AttnArgs {
   // s = w + t; the window split of tile t: s = sk_G + n_tiles + t), row r of the tile:
   // partials + (8 s + r) kPS
   int32_t batch, n_tiles, sk_G;
+  // decode: per row tile, written by the workgroup that runs its first block: (first
+  // workgroup w0 on it, its number of workgroups, all units low and high 32 bits)
+  int4* tile_info;
 };
 
 // End of the packed positions of a sequence of length L with n_sink sink and n_recent
@@ -934,32 +946,6 @@ __device__ inline int sk_owner(int64_t u, int G, int64_t U) { return (int)(((u +
 // whether workgroup w has units (with fewer units than workgroups some have none, and
 // write no partial)
 __device__ inline bool sk_live(int64_t w, int G, int64_t U) { return (w + 1) * U / G > w * U / G; }
-
-// U and the units of the sequences before `seq`, summed by the 256 threads of a merge
-// workgroup (every thread gets both)
-__device__ inline void sk_sums256(const int32_t* seq_len, int batch, int seq, int tps, int max_len, int win,
-                                  int n_sink, int n_recent, long long* U, long long* P) {
-  __shared__ long long red_u[4], red_p[4];
-  const int tid = threadIdx.x;
-  long long u = 0, pb = 0;
-  for (int b = tid; b < batch; b += 256) {
-    const long long x = (long long)tps * seq_blocks(seq_len, b, max_len, win, n_sink, n_recent);
-    u += x;
-    if (b < seq) pb += x;
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    u += __shfl_xor(u, m);
-    pb += __shfl_xor(pb, m);
-  }
-  if ((tid & 63) == 0) {
-    red_u[tid >> 6] = u;
-    red_p[tid >> 6] = pb;
-  }
-  __syncthreads();
-  *U = red_u[0] + red_u[1] + red_u[2] + red_u[3];
-  *P = red_p[0] + red_p[1] + red_p[2] + red_p[3];
-}
 
 // tile -> (sequence, KV head, tile within the head)
 __device__ inline void tile_coords(const AttnArgs& a, int tile, int* seq, int* h, int* tr) {
@@ -2269,6 +2255,7 @@ struct DecShared {
                                      // past a wave's records: still inside S); between a
                                      // segment's loop and its partial, eight merge slots
   long long sk_u0, sk_u1, sk_P;      // this workgroup's next unit, its end, the units before sk_b
+  long long sk_U;                    // all units of the batch
   int32_t sk_b;                      // the sequence of the next unit (or an earlier, empty one)
   int32_t sk_tile;                   // the current segment's row tile
   uint4 qb[kMaxKB - 1][4][16];       // query operands of the K-block slots
@@ -2368,7 +2355,7 @@ __device__ inline float row_max(float x) {
   return max_over_q(x);
 }
 
-template <int VB, int KWL, int N1, int N4, bool PAGED>
+template <int VB, int KWL, int N1, int N4, bool PAGED, bool QJL>
 __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) attn_decode_kernel(AttnArgs a) {
   constexpr int NS = kMaxKB - 1;  // K-block slots (a head has at most 7)
   __shared__ DecShared S;
@@ -2464,6 +2451,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
       S.sk_u1 = u1;
       S.sk_P = Ps;
       S.sk_b = bs;
+      S.sk_U = U;
     }
   }
   if (tid < kPairTable) S.u.t.lut[tid] = lutv;
@@ -2549,7 +2537,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
     // one round of independent loads: query operands (to LDS), rows, the first block
     static_assert(NS * 64 <= kDecThreads, "one query operand per thread");
     const uint4 qg = tid < NS * 64 ? A.qb[(size_t)tile * kQB + tid] : make_uint4(0, 0, 0, 0);
-    const uint4 qjg = (A.qjl && tid < 4 * 64) ? A.qjl_qb[(size_t)tile * 256 + tid] : make_uint4(0, 0, 0, 0);
+    const uint4 qjg = (QJL && tid < 4 * 64) ? A.qjl_qb[(size_t)tile * 256 + tid] : make_uint4(0, 0, 0, 0);
     const int len_ld = A.seq_len[seq];
     const float xs = A.tile_xs[tile];
     DecBlock<VB, KWL> blk;
@@ -2567,7 +2555,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
       }
     }
     if (tid < NS * 64) (&S.qb[0][0][0])[tid] = qg;
-    if (A.qjl && tid < 4 * 64) (&S.qjlb[0][0][0])[tid] = qjg;
+    if (QJL && tid < 4 * 64) (&S.qjlb[0][0][0])[tid] = qjg;
     if (tid < 8) {
       int L;
       S.row_id[tid] = tile_row<8>(A, seq, h, tr, tid, len_ld, &L);
@@ -2579,6 +2567,11 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
       S.sk_P = Pb;
       S.sk_b = b;
       S.sk_tile = tile;
+      if (bb == 0) {  // this workgroup runs the tile's first block: the merge's pointers
+        const long long Ua = S.sk_U;
+        const int w1 = sk_owner(Ut + nb - 1, G, Ua);
+        A.tile_info[tile] = make_int4(wg, w1 - wg + 1, (int)(Ua & 0xFFFFFFFFll), (int)(Ua >> 32));
+      }
     }
     // every present row of a decode tile has the sequence's length (c0 lies inside it)
     int tile_len = 0;
@@ -2623,7 +2616,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
     // ---- stage the key records and key norms; the value words and norms stay in registers
 #pragma unroll
     for (int i = 0; i < KWL; ++i) W.ktile[kst + i * (64 / kRowW) * kKPitch] = blk.kr[i];
-    if (a.qjl && lane % kRowW == a.mse_words + 4) {  // the QJL gamma (record word mse + 4)
+    if (QJL && lane % kRowW == a.mse_words + 4) {  // the QJL gamma (record word mse + 4)
 #pragma unroll
       for (int i = 0; i < KWL; ++i) W.knt[kMaxGroups][lane / kRowW + i * (64 / kRowW)] = __builtin_bit_cast(float, blk.kr[i]);
     }
@@ -2684,7 +2677,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
       lg[4] = fmaf(nb.x, d1[0], lg[4]); lg[5] = fmaf(nb.y, d1[1], lg[5]);
       lg[6] = fmaf(nb.z, d1[2], lg[6]); lg[7] = fmaf(nb.w, d1[3], lg[7]);
     }
-    if (a.qjl) {
+    if constexpr (QJL) {
       // the residual sketch: four 32-bit slots after the MSE words, decoded like rate-1
       // codes (centroids c1 sign_j) against B = S q scaled, times gamma
       floatx4 d0 = z4, d1 = z4;
@@ -2948,6 +2941,7 @@ struct MergeArgs {
   int32_t n_q, g, n_chunks, chunk, prefill, max_len;
   int32_t win, n_sink, n_recent;  // fp16 window: its split is the last slot
   int32_t batch, n_kv, tiles_per_kv, n_tiles, sk_G;  // decode: the partials' segments (AttnArgs)
+  const int4* tile_info;                             // decode: (w0, segments, units) per tile
 };
 
 // Four workgroups (256 threads each) per row, one per quarter of the output coordinates:
@@ -2978,18 +2972,17 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   if (a.prefill) {
     nv = (len_p + a.chunk - 1) / a.chunk;
   } else {
-    const int seq = row / a.n_q, f = hq % a.g, tps = a.n_kv * a.tiles_per_kv;
+    const int seq = row / a.n_q, f = hq % a.g;
     tile = (seq * a.n_kv + hq / a.g) * a.tiles_per_kv + f / 8;
     r8 = f & 7;
-    long long P;
-    sk_sums256(a.seq_len, a.batch, seq, tps, a.max_len, a.win, a.n_sink, a.n_recent, &U, &P);
+    const int4 inf = a.tile_info[tile];  // (written only for tiles with blocks)
     const int nb = (len_p + 31) >> 5;
     int nseg = 0;
     if (nb > 0) {
-      const long long Ut = P + (long long)(tile - seq * tps) * nb;
-      w0 = sk_owner(Ut, a.sk_G, U);
+      w0 = inf.x;
       first = w0 + tile;
-      nseg = sk_owner(Ut + nb - 1, a.sk_G, U) - w0 + 1;
+      nseg = inf.y;
+      U = (long long)(((unsigned long long)(unsigned)inf.w << 32) | (unsigned)inf.z);
     }
     nv = nseg + a.win;
   }
@@ -3128,6 +3121,7 @@ struct MergeTileArgs {
   int32_t n_q, g, n_kv, tiles_per_kv, n_tok, n_chunks, chunk, prefill, max_len, seq;
   int32_t win, n_sink, n_recent;  // fp16 window: its split is the last slot
   int32_t batch, n_tiles, sk_G;   // decode: the partials' segments (AttnArgs)
+  const int4* tile_info;          // decode: (w0, segments, units) per tile
 };
 
 __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
@@ -3167,15 +3161,13 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
   int first = 0, nseg = 0, w0 = 0;
   long long U = 0;
   if (!a.prefill) {
-    const int tps = a.n_kv * a.tiles_per_kv;
-    long long P;
-    sk_sums256(a.seq_len, a.batch, seq, tps, a.max_len, a.win, a.n_sink, a.n_recent, &U, &P);
+    const int4 inf = a.tile_info[tile];  // (written only for tiles with blocks)
     const int nb = seq_blocks(a.seq_len, seq, a.max_len, a.win, a.n_sink, a.n_recent);
     if (nb > 0) {
-      const long long Ut = P + (long long)(tile - seq * tps) * nb;
-      w0 = sk_owner(Ut, a.sk_G, U);
+      w0 = inf.x;
       first = w0 + tile;
-      nseg = sk_owner(Ut + nb - 1, a.sk_G, U) - w0 + 1;
+      nseg = inf.y;
+      U = (long long)(((unsigned long long)(unsigned)inf.w << 32) | (unsigned)inf.z);
     }
   }
   // row r of the tile: global row id (-1 if absent) and visible length
@@ -3451,9 +3443,10 @@ size_t attn_ws_bytes(int64_t rows, int64_t n_chunks, size_t qb_bytes) {
   return qb_bytes + (size_t)rows * n_chunks * kPS * 4;
 }
 // decode: one 8-row partial per (workgroup, tile) segment, w + t < sk_G + n_tiles, then
-// one per tile for the window's split
+// one per tile for the window's split; then the tiles' merge pointers (16 bytes each)
+size_t decode_part_bytes(int64_t n_tiles, int sk_G) { return (size_t)(sk_G + 2 * n_tiles) * 8 * kPS * 4; }
 size_t decode_ws_bytes(int64_t n_tiles, int sk_G, size_t qb_bytes) {
-  return qb_bytes + (size_t)(sk_G + 2 * n_tiles) * 8 * kPS * 4;
+  return qb_bytes + decode_part_bytes(n_tiles, sk_G) + (size_t)n_tiles * 16;
 }
 
 struct AttnLaunch {
@@ -3485,6 +3478,9 @@ void fill_attn_args(const gtq_plan* p, int layer, const gtq_cache_view* c, AttnA
   aa.qjl_qb = aa.qjl ? reinterpret_cast<uint4*>(reinterpret_cast<char*>(aa.tile_xs) + ((size_t)L.n_tiles * 4 + 15) / 16 * 16)
                      : nullptr;
   aa.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + L.qb_bytes);
+  aa.tile_info = L.rt == 8 ? reinterpret_cast<int4*>(reinterpret_cast<char*>(ws) + L.qb_bytes +
+                                                     decode_part_bytes(L.n_tiles, L.sk_G))
+                           : nullptr;
   aa.capacity = c->capacity;
   aa.n_kv = p->n_kv;
   aa.n_q = p->n_q;
@@ -3517,11 +3513,16 @@ gtq_status launch_qrot(AttnArgs& aa, const AttnLaunch& L, const float* q, float 
 // counts (N1 <= 3, N4 <= min(3, 4 - N1))
 template <int VB, int KWL>
 void launch_decode(dim3 grid, int n1, int n4, const AttnArgs& aa, hipStream_t stream) {
-  if (aa.pm.table) {  // paged caches: every slot through the generic path
-    hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, 0, 0, true>), grid, dim3(kDecThreads), 0, stream, aa);
+  if (aa.qjl) {  // QJL plans: every slot through the generic path, and the sketch
+    if (aa.pm.table) hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, 0, 0, true, true>), grid, dim3(kDecThreads), 0, stream, aa);
+    else hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, 0, 0, false, true>), grid, dim3(kDecThreads), 0, stream, aa);
     return;
   }
-#define GTQ_DEC(A, B) hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, A, B, false>), grid, dim3(kDecThreads), 0, stream, aa)
+  if (aa.pm.table) {  // paged caches: every slot through the generic path
+    hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, 0, 0, true, false>), grid, dim3(kDecThreads), 0, stream, aa);
+    return;
+  }
+#define GTQ_DEC(A, B) hipLaunchKernelGGL((attn_decode_kernel<VB, KWL, A, B, false, false>), grid, dim3(kDecThreads), 0, stream, aa)
   switch (n1 * 4 + n4) {
     case 0: GTQ_DEC(0, 0); break;
     case 1: GTQ_DEC(0, 1); break;
@@ -3601,6 +3602,9 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
                         hipStream_t stream, const gtq_window_view* w = nullptr) {
   const float* vrot_t = p->d_rot + p->heads[(size_t)layer * p->n_kv].vrot_t_off;
   const float* partials = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + L.qb_bytes);
+  const int4* tile_info = prefill ? nullptr
+                                  : reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ws) + L.qb_bytes +
+                                                                  decode_part_bytes(L.n_tiles, L.sk_G));
   // one workgroup per row tile when few partials per row are expected (prefill: at most
   // kMergeTileChunks splits; decode: about sk_G / n_tiles + 2 segments per tile)
   const bool tile_merge = prefill ? L.n_chunks <= kMergeTileChunks : L.sk_G <= 4 * L.n_tiles;
@@ -3615,6 +3619,7 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
     mt.batch = (int32_t)(L.rows / p->n_q);
     mt.n_tiles = L.n_tiles;
     mt.sk_G = L.sk_G;
+    mt.tile_info = tile_info;
     hipLaunchKernelGGL(attn_merge_tile_kernel, dim3((unsigned)L.merge_n_tiles, merge_quarters(L.merge_n_tiles)),
                        dim3(256), 0, stream, mt);
   } else {  // one workgroup per row
@@ -3630,6 +3635,7 @@ gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const
     ma.tiles_per_kv = L.merge_tiles_per_kv;
     ma.n_tiles = L.n_tiles;
     ma.sk_G = L.sk_G;
+    ma.tile_info = tile_info;
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)L.rows, merge_quarters(L.rows)), dim3(256), 0, stream, ma);
   }
   hipError_t e = hipGetLastError();

@@ -211,10 +211,10 @@ def test_error_paths(lib):
     # 8 KB) and one range factor per tile (padded to 16 bytes), then 8-row partials of
     # 132 floats (m, l, 2 pad, acc[128]): one per (workgroup, tile) segment, i.e. G +
     # tiles - 1 of them with G = tiles * chunks workgroups for an explicit chunk, and one
-    # per tile for the window's split
+    # per tile for the window's split; then 16 bytes per tile (the merge's pointers)
     chunks, tiles = (1000 + 63) // 64, 2 * 2
     n_wg = tiles * chunks
-    exp = tiles * 8192 + (tiles * 4 + 15) // 16 * 16 + (n_wg + 2 * tiles) * 8 * 132 * 4
+    exp = tiles * 8192 + (tiles * 4 + 15) // 16 * 16 + (n_wg + 2 * tiles) * 8 * 132 * 4 + tiles * 16
     assert ws.value == exp
     assert lib.gtq_decode_workspace_bytes(p.handle, 1, 100000, 32, C.byref(ws)) == 1
     assert b"256 splits" in lib.gtq_last_error()
