@@ -616,9 +616,11 @@ def bench_logit_mae(args):
 
 def bench_window(args, n_sink=4, n_recent=128):
     """decode-8b-window: the Llama-3.1-8B-shaped layer decode (32768 cached tokens, K2V2,
-    32 query / 8 KV heads) with fp16 sink and recent-token buffers: a step appends its
-    token to the packed cache and to the fp16 ring, then attends (window split in the
-    query-rotation launch, packed partials over positions [n_sink, L - n_recent), merge)."""
+    32 query / 8 KV heads) with fp16 sink and recent-token buffers: a step
+    (gtq_decode_step_window) appends its token to the packed cache and to the fp16 ring
+    and rotates the queries in one launch, whose window-split workgroups also write the
+    token to the ring first; then the packed partials over positions [n_sink, L - n_recent)
+    and the merge."""
     import torch
 
     import packed_cache_attention_tq_amd as G
@@ -648,14 +650,18 @@ def bench_window(args, n_sink=4, n_recent=128):
 
     def run():
         for c in caches:
-            G.gtq_quantize_append(plan, 0, c, k_new, v_new, sidx, slot)
-            G.gtq_window_append(plan, 0, win, k_new, v_new, sidx, slot)
+            G.gtq_decode_step_window(plan, 0, c, win, k_new, v_new, q, seq_len, n, scale, chunk=args.chunk, out=out,
+                                     workspace=ws)
+
+    def attend():
+        for c in caches:
             G.gtq_decode_attn_window(plan, 0, c, win, q, seq_len, n, scale, chunk=args.chunk, out=out, workspace=ws)
 
     ms = graph_ms(run, args.steps, args.warmup, per=len(caches))
+    att_ms = graph_ms(attend, args.steps, min(args.warmup, 2), per=len(caches))
     packed = n - n_sink - n_recent
     alg = packed * h_kv * base.sizes.bytes_per_token + (n_sink + n_recent) * h_kv * 512
-    return {
+    res = {
         "metric": "packed-KV decode attention with fp16 sink + recent window: KV tokens/s",
         "value": round(n / (ms / 1e3), 1), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -663,9 +669,64 @@ def bench_window(args, n_sink=4, n_recent=128):
         "data": "synthetic",
         "config": {"workload": "decode-8b-window", "seq_len": n, "n_sink": n_sink, "n_recent": n_recent,
                    "k_bits_avg": kb / 64, "v_bits": vb, "cache_copies": len(caches),
-                   "step": "packed append + window append (1 token) + window decode (3 launches)"},
+                   "step": "gtq_decode_step_window: prepare (packed append, window append + window split, "
+                           "query rotation), partials, merge (3 launches)"},
+        "roofline": hbm_roofline("gtq_decode_attn_window (window split + query rotation, partials, merge)", alg,
+                                 att_ms, "decode-8b-window",
+                                 {"timing": "HIP events around a graph of back-to-back gtq_decode_attn_window "
+                                            "calls (3 launches each)"}),
         "step_hbm_gbs": round(alg / (ms / 1e3) / 1e9, 1),
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded slice ...")
+        res["cpu_baseline"] = cpu_baseline_window(args, rates, krot, vrot, h_kv, g, n, kb, vb, n_sink, n_recent)
+    return res
+
+
+def cpu_baseline_window(args, rates, krot, vrot, h_kv, g, n, kb, vb, n_sink, n_recent):
+    """The fp64 oracle on one KV head of the step: encode of the step's token, then the
+    window decode of its g query heads over n positions (packed records + binary16 window),
+    repeated over the KV heads until `seconds` of CPU time; KV tokens/s = positions /
+    (KV heads x time)."""
+    from gtq_inputs import head_inputs
+    from oracle import gtq_oracle as O
+
+    scale = 1 / math.sqrt(128)
+    prepared = {}
+
+    def head(h):
+        if h not in prepared:
+            inp = head_inputs(args.seed, 0, h, g, n)
+            hp = O.HeadPlan(rates[0, h], krot[0][h], vrot[0][h], vb)
+            prepared[h] = (inp, hp, O.encode_kv(hp, inp["k"][: n - 1], inp["v"][: n - 1]))
+        return prepared[h]
+
+    def leg(seconds):
+        done, t_total, slices = 0, 0.0, 0
+        for i in range(64):
+            inp, hp, enc = head(i % h_kv)
+            t0 = time.perf_counter()
+            new = O.encode_kv(hp, inp["k"][n - 1: n], inp["v"][n - 1: n])
+            O.decode_attention_window(hp, inp["q"][0], np.concatenate([enc["k_words"], new["k_words"]]),
+                                      np.concatenate([enc["k_norms"], new["k_norms"]]),
+                                      np.concatenate([enc["v_words"], new["v_words"]]),
+                                      np.concatenate([enc["v_norms"], new["v_norms"]]), inp["k"], inp["v"],
+                                      n_sink, n_recent, scale, n)
+            t_total += time.perf_counter() - t0
+            done += n
+            slices += 1
+            if t_total >= seconds:
+                break
+        return done / h_kv, t_total, f"{slices} slice(s) of 1 KV head ({g} query heads) x {n} positions"
+
+    legs = _two_legs(leg, args.cpu_seconds)
+    v, cores, det, t = legs["all"]
+    v1, _, det1, t1 = legs["one"]
+    return {"value": round(v, 1), "unit": "KV tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{det}, encode of the step's token + window decode, {t:.1f} s; extrapolated to the step "
+                      f"by rate (the work is linear in heads)",
+            "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round(v1, 1), "cores": 1, "sample": f"{det1}, {t1:.1f} s"}}
 
 
 def main():

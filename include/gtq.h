@@ -439,6 +439,22 @@ gtq_status gtq_decode_attn_window(const gtq_plan* plan, int32_t layer, const gtq
                                   int64_t max_len, float softmax_scale, int32_t chunk, float* out,
                                   float* logits, void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* One decode step with the fp16 window in three launches: every sequence b of length
+ * L = seq_len[b] >= 1 appends its newest token (k_new, v_new device
+ * [batch][n_kv_heads][128] fp32) at position L - 1 to the packed cache and to the fp16
+ * buffers, then attends as gtq_decode_attn_window with seq_len. The same results as
+ * gtq_quantize_append (slot L - 1) + gtq_window_append (pos L - 1) +
+ * gtq_decode_attn_window; the window append and the window split share a workgroup
+ * (the append of the step's token to the fp16 buffers and the first use of it), the packed
+ * append and the query rotation share the first launch ("Block-GTQ" abstract, 8th
+ * sentence, for the buffers). A sequence with seq_len 0 appends nothing (counted once, as
+ * in gtq_decode_step). Workspace: gtq_decode_window_workspace_bytes. Errors: as
+ * gtq_decode_attn_window; EUNSUPPORTED with more than 8 query heads per KV head. */
+gtq_status gtq_decode_step_window(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                  const gtq_window_view* window, const float* k_new, const float* v_new,
+                                  const float* q, const int32_t* seq_len, int64_t max_len, float softmax_scale,
+                                  int32_t chunk, float* out, void* workspace, size_t ws_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -119,6 +119,9 @@ _SIGS = [
     ("gtq_decode_attn_window", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.POINTER(WindowView),
                                            C.c_void_p, C.c_void_p, C.c_int64, C.c_float, C.c_int32, C.c_void_p,
                                            C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("gtq_decode_step_window", C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(CacheView), C.POINTER(WindowView),
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_float,
+                                           C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
 ]
 EXPORTS = [s[0] for s in _SIGS]
 
@@ -565,4 +568,25 @@ def gtq_decode_attn_window(plan: Plan, layer: int, cache: PackedCache, win: Wind
                                       _dev(workspace, None, "workspace"),
                                       workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gtq_decode_attn_window")
+    return out
+
+
+def gtq_decode_step_window(plan: Plan, layer: int, cache: PackedCache, win: WindowCache, k_new, v_new, q, seq_len,
+                           max_len: int, scale: float, chunk: int = 0, out=None, workspace=None, stream=None):
+    """One decode step with the fp16 window: append at seq_len - 1 (packed and fp16), then attend."""
+    _decode_sizes(plan, cache, q, seq_len, max_len, k_new=k_new, v_new=v_new)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, q.numel(), "out")
+    if workspace is None:
+        nb = gtq_decode_window_workspace_bytes(plan, cache.batch, max_len, chunk)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    cv, wv = cache.view(), win.view()
+    st = lib().gtq_decode_step_window(plan.handle, layer, C.byref(cv), C.byref(wv),
+                                      _dev(k_new, torch.float32, "k_new"), _dev(v_new, torch.float32, "v_new"),
+                                      _dev(q, torch.float32, "q"), _dev(seq_len, torch.int32, "seq_len"), max_len,
+                                      float(scale), chunk, _dev(out, torch.float32, "out"),
+                                      _dev(workspace, None, "workspace"),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gtq_decode_step_window")
     return out

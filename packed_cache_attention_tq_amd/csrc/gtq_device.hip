@@ -1215,17 +1215,10 @@ struct WindowAppendArgs {
   int32_t batch, n_kv, n_sink, sink_slots, n_recent;
 };
 
-__global__ void __launch_bounds__(kD) window_append_kernel(WindowAppendArgs w) {
-  const int64_t t = blockIdx.x;
-  const int h = blockIdx.y, c = threadIdx.x;
-  const int seq = w.seq_idx[t];
-  const int64_t pos = w.pos[t];
-  if (seq < 0 || seq >= w.batch || pos < 0) {
-    if (c == 0 && h == 0) atomicAdd(w.overflow, 1ull);
-    return;
-  }
-  const size_t row = ((size_t)t * w.n_kv + h) * kD + c;
-  const _Float16 kh = (_Float16)w.k[row], vh = (_Float16)w.v[row];
+// coordinate c of input row `row` (token x KV head) as binary16 into the sink slot (pos <
+// n_sink) or the recent ring slot pos % n_recent of (seq, h)
+__device__ inline void window_store(const WindowAppendArgs& w, size_t row, int seq, int h, int64_t pos, int c) {
+  const _Float16 kh = (_Float16)w.k[row * kD + c], vh = (_Float16)w.v[row * kD + c];
   const size_t sh = (size_t)seq * w.n_kv + h;
   uint16_t *kd, *vd;
   int slot, slots;
@@ -1244,6 +1237,18 @@ __global__ void __launch_bounds__(kD) window_append_kernel(WindowAppendArgs w) {
   }
   kd[(sh * slots + slot) * kD + c] = __builtin_bit_cast(uint16_t, kh);
   vd[((sh * (slots / 8) + slot / 8) * kD + c) * 8 + (slot & 7)] = __builtin_bit_cast(uint16_t, vh);
+}
+
+__global__ void __launch_bounds__(kD) window_append_kernel(WindowAppendArgs w) {
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y, c = threadIdx.x;
+  const int seq = w.seq_idx[t];
+  const int64_t pos = w.pos[t];
+  if (seq < 0 || seq >= w.batch || pos < 0) {
+    if (c == 0 && h == 0) atomicAdd(w.overflow, 1ull);
+    return;
+  }
+  window_store(w, (size_t)t * w.n_kv + h, seq, h, pos, c);
 }
 
 // ---------------------------------------------------------------- partials
@@ -1981,6 +1986,32 @@ __global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_window_kernel(AttnA
   __shared__ AttnShared S;
   if ((int)blockIdx.x < n_tiles) qrot_body<8>(a, blockIdx.x);
   else window_split(a, S, blockIdx.x - n_tiles);
+}
+
+// The prepare launch of a decode step with the fp16 window (one row tile per KV head:
+// g <= 8): workgroups [0, n_app) append each sequence's step token (at seq_len - 1) to the
+// packed cache, [n_app, n_app + n_tiles) rotate one row tile's queries, the rest first
+// write the step token of their tile's sequence and KV head into the fp16 buffers and
+// then compute the tile's window split, which reads it.
+__global__ void __launch_bounds__(1024) decode_prep_window_kernel(AppendArgs ap, AttnArgs aa, WindowAppendArgs wa,
+                                                                   int n_app, int roles, int n_tiles) {
+  static_assert(64 * kQrotWaves == 1024, "one block size for the three roles");
+  __shared__ AttnShared S;
+  const int w = blockIdx.x;
+  if (w < n_app) {
+    if (roles == 1) append_token_body(ap, w / ap.n_kv, w % ap.n_kv, 3);
+    else append_token_body(ap, w / (3 * ap.n_kv), (w / 3) % ap.n_kv, w % 3);
+  } else if (w < n_app + n_tiles) {
+    qrot_body<8>(aa, w - n_app);
+  } else {
+    const int tile = w - n_app - n_tiles;
+    int seq, h, tr;
+    tile_coords(aa, tile, &seq, &h, &tr);
+    const int len = aa.seq_len[seq];
+    if (len >= 1 && threadIdx.x < kD) window_store(wa, (size_t)seq * wa.n_kv + h, seq, h, (int64_t)len - 1, threadIdx.x);
+    __syncthreads();  // (the split below reads the token's slot)
+    window_split(aa, S, tile);
+  }
 }
 
 // Phase 1 of the attention: per (row tile of RT rows, split) online-softmax partials.
@@ -4137,6 +4168,54 @@ gtq_status gtq_decode_attn_window(const gtq_plan* plan, int32_t layer, const gtq
                      L.n_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq_decode_attn_window: launch");
+  st = launch_partials(plan, layer, aa, L, stream);
+  if (st != GTQ_OK) return st;
+  return launch_merge(plan, layer, L, seq_len, 0, 0, (int)max_len, out, workspace, stream, window);
+}
+
+gtq_status gtq_decode_step_window(const gtq_plan* plan, int32_t layer, const gtq_cache_view* cache,
+                                  const gtq_window_view* window, const float* k_new, const float* v_new,
+                                  const float* q, const int32_t* seq_len, int64_t max_len, float softmax_scale,
+                                  int32_t chunk, float* out, void* workspace, size_t ws_bytes, void* hip_stream) {
+  const char* fn = "gtq_decode_step_window";
+  AttnLaunch L;
+  gtq_status st = decode_check(plan, layer, cache, max_len, chunk, ws_bytes, workspace, &L, fn, 1);
+  if (st != GTQ_OK) return st;
+  if (!check_window(plan, layer, window, cache->batch, fn, &st)) return st;
+  if (!k_new || !v_new || !q || !seq_len || !out) return fail(GTQ_EINVAL, "gtq_decode_step_window: NULL pointer");
+  if (!isfinite(softmax_scale)) return fail(GTQ_EINVAL, "gtq_decode_step_window: softmax_scale not finite");
+  if (L.tiles_per_kv != 1)
+    return fail(GTQ_EUNSUPPORTED, "gtq_decode_step_window: more than 8 query heads per KV head (use the "
+                                  "separate appends and gtq_decode_attn_window)");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  AppendArgs ap{};
+  fill_append_args(plan, layer, cache, k_new, v_new, ap);
+  ap.step_len = seq_len;
+  ap.n_tok = cache->batch;
+  AttnArgs aa{};
+  fill_attn_args(plan, layer, cache, aa, L, workspace);
+  aa.prefill = 0;
+  aa.max_len = (int32_t)max_len;
+  aa.q = q;
+  aa.qscale = softmax_scale * LOG2E_F;
+  aa.seq_len = seq_len;
+  aa.win = 1;
+  aa.wk_sink = window->k_sink;
+  aa.wv_sink = window->v_sink;
+  aa.wk_rec = window->k_recent;
+  aa.wv_rec = window->v_recent;
+  aa.n_sink = window->n_sink;
+  aa.sink_slots = sink_slots_of(window);
+  aa.n_recent = window->n_recent;
+  WindowAppendArgs wa{window->k_sink, window->v_sink, window->k_recent, window->v_recent, k_new, v_new, nullptr,
+                      nullptr, plan->d_overflow, window->batch, plan->n_kv, window->n_sink, sink_slots_of(window),
+                      window->n_recent};
+  const int roles = append_roles((int64_t)cache->batch * plan->n_kv);
+  const int n_app = cache->batch * plan->n_kv * roles;
+  hipLaunchKernelGGL(decode_prep_window_kernel, dim3((unsigned)(n_app + 2 * L.n_tiles)), dim3(1024), 0, stream, ap,
+                     aa, wa, n_app, roles, L.n_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "gtq_decode_step_window: launch");
   st = launch_partials(plan, layer, aa, L, stream);
   if (st != GTQ_OK) return st;
   return launch_merge(plan, layer, L, seq_len, 0, 0, (int)max_len, out, workspace, stream, window);

@@ -607,6 +607,71 @@ def test_window_decode(G, ns, nr, chunk):
     plan.destroy()
 
 
+@pytest.mark.parametrize("ns,nr", [(4, 64), (0, 96), (40, 32)])
+def test_window_decode_step(G, ns, nr):
+    """gtq_decode_step_window: each sequence appends its newest token at seq_len - 1 to
+    the packed cache and the fp16 buffers and attends (lengths 300, 1, 0, 150; ring wrap
+    for the 300 one): packed cache and fp16 buffers identical to the separate appends,
+    outputs identical to gtq_decode_attn_window after them, and against the oracle."""
+    _say(f"case: fused fp16 window decode step n_sink={ns} n_recent={nr}")
+    lens = [300, 1, 0, 150]
+    case = Case(8, 1, 2, 4, 300, 128, 2, batch=4)
+    plan = case.plan()
+    cap = 320
+    caches = [G.PackedCache(plan, 4, cap) for _ in range(2)]
+    wins = [G.WindowCache(plan, 4, ns, nr) for _ in range(2)]
+    for b, L in enumerate(lens):   # the prompt: every token but the step's newest
+        if L <= 1:
+            continue
+        k, v = case.kv(0, b, 0, L - 1)
+        pos = _window_positions_to_fill(L - 1, ns, nr)
+        for c, w in zip(caches, wins):
+            G.gtq_quantize_append_chunk(plan, 0, c, _dev(k), _dev(v), b, 0)
+            if len(pos):
+                G.gtq_window_append(plan, 0, w, _dev(k[pos]), _dev(v[pos]), _dev(np.full(len(pos), b, np.int32)),
+                                    _dev(pos))
+    knew = np.zeros((4, case.H, 128), np.float32)
+    vnew = np.zeros((4, case.H, 128), np.float32)
+    for b, L in enumerate(lens):
+        if L > 0:
+            k, v = case.kv(0, b, L - 1, L)
+            knew[b], vnew[b] = k[0], v[0]
+    q = np.stack([case.q(0, b) for b in range(4)])
+    sl = _dev(np.array(lens, np.int32))
+    sc = scale_default()
+    ov0 = plan.overflow_count()
+    out = G.gtq_decode_step_window(plan, 0, caches[0], wins[0], _dev(knew), _dev(vnew), _dev(q), sl, cap, sc)
+    torch.cuda.synchronize()
+    assert plan.overflow_count() == ov0 + 1     # the sequence of length 0 appends nothing
+    live = [b for b, L in enumerate(lens) if L > 0]
+    lb = _dev(np.array(live, np.int32))
+    pos = _dev(np.array([lens[b] - 1 for b in live], np.int64))
+    G.gtq_quantize_append(plan, 0, caches[1], _dev(knew[live]), _dev(vnew[live]), lb, pos)
+    G.gtq_window_append(plan, 0, wins[1], _dev(knew[live]), _dev(vnew[live]), lb, pos)
+    out_sep = G.gtq_decode_attn_window(plan, 0, caches[1], wins[1], _dev(q), sl, cap, sc)
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_norms", "v_codes", "v_norms"):
+        assert torch.equal(getattr(caches[0], name), getattr(caches[1], name)), name
+    for name in ("k_sink", "v_sink", "k_recent", "v_recent"):
+        a0, a1 = getattr(wins[0], name), getattr(wins[1], name)
+        assert torch.equal(a0.view(torch.int16), a1.view(torch.int16)), name
+    assert torch.equal(out, out_sep)
+    o = out.cpu().numpy()
+    assert np.count_nonzero(o[2]) == 0
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        recs = _records_from_gpu(case, caches[0], 0, b, L)
+        for h in range(case.H):
+            e = recs[h]
+            sl_ = slice(h * case.g, (h + 1) * case.g)
+            inp = case.inputs[0, h][b]
+            _, o_ref = O.decode_attention_window(case.heads[0, h], q[b, sl_], e["k_words"], e["k_norms"],
+                                                 e["v_words"], e["v_norms"], inp["k"], inp["v"], ns, nr, sc, L)
+            assert_close(o[b, sl_], o_ref, f"window step out b{b} h{h}")
+    plan.destroy()
+
+
 def test_window_errors(G):
     _say("case: fp16 window argument errors")
     case = Case(7, 1, 2, 4, 64, 128, 2, batch=1)
