@@ -69,8 +69,9 @@ def parse():
     p.add_argument("--v-hadamard", action="store_true",
                    help="decode-8b: randomized Hadamard value rotations (applied as fast transforms)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
-                   help="after timing, run a plain device copy (torch.neg) of this many MiB three "
-                        "times: a kernel of known traffic that calibrates the HBM byte counters")
+                   help="decode, append and prefill workloads: after timing, run a plain device copy "
+                        "(torch.neg) of this many MiB three times: a kernel of known traffic that "
+                        "calibrates the HBM byte counters")
     return p.parse_args()
 
 
@@ -431,6 +432,8 @@ def bench_append(args):
         "roofline": hbm_roofline("append_gemm_kernel", alg, ms, "append-32b",
                                  {"timing": "HIP events around a graph of the 16 chunk launches"}),
     }
+    if args.calib_copy_mib > 0:
+        calib_copy(args.calib_copy_mib)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_append(args, rates, krot, vrot, kb, vb, chunk, h_kv, g)
     return res
@@ -516,6 +519,8 @@ def bench_prefill(args):
                      "alg_flop_per_call": flop, "note": "algorithmic flop: 4 x 128 per visible (query, key) pair and "
                                                         "query head; the split operands execute twice that"},
     }
+    if args.calib_copy_mib > 0:
+        calib_copy(args.calib_copy_mib)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(args, rates, krot, vrot, vb, g, pos0, chunk)
     return res
