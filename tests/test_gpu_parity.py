@@ -469,6 +469,59 @@ def test_qjl_residual_sketch(G, k_budget):
         G.gtq_prefill_attn(plan, 0, cache, _dev(np.zeros((4, case.HQ, 128), np.float32)), 0, 100, sc)
 
 
+def test_qjl_wide_window_paged(G):
+    """QJL keys with 16 query heads per KV head (two row tiles per head), 13-word records
+    (8 key words per lane) and 3-bit values: decode over the GPU's records against the
+    oracle; the fp16-window decode against the oracle's window decode; a paged cache (64-token
+    pages, shuffled) filled the same way gives the same records and decode outputs."""
+    _say("case: QJL, g=16, window and paged")
+    lens, P, maxp = [200, 90], 64, 4
+    case = Case(33, 1, 2, 16, 200, 128, 3, batch=2, qjl=True)
+    plan = case.plan()
+    cont = G.PackedCache(plan, 2, P * maxp)
+    pc = G.PagedCache(plan, 2, 8, P, maxp)
+    perm = np.random.default_rng(5).permutation(8)
+    tab = np.full((2, maxp), -1, np.int32)
+    tab[0, :4] = perm[:4]
+    tab[1, :2] = perm[4:6]
+    pc.block_table.copy_(torch.from_numpy(tab))
+    for c in (cont, pc):
+        for b, n in enumerate(lens):
+            k, v = case.kv(0, b, 0, n)
+            G.gtq_quantize_append_chunk(plan, 0, c, _dev(k), _dev(v), b, 0)
+    q = np.stack([case.q(0, b) for b in range(2)])
+    sl = _dev(np.array(lens, np.int32))
+    sc = scale_default()
+    out = G.gtq_decode_attn(plan, 0, cont, _dev(q), sl, P * maxp, sc)
+    out_p = G.gtq_decode_attn(plan, 0, pc, _dev(q), sl, P * maxp, sc)
+    win = G.WindowCache(plan, 2, 4, 32)
+    for b, n in enumerate(lens):
+        k, v = case.kv(0, b, 0, n)
+        pos = _window_positions_to_fill(n, 4, 32)
+        G.gtq_window_append(plan, 0, win, _dev(k[pos]), _dev(v[pos]), _dev(np.full(len(pos), b, np.int32)),
+                            _dev(pos))
+    out_w = G.gtq_decode_attn_window(plan, 0, cont, win, _dev(q), sl, P * maxp, sc, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_p)
+    ties = 0
+    for b, n in enumerate(lens):
+        encs = _encode(case, 0, b, n)
+        t, _ = _check_append(case, cont, 0, b, n, encs, f"qjl wide b{b}")
+        ties += t
+        recs = _records_from_gpu(case, cont, 0, b, n)
+        _, ref = _oracle_decode(case, 0, b, n, recs, q[b], sc)
+        assert_close(out[b].cpu().numpy(), ref, f"qjl wide decode b{b}")
+        for h in range(case.H):
+            e = recs[h]
+            sl_ = slice(h * case.g, (h + 1) * case.g)
+            inp = case.inputs[0, h][b]
+            _, o_ref = O.decode_attention_window(case.heads[0, h], q[b, sl_], e["k_words"], e["k_norms"],
+                                                 e["v_words"], e["v_norms"], inp["k"], inp["v"], 4, 32, sc, n)
+            assert_close(out_w[b, sl_].cpu().numpy(), o_ref, f"qjl window decode b{b} h{h}")
+    _say(f"  qjl wide: append ties={ties}")
+    plan.destroy()
+
+
 def test_edge_cases(G):
     """Zero vectors (norm 0, codes 2^(b-1)), sequences of length 0 and 1, determinism."""
     _say("case: edge cases")
