@@ -317,8 +317,15 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
   };
   float xr[8];
   bool xok = load_tile(blockIdx.x, xr);
+  using KArgsA = const __attribute__((address_space(4))) AppendArgs;
+  KArgsA* const ka0 = (KArgsA*)__builtin_amdgcn_kernarg_segment_ptr();
 
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    // the arguments the tile reads, loaded again in each tile rather than held in
+    // registers across the loop
+    KArgsA* kap = ka0;
+    asm volatile("" : "+s"(kap));
+    const AppendArgs& A = *(const AppendArgs*)kap;
     const int64_t ts = s_begin + tile * kAppTile;
     float x[8];
 #pragma unroll
@@ -327,7 +334,7 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
     __syncthreads();                  // the previous tile's stores have read the buffers
     if (tid < kAppTile * 16) (&S.pk[0][0])[tid] = 0u;
     (&S.pv[0][0])[tid] = 0u;          // 4 x 128 == kAppThreads
-    if (a.nc && tid < kAppTile * 5) (&S.cs[0][0])[tid] = 0.0;
+    if (A.nc && tid < kAppTile * 5) (&S.cs[0][0])[tid] = 0.0;
     // ---- norms (fp64, per token and group; every lane of the row gets all sums), then
     //      u = x / nu split as 256 u = U_hi + U_lo
     double sg[kMaxGroups] = {0.0, 0.0, 0.0, 0.0};
@@ -363,7 +370,7 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
     if (sub < ng) {
       const double nu = sqrt(own);
       S.nu[tau][vrole ? 4 : sub] = (float)nu;
-      if (a.nc) S.nu64[tau][vrole ? 4 : sub] = nu;
+      if (A.nc) S.nu64[tau][vrole ? 4 : sub] = nu;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -417,7 +424,7 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
         for (int v8 = 0; v8 < 8; ++v8) cds[v8] += zv[v8] >= tv[v8] ? step : 0;
       }
     }
-    if (a.nc) {
+    if (A.nc) {
       // sum of C[code]^2 over each group's outputs in the row, for each of the lane's 8
       // tokens (the row's groups are g_lo .. g_hi)
       const float* cr = S.cen[rp];
@@ -476,21 +483,21 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
       for (int e = tid; e < kAppTile * kw; e += kAppThreads) {
         const int t = e / kw, w = e - t * kw;
         const int64_t s = ts + t;
-        if (s >= a.pos0 && s < s_end) {
-          const int64_t ti = token_index(a.pm, a.capacity, a.n_kv, a.seq, h, s);
-          if (ti >= 0) a.k_codes[ti * kw + w] = S.pk[t][w];
+        if (s >= A.pos0 && s < s_end) {
+          const int64_t ti = token_index(A.pm, A.capacity, A.n_kv, A.seq, h, s);
+          if (ti >= 0) A.k_codes[ti * kw + w] = S.pk[t][w];
         }
       }
       if (tid < kAppTile * kNS) {
         const int t = tid / kNS, g = tid - kNS * t;
         const int64_t s = ts + t;
-        if (s >= a.pos0 && s < s_end) {
-          const int64_t ti = token_index(a.pm, a.capacity, a.n_kv, a.seq, h, s);
+        if (s >= A.pos0 && s < s_end) {
+          const int64_t ti = token_index(A.pm, A.capacity, A.n_kv, A.seq, h, s);
           if (ti >= 0)
-            a.k_norms[ti * kNS + g] =
-                g >= n_groups ? 0.f : (a.nc ? corrected_norm(S.nu64[t][g], S.cs[t][g], nd_store) : S.nu[t][g]);
+            A.k_norms[ti * kNS + g] =
+                g >= n_groups ? 0.f : (A.nc ? corrected_norm(S.nu64[t][g], S.cs[t][g], nd_store) : S.nu[t][g]);
           else if (g == 0 && h == 0)
-            atomicAdd(a.overflow, 1ull);  // once per token in an absent page
+            atomicAdd(A.overflow, 1ull);  // once per token in an absent page
         }
       }
     } else {
@@ -498,17 +505,17 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
       for (int e = tid; e < 4 * vw; e += kAppThreads) {
         const int b = e / vw, w = e - b * vw;
         const int64_t sb = ts + 8 * b;
-        if (sb + 8 <= a.pos0 || sb >= s_end) continue;  // no token of this block in the chunk
-        const int64_t bi = token_index(a.pm, a.capacity, a.n_kv, a.seq, h, sb);  // (8-aligned: a block index x 8)
+        if (sb + 8 <= A.pos0 || sb >= s_end) continue;  // no token of this block in the chunk
+        const int64_t bi = token_index(A.pm, A.capacity, A.n_kv, A.seq, h, sb);  // (8-aligned: a block index x 8)
         if (bi < 0) continue;
-        uint32_t* blk = a.v_codes + (size_t)(bi / GTQ_VBLOCK) * vw;
-        if (sb >= a.pos0 && sb + 8 <= s_end) {
+        uint32_t* blk = A.v_codes + (size_t)(bi / GTQ_VBLOCK) * vw;
+        if (sb >= A.pos0 && sb + 8 <= s_end) {
           blk[w] = S.pv[b][w];
         } else {
           // bits of the block's tokens inside the chunk only
           uint32_t mask = 0;
           for (int jt = 0; jt < 8; ++jt) {
-            if (sb + jt < a.pos0 || sb + jt >= s_end) continue;
+            if (sb + jt < A.pos0 || sb + jt >= s_end) continue;
             const int c_lo = (32 * w) / (8 * vb), c_hi = min(kD - 1, (32 * w + 31) / (8 * vb));
             for (int cc = c_lo; cc <= c_hi; ++cc) {
               const int bit = 8 * vb * cc + vb * jt - 32 * w;
@@ -525,8 +532,8 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
       }
       if (tid < kAppTile) {
         const int64_t s = ts + tid;
-        const int64_t ti = (s >= a.pos0 && s < s_end) ? token_index(a.pm, a.capacity, a.n_kv, a.seq, h, s) : -1;
-        if (ti >= 0) a.v_norms[ti] = a.nc ? corrected_norm(S.nu64[tid][4], S.cs[tid][4], kD) : S.nu[tid][4];
+        const int64_t ti = (s >= A.pos0 && s < s_end) ? token_index(A.pm, A.capacity, A.n_kv, A.seq, h, s) : -1;
+        if (ti >= 0) A.v_norms[ti] = A.nc ? corrected_norm(S.nu64[tid][4], S.cs[tid][4], kD) : S.nu[tid][4];
       }
     }
   }
