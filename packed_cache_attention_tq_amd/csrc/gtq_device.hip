@@ -3029,7 +3029,9 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
     const int sg = (a.win && k == nv - 1) ? a.sk_G + a.n_tiles + tile : first + k;
     return a.partials + ((size_t)sg * 8 + r8) * kPS;
   };
-  auto live = [&](int k) { return a.prefill || (a.win && k == nv - 1) || sk_live(w0 + k, a.sk_G, U); };
+  // (with at least as many units as workgroups every workgroup has some: no division)
+  const bool all_live = a.prefill || (long long)a.sk_G <= U;
+  auto live = [&](int k) { return all_live || (a.win && k == nv - 1) || sk_live(w0 + k, a.sk_G, U); };
   // inverse rotation operand: thread (output oi of this quarter, eighth e) holds
   // Pi_V^T[oi][16 e .. + 15] (none for a Hadamard Pi_V, applied as a transform by the
   // first quarter alone)
@@ -3232,7 +3234,9 @@ __global__ void __launch_bounds__(256) attn_merge_tile_kernel(MergeTileArgs a) {
       const int sg = (a.win && k == nv - 1) ? a.sk_G + a.n_tiles + tile : first + k;
       return a.partials + ((size_t)sg * 8 + r) * kPS;
     };
-    auto live = [&](int k) { return a.prefill || (a.win && k == nv - 1) || sk_live(w0 + k, a.sk_G, U); };
+    // (with at least as many units as workgroups every workgroup has some: no division)
+    const bool all_live = a.prefill || (long long)a.sk_G <= U;
+    auto live = [&](int k) { return all_live || (a.win && k == nv - 1) || sk_live(w0 + k, a.sk_G, U); };
     float mk[kMergeTileChunks], lk[kMergeTileChunks];
     float4 xk[kMergeTileChunks];
     float M = -INFINITY;
