@@ -249,6 +249,7 @@ def test_binding_rejects_undersized_tensors(lib):
     plan = G.Plan(1, H, H * g, 128, 2, np.stack([r, r])[None], [[kr, kr]], np.stack([vr, vr])[None],
                   host_only=True)
     cache = G.PackedCache(plan, 3, 64, device="cpu")
+    win = G.WindowCache(plan, 3, 4, 32, device="cpu")
     z = lambda *s, dt=torch.float32: torch.zeros(*s, dtype=dt)
     cases = [
         (lambda: G.gtq_decode_attn(plan, 0, cache, z(3, H * g - 1, 128), z(3, dt=torch.int32), 64, 0.1), "q"),
@@ -265,6 +266,10 @@ def test_binding_rejects_undersized_tensors(lib):
         (lambda: G.gtq_decode_step(plan, 0, cache, z(3, H, 128), z(2, H, 128), z(3, H * g, 128),
                                    z(3, dt=torch.int32), 64, 0.1), "v_new"),
         (lambda: G.gtq_prefill_attn(plan, 0, cache, z(7, H * g + 1, 128), 0, 0, 0.1), "q"),
+        (lambda: G.gtq_decode_step_window(plan, 0, cache, win, z(3, H - 1, 128), z(3, H, 128), z(3, H * g, 128),
+                                          z(3, dt=torch.int32), 64, 0.1), "k_new"),
+        (lambda: G.gtq_decode_attn_window(plan, 0, cache, win, z(3, H * g, 128), z(3, dt=torch.int32), 64, 0.1,
+                                          out=z(2, H * g, 128)), "out"),
     ]
     for fn, name in cases:
         with pytest.raises(ValueError, match=rf"^{name} holds"):
