@@ -1425,140 +1425,6 @@ __device__ inline void stage_block(AttnWave& W, const BlockData<VB, KWL>& B, int
   }
 }
 
-// One step of a wave's online softmax over the block staged in W.
-template <int VB, int NKB>
-__device__ inline void attn_block(const AttnShared& S, const AttnWave& W, const AttnArgs& a,
-                                  int t0, int lane, int q, int n, int my_row, int my_len, int my_lo,
-                                  const QkConst<NKB>& C, uint32_t nq_off, uint32_t vn_off,
-                                  floatx4 (&oacc)[8], float& m_run, float& l_run) {
-  const char* sb = reinterpret_cast<const char*>(&S);
-
-  // ---- QK per K-block (one rate and group each): A = the decoded codes of tokens
-  //      tau0 + 8 (n >> 2)... of the two 16-token halves, B = the rotated queries; the
-  //      product times the token's group norm adds into the logits of tokens 8q + j
-  float lg[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) lg[j] = 0.f;
-  const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < NKB; ++i) {
-    const char* rp = sb + (C.ko[i] >> 5);
-    const uint32_t* r = reinterpret_cast<const uint32_t*>(rp);
-    const uint32_t f0 = __builtin_amdgcn_alignbit(r[1], r[0], C.ko[i]);
-    const uint32_t f1 = __builtin_amdgcn_alignbit(r[4 * kKPitch + 1], r[4 * kKPitch], C.ko[i]);
-    H8 a0, a1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a0.u[j] = lds_u32(sb, C.lb[i] + (__builtin_amdgcn_ubfe(f0, C.w2[i] * j, C.w2[i]) << 2));
-      a1.u[j] = lds_u32(sb, C.lb[i] + (__builtin_amdgcn_ubfe(f1, C.w2[i] * j, C.w2[i]) << 2));
-    }
-    H8 qv;
-    qv.v = S.qb[i][q][n];
-    const floatx4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0.h, qv.h, z4, 0, 0, 0);
-    const floatx4 d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1.h, qv.h, z4, 0, 0, 0);
-    const float4 na = *reinterpret_cast<const float4*>(sb + nq_off + C.no[i]);
-    const float4 nb = *reinterpret_cast<const float4*>(sb + nq_off + C.no[i] + 16);
-    lg[0] = fmaf(na.x, d0[0], lg[0]);
-    lg[1] = fmaf(na.y, d0[1], lg[1]);
-    lg[2] = fmaf(na.z, d0[2], lg[2]);
-    lg[3] = fmaf(na.w, d0[3], lg[3]);
-    lg[4] = fmaf(nb.x, d1[0], lg[4]);
-    lg[5] = fmaf(nb.y, d1[1], lg[5]);
-    lg[6] = fmaf(nb.z, d1[2], lg[6]);
-    lg[7] = fmaf(nb.w, d1[3], lg[7]);
-  }
-  // ---- whole logits (lanes n and 15 - n hold the high and low parts of one row); each
-  //      of the two lanes then carries on with four of the eight tokens: the high lane
-  //      with tokens 8q..8q+3, the low lane with 8q+4..8q+7
-#pragma unroll
-  for (int j = 0; j < 8; ++j) lg[j] += dpp_row_mirror(lg[j]);
-  const bool lo = n >= 8;
-  const int tb = t0 + 8 * q + (lo ? 4 : 0);
-  float x[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    x[u] = lo ? lg[4 + u] : lg[u];
-    if (tb + u >= my_len || tb + u < my_lo) x[u] = -INFINITY;
-  }
-  if (a.logits) {
-    const int id = S.row_id[my_row];
-    if (id >= 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (tb + u < my_len && tb + u >= my_lo) a.logits[(size_t)id * a.logits_ld + tb + u] = x[u] * LN2_F;
-    }
-  }
-  float mblk = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mblk = fmaxf(mblk, dpp_row_mirror(mblk));
-  mblk = max_over_q(mblk);
-  const bool grow = mblk > m_run;
-  if (__any(grow)) {
-    const float m_new = grow ? mblk : m_run;
-    // the accumulators only need rescaling once they hold something
-    const bool rescale = grow && m_run != -INFINITY;
-    if (__any(rescale)) {
-      const float f = rescale ? exp2f(m_run - m_new) : 1.f;
-      l_run *= f;
-      // accumulator rows 4q + e live in lanes with n == row: fetch their factors
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float fe = __shfl(f, 4 * q + e);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) oacc[t][e] *= fe;
-      }
-    }
-    m_run = m_new;
-  }
-  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-  // ---- probabilities times value norms, split into binary16 high and low parts
-  const float4 vv = *reinterpret_cast<const float4*>(sb + vn_off);
-  const float vn[4] = {vv.x, vv.y, vv.z, vv.w};
-  float pv[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    // x - m_use <= 0: the hardware 2^x (denormal results flush to 0) is exact enough
-    const float p = (x[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[u] - m_use);
-    l_run += p;
-    pv[u] = (p == 0.f) ? 0.f : p * vn[u];
-  }
-  H8 hv, lv;  // (only words 0 and 1 are used)
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const auto h = __builtin_amdgcn_cvt_pkrtz(pv[2 * k], pv[2 * k + 1]);
-    const auto l = __builtin_amdgcn_cvt_pkrtz(pv[2 * k] - (float)h[0], pv[2 * k + 1] - (float)h[1]);
-    hv.u[k] = __builtin_bit_cast(uint32_t, h);
-    lv.u[k] = __builtin_bit_cast(uint32_t, l);
-  }
-  // A-row n < 8: high parts of row n; A-row n >= 8: low parts of row 15 - n. The high
-  // lane sends its low parts to its partner and takes the partner's high parts.
-  H8 pa;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t keep = lo ? lv.u[k] : hv.u[k];
-    const uint32_t recv = dpp_row_mirror_u(lo ? hv.u[k] : lv.u[k]);
-    pa.u[k] = lo ? recv : keep;
-    pa.u[2 + k] = lo ? keep : recv;
-  }
-  // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
-  uint32_t vw[2 * VB];
-#pragma unroll
-  for (int i = 0; i < (2 * VB + 3) / 4; ++i) {
-    const uint4 x = W.vcodes[i][lane];
-    vw[4 * i] = x.x;
-    if (4 * i + 1 < 2 * VB) vw[4 * i + 1] = x.y;
-    if (4 * i + 2 < 2 * VB) vw[4 * i + 2] = x.z;
-    if (4 * i + 3 < 2 * VB) vw[4 * i + 3] = x.w;
-  }
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dequant8<VB>(S, vfield<VB>(vw, t)), oacc[t], 0, 0, 0);
-  __builtin_amdgcn_wave_barrier();
-}
-
-// The same step for a 16-row tile: separate MFMAs for the high and the low query parts
-// (and for the high and low parts of p * nu_V), so that lane (q, n) carries row n alone:
-// no row-mirror adds and no duplicated softmax lanes. Used where many query rows share a
-// KV head (prefill).
 template <int VB, int NKB>
 __device__ inline void attn_block16(const AttnSharedT<16>& S, const AttnWave& W, const AttnArgs& a,
                                     int t0, int lane, int q, int n, int my_len, float xs,
@@ -2021,10 +1887,11 @@ __global__ void __launch_bounds__(1024) decode_prep_window_kernel(AppendArgs ap,
   }
 }
 
-// Phase 1 of the attention: per (row tile of RT rows, split) online-softmax partials.
+// Prefill partials: per (row tile of RT = 16 rows, split) online-softmax partials.
 // (at most 128 registers: two workgroups per compute unit)
 template <int VB, int KWL, int NKB, int RT, bool PAGED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) attn_partials_kernel(AttnArgs a) {
+  static_assert(RT == 16, "prefill tiles of 16 rows (decode tiles run attn_decode_kernel)");
   constexpr int kTileQB = (RT / 8) * kQB;
   __shared__ AttnSharedT<RT> S;
   const int tid = threadIdx.x;
@@ -2113,9 +1980,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   const int c1 = min(c0 + a.chunk, tile_len);
   constexpr int kStep = kBlk * kWaves;
 
-  const int my_row = RT == 16 ? n : (n < 8 ? n : 15 - n);
-  const int my_len = S.row_len[my_row];
-  const int my_lo = a.win ? a.n_sink : 0;  // sink positions read the fp16 buffers
+  const int my_len = S.row_len[n];
   AttnWave& W = S.u.w[wave];
   const char* sb = reinterpret_cast<const char*>(&S);
   int st[KWL];  // staging slot of word lane + 64 i: token (lw / kw) at pitch 17; words past
@@ -2142,9 +2007,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     C.no[i] = grp * kBlk * 4;
   }
   const uint32_t nq_off = (uint32_t)(reinterpret_cast<const char*>(&W.knt[0][8 * q]) - sb);
-  // value norms: the four tokens this lane finishes (8-row tiles) or all eight (16-row)
-  const uint32_t vn_off =
-      (uint32_t)(reinterpret_cast<const char*>(&W.vn[8 * q + (RT == 8 && n >= 8 ? 4 : 0)]) - sb);
+  // value norms: the eight tokens this lane finishes
+  const uint32_t vn_off = (uint32_t)(reinterpret_cast<const char*>(&W.vn[8 * q]) - sb);
 
   floatx4 oacc[8];
 #pragma unroll
@@ -2164,60 +2028,29 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         load_block<VB, KWL>(blk[0], R, t0 + kStep, kw, lane, voff_v);
       }
     }
-    if constexpr (RT == 8)
-      attn_block<VB, NKB>(S, W, a, t0, lane, q, n, my_row, my_len, my_lo, C, nq_off, vn_off, oacc, m_run, l_run);
-    else
-      attn_block16<VB, NKB>(S, W, a, t0, lane, q, n, my_len, xs, C, nq_off, vn_off, oacc, m_run, l_run);
+    attn_block16<VB, NKB>(S, W, a, t0, lane, q, n, my_len, xs, C, nq_off, vn_off, oacc, m_run, l_run);
   }
 
-  if constexpr (RT == 8) {
-    // ---- epilogue: rows 0..7 = high row + mirrored low row, merged over the waves
-    l_run += dpp_row_mirror(l_run);  // the two lanes of a row summed different tokens
-    l_run = sum_over_q(l_run);
-    if (q == 0 && n < 8) {
-      S.om[wave][n] = m_run;
-      S.ol[wave][n] = l_run;
-    }
-    // combined rows 4q + e (q < 2): own high row plus the low row held by lane l ^ 48
-    float vrow[8][4];
+  // ---- epilogue, 16 rows: lane (q, n) holds row n (its l over its own tokens) and the
+  //      accumulator rows 4q + e; two rounds of 8 rows through the shared slots
+  l_run = sum_over_q(l_run);
+  if (q == 0) {
+    S.om[wave][n] = m_run;
+    S.ol[wave][n] = l_run;
+  }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
-    }
-    __syncthreads();  // every wave is done with its key tile
-    if (q < 2) {
+  for (int hf = 0; hf < 2; ++hf) {
+    __syncthreads();  // hf 0: every wave is done with its stage; hf 1: round 0 was read
+    if ((q >> 1) == hf) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float* dst = &S.u.slot[wave][4 * q + e][8 * n];
-        *reinterpret_cast<float4*>(dst) = make_float4(vrow[0][e], vrow[1][e], vrow[2][e], vrow[3][e]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(vrow[4][e], vrow[5][e], vrow[6][e], vrow[7][e]);
+        float* dst = &S.u.slot[wave][4 * (q & 1) + e][8 * n];
+        *reinterpret_cast<float4*>(dst) = make_float4(oacc[0][e], oacc[1][e], oacc[2][e], oacc[3][e]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(oacc[4][e], oacc[5][e], oacc[6][e], oacc[7][e]);
       }
     }
     __syncthreads();
-    write_partials(a, S, tid, 0, chunk_idx);
-  } else {
-    // ---- epilogue, 16 rows: lane (q, n) holds row n (its l over its own tokens) and the
-    //      accumulator rows 4q + e; two rounds of 8 rows through the shared slots
-    l_run = sum_over_q(l_run);
-    if (q == 0) {
-      S.om[wave][n] = m_run;
-      S.ol[wave][n] = l_run;
-    }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      __syncthreads();  // hf 0: every wave is done with its stage; hf 1: round 0 was read
-      if ((q >> 1) == hf) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float* dst = &S.u.slot[wave][4 * (q & 1) + e][8 * n];
-          *reinterpret_cast<float4*>(dst) = make_float4(oacc[0][e], oacc[1][e], oacc[2][e], oacc[3][e]);
-          *reinterpret_cast<float4*>(dst + 4) = make_float4(oacc[4][e], oacc[5][e], oacc[6][e], oacc[7][e]);
-        }
-      }
-      __syncthreads();
-      write_partials(a, S, tid, 8 * hf, chunk_idx);
-    }
+    write_partials(a, S, tid, 8 * hf, chunk_idx);
   }
 }
 
