@@ -280,22 +280,24 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
   // ---- this thread's 8 inputs of a tile: token tau = tid >> 4 (one 16-lane row per
   //      token), columns c = (tid & 15) + 16 i
   const int tau = tid >> 4, sub = tid & 15;
-  int src_col[8], grp_of[8];
+  // packed to keep them out of the register budget: input i's source column in byte
+  // i & 3 of colp[i >> 2], its key group in bits 2i, 2i + 1 of grpp
+  uint32_t colp[2] = {0u, 0u}, grpp = 0u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = sub + 16 * i;  // record position (keys) or coordinate (values)
-    if (vrole) {
-      src_col[i] = c;
-      grp_of[i] = 0;
-    } else {
-      int g = 0;
+    int col = c, g = 0;
+    if (!vrole) {
 #pragma unroll
       for (int gg = 1; gg < kMaxGroups; ++gg)
         if (gg < n_groups && c >= hp->pos_off[gg]) g = gg;
-      src_col[i] = hp->coord[c];
-      grp_of[i] = g;
+      col = hp->coord[c];
     }
+    colp[i >> 2] |= (uint32_t)col << (8 * (i & 3));
+    grpp |= (uint32_t)g << (2 * i);
   }
+  auto src_col = [&](int i) { return (int)__builtin_amdgcn_ubfe(colp[i >> 2], 8 * (i & 3), 8); };
+  auto grp_of = [&](int i) { return (int)__builtin_amdgcn_ubfe(grpp, 2 * i, 2); };
   // (head fields the tile loop needs are all read before it: the loop's global stores
   // could alias them, so reads inside it would be repeated and waited for on every tile)
   const int nd_store = (tid < kAppTile * kNS && tid % kNS < n_groups) ? hp->dim[tid % kNS] : 1;
@@ -312,7 +314,7 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
     const bool ok = tile < n_tiles && s >= a.pos0 && s < s_end;
     const size_t row = ok ? ((size_t)(s - a.pos0) * a.n_kv + h) * kD : (size_t)h * kD;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xr[i] = src[row + src_col[i]];
+    for (int i = 0; i < 8; ++i) xr[i] = src[row + src_col(i)];
     return ok;
   };
   float xr[8];
@@ -346,7 +348,7 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
       for (int i = 0; i < 8; ++i) {
         const double xv = x[i];
 #pragma unroll
-        for (int gg = 0; gg < kMaxGroups; ++gg) sg[gg] += (grp_of[i] == gg) ? xv * xv : 0.0;
+        for (int gg = 0; gg < kMaxGroups; ++gg) sg[gg] += (grp_of(i) == gg) ? xv * xv : 0.0;
       }
     }
     // every lane gets each group's sum; the stored norm is the correctly rounded fp64
@@ -376,7 +378,7 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
     for (int i = 0; i < 8; ++i) {
       double iv = inv[0];
 #pragma unroll
-      for (int gg = 1; gg < kMaxGroups; ++gg) iv = (grp_of[i] == gg) ? inv[gg] : iv;
+      for (int gg = 1; gg < kMaxGroups; ++gg) iv = (grp_of(i) == gg) ? inv[gg] : iv;
       const float u = (float)((double)x[i] * iv) * 256.f;
       const _Float16 hi = (_Float16)u;
       S.ua[0][tau][sub + 16 * i] = hi;
@@ -478,7 +480,11 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
       }
     }
     __syncthreads();
-    // ---- store
+    // ---- store (thread indices from an opaque copy: the store addresses are derived
+    //      here rather than held, or spilled, across the tile)
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o;
     if (!vrole) {
       for (int e = tid; e < kAppTile * kw; e += kAppThreads) {
         const int t = e / kw, w = e - t * kw;
