@@ -591,7 +591,7 @@ __device__ inline T pick(const T (&v)[kMaxGroups], int g) {
   return g == 3 ? v[3] : (g == 2 ? v[2] : (g == 1 ? v[1] : v[0]));
 }
 
-__device__ inline void append_token_body(const AppendArgs& a, int64_t tok, int h, int role) {
+__device__ __attribute__((always_inline)) inline void append_token_body(const AppendArgs& a, int64_t tok, int h, int role) {
   __shared__ float xnat[2 * kD];        // key then value, natural order
   __shared__ __align__(16) float xs[2 * kD];  // key (record order) then value coordinates
   __shared__ float red[4][2 * kD];
@@ -1037,8 +1037,11 @@ __device__ inline float swap_q3(float x) { return xor16(xor32(x)); }
 // of rows 7..0 in columns 8..15; tiles of 16 rows (RT = 16, prefill) write two operands,
 // high parts then low parts, with row n in column n.
 constexpr int kQrotWaves = 16;
-template <int RT>
-__device__ inline void qrot_body(const AttnArgs& a, int tile) {
+// mid() runs once this thread's loads are issued (the decode step's prepare puts a token
+// append there, so that both bodies' loads are in flight together); QJL_OK = false leaves the
+// sketch rows unloaded (callers that never see a QJL plan).
+template <int RT, bool QJL_OK = true, typename Mid>
+__device__ __attribute__((always_inline)) inline void qrot_body_with(const AttnArgs& a, int tile, Mid&& mid) {
   constexpr int kParts = RT / 8;       // B operands per tile (1, or 2 for hi and lo)
   constexpr int kTileQB = kParts * kQB;
   __shared__ __align__(16) float qnat[RT][kD];
@@ -1074,13 +1077,14 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
   }
   const int crd = tid < kD ? hp->coord[tid] : 0;
   // QJL plans (decode tiles): this thread's sixteenth of row i of the sketch matrix S
-  const bool qjl = RT == 8 && a.qjl;
+  const bool qjl = RT == 8 && QJL_OK && a.qjl;
   float4 sr[4];
   {
     const float4* row = reinterpret_cast<const float4*>(a.rot + hp->qjl_off + (size_t)i * kD + 16 * part);
 #pragma unroll
     for (int u = 0; u < 4; ++u) sr[u] = qjl ? row[u] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  mid();
   __shared__ uint4 qjb[4][4][16];
 #pragma unroll
   for (int pp = 0; pp < RT * kD / kT; ++pp) (&qnat[0][0])[tid + kT * pp] = qv[pp];
@@ -1198,6 +1202,11 @@ __device__ inline void qrot_body(const AttnArgs& a, int tile) {
 }
 
 template <int RT>
+__device__ inline void qrot_body(const AttnArgs& a, int tile) {
+  qrot_body_with<RT>(a, tile, [] {});
+}
+
+template <int RT>
 __global__ void __launch_bounds__(64 * kQrotWaves) attn_qrot_kernel(AttnArgs a) { qrot_body<RT>(a, blockIdx.x); }
 
 // Decode step preparation in one launch: workgroups [0, n_app) append the step's
@@ -1211,6 +1220,16 @@ __global__ void __launch_bounds__(1024) decode_prep_kernel(AppendArgs ap, AttnAr
     else append_token_body(ap, w / (3 * ap.n_kv), (w / 3) % ap.n_kv, w % 3);
   }
   else qrot_body<8>(aa, w - n_app);
+}
+
+// The same preparation when every token-head has one workgroup and one row tile (one
+// row tile per KV head, many token-heads, no QJL sketch): workgroup w = sequence w / n_kv,
+// KV head w % n_kv both appends that token and rotates that tile's queries, with the
+// rotation's loads issued before the append, so the launch runs in one round of workgroups
+// instead of two.
+__global__ void __launch_bounds__(1024) decode_prep_pair_kernel(AppendArgs ap, AttnArgs aa) {
+  const int w = blockIdx.x;
+  qrot_body_with<8, false>(aa, w, [&] { append_token_body(ap, w / ap.n_kv, w % ap.n_kv, 3); });
 }
 
 // fp16 window copies: token t / KV head h (one 128-thread workgroup) to its sink slot
@@ -3832,8 +3851,12 @@ gtq_status gtq_decode_prepare(const gtq_plan* plan, int32_t layer, const gtq_cac
   aa.qscale = softmax_scale * LOG2E_F;
   const int roles = append_roles((int64_t)cache->batch * plan->n_kv);
   const int n_app = cache->batch * plan->n_kv * roles;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)(n_app + L.n_tiles)), dim3(1024), 0, (hipStream_t)hip_stream,
-                     ap, aa, n_app, roles);
+  if (roles == 1 && L.tiles_per_kv == 1 && !aa.qjl)  // (then n_app == L.n_tiles)
+    hipLaunchKernelGGL(decode_prep_pair_kernel, dim3((unsigned)L.n_tiles), dim3(1024), 0, (hipStream_t)hip_stream,
+                       ap, aa);
+  else
+    hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)(n_app + L.n_tiles)), dim3(1024), 0,
+                       (hipStream_t)hip_stream, ap, aa, n_app, roles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq_decode_prepare: launch");
   return ok();

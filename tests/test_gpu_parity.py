@@ -233,6 +233,57 @@ def test_decode_step_fused(G, nc):
     _say(f"  append ties={ties}; decode of 3 sequences compared")
 
 
+@pytest.mark.parametrize("nc,v_hadamard", [(False, False), (True, False), (False, True)])
+def test_decode_step_one_round_prepare(G, nc, v_hadamard):
+    """gtq_decode_step with as many token-heads as the chip has compute units and one row
+    tile per KV head (32 sequences x 4 KV heads, g = 8): the prepare launch gives each
+    workgroup one token append and one tile's query rotation. Caches and outputs equal the
+    separate append + decode calls bit for bit; records and outputs of sampled sequences
+    against the oracle; a sequence of length 0 appends nothing and is counted once."""
+    _say(f"case: decode step, one-round prepare (32 x 4 token-heads), nc={nc} v_hadamard={v_hadamard}")
+    B, H, g, cap = 32, 4, 8, 96
+    case = Case(41, 1, H, g, cap, 128, 2, batch=B, nc=nc, v_hadamard=v_hadamard)
+    plan = case.plan()
+    rng = np.random.default_rng(7)
+    lens = [int(x) for x in rng.integers(1, cap + 1, B)]
+    lens[5] = 0
+    lens[9] = cap
+    cache = G.PackedCache(plan, B, cap)
+    knew = np.zeros((B, H, 128), np.float32)
+    vnew = np.zeros((B, H, 128), np.float32)
+    for b, n in enumerate(lens):
+        if n > 1:
+            k, v = case.kv(0, b, 0, n - 1)
+            G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k), _dev(v), b, 0)
+        if n > 0:
+            k, v = case.kv(0, b, n - 1, n)
+            knew[b], vnew[b] = k[0], v[0]
+    ref_cache = cache.clone()
+    q = np.stack([case.q(0, b) for b in range(B)])
+    sl = _dev(np.array(lens, np.int32))
+    sc = scale_default()
+    out = G.gtq_decode_step(plan, 0, cache, _dev(knew), _dev(vnew), _dev(q), sl, cap, sc)
+    live = [b for b, n in enumerate(lens) if n > 0]
+    G.gtq_quantize_append(plan, 0, ref_cache, _dev(knew[live]), _dev(vnew[live]),
+                          _dev(np.array(live, np.int32)), _dev(np.array([lens[b] - 1 for b in live], np.int64)))
+    out_sep = G.gtq_decode_attn(plan, 0, ref_cache, _dev(q), sl, cap, sc)
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_norms", "v_codes", "v_norms"):
+        assert torch.equal(getattr(cache, name), getattr(ref_cache, name)), name
+    assert torch.equal(out, out_sep)
+    assert plan.overflow_count() == 1
+    assert torch.count_nonzero(out[5]) == 0
+    ties = 0
+    for b in (0, 9, 17, 31):
+        n = lens[b]
+        enc = _encode(case, 0, b, n)
+        t, _ = _check_append(case, cache, 0, b, n, enc, f"one-round step b{b}")
+        ties += t
+        _, out_ref = _oracle_decode(case, 0, b, n, _records_from_gpu(case, cache, 0, b, n), q[b], sc)
+        assert_close(out[b].cpu().numpy(), out_ref, f"one-round step out b{b}")
+    _say(f"  append ties={ties}; 4 sampled sequences compared")
+
+
 @pytest.mark.parametrize("k_budget,v_bits,g,layout", [(128, 1, 8, 0), (192, 3, 8, 0), (160, 4, 2, 0),
                                                       (64, 2, 8, 0), (256, 2, 4, 0), (192, 3, 2, 1),
                                                       (96, 1, 1, 1)])
