@@ -284,6 +284,53 @@ def test_decode_step_one_round_prepare(G, nc, v_hadamard):
     _say(f"  append ties={ties}; 4 sampled sequences compared")
 
 
+def test_decode_step_one_round_prepare_paged(G):
+    """The one-round decode-step prepare (32 sequences x 4 KV heads, g = 8) over a paged
+    cache (32-token pages, pool pages shuffled): the same records as over a contiguous
+    cache, and the outputs of both against the oracle (sampled sequences)."""
+    _say("case: decode step, one-round prepare, paged cache (32 x 4 token-heads)")
+    B, H, g, P, maxp = 32, 4, 8, 32, 3
+    cap = P * maxp
+    case = Case(43, 1, H, g, cap, 128, 2, batch=B)
+    plan = case.plan()
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(1, cap + 1, B)]
+    cont = G.PackedCache(plan, B, cap)
+    pc = G.PagedCache(plan, B, B * maxp, P, maxp)
+    pc.block_table.copy_(torch.from_numpy(rng.permutation(B * maxp).astype(np.int32).reshape(B, maxp)))
+    knew = np.zeros((B, H, 128), np.float32)
+    vnew = np.zeros((B, H, 128), np.float32)
+    for b, n in enumerate(lens):
+        k, v = case.kv(0, b, 0, n)
+        if n > 1:
+            for c in (cont, pc):
+                G.gtq_quantize_append_chunk(plan, 0, c, _dev(k[:n - 1]), _dev(v[:n - 1]), b, 0)
+        knew[b], vnew[b] = k[n - 1], v[n - 1]
+    q = np.stack([case.q(0, b) for b in range(B)])
+    sl = _dev(np.array(lens, np.int32))
+    sc = scale_default()
+    o_c = G.gtq_decode_step(plan, 0, cont, _dev(knew), _dev(vnew), _dev(q), sl, cap, sc)
+    o_p = G.gtq_decode_step(plan, 0, pc, _dev(knew), _dev(vnew), _dev(q), sl, cap, sc)
+    torch.cuda.synchronize()
+    # (a paged cache decodes every K-block slot through the generic path, so its outputs
+    # round differently from the contiguous kernel's specialized slots: both are compared
+    # with the oracle, and with each other at the same tolerance)
+    assert_close(o_p.cpu().numpy(), o_c.cpu().numpy(), "one-round step paged vs contiguous")
+    assert plan.overflow_count() == 0
+    kc, kn, vc, vn = _cache_arrays(cont, case)
+    for b in (0, 13, 31):
+        n = lens[b]
+        for h, (kw, knn, vcodes, vnn) in enumerate(_gather_paged(case, pc, b, n)):
+            assert np.array_equal(kw, kc[b, h, :n]), f"paged K codes b{b} h{h}"
+            assert np.array_equal(knn, kn[b, h, :n]), f"paged K norms b{b} h{h}"
+            assert np.array_equal(vnn, vn[b, h, :n]), f"paged V norms b{b} h{h}"
+            assert np.array_equal(vcodes, v_codes_from_physical(vc[b, h], n, case.v_bits)), f"paged V b{b} h{h}"
+        _, ref = _oracle_decode(case, 0, b, n, _records_from_gpu(case, cont, 0, b, n), q[b], sc)
+        assert_close(o_p[b].cpu().numpy(), ref, f"one-round paged step out b{b}")
+        assert_close(o_c[b].cpu().numpy(), ref, f"one-round contiguous step out b{b}")
+    _say("  paged one-round step: records and outputs of 3 sequences compared")
+
+
 @pytest.mark.parametrize("k_budget,v_bits,g,layout", [(128, 1, 8, 0), (192, 3, 8, 0), (160, 4, 2, 0),
                                                       (64, 2, 8, 0), (256, 2, 4, 0), (192, 3, 2, 1),
                                                       (96, 1, 1, 1)])
