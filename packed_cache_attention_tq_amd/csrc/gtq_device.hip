@@ -1023,8 +1023,11 @@ __device__ inline float sum_over_q(float x) {
   x += xor16(x);
   return x + xor32(x);
 }
-// value of lane l ^ 48
-__device__ inline float swap_q3(float x) { return xor16(xor32(x)); }
+// value of lane l ^ 48 through the LDS crossbar, one instruction per value (lane = this
+// lane's index): cheaper than two lane swaps where many values move at once
+__device__ inline float lane_xor48(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 48) << 2, __builtin_bit_cast(int, x)));
+}
 
 // ---------------------------------------------------------------- query rotation
 
@@ -1796,7 +1799,7 @@ __device__ inline void window_split(const AttnArgs& a, AttnShared& S, int tile) 
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
+    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + lane_xor48(oacc[t][3 - e], (int)(threadIdx.x & 63));
   }
   if (active && q < 2) {
 #pragma unroll
@@ -2746,7 +2749,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + swap_q3(oacc[t][3 - e]);
+    for (int e = 0; e < 4; ++e) vrow[t][e] = oacc[t][e] + lane_xor48(oacc[t][3 - e], tid_x & 63);
   }
   __syncthreads();  // every wave is done with its key tile
   if (q_x == 0 && n_x < 8) {
@@ -2762,7 +2765,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, S.om[w][r]);
     const float mw = S.om[wave][r];
-    wt[e] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+    wt[e] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);  // (<= 1; tiny weights may flush)
   }
   if (wave >= 8 && q_x < 2) {
 #pragma unroll
@@ -2799,7 +2802,7 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int w = 0; w < kDecWaves; ++w) {
           const float mw = S.om[w][r];
-          l = fmaf((mw == -INFINITY) ? 0.f : exp2f(mw - M), S.ol[w][r], l);
+          l = fmaf((mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M), S.ol[w][r], l);
         }
       }
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
