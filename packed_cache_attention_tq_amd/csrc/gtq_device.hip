@@ -2161,7 +2161,7 @@ struct DecShared {
   uint4 qjlb[4][4][16];              // QJL plans: the residual sketch's operands
   int32_t row_id[8];
   int32_t row_len[8];
-  float om[kDecWaves][8];
+  alignas(16) float om[kDecWaves][8];  // (rows read as float4)
   float ol[kDecWaves][8];
 };
 static_assert(offsetof(DecShared, u) == 0, "tables at the start of the shared block");
@@ -2757,15 +2757,21 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
     S.ol[wave][n_x] = l_run;
   }
   __syncthreads();
-  float wt[4];  // 2^(m_wave - M) of rows 4 (q_x & 1) + e
+  float wt[4];  // 2^(m_wave - M) of rows 4 (q_x & 1) + e (the four rows read as one float4)
+  {
+    const int r4 = 4 * (q_x & 1);
+    float4 M = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = 4 * (q_x & 1) + e;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, S.om[w][r]);
-    const float mw = S.om[wave][r];
-    wt[e] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);  // (<= 1; tiny weights may flush)
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float4 o = *reinterpret_cast<const float4*>(&S.om[w][r4]);
+      M = make_float4(fmaxf(M.x, o.x), fmaxf(M.y, o.y), fmaxf(M.z, o.z), fmaxf(M.w, o.w));
+    }
+    const float4 mw = *reinterpret_cast<const float4*>(&S.om[wave][r4]);
+    // (<= 1; tiny weights may flush)
+    wt[0] = (mw.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw.x - M.x);
+    wt[1] = (mw.y == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw.y - M.y);
+    wt[2] = (mw.z == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw.z - M.z);
+    wt[3] = (mw.w == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw.w - M.w);
   }
   if (wave >= 8 && q_x < 2) {
 #pragma unroll
