@@ -1301,9 +1301,12 @@ struct AttnWave {
 // Shared block of a partials workgroup whose row tile has RT rows (8: high/low query
 // parts share one B operand; 16: separate high and low B operands).
 template <int RT>
+constexpr int kQ2Copies = RT == 16 ? 8 : 1;
+template <int RT>
 struct AttnSharedT {
   uint4 oct1[256];                   // byte-indexed decode tables (DevCodebook::oct1, quad2)
-  uint2 quad2[256];
+  uint2 quad2[256][kQ2Copies<RT>];   // (16-row tiles: each entry 8 times, lane l reads copy
+                                     // l mod 8, so that random lookups meet fewer bank conflicts)
   uint32_t lut[kPairTable + 4];      // decode table (DevCodebook::pair)
   uint4 qb[(RT / 8) * kMaxKB][4][16];  // QK B operand(s) per K-block and lane
   int32_t row_id[RT];
@@ -1326,7 +1329,9 @@ __device__ inline half8 dequant8(const SH& S, uint32_t F) {
   if constexpr (R == 1) {
     o.v = S.oct1[F & 0xFFu];
   } else if constexpr (R == 2) {
-    const uint2 x = S.quad2[F & 0xFFu], y = S.quad2[(F >> 8) & 0xFFu];
+    constexpr int C = sizeof(S.quad2[0]) / sizeof(uint2);  // copies of an entry
+    const int c = (int)(threadIdx.x & (C - 1));
+    const uint2 x = S.quad2[F & 0xFFu][c], y = S.quad2[(F >> 8) & 0xFFu][c];
     o.u[0] = x.x;
     o.u[1] = x.y;
     o.u[2] = y.x;
@@ -1993,8 +1998,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     const int e = tid + kThreads * u;
     if (e < kPairTable) S.lut[e] = lutv[u];
   }
-  if (tid < 256) S.oct1[tid] = tabv;
-  else S.quad2[tid - 256] = make_uint2(tabv.x, tabv.y);
+  if (tid < 256) {
+    S.oct1[tid] = tabv;
+  } else {
+#pragma unroll
+    for (int c = 0; c < kQ2Copies<RT>; ++c) S.quad2[tid - 256][c] = make_uint2(tabv.x, tabv.y);
+  }
   if (tid < RT) {
     int L;
     S.row_id[tid] = tile_row<RT>(a, seq, h, tr, tid, len_ld, &L);
@@ -3504,7 +3513,7 @@ gtq_status launch_partials(const gtq_plan* p, int layer, AttnArgs& aa, const Att
 
 // merge workgroups per row (tile): one per quarter of the inverse rotation while few rows
 // (tiles) leave most compute units idle, else one
-inline unsigned merge_quarters(int64_t n) { return n < 256 ? 4u : 1u; }
+inline unsigned merge_quarters(int64_t n) { return n <= 256 ? 4u : 1u; }
 
 gtq_status launch_merge(const gtq_plan* p, int layer, const AttnLaunch& L, const int32_t* seq_len,
                         int64_t pos0, int prefill, int max_len, float* out, const void* ws,
