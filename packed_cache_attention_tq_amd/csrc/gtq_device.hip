@@ -237,8 +237,16 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, n = lane & 15;
-  const int h = blockIdx.y;
-  const bool vrole = blockIdx.z != 0;
+  // a one-dimensional grid of gx x n_kv x 2 workgroups: workgroup w takes KV head
+  // w mod n_kv, and its first tile and role from w / n_kv. Consecutive workgroups go to
+  // the eight accelerator dies (XCDs) in turn, so with n_kv a divisor or a multiple of 8
+  // all workgroups of a head run on the same dies, and each die's L2 fetches only its
+  // own heads' rotations.
+  const int h = (int)(blockIdx.x % (unsigned)a.n_kv);
+  const int wr = (int)(blockIdx.x / (unsigned)a.n_kv);
+  const int gx = (int)(gridDim.x / (2u * (unsigned)a.n_kv));
+  const int bx = wr % gx;
+  const bool vrole = wr >= gx;
   const DevHead* __restrict__ hp = a.heads + h;
   const int n_groups = hp->n_groups;
 
@@ -318,11 +326,11 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
     return ok;
   };
   float xr[8];
-  bool xok = load_tile(blockIdx.x, xr);
+  bool xok = load_tile(bx, xr);
   using KArgsA = const __attribute__((address_space(4))) AppendArgs;
   KArgsA* const ka0 = (KArgsA*)__builtin_amdgcn_kernarg_segment_ptr();
 
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  for (int64_t tile = bx; tile < n_tiles; tile += gx) {
     // the arguments the tile reads, loaded again in each tile rather than held in
     // registers across the loop
     KArgsA* kap = ka0;
@@ -332,7 +340,7 @@ __global__ void __launch_bounds__(kAppThreads) __attribute__((amdgpu_waves_per_e
     float x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = xok ? xr[i] : 0.f;
-    xok = load_tile(tile + gridDim.x, xr);  // next tile, in flight during this one
+    xok = load_tile(tile + gx, xr);  // next tile, in flight during this one
     __syncthreads();                  // the previous tile's stores have read the buffers
     if (tid < kAppTile * 16) (&S.pk[0][0])[tid] = 0u;
     (&S.pv[0][0])[tid] = 0u;          // 4 x 128 == kAppThreads
@@ -3332,7 +3340,7 @@ gtq_status launch_append(const gtq_plan* p, int layer, const gtq_cache_view* c, 
   // next tile's inputs in flight
   const int64_t per_head = std::max<int64_t>(1, 512 / (2 * (int64_t)p->n_kv));
   const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(n_tiles, per_head));
-  hipLaunchKernelGGL(append_gemm_kernel, dim3(gx, p->n_kv, 2), dim3(kAppThreads), 0, stream, a);
+  hipLaunchKernelGGL(append_gemm_kernel, dim3((unsigned)(gx * p->n_kv * 2)), dim3(kAppThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "gtq append: launch");
   return ok();
