@@ -360,6 +360,25 @@ def test_append_and_decode_rates(G, k_budget, v_bits, g, layout):
     assert_close(out[0].cpu().numpy(), out_ref, "out")
 
 
+@pytest.mark.parametrize("H,n,splits", [(3, 300, (0, 37, 300)), (5, 2100, (0, 1000, 2100))])
+def test_chunk_append_head_counts(G, H, n, splits):
+    """Chunked append with KV-head counts that do not divide the eight dies: the append's
+    one-dimensional grid gives workgroup w the KV head w mod H, and with 5 heads over 66
+    tiles some workgroups take two tiles. Every head's codes (up to counted threshold
+    ties) and norms (bit for bit) against the oracle, ragged tails included."""
+    _say(f"case: chunked append with {H} KV heads, {n} tokens in chunks at {splits}")
+    case = Case(4, 1, H, 2, n, 128, 2, batch=1)
+    plan = case.plan()
+    cache = G.PackedCache(plan, 1, (n + 31) // 32 * 32)
+    k, v = case.kv(0, 0)
+    for lo, hi in zip(splits[:-1], splits[1:]):
+        G.gtq_quantize_append_chunk(plan, 0, cache, _dev(k[lo:hi]), _dev(v[lo:hi]), 0, lo)
+    torch.cuda.synchronize()
+    enc = _encode(case, 0, 0, n)
+    ties, ulps = _check_append(case, cache, 0, 0, n, enc, f"chunked append H={H}")
+    _say(f"  append ties={ties} norm-ulps={ulps}")
+
+
 def test_scatter_append_random_order_and_overflow(G):
     _say("case: scatter append in random order + overflow counting")
     n = 150
