@@ -2739,10 +2739,13 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
       pa.u[k] = lo ? recv : keep;
       pa.u[2 + k] = lo ? keep : recv;
     }
-    // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis)
+    // ---- PV over the 8 value tiles (coordinate 8n + t of the rotated basis), at raised
+    //      wave priority so that a wave holding its operands issues its products first
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa.h, dec_dequant8<VB>(sb, DL, vfield<VB>(blk.vw, t)), oacc[t], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
     if (more) {
       if constexpr (PAGED) {
         dec_load_v<VB, KWL>(blk, page_views(__builtin_amdgcn_readfirstlane(pg_next)), t_next, voff_v);
